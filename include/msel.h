@@ -1,0 +1,165 @@
+/*
+ * msel.h -- C ABI of the MI355X (gfx950) selective-scan library, libmsel.so.
+ *
+ * The library computes the selective state-space scan at the heart of Mamba, per batch row b,
+ * channel d and state n:
+ *
+ *   Delta_t = softplus(delta_t + bias[d])   (or delta_t + bias[d] when the softplus flag is 0)
+ *   dA_t    = exp(Delta_t * A[d,n])         zero-order hold for the transition
+ *   dB_t x_t = Delta_t * B[b,n,t] * u_t      Euler for the input
+ *   h_t     = dA_t * h_{t-1} + dB_t x_t      the selective recurrence (h_{-1} = h0 or 0)
+ *   y_t     = sum_n C[b,n,t] * h_t + D[d] * u_t
+ *   out_t   = y_t * silu(z_t)                (out_t = y_t when z is NULL)
+ *
+ * Sources (five web pages collected on "mamba paper"): the selection mechanism that makes
+ * Delta, B and C functions of the token (page 1, abstract paragraph); the mix of zero-order
+ * hold and Euler discretization (page 5, Mamba-3 post, discretization bullet); the recurrent
+ * mode that reads one time step at a time (page 3); the work-efficient parallel scan of the
+ * recurrence (page 1); the fused scan that splits long sequences into chunks and continues
+ * from the intermediate state of the previous chunk (page 4, Appendix D "Hardware-aware
+ * Algorithm For Selective SSMs", Speed paragraph); states recomputed, not stored, in the
+ * backward pass (page 1; page 4 Appendix D, Memory paragraph); the cache that keeps the SSM
+ * state after the scan (page 1, page 2).  The D skip term inside the gate and the gate itself
+ * follow the plainest reading of that description.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, contiguous, row-major.
+ *  - The caller owns every buffer.  The library allocates nothing, keeps no state between
+ *    calls, is re-entrant, and never synchronizes: work is enqueued on `stream` and the
+ *    call returns.  Errors in the arguments are detected on the host before anything is
+ *    enqueued; the return value is then not MSEL_OK and no device memory is touched.
+ *  - Inputs are read-only.  Outputs must not be the same pointer as any input (checked).
+ *  - Layouts:
+ *      u, delta, z, out                  [batch, dim, seqlen]     activation dtype
+ *      B, C                              [batch, dstate, seqlen]  activation dtype
+ *      A                                 [dim, dstate]            fp32
+ *      D, delta_bias                     [dim]                    fp32
+ *      h0, final_state                   [batch, dim, dstate]     fp32
+ *      chunk_states                      [batch, dim, n_chunks, dstate] fp32,
+ *                                        n_chunks = ceil(seqlen / msel_chunk_len()),
+ *                                        entry c = state before time step c*chunk_len
+ *  - Activation dtype: MSEL_F32 (fp32) or MSEL_BF16 (bfloat16, stored 2 bytes, rounded to
+ *    nearest even on output).  The state, every accumulation and A, D, bias are fp32.
+ *  - Activation pointers must be 16-byte aligned.
+ */
+#ifndef MSEL_H
+#define MSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t, declared the same way the HIP runtime declares it. */
+typedef struct ihipStream_t *hipStream_t;
+
+#define MSEL_ABI_VERSION 1
+
+typedef enum {
+    MSEL_OK = 0,
+    MSEL_ERR_NULL = 1,        /* a required pointer is NULL                                */
+    MSEL_ERR_SHAPE = 2,       /* a size is < 1, or sizes overflow the supported range      */
+    MSEL_ERR_DTYPE = 3,       /* dtype is not MSEL_F32 / MSEL_BF16, or softplus not 0/1     */
+    MSEL_ERR_ALIGN = 4,       /* an activation pointer is not 16-byte aligned              */
+    MSEL_ERR_UNSUPPORTED = 5, /* dstate outside 1..MSEL_MAX_DSTATE                          */
+    MSEL_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than msel_scan_bwd_workspace_bytes */
+    MSEL_ERR_ALIAS = 7,       /* an output pointer equals an input pointer                 */
+    MSEL_ERR_HIP = 8,         /* the HIP runtime reported an error at launch               */
+    MSEL_ERR_VERSION = 9      /* args->abi_version != MSEL_ABI_VERSION                     */
+} msel_status;
+
+typedef enum { MSEL_F32 = 0, MSEL_BF16 = 1 } msel_dtype;
+
+#define MSEL_MAX_DSTATE 16
+
+/* Problem description shared by the three entry points. */
+typedef struct {
+    int32_t abi_version;    /* must be MSEL_ABI_VERSION                                    */
+    int32_t batch;          /* >= 1                                                        */
+    int32_t dim;            /* channels, >= 1                                              */
+    int32_t dstate;         /* N, 1..MSEL_MAX_DSTATE                                       */
+    int32_t seqlen;         /* L, >= 1                                                     */
+    int32_t dtype;          /* msel_dtype of u, delta, z, B, C, out (and of the gradients   */
+                            /* du, ddelta, dz, dout)                                       */
+    int32_t delta_softplus; /* 1: Delta = softplus(delta + bias); 0: Delta = delta + bias   */
+    int32_t reserved;       /* must be 0                                                   */
+    const void *u;          /* required                                                    */
+    const void *delta;      /* required: raw Delta before bias and softplus                */
+    const void *B;          /* required                                                    */
+    const void *C;          /* required by fwd and bwd; ignored by chunk_carry             */
+    const void *z;          /* optional gate input; NULL means out = y                     */
+    const float *A;         /* required                                                    */
+    const float *D;         /* optional skip weight; NULL means 0                          */
+    const float *delta_bias;/* optional; NULL means 0                                      */
+    const float *h0;        /* optional initial state; NULL means 0                        */
+    void *out;              /* fwd: required output                                        */
+    float *final_state;     /* fwd / chunk_carry: optional output, state after step L-1    */
+    float *chunk_states;    /* fwd: optional output; chunk_carry: required output;          */
+                            /* bwd: optional input (recomputed into the workspace if NULL) */
+} msel_scan_args;
+
+/* Gradients of a scalar loss given dL/dout.  Every output is overwritten, not accumulated. */
+typedef struct {
+    const void *dout;       /* required, activation dtype                                  */
+    void *du;               /* required, activation dtype                                  */
+    void *ddelta;           /* required, activation dtype: gradient w.r.t. the raw delta    */
+    void *dz;               /* activation dtype; required iff args->z != NULL               */
+    float *dA;              /* optional [dim, dstate]                                      */
+    float *dB;              /* optional [batch, dstate, seqlen]                             */
+    float *dC;              /* optional [batch, dstate, seqlen]                             */
+    float *dD;              /* optional [dim] (computed even when args->D is NULL)          */
+    float *ddelta_bias;     /* optional [dim]                                              */
+    float *dh0;             /* optional [batch, dim, dstate]: gradient w.r.t. h0            */
+} msel_scan_grads;
+
+/* Version of this ABI, MSEL_ABI_VERSION of the built library. */
+int32_t msel_abi_version(void);
+
+/* Length T of the chunks the scan is split into (a multiple of 64); chunk_states hold one
+ * state per chunk. */
+int32_t msel_chunk_len(void);
+
+/* ceil(seqlen / msel_chunk_len()), or 0 if seqlen < 1. */
+int32_t msel_num_chunks(int32_t seqlen);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *msel_status_string(msel_status status);
+
+/* Host-only argument checks used by the entry points below; they touch no device memory and
+ * make no HIP call.  `grads` and `workspace` are checked by msel_validate_bwd only. */
+msel_status msel_validate_fwd(const msel_scan_args *args);
+msel_status msel_validate_chunk_carry(const msel_scan_args *args);
+msel_status msel_validate_bwd(const msel_scan_args *args, const msel_scan_grads *grads,
+                              const void *workspace, size_t workspace_bytes);
+
+/* Fused forward scan (page 4, Appendix D, Speed: one fused pass, chunked with carried
+ * states).  Reads u, delta, B, C, z once, keeps the state on chip, writes out, and optionally
+ * final_state and chunk_states.  Deterministic: the same inputs give the same bits. */
+msel_status msel_scan_fwd(const msel_scan_args *args, hipStream_t stream);
+
+/* Chunk-carry pass (page 4, Appendix D, Speed: "as long as we have the intermediate scan
+ * states, we can continue the scan with the next chunk").  For every chunk it computes the
+ * state transition over the chunk and the chunk's local end state, then links them,
+ * H_{c+1} = P_c * H_c + S_c with H_0 = h0, into chunk_states (required) and final_state
+ * (optional).  Reads u, delta, B, A, delta_bias, h0 only. */
+msel_status msel_scan_chunk_carry(const msel_scan_args *args, hipStream_t stream);
+
+/* Workspace the backward needs, in bytes (0 when args->chunk_states is given and no other
+ * scratch is needed).  Returns 0 for invalid args. */
+size_t msel_scan_bwd_workspace_bytes(const msel_scan_args *args);
+
+/* Backward with recomputation (page 1; page 4 Appendix D, Memory: intermediate states are
+ * recomputed, not stored).  If args->chunk_states is NULL the chunk-carry pass first rebuilds
+ * them into `workspace`.  Reductions over channels (dB, dC) and over batch and time (dA, dD,
+ * ddelta_bias) use fp32 atomics, so those outputs may differ in the last bits between runs;
+ * du, ddelta, dz and dh0 are deterministic. */
+msel_status msel_scan_bwd(const msel_scan_args *args, const msel_scan_grads *grads,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSEL_H */

@@ -1,0 +1,11 @@
+"""MI355X (gfx950) selective SSM scan: a C-ABI HIP library (libmsel.so) and its thin binding.
+
+    from selective_state_space_26_amd import msel_scan_fwd, msel_scan_bwd, msel_scan_chunk_carry
+
+The kernels live in ``csrc/``; ``build.py`` compiles them in-tree.  Importing this package does
+not load the library; the first call does, and raises if it is not built.
+"""
+from .scan import (chunk_len, msel_scan_bwd, msel_scan_chunk_carry, msel_scan_fwd,  # noqa: F401
+                   num_chunks)
+
+__all__ = ["msel_scan_fwd", "msel_scan_bwd", "msel_scan_chunk_carry", "chunk_len", "num_chunks"]

@@ -1,0 +1,92 @@
+"""ctypes view of include/msel.h and the loader of the in-tree libmsel.so.
+
+There is no fallback of any kind: if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmsel.so")
+
+ABI_VERSION = 1
+MSEL_F32, MSEL_BF16 = 0, 1
+STATUS = {0: "MSEL_OK", 1: "MSEL_ERR_NULL", 2: "MSEL_ERR_SHAPE", 3: "MSEL_ERR_DTYPE",
+          4: "MSEL_ERR_ALIGN", 5: "MSEL_ERR_UNSUPPORTED", 6: "MSEL_ERR_WORKSPACE",
+          7: "MSEL_ERR_ALIAS", 8: "MSEL_ERR_HIP", 9: "MSEL_ERR_VERSION"}
+
+_P = ctypes.c_void_p
+
+
+class ScanArgs(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("dim", ctypes.c_int32), ("dstate", ctypes.c_int32),
+                ("seqlen", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("delta_softplus", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("u", _P), ("delta", _P), ("B", _P), ("C", _P), ("z", _P), ("A", _P),
+                ("D", _P), ("delta_bias", _P), ("h0", _P), ("out", _P), ("final_state", _P),
+                ("chunk_states", _P)]
+
+
+class ScanGrads(ctypes.Structure):
+    _fields_ = [("dout", _P), ("du", _P), ("ddelta", _P), ("dz", _P), ("dA", _P), ("dB", _P),
+                ("dC", _P), ("dD", _P), ("ddelta_bias", _P), ("dh0", _P)]
+
+
+class MselError(RuntimeError):
+    def __init__(self, fn: str, code: int, text: str):
+        super().__init__(f"{fn} returned {STATUS.get(code, code)}: {text}")
+        self.code = code
+
+
+_lib = None
+
+EXPORTS = ["msel_abi_version", "msel_chunk_len", "msel_num_chunks", "msel_status_string",
+           "msel_validate_fwd", "msel_validate_chunk_carry", "msel_validate_bwd",
+           "msel_scan_fwd", "msel_scan_chunk_carry", "msel_scan_bwd_workspace_bytes",
+           "msel_scan_bwd"]
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libmsel.so (once).  Raises if it is missing: the product has no other path."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run `python -m selective_state_space_26_amd.build`"
+                           " (or __graft_entry__.build())")
+    lib = ctypes.CDLL(p)
+    a, g = ctypes.POINTER(ScanArgs), ctypes.POINTER(ScanGrads)
+    lib.msel_abi_version.restype = ctypes.c_int32
+    lib.msel_abi_version.argtypes = []
+    lib.msel_chunk_len.restype = ctypes.c_int32
+    lib.msel_chunk_len.argtypes = []
+    lib.msel_num_chunks.restype = ctypes.c_int32
+    lib.msel_num_chunks.argtypes = [ctypes.c_int32]
+    lib.msel_status_string.restype = ctypes.c_char_p
+    lib.msel_status_string.argtypes = [ctypes.c_int]
+    for fn in ("msel_validate_fwd", "msel_validate_chunk_carry"):
+        getattr(lib, fn).restype = ctypes.c_int
+        getattr(lib, fn).argtypes = [a]
+    lib.msel_validate_bwd.restype = ctypes.c_int
+    lib.msel_validate_bwd.argtypes = [a, g, _P, ctypes.c_size_t]
+    lib.msel_scan_fwd.restype = ctypes.c_int
+    lib.msel_scan_fwd.argtypes = [a, _P]
+    lib.msel_scan_chunk_carry.restype = ctypes.c_int
+    lib.msel_scan_chunk_carry.argtypes = [a, _P]
+    lib.msel_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.msel_scan_bwd_workspace_bytes.argtypes = [a]
+    lib.msel_scan_bwd.restype = ctypes.c_int
+    lib.msel_scan_bwd.argtypes = [a, g, _P, ctypes.c_size_t, _P]
+    if lib.msel_abi_version() != ABI_VERSION:
+        raise RuntimeError("libmsel.so ABI version mismatch")
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def check(fn: str, code: int) -> None:
+    if code != 0:
+        raise MselError(fn, code, load().msel_status_string(code).decode())

@@ -1,0 +1,213 @@
+// msel_api.cpp -- the extern "C" entry points declared in include/msel.h.
+//
+// Every entry point first validates its arguments on the host (no HIP call, no device memory
+// touched) and only then enqueues kernels on the caller's stream.  The library never
+// allocates, never synchronizes and keeps no state.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "../../include/msel.h"
+#include "msel_kernels.hpp"
+
+namespace {
+
+constexpr int64_t kMaxSeq = int64_t(1) << 30;
+constexpr int64_t kMaxRows = int64_t(1) << 30;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+msel_status check_common(const msel_scan_args* a) {
+    if (a == nullptr) return MSEL_ERR_NULL;
+    if (a->abi_version != MSEL_ABI_VERSION || a->reserved != 0) return MSEL_ERR_VERSION;
+    if (a->batch < 1 || a->dim < 1 || a->dstate < 1 || a->seqlen < 1) return MSEL_ERR_SHAPE;
+    if (static_cast<int64_t>(a->batch) * a->dim > kMaxRows || a->seqlen > kMaxSeq)
+        return MSEL_ERR_SHAPE;
+    if (a->dtype != MSEL_F32 && a->dtype != MSEL_BF16) return MSEL_ERR_DTYPE;
+    if (a->delta_softplus != 0 && a->delta_softplus != 1) return MSEL_ERR_DTYPE;
+    if (a->dstate > MSEL_MAX_DSTATE) return MSEL_ERR_UNSUPPORTED;
+    if (a->u == nullptr || a->delta == nullptr || a->B == nullptr || a->A == nullptr)
+        return MSEL_ERR_NULL;
+    const void* act[] = {a->u, a->delta, a->B, a->C, a->z};
+    for (const void* p : act)
+        if (p != nullptr && !aligned(p, 16)) return MSEL_ERR_ALIGN;
+    const void* f32[] = {a->A, a->D, a->delta_bias, a->h0, a->final_state, a->chunk_states};
+    for (const void* p : f32)
+        if (p != nullptr && !aligned(p, 4)) return MSEL_ERR_ALIGN;
+    return MSEL_OK;
+}
+
+bool same_as_input(const msel_scan_args* a, const void* o) {
+    if (o == nullptr) return false;
+    const void* in[] = {a->u, a->delta, a->B, a->C, a->z, a->A, a->D, a->delta_bias, a->h0};
+    for (const void* p : in)
+        if (p != nullptr && p == o) return true;
+    return false;
+}
+
+msel::ScanParams to_params(const msel_scan_args* a) {
+    msel::ScanParams p;
+    p.B = a->batch;
+    p.D = a->dim;
+    p.N = a->dstate;
+    p.L = a->seqlen;
+    p.nchunks = msel_num_chunks(a->seqlen);
+    p.softplus = a->delta_softplus;
+    p.u = a->u;
+    p.delta = a->delta;
+    p.Bm = a->B;
+    p.Cm = a->C;
+    p.z = a->z;
+    p.A = a->A;
+    p.Dv = a->D;
+    p.bias = a->delta_bias;
+    p.h0 = a->h0;
+    p.out = a->out;
+    p.final_state = a->final_state;
+    p.chunk_states = a->chunk_states;
+    return p;
+}
+
+size_t chunk_state_bytes(const msel_scan_args* a) {
+    return static_cast<size_t>(a->batch) * a->dim * msel_num_chunks(a->seqlen) * a->dstate *
+           sizeof(float);
+}
+
+msel_status hip_status(hipError_t e) { return e == hipSuccess ? MSEL_OK : MSEL_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t msel_abi_version(void) { return MSEL_ABI_VERSION; }
+
+int32_t msel_chunk_len(void) { return msel::kChunk; }
+
+int32_t msel_num_chunks(int32_t seqlen) {
+    if (seqlen < 1) return 0;
+    return static_cast<int32_t>((static_cast<int64_t>(seqlen) + msel::kChunk - 1) / msel::kChunk);
+}
+
+const char* msel_status_string(msel_status s) {
+    switch (s) {
+        case MSEL_OK: return "MSEL_OK";
+        case MSEL_ERR_NULL: return "MSEL_ERR_NULL: a required pointer is NULL";
+        case MSEL_ERR_SHAPE: return "MSEL_ERR_SHAPE: a size is out of range";
+        case MSEL_ERR_DTYPE: return "MSEL_ERR_DTYPE: unknown dtype or softplus flag";
+        case MSEL_ERR_ALIGN: return "MSEL_ERR_ALIGN: a pointer is not aligned";
+        case MSEL_ERR_UNSUPPORTED: return "MSEL_ERR_UNSUPPORTED: dstate above MSEL_MAX_DSTATE";
+        case MSEL_ERR_WORKSPACE: return "MSEL_ERR_WORKSPACE: workspace missing or too small";
+        case MSEL_ERR_ALIAS: return "MSEL_ERR_ALIAS: an output aliases an input";
+        case MSEL_ERR_HIP: return "MSEL_ERR_HIP: the HIP runtime reported an error";
+        case MSEL_ERR_VERSION: return "MSEL_ERR_VERSION: ABI version or reserved field mismatch";
+    }
+    return "MSEL_ERR_UNKNOWN";
+}
+
+msel_status msel_validate_fwd(const msel_scan_args* a) {
+    msel_status s = check_common(a);
+    if (s != MSEL_OK) return s;
+    if (a->C == nullptr || a->out == nullptr) return MSEL_ERR_NULL;
+    if (!aligned(a->out, 16)) return MSEL_ERR_ALIGN;
+    if (same_as_input(a, a->out) || same_as_input(a, a->final_state) ||
+        same_as_input(a, a->chunk_states))
+        return MSEL_ERR_ALIAS;
+    return MSEL_OK;
+}
+
+msel_status msel_validate_chunk_carry(const msel_scan_args* a) {
+    msel_status s = check_common(a);
+    if (s != MSEL_OK) return s;
+    if (a->chunk_states == nullptr) return MSEL_ERR_NULL;
+    if (same_as_input(a, a->chunk_states) || same_as_input(a, a->final_state))
+        return MSEL_ERR_ALIAS;
+    return MSEL_OK;
+}
+
+size_t msel_scan_bwd_workspace_bytes(const msel_scan_args* a) {
+    if (check_common(a) != MSEL_OK) return 0;
+    if (a->chunk_states != nullptr) return 0;
+    return chunk_state_bytes(a);
+}
+
+msel_status msel_validate_bwd(const msel_scan_args* a, const msel_scan_grads* g,
+                              const void* workspace, size_t workspace_bytes) {
+    msel_status s = check_common(a);
+    if (s != MSEL_OK) return s;
+    if (a->C == nullptr || g == nullptr || g->dout == nullptr || g->du == nullptr ||
+        g->ddelta == nullptr)
+        return MSEL_ERR_NULL;
+    if (a->z != nullptr && g->dz == nullptr) return MSEL_ERR_NULL;
+    const void* act[] = {g->dout, g->du, g->ddelta, g->dz};
+    for (const void* p : act)
+        if (p != nullptr && !aligned(p, 16)) return MSEL_ERR_ALIGN;
+    const void* f32[] = {g->dA, g->dB, g->dC, g->dD, g->ddelta_bias, g->dh0};
+    for (const void* p : f32)
+        if (p != nullptr && !aligned(p, 4)) return MSEL_ERR_ALIGN;
+    const void* outs[] = {g->du, g->ddelta, g->dz, g->dA, g->dB, g->dC, g->dD, g->ddelta_bias,
+                          g->dh0};
+    for (const void* o : outs)
+        if (same_as_input(a, o) || (o != nullptr && (o == g->dout || o == a->chunk_states)))
+            return MSEL_ERR_ALIAS;
+    const size_t need = msel_scan_bwd_workspace_bytes(a);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need) return MSEL_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return MSEL_ERR_ALIGN;
+        if (same_as_input(a, workspace) || workspace == g->dout) return MSEL_ERR_ALIAS;
+        for (const void* o : outs)
+            if (o != nullptr && o == workspace) return MSEL_ERR_ALIAS;
+    }
+    return MSEL_OK;
+}
+
+msel_status msel_scan_fwd(const msel_scan_args* a, hipStream_t stream) {
+    msel_status s = msel_validate_fwd(a);
+    if (s != MSEL_OK) return s;
+    return hip_status(msel::launch_scan_fwd(to_params(a), a->dtype == MSEL_BF16, stream));
+}
+
+msel_status msel_scan_chunk_carry(const msel_scan_args* a, hipStream_t stream) {
+    msel_status s = msel_validate_chunk_carry(a);
+    if (s != MSEL_OK) return s;
+    return hip_status(msel::launch_chunk_carry(to_params(a), a->dtype == MSEL_BF16, stream));
+}
+
+msel_status msel_scan_bwd(const msel_scan_args* a, const msel_scan_grads* g, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    msel_status s = msel_validate_bwd(a, g, workspace, workspace_bytes);
+    if (s != MSEL_OK) return s;
+    const bool bf16 = a->dtype == MSEL_BF16;
+    msel::ScanParams p = to_params(a);
+    const float* cst = a->chunk_states;
+    if (cst == nullptr) {
+        msel::ScanParams pc = p;
+        pc.chunk_states = static_cast<float*>(workspace);
+        pc.final_state = nullptr;
+        hipError_t e = msel::launch_chunk_carry(pc, bf16, stream);
+        if (e != hipSuccess) return MSEL_ERR_HIP;
+        cst = pc.chunk_states;
+    }
+    const size_t DN = static_cast<size_t>(a->dim) * a->dstate;
+    const size_t BNL = static_cast<size_t>(a->batch) * a->dstate * a->seqlen;
+    hipError_t e = hipSuccess;
+    if (e == hipSuccess) e = msel::launch_fill_zero(g->dA, DN, stream);
+    if (e == hipSuccess) e = msel::launch_fill_zero(g->dB, BNL, stream);
+    if (e == hipSuccess) e = msel::launch_fill_zero(g->dC, BNL, stream);
+    if (e == hipSuccess) e = msel::launch_fill_zero(g->dD, a->dim, stream);
+    if (e == hipSuccess) e = msel::launch_fill_zero(g->ddelta_bias, a->dim, stream);
+    if (e != hipSuccess) return MSEL_ERR_HIP;
+    msel::GradParams gp;
+    gp.dout = g->dout;
+    gp.du = g->du;
+    gp.ddelta = g->ddelta;
+    gp.dz = g->dz;
+    gp.dA = g->dA;
+    gp.dB = g->dB;
+    gp.dC = g->dC;
+    gp.dD = g->dD;
+    gp.dbias = g->ddelta_bias;
+    gp.dh0 = g->dh0;
+    return hip_status(msel::launch_scan_bwd(p, gp, cst, bf16, stream));
+}
+
+}  // extern "C"

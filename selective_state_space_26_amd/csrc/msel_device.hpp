@@ -1,0 +1,282 @@
+// msel_device.hpp -- device-side building blocks of the gfx950 selective scan.
+//
+// * fp32 transcendentals as single CDNA instructions (v_exp_f32 is 2^x, v_log_f32 is log2).
+// * bf16 <-> fp32 conversion (bf16 is the upper half of an fp32 word; stores round to
+//   nearest even with the gfx950 v_cvt_pk_bf16_f32 instruction).
+// * Row loads/stores of K consecutive time steps per lane, vectorized when the row is 16-byte
+//   aligned and fully in range, element-wise with bounds checks otherwise.
+// * Affine-pair scans over a 64-lane wavefront.  The recurrence h_t = a_t h_{t-1} + b_t is
+//   affine in h, so pairs compose associatively, (a2,b2) o (a1,b1) = (a2 a1, a2 b1 + b2);
+//   that is what makes the work-efficient parallel scan of page 1 possible.  The forward scan
+//   uses DPP row_shr 1/2/4/8 inside 16-lane rows and row_bcast 15/31 across rows; the
+//   reverse (suffix) scan uses DPP row_shl inside rows and ds_swizzle / readlane across rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msel {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}).  log1p(e) for e in (0, 1] uses the classic
+// correction log1p(e) = log(w) * e / (w - 1), w = 1 + e rounded, which cancels the rounding
+// of w; when w rounds to 1, log1p(e) = e to working precision.
+__device__ __forceinline__ float softplus_f(float x) {
+    float e = exp2_hw(-fabsf(x) * kLog2e);
+    float w = 1.0f + e;
+    float l = (w == 1.0f) ? e : log2_hw(w) * kLn2 * (e * rcp_hw(w - 1.0f));
+    return fmaxf(x, 0.0f) + l;
+}
+
+__device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
+
+// ---------------------------------------------------------------------------------------
+// dtype traits: float rows, or bf16 rows stored as uint16_t.
+
+struct bf16_t {
+    uint16_t bits;
+};
+
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+    static constexpr int kPerVec = 4;  // elements per 16-byte vector
+    __device__ static float load1(const float* p) { return *p; }
+    __device__ static void store1(float* p, float v) { *p = v; }
+};
+
+template <> struct Elem<bf16_t> {
+    static constexpr int kPerVec = 8;
+    __device__ static float load1(const bf16_t* p) {
+        return __uint_as_float(static_cast<uint32_t>(p->bits) << 16);
+    }
+    __device__ static void store1(bf16_t* p, float v) {
+        __bf16 h = static_cast<__bf16>(v);
+        p->bits = __builtin_bit_cast(uint16_t, h);
+    }
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    bf2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Load K consecutive elements row[t0 .. t0+K) as fp32; out-of-range elements read `fill`.
+// VEC: the row base is 16-byte aligned and t0 is a multiple of the vector width.
+template <typename T, int K, bool VEC>
+__device__ __forceinline__ void load_k(const T* __restrict__ row, int t0, int L, float (&v)[K],
+                                       float fill) {
+    static_assert(K % Elem<T>::kPerVec == 0, "K must be a whole number of 16-byte vectors");
+    if (VEC && t0 + K <= L) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(row + t0);
+#pragma unroll
+        for (int j = 0; j < K / Elem<T>::kPerVec; ++j) {
+            u32x4 w = __builtin_nontemporal_load(p + j);
+            if constexpr (sizeof(T) == 4) {
+                v[4 * j + 0] = __uint_as_float(w.x);
+                v[4 * j + 1] = __uint_as_float(w.y);
+                v[4 * j + 2] = __uint_as_float(w.z);
+                v[4 * j + 3] = __uint_as_float(w.w);
+            } else {
+                v[8 * j + 0] = bf16lo(w.x);
+                v[8 * j + 1] = bf16hi(w.x);
+                v[8 * j + 2] = bf16lo(w.y);
+                v[8 * j + 3] = bf16hi(w.y);
+                v[8 * j + 4] = bf16lo(w.z);
+                v[8 * j + 5] = bf16hi(w.z);
+                v[8 * j + 6] = bf16lo(w.w);
+                v[8 * j + 7] = bf16hi(w.w);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = (t0 + k < L) ? Elem<T>::load1(row + t0 + k) : fill;
+    }
+}
+
+// Same as load_k but through the normal (cached) path: for B and C, which every channel of a
+// batch row re-reads.
+template <typename T, int K, bool VEC>
+__device__ __forceinline__ void load_k_cached(const T* __restrict__ row, int t0, int L,
+                                              float (&v)[K]) {
+    if (VEC && t0 + K <= L) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(row + t0);
+#pragma unroll
+        for (int j = 0; j < K / Elem<T>::kPerVec; ++j) {
+            u32x4 w = p[j];
+            if constexpr (sizeof(T) == 4) {
+                v[4 * j + 0] = __uint_as_float(w.x);
+                v[4 * j + 1] = __uint_as_float(w.y);
+                v[4 * j + 2] = __uint_as_float(w.z);
+                v[4 * j + 3] = __uint_as_float(w.w);
+            } else {
+                v[8 * j + 0] = bf16lo(w.x);
+                v[8 * j + 1] = bf16hi(w.x);
+                v[8 * j + 2] = bf16lo(w.y);
+                v[8 * j + 3] = bf16hi(w.y);
+                v[8 * j + 4] = bf16lo(w.z);
+                v[8 * j + 5] = bf16hi(w.z);
+                v[8 * j + 6] = bf16lo(w.w);
+                v[8 * j + 7] = bf16hi(w.w);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = (t0 + k < L) ? Elem<T>::load1(row + t0 + k) : 0.0f;
+    }
+}
+
+template <typename T, int K, bool VEC>
+__device__ __forceinline__ void store_k(T* __restrict__ row, int t0, int L, const float (&v)[K]) {
+    if (VEC && t0 + K <= L) {
+        u32x4* p = reinterpret_cast<u32x4*>(row + t0);
+#pragma unroll
+        for (int j = 0; j < K / Elem<T>::kPerVec; ++j) {
+            u32x4 w;
+            if constexpr (sizeof(T) == 4) {
+                w.x = __float_as_uint(v[4 * j + 0]);
+                w.y = __float_as_uint(v[4 * j + 1]);
+                w.z = __float_as_uint(v[4 * j + 2]);
+                w.w = __float_as_uint(v[4 * j + 3]);
+            } else {
+                w.x = pack_bf16(v[8 * j + 0], v[8 * j + 1]);
+                w.y = pack_bf16(v[8 * j + 2], v[8 * j + 3]);
+                w.z = pack_bf16(v[8 * j + 4], v[8 * j + 5]);
+                w.w = pack_bf16(v[8 * j + 6], v[8 * j + 7]);
+            }
+            __builtin_nontemporal_store(w, p + j);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (t0 + k < L) Elem<T>::store1(row + t0 + k, v[k]);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Cross-lane moves.
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp(float old, float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                 __builtin_bit_cast(int, v), CTRL,
+                                                                 ROW_MASK, 0xf, false));
+}
+
+// DPP controls (GFX9 encoding).
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowShl1 = 0x101, kRowShl2 = 0x102, kRowShl4 = 0x104, kRowShl8 = 0x108;
+constexpr int kWaveShr1 = 0x138, kWaveShl1 = 0x130;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+// Lane `lane` of the result is v, the other lanes keep old (lane is wave-uniform).
+__device__ __forceinline__ float writelane(float v, int lane, float old) {
+    return (static_cast<int>(__lane_id()) == lane) ? v : old;
+}
+
+// One Hillis-Steele step: element l absorbs element l-s (which precedes it in time).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void fwd_step(float& P, float& S) {
+    float Pp = dpp<CTRL, ROW_MASK>(1.0f, P);
+    float Sp = dpp<CTRL, ROW_MASK>(0.0f, S);
+    S = fmaf(P, Sp, S);
+    P = P * Pp;
+}
+
+// Inclusive scan over the 64 lanes of a wave, lane 0 first in time:
+// (P_l, S_l) <- (P_l,S_l) o (P_{l-1},S_{l-1}) o ... o (P_0,S_0).
+__device__ __forceinline__ void wave_scan_fwd(float& P, float& S) {
+    fwd_step<kRowShr1, 0xf>(P, S);
+    fwd_step<kRowShr2, 0xf>(P, S);
+    fwd_step<kRowShr4, 0xf>(P, S);
+    fwd_step<kRowShr8, 0xf>(P, S);
+    fwd_step<kRowBcast15, 0xa>(P, S);
+    fwd_step<kRowBcast31, 0xc>(P, S);
+}
+
+// Exclusive version of an inclusive forward scan: lane l gets lane l-1's value, lane 0 the
+// identity (1, 0).
+__device__ __forceinline__ void wave_shift_fwd(float P, float S, float& Pex, float& Sex) {
+    Pex = dpp<kWaveShr1, 0xf>(1.0f, P);
+    Sex = dpp<kWaveShr1, 0xf>(0.0f, S);
+}
+
+// One reverse step: element l absorbs element l+s (which follows it in time), for the
+// backward recurrence g_t = e_t g_{t+1} + c_t: (P_l,S_l) <- (P_l, S_l) o' (P_{l+s}, S_{l+s})
+// meaning g_l_in = P_{l+s} x + S_{l+s} is fed into lane l: S_l += P_l S_{l+s}, P_l *= P_{l+s}.
+template <int CTRL>
+__device__ __forceinline__ void rev_step(float& P, float& S) {
+    float Pp = dpp<CTRL, 0xf>(1.0f, P);
+    float Sp = dpp<CTRL, 0xf>(0.0f, S);
+    S = fmaf(P, Sp, S);
+    P = P * Pp;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Inclusive suffix scan over 64 lanes, lane 63 last in time: lane l ends with the composition
+// of lanes l..63 (lane 63 applied first).
+__device__ __forceinline__ void wave_scan_rev(float& P, float& S) {
+    rev_step<kRowShl1>(P, S);
+    rev_step<kRowShl2>(P, S);
+    rev_step<kRowShl4>(P, S);
+    rev_step<kRowShl8>(P, S);
+    const int lane = lane_id();
+    // rows: lanes 0-15 absorb lane 16's row total, lanes 32-47 absorb lane 48's.
+    // ds_swizzle bit mode within 32-lane halves: and_mask 0, or_mask 16 -> every lane reads
+    // lane 16 of its half.
+    {
+        constexpr int pat = (0x00) | (0x10 << 5);
+        float Pp = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, P), pat));
+        float Sp = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, S), pat));
+        bool take = (lane & 16) == 0;
+        Pp = take ? Pp : 1.0f;
+        Sp = take ? Sp : 0.0f;
+        S = fmaf(P, Sp, S);
+        P = P * Pp;
+    }
+    // lanes 0-31 absorb lane 32's total (the suffix of lanes 32..63).
+    {
+        float Pp = readlane(P, 32);
+        float Sp = readlane(S, 32);
+        bool take = lane < 32;
+        Pp = take ? Pp : 1.0f;
+        Sp = take ? Sp : 0.0f;
+        S = fmaf(P, Sp, S);
+        P = P * Pp;
+    }
+}
+
+// Exclusive suffix: lane l gets lane l+1's inclusive suffix, lane 63 the identity.
+__device__ __forceinline__ void wave_shift_rev(float P, float S, float& Pex, float& Sex) {
+    Pex = dpp<kWaveShl1, 0xf>(1.0f, P);
+    Sex = dpp<kWaveShl1, 0xf>(0.0f, S);
+}
+
+// Sum over the 64 lanes; every lane gets the total.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<kRowShr1, 0xf>(0.0f, v);
+    v += dpp<kRowShr2, 0xf>(0.0f, v);
+    v += dpp<kRowShr4, 0xf>(0.0f, v);
+    v += dpp<kRowShr8, 0xf>(0.0f, v);
+    v += dpp<kRowBcast15, 0xa>(0.0f, v);
+    v += dpp<kRowBcast31, 0xc>(0.0f, v);
+    return readlane(v, 63);
+}
+
+}  // namespace msel

@@ -1,0 +1,51 @@
+// msel_kernels.hpp -- internal interface between the C ABI (msel_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msel {
+
+// Chunk length of the scan: 64 lanes x 8 time steps.  chunk_states hold the state before
+// every multiple of it; the backward and the chunk-carry pass work one chunk per wave step.
+constexpr int kChunk = 512;
+
+struct ScanParams {
+    int B, D, N, L, nchunks;
+    int softplus;
+    const void* u;
+    const void* delta;
+    const void* Bm;
+    const void* Cm;
+    const void* z;
+    const float* A;
+    const float* Dv;
+    const float* bias;
+    const float* h0;
+    void* out;
+    float* final_state;
+    float* chunk_states;
+};
+
+struct GradParams {
+    const void* dout;
+    void* du;
+    void* ddelta;
+    void* dz;
+    float* dA;
+    float* dB;
+    float* dC;
+    float* dD;
+    float* dbias;
+    float* dh0;
+};
+
+// All launchers enqueue on `stream` and return the hipGetLastError() after the launch.
+hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_chunk_carry(const ScanParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float* chunk_states,
+                           bool bf16, hipStream_t stream);
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
+
+}  // namespace msel

@@ -1,0 +1,155 @@
+// scan_fwd.hip -- fused forward selective scan for gfx950.
+//
+// One wavefront owns one (batch, channel) recurrence and walks the sequence in tiles of
+// 64*K time steps; lane l holds the K consecutive steps [tile + l*K, tile + (l+1)*K).  The
+// scan is fused in one pass over HBM (page 4, Appendix D, Speed paragraph: memory-bound
+// operations are fused so that u, Delta, B, C, z are read once and only out is written):
+//
+//   per tile: load u, delta (and later z) for the lane's K steps, Delta = softplus(delta+bias),
+//   per state n:
+//     pass 1  a_k = exp2(Delta_k * A'_n)           (A' = A*log2 e: ZOH transition)
+//             b_k = Delta_k u_k * B_{n,k}           (Euler input)
+//             lane-local chain from 0 -> S, and P = exp2(A'_n * sum Delta) (lane transition)
+//     scan    inclusive DPP scan of (P, S) over the 64 lanes, shifted to exclusive, applied to
+//             the state carried from the previous tile -> state entering the lane (page 1:
+//             the recurrence is parallelized with a work-efficient scan)
+//     pass 2  replay the chain from that state, y_k += C_{n,k} h_k
+//   epilogue: y += D u (initialised up front), out = y * silu(z), one store.
+//
+// The state never leaves registers: the carried state of all N states lives in one VGPR
+// (lane n holds h_n), so long sequences are handled by the tile loop with the state carried
+// across tiles (page 4, Appendix D: split the sequence into chunks, continue the scan from the
+// intermediate state).  Lanes at multiples of the chunk length also write the state entering
+// them to chunk_states.
+#include "msel_device.hpp"
+#include "msel_kernels.hpp"
+
+namespace msel {
+
+template <typename T, int K, bool VEC, bool HAS_Z, bool SOFTPLUS>
+__global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ch = blockIdx.x * (blockDim.x >> 6) + wave;  // b * D + d
+    if (ch >= p.B * p.D) return;  // whole wavefront leaves; this kernel has no barriers
+    const int b = ch / p.D;
+    const int d = ch - b * p.D;
+    const int L = p.L;
+    const int N = p.N;
+    const size_t row = static_cast<size_t>(ch) * L;
+    const T* __restrict__ u = static_cast<const T*>(p.u) + row;
+    const T* __restrict__ dl = static_cast<const T*>(p.delta) + row;
+    const T* __restrict__ zr = HAS_Z ? static_cast<const T*>(p.z) + row : nullptr;
+    T* __restrict__ out = static_cast<T*>(p.out) + row;
+    const T* __restrict__ Bb = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
+    const T* __restrict__ Cb = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
+    const float bias = p.bias ? p.bias[d] : 0.0f;
+    const float Dd = p.Dv ? p.Dv[d] : 0.0f;
+    const float* __restrict__ Arow = p.A + static_cast<size_t>(d) * N;
+
+    float carry = 0.0f;  // lane n: state h_n entering the current tile
+    if (p.h0 != nullptr && lane < N) carry = p.h0[static_cast<size_t>(ch) * N + lane];
+
+    constexpr int TILE = 64 * K;
+    for (int tile = 0; tile < L; tile += TILE) {
+        const int t0 = tile + lane * K;
+        float dt[K], du[K], y[K];
+        float sum_dt = 0.0f;
+        {
+            float uu[K], dd[K];
+            load_k<T, K, VEC>(u, t0, L, uu, 0.0f);
+            load_k<T, K, VEC>(dl, t0, L, dd, 0.0f);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const float x = dd[k] + bias;
+                const float v = SOFTPLUS ? softplus_f(x) : x;
+                dt[k] = (t0 + k < L) ? v : 0.0f;  // Delta = 0 past the end: identity step
+                du[k] = dt[k] * uu[k];
+                y[k] = Dd * uu[k];
+                sum_dt += dt[k];
+            }
+        }
+        float* cs_dst = nullptr;  // lanes that start a chunk record the state entering them
+        if (p.chunk_states != nullptr && t0 < L && (t0 % kChunk) == 0)
+            cs_dst = p.chunk_states + (static_cast<size_t>(ch) * p.nchunks + t0 / kChunk) * N;
+
+        for (int n = 0; n < N; ++n) {
+            const float An = Arow[n] * kLog2e;
+            float a[K], bb[K], bc[K];
+            load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, bc);
+            float h = 0.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                a[k] = exp2_hw(dt[k] * An);
+                bb[k] = du[k] * bc[k];
+                h = fmaf(a[k], h, bb[k]);
+            }
+            float P = exp2_hw(An * sum_dt);
+            float S = h;
+            wave_scan_fwd(P, S);
+            float Pex, Sex;
+            wave_shift_fwd(P, S, Pex, Sex);
+            const float cn = readlane(carry, n);
+            const float hin = fmaf(Pex, cn, Sex);
+            carry = writelane(fmaf(readlane(P, 63), cn, readlane(S, 63)), n, carry);
+            if (cs_dst != nullptr) cs_dst[n] = hin;
+
+            load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n) * L, t0, L, bc);
+            h = hin;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                h = fmaf(a[k], h, bb[k]);
+                y[k] = fmaf(bc[k], h, y[k]);
+            }
+        }
+        if constexpr (HAS_Z) {
+            float zz[K];
+            load_k<T, K, VEC>(zr, t0, L, zz, 0.0f);
+#pragma unroll
+            for (int k = 0; k < K; ++k) y[k] *= zz[k] * sigmoid_f(zz[k]);
+        }
+        store_k<T, K, VEC>(out, t0, L, y);
+    }
+    if (p.final_state != nullptr && lane < N)
+        p.final_state[static_cast<size_t>(ch) * N + lane] = carry;
+}
+
+namespace {
+
+constexpr int kFwdWaves = 4;
+
+template <typename T, int K, bool VEC, bool HAS_Z, bool SP>
+hipError_t fwd_go(const ScanParams& p, hipStream_t s) {
+    const int ch = p.B * p.D;
+    dim3 grid((ch + kFwdWaves - 1) / kFwdWaves), block(64 * kFwdWaves);
+    hipLaunchKernelGGL((scan_fwd_kernel<T, K, VEC, HAS_Z, SP>), grid, block, 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T, int K>
+hipError_t fwd_dispatch(const ScanParams& p, hipStream_t s) {
+    const bool vec = (static_cast<size_t>(p.L) * sizeof(T)) % 16 == 0;
+    const bool hz = p.z != nullptr;
+    const bool sp = p.softplus != 0;
+#define MSEL_FWD(V, Z, S) \
+    if (vec == V && hz == Z && sp == S) return fwd_go<T, K, V, Z, S>(p, s);
+    MSEL_FWD(true, true, true)
+    MSEL_FWD(true, true, false)
+    MSEL_FWD(true, false, true)
+    MSEL_FWD(true, false, false)
+    MSEL_FWD(false, true, true)
+    MSEL_FWD(false, true, false)
+    MSEL_FWD(false, false, true)
+    MSEL_FWD(false, false, false)
+#undef MSEL_FWD
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, hipStream_t stream) {
+    if (bf16) return fwd_dispatch<bf16_t, 16>(p, stream);
+    return fwd_dispatch<float, 16>(p, stream);
+}
+
+}  // namespace msel

@@ -1,0 +1,167 @@
+"""Python binding of libmsel.so: the same three entry points, argument marshalling only.
+
+PyTorch supplies device memory and the current HIP stream; every step of the scan runs in the
+library's HIP kernels.  Tensors must already be on the GPU, contiguous, with the layouts of
+include/msel.h:
+
+    u, delta, z, out, dout, du, ddelta, dz : [batch, dim, seqlen]   float32 or bfloat16
+    B, C                                   : [batch, dstate, seqlen] same dtype as u
+    A                                      : [dim, dstate]           float32
+    D, delta_bias                          : [dim]                   float32
+    h0, final_state, dh0                   : [batch, dim, dstate]    float32
+    chunk_states                           : [batch, dim, n_chunks, dstate] float32
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return _lib.MSEL_F32
+    if dt == torch.bfloat16:
+        return _lib.MSEL_BF16
+    raise TypeError(f"activation dtype must be float32 or bfloat16, got {dt}")
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def chunk_len() -> int:
+    return int(_lib.load().msel_chunk_len())
+
+
+def num_chunks(seqlen: int) -> int:
+    return int(_lib.load().msel_num_chunks(int(seqlen)))
+
+
+def _args(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus):
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, dim, seqlen]")
+    bsz, dim, L = u.shape
+    N = A.shape[1] if A.dim() == 2 else -1
+    dev, dt = u.device, u.dtype
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    _need(u, "u", (bsz, dim, L), dt, dev)
+    _need(delta, "delta", (bsz, dim, L), dt, dev)
+    _need(A, "A", (dim, N), torch.float32, dev)
+    _need(B, "B", (bsz, N, L), dt, dev)
+    _need(C, "C", (bsz, N, L), dt, dev)
+    _need(z, "z", (bsz, dim, L), dt, dev)
+    _need(D, "D", (dim,), torch.float32, dev)
+    _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    _need(h0, "h0", (bsz, dim, N), torch.float32, dev)
+    a = _lib.ScanArgs()
+    a.abi_version = _lib.ABI_VERSION
+    a.batch, a.dim, a.dstate, a.seqlen = int(bsz), int(dim), int(N), int(L)
+    a.dtype = _dtype_code(dt)
+    a.delta_softplus = 1 if delta_softplus else 0
+    a.reserved = 0
+    a.u, a.delta, a.B, a.C, a.z = _ptr(u), _ptr(delta), _ptr(B), _ptr(C), _ptr(z)
+    a.A, a.D, a.delta_bias, a.h0 = _ptr(A), _ptr(D), _ptr(delta_bias), _ptr(h0)
+    return a, (bsz, dim, N, L)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def msel_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                  h0=None, return_final_state=True, return_chunk_states=False, out=None,
+                  final_state=None, chunk_states=None):
+    """Fused forward scan.  Returns (out, final_state or None, chunk_states or None)."""
+    a, (bsz, dim, N, L) = _args(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
+    dev = u.device
+    out = torch.empty_like(u) if out is None else _need(out, "out", (bsz, dim, L), u.dtype, dev)
+    if return_final_state and final_state is None:
+        final_state = torch.empty((bsz, dim, N), device=dev, dtype=torch.float32)
+    if return_chunk_states and chunk_states is None:
+        chunk_states = torch.empty((bsz, dim, num_chunks(L), N), device=dev,
+                                   dtype=torch.float32)
+    _need(final_state, "final_state", (bsz, dim, N), torch.float32, dev)
+    _need(chunk_states, "chunk_states", (bsz, dim, num_chunks(L), N), torch.float32, dev)
+    a.out, a.final_state, a.chunk_states = _ptr(out), _ptr(final_state), _ptr(chunk_states)
+    _lib.check("msel_scan_fwd", _lib.load().msel_scan_fwd(ctypes.byref(a), _stream(dev)))
+    return out, final_state, chunk_states
+
+
+def msel_scan_chunk_carry(u, delta, A, B, delta_bias=None, delta_softplus=True, h0=None,
+                          return_final_state=True, chunk_states=None, final_state=None):
+    """Chunk-carry pass.  Returns (chunk_states, final_state or None)."""
+    if u.dim() != 3 or A.dim() != 2:
+        raise ValueError("u must be [batch, dim, seqlen] and A [dim, dstate]")
+    bsz, dim, L = u.shape
+    N = A.shape[1]
+    dev = u.device
+    _need(B, "B", (bsz, N, L), u.dtype, dev)
+    a, _ = _args(u, delta, A, B, B, None, None, delta_bias, h0, delta_softplus)
+    a.C = None
+    if chunk_states is None:
+        chunk_states = torch.empty((bsz, dim, num_chunks(L), N), device=dev,
+                                   dtype=torch.float32)
+    if return_final_state and final_state is None:
+        final_state = torch.empty((bsz, dim, N), device=dev, dtype=torch.float32)
+    _need(chunk_states, "chunk_states", (bsz, dim, num_chunks(L), N), torch.float32, dev)
+    _need(final_state, "final_state", (bsz, dim, N), torch.float32, dev)
+    a.chunk_states, a.final_state = _ptr(chunk_states), _ptr(final_state)
+    _lib.check("msel_scan_chunk_carry",
+               _lib.load().msel_scan_chunk_carry(ctypes.byref(a), _stream(dev)))
+    return chunk_states, final_state
+
+
+def msel_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
+                  delta_softplus=True, h0=None, chunk_states=None, want_dA=True, want_dB=True,
+                  want_dC=True, want_dD=True, want_ddelta_bias=True, want_dh0=False,
+                  workspace=None):
+    """Backward with recomputation.  Returns a dict of gradients (absent ones are None)."""
+    a, (bsz, dim, N, L) = _args(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
+    dev, dt = u.device, u.dtype
+    _need(dout, "dout", (bsz, dim, L), dt, dev)
+    _need(chunk_states, "chunk_states", (bsz, dim, num_chunks(L), N), torch.float32, dev)
+    a.chunk_states = _ptr(chunk_states)
+    f32 = dict(device=dev, dtype=torch.float32)
+    r = {
+        "du": torch.empty_like(u), "ddelta": torch.empty_like(u),
+        "dz": torch.empty_like(u) if z is not None else None,
+        "dA": torch.empty((dim, N), **f32) if want_dA else None,
+        "dB": torch.empty((bsz, N, L), **f32) if want_dB else None,
+        "dC": torch.empty((bsz, N, L), **f32) if want_dC else None,
+        "dD": torch.empty((dim,), **f32) if want_dD else None,
+        "ddelta_bias": torch.empty((dim,), **f32) if want_ddelta_bias else None,
+        "dh0": torch.empty((bsz, dim, N), **f32) if want_dh0 else None,
+    }
+    g = _lib.ScanGrads()
+    g.dout = _ptr(dout)
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        setattr(g, k, _ptr(r[k]))
+    lib = _lib.load()
+    need = int(lib.msel_scan_bwd_workspace_bytes(ctypes.byref(a)))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    ws_ptr = _ptr(workspace) if need > 0 else None
+    ws_bytes = workspace.numel() * workspace.element_size() if need > 0 else 0
+    _lib.check("msel_scan_bwd", lib.msel_scan_bwd(ctypes.byref(a), ctypes.byref(g), ws_ptr,
+                                                  ws_bytes, _stream(dev)))
+    return r

@@ -1,0 +1,108 @@
+"""GPU parity at the full sizes of the five workloads, in the launch configuration the
+benchmark times, checked against the fp64 oracle on outputs it can compute separately:
+
+* channels are independent in the forward, so sampled (batch, channel) rows of out,
+  final_state and chunk_states are recomputed by the oracle on just those rows;
+* per-channel gradients (du, ddelta, dz) are checked on every channel of one batch row;
+* dB and dC sum over all channels of a batch row: the oracle runs that whole row;
+* dA, dD and ddelta_bias sum over batch and time: the oracle runs sampled channels over all
+  batch rows.
+
+Tolerance as in the small tests: 1e-4 (fp32 inputs) or 1e-2 (bf16 inputs) of max|oracle|.
+"""
+import numpy as np
+import pytest
+
+import msel_inputs
+import oracle
+from helpers import assert_close, host, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import selective_state_space_26_amd as msel  # noqa: E402
+
+T = msel.chunk_len()
+
+
+def _sample_channels(w, k, seed):
+    rng = np.random.default_rng(seed)
+    pairs = {(0, 0), (w.batch - 1, w.dim - 1)}
+    while len(pairs) < k:
+        pairs.add((int(rng.integers(w.batch)), int(rng.integers(w.dim))))
+    return sorted(pairs)
+
+
+def _check_fwd_samples(w, t, out, fin, cs, k):
+    for b, d in _sample_channels(w, k, seed=w.seed):
+        s = msel_inputs.channel_slice(t, b, [d])
+        ro, rf, rcs = oracle.fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"],
+                                 s["bias"], s["h0"], chunk_len=T)
+        assert_close(f"out[{b},{d}]", host(out[b, d]), ro[0, 0], w.dtype)
+        assert_close(f"final[{b},{d}]", host(fin[b, d]), rf[0, 0], w.dtype)
+        if cs is not None:
+            assert_close(f"chunk_states[{b},{d}]", host(cs[b, d]), rcs[0, 0], w.dtype)
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_fwd_full_size(wid):
+    w = msel_inputs.WORKLOADS[wid]
+    log(f"fwd full {w}")
+    t = msel_inputs.make_workload(w, with_dout=False)
+    dv = to_device(t)
+    out, fin, cs = msel.msel_scan_fwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"],
+                                      dv["z"], dv["bias"], True, return_chunk_states=True)
+    torch.cuda.synchronize()
+    _check_fwd_samples(w, t, out, fin, cs, k=12 if wid == 3 else 24)
+
+
+@pytest.mark.parametrize("wid", [2, 4])
+def test_bwd_full_size(wid):
+    w = msel_inputs.WORKLOADS[wid]
+    log(f"bwd full {w}")
+    t = msel_inputs.make_workload(w, with_dout=True)
+    dv = to_device(t)
+    g = msel.msel_scan_bwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["dout"], dv["D"],
+                           dv["z"], dv["bias"], True, chunk_states=None)
+    torch.cuda.synchronize()
+    # one whole batch row: dB, dC and every per-channel gradient of that row
+    b = w.batch // 2
+    s = msel_inputs.channel_slice(t, b, np.arange(w.dim))
+    r = oracle.bwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["dout"], s["D"], s["z"],
+                   s["bias"])
+    for k in ("dB", "dC"):
+        assert_close(f"{k}[{b}]", host(g[k][b]), r[k][0], w.dtype)
+    for k in ("du", "ddelta", "dz"):
+        assert_close(f"{k}[{b}]", host(g[k][b]), r[k][0], w.dtype)
+    # sampled channels over every batch row: dA, dD, ddelta_bias
+    ds = sorted({0, w.dim - 1, *np.random.default_rng(w.seed).integers(w.dim, size=6).tolist()})
+    sub = {k: (None if t.get(k) is None else t.values(k)) for k in t}
+    r2 = oracle.bwd(sub["u"][:, ds], sub["delta"][:, ds], t["A"][ds], sub["B"], sub["C"],
+                    sub["dout"][:, ds], t["D"][ds], sub["z"][:, ds], t["bias"][ds])
+    assert_close("dA", host(g["dA"][ds]), r2["dA"], w.dtype)
+    assert_close("dD", host(g["dD"][ds]), r2["dD"], w.dtype)
+    assert_close("ddelta_bias", host(g["ddelta_bias"][ds]), r2["ddelta_bias"], w.dtype)
+
+
+def test_tiny_workload_exact_oracle():
+    """The tiny workload in full, forward and backward."""
+    w = msel_inputs.WORKLOADS[0]
+    log(f"tiny full {w}")
+    t = msel_inputs.make_workload(w, with_dout=True)
+    dv = to_device(t)
+    out, fin, cs = msel.msel_scan_fwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"],
+                                      dv["z"], dv["bias"], True, return_chunk_states=True)
+    g = msel.msel_scan_bwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["dout"], dv["D"],
+                           dv["z"], dv["bias"], True)
+    torch.cuda.synchronize()
+    v = {k: t.values(k) for k in t}
+    ro, rf = oracle.fwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"], v["bias"])
+    assert_close("out", host(out), ro, "f32")
+    assert_close("final", host(fin), rf, "f32")
+    r = oracle.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
+                   v["bias"])
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias"):
+        assert_close(k, host(g[k]), r[k], "f32")

@@ -1,0 +1,231 @@
+"""GPU parity of the HIP path against the fp64 oracle on small seeded problems.
+
+Shapes span several tiles and chunks with ragged tails, both dtypes, with and without the gate,
+softplus, D, bias and h0, and the degenerate sizes (seqlen 1, dstate 1, one channel).  The bar
+is max|gpu - oracle| <= tol * max|oracle| per output tensor: tol = 1e-4 for fp32 inputs and
+1e-2 for bf16 inputs (fp32 state and accumulation), on the same seeded inputs.
+"""
+import numpy as np
+import pytest
+
+import msel_inputs
+import oracle
+from helpers import assert_close, host, log, oracle_vals, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import selective_state_space_26_amd as msel  # noqa: E402
+
+T = msel.chunk_len()
+
+FWD_CASES = [
+    # batch, dim, dstate, seqlen, dtype, z, softplus, D/bias, h0
+    (1, 4, 4, 64, "f32", True, True, True, False),       # the tiny workload
+    (2, 5, 16, 2500, "f32", True, True, True, True),     # 3 tiles, ragged tail
+    (2, 5, 16, 2500, "bf16", True, True, True, True),    # unaligned bf16 rows
+    (2, 3, 16, 4096, "bf16", False, True, True, False),  # aligned, whole tiles
+    (3, 7, 5, 1000, "f32", False, False, False, True),   # odd dstate, no softplus/D/bias
+    (1, 2, 16, 1, "f32", True, True, True, True),        # single step
+    (1, 1, 1, 777, "bf16", True, True, True, False),     # dstate 1, one channel
+    (2, 9, 16, 520, "f32", True, True, True, False),     # one chunk + 8 steps
+    (1, 3, 8, 3 * 512, "bf16", True, False, True, True), # exact chunk multiple
+]
+
+
+def _case_inputs(bsz, dim, N, L, dtype, with_z, sp, with_db, with_h0, seed=123, dout=False):
+    t = msel_inputs.make(bsz, dim, N, L, dtype, seed, with_z=with_z, with_D=with_db,
+                         with_bias=with_db, with_h0=with_h0, with_dout=dout)
+    if not sp:
+        # without softplus keep Delta = delta + bias positive and small, as a learned step is
+        v = np.abs(t.values("delta")) * np.float32(0.2)
+        t["delta"] = msel_inputs.f32_to_bf16_bits(v) if dtype == "bf16" else v
+        if t.get("bias") is not None:
+            t["bias"] = (np.abs(t["bias"]) * np.float32(0.01)).astype(np.float32)
+    return t
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: "x".join(map(str, c[:5])))
+def test_fwd_matches_oracle(case):
+    bsz, dim, N, L, dtype, with_z, sp, with_db, with_h0 = case
+    log(f"fwd {case}")
+    t = _case_inputs(*case)
+    dv = to_device(t)
+    out, fin, cs = msel.msel_scan_fwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"],
+                                      dv["z"], dv["bias"], sp, dv["h0"],
+                                      return_chunk_states=True)
+    torch.cuda.synchronize()
+    v = oracle_vals(t)
+    ro, rf, rcs = oracle.fwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"],
+                             v["bias"], v["h0"], softplus=sp, chunk_len=T)
+    assert_close("out", host(out), ro, dtype)
+    assert_close("final_state", host(fin), rf, dtype)
+    assert_close("chunk_states", host(cs), rcs, dtype)
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: "x".join(map(str, c[:5])))
+def test_chunk_carry_matches_oracle(case):
+    bsz, dim, N, L, dtype, with_z, sp, with_db, with_h0 = case
+    log(f"chunk_carry {case}")
+    t = _case_inputs(*case)
+    dv = to_device(t)
+    cs, fin = msel.msel_scan_chunk_carry(dv["u"], dv["delta"], dv["A"], dv["B"], dv["bias"], sp,
+                                         dv["h0"])
+    torch.cuda.synchronize()
+    v = oracle_vals(t)
+    rcs, rf = oracle.chunk_states_formula(v["u"], v["delta"], v["A"], v["B"], T, h0=v["h0"],
+                                          bias=v["bias"], softplus=sp)
+    assert_close("chunk_states", host(cs), rcs, dtype)
+    assert_close("final_state", host(fin), rf, dtype)
+
+
+BWD_CASES = [
+    (1, 4, 4, 64, "f32", True, True, True, True),
+    (2, 6, 16, 1100, "f32", True, True, True, True),
+    (2, 6, 16, 1100, "bf16", True, True, True, True),
+    (2, 5, 16, 2048, "bf16", False, True, True, False),
+    (3, 3, 7, 700, "f32", False, False, False, True),
+    (1, 3, 16, 1, "f32", True, True, True, True),
+    (2, 9, 16, 1536, "f32", True, True, True, False),   # dim not a multiple of the workgroup
+]
+
+
+@pytest.mark.parametrize("given_states", [False, True])
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "x".join(map(str, c[:5])))
+def test_bwd_matches_oracle(case, given_states):
+    bsz, dim, N, L, dtype, with_z, sp, with_db, with_h0 = case
+    log(f"bwd {case} given_states={given_states}")
+    t = _case_inputs(*case, dout=True)
+    dv = to_device(t)
+    cs = None
+    if given_states:
+        _, _, cs = msel.msel_scan_fwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"],
+                                      dv["z"], dv["bias"], sp, dv["h0"],
+                                      return_final_state=False, return_chunk_states=True)
+    g = msel.msel_scan_bwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["dout"], dv["D"],
+                           dv["z"], dv["bias"], sp, dv["h0"], chunk_states=cs, want_dh0=True)
+    torch.cuda.synchronize()
+    v = oracle_vals(t)
+    r = oracle.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
+                   v["bias"], v["h0"], softplus=sp)
+    names = ["du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"]
+    if with_z:
+        names.append("dz")
+    for k in names:
+        assert_close(k, host(g[k]), r[k], dtype)
+    if not with_z:
+        assert g["dz"] is None
+
+
+def test_fwd_is_deterministic():
+    log("fwd determinism")
+    t = _case_inputs(2, 5, 16, 2500, "bf16", True, True, True, True)
+    dv = to_device(t)
+    a = msel.msel_scan_fwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"], dv["z"],
+                           dv["bias"], True, dv["h0"], return_chunk_states=True)
+    b = msel.msel_scan_fwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"], dv["z"],
+                           dv["bias"], True, dv["h0"], return_chunk_states=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_delta_zero_gives_exact_skip(dtype):
+    """softplus off, delta = bias = 0: a = 1, dB x = 0, so out = D*u exactly and h stays 0."""
+    log(f"delta=0 {dtype}")
+    t = msel_inputs.make(2, 6, 16, 1300, dtype, 5, with_z=False, with_bias=False)
+    dv = to_device(t)
+    dv["delta"] = torch.zeros_like(dv["delta"])
+    out, fin, _ = msel.msel_scan_fwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"],
+                                     None, None, False)
+    torch.cuda.synchronize()
+    ref = (dv["D"][None, :, None] * dv["u"].float()).to(dv["u"].dtype)
+    assert torch.equal(out, ref)
+    assert torch.count_nonzero(fin).item() == 0
+
+
+def test_state_reset_is_bitwise():
+    """A step with Delta*A <= -750 zeroes exp(Delta A) in fp32: later outputs forget u before it."""
+    log("state reset")
+    L, t0 = 2300, 1111
+    t = msel_inputs.make(1, 4, 16, L, "f32", 6, with_bias=False)
+    dv = to_device(t)
+    delta = dv["delta"].abs() * 0.2
+    delta[:, :, t0] = 750.0
+    args = (delta, dv["A"], dv["B"], dv["C"], dv["D"], dv["z"], None, False)
+    o1, f1, _ = msel.msel_scan_fwd(dv["u"], *args)
+    u2 = dv["u"].clone()
+    u2[:, :, :t0] += torch.randn_like(u2[:, :, :t0])
+    o2, f2, _ = msel.msel_scan_fwd(u2, *args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :, t0:], o2[:, :, t0:])
+    assert torch.equal(f1, f2)
+    assert not torch.equal(o1[:, :, :t0], o2[:, :, :t0])
+
+
+def test_causality_is_bitwise():
+    log("causality")
+    L, t1 = 3000, 1500
+    t = msel_inputs.make(2, 3, 16, L, "bf16", 8)
+    dv = to_device(t)
+    args = (dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"], dv["z"], dv["bias"], True)
+    o1, _, _ = msel.msel_scan_fwd(dv["u"], *args)
+    u2 = dv["u"].clone()
+    u2[:, :, t1 + 1:] = 1.0
+    o2, _, _ = msel.msel_scan_fwd(u2, *args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :, :t1 + 1], o2[:, :, :t1 + 1])
+
+
+def test_resume_from_final_state():
+    """Two calls chained through h0 = final_state equal one call over the whole sequence."""
+    log("resume")
+    L, L1 = 3000, 1234
+    t = msel_inputs.make(2, 4, 16, L, "f32", 9)
+    dv = to_device(t)
+    full, fin, _ = msel.msel_scan_fwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"],
+                                      dv["z"], dv["bias"], True)
+    s1, s2 = slice(0, L1), slice(L1, L)
+    part = lambda x, s: x[:, :, s].contiguous()
+    o1, f1, _ = msel.msel_scan_fwd(*(part(dv[k], s1) for k in ("u", "delta")), dv["A"],
+                                   *(part(dv[k], s1) for k in ("B", "C")), dv["D"],
+                                   part(dv["z"], s1), dv["bias"], True)
+    o2, f2, _ = msel.msel_scan_fwd(*(part(dv[k], s2) for k in ("u", "delta")), dv["A"],
+                                   *(part(dv[k], s2) for k in ("B", "C")), dv["D"],
+                                   part(dv["z"], s2), dv["bias"], True, f1)
+    torch.cuda.synchronize()
+    assert_close("resumed out", host(torch.cat([o1, o2], 2)), host(full), "f32")
+    assert_close("resumed final", host(f2), host(fin), "f32")
+
+
+def test_fwd_chunk_states_agree_with_chunk_carry():
+    log("fwd chunk states vs chunk carry")
+    t = msel_inputs.make(2, 5, 16, 5000, "bf16", 10, with_h0=True)
+    dv = to_device(t)
+    _, fin, cs = msel.msel_scan_fwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"],
+                                    dv["z"], dv["bias"], True, dv["h0"],
+                                    return_chunk_states=True)
+    cs2, fin2 = msel.msel_scan_chunk_carry(dv["u"], dv["delta"], dv["A"], dv["B"], dv["bias"],
+                                           True, dv["h0"])
+    torch.cuda.synchronize()
+    assert_close("chunk_states", host(cs2), host(cs), "f32")
+    assert_close("final", host(fin2), host(fin), "f32")
+
+
+def test_binding_rejects_bad_inputs_before_launch():
+    log("binding checks")
+    x = torch.zeros(1, 2, 8, device="cuda")
+    A = torch.zeros(2, 4, device="cuda")
+    Bm = torch.zeros(1, 4, 8, device="cuda")
+    with pytest.raises(ValueError):
+        msel.msel_scan_fwd(x, x, A, Bm, Bm[:, :, :4])
+    with pytest.raises(TypeError):
+        msel.msel_scan_fwd(x.half(), x.half(), A, Bm.half(), Bm.half())
+    with pytest.raises(Exception):
+        msel.msel_scan_fwd(x, x, torch.zeros(2, 17, device="cuda"),
+                           torch.zeros(1, 17, 8, device="cuda"),
+                           torch.zeros(1, 17, 8, device="cuda"))
