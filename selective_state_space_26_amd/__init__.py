@@ -5,7 +5,8 @@
 The kernels live in ``csrc/``; ``build.py`` compiles them in-tree.  Importing this package does
 not load the library; the first call does, and raises if it is not built.
 """
-from .scan import (chunk_len, msel_scan_bwd, msel_scan_chunk_carry, msel_scan_fwd,  # noqa: F401
-                   num_chunks)
+from .scan import (bwd_workspace_bytes, chunk_len, msel_scan_bwd,  # noqa: F401
+                   msel_scan_chunk_carry, msel_scan_fwd, num_chunks)
 
-__all__ = ["msel_scan_fwd", "msel_scan_bwd", "msel_scan_chunk_carry", "chunk_len", "num_chunks"]
+__all__ = ["msel_scan_fwd", "msel_scan_bwd", "msel_scan_chunk_carry", "chunk_len", "num_chunks",
+           "bwd_workspace_bytes"]

@@ -64,9 +64,9 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
             for (int k = 0; k < K; ++k) h = fmaf(exp2_hw(dt[k] * An), h, du[k] * bc[k]);
             float P = exp2_hw(An * sum_dt);
             float S = h;
-            wave_scan_fwd(P, S);
+            scan_fwd_fused(P, S);
             const float cn = readlane(carry, n);
-            carry = writelane(fmaf(readlane(P, 63), cn, readlane(S, 63)), n, carry);
+            carry = writelane(readlane(fmaf(P, cn, S), 63), n, carry);
         }
     }
     if (p.final_state != nullptr && lane < N)

@@ -68,11 +68,6 @@ msel::ScanParams to_params(const msel_scan_args* a) {
     return p;
 }
 
-size_t chunk_state_bytes(const msel_scan_args* a) {
-    return static_cast<size_t>(a->batch) * a->dim * msel_num_chunks(a->seqlen) * a->dstate *
-           sizeof(float);
-}
-
 msel_status hip_status(hipError_t e) { return e == hipSuccess ? MSEL_OK : MSEL_ERR_HIP; }
 
 }  // namespace
@@ -126,8 +121,8 @@ msel_status msel_validate_chunk_carry(const msel_scan_args* a) {
 
 size_t msel_scan_bwd_workspace_bytes(const msel_scan_args* a) {
     if (check_common(a) != MSEL_OK) return 0;
-    if (a->chunk_states != nullptr) return 0;
-    return chunk_state_bytes(a);
+    return msel::bwd_workspace_bytes(a->batch, a->dim, a->dstate, a->seqlen,
+                                     a->chunk_states == nullptr);
 }
 
 msel_status msel_validate_bwd(const msel_scan_args* a, const msel_scan_grads* g,
@@ -150,13 +145,12 @@ msel_status msel_validate_bwd(const msel_scan_args* a, const msel_scan_grads* g,
         if (same_as_input(a, o) || (o != nullptr && (o == g->dout || o == a->chunk_states)))
             return MSEL_ERR_ALIAS;
     const size_t need = msel_scan_bwd_workspace_bytes(a);
-    if (need > 0) {
-        if (workspace == nullptr || workspace_bytes < need) return MSEL_ERR_WORKSPACE;
-        if (!aligned(workspace, 16)) return MSEL_ERR_ALIGN;
-        if (same_as_input(a, workspace) || workspace == g->dout) return MSEL_ERR_ALIAS;
-        for (const void* o : outs)
-            if (o != nullptr && o == workspace) return MSEL_ERR_ALIAS;
-    }
+    if (workspace == nullptr || workspace_bytes < need) return MSEL_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MSEL_ERR_ALIGN;
+    if (same_as_input(a, workspace) || workspace == g->dout || workspace == a->chunk_states)
+        return MSEL_ERR_ALIAS;
+    for (const void* o : outs)
+        if (o != nullptr && o == workspace) return MSEL_ERR_ALIAS;
     return MSEL_OK;
 }
 
@@ -178,15 +172,6 @@ msel_status msel_scan_bwd(const msel_scan_args* a, const msel_scan_grads* g, voi
     if (s != MSEL_OK) return s;
     const bool bf16 = a->dtype == MSEL_BF16;
     msel::ScanParams p = to_params(a);
-    const float* cst = a->chunk_states;
-    if (cst == nullptr) {
-        msel::ScanParams pc = p;
-        pc.chunk_states = static_cast<float*>(workspace);
-        pc.final_state = nullptr;
-        hipError_t e = msel::launch_chunk_carry(pc, bf16, stream);
-        if (e != hipSuccess) return MSEL_ERR_HIP;
-        cst = pc.chunk_states;
-    }
     const size_t DN = static_cast<size_t>(a->dim) * a->dstate;
     const size_t BNL = static_cast<size_t>(a->batch) * a->dstate * a->seqlen;
     hipError_t e = hipSuccess;
@@ -207,7 +192,7 @@ msel_status msel_scan_bwd(const msel_scan_args* a, const msel_scan_grads* g, voi
     gp.dD = g->dD;
     gp.dbias = g->ddelta_bias;
     gp.dh0 = g->dh0;
-    return hip_status(msel::launch_scan_bwd(p, gp, cst, bf16, stream));
+    return hip_status(msel::launch_scan_bwd(p, gp, a->chunk_states, workspace, bf16, stream));
 }
 
 }  // extern "C"

@@ -279,4 +279,96 @@ __device__ __forceinline__ float wave_sum(float v) {
     return readlane(v, 63);
 }
 
+
+// ---------------------------------------------------------------------------------------
+// Scans with the DPP move fused into the arithmetic.  With bound_ctrl off, a lane whose DPP
+// source does not exist (or whose row is masked off) is not written at all, which is exactly
+// the identity element of the affine composition, so no identity values have to be set up:
+//   v_fmac_f32_dpp S, S, P  ->  S_l = S_{src} * P_l + S_l
+//   v_mul_f32_dpp  P, P, P  ->  P_l = P_{src} * P_l
+// (the fmac reads P before the mul overwrites it).  GFX9 needs two wait states between a VALU
+// write of a VGPR and a DPP read of it; the s_nop after every level (and before the first)
+// provides them.
+
+#define MSEL_FWD_LEVEL(CTRL, RMASK)                                              \
+    "v_fmac_f32_dpp %[S], %[S], %[P] " CTRL " row_mask:" RMASK " bank_mask:0xf\n" \
+    "v_mul_f32_dpp %[P], %[P], %[P] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"  \
+    "s_nop 1\n"
+
+// Inclusive forward scan over the 64 lanes of a wave (lane 0 first in time).
+__device__ __forceinline__ void scan_fwd_fused(float& P, float& S) {
+    asm volatile("s_nop 1\n"
+                 MSEL_FWD_LEVEL("row_shr:1", "0xf")
+                 MSEL_FWD_LEVEL("row_shr:2", "0xf")
+                 MSEL_FWD_LEVEL("row_shr:4", "0xf")
+                 MSEL_FWD_LEVEL("row_shr:8", "0xf")
+                 MSEL_FWD_LEVEL("row_bcast:15", "0xa")
+                 MSEL_FWD_LEVEL("row_bcast:31", "0xc")
+                 : [P] "+v"(P), [S] "+v"(S));
+}
+
+// Inclusive suffix scan over the 64 lanes (lane 63 last in time): the row levels are fused
+// DPP row_shl; the two cross-row levels use ds_swizzle and readlane.
+__device__ __forceinline__ void scan_rev_fused(float& P, float& S) {
+    asm volatile("s_nop 1\n"
+                 MSEL_FWD_LEVEL("row_shl:1", "0xf")
+                 MSEL_FWD_LEVEL("row_shl:2", "0xf")
+                 MSEL_FWD_LEVEL("row_shl:4", "0xf")
+                 MSEL_FWD_LEVEL("row_shl:8", "0xf")
+                 : [P] "+v"(P), [S] "+v"(S));
+    const int lane = lane_id();
+    {
+        constexpr int pat = (0x10 << 5);  // every lane of a 32-lane half reads its lane 16
+        const float Pp = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, P), pat));
+        const float Sp = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, S), pat));
+        const bool take = (lane & 16) == 0;
+        S = take ? fmaf(P, Sp, S) : S;
+        P = take ? P * Pp : P;
+    }
+    {
+        const float Pp = readlane(P, 32);
+        const float Sp = readlane(S, 32);
+        const bool take = lane < 32;
+        S = take ? fmaf(P, Sp, S) : S;
+        P = take ? P * Pp : P;
+    }
+}
+
+// Lane l gets v of lane l-1; lane 0 gets `first`.
+__device__ __forceinline__ float shift_up(float v, float first) {
+    float r = first;
+    asm volatile("s_nop 1\n"
+                 "v_mov_b32_dpp %[r], %[v] wave_shr:1 row_mask:0xf bank_mask:0xf\n"
+                 : [r] "+v"(r) : [v] "v"(v));
+    return r;
+}
+
+// Lane l gets v of lane l+1; lane 63 gets `last`.
+__device__ __forceinline__ float shift_down(float v, float last) {
+    float r = last;
+    asm volatile("s_nop 1\n"
+                 "v_mov_b32_dpp %[r], %[v] wave_shl:1 row_mask:0xf bank_mask:0xf\n"
+                 : [r] "+v"(r) : [v] "v"(v));
+    return r;
+}
+
+// Sum over the 64 lanes with fused DPP adds; the total is returned in every lane.
+__device__ __forceinline__ float wave_sum_fused(float v) {
+    asm volatile("s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_shr:1 row_mask:0xf bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_shr:2 row_mask:0xf bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_shr:4 row_mask:0xf bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_shr:8 row_mask:0xf bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_bcast:15 row_mask:0xa bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_bcast:31 row_mask:0xc bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 : [v] "+v"(v));
+    return readlane(v, 63);
+}
+
 }  // namespace msel

@@ -44,8 +44,11 @@ struct GradParams {
 // All launchers enqueue on `stream` and return the hipGetLastError() after the launch.
 hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_chunk_carry(const ScanParams& p, bool bf16, hipStream_t stream);
+// Backward: the summary/link passes write into `workspace` (bwd_workspace_bytes), then the
+// chunk-parallel main kernel.  chunk_states may be NULL (rebuilt in the workspace).
+size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states);
 hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float* chunk_states,
-                           bool bf16, hipStream_t stream);
+                           void* workspace, bool bf16, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
 
 }  // namespace msel

@@ -1,12 +1,11 @@
 // scan_bwd.hip -- backward selective scan with recomputation, for gfx950.
 //
 // Page 1 and page 4 (Appendix D, Memory paragraph): the intermediate states are not stored
-// but recomputed in the backward pass when the inputs are loaded from HBM into on-chip
-// memory.  Only the chunk-boundary states H_c (one per kChunk steps, from the forward or the
-// chunk-carry pass) are read; inside a chunk the states are rebuilt in registers.
+// but recomputed in the backward pass from the inputs loaded from HBM.  Only one state per
+// chunk of kChunk steps exists outside the chip.
 //
-// Gradients of a loss with respect to the inputs, given dout (a = exp(Delta A), p = Delta B u,
-// y = C.h + D u before the gate, s = sigmoid(z)):
+// Gradients of a loss with respect to the inputs, given dout (a = exp(Delta A), y = C.h + D u
+// before the gate, s = sigmoid(z)):
 //   dy_t  = dout_t * z s                 dz_t = dout_t * y_t * s (1 + z (1 - s))
 //   lam_t = C_t dy_t + a_{t+1} lam_{t+1} (adjoint of h_t, zero beyond the last step)
 //   dC_t += dy_t h_t      dB_t += lam_t Delta_t u_t      (summed over channels)
@@ -15,88 +14,222 @@
 //   ddelta_t = dDelta_t * sigmoid(delta_t + bias) with the softplus, dbias += ddelta_t
 //   dD += dy_t u_t       dh0 = a_0 lam_0
 //
-// Layout: a workgroup holds kBwdWaves wavefronts, one per channel of the same batch row, and
-// walks the chunks from last to first.  Lane l covers steps [c*T + l*K, c*T + (l+1)*K).  Per
-// state n: forward pass 1 + DPP scan + pass 2 rebuilds h_t from H_c; the adjoint runs the same
-// way in reverse (lane-local chain, DPP suffix scan, replay) starting from the carry of the
-// chunk after it.  dB and dC are summed over the workgroup's channels with LDS atomics into a
-// double-buffered [K][64] tile (one buffer per state, alternating), then flushed to HBM with
-// fp32 global atomics.  dA partials stay lane-private in LDS until the end.
+// Three launches, all parallel over chunks:
+//  1. summary: one wavefront per (batch, channel, chunk).  For every state n it forms the
+//     chunk's local end state from a zero start (forward) and the adjoint at the chunk's
+//     first step from a zero adjoint beyond the chunk (reverse), both with the lane-local
+//     chains + DPP scans used by the forward kernel, plus sum(Delta) and Delta at the first
+//     step.
+//  2. link: one thread per (batch, channel, state) walks the chunks:
+//       H_{c+1} = exp(A sum Delta_c) H_c + S_c                      (H_0 = h0)
+//       G_{c-1} = exp(A sum Delta_c) G_c + exp(A Delta_first_c) Sr_c (G_last = 0)
+//     H_c is the state entering chunk c, G_c = a lam at the first step after chunk c; the
+//     walk ends with G = a_0 lam_0 = dh0.  (This is the chunk carry of page 4, Appendix D,
+//     run once forward for the states and once backward for the adjoint.)
+//  3. main: one workgroup per (batch, chunk, group of channels).  Each wavefront takes one
+//     channel at a time: the states inside the chunk are rebuilt from H_c, the adjoint from
+//     G_c, and every gradient term is formed in registers.  dB and dC, which sum over
+//     channels, are accumulated over all the group's channels in LDS and written to HBM once
+//     per workgroup with fp32 global atomics.  LDS float atomics are avoided (they run at a
+//     small fraction of the plain LDS rate on this chip): the wavefronts visit the states in
+//     rotated order, one state per wavefront per step, so each accumulator slot has one
+//     writer per step and a plain read-add-write suffices.
 #include "msel_device.hpp"
 #include "msel_kernels.hpp"
 
 namespace msel {
 
-constexpr int kBwdWaves = 4;
 constexpr int kMaxN = 16;
+constexpr int kSumWaves = 4;
+constexpr int kMainWaves = 8;
+
+struct BwdWork {
+    float* H;       // [B*D*nch*N]: chunk-start states (may be the caller's chunk_states)
+    float* G;       // [B*D*nch*N]: adjoint carry after each chunk
+    float* sdt;     // [B*D*nch]: sum of Delta over the chunk
+    float* dfirst;  // [B*D*nch]: Delta at the chunk's first step
+    int want_fwd;   // the summary/link passes also build H
+};
+
+template <typename T, bool VEC, bool HAS_Z, bool SOFTPLUS, bool FWD>
+__global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams p, GradParams g,
+                                                                     BwdWork w) {
+    constexpr int K = kChunk / 64;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nch = p.nchunks;
+    const int idx = blockIdx.x * kSumWaves + wave;  // (b*D + d) * nch + c
+    if (idx >= p.B * p.D * nch) return;
+    const int ch = idx / nch;
+    const int c = idx - ch * nch;
+    const int b = ch / p.D;
+    const int d = ch - b * p.D;
+    const int L = p.L;
+    const int N = p.N;
+    const size_t row = static_cast<size_t>(ch) * L;
+    const T* __restrict__ dl = static_cast<const T*>(p.delta) + row;
+    const T* __restrict__ go = static_cast<const T*>(g.dout) + row;
+    const T* __restrict__ Bb = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
+    const T* __restrict__ Cb = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
+    const float bias = p.bias ? p.bias[d] : 0.0f;
+    const float* __restrict__ Arow = p.A + static_cast<size_t>(d) * N;
+    const int t0 = c * kChunk + lane * K;
+
+    float dt[K], dy[K], du[K];
+    float sum_dt = 0.0f;
+    {
+        float dd[K], gg[K];
+        load_k<T, K, VEC>(dl, t0, L, dd, 0.0f);
+        load_k<T, K, VEC>(go, t0, L, gg, 0.0f);
+        float zz[HAS_Z ? K : 1], uu[FWD ? K : 1];
+        if constexpr (HAS_Z) load_k<T, K, VEC>(static_cast<const T*>(p.z) + row, t0, L, zz, 0.0f);
+        if constexpr (FWD) load_k<T, K, VEC>(static_cast<const T*>(p.u) + row, t0, L, uu, 0.0f);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float x = dd[k] + bias;
+            const float v = SOFTPLUS ? softplus_f(x) : x;
+            dt[k] = (t0 + k < L) ? v : 0.0f;
+            sum_dt += dt[k];
+            if constexpr (HAS_Z) dy[k] = gg[k] * zz[k] * sigmoid_f(zz[k]);
+            else dy[k] = gg[k];
+            if constexpr (FWD) du[k] = dt[k] * uu[k];
+        }
+    }
+    const float dt_next = shift_down(dt[0], 0.0f);
+    const float chunk_dt = wave_sum_fused(sum_dt);
+    if (lane == 0) {
+        w.sdt[idx] = chunk_dt;
+        w.dfirst[idx] = dt[0];
+    }
+    for (int n = 0; n < N; ++n) {
+        const float An2 = Arow[n] * kLog2e;
+        float a[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) a[k] = exp2_hw(dt[k] * An2);
+        if constexpr (FWD) {
+            float bv[K];
+            load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, bv);
+            float h = 0.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k) h = fmaf(a[k], h, du[k] * bv[k]);
+            float P = exp2_hw(An2 * sum_dt);
+            float S = h;
+            scan_fwd_fused(P, S);
+            if (lane == 63) w.H[static_cast<size_t>(idx) * N + n] = S;
+        }
+        float cv[K];
+        load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n) * L, t0, L, cv);
+        const float a_next = shift_down(a[0], 1.0f);
+        float r = 0.0f;
+#pragma unroll
+        for (int k = K - 1; k >= 0; --k) {
+            const float e = (k == K - 1) ? a_next : a[k + 1];
+            r = fmaf(e, r, cv[k] * dy[k]);
+        }
+        float Pr = exp2_hw(An2 * (sum_dt - dt[0] + dt_next));
+        float Sr = r;
+        scan_rev_fused(Pr, Sr);
+        if (lane == 0) w.G[static_cast<size_t>(idx) * N + n] = Sr;
+    }
+}
+
+template <bool FWD>
+__global__ __launch_bounds__(256) void bwd_link_kernel(ScanParams p, GradParams g, BwdWork w) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int N = p.N;
+    if (i >= p.B * p.D * N) return;
+    const int ch = i / N;
+    const int n = i - ch * N;
+    const int d = ch % p.D;
+    const int nch = p.nchunks;
+    const float A2 = p.A[static_cast<size_t>(d) * N + n] * kLog2e;
+    const size_t base = static_cast<size_t>(ch) * nch;
+    if (FWD) {
+        float H = p.h0 ? p.h0[static_cast<size_t>(ch) * N + n] : 0.0f;
+        for (int c = 0; c < nch; ++c) {
+            float* slot = w.H + (base + c) * N + n;
+            const float S = *slot;
+            *slot = H;
+            H = fmaf(exp2_hw(A2 * w.sdt[base + c]), H, S);
+        }
+    }
+    float G = 0.0f;
+    for (int c = nch - 1; c >= 0; --c) {
+        float* slot = w.G + (base + c) * N + n;
+        const float Sr = *slot;
+        *slot = G;
+        G = fmaf(exp2_hw(A2 * w.sdt[base + c]), G, exp2_hw(A2 * w.dfirst[base + c]) * Sr);
+    }
+    if (g.dh0 != nullptr) g.dh0[static_cast<size_t>(ch) * N + n] = G;
+}
+
+// LDS accumulator layout of the main kernel: [group][n][k][65] floats per tensor, where the
+// padded stride 65 keeps both the per-lane updates (consecutive lanes) and the flush
+// (consecutive time steps) free of bank conflicts.
+constexpr int kAccKP = 65;
+
+__host__ __device__ constexpr int acc_groups(int N, int W) { return (W + N - 1) / N; }
 
 template <typename T, bool VEC, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(64 * kBwdWaves) void scan_bwd_kernel(ScanParams p, GradParams g,
-                                                                   const float* __restrict__ cst) {
+__global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p, GradParams g,
+                                                                   BwdWork w, int per_wave) {
     constexpr int K = kChunk / 64;
-    constexpr int W = kBwdWaves;
-    constexpr int KP = 65;      // padded lane stride of the [K][64] accumulator tile
-    constexpr int ACC = K * KP;
-    __shared__ float accB[2][ACC];
-    __shared__ float accC[2][ACC];
-    __shared__ float accA[W][kMaxN][64];
+    constexpr int W = kMainWaves;
+    constexpr int KP = kAccKP;
+    extern __shared__ float acc[];  // [2 tensors][groups][N][K][KP]
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int b = blockIdx.y;
-    const int d_raw = blockIdx.x * W + wave;
-    const bool active = d_raw < p.D;
-    const int d = active ? d_raw : 0;
+    const int b = blockIdx.z;
+    const int c = blockIdx.y;
     const int N = p.N;
     const int L = p.L;
     const int nch = p.nchunks;
+    const int groups = acc_groups(N, W);
+    const int tile = N * K * KP;             // floats per (tensor, group)
+    float* accB = acc;
+    float* accC = acc + groups * tile;
+    for (int i = tid; i < 2 * groups * tile; i += 64 * W) acc[i] = 0.0f;
 
-    for (int i = tid; i < 2 * ACC; i += 64 * W) {
-        (&accB[0][0])[i] = 0.0f;
-        (&accC[0][0])[i] = 0.0f;
-    }
-    for (int i = tid; i < W * kMaxN * 64; i += 64 * W) (&accA[0][0][0])[i] = 0.0f;
-    __syncthreads();
+    // Wave w updates state (j + w) mod N of its group's tiles at step j, so within a step
+    // every accumulator slot has a single writer; the barrier at the top of each step orders
+    // the read-add-writes of consecutive steps.
+    const int grp = wave / N;
+    const int rot = wave - grp * N;
+    float* myB = accB + grp * tile;
+    float* myC = accC + grp * tile;
 
-    const size_t ch = static_cast<size_t>(b) * p.D + d;
-    const size_t row = ch * L;
-    const T* __restrict__ u = static_cast<const T*>(p.u) + row;
-    const T* __restrict__ dl = static_cast<const T*>(p.delta) + row;
-    const T* __restrict__ zr = HAS_Z ? static_cast<const T*>(p.z) + row : nullptr;
-    const T* __restrict__ go = static_cast<const T*>(g.dout) + row;
-    T* __restrict__ du_o = static_cast<T*>(g.du) + row;
-    T* __restrict__ dd_o = static_cast<T*>(g.ddelta) + row;
-    T* __restrict__ dz_o = HAS_Z ? static_cast<T*>(g.dz) + row : nullptr;
+    const int t0 = c * kChunk + lane * K;
     const T* __restrict__ Bb = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
     const T* __restrict__ Cb = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
-    const float bias = p.bias ? p.bias[d] : 0.0f;
-    const float Dd = p.Dv ? p.Dv[d] : 0.0f;
-    const float* __restrict__ Arow = p.A + static_cast<size_t>(d) * N;
-    const float* __restrict__ Hrow = cst + ch * nch * N;
 
-    float G = 0.0f;  // lane n: a_t lam_t at the first step of the chunk after the current one
-    float dD_acc = 0.0f, dbias_acc = 0.0f;
-    int it = 0;      // running (chunk, state) counter: selects the accumulator buffer
+    for (int r = 0; r < per_wave; ++r) {
+        const int d = (blockIdx.x * per_wave + r) * W + wave;
+        const bool active = d < p.D;  // wave-uniform; inactive waves still join the barriers
+        const size_t ch = static_cast<size_t>(b) * p.D + (active ? d : 0);
+        const size_t row = ch * L;
+        const float bias = (active && p.bias) ? p.bias[d] : 0.0f;
+        const float Dd = (active && p.Dv) ? p.Dv[d] : 0.0f;
+        const float* __restrict__ Arow = p.A + static_cast<size_t>(active ? d : 0) * N;
+        const float* __restrict__ Hc = w.H + (ch * nch + c) * N;
+        const float* __restrict__ Gc = w.G + (ch * nch + c) * N;
 
-    for (int c = nch - 1; c >= 0; --c) {
-        const int t0 = c * kChunk + lane * K;
         float dt[K], dtu[K], uu[K], dy[K], sB[K], sgA[K], dsp[K];
         float y[HAS_Z ? K : 1], gz[HAS_Z ? K : 1];
-        float sum_dt = 0.0f, dt_next = 0.0f;
+        float sum_dt = 0.0f, dD_part = 0.0f, dt_next = 0.0f;
         if (active) {
             float dd[K], gg[K];
-            load_k<T, K, VEC>(u, t0, L, uu, 0.0f);
-            load_k<T, K, VEC>(dl, t0, L, dd, 0.0f);
-            load_k<T, K, VEC>(go, t0, L, gg, 0.0f);
+            load_k<T, K, VEC>(static_cast<const T*>(p.u) + row, t0, L, uu, 0.0f);
+            load_k<T, K, VEC>(static_cast<const T*>(p.delta) + row, t0, L, dd, 0.0f);
+            load_k<T, K, VEC>(static_cast<const T*>(g.dout) + row, t0, L, gg, 0.0f);
             float zz[HAS_Z ? K : 1];
-            if constexpr (HAS_Z) load_k<T, K, VEC>(zr, t0, L, zz, 0.0f);
+            if constexpr (HAS_Z) load_k<T, K, VEC>(static_cast<const T*>(p.z) + row, t0, L, zz, 0.0f);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                const bool valid = t0 + k < L;
                 const float x = dd[k] + bias;
                 const float v = SOFTPLUS ? softplus_f(x) : x;
-                dt[k] = valid ? v : 0.0f;
+                dt[k] = (t0 + k < L) ? v : 0.0f;
                 dsp[k] = SOFTPLUS ? sigmoid_f(x) : 1.0f;
                 dtu[k] = dt[k] * uu[k];
                 sum_dt += dt[k];
@@ -108,129 +241,120 @@ __global__ __launch_bounds__(64 * kBwdWaves) void scan_bwd_kernel(ScanParams p, 
                 } else {
                     dy[k] = gg[k];
                 }
-                dD_acc = fmaf(dy[k], uu[k], dD_acc);
+                dD_part = fmaf(dy[k], uu[k], dD_part);
                 sB[k] = 0.0f;
                 sgA[k] = 0.0f;
             }
-            dt_next = dpp<kWaveShl1, 0xf>(0.0f, dt[0]);  // Delta at the next lane's first step
+            dt_next = shift_down(dt[0], 0.0f);
         }
 
-        for (int n = 0; n < N; ++n, ++it) {
-            const int buf = it & 1;
-            if (active) {
-                const float An = Arow[n];
-                const float An2 = An * kLog2e;
-                float bv[K], cv[K];
-                load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, bv);
-                load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n) * L, t0, L, cv);
-                // forward recompute of the states inside the chunk
-                float a[K], bb[K], hs[K];
-                float h = 0.0f;
-#pragma unroll
-                for (int k = 0; k < K; ++k) {
-                    a[k] = exp2_hw(dt[k] * An2);
-                    bb[k] = dtu[k] * bv[k];
-                    h = fmaf(a[k], h, bb[k]);
-                }
-                float P = exp2_hw(An2 * sum_dt);
-                float S = h;
-                wave_scan_fwd(P, S);
-                float Pex, Sex;
-                wave_shift_fwd(P, S, Pex, Sex);
-                const float hin = fmaf(Pex, Hrow[static_cast<size_t>(c) * N + n], Sex);
-                h = hin;
-#pragma unroll
-                for (int k = 0; k < K; ++k) {
-                    h = fmaf(a[k], h, bb[k]);
-                    hs[k] = h;
-                    if constexpr (HAS_Z) y[k] = fmaf(cv[k], h, y[k]);
-                }
-                // adjoint: lam_t = C_t dy_t + e_t lam_{t+1}, e_t = a_{t+1}.  The last step of
-                // lane 63 takes e = 1 and the carry G, which already holds a*lam of the next
-                // chunk's first step.
-                const float a_next = dpp<kWaveShl1, 0xf>(1.0f, a[0]);
-                float cdy[K];
-                float r = 0.0f;
-#pragma unroll
-                for (int k = K - 1; k >= 0; --k) {
-                    cdy[k] = cv[k] * dy[k];
-                    const float e = (k == K - 1) ? a_next : a[k + 1];
-                    r = fmaf(e, r, cdy[k]);
-                }
-                float Pr = exp2_hw(An2 * (sum_dt - dt[0] + dt_next));
-                float Sr = r;
-                wave_scan_rev(Pr, Sr);
-                float Prx, Srx;
-                wave_shift_rev(Pr, Sr, Prx, Srx);
-                float lam = fmaf(Prx, readlane(G, n), Srx);
-                float dA_part = 0.0f;
-#pragma unroll
-                for (int k = K - 1; k >= 0; --k) {
-                    const float e = (k == K - 1) ? a_next : a[k + 1];
-                    lam = fmaf(e, lam, cdy[k]);
-                    const float hprev = (k == 0) ? hin : hs[k - 1];
-                    const float gk = lam * hprev * a[k];
-                    dA_part = fmaf(gk, dt[k], dA_part);
-                    sgA[k] = fmaf(gk, An, sgA[k]);
-                    sB[k] = fmaf(lam, bv[k], sB[k]);
-                    atomicAdd(&accB[buf][k * KP + lane], lam * dtu[k]);
-                    atomicAdd(&accC[buf][k * KP + lane], dy[k] * hs[k]);
-                }
-                G = writelane(readlane(a[0] * lam, 0), n, G);
-                accA[wave][n][lane] += dA_part;
-            }
+        for (int j = 0; j < N; ++j) {
             __syncthreads();
-            // flush this state's dB/dC tile; the buffer is written again two iterations later,
-            // after the next barrier.
-            for (int i = tid; i < kChunk; i += 64 * W) {
-                const int k = i % K;
-                const int ln = i / K;
-                const int t = c * kChunk + i;
-                const float vb = accB[buf][k * KP + ln];
-                const float vc = accC[buf][k * KP + ln];
-                accB[buf][k * KP + ln] = 0.0f;
-                accC[buf][k * KP + ln] = 0.0f;
-                if (t < L) {
-                    const size_t o = (static_cast<size_t>(b) * N + n) * L + t;
-                    if (g.dB != nullptr) unsafeAtomicAdd(g.dB + o, vb);
-                    if (g.dC != nullptr) unsafeAtomicAdd(g.dC + o, vc);
-                }
-            }
-        }
-
-        if (active) {
-            float o1[K], o2[K];
+            if (!active) continue;
+            int n = j + rot;
+            if (n >= N) n -= N;
+            const float An = Arow[n];
+            const float An2 = An * kLog2e;
+            const float Hn = Hc[n];
+            const float Gn = Gc[n];
+            float bv[K], cv[K];
+            load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, bv);
+            load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n) * L, t0, L, cv);
+            // states inside the chunk, rebuilt from H_c
+            float a[K], bb[K], hs[K];
+            float h = 0.0f;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                const bool valid = t0 + k < L;
-                o1[k] = fmaf(sB[k], dt[k], dy[k] * Dd);               // du
-                o2[k] = fmaf(sB[k], uu[k], sgA[k]) * dsp[k];         // ddelta
-                dbias_acc += valid ? o2[k] : 0.0f;
+                a[k] = exp2_hw(dt[k] * An2);
+                bb[k] = dtu[k] * bv[k];
+                h = fmaf(a[k], h, bb[k]);
             }
-            store_k<T, K, VEC>(du_o, t0, L, o1);
-            store_k<T, K, VEC>(dd_o, t0, L, o2);
-            if constexpr (HAS_Z) {
+            float P = exp2_hw(An2 * sum_dt);
+            float S = h;
+            scan_fwd_fused(P, S);
+            const float hin = shift_up(fmaf(P, Hn, S), Hn);
+            h = hin;
 #pragma unroll
-                for (int k = 0; k < K; ++k) o1[k] = gz[k] * y[k];
-                store_k<T, K, VEC>(dz_o, t0, L, o1);
+            for (int k = 0; k < K; ++k) {
+                h = fmaf(a[k], h, bb[k]);
+                hs[k] = h;
+                if constexpr (HAS_Z) y[k] = fmaf(cv[k], h, y[k]);
+            }
+            // adjoint inside the chunk, rebuilt from G_c: lam_t = C_t dy_t + e_t lam_{t+1},
+            // e_t = a_{t+1}; lane 63's last step takes e = 1 and the carry G_c.
+            const float a_next = shift_down(a[0], 1.0f);
+            float cdy[K];
+            float rr = 0.0f;
+#pragma unroll
+            for (int k = K - 1; k >= 0; --k) {
+                cdy[k] = cv[k] * dy[k];
+                const float e = (k == K - 1) ? a_next : a[k + 1];
+                rr = fmaf(e, rr, cdy[k]);
+            }
+            float Pr = exp2_hw(An2 * (sum_dt - dt[0] + dt_next));
+            float Sr = rr;
+            scan_rev_fused(Pr, Sr);
+            float lam = shift_down(fmaf(Pr, Gn, Sr), Gn);
+            float dA_part = 0.0f;
+            float* sBn = myB + n * K * KP + lane;
+            float* sCn = myC + n * K * KP + lane;
+#pragma unroll
+            for (int k = K - 1; k >= 0; --k) {
+                const float e = (k == K - 1) ? a_next : a[k + 1];
+                lam = fmaf(e, lam, cdy[k]);
+                const float hprev = (k == 0) ? hin : hs[k - 1];
+                const float gk = lam * hprev * a[k];
+                dA_part = fmaf(gk, dt[k], dA_part);
+                sgA[k] = fmaf(gk, An, sgA[k]);
+                sB[k] = fmaf(lam, bv[k], sB[k]);
+                sBn[k * KP] = fmaf(lam, dtu[k], sBn[k * KP]);
+                sCn[k * KP] = fmaf(dy[k], hs[k], sCn[k * KP]);
+            }
+            if (g.dA != nullptr) {
+                const float sA = wave_sum_fused(dA_part);
+                if (lane == 0) unsafeAtomicAdd(g.dA + static_cast<size_t>(d) * N + n, sA);
             }
         }
-    }
+        if (!active) continue;
 
-    if (active) {
-        if (g.dA != nullptr) {
-            for (int n = 0; n < N; ++n) {
-                const float s = wave_sum(accA[wave][n][lane]);
-                if (lane == 0) unsafeAtomicAdd(g.dA + static_cast<size_t>(d) * N + n, s);
-            }
+        float o1[K], o2[K];
+        float db_part = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            o1[k] = fmaf(sB[k], dt[k], dy[k] * Dd);            // du
+            o2[k] = fmaf(sB[k], uu[k], sgA[k]) * dsp[k];      // ddelta
+            db_part += (t0 + k < L) ? o2[k] : 0.0f;
         }
-        const float sD = wave_sum(dD_acc);
-        const float sb = wave_sum(dbias_acc);
+        store_k<T, K, VEC>(static_cast<T*>(g.du) + row, t0, L, o1);
+        store_k<T, K, VEC>(static_cast<T*>(g.ddelta) + row, t0, L, o2);
+        if constexpr (HAS_Z) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) o1[k] = gz[k] * y[k];
+            store_k<T, K, VEC>(static_cast<T*>(g.dz) + row, t0, L, o1);
+        }
+        const float sD = wave_sum_fused(dD_part);
+        const float sb = wave_sum_fused(db_part);
         if (lane == 0) {
             if (g.dD != nullptr) unsafeAtomicAdd(g.dD + d, sD);
             if (g.dbias != nullptr) unsafeAtomicAdd(g.dbias + d, sb);
         }
-        if (g.dh0 != nullptr && lane < N) g.dh0[ch * N + lane] = G;
+    }
+
+    __syncthreads();
+    for (int i = tid; i < N * kChunk; i += 64 * W) {
+        const int n = i / kChunk;
+        const int tt = i - n * kChunk;
+        const int t = c * kChunk + tt;
+        if (t >= L) continue;
+        const int slot = (n * K + tt % K) * KP + tt / K;
+        float vb = 0.0f, vc = 0.0f;
+        for (int q = 0; q < groups; ++q) {
+            vb += accB[q * tile + slot];
+            vc += accC[q * tile + slot];
+        }
+        const size_t o = (static_cast<size_t>(b) * N + n) * L + t;
+        if (g.dB != nullptr) unsafeAtomicAdd(g.dB + o, vb);
+        if (g.dC != nullptr) unsafeAtomicAdd(g.dC + o, vc);
     }
 }
 
@@ -249,23 +373,73 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream) {
     return hipGetLastError();
 }
 
+size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states) {
+    const size_t nch = (static_cast<size_t>(L) + kChunk - 1) / kChunk;
+    const size_t states = static_cast<size_t>(B) * D * nch * N * sizeof(float);
+    const size_t per_chunk = static_cast<size_t>(B) * D * nch * sizeof(float);
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    return (need_states ? up(states) : 0) + up(states) + 2 * up(per_chunk);
+}
+
 namespace {
 
+// Channels per wavefront in the main kernel: aim at about 1024 workgroups so that every CU
+// gets several, while keeping the number of dB/dC partial sums (one per workgroup) small.
+int main_per_wave(const ScanParams& p) {
+    const long long slots = static_cast<long long>(p.B) * p.nchunks;
+    long long per = (static_cast<long long>(p.D) * slots + 1024LL * kMainWaves - 1) /
+                    (1024LL * kMainWaves);
+    const long long max_per = (p.D + kMainWaves - 1) / kMainWaves;
+    if (per < 1) per = 1;
+    if (per > max_per) per = max_per;
+    return static_cast<int>(per);
+}
+
 template <typename T, bool VEC, bool HAS_Z, bool SP>
-hipError_t bwd_go(const ScanParams& p, const GradParams& g, const float* cst, hipStream_t s) {
-    dim3 grid((p.D + kBwdWaves - 1) / kBwdWaves, p.B), block(64 * kBwdWaves);
-    hipLaunchKernelGGL((scan_bwd_kernel<T, VEC, HAS_Z, SP>), grid, block, 0, s, p, g, cst);
+hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hipStream_t s) {
+    const int rows = p.B * p.D * p.nchunks;
+    dim3 sgrid((rows + kSumWaves - 1) / kSumWaves), sblock(64 * kSumWaves);
+    if (w.want_fwd)
+        hipLaunchKernelGGL((bwd_summary_kernel<T, VEC, HAS_Z, SP, true>), sgrid, sblock, 0, s, p,
+                           g, w);
+    else
+        hipLaunchKernelGGL((bwd_summary_kernel<T, VEC, HAS_Z, SP, false>), sgrid, sblock, 0, s, p,
+                           g, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int links = p.B * p.D * p.N;
+    dim3 lgrid((links + 255) / 256), lblock(256);
+    if (w.want_fwd)
+        hipLaunchKernelGGL(bwd_link_kernel<true>, lgrid, lblock, 0, s, p, g, w);
+    else
+        hipLaunchKernelGGL(bwd_link_kernel<false>, lgrid, lblock, 0, s, p, g, w);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int per_wave = main_per_wave(p);
+    const int cgroups = (p.D + per_wave * kMainWaves - 1) / (per_wave * kMainWaves);
+    const size_t lds = 2 * static_cast<size_t>(acc_groups(p.N, kMainWaves)) * p.N *
+                       (kChunk / 64) * kAccKP * sizeof(float);
+    // the accumulator tiles exceed the 64 KB default for N = 16; the largest need over
+    // N <= kMaxN is 2 * 16 * K * KP floats
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&bwd_main_kernel<T, VEC, HAS_Z, SP>),
+        hipFuncAttributeMaxDynamicSharedMemorySize,
+        static_cast<int>(2 * kMaxN * (kChunk / 64) * kAccKP * sizeof(float)));
+    if (attr != hipSuccess) return attr;
+    dim3 mgrid(cgroups, p.nchunks, p.B), mblock(64 * kMainWaves);
+    hipLaunchKernelGGL((bwd_main_kernel<T, VEC, HAS_Z, SP>), mgrid, mblock, lds, s, p, g, w,
+                       per_wave);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t bwd_dispatch(const ScanParams& p, const GradParams& g, const float* cst,
+hipError_t bwd_dispatch(const ScanParams& p, const GradParams& g, const BwdWork& w,
                         hipStream_t s) {
     const bool vec = (static_cast<size_t>(p.L) * sizeof(T)) % 16 == 0;
     const bool hz = p.z != nullptr;
     const bool sp = p.softplus != 0;
 #define MSEL_BWD(V, Z, S) \
-    if (vec == V && hz == Z && sp == S) return bwd_go<T, V, Z, S>(p, g, cst, s);
+    if (vec == V && hz == Z && sp == S) return bwd_go<T, V, Z, S>(p, g, w, s);
     MSEL_BWD(true, true, true)
     MSEL_BWD(true, true, false)
     MSEL_BWD(true, false, true)
@@ -281,10 +455,28 @@ hipError_t bwd_dispatch(const ScanParams& p, const GradParams& g, const float* c
 }  // namespace
 
 hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float* chunk_states,
-                           bool bf16, hipStream_t stream) {
+                           void* workspace, bool bf16, hipStream_t stream) {
     if (p.N > kMaxN) return hipErrorInvalidValue;
-    if (bf16) return bwd_dispatch<bf16_t>(p, g, chunk_states, stream);
-    return bwd_dispatch<float>(p, g, chunk_states, stream);
+    const size_t nch = static_cast<size_t>(p.nchunks);
+    const size_t states = static_cast<size_t>(p.B) * p.D * nch * p.N * sizeof(float);
+    const size_t per_chunk = static_cast<size_t>(p.B) * p.D * nch * sizeof(float);
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    char* ws = static_cast<char*>(workspace);
+    BwdWork w;
+    w.want_fwd = chunk_states == nullptr;
+    if (w.want_fwd) {
+        w.H = reinterpret_cast<float*>(ws);
+        ws += up(states);
+    } else {
+        w.H = const_cast<float*>(chunk_states);
+    }
+    w.G = reinterpret_cast<float*>(ws);
+    ws += up(states);
+    w.sdt = reinterpret_cast<float*>(ws);
+    ws += up(per_chunk);
+    w.dfirst = reinterpret_cast<float*>(ws);
+    if (bf16) return bwd_dispatch<bf16_t>(p, g, w, stream);
+    return bwd_dispatch<float>(p, g, w, stream);
 }
 
 }  // namespace msel

@@ -10,9 +10,10 @@
 //     pass 1  a_k = exp2(Delta_k * A'_n)           (A' = A*log2 e: ZOH transition)
 //             b_k = Delta_k u_k * B_{n,k}           (Euler input)
 //             lane-local chain from 0 -> S, and P = exp2(A'_n * sum Delta) (lane transition)
-//     scan    inclusive DPP scan of (P, S) over the 64 lanes, shifted to exclusive, applied to
-//             the state carried from the previous tile -> state entering the lane (page 1:
-//             the recurrence is parallelized with a work-efficient scan)
+//     scan    inclusive DPP scan of (P, S) over the 64 lanes (DPP fused into the fma/mul),
+//             applied to the state carried from the previous tile and shifted by one lane ->
+//             state entering the lane (page 1: the recurrence is parallelized with a
+//             work-efficient scan)
 //     pass 2  replay the chain from that state, y_k += C_{n,k} h_k
 //   epilogue: y += D u (initialised up front), out = y * silu(z), one store.
 //
@@ -86,12 +87,11 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
             }
             float P = exp2_hw(An * sum_dt);
             float S = h;
-            wave_scan_fwd(P, S);
-            float Pex, Sex;
-            wave_shift_fwd(P, S, Pex, Sex);
+            scan_fwd_fused(P, S);
             const float cn = readlane(carry, n);
-            const float hin = fmaf(Pex, cn, Sex);
-            carry = writelane(fmaf(readlane(P, 63), cn, readlane(S, 63)), n, carry);
+            const float Q = fmaf(P, cn, S);       // state after the lane's last step
+            const float hin = shift_up(Q, cn);    // state entering the lane
+            carry = writelane(readlane(Q, 63), n, carry);
             if (cs_dst != nullptr) cs_dst[n] = hin;
 
             load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n) * L, t0, L, bc);

@@ -131,6 +131,21 @@ def msel_scan_chunk_carry(u, delta, A, B, delta_bias=None, delta_softplus=True, 
     return chunk_states, final_state
 
 
+def bwd_workspace_bytes(u, A, chunk_states_given=False) -> int:
+    """Bytes of workspace msel_scan_bwd needs for this problem (msel_scan_bwd_workspace_bytes)."""
+    bsz, dim, L = u.shape
+    a = _lib.ScanArgs()
+    a.abi_version = _lib.ABI_VERSION
+    a.batch, a.dim, a.dstate, a.seqlen = int(bsz), int(dim), int(A.shape[1]), int(L)
+    a.dtype = _dtype_code(u.dtype)
+    a.delta_softplus, a.reserved = 1, 0
+    # the size depends only on the shapes; non-null placeholders satisfy the argument checks
+    for f in ("u", "delta", "B", "A"):
+        setattr(a, f, 256)
+    a.chunk_states = 256 if chunk_states_given else None
+    return int(_lib.load().msel_scan_bwd_workspace_bytes(ctypes.byref(a)))
+
+
 def msel_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
                   delta_softplus=True, h0=None, chunk_states=None, want_dA=True, want_dB=True,
                   want_dC=True, want_dD=True, want_ddelta_bias=True, want_dh0=False,

@@ -105,7 +105,7 @@ def test_valid_args_pass_validation(lib):
     a.chunk_states = _addr()
     assert lib.msel_validate_chunk_carry(ctypes.byref(a)) == 0
     g = _good_grads(a)
-    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), None, 0) == 0
+    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), _addr(), 1 << 20) == 0
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -183,17 +183,23 @@ def test_bwd_workspace_rules(lib):
     a = _good_args(bsz=2, dim=3, N=16, L=1000)
     g = _good_grads(a)
     T = lib.msel_chunk_len()
+    nch = -(-1000 // T)
+    up = lambda x: (x + 255) // 256 * 256
+    states, per_chunk = 2 * 3 * nch * 16 * 4, 2 * 3 * nch * 4
     need = lib.msel_scan_bwd_workspace_bytes(ctypes.byref(a))
-    assert need == 2 * 3 * (-(-1000 // T)) * 16 * 4
+    assert need == 2 * up(states) + 2 * up(per_chunk)
     assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), None, 0) == 6
     ws = _addr()
     assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), ws, need - 1) == 6
     assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), ws, need) == 0
-    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), ws + 4, need) == 4
+    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), ws + 16, need) == 4
     assert lib.msel_scan_bwd(ctypes.byref(a), ctypes.byref(g), None, 0, None) == 6
+    # with caller-provided chunk states the workspace only holds the adjoint carries
     a.chunk_states = _addr()
-    assert lib.msel_scan_bwd_workspace_bytes(ctypes.byref(a)) == 0
-    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), None, 0) == 0
+    need2 = lib.msel_scan_bwd_workspace_bytes(ctypes.byref(a))
+    assert need2 == up(states) + 2 * up(per_chunk)
+    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), ws, need2) == 0
+    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), a.chunk_states, need2) == 7
 
 
 @pytest.mark.parametrize("field,code", [("dout", 1), ("du", 1), ("ddelta", 1), ("dz", 1)])
@@ -202,7 +208,7 @@ def test_bwd_required_grads(lib, field, code):
     a.chunk_states = _addr()
     g = _good_grads(a)
     setattr(g, field, None)
-    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), None, 0) == code
+    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), _addr(), 1 << 20) == code
 
 
 def test_bwd_dz_optional_without_gate(lib):
@@ -211,24 +217,29 @@ def test_bwd_dz_optional_without_gate(lib):
     a.z = None
     g = _good_grads(a)
     g.dz = None
-    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), None, 0) == 0
+    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), _addr(), 1 << 20) == 0
 
 
 def test_bwd_alias_and_alignment(lib):
     a = _good_args()
     a.chunk_states = _addr()
+    ws, big = _addr(), 1 << 20
+    check = lambda g: lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), ws, big)
     g = _good_grads(a)
     g.du = a.u
-    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), None, 0) == 7
+    assert check(g) == 7
     g = _good_grads(a)
     g.ddelta = g.dout
-    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), None, 0) == 7
+    assert check(g) == 7
+    g = _good_grads(a)
+    g.dB = ws
+    assert check(g) == 7
     g = _good_grads(a)
     g.dz = g.dz + 4
-    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), None, 0) == 4
+    assert check(g) == 4
     g = _good_grads(a)
     g.dB = g.dB + 1
-    assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), None, 0) == 4
+    assert check(g) == 4
 
 
 def test_python_binding_refuses_cpu_tensors():
