@@ -3,9 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu]
 
 A step is one pass of the whole hot path over one batch of synthetic input resident in HBM:
-the fused forward scan (out and final state), then the backward with recomputation (all
-gradients), which first runs the chunk-carry pass forward for the chunk-boundary states and
-backward for the adjoint, so nothing is stored between the two passes.  The standalone
+the fused forward scan (out, final state and the state at every chunk boundary), then the
+backward with recomputation (all gradients): it rebuilds every state inside the chunks from
+those boundary states and runs the chunk carry backward for the adjoint.  The standalone
 chunk-carry entry point is timed separately.  The
 default workload is batch 8, d_model 768 x expand 2 = 1536 channels, dstate 16, seqlen 2048,
 bf16 activations with fp32 state -- the workload that runs both the forward and the backward.
@@ -83,19 +83,20 @@ def main():
          for k, v in t.items()}
     nch = msel.num_chunks(w.seqlen)
     names = ("fwd", "bwd")
-    ws = torch.empty(msel.bwd_workspace_bytes(d["u"], d["A"]), device=dev, dtype=torch.uint8)
+    ws = torch.empty(msel.bwd_workspace_bytes(d["u"], d["A"], True), device=dev,
+                     dtype=torch.uint8)
 
     def step(ev=None):
-        """fwd (out, final state) then bwd with recomputation: chunk states are rebuilt by the
-        chunk-carry pass inside msel_scan_bwd, nothing is stored between the two passes."""
+        """fwd (out, final state, one state per chunk) then bwd, which recomputes every state
+        inside the chunks and runs the chunk carry backward for the adjoint."""
         if ev is not None:
             ev[0].record()
-        out, fin, _ = msel.msel_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],
-                                         d["z"], d["bias"], True)
+        out, fin, cs = msel.msel_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],
+                                          d["z"], d["bias"], True, return_chunk_states=True)
         if ev is not None:
             ev[1].record()
         g = msel.msel_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dout"], d["D"],
-                               d["z"], d["bias"], True, chunk_states=None, workspace=ws)
+                               d["z"], d["bias"], True, chunk_states=cs, workspace=ws)
         if ev is not None:
             ev[2].record()
         return out, fin, g
@@ -132,7 +133,8 @@ def main():
         kernels[n] = {"ms": round(per[n], 4), "alg_bytes": alg[n], "GB/s": round(gbs, 1),
                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "tc_per_s": float(f"{tc / (per[n] * 1e-3):.4g}")}
-    kernels["bwd"]["note"] = "msel_scan_bwd call: summary + link + main kernels and zero-fills"
+    kernels["bwd"]["note"] = ("msel_scan_bwd call: convert + summary + link + main kernels and "
+                              "zero-fills")
     dom = max(names, key=lambda n: per[n])
     ach = alg[dom] / (per[dom] * 1e-3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
@@ -148,7 +150,7 @@ def main():
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
-                   "seqlen": w.seqlen, "step": "fwd + bwd (chunk states recomputed)"},
+                   "seqlen": w.seqlen, "step": "fwd (with chunk-boundary states) + bwd"},
         "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

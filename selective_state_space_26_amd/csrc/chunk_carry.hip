@@ -55,10 +55,13 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
                 sum_dt += dt[k];
             }
         }
+        Raw<T, K> Bn;
+        load_raw<T, K, VEC>(Bb, t0, L, Bn);
         for (int n = 0; n < N; ++n) {
             const float An = Arow[n] * kLog2e;
             float bc[K];
-            load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, bc);
+            unpack(Bn, bc);
+            if (n + 1 < N) load_raw<T, K, VEC>(Bb + static_cast<size_t>(n + 1) * L, t0, L, Bn);
             float h = 0.0f;
 #pragma unroll
             for (int k = 0; k < K; ++k) h = fmaf(exp2_hw(dt[k] * An), h, du[k] * bc[k]);

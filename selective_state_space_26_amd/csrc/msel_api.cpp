@@ -7,7 +7,7 @@
 
 #include <stdint.h>
 
-#include "../../include/msel.h"
+#include "msel.h"  // include/ is on the include path
 #include "msel_kernels.hpp"
 
 namespace {

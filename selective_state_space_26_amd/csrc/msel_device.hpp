@@ -165,6 +165,65 @@ __device__ __forceinline__ void store_k(T* __restrict__ row, int t0, int L, cons
     }
 }
 
+// Raw (still packed) rows: loads issued early and unpacked to fp32 only when used, so that
+// the next state's B/C rows can be in flight while the current state is computed.
+template <typename T, int K>
+struct Raw {
+    static constexpr int kVecs = K * static_cast<int>(sizeof(T)) / 16;
+    u32x4 v[kVecs];
+};
+
+template <typename T, int K, bool VEC>
+__device__ __forceinline__ void load_raw(const T* __restrict__ row, int t0, int L, Raw<T, K>& r) {
+    if (VEC && t0 + K <= L) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(row + t0);
+#pragma unroll
+        for (int j = 0; j < Raw<T, K>::kVecs; ++j) r.v[j] = p[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < Raw<T, K>::kVecs; ++j) {
+            uint32_t wds[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (sizeof(T) == 4) {
+                    const int t = t0 + 4 * j + q;
+                    wds[q] = (t < L) ? __float_as_uint(reinterpret_cast<const float*>(row)[t]) : 0u;
+                } else {
+                    const int t = t0 + 8 * j + 2 * q;
+                    const uint16_t* h = reinterpret_cast<const uint16_t*>(row);
+                    const uint32_t lo = (t < L) ? h[t] : 0u;
+                    const uint32_t hi = (t + 1 < L) ? h[t + 1] : 0u;
+                    wds[q] = lo | (hi << 16);
+                }
+            }
+            r.v[j] = u32x4{wds[0], wds[1], wds[2], wds[3]};
+        }
+    }
+}
+
+template <typename T, int K>
+__device__ __forceinline__ void unpack(const Raw<T, K>& r, float (&v)[K]) {
+#pragma unroll
+    for (int j = 0; j < Raw<T, K>::kVecs; ++j) {
+        const u32x4 w = r.v[j];
+        if constexpr (sizeof(T) == 4) {
+            v[4 * j + 0] = __uint_as_float(w.x);
+            v[4 * j + 1] = __uint_as_float(w.y);
+            v[4 * j + 2] = __uint_as_float(w.z);
+            v[4 * j + 3] = __uint_as_float(w.w);
+        } else {
+            v[8 * j + 0] = bf16lo(w.x);
+            v[8 * j + 1] = bf16hi(w.x);
+            v[8 * j + 2] = bf16lo(w.y);
+            v[8 * j + 3] = bf16hi(w.y);
+            v[8 * j + 4] = bf16lo(w.z);
+            v[8 * j + 5] = bf16hi(w.z);
+            v[8 * j + 6] = bf16lo(w.w);
+            v[8 * j + 7] = bf16hi(w.w);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------------------
 // Cross-lane moves.
 

@@ -14,7 +14,8 @@
 //   ddelta_t = dDelta_t * sigmoid(delta_t + bias) with the softplus, dbias += ddelta_t
 //   dD += dy_t u_t       dh0 = a_0 lam_0
 //
-// Three launches, all parallel over chunks:
+// Four launches, all parallel over chunks:
+//  0. convert: B and C to fp32 rows padded to whole chunks (read by every channel below).
 //  1. summary: one wavefront per (batch, channel, chunk).  For every state n it forms the
 //     chunk's local end state from a zero start (forward) and the adjoint at the chunk's
 //     first step from a zero adjoint beyond the chunk (reverse), both with the lane-local
@@ -41,9 +42,11 @@ namespace msel {
 
 constexpr int kMaxN = 16;
 constexpr int kSumWaves = 4;
-constexpr int kMainWaves = 8;
+constexpr int kMainWaves = 12;  // 3 per SIMD: the main kernel needs ~160 VGPRs
 
 struct BwdWork {
+    float* Bf;      // [B*N*nch*kChunk]: B as fp32, rows zero-padded to whole chunks
+    float* Cf;      // [B*N*nch*kChunk]: C likewise
     float* H;       // [B*D*nch*N]: chunk-start states (may be the caller's chunk_states)
     float* G;       // [B*D*nch*N]: adjoint carry after each chunk
     float* sdt;     // [B*D*nch]: sum of Delta over the chunk
@@ -69,8 +72,10 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
     const size_t row = static_cast<size_t>(ch) * L;
     const T* __restrict__ dl = static_cast<const T*>(p.delta) + row;
     const T* __restrict__ go = static_cast<const T*>(g.dout) + row;
-    const T* __restrict__ Bb = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
-    const T* __restrict__ Cb = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
+    // fp32 copies of B and C with rows padded to whole chunks (built by the convert pass)
+    const int Lp = nch * kChunk;
+    const float* __restrict__ Bb = w.Bf + static_cast<size_t>(b) * N * Lp;
+    const float* __restrict__ Cb = w.Cf + static_cast<size_t>(b) * N * Lp;
     const float bias = p.bias ? p.bias[d] : 0.0f;
     const float* __restrict__ Arow = p.A + static_cast<size_t>(d) * N;
     const int t0 = c * kChunk + lane * K;
@@ -101,14 +106,22 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
         w.sdt[idx] = chunk_dt;
         w.dfirst[idx] = dt[0];
     }
+    Raw<float, K> Bn, Cn;
+    if constexpr (FWD) load_raw<float, K, true>(Bb, t0, Lp, Bn);
+    load_raw<float, K, true>(Cb, t0, Lp, Cn);
     for (int n = 0; n < N; ++n) {
         const float An2 = Arow[n] * kLog2e;
+        float bv[K], cv[K];
+        if constexpr (FWD) unpack(Bn, bv);
+        unpack(Cn, cv);
+        if (n + 1 < N) {  // prefetch the next state's rows
+            if constexpr (FWD) load_raw<float, K, true>(Bb + static_cast<size_t>(n + 1) * Lp, t0, Lp, Bn);
+            load_raw<float, K, true>(Cb + static_cast<size_t>(n + 1) * Lp, t0, Lp, Cn);
+        }
         float a[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) a[k] = exp2_hw(dt[k] * An2);
         if constexpr (FWD) {
-            float bv[K];
-            load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, bv);
             float h = 0.0f;
 #pragma unroll
             for (int k = 0; k < K; ++k) h = fmaf(a[k], h, du[k] * bv[k]);
@@ -117,8 +130,6 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
             scan_fwd_fused(P, S);
             if (lane == 63) w.H[static_cast<size_t>(idx) * N + n] = S;
         }
-        float cv[K];
-        load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n) * L, t0, L, cv);
         const float a_next = shift_down(a[0], 1.0f);
         float r = 0.0f;
 #pragma unroll
@@ -186,6 +197,7 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
     const int N = p.N;
     const int L = p.L;
     const int nch = p.nchunks;
+    const int Lp = nch * kChunk;
     const int groups = acc_groups(N, W);
     const int tile = N * K * KP;             // floats per (tensor, group)
     float* accB = acc;
@@ -193,33 +205,41 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
     for (int i = tid; i < 2 * groups * tile; i += 64 * W) acc[i] = 0.0f;
 
     // Wave w updates state (j + w) mod N of its group's tiles at step j, so within a step
-    // every accumulator slot has a single writer; the barrier at the top of each step orders
-    // the read-add-writes of consecutive steps.
+    // every accumulator slot has a single writer; the barrier in each step orders the
+    // read-add-writes of consecutive steps.
     const int grp = wave / N;
     const int rot = wave - grp * N;
     float* myB = accB + grp * tile;
     float* myC = accC + grp * tile;
 
     const int t0 = c * kChunk + lane * K;
-    const T* __restrict__ Bb = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
-    const T* __restrict__ Cb = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
+    const float* __restrict__ Bb = w.Bf + static_cast<size_t>(b) * N * Lp;
+    const float* __restrict__ Cb = w.Cf + static_cast<size_t>(b) * N * Lp;
 
     for (int r = 0; r < per_wave; ++r) {
         const int d = (blockIdx.x * per_wave + r) * W + wave;
         const bool active = d < p.D;  // wave-uniform; inactive waves still join the barriers
         const size_t ch = static_cast<size_t>(b) * p.D + (active ? d : 0);
         const size_t row = ch * L;
-        const float bias = (active && p.bias) ? p.bias[d] : 0.0f;
-        const float Dd = (active && p.Dv) ? p.Dv[d] : 0.0f;
-        const float* __restrict__ Arow = p.A + static_cast<size_t>(active ? d : 0) * N;
-        const float* __restrict__ Hc = w.H + (ch * nch + c) * N;
-        const float* __restrict__ Gc = w.G + (ch * nch + c) * N;
+        const int dd_ = active ? d : 0;
+        const float bias = p.bias ? p.bias[dd_] : 0.0f;
+        const float Dd = p.Dv ? p.Dv[dd_] : 0.0f;
+        // per-channel rows of A, H_c and G_c, one value per lane (lane n holds state n)
+        const size_t hg = (ch * nch + c) * N;
+        const float Av = (lane < N) ? p.A[static_cast<size_t>(dd_) * N + lane] : 0.0f;
+        const float Hv = (lane < N) ? w.H[hg + lane] : 0.0f;
+        const float Gv = (lane < N) ? w.G[hg + lane] : 0.0f;
 
-        float dt[K], dtu[K], uu[K], dy[K], sB[K], sgA[K], dsp[K];
-        float y[HAS_Z ? K : 1], gz[HAS_Z ? K : 1];
-        float sum_dt = 0.0f, dD_part = 0.0f, dt_next = 0.0f;
-        if (active) {
-            float dd[K], gg[K];
+        int n = rot;  // state of step 0; rows of the next step are prefetched
+        Raw<float, K> Bn, Cn;
+        load_raw<float, K, true>(Bb + static_cast<size_t>(n) * Lp, t0, Lp, Bn);
+        load_raw<float, K, true>(Cb + static_cast<size_t>(n) * Lp, t0, Lp, Cn);
+
+        float dt[K], dtu[K], dy[K], sB[K], sgA[K];
+        float y[HAS_Z ? K : 1];
+        float sum_dt = 0.0f, dD_part = 0.0f;
+        {
+            float uu[K], dd[K], gg[K];
             load_k<T, K, VEC>(static_cast<const T*>(p.u) + row, t0, L, uu, 0.0f);
             load_k<T, K, VEC>(static_cast<const T*>(p.delta) + row, t0, L, dd, 0.0f);
             load_k<T, K, VEC>(static_cast<const T*>(g.dout) + row, t0, L, gg, 0.0f);
@@ -230,13 +250,10 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
                 const float x = dd[k] + bias;
                 const float v = SOFTPLUS ? softplus_f(x) : x;
                 dt[k] = (t0 + k < L) ? v : 0.0f;
-                dsp[k] = SOFTPLUS ? sigmoid_f(x) : 1.0f;
                 dtu[k] = dt[k] * uu[k];
                 sum_dt += dt[k];
                 if constexpr (HAS_Z) {
-                    const float s = sigmoid_f(zz[k]);
-                    dy[k] = gg[k] * zz[k] * s;
-                    gz[k] = gg[k] * s * fmaf(zz[k], 1.0f - s, 1.0f);
+                    dy[k] = gg[k] * zz[k] * sigmoid_f(zz[k]);
                     y[k] = Dd * uu[k];
                 } else {
                     dy[k] = gg[k];
@@ -245,29 +262,33 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
                 sB[k] = 0.0f;
                 sgA[k] = 0.0f;
             }
-            dt_next = shift_down(dt[0], 0.0f);
         }
+        const float dt_next = shift_down(dt[0], 0.0f);
+        float dAv = 0.0f;  // lane n: dA[d, n] contribution of this (batch row, chunk)
 
         for (int j = 0; j < N; ++j) {
+            float bv[K], cv[K];
+            unpack(Bn, bv);
+            unpack(Cn, cv);
+            const int nc = n;
+            if (j + 1 < N) {
+                n = (n + 1 == N) ? 0 : n + 1;
+                load_raw<float, K, true>(Bb + static_cast<size_t>(n) * Lp, t0, Lp, Bn);
+                load_raw<float, K, true>(Cb + static_cast<size_t>(n) * Lp, t0, Lp, Cn);
+            }
             __syncthreads();
             if (!active) continue;
-            int n = j + rot;
-            if (n >= N) n -= N;
-            const float An = Arow[n];
+            const float An = readlane(Av, nc);
             const float An2 = An * kLog2e;
-            const float Hn = Hc[n];
-            const float Gn = Gc[n];
-            float bv[K], cv[K];
-            load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, bv);
-            load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n) * L, t0, L, cv);
+            const float Hn = readlane(Hv, nc);
+            const float Gn = readlane(Gv, nc);
             // states inside the chunk, rebuilt from H_c
-            float a[K], bb[K], hs[K];
+            float a[K], hs[K];
             float h = 0.0f;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 a[k] = exp2_hw(dt[k] * An2);
-                bb[k] = dtu[k] * bv[k];
-                h = fmaf(a[k], h, bb[k]);
+                h = fmaf(a[k], h, dtu[k] * bv[k]);
             }
             float P = exp2_hw(An2 * sum_dt);
             float S = h;
@@ -276,32 +297,30 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
             h = hin;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                h = fmaf(a[k], h, bb[k]);
+                h = fmaf(a[k], h, dtu[k] * bv[k]);
                 hs[k] = h;
                 if constexpr (HAS_Z) y[k] = fmaf(cv[k], h, y[k]);
             }
             // adjoint inside the chunk, rebuilt from G_c: lam_t = C_t dy_t + e_t lam_{t+1},
             // e_t = a_{t+1}; lane 63's last step takes e = 1 and the carry G_c.
             const float a_next = shift_down(a[0], 1.0f);
-            float cdy[K];
             float rr = 0.0f;
 #pragma unroll
             for (int k = K - 1; k >= 0; --k) {
-                cdy[k] = cv[k] * dy[k];
                 const float e = (k == K - 1) ? a_next : a[k + 1];
-                rr = fmaf(e, rr, cdy[k]);
+                rr = fmaf(e, rr, cv[k] * dy[k]);
             }
             float Pr = exp2_hw(An2 * (sum_dt - dt[0] + dt_next));
             float Sr = rr;
             scan_rev_fused(Pr, Sr);
             float lam = shift_down(fmaf(Pr, Gn, Sr), Gn);
             float dA_part = 0.0f;
-            float* sBn = myB + n * K * KP + lane;
-            float* sCn = myC + n * K * KP + lane;
+            float* sBn = myB + nc * K * KP + lane;
+            float* sCn = myC + nc * K * KP + lane;
 #pragma unroll
             for (int k = K - 1; k >= 0; --k) {
                 const float e = (k == K - 1) ? a_next : a[k + 1];
-                lam = fmaf(e, lam, cdy[k]);
+                lam = fmaf(e, lam, cv[k] * dy[k]);
                 const float hprev = (k == 0) ? hin : hs[k - 1];
                 const float gk = lam * hprev * a[k];
                 dA_part = fmaf(gk, dt[k], dA_part);
@@ -310,51 +329,91 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
                 sBn[k * KP] = fmaf(lam, dtu[k], sBn[k * KP]);
                 sCn[k * KP] = fmaf(dy[k], hs[k], sCn[k * KP]);
             }
-            if (g.dA != nullptr) {
-                const float sA = wave_sum_fused(dA_part);
-                if (lane == 0) unsafeAtomicAdd(g.dA + static_cast<size_t>(d) * N + n, sA);
-            }
+            dAv = writelane(dAv + wave_sum_fused(dA_part), nc, dAv);
         }
         if (!active) continue;
 
+        // inputs that were not kept live across the steps are reloaded (L2-resident by now)
         float o1[K], o2[K];
         float db_part = 0.0f;
+        {
+            float uu[K], dd[K];
+            load_k_cached<T, K, VEC>(static_cast<const T*>(p.u) + row, t0, L, uu);
+            load_k_cached<T, K, VEC>(static_cast<const T*>(p.delta) + row, t0, L, dd);
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            o1[k] = fmaf(sB[k], dt[k], dy[k] * Dd);            // du
-            o2[k] = fmaf(sB[k], uu[k], sgA[k]) * dsp[k];      // ddelta
-            db_part += (t0 + k < L) ? o2[k] : 0.0f;
+            for (int k = 0; k < K; ++k) {
+                const float dsp = SOFTPLUS ? sigmoid_f(dd[k] + bias) : 1.0f;
+                o1[k] = fmaf(sB[k], dt[k], dy[k] * Dd);            // du
+                o2[k] = fmaf(sB[k], uu[k], sgA[k]) * dsp;         // ddelta
+                db_part += (t0 + k < L) ? o2[k] : 0.0f;
+            }
         }
         store_k<T, K, VEC>(static_cast<T*>(g.du) + row, t0, L, o1);
         store_k<T, K, VEC>(static_cast<T*>(g.ddelta) + row, t0, L, o2);
         if constexpr (HAS_Z) {
+            float zz[K], gg[K];
+            load_k_cached<T, K, VEC>(static_cast<const T*>(p.z) + row, t0, L, zz);
+            load_k_cached<T, K, VEC>(static_cast<const T*>(g.dout) + row, t0, L, gg);
 #pragma unroll
-            for (int k = 0; k < K; ++k) o1[k] = gz[k] * y[k];
+            for (int k = 0; k < K; ++k) {
+                const float s = sigmoid_f(zz[k]);
+                o1[k] = gg[k] * s * fmaf(zz[k], 1.0f - s, 1.0f) * y[k];   // dz
+            }
             store_k<T, K, VEC>(static_cast<T*>(g.dz) + row, t0, L, o1);
         }
+        // one vector atomic per channel: lanes < N add dA[d, lane], lane N dD[d], N+1 dbias[d]
         const float sD = wave_sum_fused(dD_part);
         const float sb = wave_sum_fused(db_part);
-        if (lane == 0) {
-            if (g.dD != nullptr) unsafeAtomicAdd(g.dD + d, sD);
-            if (g.dbias != nullptr) unsafeAtomicAdd(g.dbias + d, sb);
+        float* dst = nullptr;
+        float val = 0.0f;
+        if (lane < N) {
+            dst = g.dA ? g.dA + static_cast<size_t>(d) * N + lane : nullptr;
+            val = dAv;
+        } else if (lane == N) {
+            dst = g.dD ? g.dD + d : nullptr;
+            val = sD;
+        } else if (lane == N + 1) {
+            dst = g.dbias ? g.dbias + d : nullptr;
+            val = sb;
         }
+        if (dst != nullptr) unsafeAtomicAdd(dst, val);
     }
 
     __syncthreads();
     for (int i = tid; i < N * kChunk; i += 64 * W) {
-        const int n = i / kChunk;
-        const int tt = i - n * kChunk;
+        const int nn = i / kChunk;
+        const int tt = i - nn * kChunk;
         const int t = c * kChunk + tt;
         if (t >= L) continue;
-        const int slot = (n * K + tt % K) * KP + tt / K;
+        const int slot = (nn * K + tt % K) * KP + tt / K;
         float vb = 0.0f, vc = 0.0f;
         for (int q = 0; q < groups; ++q) {
             vb += accB[q * tile + slot];
             vc += accC[q * tile + slot];
         }
-        const size_t o = (static_cast<size_t>(b) * N + n) * L + t;
+        const size_t o = (static_cast<size_t>(b) * N + nn) * L + t;
         if (g.dB != nullptr) unsafeAtomicAdd(g.dB + o, vb);
         if (g.dC != nullptr) unsafeAtomicAdd(g.dC + o, vc);
+    }
+}
+
+// B and C as fp32 rows padded with zeros to whole chunks: [B][N][nch*kChunk].
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_convert_kernel(ScanParams p, BwdWork w) {
+    const int Lp = p.nchunks * kChunk;
+    const size_t total = static_cast<size_t>(p.B) * p.N * Lp;
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+         i += stride) {
+        const size_t rown = i / Lp;
+        const int t = static_cast<int>(i - rown * Lp);
+        float vb = 0.0f, vc = 0.0f;
+        if (t < p.L) {
+            vb = Elem<T>::load1(static_cast<const T*>(p.Bm) + rown * p.L + t);
+            vc = Elem<T>::load1(static_cast<const T*>(p.Cm) + rown * p.L + t);
+        }
+        w.Bf[i] = vb;
+        w.Cf[i] = vc;
     }
 }
 
@@ -377,8 +436,9 @@ size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states) {
     const size_t nch = (static_cast<size_t>(L) + kChunk - 1) / kChunk;
     const size_t states = static_cast<size_t>(B) * D * nch * N * sizeof(float);
     const size_t per_chunk = static_cast<size_t>(B) * D * nch * sizeof(float);
+    const size_t rows = static_cast<size_t>(B) * N * nch * kChunk * sizeof(float);
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-    return (need_states ? up(states) : 0) + up(states) + 2 * up(per_chunk);
+    return 2 * up(rows) + (need_states ? up(states) : 0) + up(states) + 2 * up(per_chunk);
 }
 
 namespace {
@@ -397,6 +457,9 @@ int main_per_wave(const ScanParams& p) {
 
 template <typename T, bool VEC, bool HAS_Z, bool SP>
 hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hipStream_t s) {
+    hipLaunchKernelGGL(bwd_convert_kernel<T>, dim3(1024), dim3(256), 0, s, p, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const int rows = p.B * p.D * p.nchunks;
     dim3 sgrid((rows + kSumWaves - 1) / kSumWaves), sblock(64 * kSumWaves);
     if (w.want_fwd)
@@ -405,7 +468,7 @@ hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hi
     else
         hipLaunchKernelGGL((bwd_summary_kernel<T, VEC, HAS_Z, SP, false>), sgrid, sblock, 0, s, p,
                            g, w);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int links = p.B * p.D * p.N;
     dim3 lgrid((links + 255) / 256), lblock(256);
@@ -460,9 +523,14 @@ hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float
     const size_t nch = static_cast<size_t>(p.nchunks);
     const size_t states = static_cast<size_t>(p.B) * p.D * nch * p.N * sizeof(float);
     const size_t per_chunk = static_cast<size_t>(p.B) * p.D * nch * sizeof(float);
+    const size_t rows = static_cast<size_t>(p.B) * p.N * nch * kChunk * sizeof(float);
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     char* ws = static_cast<char*>(workspace);
     BwdWork w;
+    w.Bf = reinterpret_cast<float*>(ws);
+    ws += up(rows);
+    w.Cf = reinterpret_cast<float*>(ws);
+    ws += up(rows);
     w.want_fwd = chunk_states == nullptr;
     if (w.want_fwd) {
         w.H = reinterpret_cast<float*>(ws);
