@@ -26,19 +26,54 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-VALU_PEAK_TOPS = 39.32         # 256 CUs x 64 fp32 lanes/clk x 2.4 GHz, in 1e12 lane-ops/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector: 256 CUs x 256 flop/clk x 2.4 GHz
 METRIC = "selective-scan fwd/bwd tokens·channels/s and achieved HBM GB/s (% of peak)"
+# fp32 flops per (batch, channel, time, state) update, FMA = 2, exp2 = 1 (the arithmetic of
+# the recurrence itself; the parallel scan's replay and combine steps are not counted)
+FLOPS_FWD = 7      # Delta*A, exp2, (Delta u)*B, h = a h + p, y += C h
+FLOPS_BWD = 20     # recompute h (5), adjoint (3), g = lam h a (2), dA, dDelta, du, dB, dC (10)
+FLOPS_BWD_Z = 2    # y += C h, rebuilt for dz when there is a gate
+TRAFFIC_FILE = "profiles/bwd_main_kernel_d768x2_bf16_traffic.txt"
 
 
 def algorithmic_bytes(w, nchunks):
+    """Bytes each pass must move at least once between HBM and the chip."""
     s = 2 if w.dtype == "bf16" else 4
     tc = w.batch * w.dim * w.seqlen
     bnl = w.batch * w.dstate * w.seqlen
+    states = w.batch * w.dim * nchunks * w.dstate * 4
     dn, d = w.dim * w.dstate, w.dim
-    fwd = 4 * tc * s + 2 * bnl * s + w.batch * w.dim * w.dstate * 4 + dn * 4 + 2 * d * 4
-    cc = 2 * tc * s + bnl * s + w.batch * w.dim * nchunks * w.dstate * 4 + dn * 4 + d * 4
+    fwd = 4 * tc * s + 2 * bnl * s + states + w.batch * w.dim * w.dstate * 4 + dn * 4 + 2 * d * 4
+    cc = 2 * tc * s + bnl * s + states + dn * 4 + d * 4
+    # the gradient kernel: u, delta, dout, z in; du, ddelta, dz out; fp32 B, C in; dB, dC out;
+    # chunk-start states and adjoint carries in; A, D, bias in; dA, dD, dbias out
+    bwd_main = 7 * tc * s + 2 * bnl * 4 + 2 * bnl * 4 + 2 * states + 2 * (dn + 2 * d) * 4
+    # the whole msel_scan_bwd call adds the fp32 copies of B and C (bf16 in, fp32 out) and
+    # the summary pass, whose inputs are the same tensors
     bwd = 7 * tc * s + 2 * bnl * s + 2 * bnl * 4 + 2 * dn * 4 + 4 * d * 4
-    return {"fwd": fwd, "chunk_carry": cc, "bwd": bwd}
+    return {"fwd": fwd, "chunk_carry": cc, "bwd_main": bwd_main, "bwd": bwd}
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch of the gradient kernel from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None when there is none for this workload or the kernel's sources
+    have changed since the counters were taken."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    from selective_state_space_26_amd.profsum import source_digest
+    if kv.get("workload") != workload_name or kv.get("source_sha256") != source_digest():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -48,8 +83,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-channels", type=int, default=192,
-                    help="channels per batch row in the CPU-baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle over the whole workload for at least this long")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before the steps, copy a buffer of this many MiB once (a plain copy "
+                         "kernel of known size that scales the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -82,13 +120,28 @@ def main():
     d = {k: put(v, act if k in ("u", "delta", "z", "B", "C", "dout") else torch.float32)
          for k, v in t.items()}
     nch = msel.num_chunks(w.seqlen)
-    names = ("fwd", "bwd")
     ws = torch.empty(msel.bwd_workspace_bytes(d["u"], d["A"], True), device=dev,
                      dtype=torch.uint8)
 
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def new_events(k):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+        for e in ev:   # the library records the gradient-kernel events itself: create them
+            e.record()
+        return ev
+
     def step(ev=None):
         """fwd (out, final state, one state per chunk) then bwd, which recomputes every state
-        inside the chunks and runs the chunk carry backward for the adjoint."""
+        inside the chunks and runs the chunk carry backward for the adjoint.  All launches go
+        to torch's current stream, on which the events are recorded."""
         if ev is not None:
             ev[0].record()
         out, fin, cs = msel.msel_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],
@@ -96,7 +149,8 @@ def main():
         if ev is not None:
             ev[1].record()
         g = msel.msel_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dout"], d["D"],
-                               d["z"], d["bias"], True, chunk_states=cs, workspace=ws)
+                               d["z"], d["bias"], True, chunk_states=cs, workspace=ws,
+                               main_events=None if ev is None else (ev[3], ev[4]))
         if ev is not None:
             ev[2].record()
         return out, fin, g
@@ -104,7 +158,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [new_events(5) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -112,10 +166,14 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    per = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
-           for i, n in enumerate(names)}
+    per = {
+        "fwd": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+        "bwd": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+        "bwd_main": float(np.mean([e[3].elapsed_time(e[4]) for e in evs])),
+    }
 
     tc = w.batch * w.dim * w.seqlen
+    upd = tc * w.dstate
     alg = algorithmic_bytes(w, nch)
     # the standalone chunk-carry pass, timed on its own after the steps
     cc_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -127,22 +185,43 @@ def main():
     cc_ev[1].record()
     torch.cuda.synchronize()
     per["chunk_carry"] = cc_ev[0].elapsed_time(cc_ev[1]) / args.steps
+
+    fl_bwd = FLOPS_BWD + (FLOPS_BWD_Z if d.get("z") is not None else 0)
+    flops = {"fwd": FLOPS_FWD * upd, "bwd_main": fl_bwd * upd}
     kernels = {}
-    for n in ("fwd", "chunk_carry", "bwd"):
-        gbs = alg[n] / (per[n] * 1e-3) / 1e9
+    for n in ("fwd", "chunk_carry", "bwd_main", "bwd"):
+        sec = per[n] * 1e-3
+        gbs = alg[n] / sec / 1e9
         kernels[n] = {"ms": round(per[n], 4), "alg_bytes": alg[n], "GB/s": round(gbs, 1),
                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                      "tc_per_s": float(f"{tc / (per[n] * 1e-3):.4g}")}
-    kernels["bwd"]["note"] = ("msel_scan_bwd call: convert + summary + link + main kernels and "
-                              "zero-fills")
-    dom = max(names, key=lambda n: per[n])
-    ach = alg[dom] / (per[dom] * 1e-3) / 1e9
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                      "tc_per_s": float(f"{tc / sec:.4g}")}
+        if n in flops:
+            kernels[n]["TFLOP/s"] = round(flops[n] / sec / 1e12, 2)
+    kernels["fwd"]["what"] = "scan_fwd_kernel (one launch)"
+    kernels["chunk_carry"]["what"] = "chunk_carry_kernel (one launch), timed apart from the step"
+    kernels["bwd_main"]["what"] = "bwd_main_kernel, the chunk-parallel gradient kernel"
+    kernels["bwd"]["what"] = ("the msel_scan_bwd call: zero-fills, convert, summary, link and "
+                              "bwd_main_kernel")
+
+    # the dominant kernel: the gradient kernel, bound by VALU arithmetic (an exp2 per update
+    # and ~20 flops), measured with the library's events on the launch stream
+    sec = per["bwd_main"] * 1e-3
+    ach = flops["bwd_main"] / sec / 1e12
+    roofline = {
+        "kernel": "bwd_main_kernel", "bound": "alu", "achieved": round(ach, 2),
+        "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(ach / FP32_VECTOR_PEAK_TFLOPS, 4),
+        "traffic": measured_traffic(w.name),
+        "flops_per_launch": flops["bwd_main"],
+        "flops_per_update": fl_bwd, "updates_per_launch": upd,
+        "alg_bytes_per_launch": alg["bwd_main"],
+        "hbm_GBs": kernels["bwd_main"]["GB/s"], "hbm_frac": kernels["bwd_main"]["hbm_frac"],
+        "ms_per_launch": round(per["bwd_main"], 4),
+    }
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(w, t, args.cpu_channels)
+        cpu = cpu_baseline(w, t, args.cpu_seconds)
 
     line = {
         "metric": METRIC, "value": float(f"{tc / (ms_per_step * 1e-3):.5g}"),
@@ -156,29 +235,26 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, t, channels):
-    """The fp64 oracle, as it stands, on the first `channels` channels of every batch row:
-    forward + backward, timed on this host's cores."""
-    import numpy as np
-
+def cpu_baseline(w, t, min_seconds):
+    """The fp64 oracle, as it stands: forward then backward over the whole workload, repeated
+    until at least `min_seconds` have passed, on at most 16 of this host's cores."""
     import oracle
-    ch = min(channels, w.dim)
     v = {k: (None if t.get(k) is None else t.values(k)) for k in t}
-    sl = lambda x: None if x is None else np.ascontiguousarray(x[:, :ch])
-    sub = dict(u=sl(v["u"]), delta=sl(v["delta"]), z=sl(v["z"]), dout=sl(v["dout"]),
-               A=v["A"][:ch], D=v["D"][:ch], bias=v["bias"][:ch], B=v["B"], C=v["C"])
-    nthreads = oracle.default_threads()
+    nthreads = min(16, oracle.default_threads())
+    reps, el = 0, 0.0
     s = time.perf_counter()
-    oracle.fwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"],
-               sub["bias"], nthreads=nthreads)
-    oracle.bwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["dout"], sub["D"],
-               sub["z"], sub["bias"], nthreads=nthreads)
-    el = time.perf_counter() - s
-    tcs = w.batch * ch * w.seqlen
+    while el < min_seconds:
+        oracle.fwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"], v["bias"],
+                   nthreads=nthreads)
+        oracle.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
+                   v["bias"], nthreads=nthreads)
+        reps += 1
+        el = time.perf_counter() - s
+    tcs = reps * w.batch * w.dim * w.seqlen
     return {"value": float(f"{tcs / el:.4g}"), "unit": "token*channels/s", "cores": nthreads,
             "kind": "oracle", "seconds": round(el, 3),
-            "sample": f"fwd+bwd (chunk states recomputed inside the loop) on channels 0..{ch - 1}"
-                      f" of all {w.batch} batch rows, full seqlen {w.seqlen}"}
+            "sample": f"{reps} x (fwd + bwd) over the whole workload: all {w.batch} batch rows, "
+                      f"{w.dim} channels, seqlen {w.seqlen}, fp64"}
 
 
 if __name__ == "__main__":

@@ -52,8 +52,9 @@
 extern "C" {
 #endif
 
-/* hipStream_t, declared the same way the HIP runtime declares it. */
+/* hipStream_t and hipEvent_t, declared the same way the HIP runtime declares them. */
 typedef struct ihipStream_t *hipStream_t;
+typedef struct ihipEvent_t *hipEvent_t;
 
 #define MSEL_ABI_VERSION 1
 
@@ -162,6 +163,15 @@ size_t msel_scan_bwd_workspace_bytes(const msel_scan_args *args);
  * are deterministic. */
 msel_status msel_scan_bwd(const msel_scan_args *args, const msel_scan_grads *grads,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* msel_scan_bwd for profiling: the same launches and results, and in addition the caller's
+ * events ev_begin and ev_end (hipEvent_t created by the caller; either may be NULL) are
+ * recorded on `stream` immediately before and after the chunk-parallel gradient kernel, the
+ * longest of the backward's launches, so that it can be timed on the stream it runs on.  A
+ * failed event record returns MSEL_ERR_HIP. */
+msel_status msel_scan_bwd_profiled(const msel_scan_args *args, const msel_scan_grads *grads,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                   hipEvent_t ev_begin, hipEvent_t ev_end);
 
 #ifdef __cplusplus
 }

@@ -45,7 +45,7 @@ _lib = None
 EXPORTS = ["msel_abi_version", "msel_chunk_len", "msel_num_chunks", "msel_status_string",
            "msel_validate_fwd", "msel_validate_chunk_carry", "msel_validate_bwd",
            "msel_scan_fwd", "msel_scan_chunk_carry", "msel_scan_bwd_workspace_bytes",
-           "msel_scan_bwd"]
+           "msel_scan_bwd", "msel_scan_bwd_profiled"]
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
@@ -80,6 +80,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.msel_scan_bwd_workspace_bytes.argtypes = [a]
     lib.msel_scan_bwd.restype = ctypes.c_int
     lib.msel_scan_bwd.argtypes = [a, g, _P, ctypes.c_size_t, _P]
+    lib.msel_scan_bwd_profiled.restype = ctypes.c_int
+    lib.msel_scan_bwd_profiled.argtypes = [a, g, _P, ctypes.c_size_t, _P, _P, _P]
     if lib.msel_abi_version() != ABI_VERSION:
         raise RuntimeError("libmsel.so ABI version mismatch")
     if path is None:

@@ -166,8 +166,9 @@ msel_status msel_scan_chunk_carry(const msel_scan_args* a, hipStream_t stream) {
     return hip_status(msel::launch_chunk_carry(to_params(a), a->dtype == MSEL_BF16, stream));
 }
 
-msel_status msel_scan_bwd(const msel_scan_args* a, const msel_scan_grads* g, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
+msel_status msel_scan_bwd_profiled(const msel_scan_args* a, const msel_scan_grads* g,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                   hipEvent_t ev_begin, hipEvent_t ev_end) {
     msel_status s = msel_validate_bwd(a, g, workspace, workspace_bytes);
     if (s != MSEL_OK) return s;
     const bool bf16 = a->dtype == MSEL_BF16;
@@ -192,7 +193,13 @@ msel_status msel_scan_bwd(const msel_scan_args* a, const msel_scan_grads* g, voi
     gp.dD = g->dD;
     gp.dbias = g->ddelta_bias;
     gp.dh0 = g->dh0;
-    return hip_status(msel::launch_scan_bwd(p, gp, a->chunk_states, workspace, bf16, stream));
+    return hip_status(msel::launch_scan_bwd(p, gp, a->chunk_states, workspace, bf16, stream,
+                                            ev_begin, ev_end));
+}
+
+msel_status msel_scan_bwd(const msel_scan_args* a, const msel_scan_grads* g, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    return msel_scan_bwd_profiled(a, g, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 }  // extern "C"

@@ -47,8 +47,11 @@ hipError_t launch_chunk_carry(const ScanParams& p, bool bf16, hipStream_t stream
 // Backward: the summary/link passes write into `workspace` (bwd_workspace_bytes), then the
 // chunk-parallel main kernel.  chunk_states may be NULL (rebuilt in the workspace).
 size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states);
+// ev_begin / ev_end (either may be null) are recorded on `stream` right before and after the
+// gradient kernel, so that a caller can time it alone.
 hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float* chunk_states,
-                           void* workspace, bool bf16, hipStream_t stream);
+                           void* workspace, bool bf16, hipStream_t stream,
+                           hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
 
 }  // namespace msel

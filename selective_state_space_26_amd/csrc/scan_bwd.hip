@@ -455,8 +455,13 @@ int main_per_wave(const ScanParams& p) {
     return static_cast<int>(per);
 }
 
+struct Timing {
+    hipEvent_t begin, end;
+};
+
 template <typename T, bool VEC, bool HAS_Z, bool SP>
-hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hipStream_t s) {
+hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hipStream_t s,
+                  Timing tm) {
     hipLaunchKernelGGL(bwd_convert_kernel<T>, dim3(1024), dim3(256), 0, s, p, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -490,19 +495,22 @@ hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hi
         static_cast<int>(2 * kMaxN * (kChunk / 64) * kAccKP * sizeof(float)));
     if (attr != hipSuccess) return attr;
     dim3 mgrid(cgroups, p.nchunks, p.B), mblock(64 * kMainWaves);
+    if (tm.begin != nullptr && (e = hipEventRecord(tm.begin, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_main_kernel<T, VEC, HAS_Z, SP>), mgrid, mblock, lds, s, p, g, w,
                        per_wave);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e == hipSuccess && tm.end != nullptr) e = hipEventRecord(tm.end, s);
+    return e;
 }
 
 template <typename T>
 hipError_t bwd_dispatch(const ScanParams& p, const GradParams& g, const BwdWork& w,
-                        hipStream_t s) {
+                        hipStream_t s, Timing tm) {
     const bool vec = (static_cast<size_t>(p.L) * sizeof(T)) % 16 == 0;
     const bool hz = p.z != nullptr;
     const bool sp = p.softplus != 0;
 #define MSEL_BWD(V, Z, S) \
-    if (vec == V && hz == Z && sp == S) return bwd_go<T, V, Z, S>(p, g, w, s);
+    if (vec == V && hz == Z && sp == S) return bwd_go<T, V, Z, S>(p, g, w, s, tm);
     MSEL_BWD(true, true, true)
     MSEL_BWD(true, true, false)
     MSEL_BWD(true, false, true)
@@ -518,7 +526,8 @@ hipError_t bwd_dispatch(const ScanParams& p, const GradParams& g, const BwdWork&
 }  // namespace
 
 hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float* chunk_states,
-                           void* workspace, bool bf16, hipStream_t stream) {
+                           void* workspace, bool bf16, hipStream_t stream, hipEvent_t ev_begin,
+                           hipEvent_t ev_end) {
     if (p.N > kMaxN) return hipErrorInvalidValue;
     const size_t nch = static_cast<size_t>(p.nchunks);
     const size_t states = static_cast<size_t>(p.B) * p.D * nch * p.N * sizeof(float);
@@ -543,8 +552,9 @@ hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float
     w.sdt = reinterpret_cast<float*>(ws);
     ws += up(per_chunk);
     w.dfirst = reinterpret_cast<float*>(ws);
-    if (bf16) return bwd_dispatch<bf16_t>(p, g, w, stream);
-    return bwd_dispatch<float>(p, g, w, stream);
+    const Timing tm{ev_begin, ev_end};
+    if (bf16) return bwd_dispatch<bf16_t>(p, g, w, stream, tm);
+    return bwd_dispatch<float>(p, g, w, stream, tm);
 }
 
 }  // namespace msel

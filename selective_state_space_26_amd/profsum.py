@@ -1,0 +1,141 @@
+"""Summaries of rocprofv3 output for the scan kernels (part of the measurement harness).
+
+    python -m selective_state_space_26_amd.profsum stats KERNEL_STATS_CSV OUT.md --command "..."
+    python -m selective_state_space_26_amd.profsum traffic FETCH_CSV WRITE_CSV OUT.txt \\
+        --kernel bwd_main_kernel --copy-mib 512 --workload NAME --command-fetch "..." \\
+        --command-write "..."
+
+`stats` turns a `--kernel-trace --stats` kernel_stats.csv into a short markdown table.
+
+`traffic` reads two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` counter_collection.csv files (KiB
+per dispatch), takes the largest `copyBuffer` dispatch of the run (a plain device-to-device
+copy of --copy-mib MiB that the bench makes before its steps) as the calibration of each
+counter, and writes the HBM bytes per launch of --kernel: counter KiB x 1024 x (copy bytes /
+copy counter bytes).  The file records the SHA-256 of the kernel's sources, so that readers
+can tell when the counters no longer describe the code.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BWD_SOURCES = ("selective_state_space_26_amd/csrc/scan_bwd.hip",
+               "selective_state_space_26_amd/csrc/msel_device.hpp",
+               "selective_state_space_26_amd/csrc/msel_kernels.hpp")
+
+
+def source_digest(files=BWD_SOURCES) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def short_name(name: str) -> str:
+    n = name
+    if n.startswith("void "):
+        n = n[5:]
+    return n.split("(")[0]
+
+
+def stats(csv_path: str, out: str, command: str) -> None:
+    rows = list(csv.DictReader(open(csv_path)))
+    lines = [f"# rocprofv3 kernel statistics: {os.path.basename(out)}", "",
+             "Command (from the repository root on the GPU host):", "", "```", command, "```",
+             "", "| kernel | calls | avg us | min us | max us | % of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        lines.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(csv_path: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter (rows summed per dispatch)."""
+    by = defaultdict(float)
+    names = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        key = r["Dispatch_Id"]
+        by[key] += float(r["Counter_Value"])
+        names[key] = r["Kernel_Name"]
+    out = defaultdict(list)
+    for k, v in by.items():
+        out[names[k]].append(v)
+    return out
+
+
+def traffic(fetch_csv, write_csv, out, kernel, copy_mib, workload, cmd_fetch, cmd_write):
+    copy_bytes = copy_mib * (1 << 20)
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        d = _per_dispatch(path, counter)
+        copies = [v for name, vs in d.items() if "copyBuffer" in name for v in vs]
+        if not copies:
+            raise SystemExit(f"no copyBuffer dispatch in {path}")
+        cal_kib = max(copies)
+        factor = copy_bytes / (cal_kib * 1024.0)
+        mine = [v for name, vs in d.items() if kernel in name for v in vs]
+        if not mine:
+            raise SystemExit(f"no {kernel} dispatch in {path}")
+        kib = statistics.mean(mine)
+        res[counter] = dict(kib=kib, n=len(mine), cal_kib=cal_kib, factor=factor,
+                            bytes=kib * 1024.0 * factor)
+    total = res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"]
+    lines = [
+        f"# HBM traffic of {kernel} on workload {workload}, from two rocprofv3 --pmc passes",
+        f"# fetch pass: {cmd_fetch}",
+        f"# write pass: {cmd_write}",
+        "# counter KiB are per dispatch (mean over the dispatches of the kernel); each counter",
+        f"# is scaled by a plain {copy_mib} MiB device copy read by the same counter",
+        f"workload = {workload}",
+        f"kernel = {kernel}",
+        f"source_sha256 = {source_digest()}",
+    ]
+    for c, r in res.items():
+        lc = c.lower()
+        lines += [f"{lc}_kib_per_dispatch = {r['kib']:.1f}",
+                  f"{lc}_dispatches = {r['n']}",
+                  f"{lc}_copy_kib = {r['cal_kib']:.1f}",
+                  f"{lc}_copy_factor = {r['factor']:.4f}",
+                  f"{lc}_bytes_per_launch = {r['bytes']:.0f}"]
+    lines.append(f"traffic_bytes_per_launch = {total:.0f}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("out")
+    s.add_argument("--command", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_csv")
+    t.add_argument("write_csv")
+    t.add_argument("out")
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--command-fetch", required=True)
+    t.add_argument("--command-write", required=True)
+    a = ap.parse_args()
+    if a.cmd == "stats":
+        stats(a.csv, a.out, a.command)
+    else:
+        traffic(a.fetch_csv, a.write_csv, a.out, a.kernel, a.copy_mib, a.workload,
+                a.command_fetch, a.command_write)
+
+
+if __name__ == "__main__":
+    main()

@@ -149,8 +149,12 @@ def bwd_workspace_bytes(u, A, chunk_states_given=False) -> int:
 def msel_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
                   delta_softplus=True, h0=None, chunk_states=None, want_dA=True, want_dB=True,
                   want_dC=True, want_dD=True, want_ddelta_bias=True, want_dh0=False,
-                  workspace=None):
-    """Backward with recomputation.  Returns a dict of gradients (absent ones are None)."""
+                  workspace=None, main_events=None):
+    """Backward with recomputation.  Returns a dict of gradients (absent ones are None).
+
+    main_events: optional pair of torch.cuda.Event (enable_timing=True) that the library
+    records on the current stream right before and after its gradient kernel
+    (msel_scan_bwd_profiled); each must have been recorded once already so that it exists."""
     a, (bsz, dim, N, L) = _args(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
     dev, dt = u.device, u.dtype
     _need(dout, "dout", (bsz, dim, L), dt, dev)
@@ -177,6 +181,14 @@ def msel_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     ws_ptr = _ptr(workspace) if need > 0 else None
     ws_bytes = workspace.numel() * workspace.element_size() if need > 0 else 0
-    _lib.check("msel_scan_bwd", lib.msel_scan_bwd(ctypes.byref(a), ctypes.byref(g), ws_ptr,
-                                                  ws_bytes, _stream(dev)))
+    if main_events is None:
+        _lib.check("msel_scan_bwd", lib.msel_scan_bwd(ctypes.byref(a), ctypes.byref(g), ws_ptr,
+                                                      ws_bytes, _stream(dev)))
+    else:
+        ev = [ctypes.c_void_p(e.cuda_event) for e in main_events]
+        if not all(e.value for e in ev):
+            raise ValueError("main_events must have been recorded once before use")
+        _lib.check("msel_scan_bwd_profiled",
+                   lib.msel_scan_bwd_profiled(ctypes.byref(a), ctypes.byref(g), ws_ptr, ws_bytes,
+                                              _stream(dev), ev[0], ev[1]))
     return r

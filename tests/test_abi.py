@@ -129,6 +129,7 @@ def test_null_args_pointer(lib):
     assert lib.msel_scan_fwd(None, None) == 1
     assert lib.msel_scan_chunk_carry(None, None) == 1
     assert lib.msel_scan_bwd(None, None, None, 0, None) == 1
+    assert lib.msel_scan_bwd_profiled(None, None, None, 0, None, None, None) == 1
     assert lib.msel_scan_bwd_workspace_bytes(None) == 0
 
 
@@ -195,6 +196,8 @@ def test_bwd_workspace_rules(lib):
     assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), ws, need) == 0
     assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), ws + 16, need) == 4
     assert lib.msel_scan_bwd(ctypes.byref(a), ctypes.byref(g), None, 0, None) == 6
+    assert lib.msel_scan_bwd_profiled(ctypes.byref(a), ctypes.byref(g), None, 0, None, None,
+                                      None) == 6
     # with caller-provided chunk states the workspace only holds the adjoint carries
     a.chunk_states = _addr()
     need2 = lib.msel_scan_bwd_workspace_bytes(ctypes.byref(a))

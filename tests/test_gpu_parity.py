@@ -229,3 +229,27 @@ def test_binding_rejects_bad_inputs_before_launch():
         msel.msel_scan_fwd(x, x, torch.zeros(2, 17, device="cuda"),
                            torch.zeros(1, 17, 8, device="cuda"),
                            torch.zeros(1, 17, 8, device="cuda"))
+
+
+def test_bwd_profiled_matches_bwd_and_times_the_gradient_kernel():
+    """msel_scan_bwd_profiled gives the same deterministic gradients as msel_scan_bwd and its
+    events bracket a non-empty stretch of the stream."""
+    log("bwd profiled")
+    t = _case_inputs(2, 6, 16, 1100, "f32", True, True, True, True, dout=True)
+    dv = to_device(t)
+    args = (dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["dout"], dv["D"], dv["z"],
+            dv["bias"], True, dv["h0"])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in ev:
+        e.record()
+    a = msel.msel_scan_bwd(*args, want_dh0=True)
+    b = msel.msel_scan_bwd(*args, want_dh0=True, main_events=ev)
+    torch.cuda.synchronize()
+    for k in ("du", "ddelta", "dz", "dh0"):
+        assert torch.equal(a[k], b[k]), k
+    v = oracle_vals(t)
+    r = oracle.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
+                   v["bias"], v["h0"])
+    for k in ("dA", "dB", "dC", "dD", "ddelta_bias"):
+        assert_close(k, host(b[k]), r[k], "f32")
+    assert ev[0].elapsed_time(ev[1]) > 0.0
