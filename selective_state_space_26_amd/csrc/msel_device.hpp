@@ -393,6 +393,51 @@ __device__ __forceinline__ void scan_rev_fused(float& P, float& S) {
     }
 }
 
+// The forward scan of (P, S) and the row levels of the suffix scan of (Pr, Sr) in one
+// instruction stream.  The two are independent, so each one's DPP reads come at least two
+// instructions after the other's writes and the row levels need no wait states; only the two
+// cross-row levels of the forward scan keep theirs.  On return (P, S) is the full inclusive
+// scan over the wave and (Pr, Sr) the suffix scan within each 16-lane row (finish it with
+// rev_rows_apply).
+__device__ __forceinline__ void scan_fwd_and_rev_rows(float& P, float& S, float& Pr, float& Sr) {
+#define MSEL_PAIR_LEVEL(CF, CR)                                                         \
+    "v_fmac_f32_dpp %[S], %[S], %[P] " CF " row_mask:0xf bank_mask:0xf\n"              \
+    "v_mul_f32_dpp %[P], %[P], %[P] " CF " row_mask:0xf bank_mask:0xf\n"               \
+    "v_fmac_f32_dpp %[Sr], %[Sr], %[Pr] " CR " row_mask:0xf bank_mask:0xf\n"           \
+    "v_mul_f32_dpp %[Pr], %[Pr], %[Pr] " CR " row_mask:0xf bank_mask:0xf\n"
+    asm volatile("s_nop 1\n"
+                 MSEL_PAIR_LEVEL("row_shr:1", "row_shl:1")
+                 MSEL_PAIR_LEVEL("row_shr:2", "row_shl:2")
+                 MSEL_PAIR_LEVEL("row_shr:4", "row_shl:4")
+                 MSEL_PAIR_LEVEL("row_shr:8", "row_shl:8")
+                 MSEL_FWD_LEVEL("row_bcast:15", "0xa")
+                 MSEL_FWD_LEVEL("row_bcast:31", "0xc")
+                 : [P] "+v"(P), [S] "+v"(S), [Pr] "+v"(Pr), [Sr] "+v"(Sr));
+#undef MSEL_PAIR_LEVEL
+}
+
+// Finishes a suffix scan whose row levels are done: (P, S) of lane l compose lanes l..15 of
+// its row.  `carry` is the value entering from beyond lane 63 (wave-uniform).  Returns, in
+// every lane, the suffix composition of lanes l..63 applied to `carry`:
+//   V_l = S_l + P_l R(row),  R(3) = carry,  R(r) = S_{16(r+1)} + P_{16(r+1)} R(r+1),
+// read from the first lane of each following row (no LDS round trip).
+__device__ __forceinline__ float rev_rows_apply(float P, float S, float carry) {
+    const float R3 = carry;
+    const float R2 = fmaf(readlane(P, 48), R3, readlane(S, 48));
+    const float R1 = fmaf(readlane(P, 32), R2, readlane(S, 32));
+    const float R0 = fmaf(readlane(P, 16), R1, readlane(S, 16));
+    const int row = lane_id() >> 4;
+    const float R = row == 0 ? R0 : (row == 1 ? R1 : (row == 2 ? R2 : R3));
+    return fmaf(P, R, S);
+}
+
+// Sum over each group of four consecutive lanes (every lane of the group gets it).
+__device__ __forceinline__ float quad_sum(float v) {
+    v += dpp<0xB1, 0xf>(0.0f, v);  // quad_perm [1,0,3,2]
+    v += dpp<0x4E, 0xf>(0.0f, v);  // quad_perm [2,3,0,1]
+    return v;
+}
+
 // Lane l gets v of lane l-1; lane 0 gets `first`.
 __device__ __forceinline__ float shift_up(float v, float first) {
     float r = first;

@@ -174,12 +174,25 @@ __global__ __launch_bounds__(256) void bwd_link_kernel(ScanParams p, GradParams 
     if (g.dh0 != nullptr) g.dh0[static_cast<size_t>(ch) * N + n] = G;
 }
 
-// LDS accumulator layout of the main kernel: [group][n][k][65] floats per tensor, where the
-// padded stride 65 keeps both the per-lane updates (consecutive lanes) and the flush
-// (consecutive time steps) free of bank conflicts.
+// LDS layout of the main kernel:
+//  * dB and dC accumulators [2 tensors][group][n][k][65] floats: the padded stride 65 keeps
+//    both the per-lane updates (consecutive lanes) and the flush (consecutive time steps)
+//    free of bank conflicts;
+//  * per-wave dA partials [wave][n][68]: one row of 64 lane partials per state, summed once
+//    per channel;
+//  * (static) one int per (group, state): 1 + the global step of the last completed update
+//    of that state's accumulator rows (see the ring protocol in the kernel).
 constexpr int kAccKP = 65;
+constexpr int kDaStride = 68;
+constexpr int kMaxRingFlags = 32;  // groups * N <= W + N - 1
 
 __host__ __device__ constexpr int acc_groups(int N, int W) { return (W + N - 1) / N; }
+
+__host__ __device__ constexpr size_t main_lds_bytes(int N, int W) {
+    return (2 * static_cast<size_t>(acc_groups(N, W)) * N * (kChunk / 64) * kAccKP +
+            static_cast<size_t>(W) * N * kDaStride) * sizeof(float);
+}
+static_assert(kMainWaves + kMaxN - 1 <= kMaxRingFlags, "ring flags do not fit");
 
 template <typename T, bool VEC, bool HAS_Z, bool SOFTPLUS>
 __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p, GradParams g,
@@ -187,7 +200,7 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
     constexpr int K = kChunk / 64;
     constexpr int W = kMainWaves;
     constexpr int KP = kAccKP;
-    extern __shared__ float acc[];  // [2 tensors][groups][N][K][KP]
+    extern __shared__ float acc[];
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -202,13 +215,27 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
     const int tile = N * K * KP;             // floats per (tensor, group)
     float* accB = acc;
     float* accC = acc + groups * tile;
+    float* dAs = acc + 2 * groups * tile + wave * N * kDaStride;  // this wave's dA rows
+    __shared__ int ring_flags[kMaxRingFlags];
     for (int i = tid; i < 2 * groups * tile; i += 64 * W) acc[i] = 0.0f;
+    for (int i = tid; i < groups * N; i += 64 * W) ring_flags[i] = 0;
+    __syncthreads();
 
-    // Wave w updates state (j + w) mod N of its group's tiles at step j, so within a step
-    // every accumulator slot has a single writer; the barrier in each step orders the
-    // read-add-writes of consecutive steps.
+    // Ring protocol for the shared accumulator rows.  The waves of a group take the states in
+    // rotated order: at global step g (= channel round * N + step) wave `rot` updates state
+    // (rot + g) mod N.  The previous update of that state was made kp steps earlier by wave
+    // (rot + kp) mod N, kp = 1 unless rot is the group's last wave (then kp = N - rot, the
+    // wrap to wave 0).  So each wave waits only for its ring successor's previous step, not
+    // for the whole workgroup: a wave publishes the step it finished in its state's flag and
+    // the next writer of that state spins on it.  Every wave runs every step (inactive ones
+    // only publish), the chain ends at step 0, and all waves of the workgroup are resident,
+    // so the waits always end.
     const int grp = wave / N;
     const int rot = wave - grp * N;
+    const int Wg = (W - grp * N < N) ? W - grp * N : N;  // waves sharing this group's rows
+    const int kp = (rot + 1 < Wg) ? 1 : N - rot;
+    int* gflags = ring_flags + grp * N;
+    int gstep = 0;
     float* myB = accB + grp * tile;
     float* myC = accC + grp * tile;
 
@@ -218,7 +245,7 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
 
     for (int r = 0; r < per_wave; ++r) {
         const int d = (blockIdx.x * per_wave + r) * W + wave;
-        const bool active = d < p.D;  // wave-uniform; inactive waves still join the barriers
+        const bool active = d < p.D;  // wave-uniform; inactive waves still run the protocol
         const size_t ch = static_cast<size_t>(b) * p.D + (active ? d : 0);
         const size_t row = ch * L;
         const int dd_ = active ? d : 0;
@@ -239,12 +266,13 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
         float y[HAS_Z ? K : 1];
         float sum_dt = 0.0f, dD_part = 0.0f;
         {
+            // cached loads: the same rows are read again after the state loop
             float uu[K], dd[K], gg[K];
-            load_k<T, K, VEC>(static_cast<const T*>(p.u) + row, t0, L, uu, 0.0f);
-            load_k<T, K, VEC>(static_cast<const T*>(p.delta) + row, t0, L, dd, 0.0f);
-            load_k<T, K, VEC>(static_cast<const T*>(g.dout) + row, t0, L, gg, 0.0f);
+            load_k_cached<T, K, VEC>(static_cast<const T*>(p.u) + row, t0, L, uu);
+            load_k_cached<T, K, VEC>(static_cast<const T*>(p.delta) + row, t0, L, dd);
+            load_k_cached<T, K, VEC>(static_cast<const T*>(g.dout) + row, t0, L, gg);
             float zz[HAS_Z ? K : 1];
-            if constexpr (HAS_Z) load_k<T, K, VEC>(static_cast<const T*>(p.z) + row, t0, L, zz, 0.0f);
+            if constexpr (HAS_Z) load_k_cached<T, K, VEC>(static_cast<const T*>(p.z) + row, t0, L, zz);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float x = dd[k] + bias;
@@ -263,8 +291,9 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
                 sgA[k] = 0.0f;
             }
         }
-        const float dt_next = shift_down(dt[0], 0.0f);
-        float dAv = 0.0f;  // lane n: dA[d, n] contribution of this (batch row, chunk)
+        // sum of Delta over the steps whose a multiplies the adjoint inside this lane:
+        // a_{t+1} for t in the lane, i.e. this lane's steps 1..K-1 and the next lane's first
+        const float rsum_dt = sum_dt - dt[0] + shift_down(dt[0], 0.0f);
 
         for (int j = 0; j < N; ++j) {
             float bv[K], cv[K];
@@ -276,64 +305,85 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
                 load_raw<float, K, true>(Bb + static_cast<size_t>(n) * Lp, t0, Lp, Bn);
                 load_raw<float, K, true>(Cb + static_cast<size_t>(n) * Lp, t0, Lp, Cn);
             }
-            __syncthreads();
-            if (!active) continue;
+            // wait until the previous update of state nc (step gstep - kp) is complete
+            const int need = gstep - kp + 1;
+            if (need > 0) {
+                while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                           gflags + nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < need)
+                    __builtin_amdgcn_s_sleep(1);
+            }
+            asm volatile("" ::: "memory");
+            if (active) {
+            // this step's accumulator slots: each tensor's reads are issued together, ahead of
+            // their use, and written back as soon as its pass is done
+            float* sBn = myB + nc * K * KP + lane;
+            float* sCn = myC + nc * K * KP + lane;
+            float oc[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) oc[k] = sCn[k * KP];
             const float An = readlane(Av, nc);
             const float An2 = An * kLog2e;
             const float Hn = readlane(Hv, nc);
             const float Gn = readlane(Gv, nc);
-            // states inside the chunk, rebuilt from H_c
-            float a[K], hs[K];
+            // lane-local chains: states from a zero start, adjoint from a zero end
+            float a[K], bb[K], cd[K];
             float h = 0.0f;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 a[k] = exp2_hw(dt[k] * An2);
-                h = fmaf(a[k], h, dtu[k] * bv[k]);
+                bb[k] = dtu[k] * bv[k];
+                h = fmaf(a[k], h, bb[k]);
+                cd[k] = cv[k] * dy[k];
             }
-            float P = exp2_hw(An2 * sum_dt);
-            float S = h;
-            scan_fwd_fused(P, S);
-            const float hin = shift_up(fmaf(P, Hn, S), Hn);
-            h = hin;
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                h = fmaf(a[k], h, dtu[k] * bv[k]);
-                hs[k] = h;
-                if constexpr (HAS_Z) y[k] = fmaf(cv[k], h, y[k]);
-            }
-            // adjoint inside the chunk, rebuilt from G_c: lam_t = C_t dy_t + e_t lam_{t+1},
-            // e_t = a_{t+1}; lane 63's last step takes e = 1 and the carry G_c.
             const float a_next = shift_down(a[0], 1.0f);
             float rr = 0.0f;
 #pragma unroll
-            for (int k = K - 1; k >= 0; --k) {
-                const float e = (k == K - 1) ? a_next : a[k + 1];
-                rr = fmaf(e, rr, cv[k] * dy[k]);
+            for (int k = K - 1; k >= 0; --k) rr = fmaf((k == K - 1) ? a_next : a[k + 1], rr, cd[k]);
+            float P = exp2_hw(An2 * sum_dt), S = h;
+            float Pr = exp2_hw(An2 * rsum_dt), Sr = rr;
+            scan_fwd_and_rev_rows(P, S, Pr, Sr);
+            // state entering the lane (from H_c) and adjoint entering it from the right (G_c)
+            const float hin = shift_up(fmaf(P, Hn, S), Hn);
+            float lam = shift_down(rev_rows_apply(Pr, Sr, Gn), Gn);
+            float hs[K];
+            h = hin;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                h = fmaf(a[k], h, bb[k]);
+                hs[k] = h;
+                if constexpr (HAS_Z) y[k] = fmaf(cv[k], h, y[k]);
+                oc[k] = fmaf(dy[k], h, oc[k]);
             }
-            float Pr = exp2_hw(An2 * (sum_dt - dt[0] + dt_next));
-            float Sr = rr;
-            scan_rev_fused(Pr, Sr);
-            float lam = shift_down(fmaf(Pr, Gn, Sr), Gn);
+            float ob[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                sCn[k * KP] = oc[k];
+                ob[k] = sBn[k * KP];
+            }
             float dA_part = 0.0f;
-            float* sBn = myB + nc * K * KP + lane;
-            float* sCn = myC + nc * K * KP + lane;
 #pragma unroll
             for (int k = K - 1; k >= 0; --k) {
-                const float e = (k == K - 1) ? a_next : a[k + 1];
-                lam = fmaf(e, lam, cv[k] * dy[k]);
+                lam = fmaf((k == K - 1) ? a_next : a[k + 1], lam, cd[k]);
                 const float hprev = (k == 0) ? hin : hs[k - 1];
                 const float gk = lam * hprev * a[k];
                 dA_part = fmaf(gk, dt[k], dA_part);
                 sgA[k] = fmaf(gk, An, sgA[k]);
                 sB[k] = fmaf(lam, bv[k], sB[k]);
-                sBn[k * KP] = fmaf(lam, dtu[k], sBn[k * KP]);
-                sCn[k * KP] = fmaf(dy[k], hs[k], sCn[k * KP]);
+                ob[k] = fmaf(lam, dtu[k], ob[k]);
             }
-            dAv = writelane(dAv + wave_sum_fused(dA_part), nc, dAv);
+#pragma unroll
+            for (int k = 0; k < K; ++k) sBn[k * KP] = ob[k];
+            dAs[nc * kDaStride + lane] = dA_part;
+            }
+            // publish: this step's LDS writes are complete
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __hip_atomic_store(gflags + nc, gstep + 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+            ++gstep;
         }
         if (!active) continue;
 
-        // inputs that were not kept live across the steps are reloaded (L2-resident by now)
+        // inputs that were not kept live across the steps are reloaded (L2-resident)
         float o1[K], o2[K];
         float db_part = 0.0f;
         {
@@ -361,18 +411,28 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
             }
             store_k<T, K, VEC>(static_cast<T*>(g.dz) + row, t0, L, o1);
         }
-        // one vector atomic per channel: lanes < N add dA[d, lane], lane N dD[d], N+1 dbias[d]
+        // dA[d, n]: lanes 4n..4n+3 each sum 16 of the 64 lane partials of state n, then the
+        // quad is summed; the wave's own dA rows need no barrier (same-wave LDS order)
+        const int qn = lane >> 2;
+        float sa = 0.0f;
+        if (qn < N) {
+            const float* src = dAs + qn * kDaStride + (lane & 3) * 16;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) sa += src[q];
+        }
+        sa = quad_sum(sa);
         const float sD = wave_sum_fused(dD_part);
         const float sb = wave_sum_fused(db_part);
+        // one vector atomic per channel: lane 4n adds dA[d, n], lane 1 dD[d], lane 2 dbias[d]
         float* dst = nullptr;
         float val = 0.0f;
-        if (lane < N) {
-            dst = g.dA ? g.dA + static_cast<size_t>(d) * N + lane : nullptr;
-            val = dAv;
-        } else if (lane == N) {
+        if ((lane & 3) == 0 && qn < N) {
+            dst = g.dA ? g.dA + static_cast<size_t>(d) * N + qn : nullptr;
+            val = sa;
+        } else if (lane == 1) {
             dst = g.dD ? g.dD + d : nullptr;
             val = sD;
-        } else if (lane == N + 1) {
+        } else if (lane == 2) {
             dst = g.dbias ? g.dbias + d : nullptr;
             val = sb;
         }
@@ -485,14 +545,12 @@ hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hi
     if (e != hipSuccess) return e;
     const int per_wave = main_per_wave(p);
     const int cgroups = (p.D + per_wave * kMainWaves - 1) / (per_wave * kMainWaves);
-    const size_t lds = 2 * static_cast<size_t>(acc_groups(p.N, kMainWaves)) * p.N *
-                       (kChunk / 64) * kAccKP * sizeof(float);
-    // the accumulator tiles exceed the 64 KB default for N = 16; the largest need over
-    // N <= kMaxN is 2 * 16 * K * KP floats
+    const size_t lds = main_lds_bytes(p.N, kMainWaves);
+    // the LDS exceeds the 64 KB default; allow the largest need over N <= kMaxN
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&bwd_main_kernel<T, VEC, HAS_Z, SP>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
-        static_cast<int>(2 * kMaxN * (kChunk / 64) * kAccKP * sizeof(float)));
+        static_cast<int>(main_lds_bytes(kMaxN, kMainWaves)));
     if (attr != hipSuccess) return attr;
     dim3 mgrid(cgroups, p.nchunks, p.B), mblock(64 * kMainWaves);
     if (tm.begin != nullptr && (e = hipEventRecord(tm.begin, s)) != hipSuccess) return e;
