@@ -200,6 +200,9 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
     constexpr int K = kChunk / 64;
     constexpr int W = kMainWaves;
     constexpr int KP = kAccKP;
+    // bf16 rows are small enough that the next channel's u and delta can be fetched during
+    // the current channel's last step, next to this channel's z and dout (for dz)
+    constexpr bool kEarlyUD = sizeof(T) == 2;
     extern __shared__ float acc[];
 
     const int tid = threadIdx.x;
@@ -242,13 +245,31 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
     const int t0 = c * kChunk + lane * K;
     const float* __restrict__ Bb = w.Bf + static_cast<size_t>(b) * N * Lp;
     const float* __restrict__ Cb = w.Cf + static_cast<size_t>(b) * N * Lp;
+    const T* __restrict__ gu = static_cast<const T*>(p.u);
+    const T* __restrict__ gd = static_cast<const T*>(p.delta);
+    const T* __restrict__ gg_ = static_cast<const T*>(g.dout);
+    const T* __restrict__ gz = static_cast<const T*>(p.z);
+    auto chan_row = [&](int d) { return (static_cast<size_t>(b) * p.D + d) * L; };
+
+    // raw input rows of the channel about to start, fetched ahead of time
+    Raw<T, K> ru, rd, rg, rz;
+    const int d_first = blockIdx.x * per_wave * W + wave;
+    if (d_first < p.D) {
+        const size_t row = chan_row(d_first);
+        load_raw<T, K, VEC>(gu + row, t0, L, ru);
+        load_raw<T, K, VEC>(gd + row, t0, L, rd);
+        load_raw<T, K, VEC>(gg_ + row, t0, L, rg);
+        if constexpr (HAS_Z) load_raw<T, K, VEC>(gz + row, t0, L, rz);
+    }
 
     for (int r = 0; r < per_wave; ++r) {
         const int d = (blockIdx.x * per_wave + r) * W + wave;
         const bool active = d < p.D;  // wave-uniform; inactive waves still run the protocol
-        const size_t ch = static_cast<size_t>(b) * p.D + (active ? d : 0);
-        const size_t row = ch * L;
+        const bool next_active = (r + 1 < per_wave) && (d + W < p.D);
         const int dd_ = active ? d : 0;
+        const size_t ch = static_cast<size_t>(b) * p.D + dd_;
+        const size_t row = ch * L;
+        const size_t row_next = chan_row(next_active ? d + W : 0);
         const float bias = p.bias ? p.bias[dd_] : 0.0f;
         const float Dd = p.Dv ? p.Dv[dd_] : 0.0f;
         // per-channel rows of A, H_c and G_c, one value per lane (lane n holds state n)
@@ -266,13 +287,12 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
         float y[HAS_Z ? K : 1];
         float sum_dt = 0.0f, dD_part = 0.0f;
         {
-            // cached loads: the same rows are read again after the state loop
-            float uu[K], dd[K], gg[K];
-            load_k_cached<T, K, VEC>(static_cast<const T*>(p.u) + row, t0, L, uu);
-            load_k_cached<T, K, VEC>(static_cast<const T*>(p.delta) + row, t0, L, dd);
-            load_k_cached<T, K, VEC>(static_cast<const T*>(g.dout) + row, t0, L, gg);
+            float uu[K], dd[K], go[K];
+            unpack(ru, uu);
+            unpack(rd, dd);
+            unpack(rg, go);
             float zz[HAS_Z ? K : 1];
-            if constexpr (HAS_Z) load_k_cached<T, K, VEC>(static_cast<const T*>(p.z) + row, t0, L, zz);
+            if constexpr (HAS_Z) unpack(rz, zz);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float x = dd[k] + bias;
@@ -281,10 +301,10 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
                 dtu[k] = dt[k] * uu[k];
                 sum_dt += dt[k];
                 if constexpr (HAS_Z) {
-                    dy[k] = gg[k] * zz[k] * sigmoid_f(zz[k]);
+                    dy[k] = go[k] * zz[k] * sigmoid_f(zz[k]);
                     y[k] = Dd * uu[k];
                 } else {
-                    dy[k] = gg[k];
+                    dy[k] = go[k];
                 }
                 dD_part = fmaf(dy[k], uu[k], dD_part);
                 sB[k] = 0.0f;
@@ -294,16 +314,33 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
         // sum of Delta over the steps whose a multiplies the adjoint inside this lane:
         // a_{t+1} for t in the lane, i.e. this lane's steps 1..K-1 and the next lane's first
         const float rsum_dt = sum_dt - dt[0] + shift_down(dt[0], 0.0f);
+        // this channel's z and dout, fetched during the last step for dz
+        Raw<T, K> cz, cg;
 
-        for (int j = 0; j < N; ++j) {
+        // One step: state nc of this channel.  `last` (the final state) fetches no B/C rows
+        // and finishes dz, which needs y summed over every state.
+        auto step = [&](const bool last) __attribute__((always_inline)) {
             float bv[K], cv[K];
             unpack(Bn, bv);
             unpack(Cn, cv);
             const int nc = n;
-            if (j + 1 < N) {
+            if (!last) {
                 n = (n + 1 == N) ? 0 : n + 1;
                 load_raw<float, K, true>(Bb + static_cast<size_t>(n) * Lp, t0, Lp, Bn);
                 load_raw<float, K, true>(Cb + static_cast<size_t>(n) * Lp, t0, Lp, Cn);
+            } else {
+                if constexpr (HAS_Z) {
+                    if (active) {
+                        load_raw<T, K, VEC>(gz + row, t0, L, cz);
+                        load_raw<T, K, VEC>(gg_ + row, t0, L, cg);
+                    }
+                }
+                if constexpr (kEarlyUD) {
+                    if (next_active) {
+                        load_raw<T, K, VEC>(gu + row_next, t0, L, ru);
+                        load_raw<T, K, VEC>(gd + row_next, t0, L, rd);
+                    }
+                }
             }
             // wait until the previous update of state nc (step gstep - kp) is complete
             const int need = gstep - kp + 1;
@@ -314,85 +351,118 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
             }
             asm volatile("" ::: "memory");
             if (active) {
-            // this step's accumulator slots: each tensor's reads are issued together, ahead of
-            // their use, and written back as soon as its pass is done
-            float* sBn = myB + nc * K * KP + lane;
-            float* sCn = myC + nc * K * KP + lane;
-            float oc[K];
+                // this step's accumulator slots: each tensor's reads are issued together,
+                // ahead of their use, and written back as soon as its pass is done
+                float* sBn = myB + nc * K * KP + lane;
+                float* sCn = myC + nc * K * KP + lane;
+                float oc[K];
 #pragma unroll
-            for (int k = 0; k < K; ++k) oc[k] = sCn[k * KP];
-            const float An = readlane(Av, nc);
-            const float An2 = An * kLog2e;
-            const float Hn = readlane(Hv, nc);
-            const float Gn = readlane(Gv, nc);
-            // lane-local chains: states from a zero start, adjoint from a zero end
-            float a[K], bb[K], cd[K];
-            float h = 0.0f;
+                for (int k = 0; k < K; ++k) oc[k] = sCn[k * KP];
+                const float An = readlane(Av, nc);
+                const float An2 = An * kLog2e;
+                const float Hn = readlane(Hv, nc);
+                const float Gn = readlane(Gv, nc);
+                // lane-local chains: states from a zero start, adjoint from a zero end
+                float a[K], bb[K], cd[K];
+                float h = 0.0f;
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                a[k] = exp2_hw(dt[k] * An2);
-                bb[k] = dtu[k] * bv[k];
-                h = fmaf(a[k], h, bb[k]);
-                cd[k] = cv[k] * dy[k];
-            }
-            const float a_next = shift_down(a[0], 1.0f);
-            float rr = 0.0f;
+                for (int k = 0; k < K; ++k) {
+                    a[k] = exp2_hw(dt[k] * An2);
+                    bb[k] = dtu[k] * bv[k];
+                    h = fmaf(a[k], h, bb[k]);
+                    cd[k] = cv[k] * dy[k];
+                }
+                const float a_next = shift_down(a[0], 1.0f);
+                float rr = 0.0f;
 #pragma unroll
-            for (int k = K - 1; k >= 0; --k) rr = fmaf((k == K - 1) ? a_next : a[k + 1], rr, cd[k]);
-            float P = exp2_hw(An2 * sum_dt), S = h;
-            float Pr = exp2_hw(An2 * rsum_dt), Sr = rr;
-            scan_fwd_and_rev_rows(P, S, Pr, Sr);
-            // state entering the lane (from H_c) and adjoint entering it from the right (G_c)
-            const float hin = shift_up(fmaf(P, Hn, S), Hn);
-            float lam = shift_down(rev_rows_apply(Pr, Sr, Gn), Gn);
-            float hs[K];
-            h = hin;
+                for (int k = K - 1; k >= 0; --k)
+                    rr = fmaf((k == K - 1) ? a_next : a[k + 1], rr, cd[k]);
+                float P = exp2_hw(An2 * sum_dt), S = h;
+                float Pr = exp2_hw(An2 * rsum_dt), Sr = rr;
+                scan_fwd_and_rev_rows(P, S, Pr, Sr);
+                // state entering the lane (from H_c), adjoint entering it from the right (G_c)
+                const float hin = shift_up(fmaf(P, Hn, S), Hn);
+                float lam = shift_down(rev_rows_apply(Pr, Sr, Gn), Gn);
+                float hs[K];
+                h = hin;
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                h = fmaf(a[k], h, bb[k]);
-                hs[k] = h;
-                if constexpr (HAS_Z) y[k] = fmaf(cv[k], h, y[k]);
-                oc[k] = fmaf(dy[k], h, oc[k]);
-            }
-            float ob[K];
+                for (int k = 0; k < K; ++k) {
+                    h = fmaf(a[k], h, bb[k]);
+                    hs[k] = h;
+                    if constexpr (HAS_Z) y[k] = fmaf(cv[k], h, y[k]);
+                    oc[k] = fmaf(dy[k], h, oc[k]);
+                }
+                float ob[K];
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                sCn[k * KP] = oc[k];
-                ob[k] = sBn[k * KP];
-            }
-            float dA_part = 0.0f;
+                for (int k = 0; k < K; ++k) {
+                    sCn[k * KP] = oc[k];
+                    ob[k] = sBn[k * KP];
+                }
+                if constexpr (HAS_Z) {
+                    if (last) {  // y is complete: dz = dout * y * silu'(z)
+                        float zz[K], go[K], o[K];
+                        unpack(cz, zz);
+                        unpack(cg, go);
 #pragma unroll
-            for (int k = K - 1; k >= 0; --k) {
-                lam = fmaf((k == K - 1) ? a_next : a[k + 1], lam, cd[k]);
-                const float hprev = (k == 0) ? hin : hs[k - 1];
-                const float gk = lam * hprev * a[k];
-                dA_part = fmaf(gk, dt[k], dA_part);
-                sgA[k] = fmaf(gk, An, sgA[k]);
-                sB[k] = fmaf(lam, bv[k], sB[k]);
-                ob[k] = fmaf(lam, dtu[k], ob[k]);
-            }
+                        for (int k = 0; k < K; ++k) {
+                            const float sg = sigmoid_f(zz[k]);
+                            o[k] = go[k] * sg * fmaf(zz[k], 1.0f - sg, 1.0f) * y[k];
+                        }
+                        store_k<T, K, VEC>(static_cast<T*>(g.dz) + row, t0, L, o);
+                    }
+                }
+                float dA_part = 0.0f;
 #pragma unroll
-            for (int k = 0; k < K; ++k) sBn[k * KP] = ob[k];
-            dAs[nc * kDaStride + lane] = dA_part;
+                for (int k = K - 1; k >= 0; --k) {
+                    lam = fmaf((k == K - 1) ? a_next : a[k + 1], lam, cd[k]);
+                    const float hprev = (k == 0) ? hin : hs[k - 1];
+                    const float gk = lam * hprev * a[k];
+                    dA_part = fmaf(gk, dt[k], dA_part);
+                    sgA[k] = fmaf(gk, An, sgA[k]);
+                    sB[k] = fmaf(lam, bv[k], sB[k]);
+                    ob[k] = fmaf(lam, dtu[k], ob[k]);
+                }
+#pragma unroll
+                for (int k = 0; k < K; ++k) sBn[k * KP] = ob[k];
+                dAs[nc * kDaStride + lane] = dA_part;
             }
             // publish: this step's LDS writes are complete
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __hip_atomic_store(gflags + nc, gstep + 1, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
             ++gstep;
+        };
+
+        for (int j = 0; j + 1 < N; ++j) step(false);
+        step(true);
+
+        // the rest of the next channel's inputs, in flight while this one is finished
+        if (next_active) {
+            if constexpr (!kEarlyUD) {
+                load_raw<T, K, VEC>(gu + row_next, t0, L, ru);
+                load_raw<T, K, VEC>(gd + row_next, t0, L, rd);
+            }
+            load_raw<T, K, VEC>(gg_ + row_next, t0, L, rg);
+            if constexpr (HAS_Z) load_raw<T, K, VEC>(gz + row_next, t0, L, rz);
         }
         if (!active) continue;
 
-        // inputs that were not kept live across the steps are reloaded (L2-resident)
+        // du and ddelta.  With the softplus, sigmoid(delta + bias) = 1 - exp(-Delta) and
+        // u = (Delta u) / Delta come from values already in registers (where Delta underflows
+        // to 0 the sigmoid factor is 0 as well); without it u is read again (L2-resident).
         float o1[K], o2[K];
         float db_part = 0.0f;
         {
-            float uu[K], dd[K];
-            load_k_cached<T, K, VEC>(static_cast<const T*>(p.u) + row, t0, L, uu);
-            load_k_cached<T, K, VEC>(static_cast<const T*>(p.delta) + row, t0, L, dd);
+            float uu[K];
+            if constexpr (SOFTPLUS) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) uu[k] = dt[k] > 1e-30f ? dtu[k] * rcp_hw(dt[k]) : 0.0f;
+            } else {
+                load_k_cached<T, K, VEC>(gu + row, t0, L, uu);
+            }
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                const float dsp = SOFTPLUS ? sigmoid_f(dd[k] + bias) : 1.0f;
+                const float dsp = SOFTPLUS ? 1.0f - exp2_hw(-dt[k] * kLog2e) : 1.0f;
                 o1[k] = fmaf(sB[k], dt[k], dy[k] * Dd);            // du
                 o2[k] = fmaf(sB[k], uu[k], sgA[k]) * dsp;         // ddelta
                 db_part += (t0 + k < L) ? o2[k] : 0.0f;
@@ -400,17 +470,6 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
         }
         store_k<T, K, VEC>(static_cast<T*>(g.du) + row, t0, L, o1);
         store_k<T, K, VEC>(static_cast<T*>(g.ddelta) + row, t0, L, o2);
-        if constexpr (HAS_Z) {
-            float zz[K], gg[K];
-            load_k_cached<T, K, VEC>(static_cast<const T*>(p.z) + row, t0, L, zz);
-            load_k_cached<T, K, VEC>(static_cast<const T*>(g.dout) + row, t0, L, gg);
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const float s = sigmoid_f(zz[k]);
-                o1[k] = gg[k] * s * fmaf(zz[k], 1.0f - s, 1.0f) * y[k];   // dz
-            }
-            store_k<T, K, VEC>(static_cast<T*>(g.dz) + row, t0, L, o1);
-        }
         // dA[d, n]: lanes 4n..4n+3 each sum 16 of the 64 lane partials of state n, then the
         // quad is summed; the wave's own dA rows need no barrier (same-wave LDS order)
         const int qn = lane >> 2;
@@ -503,12 +562,23 @@ size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states) {
 
 namespace {
 
-// Channels per wavefront in the main kernel: aim at about 1024 workgroups so that every CU
-// gets several, while keeping the number of dB/dC partial sums (one per workgroup) small.
+// Channels per wavefront in the main kernel: about one workgroup per compute unit, so that
+// each workgroup walks many channels of one (batch row, chunk) and flushes its dB/dC sums once.
+int compute_units() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    return cus;
+}
+
 int main_per_wave(const ScanParams& p) {
+    static const int cus = compute_units();
     const long long slots = static_cast<long long>(p.B) * p.nchunks;
-    long long per = (static_cast<long long>(p.D) * slots + 1024LL * kMainWaves - 1) /
-                    (1024LL * kMainWaves);
+    const long long target = cus;
+    long long per = (static_cast<long long>(p.D) * slots + target * kMainWaves - 1) /
+                    (target * kMainWaves);
     const long long max_per = (p.D + kMainWaves - 1) / kMainWaves;
     if (per < 1) per = 1;
     if (per > max_per) per = max_per;
