@@ -63,6 +63,7 @@ template <> struct Elem<bf16_t> {
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -414,6 +415,65 @@ __device__ __forceinline__ void scan_fwd_and_rev_rows(float& P, float& S, float&
                  MSEL_FWD_LEVEL("row_bcast:31", "0xc")
                  : [P] "+v"(P), [S] "+v"(S), [Pr] "+v"(Pr), [Sr] "+v"(Sr));
 #undef MSEL_PAIR_LEVEL
+}
+
+// Row levels (16-lane rows) of four independent scans in one instruction stream: (P1, S1) and
+// (P2, S2) forward (row_shr), (Q1, R1) and (Q2, R2) suffix (row_shl).  Each DPP read comes at
+// least three instructions after the write of its source, so no wait states are needed.
+__device__ __forceinline__ void scan_rows4(float& P1, float& S1, float& Q1, float& R1, float& P2,
+                                           float& S2, float& Q2, float& R2) {
+#define MSEL_ROW4(CF, CR)                                                            \
+    "v_fmac_f32_dpp %[S1], %[S1], %[P1] " CF " row_mask:0xf bank_mask:0xf\n"         \
+    "v_mul_f32_dpp %[P1], %[P1], %[P1] " CF " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %[R1], %[R1], %[Q1] " CR " row_mask:0xf bank_mask:0xf\n"         \
+    "v_mul_f32_dpp %[Q1], %[Q1], %[Q1] " CR " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %[S2], %[S2], %[P2] " CF " row_mask:0xf bank_mask:0xf\n"         \
+    "v_mul_f32_dpp %[P2], %[P2], %[P2] " CF " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %[R2], %[R2], %[Q2] " CR " row_mask:0xf bank_mask:0xf\n"         \
+    "v_mul_f32_dpp %[Q2], %[Q2], %[Q2] " CR " row_mask:0xf bank_mask:0xf\n"
+    asm volatile("s_nop 1\n"
+                 MSEL_ROW4("row_shr:1", "row_shl:1")
+                 MSEL_ROW4("row_shr:2", "row_shl:2")
+                 MSEL_ROW4("row_shr:4", "row_shl:4")
+                 MSEL_ROW4("row_shr:8", "row_shl:8")
+                 : [P1] "+v"(P1), [S1] "+v"(S1), [Q1] "+v"(Q1), [R1] "+v"(R1),
+                   [P2] "+v"(P2), [S2] "+v"(S2), [Q2] "+v"(Q2), [R2] "+v"(R2));
+#undef MSEL_ROW4
+}
+
+// Row levels of two independent suffix scans (row_shl), interleaved; the DPP reads come two
+// instructions after the writes of their sources, which is the wait the hardware needs.
+__device__ __forceinline__ void scan_rows2_rev(float& Q1, float& R1, float& Q2, float& R2) {
+#define MSEL_ROW2(CR)                                                                \
+    "v_fmac_f32_dpp %[R1], %[R1], %[Q1] " CR " row_mask:0xf bank_mask:0xf\n"         \
+    "v_mul_f32_dpp %[Q1], %[Q1], %[Q1] " CR " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %[R2], %[R2], %[Q2] " CR " row_mask:0xf bank_mask:0xf\n"         \
+    "v_mul_f32_dpp %[Q2], %[Q2], %[Q2] " CR " row_mask:0xf bank_mask:0xf\n"
+    asm volatile("s_nop 1\n"
+                 MSEL_ROW2("row_shl:1")
+                 MSEL_ROW2("row_shl:2")
+                 MSEL_ROW2("row_shl:4")
+                 MSEL_ROW2("row_shl:8")
+                 : [Q1] "+v"(Q1), [R1] "+v"(R1), [Q2] "+v"(Q2), [R2] "+v"(R2));
+#undef MSEL_ROW2
+}
+
+// Totals of scans whose row levels are done (wave-uniform results):
+//  forward: the composition of all 64 lanes, from the last lane of each row;
+//  suffix:  the composition of all 64 lanes, from the first lane of each row.
+// Only the S part is returned (the end state from a zero start, resp. the value at lane 0
+// from a zero carry).
+__device__ __forceinline__ float fwd_rows_total(float P, float S) {
+    float t = readlane(S, 15);
+    t = fmaf(readlane(P, 31), t, readlane(S, 31));
+    t = fmaf(readlane(P, 47), t, readlane(S, 47));
+    return fmaf(readlane(P, 63), t, readlane(S, 63));
+}
+__device__ __forceinline__ float rev_rows_total(float P, float S) {
+    float t = readlane(S, 48);
+    t = fmaf(readlane(P, 32), t, readlane(S, 32));
+    t = fmaf(readlane(P, 16), t, readlane(S, 16));
+    return fmaf(readlane(P, 0), t, readlane(S, 0));
 }
 
 // Finishes a suffix scan whose row levels are done: (P, S) of lane l compose lanes l..15 of

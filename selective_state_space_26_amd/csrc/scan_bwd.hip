@@ -80,7 +80,7 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
     const float* __restrict__ Arow = p.A + static_cast<size_t>(d) * N;
     const int t0 = c * kChunk + lane * K;
 
-    float dt[K], dy[K], du[K];
+    float dt[K], dy[K], du[FWD ? K : 1];
     float sum_dt = 0.0f;
     {
         float dd[K], gg[K];
@@ -100,47 +100,79 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
             if constexpr (FWD) du[k] = dt[k] * uu[k];
         }
     }
-    const float dt_next = shift_down(dt[0], 0.0f);
+    // the adjoint's transition inside a lane multiplies a_{t+1}: this lane's steps 1..K-1
+    // and the next lane's first step
+    const float rsum_dt = sum_dt - dt[0] + shift_down(dt[0], 0.0f);
     const float chunk_dt = wave_sum_fused(sum_dt);
     if (lane == 0) {
         w.sdt[idx] = chunk_dt;
         w.dfirst[idx] = dt[0];
     }
-    Raw<float, K> Bn, Cn;
-    if constexpr (FWD) load_raw<float, K, true>(Bb, t0, Lp, Bn);
-    load_raw<float, K, true>(Cb, t0, Lp, Cn);
-    for (int n = 0; n < N; ++n) {
-        const float An2 = Arow[n] * kLog2e;
-        float bv[K], cv[K];
-        if constexpr (FWD) unpack(Bn, bv);
-        unpack(Cn, cv);
-        if (n + 1 < N) {  // prefetch the next state's rows
-            if constexpr (FWD) load_raw<float, K, true>(Bb + static_cast<size_t>(n + 1) * Lp, t0, Lp, Bn);
-            load_raw<float, K, true>(Cb + static_cast<size_t>(n + 1) * Lp, t0, Lp, Cn);
-        }
-        float a[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) a[k] = exp2_hw(dt[k] * An2);
+
+    // Two states per iteration (the second repeats the first when N is odd), so that the
+    // lane-local chains and the row scans of both are independent instruction streams.
+    // Per state: forward local end state from a zero start (only when H is rebuilt here) and
+    // the adjoint at the chunk's first step from a zero adjoint after the chunk.
+    Raw<float, K> B1, C1, B2, C2;
+    auto fetch = [&](int n, Raw<float, K>& Bn, Raw<float, K>& Cn) __attribute__((always_inline)) {
+        if constexpr (FWD) load_raw<float, K, true>(Bb + static_cast<size_t>(n) * Lp, t0, Lp, Bn);
+        load_raw<float, K, true>(Cb + static_cast<size_t>(n) * Lp, t0, Lp, Cn);
+    };
+    fetch(0, B1, C1);
+    fetch(N > 1 ? 1 : 0, B2, C2);
+    for (int n = 0; n < N; n += 2) {
+        const int n2 = (n + 1 < N) ? n + 1 : n;
+        float bv1[K], cv1[K], bv2[K], cv2[K];
         if constexpr (FWD) {
-            float h = 0.0f;
-#pragma unroll
-            for (int k = 0; k < K; ++k) h = fmaf(a[k], h, du[k] * bv[k]);
-            float P = exp2_hw(An2 * sum_dt);
-            float S = h;
-            scan_fwd_fused(P, S);
-            if (lane == 63) w.H[static_cast<size_t>(idx) * N + n] = S;
+            unpack(B1, bv1);
+            unpack(B2, bv2);
         }
-        const float a_next = shift_down(a[0], 1.0f);
-        float r = 0.0f;
+        unpack(C1, cv1);
+        unpack(C2, cv2);
+        if (n + 2 < N) {  // prefetch the next pair's rows
+            fetch(n + 2, B1, C1);
+            fetch(n + 3 < N ? n + 3 : n + 2, B2, C2);
+        }
+        const float A1 = Arow[n] * kLog2e, A2 = Arow[n2] * kLog2e;
+        float a1[K], a2[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            a1[k] = exp2_hw(dt[k] * A1);
+            a2[k] = exp2_hw(dt[k] * A2);
+        }
+        float P1 = 1.0f, S1 = 0.0f, P2 = 1.0f, S2 = 0.0f;
+        if constexpr (FWD) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                S1 = fmaf(a1[k], S1, du[k] * bv1[k]);
+                S2 = fmaf(a2[k], S2, du[k] * bv2[k]);
+            }
+            P1 = exp2_hw(A1 * sum_dt);
+            P2 = exp2_hw(A2 * sum_dt);
+        }
+        const float e1 = shift_down(a1[0], 1.0f), e2 = shift_down(a2[0], 1.0f);
+        float R1 = 0.0f, R2 = 0.0f;
 #pragma unroll
         for (int k = K - 1; k >= 0; --k) {
-            const float e = (k == K - 1) ? a_next : a[k + 1];
-            r = fmaf(e, r, cv[k] * dy[k]);
+            const float cdk1 = cv1[k] * dy[k], cdk2 = cv2[k] * dy[k];
+            R1 = fmaf((k == K - 1) ? e1 : a1[k + 1], R1, cdk1);
+            R2 = fmaf((k == K - 1) ? e2 : a2[k + 1], R2, cdk2);
         }
-        float Pr = exp2_hw(An2 * (sum_dt - dt[0] + dt_next));
-        float Sr = r;
-        scan_rev_fused(Pr, Sr);
-        if (lane == 0) w.G[static_cast<size_t>(idx) * N + n] = Sr;
+        float Q1 = exp2_hw(A1 * rsum_dt), Q2 = exp2_hw(A2 * rsum_dt);
+        if constexpr (FWD) scan_rows4(P1, S1, Q1, R1, P2, S2, Q2, R2);
+        else scan_rows2_rev(Q1, R1, Q2, R2);
+        const float G1 = rev_rows_total(Q1, R1), G2 = rev_rows_total(Q2, R2);
+        if constexpr (FWD) {
+            const float H1 = fwd_rows_total(P1, S1), H2 = fwd_rows_total(P2, S2);
+            if (lane == 0) {
+                w.H[static_cast<size_t>(idx) * N + n] = H1;
+                w.H[static_cast<size_t>(idx) * N + n2] = H2;
+            }
+        }
+        if (lane == 0) {
+            w.G[static_cast<size_t>(idx) * N + n] = G1;
+            w.G[static_cast<size_t>(idx) * N + n2] = G2;
+        }
     }
 }
 
@@ -178,20 +210,32 @@ __global__ __launch_bounds__(256) void bwd_link_kernel(ScanParams p, GradParams 
 //  * dB and dC accumulators [2 tensors][group][n][k][65] floats: the padded stride 65 keeps
 //    both the per-lane updates (consecutive lanes) and the flush (consecutive time steps)
 //    free of bank conflicts;
-//  * per-wave dA partials [wave][n][68]: one row of 64 lane partials per state, summed once
-//    per channel;
+//  * B and C of the workgroup's (batch row, chunk) as fp32, [2 tensors][n][2][64 lanes][4]:
+//    lane l's 8 steps are two 16-byte vectors, consecutive lanes adjacent (conflict-free);
+//  * per-wave dA partials [wave][n][16]: sums over groups of four lanes, per state;
 //  * (static) one int per (group, state): 1 + the global step of the last completed update
 //    of that state's accumulator rows (see the ring protocol in the kernel).
 constexpr int kAccKP = 65;
-constexpr int kDaStride = 68;
+constexpr int kDaQuads = 16;
 constexpr int kMaxRingFlags = 32;  // groups * N <= W + N - 1
 
 __host__ __device__ constexpr int acc_groups(int N, int W) { return (W + N - 1) / N; }
 
 __host__ __device__ constexpr size_t main_lds_bytes(int N, int W) {
     return (2 * static_cast<size_t>(acc_groups(N, W)) * N * (kChunk / 64) * kAccKP +
-            static_cast<size_t>(W) * N * kDaStride) * sizeof(float);
+            2 * static_cast<size_t>(N) * kChunk + static_cast<size_t>(W) * N * kDaQuads) *
+           sizeof(float);
 }
+
+// The largest need over 1 <= N <= kMaxN (it is not at kMaxN: fewer states can need more
+// accumulator groups).
+__host__ __device__ constexpr size_t main_lds_bytes_max(int W) {
+    size_t m = 0;
+    for (int n = 1; n <= kMaxN; ++n) m = main_lds_bytes(n, W) > m ? main_lds_bytes(n, W) : m;
+    return m;
+}
+static_assert(main_lds_bytes_max(kMainWaves) + kMaxRingFlags * sizeof(int) <= 160 * 1024,
+              "main kernel LDS exceeds a compute unit's 160 KB");
 static_assert(kMainWaves + kMaxN - 1 <= kMaxRingFlags, "ring flags do not fit");
 
 template <typename T, bool VEC, bool HAS_Z, bool SOFTPLUS>
@@ -213,15 +257,33 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
     const int N = p.N;
     const int L = p.L;
     const int nch = p.nchunks;
-    const int Lp = nch * kChunk;
     const int groups = acc_groups(N, W);
     const int tile = N * K * KP;             // floats per (tensor, group)
     float* accB = acc;
     float* accC = acc + groups * tile;
-    float* dAs = acc + 2 * groups * tile + wave * N * kDaStride;  // this wave's dA rows
+    float* BCs = acc + 2 * groups * tile;                   // B rows, then C rows
+    float* dAs = BCs + 2 * N * kChunk + wave * N * kDaQuads;  // this wave's dA partials
     __shared__ int ring_flags[kMaxRingFlags];
     for (int i = tid; i < 2 * groups * tile; i += 64 * W) acc[i] = 0.0f;
     for (int i = tid; i < groups * N; i += 64 * W) ring_flags[i] = 0;
+    {
+        // B and C of this (batch row, chunk), read once per workgroup, zero past the end
+        const T* __restrict__ Bg = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
+        const T* __restrict__ Cg = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
+        for (int i = tid; i < N * kChunk; i += 64 * W) {
+            const int nn = i / kChunk;
+            const int tl = i - nn * kChunk;
+            const int t = c * kChunk + tl;
+            float vb = 0.0f, vc = 0.0f;
+            if (t < L) {
+                vb = Elem<T>::load1(Bg + static_cast<size_t>(nn) * L + t);
+                vc = Elem<T>::load1(Cg + static_cast<size_t>(nn) * L + t);
+            }
+            const int o = ((nn * 2 + (tl % K) / 4) * 64 + tl / K) * 4 + tl % 4;
+            BCs[o] = vb;
+            BCs[N * kChunk + o] = vc;
+        }
+    }
     __syncthreads();
 
     // Ring protocol for the shared accumulator rows.  The waves of a group take the states in
@@ -243,8 +305,8 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
     float* myC = accC + grp * tile;
 
     const int t0 = c * kChunk + lane * K;
-    const float* __restrict__ Bb = w.Bf + static_cast<size_t>(b) * N * Lp;
-    const float* __restrict__ Cb = w.Cf + static_cast<size_t>(b) * N * Lp;
+    const f32x4* __restrict__ B4 = reinterpret_cast<const f32x4*>(BCs);
+    const f32x4* __restrict__ C4 = reinterpret_cast<const f32x4*>(BCs + N * kChunk);
     const T* __restrict__ gu = static_cast<const T*>(p.u);
     const T* __restrict__ gd = static_cast<const T*>(p.delta);
     const T* __restrict__ gg_ = static_cast<const T*>(g.dout);
@@ -278,10 +340,7 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
         const float Hv = (lane < N) ? w.H[hg + lane] : 0.0f;
         const float Gv = (lane < N) ? w.G[hg + lane] : 0.0f;
 
-        int n = rot;  // state of step 0; rows of the next step are prefetched
-        Raw<float, K> Bn, Cn;
-        load_raw<float, K, true>(Bb + static_cast<size_t>(n) * Lp, t0, Lp, Bn);
-        load_raw<float, K, true>(Cb + static_cast<size_t>(n) * Lp, t0, Lp, Cn);
+        int n = rot;  // state of step 0
 
         float dt[K], dtu[K], dy[K], sB[K], sgA[K];
         float y[HAS_Z ? K : 1];
@@ -317,17 +376,24 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
         // this channel's z and dout, fetched during the last step for dz
         Raw<T, K> cz, cg;
 
-        // One step: state nc of this channel.  `last` (the final state) fetches no B/C rows
-        // and finishes dz, which needs y summed over every state.
+        // One step: state nc of this channel.  `last` (the final state) also fetches inputs
+        // for dz and the next channel, and finishes dz, which needs y summed over every state.
         auto step = [&](const bool last) __attribute__((always_inline)) {
-            float bv[K], cv[K];
-            unpack(Bn, bv);
-            unpack(Cn, cv);
             const int nc = n;
+            float bv[K], cv[K];
+            {
+                const f32x4 b0 = B4[(nc * 2) * 64 + lane], b1 = B4[(nc * 2 + 1) * 64 + lane];
+                const f32x4 c0 = C4[(nc * 2) * 64 + lane], c1 = C4[(nc * 2 + 1) * 64 + lane];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    bv[q] = b0[q];
+                    bv[4 + q] = b1[q];
+                    cv[q] = c0[q];
+                    cv[4 + q] = c1[q];
+                }
+            }
             if (!last) {
                 n = (n + 1 == N) ? 0 : n + 1;
-                load_raw<float, K, true>(Bb + static_cast<size_t>(n) * Lp, t0, Lp, Bn);
-                load_raw<float, K, true>(Cb + static_cast<size_t>(n) * Lp, t0, Lp, Cn);
             } else {
                 if constexpr (HAS_Z) {
                     if (active) {
@@ -424,7 +490,8 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
                 }
 #pragma unroll
                 for (int k = 0; k < K; ++k) sBn[k * KP] = ob[k];
-                dAs[nc * kDaStride + lane] = dA_part;
+                const float dq = quad_sum(dA_part);
+                if ((lane & 3) == 0) dAs[nc * kDaQuads + (lane >> 2)] = dq;
             }
             // publish: this step's LDS writes are complete
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -470,28 +537,29 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
         }
         store_k<T, K, VEC>(static_cast<T*>(g.du) + row, t0, L, o1);
         store_k<T, K, VEC>(static_cast<T*>(g.ddelta) + row, t0, L, o2);
-        // dA[d, n]: lanes 4n..4n+3 each sum 16 of the 64 lane partials of state n, then the
-        // quad is summed; the wave's own dA rows need no barrier (same-wave LDS order)
-        const int qn = lane >> 2;
+        // dA[d, n]: lane n sums the 16 quad partials of state n (the wave's own rows: same-wave
+        // LDS order, no barrier needed)
         float sa = 0.0f;
-        if (qn < N) {
-            const float* src = dAs + qn * kDaStride + (lane & 3) * 16;
+        if (lane < N) {
+            const f32x4* src = reinterpret_cast<const f32x4*>(dAs + lane * kDaQuads);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) sa += src[q];
+            for (int q = 0; q < kDaQuads / 4; ++q) {
+                const f32x4 v = src[q];
+                sa += (v[0] + v[1]) + (v[2] + v[3]);
+            }
         }
-        sa = quad_sum(sa);
         const float sD = wave_sum_fused(dD_part);
         const float sb = wave_sum_fused(db_part);
-        // one vector atomic per channel: lane 4n adds dA[d, n], lane 1 dD[d], lane 2 dbias[d]
+        // one vector atomic per channel: lane n < N adds dA[d, n], lane 62 dD[d], 63 dbias[d]
         float* dst = nullptr;
         float val = 0.0f;
-        if ((lane & 3) == 0 && qn < N) {
-            dst = g.dA ? g.dA + static_cast<size_t>(d) * N + qn : nullptr;
+        if (lane < N) {
+            dst = g.dA ? g.dA + static_cast<size_t>(d) * N + lane : nullptr;
             val = sa;
-        } else if (lane == 1) {
+        } else if (lane == 62) {
             dst = g.dD ? g.dD + d : nullptr;
             val = sD;
-        } else if (lane == 2) {
+        } else if (lane == 63) {
             dst = g.dbias ? g.dbias + d : nullptr;
             val = sb;
         }
@@ -620,7 +688,7 @@ hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hi
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&bwd_main_kernel<T, VEC, HAS_Z, SP>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
-        static_cast<int>(main_lds_bytes(kMaxN, kMainWaves)));
+        static_cast<int>(main_lds_bytes_max(kMainWaves)));
     if (attr != hipSuccess) return attr;
     dim3 mgrid(cgroups, p.nchunks, p.B), mblock(64 * kMainWaves);
     if (tm.begin != nullptr && (e = hipEventRecord(tm.begin, s)) != hipSuccess) return e;

@@ -90,6 +90,8 @@ BWD_CASES = [
     (3, 3, 7, 700, "f32", False, False, False, True),
     (1, 3, 16, 1, "f32", True, True, True, True),
     (2, 9, 16, 1536, "f32", True, True, True, False),   # dim not a multiple of the workgroup
+    (2, 13, 11, 700, "f32", True, True, True, True),    # dstate 11: the largest LDS need
+    (1, 25, 10, 1030, "bf16", True, True, True, False), # two accumulator groups, ragged tail
 ]
 
 
