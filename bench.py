@@ -45,11 +45,11 @@ def algorithmic_bytes(w, nchunks):
     dn, d = w.dim * w.dstate, w.dim
     fwd = 4 * tc * s + 2 * bnl * s + states + w.batch * w.dim * w.dstate * 4 + dn * 4 + 2 * d * 4
     cc = 2 * tc * s + bnl * s + states + dn * 4 + d * 4
-    # the gradient kernel: u, delta, dout, z in; du, ddelta, dz out; fp32 B, C in; dB, dC out;
-    # chunk-start states and adjoint carries in; A, D, bias in; dA, dD, dbias out
-    bwd_main = 7 * tc * s + 2 * bnl * 4 + 2 * bnl * 4 + 2 * states + 2 * (dn + 2 * d) * 4
-    # the whole msel_scan_bwd call adds the fp32 copies of B and C (bf16 in, fp32 out) and
-    # the summary pass, whose inputs are the same tensors
+    # the gradient kernel: u, delta, dout, z in; du, ddelta, dz out; B, C in; dB, dC out
+    # (fp32); chunk-start states and adjoint carries in; A, D, bias in; dA, dD, dbias out
+    bwd_main = 7 * tc * s + 2 * bnl * s + 2 * bnl * 4 + 2 * states + 2 * (dn + 2 * d) * 4
+    # the whole msel_scan_bwd call: the same tensors once (its summary pass reads delta, dout
+    # and z a second time; that re-read is not counted)
     bwd = 7 * tc * s + 2 * bnl * s + 2 * bnl * 4 + 2 * dn * 4 + 4 * d * 4
     return {"fwd": fwd, "chunk_carry": cc, "bwd_main": bwd_main, "bwd": bwd}
 
@@ -200,7 +200,7 @@ def main():
     kernels["fwd"]["what"] = "scan_fwd_kernel (one launch)"
     kernels["chunk_carry"]["what"] = "chunk_carry_kernel (one launch), timed apart from the step"
     kernels["bwd_main"]["what"] = "bwd_main_kernel, the chunk-parallel gradient kernel"
-    kernels["bwd"]["what"] = ("the msel_scan_bwd call: zero-fills, convert, summary, link and "
+    kernels["bwd"]["what"] = ("the msel_scan_bwd call: zero-fills, summary, link and "
                               "bwd_main_kernel")
 
     # the dominant kernel: the gradient kernel, bound by VALU arithmetic (an exp2 per update

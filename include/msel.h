@@ -147,20 +147,20 @@ msel_status msel_scan_fwd(const msel_scan_args *args, hipStream_t stream);
  * (optional).  Reads u, delta, B, A, delta_bias, h0 only. */
 msel_status msel_scan_chunk_carry(const msel_scan_args *args, hipStream_t stream);
 
-/* Workspace the backward needs, in bytes: fp32 copies of B and C padded to whole chunks,
- * the adjoint carry per chunk and state, two floats per chunk, and the chunk-start states
- * when args->chunk_states is NULL (in all about 8*batch*dstate*seqlen +
- * 8*batch*dim*n_chunks*dstate bytes).  Returns 0 for invalid args.  The workspace must be
- * 256-byte aligned; its contents on entry do not matter. */
+/* Workspace the backward needs, in bytes: the adjoint carry per chunk and state, two floats
+ * per chunk, and the chunk-start states when args->chunk_states is NULL (in all about
+ * 4*batch*dim*n_chunks*(dstate + 2) bytes, twice the state part without chunk_states).
+ * Returns 0 for invalid args.  The workspace must be 256-byte aligned; its contents on entry
+ * do not matter. */
 size_t msel_scan_bwd_workspace_bytes(const msel_scan_args *args);
 
 /* Backward with recomputation (page 1; page 4 Appendix D, Memory: intermediate states are
- * recomputed, not stored).  Launches on `stream`: fp32 copies of B and C, per-chunk summaries
- * of the states and of the adjoint, their link across chunks (the chunk carry run forward and
- * backward), and the chunk-parallel gradient kernel.  Only chunk-boundary values live in the workspace.
- * Reductions over channels (dB, dC) and over batch and time (dA, dD, ddelta_bias) use fp32
- * atomics, so those outputs may differ in the last bits between runs; du, ddelta, dz and dh0
- * are deterministic. */
+ * recomputed, not stored).  Launches on `stream`: zero-fills of the summed outputs, per-chunk
+ * summaries of the states and of the adjoint, their link across chunks (the chunk carry run
+ * forward and backward), and the chunk-parallel gradient kernel.  Only chunk-boundary values
+ * live in the workspace.  Reductions over channels (dB, dC) and over batch and time (dA, dD,
+ * ddelta_bias) use fp32 atomics, so those outputs may differ in the last bits between runs;
+ * du, ddelta, dz and dh0 are deterministic. */
 msel_status msel_scan_bwd(const msel_scan_args *args, const msel_scan_grads *grads,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 

@@ -31,7 +31,8 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
     const T* __restrict__ dl = static_cast<const T*>(p.delta) + row;
     const T* __restrict__ Bb = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
     const float bias = p.bias ? p.bias[d] : 0.0f;
-    const float* __restrict__ Arow = p.A + static_cast<size_t>(d) * N;
+    // lane n holds A[d, n] * log2(e): one vector load, read per state with readlane
+    const float Av = (lane < N) ? p.A[static_cast<size_t>(d) * N + lane] * kLog2e : 0.0f;
     float* __restrict__ cs = p.chunk_states + static_cast<size_t>(ch) * p.nchunks * N;
 
     float carry = 0.0f;
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
         Raw<T, K> Bn;
         load_raw<T, K, VEC>(Bb, t0, L, Bn);
         for (int n = 0; n < N; ++n) {
-            const float An = Arow[n] * kLog2e;
+            const float An = readlane(Av, n);
             float bc[K];
             unpack(Bn, bc);
             if (n + 1 < N) load_raw<T, K, VEC>(Bb + static_cast<size_t>(n + 1) * L, t0, L, Bn);

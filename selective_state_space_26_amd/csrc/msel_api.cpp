@@ -175,13 +175,10 @@ msel_status msel_scan_bwd_profiled(const msel_scan_args* a, const msel_scan_grad
     msel::ScanParams p = to_params(a);
     const size_t DN = static_cast<size_t>(a->dim) * a->dstate;
     const size_t BNL = static_cast<size_t>(a->batch) * a->dstate * a->seqlen;
-    hipError_t e = hipSuccess;
-    if (e == hipSuccess) e = msel::launch_fill_zero(g->dA, DN, stream);
-    if (e == hipSuccess) e = msel::launch_fill_zero(g->dB, BNL, stream);
-    if (e == hipSuccess) e = msel::launch_fill_zero(g->dC, BNL, stream);
-    if (e == hipSuccess) e = msel::launch_fill_zero(g->dD, a->dim, stream);
-    if (e == hipSuccess) e = msel::launch_fill_zero(g->ddelta_bias, a->dim, stream);
-    if (e != hipSuccess) return MSEL_ERR_HIP;
+    const msel::FillList fill = {{g->dA, g->dB, g->dC, g->dD, g->ddelta_bias},
+                                 {DN, BNL, BNL, static_cast<size_t>(a->dim),
+                                  static_cast<size_t>(a->dim)}};
+    if (msel::launch_fill_zero(fill, stream) != hipSuccess) return MSEL_ERR_HIP;
     msel::GradParams gp;
     gp.dout = g->dout;
     gp.du = g->du;

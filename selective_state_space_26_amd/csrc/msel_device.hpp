@@ -458,6 +458,28 @@ __device__ __forceinline__ void scan_rows2_rev(float& Q1, float& R1, float& Q2, 
 #undef MSEL_ROW2
 }
 
+// Row levels of four independent suffix scans (row_shl), interleaved.
+__device__ __forceinline__ void scan_rows4_rev(float& Q1, float& R1, float& Q2, float& R2,
+                                               float& Q3, float& R3, float& Q4, float& R4) {
+#define MSEL_ROWR4(CR)                                                               \
+    "v_fmac_f32_dpp %[R1], %[R1], %[Q1] " CR " row_mask:0xf bank_mask:0xf\n"         \
+    "v_mul_f32_dpp %[Q1], %[Q1], %[Q1] " CR " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %[R2], %[R2], %[Q2] " CR " row_mask:0xf bank_mask:0xf\n"         \
+    "v_mul_f32_dpp %[Q2], %[Q2], %[Q2] " CR " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %[R3], %[R3], %[Q3] " CR " row_mask:0xf bank_mask:0xf\n"         \
+    "v_mul_f32_dpp %[Q3], %[Q3], %[Q3] " CR " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %[R4], %[R4], %[Q4] " CR " row_mask:0xf bank_mask:0xf\n"         \
+    "v_mul_f32_dpp %[Q4], %[Q4], %[Q4] " CR " row_mask:0xf bank_mask:0xf\n"
+    asm volatile("s_nop 1\n"
+                 MSEL_ROWR4("row_shl:1")
+                 MSEL_ROWR4("row_shl:2")
+                 MSEL_ROWR4("row_shl:4")
+                 MSEL_ROWR4("row_shl:8")
+                 : [Q1] "+v"(Q1), [R1] "+v"(R1), [Q2] "+v"(Q2), [R2] "+v"(R2),
+                   [Q3] "+v"(Q3), [R3] "+v"(R3), [Q4] "+v"(Q4), [R4] "+v"(R4));
+#undef MSEL_ROWR4
+}
+
 // Totals of scans whose row levels are done (wave-uniform results):
 //  forward: the composition of all 64 lanes, from the last lane of each row;
 //  suffix:  the composition of all 64 lanes, from the first lane of each row.

@@ -52,6 +52,12 @@ size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states);
 hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float* chunk_states,
                            void* workspace, bool bf16, hipStream_t stream,
                            hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
-hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
+// Zero-fill of up to kFillSlots float buffers in one launch (null slots are skipped).
+constexpr int kFillSlots = 5;
+struct FillList {
+    float* p[kFillSlots];
+    size_t n[kFillSlots];
+};
+hipError_t launch_fill_zero(const FillList& f, hipStream_t stream);
 
 }  // namespace msel

@@ -14,12 +14,11 @@
 //   ddelta_t = dDelta_t * sigmoid(delta_t + bias) with the softplus, dbias += ddelta_t
 //   dD += dy_t u_t       dh0 = a_0 lam_0
 //
-// Four launches, all parallel over chunks:
-//  0. convert: B and C to fp32 rows padded to whole chunks (read by every channel below).
-//  1. summary: one wavefront per (batch, channel, chunk).  For every state n it forms the
-//     chunk's local end state from a zero start (forward) and the adjoint at the chunk's
-//     first step from a zero adjoint beyond the chunk (reverse), both with the lane-local
-//     chains + DPP scans used by the forward kernel, plus sum(Delta) and Delta at the first
+// Three launches, all parallel over chunks:
+//  1. summary: one wavefront per (batch, chunk, few channels).  For every state n it forms
+//     the chunk's local end state from a zero start (forward) and the adjoint at the chunk's
+//     first step from a zero adjoint beyond the chunk (reverse), both with lane-local chains
+//     and DPP row scans finished through readlane, plus sum(Delta) and Delta at the first
 //     step.
 //  2. link: one thread per (batch, channel, state) walks the chunks:
 //       H_{c+1} = exp(A sum Delta_c) H_c + S_c                      (H_0 = h0)
@@ -27,14 +26,15 @@
 //     H_c is the state entering chunk c, G_c = a lam at the first step after chunk c; the
 //     walk ends with G = a_0 lam_0 = dh0.  (This is the chunk carry of page 4, Appendix D,
 //     run once forward for the states and once backward for the adjoint.)
-//  3. main: one workgroup per (batch, chunk, group of channels).  Each wavefront takes one
+//  3. main: about one workgroup per compute unit, each on one (batch row, chunk) and a range
+//     of channels; B and C of that chunk are staged in LDS once.  Each wavefront takes one
 //     channel at a time: the states inside the chunk are rebuilt from H_c, the adjoint from
 //     G_c, and every gradient term is formed in registers.  dB and dC, which sum over
-//     channels, are accumulated over all the group's channels in LDS and written to HBM once
-//     per workgroup with fp32 global atomics.  LDS float atomics are avoided (they run at a
-//     small fraction of the plain LDS rate on this chip): the wavefronts visit the states in
-//     rotated order, one state per wavefront per step, so each accumulator slot has one
-//     writer per step and a plain read-add-write suffices.
+//     channels, are accumulated over all the workgroup's channels in LDS and written to HBM
+//     once per workgroup with fp32 global atomics.  LDS float atomics are avoided (they run at
+//     a small fraction of the plain LDS rate on this chip): the wavefronts visit the states
+//     in rotated order and hand each state's rows on in a ring, so a plain read-add-write
+//     suffices.
 #include "msel_device.hpp"
 #include "msel_kernels.hpp"
 
@@ -45,8 +45,6 @@ constexpr int kSumWaves = 4;
 constexpr int kMainWaves = 12;  // 3 per SIMD: the main kernel needs ~160 VGPRs
 
 struct BwdWork {
-    float* Bf;      // [B*N*nch*kChunk]: B as fp32, rows zero-padded to whole chunks
-    float* Cf;      // [B*N*nch*kChunk]: C likewise
     float* H;       // [B*D*nch*N]: chunk-start states (may be the caller's chunk_states)
     float* G;       // [B*D*nch*N]: adjoint carry after each chunk
     float* sdt;     // [B*D*nch]: sum of Delta over the chunk
@@ -54,124 +52,121 @@ struct BwdWork {
     int want_fwd;   // the summary/link passes also build H
 };
 
+// Channels per wavefront in the summary: B and C rows are read (and converted) once per state
+// and used for all of them; each channel's local chains are independent instruction streams.
+template <bool FWD>
+constexpr int sum_channels() { return FWD ? 2 : 4; }
+
 template <typename T, bool VEC, bool HAS_Z, bool SOFTPLUS, bool FWD>
 __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams p, GradParams g,
                                                                      BwdWork w) {
     constexpr int K = kChunk / 64;
+    constexpr int R = sum_channels<FWD>();
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nch = p.nchunks;
-    const int idx = blockIdx.x * kSumWaves + wave;  // (b*D + d) * nch + c
-    if (idx >= p.B * p.D * nch) return;
-    const int ch = idx / nch;
-    const int c = idx - ch * nch;
-    const int b = ch / p.D;
-    const int d = ch - b * p.D;
+    const int dgroups = (p.D + R - 1) / R;
+    const int idx = blockIdx.x * kSumWaves + wave;  // ((b * nch) + c) * dgroups + dg
+    if (idx >= p.B * nch * dgroups) return;
+    const int dg = idx % dgroups;
+    const int bc = idx / dgroups;
+    const int c = bc % nch;
+    const int b = bc / nch;
     const int L = p.L;
     const int N = p.N;
-    const size_t row = static_cast<size_t>(ch) * L;
-    const T* __restrict__ dl = static_cast<const T*>(p.delta) + row;
-    const T* __restrict__ go = static_cast<const T*>(g.dout) + row;
-    // fp32 copies of B and C with rows padded to whole chunks (built by the convert pass)
-    const int Lp = nch * kChunk;
-    const float* __restrict__ Bb = w.Bf + static_cast<size_t>(b) * N * Lp;
-    const float* __restrict__ Cb = w.Cf + static_cast<size_t>(b) * N * Lp;
-    const float bias = p.bias ? p.bias[d] : 0.0f;
-    const float* __restrict__ Arow = p.A + static_cast<size_t>(d) * N;
     const int t0 = c * kChunk + lane * K;
+    const T* __restrict__ Bg = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
+    const T* __restrict__ Cg = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
 
-    float dt[K], dy[K], du[FWD ? K : 1];
-    float sum_dt = 0.0f;
-    {
+    int dch[R];        // channel of each slot (clamped; `live` says whether it exists)
+    bool live[R];
+    float Av[R];       // lane n holds A[d, n] * log2(e)
+    float dt[R][K], dy[R][K], du[FWD ? R : 1][K];
+    float sum_dt[R], rsum_dt[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int d = dg * R + r;
+        live[r] = d < p.D;
+        dch[r] = live[r] ? d : p.D - 1;
+        const size_t row = (static_cast<size_t>(b) * p.D + dch[r]) * L;
+        const float bias = p.bias ? p.bias[dch[r]] : 0.0f;
+        Av[r] = (lane < N) ? p.A[static_cast<size_t>(dch[r]) * N + lane] * kLog2e : 0.0f;
         float dd[K], gg[K];
-        load_k<T, K, VEC>(dl, t0, L, dd, 0.0f);
-        load_k<T, K, VEC>(go, t0, L, gg, 0.0f);
+        load_k<T, K, VEC>(static_cast<const T*>(p.delta) + row, t0, L, dd, 0.0f);
+        load_k<T, K, VEC>(static_cast<const T*>(g.dout) + row, t0, L, gg, 0.0f);
         float zz[HAS_Z ? K : 1], uu[FWD ? K : 1];
         if constexpr (HAS_Z) load_k<T, K, VEC>(static_cast<const T*>(p.z) + row, t0, L, zz, 0.0f);
         if constexpr (FWD) load_k<T, K, VEC>(static_cast<const T*>(p.u) + row, t0, L, uu, 0.0f);
+        sum_dt[r] = 0.0f;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const float x = dd[k] + bias;
             const float v = SOFTPLUS ? softplus_f(x) : x;
-            dt[k] = (t0 + k < L) ? v : 0.0f;
-            sum_dt += dt[k];
-            if constexpr (HAS_Z) dy[k] = gg[k] * zz[k] * sigmoid_f(zz[k]);
-            else dy[k] = gg[k];
-            if constexpr (FWD) du[k] = dt[k] * uu[k];
+            dt[r][k] = (t0 + k < L) ? v : 0.0f;
+            sum_dt[r] += dt[r][k];
+            if constexpr (HAS_Z) dy[r][k] = gg[k] * zz[k] * sigmoid_f(zz[k]);
+            else dy[r][k] = gg[k];
+            if constexpr (FWD) du[r][k] = dt[r][k] * uu[k];
         }
-    }
-    // the adjoint's transition inside a lane multiplies a_{t+1}: this lane's steps 1..K-1
-    // and the next lane's first step
-    const float rsum_dt = sum_dt - dt[0] + shift_down(dt[0], 0.0f);
-    const float chunk_dt = wave_sum_fused(sum_dt);
-    if (lane == 0) {
-        w.sdt[idx] = chunk_dt;
-        w.dfirst[idx] = dt[0];
+        // the adjoint's transition inside a lane multiplies a_{t+1}: this lane's steps
+        // 1..K-1 and the next lane's first step
+        rsum_dt[r] = sum_dt[r] - dt[r][0] + shift_down(dt[r][0], 0.0f);
+        const float chunk_dt = wave_sum_fused(sum_dt[r]);
+        if (lane == 0 && live[r]) {
+            const size_t slot = (static_cast<size_t>(b) * p.D + dch[r]) * nch + c;
+            w.sdt[slot] = chunk_dt;
+            w.dfirst[slot] = dt[r][0];
+        }
     }
 
-    // Two states per iteration (the second repeats the first when N is odd), so that the
-    // lane-local chains and the row scans of both are independent instruction streams.
-    // Per state: forward local end state from a zero start (only when H is rebuilt here) and
-    // the adjoint at the chunk's first step from a zero adjoint after the chunk.
-    Raw<float, K> B1, C1, B2, C2;
-    auto fetch = [&](int n, Raw<float, K>& Bn, Raw<float, K>& Cn) __attribute__((always_inline)) {
-        if constexpr (FWD) load_raw<float, K, true>(Bb + static_cast<size_t>(n) * Lp, t0, Lp, Bn);
-        load_raw<float, K, true>(Cb + static_cast<size_t>(n) * Lp, t0, Lp, Cn);
-    };
-    fetch(0, B1, C1);
-    fetch(N > 1 ? 1 : 0, B2, C2);
-    for (int n = 0; n < N; n += 2) {
-        const int n2 = (n + 1 < N) ? n + 1 : n;
-        float bv1[K], cv1[K], bv2[K], cv2[K];
-        if constexpr (FWD) {
-            unpack(B1, bv1);
-            unpack(B2, bv2);
+    // Per state: the forward local end state from a zero start (only when H is rebuilt here)
+    // and the adjoint at the chunk's first step from a zero adjoint after the chunk.
+    Raw<T, K> Bn, Cn;
+    if constexpr (FWD) load_raw<T, K, VEC>(Bg, t0, L, Bn);
+    load_raw<T, K, VEC>(Cg, t0, L, Cn);
+    for (int n = 0; n < N; ++n) {
+        float bv[K], cv[K];
+        if constexpr (FWD) unpack(Bn, bv);
+        unpack(Cn, cv);
+        if (n + 1 < N) {  // the next state's rows
+            if constexpr (FWD)
+                load_raw<T, K, VEC>(Bg + static_cast<size_t>(n + 1) * L, t0, L, Bn);
+            load_raw<T, K, VEC>(Cg + static_cast<size_t>(n + 1) * L, t0, L, Cn);
         }
-        unpack(C1, cv1);
-        unpack(C2, cv2);
-        if (n + 2 < N) {  // prefetch the next pair's rows
-            fetch(n + 2, B1, C1);
-            fetch(n + 3 < N ? n + 3 : n + 2, B2, C2);
-        }
-        const float A1 = Arow[n] * kLog2e, A2 = Arow[n2] * kLog2e;
-        float a1[K], a2[K];
+        float P[R], S[R], Q[R], Sr[R];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            a1[k] = exp2_hw(dt[k] * A1);
-            a2[k] = exp2_hw(dt[k] * A2);
-        }
-        float P1 = 1.0f, S1 = 0.0f, P2 = 1.0f, S2 = 0.0f;
-        if constexpr (FWD) {
+        for (int r = 0; r < R; ++r) {
+            const float An2 = readlane(Av[r], n);
+            float a[K];
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                S1 = fmaf(a1[k], S1, du[k] * bv1[k]);
-                S2 = fmaf(a2[k], S2, du[k] * bv2[k]);
+            for (int k = 0; k < K; ++k) a[k] = exp2_hw(dt[r][k] * An2);
+            P[r] = 1.0f;
+            S[r] = 0.0f;
+            if constexpr (FWD) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) S[r] = fmaf(a[k], S[r], du[r][k] * bv[k]);
+                P[r] = exp2_hw(An2 * sum_dt[r]);
             }
-            P1 = exp2_hw(A1 * sum_dt);
-            P2 = exp2_hw(A2 * sum_dt);
-        }
-        const float e1 = shift_down(a1[0], 1.0f), e2 = shift_down(a2[0], 1.0f);
-        float R1 = 0.0f, R2 = 0.0f;
+            const float e = shift_down(a[0], 1.0f);
+            float acc = 0.0f;
 #pragma unroll
-        for (int k = K - 1; k >= 0; --k) {
-            const float cdk1 = cv1[k] * dy[k], cdk2 = cv2[k] * dy[k];
-            R1 = fmaf((k == K - 1) ? e1 : a1[k + 1], R1, cdk1);
-            R2 = fmaf((k == K - 1) ? e2 : a2[k + 1], R2, cdk2);
+            for (int k = K - 1; k >= 0; --k)
+                acc = fmaf((k == K - 1) ? e : a[k + 1], acc, cv[k] * dy[r][k]);
+            Sr[r] = acc;
+            Q[r] = exp2_hw(An2 * rsum_dt[r]);
         }
-        float Q1 = exp2_hw(A1 * rsum_dt), Q2 = exp2_hw(A2 * rsum_dt);
-        if constexpr (FWD) scan_rows4(P1, S1, Q1, R1, P2, S2, Q2, R2);
-        else scan_rows2_rev(Q1, R1, Q2, R2);
-        const float G1 = rev_rows_total(Q1, R1), G2 = rev_rows_total(Q2, R2);
-        if constexpr (FWD) {
-            const float H1 = fwd_rows_total(P1, S1), H2 = fwd_rows_total(P2, S2);
-            if (lane == 0) {
-                w.H[static_cast<size_t>(idx) * N + n] = H1;
-                w.H[static_cast<size_t>(idx) * N + n2] = H2;
+        if constexpr (FWD) scan_rows4(P[0], S[0], Q[0], Sr[0], P[1], S[1], Q[1], Sr[1]);
+        else scan_rows4_rev(Q[0], Sr[0], Q[1], Sr[1], Q[2], Sr[2], Q[3], Sr[3]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float G = rev_rows_total(Q[r], Sr[r]);
+            float H = 0.0f;
+            if constexpr (FWD) H = fwd_rows_total(P[r], S[r]);
+            if (lane == 0 && live[r]) {
+                const size_t slot = ((static_cast<size_t>(b) * p.D + dch[r]) * nch + c) * N + n;
+                w.G[slot] = G;
+                if constexpr (FWD) w.H[slot] = H;
             }
-        }
-        if (lane == 0) {
-            w.G[static_cast<size_t>(idx) * N + n] = G1;
-            w.G[static_cast<size_t>(idx) * N + n2] = G2;
         }
     }
 }
@@ -584,38 +579,27 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
     }
 }
 
-// B and C as fp32 rows padded with zeros to whole chunks: [B][N][nch*kChunk].
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_convert_kernel(ScanParams p, BwdWork w) {
-    const int Lp = p.nchunks * kChunk;
-    const size_t total = static_cast<size_t>(p.B) * p.N * Lp;
+// Zeroes up to kFillSlots buffers in one launch (the reduction targets of the backward).
+__global__ void fill_zero_kernel(FillList f) {
     const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-         i += stride) {
-        const size_t rown = i / Lp;
-        const int t = static_cast<int>(i - rown * Lp);
-        float vb = 0.0f, vc = 0.0f;
-        if (t < p.L) {
-            vb = Elem<T>::load1(static_cast<const T*>(p.Bm) + rown * p.L + t);
-            vc = Elem<T>::load1(static_cast<const T*>(p.Cm) + rown * p.L + t);
-        }
-        w.Bf[i] = vb;
-        w.Cf[i] = vc;
+    for (int s = 0; s < kFillSlots; ++s) {
+        float* __restrict__ p = f.p[s];
+        if (p == nullptr) continue;
+        for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < f.n[s];
+             i += stride)
+            p[i] = 0.0f;
     }
 }
 
-__global__ void fill_zero_kernel(float* __restrict__ p, size_t n) {
-    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-    for (; i < n; i += stride) p[i] = 0.0f;
-}
-
-hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream) {
-    if (p == nullptr || n == 0) return hipSuccess;
-    size_t blocks = (n + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
+hipError_t launch_fill_zero(const FillList& f, hipStream_t stream) {
+    size_t total = 0;
+    for (int s = 0; s < kFillSlots; ++s)
+        if (f.p[s] != nullptr) total += f.n[s];
+    if (total == 0) return hipSuccess;
+    size_t blocks = (total + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
     hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                       stream, p, n);
+                       stream, f);
     return hipGetLastError();
 }
 
@@ -623,9 +607,8 @@ size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states) {
     const size_t nch = (static_cast<size_t>(L) + kChunk - 1) / kChunk;
     const size_t states = static_cast<size_t>(B) * D * nch * N * sizeof(float);
     const size_t per_chunk = static_cast<size_t>(B) * D * nch * sizeof(float);
-    const size_t rows = static_cast<size_t>(B) * N * nch * kChunk * sizeof(float);
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-    return 2 * up(rows) + (need_states ? up(states) : 0) + up(states) + 2 * up(per_chunk);
+    return (need_states ? up(states) : 0) + up(states) + 2 * up(per_chunk);
 }
 
 namespace {
@@ -660,18 +643,16 @@ struct Timing {
 template <typename T, bool VEC, bool HAS_Z, bool SP>
 hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hipStream_t s,
                   Timing tm) {
-    hipLaunchKernelGGL(bwd_convert_kernel<T>, dim3(1024), dim3(256), 0, s, p, w);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int rows = p.B * p.D * p.nchunks;
-    dim3 sgrid((rows + kSumWaves - 1) / kSumWaves), sblock(64 * kSumWaves);
+    const int per_sum = w.want_fwd ? sum_channels<true>() : sum_channels<false>();
+    const int sum_waves = p.B * p.nchunks * ((p.D + per_sum - 1) / per_sum);
+    dim3 sgrid((sum_waves + kSumWaves - 1) / kSumWaves), sblock(64 * kSumWaves);
     if (w.want_fwd)
         hipLaunchKernelGGL((bwd_summary_kernel<T, VEC, HAS_Z, SP, true>), sgrid, sblock, 0, s, p,
                            g, w);
     else
         hipLaunchKernelGGL((bwd_summary_kernel<T, VEC, HAS_Z, SP, false>), sgrid, sblock, 0, s, p,
                            g, w);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int links = p.B * p.D * p.N;
     dim3 lgrid((links + 255) / 256), lblock(256);
@@ -728,14 +709,9 @@ hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float
     const size_t nch = static_cast<size_t>(p.nchunks);
     const size_t states = static_cast<size_t>(p.B) * p.D * nch * p.N * sizeof(float);
     const size_t per_chunk = static_cast<size_t>(p.B) * p.D * nch * sizeof(float);
-    const size_t rows = static_cast<size_t>(p.B) * p.N * nch * kChunk * sizeof(float);
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     char* ws = static_cast<char*>(workspace);
     BwdWork w;
-    w.Bf = reinterpret_cast<float*>(ws);
-    ws += up(rows);
-    w.Cf = reinterpret_cast<float*>(ws);
-    ws += up(rows);
     w.want_fwd = chunk_states == nullptr;
     if (w.want_fwd) {
         w.H = reinterpret_cast<float*>(ws);

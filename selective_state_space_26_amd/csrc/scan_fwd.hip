@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
     const T* __restrict__ Cb = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
     const float bias = p.bias ? p.bias[d] : 0.0f;
     const float Dd = p.Dv ? p.Dv[d] : 0.0f;
-    const float* __restrict__ Arow = p.A + static_cast<size_t>(d) * N;
+    // lane n holds A[d, n] * log2(e): one vector load, read per state with readlane
+    const float Av = (lane < N) ? p.A[static_cast<size_t>(d) * N + lane] * kLog2e : 0.0f;
 
     float carry = 0.0f;  // lane n: state h_n entering the current tile
     if (p.h0 != nullptr && lane < N) carry = p.h0[static_cast<size_t>(ch) * N + lane];
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
             cs_dst = p.chunk_states + (static_cast<size_t>(ch) * p.nchunks + t0 / kChunk) * N;
 
         for (int n = 0; n < N; ++n) {
-            const float An = Arow[n] * kLog2e;
+            const float An = readlane(Av, n);
             float a[K], bb[K], bc[K];
             load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, bc);
             float h = 0.0f;

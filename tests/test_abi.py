@@ -187,9 +187,8 @@ def test_bwd_workspace_rules(lib):
     nch = -(-1000 // T)
     up = lambda x: (x + 255) // 256 * 256
     states, per_chunk = 2 * 3 * nch * 16 * 4, 2 * 3 * nch * 4
-    rows = 2 * 16 * nch * T * 4   # fp32 copies of B and C padded to whole chunks
     need = lib.msel_scan_bwd_workspace_bytes(ctypes.byref(a))
-    assert need == 2 * up(rows) + 2 * up(states) + 2 * up(per_chunk)
+    assert need == 2 * up(states) + 2 * up(per_chunk)
     assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), None, 0) == 6
     ws = _addr()
     assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), ws, need - 1) == 6
@@ -201,7 +200,7 @@ def test_bwd_workspace_rules(lib):
     # with caller-provided chunk states the workspace only holds the adjoint carries
     a.chunk_states = _addr()
     need2 = lib.msel_scan_bwd_workspace_bytes(ctypes.byref(a))
-    assert need2 == 2 * up(rows) + up(states) + 2 * up(per_chunk)
+    assert need2 == up(states) + 2 * up(per_chunk)
     assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), ws, need2) == 0
     assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), a.chunk_states, need2) == 7
 
