@@ -53,6 +53,7 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
     if (p.h0 != nullptr && lane < N) carry = p.h0[static_cast<size_t>(ch) * N + lane];
 
     constexpr int TILE = 64 * K;
+    static_assert(TILE % kChunk == 0, "a tile must hold whole chunks");
     for (int tile = 0; tile < L; tile += TILE) {
         const int t0 = tile + lane * K;
         float dt[K], du[K], y[K];
@@ -71,9 +72,13 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
                 sum_dt += dt[k];
             }
         }
-        float* cs_dst = nullptr;  // lanes that start a chunk record the state entering them
-        if (p.chunk_states != nullptr && t0 < L && (t0 % kChunk) == 0)
-            cs_dst = p.chunk_states + (static_cast<size_t>(ch) * p.nchunks + t0 / kChunk) * N;
+        // States entering the lanes that start a chunk: gathered into lane-distributed
+        // registers (lane n = state n), one per chunk of the tile, and stored after the state
+        // loop -- a store inside the loop would make every later load wait for it.
+        constexpr int kCpt = TILE / kChunk;  // chunks per tile
+        float csv[kCpt];
+#pragma unroll
+        for (int q = 0; q < kCpt; ++q) csv[q] = 0.0f;
 
         for (int n = 0; n < N; ++n) {
             const float An = readlane(Av, n);
@@ -93,7 +98,9 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
             const float Q = fmaf(P, cn, S);       // state after the lane's last step
             const float hin = shift_up(Q, cn);    // state entering the lane
             carry = writelane(readlane(Q, 63), n, carry);
-            if (cs_dst != nullptr) cs_dst[n] = hin;
+#pragma unroll
+            for (int q = 0; q < kCpt; ++q)
+                csv[q] = writelane(readlane(hin, q * (kChunk / K)), n, csv[q]);
 
             load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n) * L, t0, L, bc);
             h = hin;
@@ -110,6 +117,15 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
             for (int k = 0; k < K; ++k) y[k] *= zz[k] * sigmoid_f(zz[k]);
         }
         store_k<T, K, VEC>(out, t0, L, y);
+        if (p.chunk_states != nullptr && lane < N) {
+#pragma unroll
+            for (int q = 0; q < kCpt; ++q) {
+                const int cidx = tile / kChunk + q;
+                if (cidx < p.nchunks)
+                    p.chunk_states[(static_cast<size_t>(ch) * p.nchunks + cidx) * N + lane] =
+                        csv[q];
+            }
+        }
     }
     if (p.final_state != nullptr && lane < N)
         p.final_state[static_cast<size_t>(ch) * N + lane] = carry;
