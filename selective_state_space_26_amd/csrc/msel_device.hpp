@@ -557,4 +557,46 @@ __device__ __forceinline__ float wave_sum_fused(float v) {
     return readlane(v, 63);
 }
 
+// Inclusive prefix sum over the 64 lanes (lane 0 first), fused DPP adds: a lane whose DPP
+// source does not exist is not written, i.e. adds nothing.
+__device__ __forceinline__ float wave_incl_sum(float v) {
+    asm volatile("s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_shr:1 row_mask:0xf bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_shr:2 row_mask:0xf bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_shr:4 row_mask:0xf bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_shr:8 row_mask:0xf bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_bcast:15 row_mask:0xa bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_bcast:31 row_mask:0xc bank_mask:0xf\n"
+                 : [v] "+v"(v));
+    return v;
+}
+
+// Four independent 64-lane sums, interleaved so that no wait states are needed; lane 63 of
+// each result holds the total (returned wave-uniform).
+__device__ __forceinline__ void wave_sum4(float& a, float& b, float& c, float& d) {
+#define MSEL_SUM4(CTRL, RMASK)                                                       \
+    "v_add_f32_dpp %[a], %[a], %[a] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"     \
+    "v_add_f32_dpp %[b], %[b], %[b] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"     \
+    "v_add_f32_dpp %[c], %[c], %[c] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"     \
+    "v_add_f32_dpp %[d], %[d], %[d] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"
+    asm volatile("s_nop 1\n"
+                 MSEL_SUM4("row_shr:1", "0xf")
+                 MSEL_SUM4("row_shr:2", "0xf")
+                 MSEL_SUM4("row_shr:4", "0xf")
+                 MSEL_SUM4("row_shr:8", "0xf")
+                 MSEL_SUM4("row_bcast:15", "0xa")
+                 MSEL_SUM4("row_bcast:31", "0xc")
+                 : [a] "+v"(a), [b] "+v"(b), [c] "+v"(c), [d] "+v"(d));
+#undef MSEL_SUM4
+    a = readlane(a, 63);
+    b = readlane(b, 63);
+    c = readlane(c, 63);
+    d = readlane(d, 63);
+}
+
 }  // namespace msel

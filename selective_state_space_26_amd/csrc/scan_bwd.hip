@@ -53,15 +53,23 @@ struct BwdWork {
 };
 
 // Channels per wavefront in the summary: B and C rows are read (and converted) once per state
-// and used for all of them; each channel's local chains are independent instruction streams.
+// and used for all of them.
 template <bool FWD>
 constexpr int sum_channels() { return FWD ? 2 : 4; }
 
+// The summary needs only chunk totals, not the states at every step, so it uses the closed
+// form of the recurrence instead of a scan: with E_t = sum of Delta over the chunk's steps
+// 1..t (after its first step) and F'_t = sum of Delta over the steps after t,
+//   adjoint at the chunk's first step, zero beyond the chunk:  sum_t exp(A E_t) C_t dy_t
+//   end state from a zero start:                                sum_t exp(A F'_t) Delta_t u_t B_t
+// (products of a = exp(Delta A) over a run of steps are exp(A * the run's sum of Delta)).  One
+// prefix sum of Delta per channel replaces a scan per state, and every term is independent.
 template <typename T, bool VEC, bool HAS_Z, bool SOFTPLUS, bool FWD>
 __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams p, GradParams g,
                                                                      BwdWork w) {
     constexpr int K = kChunk / 64;
     constexpr int R = sum_channels<FWD>();
+    static_assert(FWD ? R == 2 : R == 4, "the reductions are done four at a time");
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nch = p.nchunks;
@@ -81,8 +89,8 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
     int dch[R];        // channel of each slot (clamped; `live` says whether it exists)
     bool live[R];
     float Av[R];       // lane n holds A[d, n] * log2(e)
-    float dt[R][K], dy[R][K], du[FWD ? R : 1][K];
-    float sum_dt[R], rsum_dt[R];
+    float E[R][K], dy[R][K];
+    float Fs[FWD ? R : 1][K], du[FWD ? R : 1][K];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int d = dg * R + r;
@@ -91,36 +99,41 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
         const size_t row = (static_cast<size_t>(b) * p.D + dch[r]) * L;
         const float bias = p.bias ? p.bias[dch[r]] : 0.0f;
         Av[r] = (lane < N) ? p.A[static_cast<size_t>(dch[r]) * N + lane] * kLog2e : 0.0f;
-        float dd[K], gg[K];
+        float dd[K], gg[K], dt[K];
         load_k<T, K, VEC>(static_cast<const T*>(p.delta) + row, t0, L, dd, 0.0f);
         load_k<T, K, VEC>(static_cast<const T*>(g.dout) + row, t0, L, gg, 0.0f);
         float zz[HAS_Z ? K : 1], uu[FWD ? K : 1];
         if constexpr (HAS_Z) load_k<T, K, VEC>(static_cast<const T*>(p.z) + row, t0, L, zz, 0.0f);
         if constexpr (FWD) load_k<T, K, VEC>(static_cast<const T*>(p.u) + row, t0, L, uu, 0.0f);
-        sum_dt[r] = 0.0f;
+        float run = 0.0f;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const float x = dd[k] + bias;
             const float v = SOFTPLUS ? softplus_f(x) : x;
-            dt[r][k] = (t0 + k < L) ? v : 0.0f;
-            sum_dt[r] += dt[r][k];
+            dt[k] = (t0 + k < L) ? v : 0.0f;  // Delta = 0 past the end: identity step
             if constexpr (HAS_Z) dy[r][k] = gg[k] * zz[k] * sigmoid_f(zz[k]);
             else dy[r][k] = gg[k];
-            if constexpr (FWD) du[r][k] = dt[r][k] * uu[k];
+            if constexpr (FWD) du[r][k] = dt[k] * uu[k];
+            run += dt[k];
+            E[r][k] = run;  // inclusive within the lane for now
         }
-        // the adjoint's transition inside a lane multiplies a_{t+1}: this lane's steps
-        // 1..K-1 and the next lane's first step
-        rsum_dt[r] = sum_dt[r] - dt[r][0] + shift_down(dt[r][0], 0.0f);
-        const float chunk_dt = wave_sum_fused(sum_dt[r]);
+        const float incl = wave_incl_sum(run);
+        const float before = shift_up(incl, 0.0f);  // Delta summed over the earlier lanes
+        const float total = readlane(incl, 63);
+        const float first = readlane(dt[0], 0);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float F = before + E[r][k];  // sum of Delta from the chunk start to t
+            if constexpr (FWD) Fs[r][k] = total - F;
+            E[r][k] = F - first;
+        }
         if (lane == 0 && live[r]) {
             const size_t slot = (static_cast<size_t>(b) * p.D + dch[r]) * nch + c;
-            w.sdt[slot] = chunk_dt;
-            w.dfirst[slot] = dt[r][0];
+            w.sdt[slot] = total;
+            w.dfirst[slot] = first;
         }
     }
 
-    // Per state: the forward local end state from a zero start (only when H is rebuilt here)
-    // and the adjoint at the chunk's first step from a zero adjoint after the chunk.
     Raw<T, K> Bn, Cn;
     if constexpr (FWD) load_raw<T, K, VEC>(Bg, t0, L, Bn);
     load_raw<T, K, VEC>(Cg, t0, L, Cn);
@@ -133,39 +146,27 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
                 load_raw<T, K, VEC>(Bg + static_cast<size_t>(n + 1) * L, t0, L, Bn);
             load_raw<T, K, VEC>(Cg + static_cast<size_t>(n + 1) * L, t0, L, Cn);
         }
-        float P[R], S[R], Q[R], Sr[R];
+        float acc[4];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float An2 = readlane(Av[r], n);
-            float a[K];
+            const float A2 = readlane(Av[r], n);
+            float sg = 0.0f, sh = 0.0f;
 #pragma unroll
-            for (int k = 0; k < K; ++k) a[k] = exp2_hw(dt[r][k] * An2);
-            P[r] = 1.0f;
-            S[r] = 0.0f;
-            if constexpr (FWD) {
-#pragma unroll
-                for (int k = 0; k < K; ++k) S[r] = fmaf(a[k], S[r], du[r][k] * bv[k]);
-                P[r] = exp2_hw(An2 * sum_dt[r]);
+            for (int k = 0; k < K; ++k) {
+                sg = fmaf(exp2_hw(A2 * E[r][k]), cv[k] * dy[r][k], sg);
+                if constexpr (FWD) sh = fmaf(exp2_hw(A2 * Fs[r][k]), du[r][k] * bv[k], sh);
             }
-            const float e = shift_down(a[0], 1.0f);
-            float acc = 0.0f;
-#pragma unroll
-            for (int k = K - 1; k >= 0; --k)
-                acc = fmaf((k == K - 1) ? e : a[k + 1], acc, cv[k] * dy[r][k]);
-            Sr[r] = acc;
-            Q[r] = exp2_hw(An2 * rsum_dt[r]);
+            acc[r] = sg;
+            if constexpr (FWD) acc[2 + r] = sh;
         }
-        if constexpr (FWD) scan_rows4(P[0], S[0], Q[0], Sr[0], P[1], S[1], Q[1], Sr[1]);
-        else scan_rows4_rev(Q[0], Sr[0], Q[1], Sr[1], Q[2], Sr[2], Q[3], Sr[3]);
+        wave_sum4(acc[0], acc[1], acc[2], acc[3]);
+        if (lane == 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float G = rev_rows_total(Q[r], Sr[r]);
-            float H = 0.0f;
-            if constexpr (FWD) H = fwd_rows_total(P[r], S[r]);
-            if (lane == 0 && live[r]) {
+            for (int r = 0; r < R; ++r) {
+                if (!live[r]) continue;
                 const size_t slot = ((static_cast<size_t>(b) * p.D + dch[r]) * nch + c) * N + n;
-                w.G[slot] = G;
-                if constexpr (FWD) w.H[slot] = H;
+                w.G[slot] = acc[r];
+                if constexpr (FWD) w.H[slot] = acc[2 + r];
             }
         }
     }
