@@ -74,65 +74,72 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Load K consecutive elements row[t0 .. t0+K) as fp32; out-of-range elements read `fill`.
-// VEC: the row base is 16-byte aligned and t0 is a multiple of the vector width.
-template <typename T, int K, bool VEC>
-__device__ __forceinline__ void load_k(const T* __restrict__ row, int t0, int L, float (&v)[K],
-                                       float fill) {
-    static_assert(K % Elem<T>::kPerVec == 0, "K must be a whole number of 16-byte vectors");
-    if (VEC && t0 + K <= L) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row + t0);
-#pragma unroll
-        for (int j = 0; j < K / Elem<T>::kPerVec; ++j) {
-            u32x4 w = __builtin_nontemporal_load(p + j);
-            if constexpr (sizeof(T) == 4) {
-                v[4 * j + 0] = __uint_as_float(w.x);
-                v[4 * j + 1] = __uint_as_float(w.y);
-                v[4 * j + 2] = __uint_as_float(w.z);
-                v[4 * j + 3] = __uint_as_float(w.w);
-            } else {
-                v[8 * j + 0] = bf16lo(w.x);
-                v[8 * j + 1] = bf16hi(w.x);
-                v[8 * j + 2] = bf16lo(w.y);
-                v[8 * j + 3] = bf16hi(w.y);
-                v[8 * j + 4] = bf16lo(w.z);
-                v[8 * j + 5] = bf16hi(w.z);
-                v[8 * j + 6] = bf16lo(w.w);
-                v[8 * j + 7] = bf16hi(w.w);
-            }
-        }
+// Unpack one 16-byte vector of T into fp32 values v[j*kPerVec ...].
+template <typename T, int K>
+__device__ __forceinline__ void unpack_vec(u32x4 w, int j, float (&v)[K]) {
+    if constexpr (sizeof(T) == 4) {
+        v[4 * j + 0] = __uint_as_float(w.x);
+        v[4 * j + 1] = __uint_as_float(w.y);
+        v[4 * j + 2] = __uint_as_float(w.z);
+        v[4 * j + 3] = __uint_as_float(w.w);
     } else {
-#pragma unroll
-        for (int k = 0; k < K; ++k) v[k] = (t0 + k < L) ? Elem<T>::load1(row + t0 + k) : fill;
+        v[8 * j + 0] = bf16lo(w.x);
+        v[8 * j + 1] = bf16hi(w.x);
+        v[8 * j + 2] = bf16lo(w.y);
+        v[8 * j + 3] = bf16hi(w.y);
+        v[8 * j + 4] = bf16lo(w.z);
+        v[8 * j + 5] = bf16hi(w.z);
+        v[8 * j + 6] = bf16lo(w.w);
+        v[8 * j + 7] = bf16hi(w.w);
     }
 }
 
-// Same as load_k but through the normal (cached) path: for B and C, which every channel of a
-// batch row re-reads.
+// Buffer resource of one row of L elements (the pointer is wave-uniform).  Buffer accesses
+// are range-checked by the hardware: a load past the end returns zeros and a store past the
+// end is dropped, so no branch or select is needed at the ragged end (an if/else around loads
+// would make the second arm wait for the first arm's loads).  The third descriptor dword is
+// the gfx9 raw-buffer format (32-bit data, no swizzle).
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const T* row, int L) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(row), 0,
+                                             L * static_cast<int>(sizeof(T)), 0x00020000);
+}
+
+// One 16-byte vector of a VEC row holding steps [t, t + width): with the row 16-byte aligned,
+// L a multiple of the vector width and t a multiple of it, the vector is wholly in range or
+// wholly past the end (then it reads zeros).  NT: non-temporal (streaming) hint.
+template <typename T, bool NT>
+__device__ __forceinline__ u32x4 load_vec(const T* __restrict__ row, int t, int L) {
+    return __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(row, L), t * static_cast<int>(sizeof(T)),
+                                                     0, NT ? 2 : 0));
+}
+
+// Load K consecutive elements row[t0 .. t0+K) as fp32; out-of-range elements read 0.
+// VEC: the row base is 16-byte aligned, L is a multiple of the vector width and t0 a
+// multiple of K.  Streaming (non-temporal) loads: for rows read once.
+template <typename T, int K, bool VEC>
+__device__ __forceinline__ void load_k(const T* __restrict__ row, int t0, int L, float (&v)[K],
+                                       float /*fill: always 0*/) {
+    static_assert(K % Elem<T>::kPerVec == 0, "K must be a whole number of 16-byte vectors");
+    constexpr int VW = Elem<T>::kPerVec;
+    if constexpr (VEC) {
+#pragma unroll
+        for (int j = 0; j < K / VW; ++j) unpack_vec<T, K>(load_vec<T, true>(row, t0 + j * VW, L), j, v);
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = (t0 + k < L) ? Elem<T>::load1(row + t0 + k) : 0.0f;
+    }
+}
+
+// Same as load_k but through the normal (cached) path, for rows that are read again.
 template <typename T, int K, bool VEC>
 __device__ __forceinline__ void load_k_cached(const T* __restrict__ row, int t0, int L,
                                               float (&v)[K]) {
-    if (VEC && t0 + K <= L) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row + t0);
+    constexpr int VW = Elem<T>::kPerVec;
+    if constexpr (VEC) {
 #pragma unroll
-        for (int j = 0; j < K / Elem<T>::kPerVec; ++j) {
-            u32x4 w = p[j];
-            if constexpr (sizeof(T) == 4) {
-                v[4 * j + 0] = __uint_as_float(w.x);
-                v[4 * j + 1] = __uint_as_float(w.y);
-                v[4 * j + 2] = __uint_as_float(w.z);
-                v[4 * j + 3] = __uint_as_float(w.w);
-            } else {
-                v[8 * j + 0] = bf16lo(w.x);
-                v[8 * j + 1] = bf16hi(w.x);
-                v[8 * j + 2] = bf16lo(w.y);
-                v[8 * j + 3] = bf16hi(w.y);
-                v[8 * j + 4] = bf16lo(w.z);
-                v[8 * j + 5] = bf16hi(w.z);
-                v[8 * j + 6] = bf16lo(w.w);
-                v[8 * j + 7] = bf16hi(w.w);
-            }
-        }
+        for (int j = 0; j < K / VW; ++j) unpack_vec<T, K>(load_vec<T, false>(row, t0 + j * VW, L), j, v);
     } else {
 #pragma unroll
         for (int k = 0; k < K; ++k) v[k] = (t0 + k < L) ? Elem<T>::load1(row + t0 + k) : 0.0f;
@@ -141,10 +148,11 @@ __device__ __forceinline__ void load_k_cached(const T* __restrict__ row, int t0,
 
 template <typename T, int K, bool VEC>
 __device__ __forceinline__ void store_k(T* __restrict__ row, int t0, int L, const float (&v)[K]) {
-    if (VEC && t0 + K <= L) {
-        u32x4* p = reinterpret_cast<u32x4*>(row + t0);
+    constexpr int VW = Elem<T>::kPerVec;
+    if constexpr (VEC) {
 #pragma unroll
-        for (int j = 0; j < K / Elem<T>::kPerVec; ++j) {
+        for (int j = 0; j < K / VW; ++j) {
+            const int t = t0 + j * VW;  // a vector wholly past the end is dropped
             u32x4 w;
             if constexpr (sizeof(T) == 4) {
                 w.x = __float_as_uint(v[4 * j + 0]);
@@ -157,7 +165,8 @@ __device__ __forceinline__ void store_k(T* __restrict__ row, int t0, int L, cons
                 w.z = pack_bf16(v[8 * j + 4], v[8 * j + 5]);
                 w.w = pack_bf16(v[8 * j + 6], v[8 * j + 7]);
             }
-            __builtin_nontemporal_store(w, p + j);
+            __builtin_amdgcn_raw_buffer_store_b128(w, row_rsrc(row, L),
+                                                   t * static_cast<int>(sizeof(T)), 0, 2);
         }
     } else {
 #pragma unroll
@@ -176,10 +185,10 @@ struct Raw {
 
 template <typename T, int K, bool VEC>
 __device__ __forceinline__ void load_raw(const T* __restrict__ row, int t0, int L, Raw<T, K>& r) {
-    if (VEC && t0 + K <= L) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row + t0);
+    constexpr int VW = Elem<T>::kPerVec;
+    if constexpr (VEC) {
 #pragma unroll
-        for (int j = 0; j < Raw<T, K>::kVecs; ++j) r.v[j] = p[j];
+        for (int j = 0; j < Raw<T, K>::kVecs; ++j) r.v[j] = load_vec<T, false>(row, t0 + j * VW, L);
     } else {
 #pragma unroll
         for (int j = 0; j < Raw<T, K>::kVecs; ++j) {
@@ -205,24 +214,7 @@ __device__ __forceinline__ void load_raw(const T* __restrict__ row, int t0, int 
 template <typename T, int K>
 __device__ __forceinline__ void unpack(const Raw<T, K>& r, float (&v)[K]) {
 #pragma unroll
-    for (int j = 0; j < Raw<T, K>::kVecs; ++j) {
-        const u32x4 w = r.v[j];
-        if constexpr (sizeof(T) == 4) {
-            v[4 * j + 0] = __uint_as_float(w.x);
-            v[4 * j + 1] = __uint_as_float(w.y);
-            v[4 * j + 2] = __uint_as_float(w.z);
-            v[4 * j + 3] = __uint_as_float(w.w);
-        } else {
-            v[8 * j + 0] = bf16lo(w.x);
-            v[8 * j + 1] = bf16hi(w.x);
-            v[8 * j + 2] = bf16lo(w.y);
-            v[8 * j + 3] = bf16hi(w.y);
-            v[8 * j + 4] = bf16lo(w.z);
-            v[8 * j + 5] = bf16hi(w.z);
-            v[8 * j + 6] = bf16lo(w.w);
-            v[8 * j + 7] = bf16hi(w.w);
-        }
-    }
+    for (int j = 0; j < Raw<T, K>::kVecs; ++j) unpack_vec<T, K>(r.v[j], j, v);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -86,25 +86,38 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
     const T* __restrict__ Bg = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
     const T* __restrict__ Cg = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
 
-    int dch[R];        // channel of each slot (clamped; `live` says whether it exists)
-    bool live[R];
+    // A slot past the last channel repeats channel D-1 exactly, so its results equal that
+    // channel's and may be stored over them: every store is then unconditional, which keeps
+    // the count of memory operations in flight known to the compiler (a conditional store
+    // before a load makes the load's wait cover everything).
+    int dch[R];
     float Av[R];       // lane n holds A[d, n] * log2(e)
     float E[R][K], dy[R][K];
     float Fs[FWD ? R : 1][K], du[FWD ? R : 1][K];
+    // all input rows first, so that their loads are in flight together
+    Raw<T, K> rd[R], rg[R], rz[HAS_Z ? R : 1], ru[FWD ? R : 1];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int d = dg * R + r;
-        live[r] = d < p.D;
-        dch[r] = live[r] ? d : p.D - 1;
+        dch[r] = d < p.D ? d : p.D - 1;
         const size_t row = (static_cast<size_t>(b) * p.D + dch[r]) * L;
+        load_raw<T, K, VEC>(static_cast<const T*>(p.delta) + row, t0, L, rd[r]);
+        load_raw<T, K, VEC>(static_cast<const T*>(g.dout) + row, t0, L, rg[r]);
+        if constexpr (HAS_Z) load_raw<T, K, VEC>(static_cast<const T*>(p.z) + row, t0, L, rz[r]);
+        if constexpr (FWD) load_raw<T, K, VEC>(static_cast<const T*>(p.u) + row, t0, L, ru[r]);
+        const float a_ = p.A[static_cast<size_t>(dch[r]) * N + (lane < N ? lane : N - 1)];
+        Av[r] = (lane < N) ? a_ * kLog2e : 0.0f;
+    }
+    float tot[R], fst[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
         const float bias = p.bias ? p.bias[dch[r]] : 0.0f;
-        Av[r] = (lane < N) ? p.A[static_cast<size_t>(dch[r]) * N + lane] * kLog2e : 0.0f;
         float dd[K], gg[K], dt[K];
-        load_k<T, K, VEC>(static_cast<const T*>(p.delta) + row, t0, L, dd, 0.0f);
-        load_k<T, K, VEC>(static_cast<const T*>(g.dout) + row, t0, L, gg, 0.0f);
+        unpack(rd[r], dd);
+        unpack(rg[r], gg);
         float zz[HAS_Z ? K : 1], uu[FWD ? K : 1];
-        if constexpr (HAS_Z) load_k<T, K, VEC>(static_cast<const T*>(p.z) + row, t0, L, zz, 0.0f);
-        if constexpr (FWD) load_k<T, K, VEC>(static_cast<const T*>(p.u) + row, t0, L, uu, 0.0f);
+        if constexpr (HAS_Z) unpack(rz[r], zz);
+        if constexpr (FWD) unpack(ru[r], uu);
         float run = 0.0f;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -119,21 +132,27 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
         }
         const float incl = wave_incl_sum(run);
         const float before = shift_up(incl, 0.0f);  // Delta summed over the earlier lanes
-        const float total = readlane(incl, 63);
-        const float first = readlane(dt[0], 0);
+        tot[r] = readlane(incl, 63);
+        fst[r] = readlane(dt[0], 0);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const float F = before + E[r][k];  // sum of Delta from the chunk start to t
-            if constexpr (FWD) Fs[r][k] = total - F;
-            E[r][k] = F - first;
+            if constexpr (FWD) Fs[r][k] = tot[r] - F;
+            E[r][k] = F - fst[r];
         }
-        if (lane == 0 && live[r]) {
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
             const size_t slot = (static_cast<size_t>(b) * p.D + dch[r]) * nch + c;
-            w.sdt[slot] = total;
-            w.dfirst[slot] = first;
+            w.sdt[slot] = tot[r];
+            w.dfirst[slot] = fst[r];
         }
     }
 
+    // results gathered per state (lane n = state n) and stored after the loop, so that the
+    // loop's loads never wait behind stores
+    float Gv[R] = {}, Hv[FWD ? R : 1] = {};
     Raw<T, K> Bn, Cn;
     if constexpr (FWD) load_raw<T, K, VEC>(Bg, t0, L, Bn);
     load_raw<T, K, VEC>(Cg, t0, L, Cn);
@@ -141,10 +160,10 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
         float bv[K], cv[K];
         if constexpr (FWD) unpack(Bn, bv);
         unpack(Cn, cv);
-        if (n + 1 < N) {  // the next state's rows
-            if constexpr (FWD)
-                load_raw<T, K, VEC>(Bg + static_cast<size_t>(n + 1) * L, t0, L, Bn);
-            load_raw<T, K, VEC>(Cg + static_cast<size_t>(n + 1) * L, t0, L, Cn);
+        {  // the next state's rows (the last state fetches its own again: no branch)
+            const int nn = (n + 1 < N) ? n + 1 : n;
+            if constexpr (FWD) load_raw<T, K, VEC>(Bg + static_cast<size_t>(nn) * L, t0, L, Bn);
+            load_raw<T, K, VEC>(Cg + static_cast<size_t>(nn) * L, t0, L, Cn);
         }
         float acc[4];
 #pragma unroll
@@ -160,14 +179,18 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
             if constexpr (FWD) acc[2 + r] = sh;
         }
         wave_sum4(acc[0], acc[1], acc[2], acc[3]);
-        if (lane == 0) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                if (!live[r]) continue;
-                const size_t slot = ((static_cast<size_t>(b) * p.D + dch[r]) * nch + c) * N + n;
-                w.G[slot] = acc[r];
-                if constexpr (FWD) w.H[slot] = acc[2 + r];
-            }
+        for (int r = 0; r < R; ++r) {
+            Gv[r] = writelane(acc[r], n, Gv[r]);
+            if constexpr (FWD) Hv[r] = writelane(acc[2 + r], n, Hv[r]);
+        }
+    }
+    if (lane < N) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const size_t slot = ((static_cast<size_t>(b) * p.D + dch[r]) * nch + c) * N + lane;
+            w.G[slot] = Gv[r];
+            if constexpr (FWD) w.H[slot] = Hv[r];
         }
     }
 }

@@ -33,6 +33,7 @@ FWD_CASES = [
     (1, 1, 1, 777, "bf16", True, True, True, False),     # dstate 1, one channel
     (2, 9, 16, 520, "f32", True, True, True, False),     # one chunk + 8 steps
     (1, 3, 8, 3 * 512, "bf16", True, False, True, True), # exact chunk multiple
+    (2, 4, 16, 1000, "bf16", True, True, True, True),    # 16-byte rows, ragged last tile
 ]
 
 
@@ -92,6 +93,7 @@ BWD_CASES = [
     (2, 9, 16, 1536, "f32", True, True, True, False),   # dim not a multiple of the workgroup
     (2, 13, 11, 700, "f32", True, True, True, True),    # dstate 11: the largest LDS need
     (1, 25, 10, 1030, "bf16", True, True, True, False), # two accumulator groups, ragged tail
+    (2, 7, 16, 1000, "bf16", True, True, True, True),   # 16-byte rows, ragged last chunk
 ]
 
 
