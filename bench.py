@@ -186,6 +186,38 @@ def main():
     torch.cuda.synchronize()
     per["chunk_carry"] = cc_ev[0].elapsed_time(cc_ev[1]) / args.steps
 
+    # the recurrent (decode) step at the same batch and channels: seqlen 1, state in place
+    st = {k: (None if v is None else (v[..., :1].contiguous() if k in ("u", "delta", "z", "B", "C")
+                                        else v)) for k, v in d.items()}
+    state = torch.zeros(w.batch, w.dim, w.dstate, device=dev, dtype=torch.float32)
+    dec_out = torch.empty_like(st["u"])
+    def decode():
+        msel.msel_scan_fwd(st["u"], st["delta"], st["A"], st["B"], st["C"], st["D"], st["z"],
+                           st["bias"], True, state, out=dec_out, final_state=state)
+    for _ in range(5):
+        decode()
+    torch.cuda.synchronize()
+    # one call costs more host time than GPU time, so the steps are captured in a HIP graph
+    # (the library only enqueues kernels) and the graph is replayed
+    dec_per_graph, dec_reps = 32, 10
+    g_side = torch.cuda.Stream()
+    g_side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(g_side):
+        with torch.cuda.graph(graph, stream=g_side):
+            for _ in range(dec_per_graph):
+                decode()
+    torch.cuda.current_stream().wait_stream(g_side)
+    graph.replay()
+    torch.cuda.synchronize()
+    dec_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    dec_ev[0].record()
+    for _ in range(dec_reps):
+        graph.replay()
+    dec_ev[1].record()
+    torch.cuda.synchronize()
+    per["decode_step"] = dec_ev[0].elapsed_time(dec_ev[1]) / (dec_per_graph * dec_reps)
+
     fl_bwd = FLOPS_BWD + (FLOPS_BWD_Z if d.get("z") is not None else 0)
     flops = {"fwd": FLOPS_FWD * upd, "bwd_main": fl_bwd * upd}
     kernels = {}
@@ -202,6 +234,17 @@ def main():
     kernels["bwd_main"]["what"] = "bwd_main_kernel, the chunk-parallel gradient kernel"
     kernels["bwd"]["what"] = ("the msel_scan_bwd call: zero-fills, summary, link and "
                               "bwd_main_kernel")
+    s_ = 2 if w.dtype == "bf16" else 4
+    dec_bytes = (2 * w.batch * w.dim * w.dstate * 4 + 4 * w.batch * w.dim * s_ +
+                 2 * w.batch * w.dstate * s_ + w.dim * w.dstate * 4 + 2 * w.dim * 4)
+    dsec = per["decode_step"] * 1e-3
+    kernels["decode_step"] = {
+        "ms": round(per["decode_step"], 4), "alg_bytes": dec_bytes,
+        "GB/s": round(dec_bytes / dsec / 1e9, 1),
+        "hbm_frac": round(dec_bytes / dsec / 1e9 / HBM_PEAK_GBS, 4),
+        "tc_per_s": float(f"{w.batch * w.dim / dsec:.4g}"),
+        "what": "scan_step_kernel: one recurrent step (seqlen 1) of every channel, state "
+                "updated in place; steps replayed from a HIP graph"}
 
     # the dominant kernel: the gradient kernel, bound by VALU arithmetic (an exp2 per update
     # and ~20 flops), measured with the library's events on the launch stream

@@ -96,7 +96,8 @@ typedef struct {
     const float *delta_bias;/* optional; NULL means 0                                      */
     const float *h0;        /* optional initial state; NULL means 0                        */
     void *out;              /* fwd: required output                                        */
-    float *final_state;     /* fwd / chunk_carry: optional output, state after step L-1    */
+    float *final_state;     /* fwd / chunk_carry: optional output, state after step L-1;
+                               may equal h0 (the state is then updated in place)          */
     float *chunk_states;    /* fwd: optional output; chunk_carry: required output;          */
                             /* bwd: optional input (recomputed into the workspace if NULL) */
 } msel_scan_args;
@@ -137,7 +138,10 @@ msel_status msel_validate_bwd(const msel_scan_args *args, const msel_scan_grads 
 
 /* Fused forward scan (page 4, Appendix D, Speed: one fused pass, chunked with carried
  * states).  Reads u, delta, B, C, z once, keeps the state on chip, writes out, and optionally
- * final_state and chunk_states.  Deterministic: the same inputs give the same bits. */
+ * final_state and chunk_states.  Deterministic: the same inputs give the same bits.
+ * seqlen == 1 is the recurrent (decode) step of page 3, recurrent mode: h0 is the cached state
+ * and final_state, which may be the same buffer, receives the next one; it runs a dedicated
+ * kernel (one 16-lane row per channel). */
 msel_status msel_scan_fwd(const msel_scan_args *args, hipStream_t stream);
 
 /* Chunk-carry pass (page 4, Appendix D, Speed: "as long as we have the intermediate scan

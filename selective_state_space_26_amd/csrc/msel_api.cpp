@@ -45,6 +45,12 @@ bool same_as_input(const msel_scan_args* a, const void* o) {
     return false;
 }
 
+// final_state may be h0 itself (the state updated in place, as a decode cache is): each
+// wavefront reads its channels' h0 before it writes their final state.
+bool final_state_aliases(const msel_scan_args* a) {
+    return a->final_state != a->h0 && same_as_input(a, a->final_state);
+}
+
 msel::ScanParams to_params(const msel_scan_args* a) {
     msel::ScanParams p;
     p.B = a->batch;
@@ -104,8 +110,10 @@ msel_status msel_validate_fwd(const msel_scan_args* a) {
     if (s != MSEL_OK) return s;
     if (a->C == nullptr || a->out == nullptr) return MSEL_ERR_NULL;
     if (!aligned(a->out, 16)) return MSEL_ERR_ALIGN;
-    if (same_as_input(a, a->out) || same_as_input(a, a->final_state) ||
-        same_as_input(a, a->chunk_states))
+    if (same_as_input(a, a->out) || final_state_aliases(a) || same_as_input(a, a->chunk_states))
+        return MSEL_ERR_ALIAS;
+    if (a->out == a->final_state || a->out == a->chunk_states ||
+        (a->chunk_states != nullptr && a->chunk_states == a->final_state))
         return MSEL_ERR_ALIAS;
     return MSEL_OK;
 }
@@ -114,7 +122,8 @@ msel_status msel_validate_chunk_carry(const msel_scan_args* a) {
     msel_status s = check_common(a);
     if (s != MSEL_OK) return s;
     if (a->chunk_states == nullptr) return MSEL_ERR_NULL;
-    if (same_as_input(a, a->chunk_states) || same_as_input(a, a->final_state))
+    if (same_as_input(a, a->chunk_states) || final_state_aliases(a) ||
+        a->chunk_states == a->final_state)
         return MSEL_ERR_ALIAS;
     return MSEL_OK;
 }

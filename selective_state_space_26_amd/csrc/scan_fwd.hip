@@ -131,6 +131,59 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
         p.final_state[static_cast<size_t>(ch) * N + lane] = carry;
 }
 
+// Recurrent mode (page 3, recurrent mode; page 1 and 2: the state kept in a cache): one
+// step per channel with the carried state, for decoding.  A 16-lane row per channel, lane n
+// for state n (lanes n >= N idle), four channels per wavefront:
+//   h_n = exp(Delta A_n) h0_n + Delta B_n u,  y = sum_n C_n h_n + D u,  out = y silu(z).
+// The sum over states is a 16-lane DPP reduction.  final_state may be h0 itself (the state is
+// updated in place): each lane reads its h0 before writing.
+template <typename T, bool HAS_Z, bool SOFTPLUS>
+__global__ __launch_bounds__(256) void scan_step_kernel(ScanParams p) {
+    const int lane = lane_id();
+    const int n = lane & 15;
+    const int ch = (blockIdx.x * blockDim.x + threadIdx.x) >> 4;  // b * D + d
+    const bool in = ch < p.B * p.D;
+    const int chc = in ? ch : 0;
+    const int b = chc / p.D;
+    const int d = chc - b * p.D;
+    const int N = p.N;
+    const bool st = in && n < N;
+    const int nc = n < N ? n : N - 1;
+    const float u = Elem<T>::load1(static_cast<const T*>(p.u) + chc);
+    const float x = Elem<T>::load1(static_cast<const T*>(p.delta) + chc) + (p.bias ? p.bias[d] : 0.0f);
+    const float dt = SOFTPLUS ? softplus_f(x) : x;
+    const size_t bn = static_cast<size_t>(b) * N + nc;  // B and C are [batch, dstate, 1]
+    const float Bv = Elem<T>::load1(static_cast<const T*>(p.Bm) + bn);
+    const float Cv = Elem<T>::load1(static_cast<const T*>(p.Cm) + bn);
+    const float An = p.A[static_cast<size_t>(d) * N + nc] * kLog2e;
+    const size_t sidx = static_cast<size_t>(chc) * N + nc;
+    const float h0 = p.h0 ? p.h0[sidx] : 0.0f;
+    const float h = fmaf(exp2_hw(dt * An), h0, dt * Bv * u);
+    float part = st ? Cv * h : 0.0f;
+    // sum over the row's 16 lanes: inclusive DPP prefix, lane 15 of the row holds the total
+    asm volatile("s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_shr:1 row_mask:0xf bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_shr:2 row_mask:0xf bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_shr:4 row_mask:0xf bank_mask:0xf\n"
+                 "s_nop 1\n"
+                 "v_add_f32_dpp %[v], %[v], %[v] row_shr:8 row_mask:0xf bank_mask:0xf\n"
+                 : [v] "+v"(part));
+    if (st) {
+        if (p.chunk_states != nullptr) p.chunk_states[sidx] = h0;  // one chunk: its entry state
+        if (p.final_state != nullptr) p.final_state[sidx] = h;
+    }
+    if (in && n == 15) {
+        float y = part + (p.Dv ? p.Dv[d] : 0.0f) * u;
+        if constexpr (HAS_Z) {
+            const float z = Elem<T>::load1(static_cast<const T*>(p.z) + chc);
+            y *= z * sigmoid_f(z);
+        }
+        Elem<T>::store1(static_cast<T*>(p.out) + chc, y);
+    }
+}
+
 namespace {
 
 constexpr int kFwdWaves = 4;
@@ -164,7 +217,20 @@ hipError_t fwd_dispatch(const ScanParams& p, hipStream_t s) {
 
 }  // namespace
 
+template <typename T>
+hipError_t step_dispatch(const ScanParams& p, hipStream_t s) {
+    const long long threads = static_cast<long long>(p.B) * p.D * 16;
+    dim3 grid(static_cast<unsigned>((threads + 255) / 256)), block(256);
+    const bool hz = p.z != nullptr, sp = p.softplus != 0;
+    if (hz && sp) hipLaunchKernelGGL((scan_step_kernel<T, true, true>), grid, block, 0, s, p);
+    if (hz && !sp) hipLaunchKernelGGL((scan_step_kernel<T, true, false>), grid, block, 0, s, p);
+    if (!hz && sp) hipLaunchKernelGGL((scan_step_kernel<T, false, true>), grid, block, 0, s, p);
+    if (!hz && !sp) hipLaunchKernelGGL((scan_step_kernel<T, false, false>), grid, block, 0, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, hipStream_t stream) {
+    if (p.L == 1) return bf16 ? step_dispatch<bf16_t>(p, stream) : step_dispatch<float>(p, stream);
     if (bf16) return fwd_dispatch<bf16_t, 16>(p, stream);
     return fwd_dispatch<float, 16>(p, stream);
 }

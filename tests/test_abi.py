@@ -157,11 +157,24 @@ def test_fp32_alignment(lib, field):
 
 
 @pytest.mark.parametrize("out_field,in_field", [("out", "u"), ("out", "z"), ("final_state", "A"),
-                                                ("chunk_states", "delta")])
+                                                ("chunk_states", "delta"), ("chunk_states", "h0"),
+                                                ("out", "final_state"),
+                                                ("chunk_states", "final_state")])
 def test_aliasing_is_rejected(lib, out_field, in_field):
     a = _good_args()
+    a.h0, a.chunk_states = _addr(), _addr()
+    assert _fwd(lib, a) == 0
     setattr(a, out_field, getattr(a, in_field))
     assert _fwd(lib, a) == 7
+
+
+def test_final_state_may_update_h0_in_place(lib):
+    a = _good_args()
+    a.h0 = _addr()
+    a.final_state = a.h0
+    assert _fwd(lib, a) == 0
+    a.chunk_states = _addr()
+    assert lib.msel_validate_chunk_carry(ctypes.byref(a)) == 0
 
 
 def test_optional_inputs_may_be_null(lib):

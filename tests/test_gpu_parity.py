@@ -257,3 +257,97 @@ def test_bwd_profiled_matches_bwd_and_times_the_gradient_kernel():
     for k in ("dA", "dB", "dC", "dD", "ddelta_bias"):
         assert_close(k, host(b[k]), r[k], "f32")
     assert ev[0].elapsed_time(ev[1]) > 0.0
+
+
+DECODE_CASES = [
+    # batch, dim, dstate, dtype, z, softplus, D/bias, h0
+    (8, 48, 16, "bf16", True, True, True, True),
+    (3, 7, 5, "f32", False, False, False, True),
+    (2, 5, 1, "bf16", True, True, True, False),
+    (1, 33, 16, "f32", True, True, True, True),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "x".join(map(str, c[:4])))
+def test_decode_step_matches_oracle(case):
+    """seqlen 1 runs the recurrent-mode step kernel: out, the next state and the one chunk
+    state (the entering state) against the oracle."""
+    bsz, dim, N, dtype, with_z, sp, with_db, with_h0 = case
+    log(f"decode {case}")
+    t = _case_inputs(bsz, dim, N, 1, dtype, with_z, sp, with_db, with_h0)
+    dv = to_device(t)
+    out, fin, cs = msel.msel_scan_fwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"],
+                                      dv["z"], dv["bias"], sp, dv["h0"],
+                                      return_chunk_states=True)
+    torch.cuda.synchronize()
+    v = oracle_vals(t)
+    ro, rf, rcs = oracle.fwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"],
+                             v["bias"], v["h0"], softplus=sp, chunk_len=T)
+    assert_close("out", host(out), ro, dtype)
+    assert_close("final_state", host(fin), rf, dtype)
+    assert_close("chunk_states", host(cs), rcs, dtype)
+
+
+def test_decode_steps_update_the_state_in_place_and_follow_the_scan():
+    """Six decode steps with final_state = h0 (one buffer) give the same outputs and final
+    state as one forward scan over the six steps (within the fp32 tolerance) and as the
+    oracle."""
+    log("decode in place")
+    bsz, dim, N, L = 2, 9, 16, 6
+    t = _case_inputs(bsz, dim, N, L, "f32", True, True, True, True)
+    dv = to_device(t)
+    state = dv["h0"].clone()
+    outs = []
+    for s in range(L):
+        sl = lambda x: None if x is None else x[..., s:s + 1].contiguous()
+        o, f, _ = msel.msel_scan_fwd(sl(dv["u"]), sl(dv["delta"]), dv["A"], sl(dv["B"]),
+                                     sl(dv["C"]), dv["D"], sl(dv["z"]), dv["bias"], True, state,
+                                     final_state=state)
+        assert f.data_ptr() == state.data_ptr()
+        outs.append(o)
+    torch.cuda.synchronize()
+    got = torch.cat(outs, dim=-1)
+    ref_out, ref_fin, _ = msel.msel_scan_fwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"],
+                                             dv["D"], dv["z"], dv["bias"], True, dv["h0"])
+    torch.cuda.synchronize()
+    assert_close("steps vs scan out", host(got), host(ref_out).astype(np.float64), "f32")
+    assert_close("steps vs scan state", host(state), host(ref_fin).astype(np.float64), "f32")
+    v = oracle_vals(t)
+    ro, rf = oracle.fwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"], v["bias"],
+                        v["h0"])
+    assert_close("out", host(got), ro, "f32")
+    assert_close("final_state", host(state), rf, "f32")
+
+
+def test_decode_step_replays_from_a_hip_graph():
+    """The decode step only enqueues a kernel, so it can be captured in a graph: three replays,
+    each followed by host work and a synchronisation, match three eager steps bit for bit."""
+    log("decode graph")
+    bsz, dim, N = 4, 24, 16
+    t = _case_inputs(bsz, dim, N, 1, "bf16", True, True, True, True)
+    dv = to_device(t)
+    args = (dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"], dv["z"], dv["bias"], True)
+    eager_state = dv["h0"].clone()
+    eager_outs = []
+    for _ in range(3):
+        o, _, _ = msel.msel_scan_fwd(*args, eager_state, final_state=eager_state)
+        eager_outs.append(o.clone())
+    torch.cuda.synchronize()
+    state = dv["h0"].clone()
+    out = torch.empty_like(dv["u"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            msel.msel_scan_fwd(*args, state, out=out, final_state=state)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    state.copy_(dv["h0"])
+    torch.cuda.synchronize()
+    for k in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = host(out).sum()  # host work between replays
+        assert torch.equal(out, eager_outs[k]), k
+    assert torch.equal(state, eager_state)
