@@ -9,6 +9,11 @@ Distributions (the workloads' recipe): u, z ~ N(0,1) and delta = 0.5*N(0,1) of s
 [1e-3, 1e-1]); A[d, n] = -(n+1) (S4D-real); B, C ~ N(0,1) of shape [batch, dstate, seqlen],
 shared by all channels; D ~ N(0,1) of shape [dim]; dout ~ N(0,1) for the backward.
 
+The short convolution before the scan (``make_conv``): x ~ N(0,1) of shape [batch, dim,
+seqlen]; taps w[d, k] and bias b[d] ~ U(-1/sqrt(W), 1/sqrt(W)) (the default initialisation of a
+depthwise 1-d convolution, whose fan-in is the width W); the incoming state (the W-1 inputs
+before the first step) ~ N(0,1) of shape [batch, dim, W-1]; dout ~ N(0,1).
+
 Every tensor has its own PCG64 stream, ``default_rng([seed, tensor_id])``, drawn in float32 and,
 for bf16 workloads, rounded to nearest-even bfloat16 on u, delta, z, B, C and dout.
 """
@@ -19,7 +24,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 TENSOR_IDS = {"u": 0, "delta": 1, "z": 2, "B": 3, "C": 4, "D": 5, "bias": 6, "dout": 7,
-              "h0": 8}
+              "h0": 8, "conv_x": 9, "conv_w": 10, "conv_b": 11, "conv_state": 12,
+              "conv_dout": 13}
 
 
 @dataclass(frozen=True)
@@ -152,3 +158,26 @@ def channel_slice(t: Tensors, b: int, ds) -> dict:
     h0 = t.get("h0")
     sub["h0"] = None if h0 is None else h0[b:b + 1, ds, :]
     return sub
+
+
+def make_conv(batch: int, dim: int, seqlen: int, width: int, dtype: str = "f32", seed: int = 0,
+              with_bias: bool = True, with_state: bool = False,
+              with_dout: bool = False) -> Tensors:
+    """Draw one problem of the short causal convolution.  x, state and dout follow ``dtype``
+    (state is a copy of earlier inputs); the taps and the bias are fp32."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(dtype)
+    t = Tensors(dtype)
+
+    def act(name, shape):
+        x = _normal(seed, name, shape)
+        return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+    bound = 1.0 / np.sqrt(width)
+    t["x"] = act("conv_x", (batch, dim, seqlen))
+    t["weight"] = rng(seed, "conv_w").uniform(-bound, bound, size=(dim, width)).astype(np.float32)
+    t["bias"] = (rng(seed, "conv_b").uniform(-bound, bound, size=dim).astype(np.float32)
+                 if with_bias else None)
+    t["state"] = act("conv_state", (batch, dim, width - 1)) if with_state else None
+    t["dout"] = act("conv_dout", (batch, dim, seqlen)) if with_dout else None
+    return t

@@ -9,6 +9,8 @@ Two independent implementations live here:
 
 * ``fwd`` / ``chunk_states_formula`` / ``bwd`` call the plain C loop in ``msel_oracle.c``
   (sequential over time, one (batch, channel) recurrence per work unit, double precision).
+* ``conv.py`` is the short causal convolution and activation that feed the scan (forward,
+  hand-derived backward, convolutional state), written out tap by tap in float64.
 * ``twin_fwd`` in ``twin.py`` is a numpy restatement, vectorized over (batch, channel, state)
   with a Python loop over time, used to cross-check the C loop on small shapes.
 
