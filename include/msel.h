@@ -61,10 +61,12 @@ typedef struct ihipEvent_t *hipEvent_t;
 typedef enum {
     MSEL_OK = 0,
     MSEL_ERR_NULL = 1,        /* a required pointer is NULL                                */
-    MSEL_ERR_SHAPE = 2,       /* a size is < 1, or sizes overflow the supported range      */
-    MSEL_ERR_DTYPE = 3,       /* dtype is not MSEL_F32 / MSEL_BF16, or softplus not 0/1     */
+    MSEL_ERR_SHAPE = 2,       /* a size is < 1, or above the supported range (seqlen up to  */
+                              /* MSEL_MAX_SEQLEN, batch*dim up to 2^30)                     */
+    MSEL_ERR_DTYPE = 3,       /* dtype is not MSEL_F32 / MSEL_BF16, or a 0/1 flag is not 0/1 */
     MSEL_ERR_ALIGN = 4,       /* an activation pointer is not 16-byte aligned              */
-    MSEL_ERR_UNSUPPORTED = 5, /* dstate outside 1..MSEL_MAX_DSTATE                          */
+    MSEL_ERR_UNSUPPORTED = 5, /* dstate outside 1..MSEL_MAX_DSTATE, or a convolution width  */
+                              /* outside 1..MSEL_MAX_CONV_WIDTH                             */
     MSEL_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than msel_scan_bwd_workspace_bytes */
     MSEL_ERR_ALIAS = 7,       /* an output pointer equals an input pointer                 */
     MSEL_ERR_HIP = 8,         /* the HIP runtime reported an error at launch               */
@@ -74,6 +76,8 @@ typedef enum {
 typedef enum { MSEL_F32 = 0, MSEL_BF16 = 1 } msel_dtype;
 
 #define MSEL_MAX_DSTATE 16
+#define MSEL_MAX_SEQLEN (1 << 28)
+#define MSEL_MAX_CONV_WIDTH 4
 
 /* Problem description shared by the three entry points. */
 typedef struct {
@@ -176,6 +180,69 @@ msel_status msel_scan_bwd(const msel_scan_args *args, const msel_scan_grads *gra
 msel_status msel_scan_bwd_profiled(const msel_scan_args *args, const msel_scan_grads *grads,
                                    void *workspace, size_t workspace_bytes, hipStream_t stream,
                                    hipEvent_t ev_begin, hipEvent_t ev_end);
+
+/* ------------------------------------------------------------------------------------------
+ * The short causal convolution and activation that produce the scan's input.
+ *
+ * The selective SSM block runs an input projection, a short convolution, an activation, the
+ * scan and an output projection; the backward recomputes the convolution and activation
+ * outputs rather than storing them (page 4, Appendix D, Memory paragraph).  The layer's cache
+ * keeps a convolutional state beside the SSM state, and the fast path calls a dedicated causal
+ * convolution kernel (page 1, the paragraphs on the cache and on the kernels).  Per batch row
+ * b, channel d and step t, with W taps:
+ *
+ *   xe      = [state_in[b,d,0..W-2], x[b,d,0..L-1]]     the W-1 earlier inputs, oldest first
+ *   pre_t   = bias[d] + sum_k weight[d,k] * xe[t+k]      tap W-1 multiplies x_t (causal)
+ *   out_t   = silu(pre_t) = pre_t * sigmoid(pre_t)       (out_t = pre_t when activation = 0)
+ *   state_out = the last W-1 entries of xe               (the cache after the call)
+ *
+ * Layouts: x, out, dout, dx [batch, dim, seqlen] in the activation dtype (16-byte aligned);
+ * weight [dim, width] fp32; bias [dim] fp32; state_in, state_out [batch, dim, width-1] in the
+ * activation dtype (copies of inputs, so exact); dweight, dbias, dstate_in fp32.  The
+ * convolution is computed in fp32.  With width 1 the state pointers are ignored.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t abi_version;    /* must be MSEL_ABI_VERSION                                    */
+    int32_t batch;          /* >= 1                                                        */
+    int32_t dim;            /* channels, >= 1                                              */
+    int32_t seqlen;         /* L, 1..MSEL_MAX_SEQLEN                                       */
+    int32_t width;          /* W, 1..MSEL_MAX_CONV_WIDTH                                   */
+    int32_t dtype;          /* msel_dtype of x, out, state_in, state_out, dout, dx          */
+    int32_t activation;     /* 1: SiLU; 0: none                                            */
+    int32_t reserved;       /* must be 0                                                   */
+    const void *x;          /* required                                                    */
+    const float *weight;    /* required                                                    */
+    const float *bias;      /* optional; NULL means 0                                      */
+    const void *state_in;   /* optional; NULL means the inputs before step 0 are 0          */
+    void *out;              /* fwd: required output; ignored by the backward               */
+    void *state_out;        /* fwd: optional output; may equal state_in (the cache is then
+                               updated in place); ignored by the backward                  */
+} msel_conv_args;
+
+/* Gradients of a scalar loss given dL/dout.  Every output is overwritten, not accumulated. */
+typedef struct {
+    const void *dout;       /* required, activation dtype                                  */
+    void *dx;               /* required, activation dtype                                  */
+    float *dweight;         /* optional [dim, width]                                       */
+    float *dbias;           /* optional [dim] (computed even when args->bias is NULL)       */
+    float *dstate_in;       /* optional [batch, dim, width-1]: gradient w.r.t. state_in     */
+} msel_conv_grads;
+
+/* Host-only argument checks of the two entry points below (no HIP call, no device access). */
+msel_status msel_validate_conv_fwd(const msel_conv_args *args);
+msel_status msel_validate_conv_bwd(const msel_conv_args *args, const msel_conv_grads *grads);
+
+/* Fused causal depthwise convolution + bias + SiLU (page 4, Appendix D, Memory; page 1, the
+ * kernels paragraph): one read of x, one write of out, the state in and out of the cache.
+ * Deterministic.  seqlen == 1 with state_out == state_in is the recurrent (decode) step. */
+msel_status msel_conv1d_fwd(const msel_conv_args *args, hipStream_t stream);
+
+/* Its backward, recomputing pre and the activation from x (page 4, Appendix D, Memory):
+ * zero-fills dweight and dbias, then one pass that reads x and dout and writes dx and
+ * dstate_in.  dweight and dbias are sums over batch and time made with fp32 atomics, so they
+ * may differ in the last bits between runs; dx and dstate_in are deterministic. */
+msel_status msel_conv1d_bwd(const msel_conv_args *args, const msel_conv_grads *grads,
+                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

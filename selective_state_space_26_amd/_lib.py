@@ -34,6 +34,18 @@ class ScanGrads(ctypes.Structure):
                 ("dC", _P), ("dD", _P), ("ddelta_bias", _P), ("dh0", _P)]
 
 
+class ConvArgs(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("dim", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("width", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("activation", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("x", _P), ("weight", _P), ("bias", _P),
+                ("state_in", _P), ("out", _P), ("state_out", _P)]
+
+
+class ConvGrads(ctypes.Structure):
+    _fields_ = [("dout", _P), ("dx", _P), ("dweight", _P), ("dbias", _P), ("dstate_in", _P)]
+
+
 class MselError(RuntimeError):
     def __init__(self, fn: str, code: int, text: str):
         super().__init__(f"{fn} returned {STATUS.get(code, code)}: {text}")
@@ -45,7 +57,8 @@ _lib = None
 EXPORTS = ["msel_abi_version", "msel_chunk_len", "msel_num_chunks", "msel_status_string",
            "msel_validate_fwd", "msel_validate_chunk_carry", "msel_validate_bwd",
            "msel_scan_fwd", "msel_scan_chunk_carry", "msel_scan_bwd_workspace_bytes",
-           "msel_scan_bwd", "msel_scan_bwd_profiled"]
+           "msel_scan_bwd", "msel_scan_bwd_profiled", "msel_validate_conv_fwd",
+           "msel_validate_conv_bwd", "msel_conv1d_fwd", "msel_conv1d_bwd"]
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
@@ -82,6 +95,15 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.msel_scan_bwd.argtypes = [a, g, _P, ctypes.c_size_t, _P]
     lib.msel_scan_bwd_profiled.restype = ctypes.c_int
     lib.msel_scan_bwd_profiled.argtypes = [a, g, _P, ctypes.c_size_t, _P, _P, _P]
+    ca, cg = ctypes.POINTER(ConvArgs), ctypes.POINTER(ConvGrads)
+    lib.msel_validate_conv_fwd.restype = ctypes.c_int
+    lib.msel_validate_conv_fwd.argtypes = [ca]
+    lib.msel_validate_conv_bwd.restype = ctypes.c_int
+    lib.msel_validate_conv_bwd.argtypes = [ca, cg]
+    lib.msel_conv1d_fwd.restype = ctypes.c_int
+    lib.msel_conv1d_fwd.argtypes = [ca, _P]
+    lib.msel_conv1d_bwd.restype = ctypes.c_int
+    lib.msel_conv1d_bwd.argtypes = [ca, cg, _P]
     if lib.msel_abi_version() != ABI_VERSION:
         raise RuntimeError("libmsel.so ABI version mismatch")
     if path is None:

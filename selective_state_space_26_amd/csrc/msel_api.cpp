@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int64_t kMaxSeq = int64_t(1) << 30;
+constexpr int64_t kMaxSeq = MSEL_MAX_SEQLEN;
 constexpr int64_t kMaxRows = int64_t(1) << 30;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -75,6 +75,56 @@ msel::ScanParams to_params(const msel_scan_args* a) {
 }
 
 msel_status hip_status(hipError_t e) { return e == hipSuccess ? MSEL_OK : MSEL_ERR_HIP; }
+
+// ---- the short causal convolution ------------------------------------------------------
+
+// Largest grid the convolution kernels launch (gridDim.x is 32-bit).
+constexpr int64_t kMaxConvGroups = (int64_t(1) << 31) - 1;
+
+size_t elem_bytes(int32_t dtype) { return dtype == MSEL_BF16 ? 2 : 4; }
+
+msel_status check_conv(const msel_conv_args* a) {
+    if (a == nullptr) return MSEL_ERR_NULL;
+    if (a->abi_version != MSEL_ABI_VERSION || a->reserved != 0) return MSEL_ERR_VERSION;
+    if (a->batch < 1 || a->dim < 1 || a->seqlen < 1 || a->width < 1) return MSEL_ERR_SHAPE;
+    if (static_cast<int64_t>(a->batch) * a->dim > kMaxRows || a->seqlen > kMaxSeq)
+        return MSEL_ERR_SHAPE;
+    if (a->dtype != MSEL_F32 && a->dtype != MSEL_BF16) return MSEL_ERR_DTYPE;
+    if (a->activation != 0 && a->activation != 1) return MSEL_ERR_DTYPE;
+    if (a->width > MSEL_MAX_CONV_WIDTH) return MSEL_ERR_UNSUPPORTED;
+    if (msel::conv_workgroups(static_cast<int64_t>(a->batch) * a->dim, a->seqlen,
+                              a->dtype == MSEL_BF16) > kMaxConvGroups)
+        return MSEL_ERR_SHAPE;
+    if (a->x == nullptr || a->weight == nullptr) return MSEL_ERR_NULL;
+    if (!aligned(a->x, 16)) return MSEL_ERR_ALIGN;
+    if (!aligned(a->weight, 4) || (a->bias != nullptr && !aligned(a->bias, 4)))
+        return MSEL_ERR_ALIGN;
+    if (a->width > 1 && a->state_in != nullptr && !aligned(a->state_in, elem_bytes(a->dtype)))
+        return MSEL_ERR_ALIGN;
+    return MSEL_OK;
+}
+
+bool conv_input(const msel_conv_args* a, const void* o) {
+    if (o == nullptr) return false;
+    const void* in[] = {a->x, a->weight, a->bias, a->state_in};
+    for (const void* p : in)
+        if (p != nullptr && p == o) return true;
+    return false;
+}
+
+msel::ConvParams to_conv_params(const msel_conv_args* a) {
+    msel::ConvParams p = {};
+    p.rows = static_cast<int64_t>(a->batch) * a->dim;
+    p.D = a->dim;
+    p.L = a->seqlen;
+    p.W = a->width;
+    p.silu = a->activation;
+    p.x = a->x;
+    p.w = a->weight;
+    p.bias = a->bias;
+    p.state_in = a->width > 1 ? a->state_in : nullptr;
+    return p;
+}
 
 }  // namespace
 
@@ -161,6 +211,65 @@ msel_status msel_validate_bwd(const msel_scan_args* a, const msel_scan_grads* g,
     for (const void* o : outs)
         if (o != nullptr && o == workspace) return MSEL_ERR_ALIAS;
     return MSEL_OK;
+}
+
+msel_status msel_validate_conv_fwd(const msel_conv_args* a) {
+    msel_status s = check_conv(a);
+    if (s != MSEL_OK) return s;
+    if (a->out == nullptr) return MSEL_ERR_NULL;
+    if (!aligned(a->out, 16)) return MSEL_ERR_ALIGN;
+    const bool state = a->width > 1 && a->state_out != nullptr;
+    if (state && !aligned(a->state_out, elem_bytes(a->dtype))) return MSEL_ERR_ALIGN;
+    if (conv_input(a, a->out) || (state && a->state_out == a->out)) return MSEL_ERR_ALIAS;
+    // state_out may be state_in itself (the cache updated in place), no other input
+    if (state && a->state_out != a->state_in && conv_input(a, a->state_out)) return MSEL_ERR_ALIAS;
+    return MSEL_OK;
+}
+
+msel_status msel_validate_conv_bwd(const msel_conv_args* a, const msel_conv_grads* g) {
+    msel_status s = check_conv(a);
+    if (s != MSEL_OK) return s;
+    if (g == nullptr || g->dout == nullptr || g->dx == nullptr) return MSEL_ERR_NULL;
+    if (!aligned(g->dout, 16) || !aligned(g->dx, 16)) return MSEL_ERR_ALIGN;
+    float* dstate = a->width > 1 ? g->dstate_in : nullptr;
+    const void* f32[] = {g->dweight, g->dbias, dstate};
+    for (const void* p : f32)
+        if (p != nullptr && !aligned(p, 4)) return MSEL_ERR_ALIGN;
+    const void* outs[] = {g->dx, g->dweight, g->dbias, dstate};
+    for (int i = 0; i < 4; ++i) {
+        const void* o = outs[i];
+        if (o == nullptr) continue;
+        if (conv_input(a, o) || o == g->dout) return MSEL_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (outs[j] == o) return MSEL_ERR_ALIAS;
+    }
+    return MSEL_OK;
+}
+
+msel_status msel_conv1d_fwd(const msel_conv_args* a, hipStream_t stream) {
+    msel_status s = msel_validate_conv_fwd(a);
+    if (s != MSEL_OK) return s;
+    msel::ConvParams p = to_conv_params(a);
+    p.out = a->out;
+    p.state_out = a->width > 1 ? a->state_out : nullptr;
+    return hip_status(msel::launch_conv_fwd(p, a->dtype == MSEL_BF16, stream));
+}
+
+msel_status msel_conv1d_bwd(const msel_conv_args* a, const msel_conv_grads* g,
+                            hipStream_t stream) {
+    msel_status s = msel_validate_conv_bwd(a, g);
+    if (s != MSEL_OK) return s;
+    msel::ConvParams p = to_conv_params(a);
+    p.dout = g->dout;
+    p.dx = g->dx;
+    p.dw = g->dweight;
+    p.dbias = g->dbias;
+    p.dstate = a->width > 1 ? g->dstate_in : nullptr;
+    const msel::FillList fill = {{g->dweight, g->dbias, nullptr, nullptr, nullptr},
+                                 {static_cast<size_t>(a->dim) * a->width,
+                                  static_cast<size_t>(a->dim), 0, 0, 0}};
+    if (msel::launch_fill_zero(fill, stream) != hipSuccess) return MSEL_ERR_HIP;
+    return hip_status(msel::launch_conv_bwd(p, a->dtype == MSEL_BF16, stream));
 }
 
 msel_status msel_scan_fwd(const msel_scan_args* a, hipStream_t stream) {

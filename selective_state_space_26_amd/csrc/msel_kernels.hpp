@@ -60,4 +60,28 @@ struct FillList {
 };
 hipError_t launch_fill_zero(const FillList& f, hipStream_t stream);
 
+// Short causal convolution (+ bias, + SiLU when silu != 0) over rows = batch * dim rows of
+// length L; W taps.  The forward reads x, state_in and writes out, state_out; the backward
+// reads x, state_in, dout and writes dx, dstate and adds into dw, dbias (zeroed by the caller).
+struct ConvParams {
+    int64_t rows;
+    int D, L, W, silu;
+    int tiles;  // set by the launcher
+    const void* x;
+    const float* w;
+    const float* bias;
+    const void* state_in;
+    void* out;
+    void* state_out;
+    const void* dout;
+    void* dx;
+    float* dw;
+    float* dbias;
+    float* dstate;
+};
+// Workgroups one launch of either kernel uses (the host rejects sizes whose grid would not fit).
+int64_t conv_workgroups(int64_t rows, int L, bool bf16);
+hipError_t launch_conv_fwd(const ConvParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_conv_bwd(const ConvParams& p, bool bf16, hipStream_t stream);
+
 }  // namespace msel

@@ -41,8 +41,11 @@ def test_struct_layout_matches_header(tmp_path):
         "#define F(S, m) printf(#S \".\" #m \" %zu\\n\", offsetof(S, m));\n"
         "int main(void) {\n"
         'printf("args %zu\\ngrads %zu\\n", sizeof(msel_scan_args), sizeof(msel_scan_grads));\n'
+        'printf("cargs %zu\\ncgrads %zu\\n", sizeof(msel_conv_args), sizeof(msel_conv_grads));\n'
         + "".join(f"F(msel_scan_args, {f})\n" for f, _ in _lib.ScanArgs._fields_)
         + "".join(f"F(msel_scan_grads, {f})\n" for f, _ in _lib.ScanGrads._fields_)
+        + "".join(f"F(msel_conv_args, {f})\n" for f, _ in _lib.ConvArgs._fields_)
+        + "".join(f"F(msel_conv_grads, {f})\n" for f, _ in _lib.ConvGrads._fields_)
         + "return 0; }\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o",
@@ -55,6 +58,12 @@ def test_struct_layout_matches_header(tmp_path):
         assert int(got[f"msel_scan_args.{f}"]) == getattr(_lib.ScanArgs, f).offset, f
     for f, _ in _lib.ScanGrads._fields_:
         assert int(got[f"msel_scan_grads.{f}"]) == getattr(_lib.ScanGrads, f).offset, f
+    assert int(got["cargs"]) == ctypes.sizeof(_lib.ConvArgs)
+    assert int(got["cgrads"]) == ctypes.sizeof(_lib.ConvGrads)
+    for f, _ in _lib.ConvArgs._fields_:
+        assert int(got[f"msel_conv_args.{f}"]) == getattr(_lib.ConvArgs, f).offset, f
+    for f, _ in _lib.ConvGrads._fields_:
+        assert int(got[f"msel_conv_grads.{f}"]) == getattr(_lib.ConvGrads, f).offset, f
 
 
 def test_constants(lib):
@@ -140,6 +149,10 @@ def test_size_overflow_is_rejected(lib):
     a = _good_args()
     a.seqlen = (1 << 30) + 1
     assert _fwd(lib, a) == 2
+    a.seqlen = (1 << 28) + 1  # byte offsets of an fp32 row must stay below 2^31
+    assert _fwd(lib, a) == 2
+    a.seqlen = 1 << 28
+    assert _fwd(lib, a) == 0
 
 
 @pytest.mark.parametrize("field", ["u", "delta", "B", "C", "z", "out"])
@@ -264,3 +277,134 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 2, 8)
     with pytest.raises(ValueError):
         msel_scan_fwd(x, x, torch.zeros(2, 4), torch.zeros(1, 4, 8), torch.zeros(1, 4, 8))
+
+
+# ---- the short causal convolution --------------------------------------------------------
+
+def _conv_args(bsz=2, dim=3, L=100, W=4, dtype=0):
+    a = _lib.ConvArgs()
+    a.abi_version = 1
+    a.batch, a.dim, a.seqlen, a.width = bsz, dim, L, W
+    a.dtype, a.activation, a.reserved = dtype, 1, 0
+    for f in ("x", "weight", "bias", "state_in", "out", "state_out"):
+        setattr(a, f, _addr())
+    return a
+
+
+def _conv_grads():
+    g = _lib.ConvGrads()
+    for f in ("dout", "dx", "dweight", "dbias", "dstate_in"):
+        setattr(g, f, _addr())
+    return g
+
+
+def _cfwd(lib, a):
+    return lib.msel_validate_conv_fwd(ctypes.byref(a))
+
+
+def _cbwd(lib, a, g):
+    return lib.msel_validate_conv_bwd(ctypes.byref(a), ctypes.byref(g))
+
+
+def test_conv_valid_args_pass(lib):
+    a = _conv_args()
+    assert _cfwd(lib, a) == 0
+    assert _cbwd(lib, a, _conv_grads()) == 0
+    a.bias = a.state_in = a.state_out = None
+    assert _cfwd(lib, a) == 0
+    g = _conv_grads()
+    g.dweight = g.dbias = g.dstate_in = None
+    assert _cbwd(lib, a, g) == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("abi_version", 2, 9), ("reserved", 3, 9),
+    ("batch", 0, 2), ("dim", 0, 2), ("seqlen", 0, 2), ("width", 0, 2), ("width", -1, 2),
+    ("seqlen", (1 << 28) + 1, 2),
+    ("dtype", 2, 3), ("activation", 2, 3), ("activation", -1, 3),
+    ("width", 5, 5), ("width", 64, 5),
+    ("x", None, 1), ("weight", None, 1), ("out", None, 1),
+])
+def test_conv_fwd_rejects(lib, field, value, code):
+    a = _conv_args()
+    setattr(a, field, value)
+    assert _cfwd(lib, a) == code
+    assert lib.msel_conv1d_fwd(ctypes.byref(a), None) == code
+
+
+def test_conv_null_pointers(lib):
+    assert lib.msel_validate_conv_fwd(None) == 1
+    assert lib.msel_conv1d_fwd(None, None) == 1
+    assert lib.msel_conv1d_bwd(None, None, None) == 1
+    a = _conv_args()
+    assert lib.msel_validate_conv_bwd(ctypes.byref(a), None) == 1
+    for f in ("dout", "dx"):
+        g = _conv_grads()
+        setattr(g, f, None)
+        assert _cbwd(lib, a, g) == 1
+        assert lib.msel_conv1d_bwd(ctypes.byref(a), ctypes.byref(g), None) == 1
+
+
+def test_conv_alignment(lib):
+    for f in ("x", "out"):
+        a = _conv_args()
+        setattr(a, f, getattr(a, f) + 8)
+        assert _cfwd(lib, a) == 4
+    for f, off in (("weight", 2), ("bias", 2), ("state_in", 2), ("state_out", 2)):
+        a = _conv_args()
+        setattr(a, f, getattr(a, f) + off)
+        assert _cfwd(lib, a) == 4, f
+    # bf16 states need 2-byte alignment only
+    a = _conv_args(dtype=1)
+    a.state_in += 2
+    a.state_out += 6
+    assert _cfwd(lib, a) == 0
+    a.state_in += 1
+    assert _cfwd(lib, a) == 4
+    for f in ("dout", "dx"):
+        a, g = _conv_args(), _conv_grads()
+        setattr(g, f, getattr(g, f) + 4)
+        assert _cbwd(lib, a, g) == 4
+    for f in ("dweight", "dbias", "dstate_in"):
+        a, g = _conv_args(), _conv_grads()
+        setattr(g, f, getattr(g, f) + 2)
+        assert _cbwd(lib, a, g) == 4
+
+
+def test_conv_width_one_ignores_state_pointers(lib):
+    a = _conv_args(W=1)
+    a.state_in = a.x + 1      # misaligned, but there is no state of width 1
+    a.state_out = a.x
+    assert _cfwd(lib, a) == 0
+    g = _conv_grads()
+    g.dstate_in = g.dx
+    assert _cbwd(lib, a, g) == 0
+
+
+@pytest.mark.parametrize("out_field,in_field", [("out", "x"), ("out", "state_in"),
+                                                ("out", "bias"), ("state_out", "x"),
+                                                ("state_out", "weight"), ("state_out", "out")])
+def test_conv_fwd_aliasing_is_rejected(lib, out_field, in_field):
+    a = _conv_args()
+    setattr(a, out_field, getattr(a, in_field))
+    assert _cfwd(lib, a) == 7
+
+
+def test_conv_state_may_update_in_place(lib):
+    a = _conv_args(L=1)
+    a.state_out = a.state_in
+    assert _cfwd(lib, a) == 0
+    a = _conv_args(L=1000)
+    a.state_out = a.state_in
+    assert _cfwd(lib, a) == 0
+
+
+@pytest.mark.parametrize("gfield,target", [("dx", "x"), ("dx", "dout"), ("dweight", "weight"),
+                                           ("dbias", "bias"), ("dstate_in", "state_in"),
+                                           ("dbias", "dweight"), ("dstate_in", "dx")])
+def test_conv_bwd_aliasing_is_rejected(lib, gfield, target):
+    a, g = _conv_args(), _conv_grads()
+    src = getattr(g, target) if hasattr(g, target) and target in dict(g._fields_) else \
+        getattr(a, target)
+    setattr(g, gfield, src)
+    assert _cbwd(lib, a, g) == 7
