@@ -234,7 +234,8 @@ msel_status msel_validate_conv_bwd(const msel_conv_args *args, const msel_conv_g
 
 /* Fused causal depthwise convolution + bias + SiLU (page 4, Appendix D, Memory; page 1, the
  * kernels paragraph): one read of x, one write of out, the state in and out of the cache.
- * Deterministic.  seqlen == 1 with state_out == state_in is the recurrent (decode) step. */
+ * Deterministic.  seqlen == 1 with state_out == state_in is the recurrent (decode) step;
+ * it runs a dedicated kernel (one thread per channel row). */
 msel_status msel_conv1d_fwd(const msel_conv_args *args, hipStream_t stream);
 
 /* Its backward, recomputing pre and the activation from x (page 4, Appendix D, Memory):

@@ -66,8 +66,8 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
                 p.chunk_states[((static_cast<size_t>(b) * p.D + dch[r]) * p.nchunks + c) * N +
                                lane] = carry[r];
             float uu[K], dd[K];
-            load_k<T, K, VEC>(u[r], t0, L, uu, 0.0f);
-            load_k<T, K, VEC>(dl[r], t0, L, dd, 0.0f);
+            load_k_cached<T, K, VEC>(u[r], t0, L, uu);
+            load_k_cached<T, K, VEC>(dl[r], t0, L, dd);
             float run = 0.0f;
 #pragma unroll
             for (int k = 0; k < K; ++k) {

@@ -12,15 +12,22 @@
 // ALU rate, so the design goal is full-width coalesced 16-byte accesses and enough bytes in
 // flight, nothing else.
 //
-// Work split: one wavefront per tile of 64*K consecutive steps of one (b, d) row, K = two
-// 16-byte vectors per lane (16 bf16 or 8 fp32 values).  Lane l holds steps
-// [t0 + l*K, t0 + (l+1)*K).  The W-1 inputs before a lane's first step come from lane l-1
-// through a wave-wide DPP shift; lane 0 takes them from a wave-uniform load of the previous
-// tile's last inputs, or of state_in for the first tile.  The backward also needs dpre at the
-// W-1 steps after a lane's last one: lane l+1 provides them, and lane 63 recomputes them from
-// the next tile's first inputs.  The first tile's wavefront is the only reader of state_in
-// and the only writer of state_out, after its reads, so the cache may be updated in place.
+// Work split: tiles of 64*K consecutive steps of one (b, d) row, K = two 16-byte vectors per
+// lane (16 bf16 or 8 fp32 values); lane l holds steps [t0 + l*K, t0 + (l+1)*K).  The forward
+// runs one wavefront per tile.  The backward runs one wavefront per segment of consecutive
+// tiles of a row, with the next tile's loads in flight while one is computed, and adds its
+// tap and bias sums with one atomic per segment.  The W-1 inputs before a lane's first step
+// come from lane l-1 through a wave-wide DPP shift; lane 0 takes them from the previous tile
+// (a wave-uniform load at a segment's start, registers inside it) or from state_in for the
+// row's first tile.  The backward also needs dpre at the W-1 steps after a lane's last one:
+// lane l+1 provides them, and lane 63 recomputes them from lane 0 of the next tile.  The first
+// tile's wavefront is the only reader of state_in and the only writer of state_out, after its
+// reads, so the cache may be updated in place.  Accesses are plain cached ones: the
+// non-temporal hint measured slower for these streams.
+// seqlen 1 (the decode step) runs a separate kernel with one thread per row.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "msel_device.hpp"
 #include "msel_kernels.hpp"
@@ -30,6 +37,8 @@ namespace msel {
 namespace {
 
 constexpr int kConvWaves = 4;  // wavefronts per workgroup
+// wavefronts a launch aims for: 16 per CU of the 256 (at most 32 fit)
+constexpr int64_t kConvTargetWaves = 4096;
 
 template <typename T>
 constexpr int conv_k() { return 2 * Elem<T>::kPerVec; }
@@ -40,25 +49,29 @@ __device__ __forceinline__ float dsilu(float p) {
     return s * fmaf(p, 1.0f - s, 1.0f);
 }
 
-struct Tile {
+__device__ __forceinline__ uint32_t div_by(uint32_t n, const FastDiv& f) {
+    return (__umulhi(n, f.m) + n) >> f.l;
+}
+
+// A wavefront's work: tiles [tile0, tile0 + ntiles) of one (b, d) row.
+struct Seg {
     int64_t row;  // b * dim + d
     int d;
-    int tile;     // index of the tile in its row
-    int tw;       // first step of the tile
-    int t0;       // first step of this lane
+    int seg;      // index of the segment in its row
+    int tile0;
+    int ntiles;
 };
 
-template <typename T>
-__device__ __forceinline__ bool tile_of(const ConvParams& p, Tile& w) {
-    constexpr int K = conv_k<T>();
-    const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const int64_t wave = static_cast<int64_t>(blockIdx.x) * kConvWaves + wid;
-    if (wave >= p.rows * p.tiles) return false;
-    w.row = wave / p.tiles;
-    w.tile = static_cast<int>(wave - w.row * p.tiles);
-    w.d = static_cast<int>(w.row % p.D);
-    w.tw = w.tile * 64 * K;
-    w.t0 = w.tw + lane_id() * K;
+__device__ __forceinline__ bool seg_of(const ConvParams& p, Seg& s) {
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t wave = blockIdx.x * kConvWaves + wid;  // < 2^31: checked on the host
+    if (wave >= static_cast<uint32_t>(p.rows) * static_cast<uint32_t>(p.segs)) return false;
+    const uint32_t row = div_by(wave, p.segs_div);
+    s.row = row;
+    s.seg = static_cast<int>(wave - row * static_cast<uint32_t>(p.segs));
+    s.d = static_cast<int>(row - div_by(row, p.dim_div) * static_cast<uint32_t>(p.D));
+    s.tile0 = s.seg * p.seg_tiles;
+    s.ntiles = min(p.seg_tiles, p.tiles - s.tile0);
     return true;
 }
 
@@ -89,25 +102,27 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_fwd_kernel(ConvParams p)
     constexpr int K = conv_k<T>();
     constexpr int H = W - 1;
     constexpr int HA = H > 0 ? H : 1;
-    Tile tl;
-    if (!tile_of<T>(p, tl)) return;
+    Seg sg;  // the forward's segments are single tiles
+    if (!seg_of(p, sg)) return;
     const int L = p.L;
-    const T* __restrict__ xr = static_cast<const T*>(p.x) + tl.row * L;
+    const int lane = lane_id();
+    const int tw = sg.tile0 * 64 * K;
+    const int t0 = tw + lane * K;
+    const T* __restrict__ xr = static_cast<const T*>(p.x) + sg.row * L;
     const T* st = (H > 0 && p.state_in != nullptr)
-                      ? static_cast<const T*>(p.state_in) + tl.row * H : nullptr;
+                      ? static_cast<const T*>(p.state_in) + sg.row * H : nullptr;
 
     float v[K];
-    load_k<T, K, VEC>(xr, tl.t0, L, v, 0.0f);
+    load_k_cached<T, K, VEC>(xr, t0, L, v);
     float wk[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) wk[i] = p.w[static_cast<size_t>(tl.d) * W + i];
-    const float b = p.bias != nullptr ? p.bias[tl.d] : 0.0f;
+    for (int i = 0; i < W; ++i) wk[i] = p.w[static_cast<size_t>(sg.d) * W + i];
+    const float b = p.bias != nullptr ? p.bias[sg.d] : 0.0f;
 
     // the H inputs before each lane's first step, oldest first
     float prev[HA];
 #pragma unroll
-    for (int j = 0; j < H; ++j)
-        prev[j] = shift_up(v[K - H + j], input_at<T, H>(xr, st, tl.tw - H + j));
+    for (int j = 0; j < H; ++j) prev[j] = shift_up(v[K - H + j], input_at<T, H>(xr, st, tw - H + j));
 
     float o[K];
 #pragma unroll
@@ -115,17 +130,17 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_fwd_kernel(ConvParams p)
         const float pre = pre_at<W, K>(wk, b, prev, v, k);
         o[k] = SILU ? pre * sigmoid_f(pre) : pre;
     }
-    store_k<T, K, VEC>(static_cast<T*>(p.out) + tl.row * L, tl.t0, L, o);
+    store_k<T, K, VEC, false>(static_cast<T*>(p.out) + sg.row * L, t0, L, o);
 
     // the cache after the call: the last H entries of [state_in, x]
-    if (H > 0 && tl.tile == 0 && p.state_out != nullptr && lane_id() < H) {
-        const int t = L - H + lane_id();
+    if (H > 0 && sg.seg == 0 && p.state_out != nullptr && lane < H) {
+        const int t = L - H + lane;
         float s = 0.0f;
         if (t >= 0)
             s = Elem<T>::load1(xr + t);
         else if (st != nullptr)
             s = Elem<T>::load1(st + H + t);
-        Elem<T>::store1(static_cast<T*>(p.state_out) + tl.row * H + lane_id(), s);
+        Elem<T>::store1(static_cast<T*>(p.state_out) + sg.row * H + lane, s);
     }
 }
 
@@ -134,129 +149,186 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_bwd_kernel(ConvParams p)
     constexpr int K = conv_k<T>();
     constexpr int H = W - 1;
     constexpr int HA = H > 0 ? H : 1;
-    Tile tl;
-    if (!tile_of<T>(p, tl)) return;
+    constexpr int TILE = 64 * K;
+    Seg sg;
+    if (!seg_of(p, sg)) return;
     const int L = p.L;
     const int lane = lane_id();
-    const T* __restrict__ xr = static_cast<const T*>(p.x) + tl.row * L;
-    const T* __restrict__ gr = static_cast<const T*>(p.dout) + tl.row * L;
+    const T* __restrict__ xr = static_cast<const T*>(p.x) + sg.row * L;
+    const T* __restrict__ gr = static_cast<const T*>(p.dout) + sg.row * L;
+    T* __restrict__ dxr = static_cast<T*>(p.dx) + sg.row * L;
     const T* st = (H > 0 && p.state_in != nullptr)
-                      ? static_cast<const T*>(p.state_in) + tl.row * H : nullptr;
+                      ? static_cast<const T*>(p.state_in) + sg.row * H : nullptr;
+    int t0 = sg.tile0 * TILE + lane * K;
 
-    float v[K], g[K];
-    load_k<T, K, VEC>(xr, tl.t0, L, v, 0.0f);
-    load_k<T, K, VEC>(gr, tl.t0, L, g, 0.0f);
+    Raw<T, K> cx, cg, nx, ng;
+    load_raw<T, K, VEC>(xr, t0, L, cx);
+    load_raw<T, K, VEC>(gr, t0, L, cg);
     float wk[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) wk[i] = p.w[static_cast<size_t>(tl.d) * W + i];
-    const float b = p.bias != nullptr ? p.bias[tl.d] : 0.0f;
-
-    float prev[HA];
+    for (int i = 0; i < W; ++i) wk[i] = p.w[static_cast<size_t>(sg.d) * W + i];
+    const float b = p.bias != nullptr ? p.bias[sg.d] : 0.0f;
+    float halo[HA];
 #pragma unroll
-    for (int j = 0; j < H; ++j)
-        prev[j] = shift_up(v[K - H + j], input_at<T, H>(xr, st, tl.tw - H + j));
-
-    // dpre at the lane's own steps (0 past the end: dout reads 0 there)
-    float dp[K];
+    for (int j = 0; j < H; ++j) halo[j] = input_at<T, H>(xr, st, sg.tile0 * TILE - H + j);
+    // sums over the segment: lane partials of dw[i] and of dbias (index W)
+    float part[W + 1];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const float pre = pre_at<W, K>(wk, b, prev, v, k);
-        dp[k] = SILU ? g[k] * dsilu(pre) : g[k];
-    }
+    for (int i = 0; i <= W; ++i) part[i] = 0.0f;
 
-    // dpre at the H steps after the tile, for lane 63: window [x of lane 63's last H steps,
-    // x of the next tile's first H steps]
-    float nxt[HA];
-    if constexpr (H > 0) {
-        const int tn = tl.tw + 64 * K;
-        float ext[2 * H], gn[H];
+    for (int i = 0; i < sg.ntiles; ++i, t0 += TILE) {
+        // the next tile in flight while this one is computed (zeros past the row's end); its
+        // first steps also complete this tile's last dpre values
+        load_raw<T, K, VEC>(xr, t0 + TILE, L, nx);
+        load_raw<T, K, VEC>(gr, t0 + TILE, L, ng);
+        float v[K], g[K];
+        unpack<T, K>(cx, v);
+        unpack<T, K>(cg, g);
+        float prev[HA];
 #pragma unroll
-        for (int j = 0; j < H; ++j) {
-            ext[j] = readlane(v[K - H + j], 63);
-            const bool in = tn + j < L;
-            ext[H + j] = in ? Elem<T>::load1(xr + tn + j) : 0.0f;
-            gn[j] = in ? Elem<T>::load1(gr + tn + j) : 0.0f;
+        for (int j = 0; j < H; ++j) prev[j] = shift_up(v[K - H + j], halo[j]);
+
+        // dpre at the lane's own steps (0 past the end: dout reads 0 there)
+        float dp[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float pre = pre_at<W, K>(wk, b, prev, v, k);
+            dp[k] = SILU ? g[k] * dsilu(pre) : g[k];
         }
-#pragma unroll
-        for (int j = 0; j < H; ++j) {
-            float pre = b;
-#pragma unroll
-            for (int i = 0; i < W; ++i) pre = fmaf(wk[i], ext[j + i], pre);
-            const float dpn = SILU ? gn[j] * dsilu(pre) : gn[j];
-            nxt[j] = shift_down(dp[j], dpn);
-        }
-    }
 
-    // dx at step s gathers w[i] * dpre[s + H - i]
-    float dx[K];
+        // dpre at the H steps after the tile, for lane 63, from the window [x of lane 63's
+        // last H steps, x of the next tile's first H steps (lane 0 of the next tile)]
+        float nxt[HA];
+        if constexpr (H > 0) {
+            float ext[2 * H], gn[H];
+            {
+                float vn[K], gnk[K];
+                unpack<T, K>(nx, vn);
+                unpack<T, K>(ng, gnk);
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        float acc = 0.0f;
+                for (int j = 0; j < H; ++j) {
+                    ext[H + j] = readlane(vn[j], 0);
+                    gn[j] = readlane(gnk[j], 0);
+                }
+            }
 #pragma unroll
-        for (int i = 0; i < W; ++i) {
-            const int e = k + H - i;
-            acc = fmaf(wk[i], e < K ? dp[e] : nxt[e - K], acc);
-        }
-        dx[k] = acc;
-    }
-    store_k<T, K, VEC>(static_cast<T*>(p.dx) + tl.row * L, tl.t0, L, dx);
-
-    // gradient w.r.t. the incoming state: entry j (step j - H) meets tap j - m at step m <= j
-    if (H > 0 && tl.tile == 0 && p.dstate != nullptr) {
-        float d0[HA];
-#pragma unroll
-        for (int m = 0; m < H; ++m) d0[m] = readlane(dp[m], 0);
-        if (lane == 0) {
+            for (int j = 0; j < H; ++j) ext[j] = readlane(v[K - H + j], 63);
 #pragma unroll
             for (int j = 0; j < H; ++j) {
-                float acc = 0.0f;
+                float pre = b;
 #pragma unroll
-                for (int m = 0; m <= j; ++m) acc = fmaf(wk[j - m], d0[m], acc);
-                p.dstate[tl.row * H + j] = acc;
+                for (int q = 0; q < W; ++q) pre = fmaf(wk[q], ext[j + q], pre);
+                const float dpn = SILU ? gn[j] * dsilu(pre) : gn[j];
+                nxt[j] = shift_down(dp[j], dpn);
             }
         }
-    }
 
-    // dw[i] = sum over steps of dpre * xe[step + i], dbias = sum of dpre
-    if (p.dw != nullptr || p.dbias != nullptr) {
-        float part[W + 1];
+        // dx at step s gathers w[i] * dpre[s + H - i]
+        float dx[K];
 #pragma unroll
-        for (int i = 0; i <= W; ++i) part[i] = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int q = 0; q < W; ++q) {
+                const int e = k + H - q;
+                acc = fmaf(wk[q], e < K ? dp[e] : nxt[e - K], acc);
+            }
+            dx[k] = acc;
+        }
+        store_k<T, K, VEC, false>(dxr, t0, L, dx);
+
+        // gradient w.r.t. the incoming state: entry j (step j - H) meets tap j - m at step
+        // m <= j, all inside lane 0 of the row's first tile
+        if (H > 0 && sg.tile0 + i == 0 && p.dstate != nullptr) {
+            float d0[HA];
+#pragma unroll
+            for (int m = 0; m < H; ++m) d0[m] = readlane(dp[m], 0);
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < H; ++j) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int m = 0; m <= j; ++m) acc = fmaf(wk[j - m], d0[m], acc);
+                    p.dstate[sg.row * H + j] = acc;
+                }
+            }
+        }
+
+        // dw[q] gathers dpre * xe[step + q], dbias gathers dpre
 #pragma unroll
         for (int k = 0; k < K; ++k) {
 #pragma unroll
-            for (int i = 0; i < W; ++i) {
-                const int e = k + i;
-                part[i] = fmaf(dp[k], e < H ? prev[e] : v[e - H], part[i]);
+            for (int q = 0; q < W; ++q) {
+                const int e = k + q;
+                part[q] = fmaf(dp[k], e < H ? prev[e] : v[e - H], part[q]);
             }
             part[W] += dp[k];
         }
+#pragma unroll
+        for (int j = 0; j < H; ++j) halo[j] = readlane(v[K - H + j], 63);
+        cx = nx;
+        cg = ng;
+    }
+
+    if (p.dw != nullptr || p.dbias != nullptr) {
         float tot[W + 1];
 #pragma unroll
-        for (int i = 0; i <= W; ++i) tot[i] = wave_sum_fused(part[i]);
-        // one vector atomic: lane i < W adds dw[d, i], lane 63 adds dbias[d]
+        for (int q = 0; q <= W; ++q) tot[q] = wave_sum_fused(part[q]);
+        // one vector atomic per segment: lane q < W adds dw[d, q], lane 63 adds dbias[d]
         float* dst = nullptr;
         float val = 0.0f;
 #pragma unroll
-        for (int i = 0; i < W; ++i)
-            if (lane == i && p.dw != nullptr) {
-                dst = p.dw + static_cast<size_t>(tl.d) * W + i;
-                val = tot[i];
+        for (int q = 0; q < W; ++q)
+            if (lane == q && p.dw != nullptr) {
+                dst = p.dw + static_cast<size_t>(sg.d) * W + q;
+                val = tot[q];
             }
         if (lane == 63 && p.dbias != nullptr) {
-            dst = p.dbias + tl.d;
+            dst = p.dbias + sg.d;
             val = tot[W];
         }
         if (dst != nullptr) unsafeAtomicAdd(dst, val);
     }
 }
 
+// The recurrent (decode) step, seqlen 1: one thread per (b, d) row.  It reads the row's
+// state and input, writes the output and the shifted state [state[1..H), x] -- after its own
+// reads, so the state may be updated in place.
+template <typename T, int W, bool SILU>
+__global__ __launch_bounds__(256) void conv_step_kernel(ConvParams p) {
+    constexpr int H = W - 1;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (row >= p.rows) return;
+    const int d = static_cast<int>(row % p.D);
+    const T* st = (H > 0 && p.state_in != nullptr)
+                      ? static_cast<const T*>(p.state_in) + row * H : nullptr;
+    float win[W];  // [state, x]
+#pragma unroll
+    for (int j = 0; j < H; ++j) win[j] = st != nullptr ? Elem<T>::load1(st + j) : 0.0f;
+    win[H] = Elem<T>::load1(static_cast<const T*>(p.x) + row);
+    float pre = p.bias != nullptr ? p.bias[d] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < W; ++i) pre = fmaf(p.w[static_cast<size_t>(d) * W + i], win[i], pre);
+    Elem<T>::store1(static_cast<T*>(p.out) + row, SILU ? pre * sigmoid_f(pre) : pre);
+    if (H > 0 && p.state_out != nullptr) {
+        T* so = static_cast<T*>(p.state_out) + row * H;
+#pragma unroll
+        for (int j = 0; j < H; ++j) Elem<T>::store1(so + j, win[j + 1]);
+    }
+}
+
 template <typename T, int W, bool SILU>
 hipError_t conv_go(const ConvParams& p, bool bwd, hipStream_t stream) {
     const bool vec = p.L % Elem<T>::kPerVec == 0;
-    const int64_t waves = p.rows * p.tiles;
+    const int64_t waves = p.rows * p.segs;
     const dim3 grid(static_cast<unsigned>((waves + kConvWaves - 1) / kConvWaves));
     const dim3 block(64 * kConvWaves);
+    if (!bwd && p.L == 1) {
+        hipLaunchKernelGGL((conv_step_kernel<T, W, SILU>),
+                           dim3(static_cast<unsigned>((p.rows + 255) / 256)), dim3(256), 0, stream,
+                           p);
+        return hipGetLastError();
+    }
     if (bwd) {
         if (vec)
             hipLaunchKernelGGL((conv_bwd_kernel<T, W, SILU, true>), grid, block, 0, stream, p);
@@ -286,15 +358,29 @@ template <typename T>
 hipError_t conv_dispatch(ConvParams p, bool bwd, hipStream_t stream) {
     p.tiles = static_cast<int>((static_cast<int64_t>(p.L) + 64 * conv_k<T>() - 1) /
                                (64 * conv_k<T>()));
+    // tiles per wavefront.  The forward takes one: wavefronts that run together then stream
+    // one contiguous stretch of memory, which measured faster than many row-wise streams.  The
+    // backward walks segments of several tiles with the next one in flight, so that it adds
+    // its tap/bias sums once per segment: the tiles of one channel run at the same time, and
+    // one atomic per tile on the same few addresses measured as a large share of its time.
+    const int64_t total = p.rows * p.tiles;
+    p.seg_tiles = bwd ? static_cast<int>(std::min<int64_t>(
+                            p.tiles, std::max<int64_t>(1, (total + kConvTargetWaves - 1) /
+                                                              kConvTargetWaves)))
+                      : 1;
+    p.segs = (p.tiles + p.seg_tiles - 1) / p.seg_tiles;
+    if (p.rows * p.segs > kMaxConvWaves) return hipErrorInvalidValue;
+    p.segs_div = make_fastdiv(static_cast<uint32_t>(p.segs));
+    p.dim_div = make_fastdiv(static_cast<uint32_t>(p.D));
     return p.silu ? conv_width<T, true>(p, bwd, stream) : conv_width<T, false>(p, bwd, stream);
 }
 
 }  // namespace
 
-int64_t conv_workgroups(int64_t rows, int L, bool bf16) {
+int64_t conv_waves(int64_t rows, int L, bool bf16) {
+    // the most a launch uses: one wavefront per tile
     const int64_t per_tile = 64 * (bf16 ? conv_k<bf16_t>() : conv_k<float>());
-    const int64_t waves = rows * ((L + per_tile - 1) / per_tile);
-    return (waves + kConvWaves - 1) / kConvWaves;
+    return rows * ((L + per_tile - 1) / per_tile);
 }
 
 hipError_t launch_conv_fwd(const ConvParams& p, bool bf16, hipStream_t stream) {

@@ -78,9 +78,6 @@ msel_status hip_status(hipError_t e) { return e == hipSuccess ? MSEL_OK : MSEL_E
 
 // ---- the short causal convolution ------------------------------------------------------
 
-// Largest grid the convolution kernels launch (gridDim.x is 32-bit).
-constexpr int64_t kMaxConvGroups = (int64_t(1) << 31) - 1;
-
 size_t elem_bytes(int32_t dtype) { return dtype == MSEL_BF16 ? 2 : 4; }
 
 msel_status check_conv(const msel_conv_args* a) {
@@ -92,8 +89,8 @@ msel_status check_conv(const msel_conv_args* a) {
     if (a->dtype != MSEL_F32 && a->dtype != MSEL_BF16) return MSEL_ERR_DTYPE;
     if (a->activation != 0 && a->activation != 1) return MSEL_ERR_DTYPE;
     if (a->width > MSEL_MAX_CONV_WIDTH) return MSEL_ERR_UNSUPPORTED;
-    if (msel::conv_workgroups(static_cast<int64_t>(a->batch) * a->dim, a->seqlen,
-                              a->dtype == MSEL_BF16) > kMaxConvGroups)
+    if (msel::conv_waves(static_cast<int64_t>(a->batch) * a->dim, a->seqlen,
+                         a->dtype == MSEL_BF16) > msel::kMaxConvWaves)
         return MSEL_ERR_SHAPE;
     if (a->x == nullptr || a->weight == nullptr) return MSEL_ERR_NULL;
     if (!aligned(a->x, 16)) return MSEL_ERR_ALIGN;

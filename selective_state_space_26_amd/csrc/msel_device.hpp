@@ -146,7 +146,9 @@ __device__ __forceinline__ void load_k_cached(const T* __restrict__ row, int t0,
     }
 }
 
-template <typename T, int K, bool VEC>
+// Store K consecutive elements row[t0 .. t0+K) (out-of-range ones are dropped).  NT: the
+// non-temporal (streaming) hint, for rows nothing reads soon.
+template <typename T, int K, bool VEC, bool NT = true>
 __device__ __forceinline__ void store_k(T* __restrict__ row, int t0, int L, const float (&v)[K]) {
     constexpr int VW = Elem<T>::kPerVec;
     if constexpr (VEC) {
@@ -166,7 +168,7 @@ __device__ __forceinline__ void store_k(T* __restrict__ row, int t0, int L, cons
                 w.w = pack_bf16(v[8 * j + 6], v[8 * j + 7]);
             }
             __builtin_amdgcn_raw_buffer_store_b128(w, row_rsrc(row, L),
-                                                   t * static_cast<int>(sizeof(T)), 0, 2);
+                                                   t * static_cast<int>(sizeof(T)), 0, NT ? 2 : 0);
         }
     } else {
 #pragma unroll

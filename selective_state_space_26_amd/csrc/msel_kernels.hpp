@@ -60,13 +60,30 @@ struct FillList {
 };
 hipError_t launch_fill_zero(const FillList& f, hipStream_t stream);
 
+// Division of a 31-bit unsigned value by a fixed divisor d >= 1 with one multiply-high, an add
+// and a shift (the round-up method of Granlund and Montgomery): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(m, n) + n) >> l for every n < 2^31 (the sum
+// then stays below 2^32).
+struct FastDiv {
+    uint32_t d, m, l;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return FastDiv{d, static_cast<uint32_t>(m), l};
+}
+
 // Short causal convolution (+ bias, + SiLU when silu != 0) over rows = batch * dim rows of
 // length L; W taps.  The forward reads x, state_in and writes out, state_out; the backward
 // reads x, state_in, dout and writes dx, dstate and adds into dw, dbias (zeroed by the caller).
 struct ConvParams {
     int64_t rows;
     int D, L, W, silu;
-    int tiles;  // set by the launcher
+    // set by the launcher: tiles per row, tiles per wavefront (a segment), segments per row
+    int tiles, seg_tiles, segs;
+    FastDiv segs_div;    // by segs
+    FastDiv dim_div;     // by D
     const void* x;
     const float* w;
     const float* bias;
@@ -79,8 +96,10 @@ struct ConvParams {
     float* dbias;
     float* dstate;
 };
-// Workgroups one launch of either kernel uses (the host rejects sizes whose grid would not fit).
-int64_t conv_workgroups(int64_t rows, int L, bool bf16);
+// Wavefronts one launch of either kernel uses; the host rejects sizes above kMaxConvWaves
+// wavefronts (their indices must stay below 2^31).
+constexpr int64_t kMaxConvWaves = (int64_t(1) << 31) - 1;
+int64_t conv_waves(int64_t rows, int L, bool bf16);
 hipError_t launch_conv_fwd(const ConvParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_conv_bwd(const ConvParams& p, bool bf16, hipStream_t stream);
 

@@ -60,8 +60,8 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
         float sum_dt = 0.0f;
         {
             float uu[K], dd[K];
-            load_k<T, K, VEC>(u, t0, L, uu, 0.0f);
-            load_k<T, K, VEC>(dl, t0, L, dd, 0.0f);
+            load_k_cached<T, K, VEC>(u, t0, L, uu);
+            load_k_cached<T, K, VEC>(dl, t0, L, dd);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float x = dd[k] + bias;
@@ -112,11 +112,11 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
         }
         if constexpr (HAS_Z) {
             float zz[K];
-            load_k<T, K, VEC>(zr, t0, L, zz, 0.0f);
+            load_k_cached<T, K, VEC>(zr, t0, L, zz);
 #pragma unroll
             for (int k = 0; k < K; ++k) y[k] *= zz[k] * sigmoid_f(zz[k]);
         }
-        store_k<T, K, VEC>(out, t0, L, y);
+        store_k<T, K, VEC, false>(out, t0, L, y);
         if (p.chunk_states != nullptr && lane < N) {
 #pragma unroll
             for (int q = 0; q < kCpt; ++q) {

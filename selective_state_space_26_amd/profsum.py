@@ -27,6 +27,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 BWD_SOURCES = ("selective_state_space_26_amd/csrc/scan_bwd.hip",
                "selective_state_space_26_amd/csrc/msel_device.hpp",
                "selective_state_space_26_amd/csrc/msel_kernels.hpp")
+CONV_SOURCES = ("selective_state_space_26_amd/csrc/conv1d.hip",
+                "selective_state_space_26_amd/csrc/msel_device.hpp",
+                "selective_state_space_26_amd/csrc/msel_kernels.hpp")
+
+
+def sources_of(kernel: str):
+    """The sources a kernel is built from (their digest goes into its traffic file)."""
+    return CONV_SOURCES if kernel.startswith("conv_") else BWD_SOURCES
 
 
 def source_digest(files=BWD_SOURCES) -> str:
@@ -99,7 +107,7 @@ def traffic(fetch_csv, write_csv, out, kernel, copy_mib, workload, cmd_fetch, cm
         f"# is scaled by a plain {copy_mib} MiB device copy read by the same counter",
         f"workload = {workload}",
         f"kernel = {kernel}",
-        f"source_sha256 = {source_digest()}",
+        f"source_sha256 = {source_digest(sources_of(kernel))}",
     ]
     for c, r in res.items():
         lc = c.lower()
