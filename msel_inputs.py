@@ -9,6 +9,10 @@ Distributions (the workloads' recipe): u, z ~ N(0,1) and delta = 0.5*N(0,1) of s
 [1e-3, 1e-1]); A[d, n] = -(n+1) (S4D-real); B, C ~ N(0,1) of shape [batch, dstate, seqlen],
 shared by all channels; D ~ N(0,1) of shape [dim]; dout ~ N(0,1) for the backward.
 
+The trapezoidal variant adds (``make(..., with_lam=True)``) the mixing weight lam ~ U[0, 1]
+of shape [batch, dim, seqlen], and for continued sequences (``with_prev=True``) the inputs of
+the step before the first, u_prev ~ N(0,1) [batch, dim] and B_prev ~ N(0,1) [batch, dstate].
+
 The short convolution before the scan (``make_conv``): x ~ N(0,1) of shape [batch, dim,
 seqlen]; taps w[d, k] and bias b[d] ~ U(-1/sqrt(W), 1/sqrt(W)) (the default initialisation of a
 depthwise 1-d convolution, whose fan-in is the width W); the incoming state (the W-1 inputs
@@ -25,7 +29,7 @@ import numpy as np
 
 TENSOR_IDS = {"u": 0, "delta": 1, "z": 2, "B": 3, "C": 4, "D": 5, "bias": 6, "dout": 7,
               "h0": 8, "conv_x": 9, "conv_w": 10, "conv_b": 11, "conv_state": 12,
-              "conv_dout": 13}
+              "conv_dout": 13, "lam": 14, "u_prev": 15, "B_prev": 16}
 
 
 @dataclass(frozen=True)
@@ -108,7 +112,8 @@ def _normal(seed, name, shape, scale=1.0):
 
 def make(batch: int, dim: int, dstate: int, seqlen: int, dtype: str = "f32", seed: int = 0,
          with_z: bool = True, with_D: bool = True, with_bias: bool = True,
-         with_dout: bool = False, with_h0: bool = False) -> Tensors:
+         with_dout: bool = False, with_h0: bool = False, with_lam: bool = False,
+         with_prev: bool = False) -> Tensors:
     """Draw one problem.  Activation-shaped tensors follow ``dtype``; A, D, bias, h0 are fp32."""
     if dtype not in ("f32", "bf16"):
         raise ValueError(dtype)
@@ -133,6 +138,12 @@ def make(batch: int, dim: int, dstate: int, seqlen: int, dtype: str = "f32", see
         t["bias"] = None
     t["h0"] = _normal(seed, "h0", (batch, dim, dstate)) if with_h0 else None
     t["dout"] = act("dout", (batch, dim, seqlen)) if with_dout else None
+    if with_lam:
+        lam = rng(seed, "lam").uniform(0.0, 1.0, size=(batch, dim, seqlen)).astype(np.float32)
+        t["lam"] = f32_to_bf16_bits(lam) if dtype == "bf16" else lam
+    if with_prev:
+        t["u_prev"] = act("u_prev", (batch, dim))
+        t["B_prev"] = act("B_prev", (batch, dstate))
     return t
 
 

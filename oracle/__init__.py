@@ -5,10 +5,12 @@ import this package.  The product path (the HIP library and its Python binding) 
 this package never imports the product package.  The two share nothing but the seeded input
 generator ``msel_inputs``.
 
-Two independent implementations live here:
+The implementations here:
 
 * ``fwd`` / ``chunk_states_formula`` / ``bwd`` call the plain C loop in ``msel_oracle.c``
   (sequential over time, one (batch, channel) recurrence per work unit, double precision).
+* ``trap.py`` is the exponential-trapezoidal variant of the scan (Mamba-3), a numpy loop over
+  time in float64 that shares nothing with the C loop.
 * ``conv.py`` is the short causal convolution and activation that feed the scan (forward,
   hand-derived backward, convolutional state), written out tap by tap in float64.
 * ``twin_fwd`` in ``twin.py`` is a numpy restatement, vectorized over (batch, channel, state)
