@@ -35,6 +35,7 @@ METRIC = "selective-scan fwd/bwd tokens·channels/s and achieved HBM GB/s (% of 
 FLOPS_FWD = 7      # Delta*A, exp2, (Delta u)*B, h = a h + p, y += C h
 FLOPS_BWD = 20     # recompute h (5), adjoint (3), g = lam h a (2), dA, dDelta, du, dB, dC (10)
 FLOPS_BWD_Z = 2    # y += C h, rebuilt for dz when there is a gate
+FLOPS_TRAP = 10    # Delta*A, exp2, c*B_prev, (gamma u)*B, p = a*(c B_prev) + .., h, y
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, per kernel, of the default workload
 TRAFFIC_FILE = "profiles/{kernel}_d768x2_bf16_traffic.txt"
 CONV_WIDTH = 4     # taps of the short causal convolution before the scan
@@ -203,6 +204,33 @@ def main():
     dec_per_graph, dec_reps = 32, 10
     per["decode_step"] = graph_time(decode, dec_per_graph, dec_reps)
 
+    # the exponential-trapezoidal forward at the same shape: one more input stream (lambda);
+    # calls alternate between two copies of the streamed inputs (~400 MB, more than the
+    # last-level cache)
+    lam = put(msel_inputs.make(w.batch, w.dim, w.dstate, w.seqlen, w.dtype, w.seed,
+                               with_lam=True)["lam"], act)
+    tsets = [{k: (d[k] if i == 0 else d[k].clone()) for k in ("u", "delta", "z")} |
+             {"lam": lam if i == 0 else lam.clone(), "out": torch.empty_like(d["u"])}
+             for i in range(2)]
+    trap_cs = torch.empty(w.batch, w.dim, nch, w.dstate, device=dev, dtype=torch.float32)
+    trap_fin = torch.empty(w.batch, w.dim, w.dstate, device=dev, dtype=torch.float32)
+
+    def trap_fwd(i):
+        c = tsets[i % 2]
+        msel.msel_scan_trap_fwd(c["u"], c["delta"], c["lam"], d["A"], d["B"], d["C"], d["D"],
+                                c["z"], d["bias"], True, out=c["out"], final_state=trap_fin,
+                                chunk_states=trap_cs)
+    for i in range(4):
+        trap_fwd(i)
+    tev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    tev[0].record()
+    for i in range(args.steps):
+        trap_fwd(i)
+    tev[1].record()
+    torch.cuda.synchronize()
+    per["trap_fwd"] = tev[0].elapsed_time(tev[1]) / args.steps
+    del tsets
+
     # the short causal convolution + SiLU that makes the scan's input, at the same batch,
     # channels, length and dtype, width 4, with bias and incoming state: forward, backward
     # (zero-fill + one kernel) and the decode step (seqlen 1, state updated in place)
@@ -247,9 +275,10 @@ def main():
     per["conv_decode_step"] = graph_time(conv_decode, dec_per_graph, dec_reps)
 
     fl_bwd = FLOPS_BWD + (FLOPS_BWD_Z if d.get("z") is not None else 0)
-    flops = {"fwd": FLOPS_FWD * upd, "bwd_main": fl_bwd * upd}
+    flops = {"fwd": FLOPS_FWD * upd, "bwd_main": fl_bwd * upd, "trap_fwd": FLOPS_TRAP * upd}
+    alg["trap_fwd"] = alg["fwd"] + tc * (2 if w.dtype == "bf16" else 4)  # + lambda
     kernels = {}
-    for n in ("fwd", "chunk_carry", "bwd_main", "bwd"):
+    for n in ("fwd", "chunk_carry", "bwd_main", "bwd", "trap_fwd"):
         sec = per[n] * 1e-3
         gbs = alg[n] / sec / 1e9
         kernels[n] = {"ms": round(per[n], 4), "alg_bytes": alg[n], "GB/s": round(gbs, 1),
@@ -258,6 +287,9 @@ def main():
         if n in flops:
             kernels[n]["TFLOP/s"] = round(flops[n] / sec / 1e12, 2)
     kernels["fwd"]["what"] = "scan_fwd_kernel (one launch)"
+    kernels["trap_fwd"]["what"] = ("scan_fwd_kernel with the exponential-trapezoidal rule "
+                                   "(msel_scan_trap_fwd, lambda as one more input), one launch, "
+                                   "timed apart from the step")
     kernels["chunk_carry"]["what"] = "chunk_carry_kernel (one launch), timed apart from the step"
     kernels["bwd_main"]["what"] = "bwd_main_kernel, the chunk-parallel gradient kernel"
     kernels["bwd"]["what"] = ("the msel_scan_bwd call: zero-fills, summary, link and "

@@ -182,6 +182,37 @@ msel_status msel_scan_bwd_profiled(const msel_scan_args *args, const msel_scan_g
                                    hipEvent_t ev_begin, hipEvent_t ev_end);
 
 /* ------------------------------------------------------------------------------------------
+ * The exponential-trapezoidal variant of the scan (Mamba-3).
+ *
+ * The input integral over a step is taken from both ends of the interval and mixed by a
+ * data-dependent weight lambda, the earlier end carried over the step by the exact transition
+ * (page 5, the Mamba-3 post, first bullet on the new discretization):
+ *
+ *   h_t = dA_t h_{t-1} + Delta_t * ( lambda_t B_t u_t + (1 - lambda_t) dA_t B_{t-1} u_{t-1} )
+ *
+ * with everything else as above.  lambda_t = 1 is the zero-order-hold/Euler scan of
+ * msel_scan_fwd; lambda_t = 1/2 is the trapezoidal rule.  The step before the first takes u_prev
+ * and B_prev (the last step of a sequence being continued, e.g. the previous decode step), or 0.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+    const void *lambda;     /* required [batch, dim, seqlen], activation dtype, in [0, 1],   */
+                            /* 16-byte aligned                                             */
+    const void *u_prev;     /* optional [batch, dim], activation dtype: u at step -1         */
+    const void *B_prev;     /* optional [batch, dstate], activation dtype: B at step -1      */
+} msel_trap_args;
+
+/* Host-only checks of msel_scan_trap_fwd's arguments (those of msel_validate_fwd, and the
+ * trapezoidal inputs'). */
+msel_status msel_validate_trap_fwd(const msel_scan_args *args, const msel_trap_args *trap);
+
+/* Fused forward scan with the exponential-trapezoidal rule: the same single pass, outputs
+ * (out, final_state, chunk_states) and conventions as msel_scan_fwd, reading lambda as one
+ * more input stream.  seqlen == 1 is the decode step (state in place allowed).  The backward
+ * and the chunk-carry pass of this variant are not part of the library. */
+msel_status msel_scan_trap_fwd(const msel_scan_args *args, const msel_trap_args *trap,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * The short causal convolution and activation that produce the scan's input.
  *
  * The selective SSM block runs an input projection, a short convolution, an activation, the

@@ -34,6 +34,10 @@ class ScanGrads(ctypes.Structure):
                 ("dC", _P), ("dD", _P), ("ddelta_bias", _P), ("dh0", _P)]
 
 
+class TrapArgs(ctypes.Structure):
+    _fields_ = [("lambda_", _P), ("u_prev", _P), ("B_prev", _P)]
+
+
 class ConvArgs(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_int32), ("batch", ctypes.c_int32),
                 ("dim", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("width", ctypes.c_int32),
@@ -58,7 +62,8 @@ EXPORTS = ["msel_abi_version", "msel_chunk_len", "msel_num_chunks", "msel_status
            "msel_validate_fwd", "msel_validate_chunk_carry", "msel_validate_bwd",
            "msel_scan_fwd", "msel_scan_chunk_carry", "msel_scan_bwd_workspace_bytes",
            "msel_scan_bwd", "msel_scan_bwd_profiled", "msel_validate_conv_fwd",
-           "msel_validate_conv_bwd", "msel_conv1d_fwd", "msel_conv1d_bwd"]
+           "msel_validate_conv_bwd", "msel_conv1d_fwd", "msel_conv1d_bwd",
+           "msel_validate_trap_fwd", "msel_scan_trap_fwd"]
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
@@ -95,6 +100,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.msel_scan_bwd.argtypes = [a, g, _P, ctypes.c_size_t, _P]
     lib.msel_scan_bwd_profiled.restype = ctypes.c_int
     lib.msel_scan_bwd_profiled.argtypes = [a, g, _P, ctypes.c_size_t, _P, _P, _P]
+    ta = ctypes.POINTER(TrapArgs)
+    lib.msel_validate_trap_fwd.restype = ctypes.c_int
+    lib.msel_validate_trap_fwd.argtypes = [a, ta]
+    lib.msel_scan_trap_fwd.restype = ctypes.c_int
+    lib.msel_scan_trap_fwd.argtypes = [a, ta, _P]
     ca, cg = ctypes.POINTER(ConvArgs), ctypes.POINTER(ConvGrads)
     lib.msel_validate_conv_fwd.restype = ctypes.c_int
     lib.msel_validate_conv_fwd.argtypes = [ca]

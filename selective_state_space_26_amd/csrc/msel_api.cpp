@@ -165,6 +165,22 @@ msel_status msel_validate_fwd(const msel_scan_args* a) {
     return MSEL_OK;
 }
 
+msel_status msel_validate_trap_fwd(const msel_scan_args* a, const msel_trap_args* tr) {
+    msel_status s = msel_validate_fwd(a);
+    if (s != MSEL_OK) return s;
+    if (tr == nullptr || tr->lambda == nullptr) return MSEL_ERR_NULL;
+    if (!aligned(tr->lambda, 16)) return MSEL_ERR_ALIGN;
+    const size_t e = a->dtype == MSEL_BF16 ? 2 : 4;
+    if ((tr->u_prev != nullptr && !aligned(tr->u_prev, e)) ||
+        (tr->B_prev != nullptr && !aligned(tr->B_prev, e)))
+        return MSEL_ERR_ALIGN;
+    const void* outs[] = {a->out, a->final_state, a->chunk_states};
+    for (const void* o : outs)
+        if (o != nullptr && (o == tr->lambda || o == tr->u_prev || o == tr->B_prev))
+            return MSEL_ERR_ALIAS;
+    return MSEL_OK;
+}
+
 msel_status msel_validate_chunk_carry(const msel_scan_args* a) {
     msel_status s = check_common(a);
     if (s != MSEL_OK) return s;
@@ -273,6 +289,17 @@ msel_status msel_scan_fwd(const msel_scan_args* a, hipStream_t stream) {
     msel_status s = msel_validate_fwd(a);
     if (s != MSEL_OK) return s;
     return hip_status(msel::launch_scan_fwd(to_params(a), a->dtype == MSEL_BF16, stream));
+}
+
+msel_status msel_scan_trap_fwd(const msel_scan_args* a, const msel_trap_args* tr,
+                               hipStream_t stream) {
+    msel_status s = msel_validate_trap_fwd(a, tr);
+    if (s != MSEL_OK) return s;
+    msel::ScanParams p = to_params(a);
+    p.lam = tr->lambda;
+    p.u_prev = tr->u_prev;
+    p.B_prev = tr->B_prev;
+    return hip_status(msel::launch_scan_fwd(p, a->dtype == MSEL_BF16, stream));
 }
 
 msel_status msel_scan_chunk_carry(const msel_scan_args* a, hipStream_t stream) {

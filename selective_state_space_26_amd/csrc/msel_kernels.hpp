@@ -26,6 +26,11 @@ struct ScanParams {
     void* out;
     float* final_state;
     float* chunk_states;
+    // exponential-trapezoidal variant only (null otherwise): the mixing weight [B, D, L], and
+    // the inputs of the step before the first, u [B, D] and B [B, N] (null: 0)
+    const void* lam = nullptr;
+    const void* u_prev = nullptr;
+    const void* B_prev = nullptr;
 };
 
 struct GradParams {

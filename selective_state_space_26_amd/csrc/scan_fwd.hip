@@ -22,12 +22,20 @@
 // across tiles (page 4, Appendix D: split the sequence into chunks, continue the scan from the
 // intermediate state).  Lanes at multiples of the chunk length also write the state entering
 // them to chunk_states.
+//
+// TRAP: the exponential-trapezoidal rule of Mamba-3 (page 5, first bullet: the input integral
+// over a step taken from both ends of the interval, mixed by a data-dependent weight lambda):
+//   b_k = a_k * ((1 - lambda_k) Delta_k u_{k-1}) * B_{n,k-1} + (lambda_k Delta_k u_k) * B_{n,k}
+// The step-(k-1) factors come from the lane's own registers, from lane l-1 for its first step
+// (a DPP shift), and from the previous tile's last step (u wave-uniform, B of state n in lane
+// n of one VGPR) or u_prev / B_prev for the first tile.  The transition a_k, the lane
+// transition P and everything after pass 1 are unchanged.
 #include "msel_device.hpp"
 #include "msel_kernels.hpp"
 
 namespace msel {
 
-template <typename T, int K, bool VEC, bool HAS_Z, bool SOFTPLUS>
+template <typename T, int K, bool VEC, bool HAS_Z, bool SOFTPLUS, bool TRAP>
 __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -51,26 +59,44 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
 
     float carry = 0.0f;  // lane n: state h_n entering the current tile
     if (p.h0 != nullptr && lane < N) carry = p.h0[static_cast<size_t>(ch) * N + lane];
+    // TRAP: the step before the tile: its u (wave-uniform) and B (lane n: state n)
+    float u_last = 0.0f, B_last = 0.0f;
+    if constexpr (TRAP) {
+        if (p.u_prev != nullptr) u_last = Elem<T>::load1(static_cast<const T*>(p.u_prev) + ch);
+        if (p.B_prev != nullptr && lane < N)
+            B_last = Elem<T>::load1(static_cast<const T*>(p.B_prev) + static_cast<size_t>(b) * N + lane);
+    }
 
     constexpr int TILE = 64 * K;
     static_assert(TILE % kChunk == 0, "a tile must hold whole chunks");
     for (int tile = 0; tile < L; tile += TILE) {
         const int t0 = tile + lane * K;
         float dt[K], du[K], y[K];
+        float cp[TRAP ? K : 1];  // TRAP: (1 - lambda_k) Delta_k u_{k-1}
         float sum_dt = 0.0f;
         {
             float uu[K], dd[K];
             load_k_cached<T, K, VEC>(u, t0, L, uu);
             load_k_cached<T, K, VEC>(dl, t0, L, dd);
+            float lm[TRAP ? K : 1];
+            if constexpr (TRAP)
+                load_k_cached<T, K, VEC>(static_cast<const T*>(p.lam) + row, t0, L, lm);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float x = dd[k] + bias;
                 const float v = SOFTPLUS ? softplus_f(x) : x;
                 dt[k] = (t0 + k < L) ? v : 0.0f;  // Delta = 0 past the end: identity step
-                du[k] = dt[k] * uu[k];
+                if constexpr (TRAP) {
+                    const float um1 = k == 0 ? shift_up(uu[K - 1], u_last) : uu[k - 1];
+                    du[k] = lm[k] * dt[k] * uu[k];
+                    cp[k] = (dt[k] - lm[k] * dt[k]) * um1;
+                } else {
+                    du[k] = dt[k] * uu[k];
+                }
                 y[k] = Dd * uu[k];
                 sum_dt += dt[k];
             }
+            if constexpr (TRAP) u_last = readlane(uu[K - 1], 63);
         }
         // States entering the lanes that start a chunk: gathered into lane-distributed
         // registers (lane n = state n), one per chunk of the tile, and stored after the state
@@ -84,11 +110,19 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
             const float An = readlane(Av, n);
             float a[K], bb[K], bc[K];
             load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, bc);
+            float bprev0 = 0.0f;  // TRAP: B_{n} of the step before the lane's first
+            if constexpr (TRAP) {
+                bprev0 = shift_up(bc[K - 1], readlane(B_last, n));
+                B_last = writelane(readlane(bc[K - 1], 63), n, B_last);
+            }
             float h = 0.0f;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 a[k] = exp2_hw(dt[k] * An);
-                bb[k] = du[k] * bc[k];
+                if constexpr (TRAP)
+                    bb[k] = fmaf(a[k], cp[k] * (k == 0 ? bprev0 : bc[k - 1]), du[k] * bc[k]);
+                else
+                    bb[k] = du[k] * bc[k];
                 h = fmaf(a[k], h, bb[k]);
             }
             float P = exp2_hw(An * sum_dt);
@@ -137,7 +171,9 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
 //   h_n = exp(Delta A_n) h0_n + Delta B_n u,  y = sum_n C_n h_n + D u,  out = y silu(z).
 // The sum over states is a 16-lane DPP reduction.  final_state may be h0 itself (the state is
 // updated in place): each lane reads its h0 before writing.
-template <typename T, bool HAS_Z, bool SOFTPLUS>
+// TRAP adds the previous step's input, carried over the step: the trapezoidal rule above with
+// u_{-1} = u_prev[b, d] and B_{-1} = B_prev[b, n].
+template <typename T, bool HAS_Z, bool SOFTPLUS, bool TRAP>
 __global__ __launch_bounds__(256) void scan_step_kernel(ScanParams p) {
     const int lane = lane_id();
     const int n = lane & 15;
@@ -158,7 +194,16 @@ __global__ __launch_bounds__(256) void scan_step_kernel(ScanParams p) {
     const float An = p.A[static_cast<size_t>(d) * N + nc] * kLog2e;
     const size_t sidx = static_cast<size_t>(chc) * N + nc;
     const float h0 = p.h0 ? p.h0[sidx] : 0.0f;
-    const float h = fmaf(exp2_hw(dt * An), h0, dt * Bv * u);
+    const float a = exp2_hw(dt * An);
+    float h;
+    if constexpr (TRAP) {
+        const float lm = Elem<T>::load1(static_cast<const T*>(p.lam) + chc);
+        const float up = p.u_prev ? Elem<T>::load1(static_cast<const T*>(p.u_prev) + chc) : 0.0f;
+        const float bp = p.B_prev ? Elem<T>::load1(static_cast<const T*>(p.B_prev) + bn) : 0.0f;
+        h = fmaf(a, fmaf((dt - lm * dt) * up, bp, h0), lm * dt * u * Bv);
+    } else {
+        h = fmaf(a, h0, dt * Bv * u);
+    }
     float part = st ? Cv * h : 0.0f;
     // sum over the row's 16 lanes: inclusive DPP prefix, lane 15 of the row holds the total
     asm volatile("s_nop 1\n"
@@ -192,7 +237,10 @@ template <typename T, int K, bool VEC, bool HAS_Z, bool SP>
 hipError_t fwd_go(const ScanParams& p, hipStream_t s) {
     const int ch = p.B * p.D;
     dim3 grid((ch + kFwdWaves - 1) / kFwdWaves), block(64 * kFwdWaves);
-    hipLaunchKernelGGL((scan_fwd_kernel<T, K, VEC, HAS_Z, SP>), grid, block, 0, s, p);
+    if (p.lam != nullptr)
+        hipLaunchKernelGGL((scan_fwd_kernel<T, K, VEC, HAS_Z, SP, true>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((scan_fwd_kernel<T, K, VEC, HAS_Z, SP, false>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 
@@ -221,11 +269,19 @@ template <typename T>
 hipError_t step_dispatch(const ScanParams& p, hipStream_t s) {
     const long long threads = static_cast<long long>(p.B) * p.D * 16;
     dim3 grid(static_cast<unsigned>((threads + 255) / 256)), block(256);
-    const bool hz = p.z != nullptr, sp = p.softplus != 0;
-    if (hz && sp) hipLaunchKernelGGL((scan_step_kernel<T, true, true>), grid, block, 0, s, p);
-    if (hz && !sp) hipLaunchKernelGGL((scan_step_kernel<T, true, false>), grid, block, 0, s, p);
-    if (!hz && sp) hipLaunchKernelGGL((scan_step_kernel<T, false, true>), grid, block, 0, s, p);
-    if (!hz && !sp) hipLaunchKernelGGL((scan_step_kernel<T, false, false>), grid, block, 0, s, p);
+    const bool hz = p.z != nullptr, sp = p.softplus != 0, tr = p.lam != nullptr;
+#define MSEL_STEP(Z, S, R) \
+    if (hz == Z && sp == S && tr == R) \
+        hipLaunchKernelGGL((scan_step_kernel<T, Z, S, R>), grid, block, 0, s, p);
+    MSEL_STEP(true, true, false)
+    MSEL_STEP(true, false, false)
+    MSEL_STEP(false, true, false)
+    MSEL_STEP(false, false, false)
+    MSEL_STEP(true, true, true)
+    MSEL_STEP(true, false, true)
+    MSEL_STEP(false, true, true)
+    MSEL_STEP(false, false, true)
+#undef MSEL_STEP
     return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@ def source_digest(files=BWD_SOURCES) -> str:
 
 
 def short_name(name: str) -> str:
-    n = name
+    n = name.replace("(anonymous namespace)::", "")
     if n.startswith("void "):
         n = n[5:]
     return n.split("(")[0]

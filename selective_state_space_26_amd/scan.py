@@ -107,6 +107,37 @@ def msel_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_soft
     return out, final_state, chunk_states
 
 
+def msel_scan_trap_fwd(u, delta, lam, A, B, C, D=None, z=None, delta_bias=None,
+                       delta_softplus=True, h0=None, u_prev=None, B_prev=None,
+                       return_final_state=True, return_chunk_states=False, out=None,
+                       final_state=None, chunk_states=None):
+    """Fused forward scan with the exponential-trapezoidal rule (lam: [batch, dim, seqlen] in
+    [0, 1]; u_prev [batch, dim] and B_prev [batch, dstate]: the inputs of the step before the
+    first).  Returns (out, final_state or None, chunk_states or None)."""
+    a, (bsz, dim, N, L) = _args(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
+    dev, dt = u.device, u.dtype
+    _need(lam, "lam", (bsz, dim, L), dt, dev)
+    _need(u_prev, "u_prev", (bsz, dim), dt, dev)
+    _need(B_prev, "B_prev", (bsz, N), dt, dev)
+    if lam is None:
+        raise ValueError("lam is required")
+    out = torch.empty_like(u) if out is None else _need(out, "out", (bsz, dim, L), dt, dev)
+    if return_final_state and final_state is None:
+        final_state = torch.empty((bsz, dim, N), device=dev, dtype=torch.float32)
+    if return_chunk_states and chunk_states is None:
+        chunk_states = torch.empty((bsz, dim, num_chunks(L), N), device=dev,
+                                   dtype=torch.float32)
+    _need(final_state, "final_state", (bsz, dim, N), torch.float32, dev)
+    _need(chunk_states, "chunk_states", (bsz, dim, num_chunks(L), N), torch.float32, dev)
+    a.out, a.final_state, a.chunk_states = _ptr(out), _ptr(final_state), _ptr(chunk_states)
+    tr = _lib.TrapArgs()
+    tr.lambda_, tr.u_prev, tr.B_prev = _ptr(lam), _ptr(u_prev), _ptr(B_prev)
+    _lib.check("msel_scan_trap_fwd", _lib.load().msel_scan_trap_fwd(ctypes.byref(a),
+                                                                    ctypes.byref(tr),
+                                                                    _stream(dev)))
+    return out, final_state, chunk_states
+
+
 def msel_scan_chunk_carry(u, delta, A, B, delta_bias=None, delta_softplus=True, h0=None,
                           return_final_state=True, chunk_states=None, final_state=None):
     """Chunk-carry pass.  Returns (chunk_states, final_state or None)."""

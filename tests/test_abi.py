@@ -42,10 +42,12 @@ def test_struct_layout_matches_header(tmp_path):
         "int main(void) {\n"
         'printf("args %zu\\ngrads %zu\\n", sizeof(msel_scan_args), sizeof(msel_scan_grads));\n'
         'printf("cargs %zu\\ncgrads %zu\\n", sizeof(msel_conv_args), sizeof(msel_conv_grads));\n'
+        'printf("targs %zu\\n", sizeof(msel_trap_args));\n'
         + "".join(f"F(msel_scan_args, {f})\n" for f, _ in _lib.ScanArgs._fields_)
         + "".join(f"F(msel_scan_grads, {f})\n" for f, _ in _lib.ScanGrads._fields_)
         + "".join(f"F(msel_conv_args, {f})\n" for f, _ in _lib.ConvArgs._fields_)
         + "".join(f"F(msel_conv_grads, {f})\n" for f, _ in _lib.ConvGrads._fields_)
+        + "".join(f"F(msel_trap_args, {f.rstrip('_')})\n" for f, _ in _lib.TrapArgs._fields_)
         + "return 0; }\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o",
@@ -64,6 +66,9 @@ def test_struct_layout_matches_header(tmp_path):
         assert int(got[f"msel_conv_args.{f}"]) == getattr(_lib.ConvArgs, f).offset, f
     for f, _ in _lib.ConvGrads._fields_:
         assert int(got[f"msel_conv_grads.{f}"]) == getattr(_lib.ConvGrads, f).offset, f
+    assert int(got["targs"]) == ctypes.sizeof(_lib.TrapArgs)
+    for f, _ in _lib.TrapArgs._fields_:
+        assert int(got[f"msel_trap_args.{f.rstrip('_')}"]) == getattr(_lib.TrapArgs, f).offset, f
 
 
 def test_constants(lib):
@@ -408,3 +413,49 @@ def test_conv_bwd_aliasing_is_rejected(lib, gfield, target):
         getattr(a, target)
     setattr(g, gfield, src)
     assert _cbwd(lib, a, g) == 7
+
+
+# ---- the exponential-trapezoidal variant ------------------------------------------------
+
+def _trap():
+    t = _lib.TrapArgs()
+    t.lambda_, t.u_prev, t.B_prev = _addr(), _addr(), _addr()
+    return t
+
+
+def test_trap_validation(lib):
+    a, t = _good_args(), _trap()
+    v = lambda: lib.msel_validate_trap_fwd(ctypes.byref(a), ctypes.byref(t))
+    assert v() == 0
+    t.u_prev = t.B_prev = None
+    assert v() == 0
+    assert lib.msel_validate_trap_fwd(ctypes.byref(a), None) == 1
+    assert lib.msel_scan_trap_fwd(ctypes.byref(a), None, None) == 1
+    t.lambda_ = None
+    assert v() == 1
+    assert lib.msel_scan_trap_fwd(ctypes.byref(a), ctypes.byref(t), None) == 1
+    t.lambda_ = _addr() + 8
+    assert v() == 4
+    t = _trap()
+    t.u_prev += 2              # fp32 inputs need 4-byte alignment
+    assert v() == 4
+    a.dtype = 1                # bf16: 2 bytes
+    assert v() == 0
+    t.B_prev += 1
+    assert v() == 4
+    # the checks of the plain forward apply too
+    a, t = _good_args(), _trap()
+    a.dstate = 17
+    assert v() == 5
+    a, t = _good_args(), _trap()
+    a.out = a.u
+    assert v() == 7
+
+
+@pytest.mark.parametrize("out_field,in_field", [("out", "lambda_"), ("final_state", "u_prev"),
+                                                ("out", "B_prev")])
+def test_trap_outputs_must_not_alias_its_inputs(lib, out_field, in_field):
+    a, t = _good_args(), _trap()
+    a.chunk_states = _addr()
+    setattr(a, out_field, getattr(t, in_field))
+    assert lib.msel_validate_trap_fwd(ctypes.byref(a), ctypes.byref(t)) == 7

@@ -1,0 +1,174 @@
+"""GPU parity of the exponential-trapezoidal forward (msel_scan_trap_fwd) against its fp64
+oracle (oracle/trap.py).
+
+Shapes span several tiles and chunks with ragged tails, both dtypes, the vector and scalar
+load paths, with and without the gate, softplus, D, bias, h0 and the previous step's inputs,
+and seqlen 1 (the decode step).  The bar is the one of the other forward tests:
+max|gpu - oracle| <= tol * max|oracle| per output (1e-4 fp32, 1e-2 bf16 inputs).  Properties:
+lambda = 1 reproduces msel_scan_fwd bit for bit (the trapezoidal terms vanish exactly), decode
+steps chained through u_prev / B_prev and an in-place state equal the oracle's whole sequence,
+and two calls continued through h0, u_prev and B_prev equal one.
+"""
+import numpy as np
+import pytest
+
+import msel_inputs
+from helpers import assert_close, host, log, to_device
+from oracle import trap as otrap
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import selective_state_space_26_amd as msel  # noqa: E402
+
+CASES = [
+    # batch, dim, dstate, seqlen, dtype, z, softplus, D/bias, h0, prev
+    (1, 4, 4, 64, "f32", True, True, True, False, False),
+    (2, 5, 16, 2500, "f32", True, True, True, True, True),    # 3 tiles, ragged tail
+    (2, 5, 16, 2500, "bf16", True, True, True, True, True),   # scalar path (2500 % 8)
+    (2, 3, 16, 4096, "bf16", False, True, True, False, True), # whole tiles
+    (3, 7, 5, 1000, "f32", False, False, False, True, False), # odd dstate, no softplus
+    (1, 1, 1, 777, "bf16", True, True, True, False, True),    # dstate 1, one channel
+    (2, 4, 16, 1000, "bf16", True, True, True, True, False),  # vector path, ragged tile
+    (2, 3, 16, 1, "f32", True, True, True, True, True),       # one step: the decode kernel
+    (1, 2, 8, 1, "bf16", False, True, True, True, True),      # one step, bf16
+]
+
+
+def _inputs(bsz, dim, N, L, dtype, with_z, sp, with_db, with_h0, prev, seed=321):
+    t = msel_inputs.make(bsz, dim, N, L, dtype, seed, with_z=with_z, with_D=with_db,
+                         with_bias=with_db, with_h0=with_h0, with_lam=True, with_prev=prev)
+    if not sp:
+        v = np.abs(t.values("delta")) * np.float32(0.2)
+        t["delta"] = msel_inputs.f32_to_bf16_bits(v) if dtype == "bf16" else v
+        if t.get("bias") is not None:
+            t["bias"] = (np.abs(t["bias"]) * np.float32(0.01)).astype(np.float32)
+    return t
+
+
+def _dev(t):
+    d = to_device(t)
+    act = torch.bfloat16 if t.dtype == "bf16" else torch.float32
+    for k in ("lam", "u_prev", "B_prev"):   # activation-dtype tensors to_device does not know
+        if t.get(k) is not None and d[k].dtype != act:
+            d[k] = d[k].to(act)
+    return d
+
+
+def _vals(t):
+    return {k: (None if t.get(k) is None else t.values(k)) for k in t}
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c[:5])) +
+                         ("_prev" if c[9] else ""))
+def test_trap_fwd_matches_oracle(case):
+    bsz, dim, N, L, dtype, with_z, sp, with_db, with_h0, prev = case
+    log(f"trap fwd {case}")
+    t = _inputs(*case)
+    d = _dev(t)
+    T = msel.chunk_len()
+    out, fin, cs = msel.msel_scan_trap_fwd(d["u"], d["delta"], d["lam"], d["A"], d["B"], d["C"],
+                                           d["D"], d["z"], d["bias"], sp, d["h0"],
+                                           d.get("u_prev"), d.get("B_prev"),
+                                           return_chunk_states=True)
+    torch.cuda.synchronize()
+    v = _vals(t)
+    ro, rf, rcs = otrap.fwd(v["u"], v["delta"], v["lam"], v["A"], v["B"], v["C"], v["D"],
+                            v["z"], v["bias"], v["h0"], v.get("u_prev"), v.get("B_prev"),
+                            softplus=sp, chunk_len=T)
+    assert_close("out", host(out), ro, dtype)
+    assert_close("final_state", host(fin), rf, dtype)
+    assert_close("chunk_states", host(cs), rcs, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lambda_one_is_msel_scan_fwd_bitwise(dtype):
+    log(f"trap lambda=1 bitwise {dtype}")
+    t = _inputs(2, 5, 16, 2500, dtype, True, True, True, True, True)
+    d = _dev(t)
+    ones = torch.ones_like(d["lam"])
+    a = msel.msel_scan_trap_fwd(d["u"], d["delta"], ones, d["A"], d["B"], d["C"], d["D"], d["z"],
+                                d["bias"], True, d["h0"], d["u_prev"], d["B_prev"],
+                                return_chunk_states=True)
+    b = msel.msel_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                           d["bias"], True, d["h0"], return_chunk_states=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_trap_decode_steps_in_place(dtype):
+    """Steps of length 1, each taking the previous step's u and B as u_prev / B_prev and
+    updating the state in place, follow the oracle's whole-sequence recurrence."""
+    bsz, dim, N, L = 2, 6, 16, 24
+    log(f"trap decode in place {dtype}")
+    t = _inputs(bsz, dim, N, L, dtype, True, True, True, True, True)
+    d = _dev(t)
+    state = d["h0"].clone()
+    outs = []
+    up, bp = d["u_prev"], d["B_prev"]
+    for s in range(L):
+        sl = lambda k: d[k][:, :, s:s + 1].contiguous()
+        o, fin, _ = msel.msel_scan_trap_fwd(sl("u"), sl("delta"), sl("lam"), d["A"], sl("B"),
+                                            sl("C"), d["D"], sl("z"), d["bias"], True, state,
+                                            up, bp, final_state=state)
+        assert fin is state
+        outs.append(o)
+        up, bp = sl("u")[:, :, 0].contiguous(), sl("B")[:, :, 0].contiguous()
+    torch.cuda.synchronize()
+    v = _vals(t)
+    ro, rf, _ = otrap.fwd(v["u"], v["delta"], v["lam"], v["A"], v["B"], v["C"], v["D"], v["z"],
+                          v["bias"], v["h0"], v["u_prev"], v["B_prev"])
+    assert_close("out", host(torch.cat(outs, dim=2)), ro, dtype)
+    assert_close("state", host(state), rf, dtype)
+
+
+def test_trap_continuation_across_calls():
+    bsz, dim, N, L, cut = 2, 5, 16, 3000, 1300
+    log("trap continuation 3000 = 1300 + 1700")
+    t = _inputs(bsz, dim, N, L, "f32", True, True, True, True, True)
+    d = _dev(t)
+    sl = lambda k, a, b: d[k][:, :, a:b].contiguous()
+    o1, f1, _ = msel.msel_scan_trap_fwd(sl("u", 0, cut), sl("delta", 0, cut), sl("lam", 0, cut),
+                                        d["A"], sl("B", 0, cut), sl("C", 0, cut), d["D"],
+                                        sl("z", 0, cut), d["bias"], True, d["h0"], d["u_prev"],
+                                        d["B_prev"])
+    o2, f2, _ = msel.msel_scan_trap_fwd(sl("u", cut, L), sl("delta", cut, L), sl("lam", cut, L),
+                                        d["A"], sl("B", cut, L), sl("C", cut, L), d["D"],
+                                        sl("z", cut, L), d["bias"], True, f1,
+                                        d["u"][:, :, cut - 1].contiguous(),
+                                        d["B"][:, :, cut - 1].contiguous())
+    torch.cuda.synchronize()
+    v = _vals(t)
+    ro, rf, _ = otrap.fwd(v["u"], v["delta"], v["lam"], v["A"], v["B"], v["C"], v["D"], v["z"],
+                          v["bias"], v["h0"], v["u_prev"], v["B_prev"])
+    assert_close("out", host(torch.cat([o1, o2], dim=2)), ro, "f32")
+    assert_close("final_state", host(f2), rf, "f32")
+
+
+def test_trap_full_size_sampled_channels():
+    """Batch 8, 1536 channels, dstate 16, seqlen 2048, bf16 -- the shape the benchmark times --
+    with 10 channels of two batch rows checked against the oracle."""
+    w = msel_inputs.WORKLOADS[2]
+    log("trap full size workload-2 shape")
+    t = msel_inputs.make(w.batch, w.dim, w.dstate, w.seqlen, w.dtype, w.seed, with_lam=True)
+    d = _dev(t)
+    out, fin, cs = msel.msel_scan_trap_fwd(d["u"], d["delta"], d["lam"], d["A"], d["B"], d["C"],
+                                           d["D"], d["z"], d["bias"], True,
+                                           return_chunk_states=True)
+    torch.cuda.synchronize()
+    v = _vals(t)
+    ds = np.array([0, 1, 511, 512, 767, 1023, 1024, 1300, 1534, 1535])
+    di = torch.as_tensor(ds, device=out.device)
+    for b in (0, 7):
+        sub = lambda k: v[k][b:b + 1][:, ds]
+        ro, rf, rcs = otrap.fwd(sub("u"), sub("delta"), sub("lam"), v["A"][ds],
+                                v["B"][b:b + 1], v["C"][b:b + 1], v["D"][ds], sub("z"),
+                                v["bias"][ds], chunk_len=msel.chunk_len())
+        assert_close("out", host(out[b:b + 1].index_select(1, di)), ro, "bf16")
+        assert_close("final_state", host(fin[b:b + 1].index_select(1, di)), rf, "bf16")
+        assert_close("chunk_states", host(cs[b:b + 1].index_select(1, di)), rcs, "bf16")
