@@ -13,6 +13,9 @@ The trapezoidal variant adds (``make(..., with_lam=True)``) the mixing weight la
 of shape [batch, dim, seqlen], and for continued sequences (``with_prev=True``) the inputs of
 the step before the first, u_prev ~ N(0,1) [batch, dim] and B_prev ~ N(0,1) [batch, dstate].
 
+The complex variant (``complex_A=True``, even dstate) takes A[d, 2j] + i A[d, 2j+1] =
+-1/2 + i pi j (S4D-Lin) for state pair j.
+
 The short convolution before the scan (``make_conv``): x ~ N(0,1) of shape [batch, dim,
 seqlen]; taps w[d, k] and bias b[d] ~ U(-1/sqrt(W), 1/sqrt(W)) (the default initialisation of a
 depthwise 1-d convolution, whose fan-in is the width W); the incoming state (the W-1 inputs
@@ -113,7 +116,7 @@ def _normal(seed, name, shape, scale=1.0):
 def make(batch: int, dim: int, dstate: int, seqlen: int, dtype: str = "f32", seed: int = 0,
          with_z: bool = True, with_D: bool = True, with_bias: bool = True,
          with_dout: bool = False, with_h0: bool = False, with_lam: bool = False,
-         with_prev: bool = False) -> Tensors:
+         with_prev: bool = False, complex_A: bool = False) -> Tensors:
     """Draw one problem.  Activation-shaped tensors follow ``dtype``; A, D, bias, h0 are fp32."""
     if dtype not in ("f32", "bf16"):
         raise ValueError(dtype)
@@ -128,8 +131,16 @@ def make(batch: int, dim: int, dstate: int, seqlen: int, dtype: str = "f32", see
     t["z"] = act("z", (batch, dim, seqlen)) if with_z else None
     t["B"] = act("B", (batch, dstate, seqlen))
     t["C"] = act("C", (batch, dstate, seqlen))
-    t["A"] = np.ascontiguousarray(
-        np.broadcast_to(-(np.arange(dstate, dtype=np.float32) + 1.0), (dim, dstate)))
+    if complex_A:
+        # the complex variant: rates -1/2 + i pi j of state pair j (S4D-Lin), interleaved
+        # (real, imaginary) along dstate
+        row = np.zeros(dstate, dtype=np.float32)
+        row[0::2] = -0.5
+        row[1::2] = np.pi * np.arange(dstate // 2, dtype=np.float32)
+        t["A"] = np.ascontiguousarray(np.broadcast_to(row, (dim, dstate)))
+    else:
+        t["A"] = np.ascontiguousarray(
+            np.broadcast_to(-(np.arange(dstate, dtype=np.float32) + 1.0), (dim, dstate)))
     t["D"] = _normal(seed, "D", (dim,)) if with_D else None
     if with_bias:
         dt0 = rng(seed, "bias").uniform(1e-3, 1e-1, size=dim)

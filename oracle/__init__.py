@@ -11,6 +11,8 @@ The implementations here:
   (sequential over time, one (batch, channel) recurrence per work unit, double precision).
 * ``trap.py`` is the exponential-trapezoidal variant of the scan (Mamba-3), a numpy loop over
   time in float64 that shares nothing with the C loop.
+* ``cplx.py`` is the complex-valued (rotational) variant: state pairs as complex numbers,
+  numpy complex128.
 * ``conv.py`` is the short causal convolution and activation that feed the scan (forward,
   hand-derived backward, convolutional state), written out tap by tap in float64.
 * ``twin_fwd`` in ``twin.py`` is a numpy restatement, vectorized over (batch, channel, state)
