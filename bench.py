@@ -36,6 +36,9 @@ FLOPS_FWD = 7      # Delta*A, exp2, (Delta u)*B, h = a h + p, y += C h
 FLOPS_BWD = 20     # recompute h (5), adjoint (3), g = lam h a (2), dA, dDelta, du, dB, dC (10)
 FLOPS_BWD_Z = 2    # y += C h, rebuilt for dz when there is a gate
 FLOPS_TRAP = 10    # Delta*A, exp2, c*B_prev, (gamma u)*B, p = a*(c B_prev) + .., h, y
+# per complex state (a pair of real states) and step: Delta*A_re, Delta*A_im, exp2, sin, cos,
+# the two products of the transition, (Delta u)*B for both parts, h = a h + p (4 fma), y (2 fma)
+FLOPS_COMPLEX_PAIR = 21
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, per kernel, of the default workload
 TRAFFIC_FILE = "profiles/{kernel}_d768x2_bf16_traffic.txt"
 CONV_WIDTH = 4     # taps of the short causal convolution before the scan
@@ -231,6 +234,29 @@ def main():
     per["trap_fwd"] = tev[0].elapsed_time(tev[1]) / args.steps
     del tsets
 
+    # the complex-valued (rotational) forward at the same shape: dstate 16 = 8 complex states,
+    # rates -1/2 + i pi j; calls alternate between the two input copies above
+    cA = put(msel_inputs.make(1, w.dim, w.dstate, 1, "f32", w.seed, complex_A=True)["A"],
+             torch.float32)
+    csets = [{k: (d[k] if i == 0 else d[k].clone()) for k in ("u", "delta", "z")} |
+             {"out": torch.empty_like(d["u"])} for i in range(2)]
+
+    def complex_fwd(i):
+        c = csets[i % 2]
+        msel.msel_scan_complex_fwd(c["u"], c["delta"], cA, d["B"], d["C"], d["D"], c["z"],
+                                   d["bias"], True, out=c["out"], final_state=trap_fin,
+                                   chunk_states=trap_cs)
+    for i in range(4):
+        complex_fwd(i)
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    cev[0].record()
+    for i in range(args.steps):
+        complex_fwd(i)
+    cev[1].record()
+    torch.cuda.synchronize()
+    per["complex_fwd"] = cev[0].elapsed_time(cev[1]) / args.steps
+    del csets
+
     # the short causal convolution + SiLU that makes the scan's input, at the same batch,
     # channels, length and dtype, width 4, with bias and incoming state: forward, backward
     # (zero-fill + one kernel) and the decode step (seqlen 1, state updated in place)
@@ -275,10 +301,12 @@ def main():
     per["conv_decode_step"] = graph_time(conv_decode, dec_per_graph, dec_reps)
 
     fl_bwd = FLOPS_BWD + (FLOPS_BWD_Z if d.get("z") is not None else 0)
-    flops = {"fwd": FLOPS_FWD * upd, "bwd_main": fl_bwd * upd, "trap_fwd": FLOPS_TRAP * upd}
+    flops = {"fwd": FLOPS_FWD * upd, "bwd_main": fl_bwd * upd, "trap_fwd": FLOPS_TRAP * upd,
+             "complex_fwd": FLOPS_COMPLEX_PAIR * upd // 2}
     alg["trap_fwd"] = alg["fwd"] + tc * (2 if w.dtype == "bf16" else 4)  # + lambda
+    alg["complex_fwd"] = alg["fwd"]
     kernels = {}
-    for n in ("fwd", "chunk_carry", "bwd_main", "bwd", "trap_fwd"):
+    for n in ("fwd", "chunk_carry", "bwd_main", "bwd", "trap_fwd", "complex_fwd"):
         sec = per[n] * 1e-3
         gbs = alg[n] / sec / 1e9
         kernels[n] = {"ms": round(per[n], 4), "alg_bytes": alg[n], "GB/s": round(gbs, 1),
@@ -287,6 +315,9 @@ def main():
         if n in flops:
             kernels[n]["TFLOP/s"] = round(flops[n] / sec / 1e12, 2)
     kernels["fwd"]["what"] = "scan_fwd_kernel (one launch)"
+    kernels["complex_fwd"]["what"] = ("scan_cplx_fwd_kernel: the complex-valued (rotational) "
+                                      "forward, dstate 16 as 8 complex states, one launch, "
+                                      "timed apart from the step")
     kernels["trap_fwd"]["what"] = ("scan_fwd_kernel with the exponential-trapezoidal rule "
                                    "(msel_scan_trap_fwd, lambda as one more input), one launch, "
                                    "timed apart from the step")

@@ -213,6 +213,27 @@ msel_status msel_scan_trap_fwd(const msel_scan_args *args, const msel_trap_args 
                                hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * The complex-valued (rotational) variant of the scan (Mamba-3).
+ *
+ * A complex state recovers state tracking (parity) that the real one cannot do; it is written
+ * as a scaling and a rotation in a plane (page 5, the Mamba-3 post, second bullet).  States
+ * (2j, 2j+1) of a channel are the real and imaginary parts of one complex state, A[d, 2j] and
+ * A[d, 2j+1] the real and imaginary parts of its rate, rows 2j and 2j+1 of B and C its input
+ * and readout weights:
+ *
+ *   h_t = exp(Delta_t (A_re + i A_im)) h_{t-1} + Delta_t u_t (B_{2j} + i B_{2j+1})
+ *   y_t = sum_j ( C_{2j} Re h_t + C_{2j+1} Im h_t ) + D u_t,    out_t = y_t silu(z_t)
+ *
+ * The arguments, layouts and outputs are msel_scan_fwd's (h0, final_state and chunk_states
+ * hold (Re, Im) pairs); dstate must be even (else MSEL_ERR_SHAPE).  With every A[d, 2j+1] = 0
+ * this is msel_scan_fwd with A[d, 2j+1] = A[d, 2j].  seqlen == 1 is the decode step (state in
+ * place allowed).  The backward and chunk-carry pass of this variant are not part of the
+ * library.
+ * ---------------------------------------------------------------------------------------- */
+msel_status msel_validate_complex_fwd(const msel_scan_args *args);
+msel_status msel_scan_complex_fwd(const msel_scan_args *args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * The short causal convolution and activation that produce the scan's input.
  *
  * The selective SSM block runs an input projection, a short convolution, an activation, the

@@ -181,6 +181,13 @@ msel_status msel_validate_trap_fwd(const msel_scan_args* a, const msel_trap_args
     return MSEL_OK;
 }
 
+msel_status msel_validate_complex_fwd(const msel_scan_args* a) {
+    msel_status s = msel_validate_fwd(a);
+    if (s != MSEL_OK) return s;
+    if (a->dstate % 2 != 0) return MSEL_ERR_SHAPE;  // states come in (Re, Im) pairs
+    return MSEL_OK;
+}
+
 msel_status msel_validate_chunk_carry(const msel_scan_args* a) {
     msel_status s = check_common(a);
     if (s != MSEL_OK) return s;
@@ -300,6 +307,12 @@ msel_status msel_scan_trap_fwd(const msel_scan_args* a, const msel_trap_args* tr
     p.u_prev = tr->u_prev;
     p.B_prev = tr->B_prev;
     return hip_status(msel::launch_scan_fwd(p, a->dtype == MSEL_BF16, stream));
+}
+
+msel_status msel_scan_complex_fwd(const msel_scan_args* a, hipStream_t stream) {
+    msel_status s = msel_validate_complex_fwd(a);
+    if (s != MSEL_OK) return s;
+    return hip_status(msel::launch_scan_cplx_fwd(to_params(a), a->dtype == MSEL_BF16, stream));
 }
 
 msel_status msel_scan_chunk_carry(const msel_scan_args* a, hipStream_t stream) {

@@ -138,6 +138,29 @@ def msel_scan_trap_fwd(u, delta, lam, A, B, C, D=None, z=None, delta_bias=None,
     return out, final_state, chunk_states
 
 
+def msel_scan_complex_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                          delta_softplus=True, h0=None, return_final_state=True,
+                          return_chunk_states=False, out=None, final_state=None,
+                          chunk_states=None):
+    """Fused forward of the complex-valued (rotational) scan: states (2j, 2j+1) are the real
+    and imaginary parts of one complex state, A[:, 2j] + i A[:, 2j+1] its rate (dstate even).
+    Returns (out, final_state or None, chunk_states or None)."""
+    a, (bsz, dim, N, L) = _args(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
+    dev = u.device
+    out = torch.empty_like(u) if out is None else _need(out, "out", (bsz, dim, L), u.dtype, dev)
+    if return_final_state and final_state is None:
+        final_state = torch.empty((bsz, dim, N), device=dev, dtype=torch.float32)
+    if return_chunk_states and chunk_states is None:
+        chunk_states = torch.empty((bsz, dim, num_chunks(L), N), device=dev,
+                                   dtype=torch.float32)
+    _need(final_state, "final_state", (bsz, dim, N), torch.float32, dev)
+    _need(chunk_states, "chunk_states", (bsz, dim, num_chunks(L), N), torch.float32, dev)
+    a.out, a.final_state, a.chunk_states = _ptr(out), _ptr(final_state), _ptr(chunk_states)
+    _lib.check("msel_scan_complex_fwd",
+               _lib.load().msel_scan_complex_fwd(ctypes.byref(a), _stream(dev)))
+    return out, final_state, chunk_states
+
+
 def msel_scan_chunk_carry(u, delta, A, B, delta_bias=None, delta_softplus=True, h0=None,
                           return_final_state=True, chunk_states=None, final_state=None):
     """Chunk-carry pass.  Returns (chunk_states, final_state or None)."""

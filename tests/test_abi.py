@@ -459,3 +459,20 @@ def test_trap_outputs_must_not_alias_its_inputs(lib, out_field, in_field):
     a.chunk_states = _addr()
     setattr(a, out_field, getattr(t, in_field))
     assert lib.msel_validate_trap_fwd(ctypes.byref(a), ctypes.byref(t)) == 7
+
+
+# ---- the complex-valued (rotational) variant ---------------------------------------------
+
+def test_complex_validation(lib):
+    a = _good_args(N=16)
+    assert lib.msel_validate_complex_fwd(ctypes.byref(a)) == 0
+    for n in (1, 3, 15):
+        a.dstate = n
+        assert lib.msel_validate_complex_fwd(ctypes.byref(a)) == 2
+        assert lib.msel_scan_complex_fwd(ctypes.byref(a), None) == 2
+        assert lib.msel_validate_fwd(ctypes.byref(a)) == 0   # the real scan takes any dstate
+    a = _good_args(N=16)
+    a.out = a.B
+    assert lib.msel_validate_complex_fwd(ctypes.byref(a)) == 7
+    assert lib.msel_validate_complex_fwd(None) == 1
+    assert lib.msel_scan_complex_fwd(None, None) == 1

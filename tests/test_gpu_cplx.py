@@ -1,0 +1,158 @@
+"""GPU parity of the complex-valued (rotational) forward (msel_scan_complex_fwd) against its
+fp64 oracle (oracle/cplx.py).
+
+Shapes span several tiles and chunks with ragged tails, both dtypes, the vector and scalar
+load paths, with and without the gate, softplus, D, bias and h0, dstate 2 to 16 and seqlen 1
+(the decode kernel); the bar is max|gpu - oracle| <= tol * max|oracle| per output (1e-4 fp32,
+1e-2 bf16 inputs).  Properties: the parity task of the pages over 3000 steps (every lane and
+tile boundary carries a rotated state), decode steps chained with the state in place, and
+the A_im = 0 case against the real scan's entry point.
+"""
+import numpy as np
+import pytest
+
+import msel_inputs
+from helpers import assert_close, host, log, to_device
+from oracle import cplx as ocplx
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import selective_state_space_26_amd as msel  # noqa: E402
+
+CASES = [
+    # batch, dim, dstate, seqlen, dtype, z, softplus, D/bias, h0
+    (1, 4, 4, 64, "f32", True, True, True, False),
+    (2, 5, 16, 2500, "f32", True, True, True, True),     # 5 tiles of 512, ragged
+    (2, 5, 16, 2500, "bf16", True, True, True, True),    # scalar path (2500 % 8)
+    (2, 3, 16, 4096, "bf16", False, True, True, False),  # whole tiles
+    (3, 7, 6, 1000, "f32", False, False, False, True),   # 3 pairs, no softplus
+    (1, 1, 2, 777, "bf16", True, True, True, True),      # one pair, one channel
+    (2, 4, 16, 1000, "bf16", True, True, True, True),    # vector path, ragged tile
+    (2, 3, 16, 1, "f32", True, True, True, True),        # decode kernel
+    (1, 2, 8, 1, "bf16", False, True, True, True),       # decode kernel, bf16
+]
+
+
+def _inputs(bsz, dim, N, L, dtype, with_z, sp, with_db, with_h0, seed=77):
+    t = msel_inputs.make(bsz, dim, N, L, dtype, seed, with_z=with_z, with_D=with_db,
+                         with_bias=with_db, with_h0=with_h0, complex_A=True)
+    if not sp:
+        v = np.abs(t.values("delta")) * np.float32(0.2)
+        t["delta"] = msel_inputs.f32_to_bf16_bits(v) if dtype == "bf16" else v
+        if t.get("bias") is not None:
+            t["bias"] = (np.abs(t["bias"]) * np.float32(0.01)).astype(np.float32)
+    return t
+
+
+def _vals(t):
+    return {k: (None if t.get(k) is None else t.values(k)) for k in t}
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c[:5])))
+def test_complex_fwd_matches_oracle(case):
+    bsz, dim, N, L, dtype, with_z, sp, with_db, with_h0 = case
+    log(f"complex fwd {case}")
+    t = _inputs(*case)
+    d = to_device(t)
+    out, fin, cs = msel.msel_scan_complex_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"],
+                                              d["D"], d["z"], d["bias"], sp, d["h0"],
+                                              return_chunk_states=True)
+    torch.cuda.synchronize()
+    v = _vals(t)
+    ro, rf, rcs = ocplx.fwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"],
+                            v["bias"], v["h0"], softplus=sp, chunk_len=msel.chunk_len())
+    assert_close("out", host(out), ro, dtype)
+    assert_close("final_state", host(fin), rf, dtype)
+    assert_close("chunk_states", host(cs), rcs, dtype)
+
+
+def test_parity_task_over_many_tiles():
+    """Delta_t = bit_t, rate 0 + i pi, no input, h0 = (1, 0), C = (1, 0): y_t is the parity
+    sign (-1)^(ones up to t) -- the state tracking that page 5 credits to the complex state."""
+    L = 3000
+    log("complex parity task, 3000 steps")
+    rng = np.random.default_rng(2024)
+    bits = rng.integers(0, 2, size=(3, 1, L)).astype(np.float32)
+    dev = torch.device("cuda")
+    delta = torch.from_numpy(bits).to(dev)
+    A = torch.tensor([[0.0, np.pi]], dtype=torch.float32, device=dev)
+    Bm = torch.zeros(3, 2, L, device=dev)
+    Cm = torch.zeros(3, 2, L, device=dev)
+    Cm[:, 0, :] = 1.0
+    h0 = torch.zeros(3, 1, 2, device=dev)
+    h0[..., 0] = 1.0
+    out, fin, _ = msel.msel_scan_complex_fwd(torch.zeros_like(delta), delta, A, Bm, Cm,
+                                             delta_softplus=False, h0=h0)
+    torch.cuda.synchronize()
+    want = (-1.0) ** np.cumsum(bits, axis=2)
+    got = host(out)
+    assert np.array_equal(np.sign(got), want)
+    assert np.max(np.abs(got - want)) < 1e-3
+
+
+def test_without_rotation_equals_the_real_scan():
+    log("complex with A_im = 0 vs msel_scan_fwd")
+    t = _inputs(2, 5, 16, 2500, "f32", True, True, True, True)
+    d = to_device(t)
+    A = d["A"].clone()
+    A[:, 1::2] = 0.0
+    Ar = A.clone()
+    Ar[:, 1::2] = A[:, 0::2]
+    a = msel.msel_scan_complex_fwd(d["u"], d["delta"], A, d["B"], d["C"], d["D"], d["z"],
+                                   d["bias"], True, d["h0"], return_chunk_states=True)
+    b = msel.msel_scan_fwd(d["u"], d["delta"], Ar, d["B"], d["C"], d["D"], d["z"], d["bias"],
+                           True, d["h0"], return_chunk_states=True)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("out", "final_state", "chunk_states"), a, b):
+        assert_close(name, host(x), host(y), "f32")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_complex_decode_steps_in_place(dtype):
+    bsz, dim, N, L = 2, 6, 16, 20
+    log(f"complex decode in place {dtype}")
+    t = _inputs(bsz, dim, N, L, dtype, True, True, True, True)
+    d = to_device(t)
+    state = d["h0"].clone()
+    outs = []
+    for s in range(L):
+        sl = lambda k: d[k][:, :, s:s + 1].contiguous()
+        o, fin, _ = msel.msel_scan_complex_fwd(sl("u"), sl("delta"), d["A"], sl("B"), sl("C"),
+                                               d["D"], sl("z"), d["bias"], True, state,
+                                               final_state=state)
+        assert fin is state
+        outs.append(o)
+    torch.cuda.synchronize()
+    v = _vals(t)
+    ro, rf, _ = ocplx.fwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"], v["bias"],
+                          v["h0"])
+    assert_close("out", host(torch.cat(outs, dim=2)), ro, dtype)
+    assert_close("state", host(state), rf, dtype)
+
+
+def test_complex_full_size_sampled_channels():
+    """Batch 8, 1536 channels, dstate 16 (8 complex states), seqlen 2048, bf16: 10 channels of
+    two batch rows against the oracle."""
+    w = msel_inputs.WORKLOADS[2]
+    log("complex full size workload-2 shape")
+    t = msel_inputs.make(w.batch, w.dim, w.dstate, w.seqlen, w.dtype, w.seed, complex_A=True)
+    d = to_device(t)
+    out, fin, cs = msel.msel_scan_complex_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"],
+                                              d["D"], d["z"], d["bias"], True,
+                                              return_chunk_states=True)
+    torch.cuda.synchronize()
+    v = _vals(t)
+    ds = np.array([0, 1, 511, 512, 767, 1023, 1024, 1300, 1534, 1535])
+    di = torch.as_tensor(ds, device=out.device)
+    for b in (0, 7):
+        sub = lambda k: v[k][b:b + 1][:, ds]
+        ro, rf, rcs = ocplx.fwd(sub("u"), sub("delta"), v["A"][ds], v["B"][b:b + 1],
+                                v["C"][b:b + 1], v["D"][ds], sub("z"), v["bias"][ds],
+                                chunk_len=msel.chunk_len())
+        assert_close("out", host(out[b:b + 1].index_select(1, di)), ro, "bf16")
+        assert_close("final_state", host(fin[b:b + 1].index_select(1, di)), rf, "bf16")
+        assert_close("chunk_states", host(cs[b:b + 1].index_select(1, di)), rcs, "bf16")
