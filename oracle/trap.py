@@ -25,7 +25,8 @@ Readings where the page is silent (each is listed in the design notes):
   step of a sequence being continued); without them it is 0.
 * h0, the gate, D, the bias and the chunk states are as in the other entry points.
 
-Everything is float64; the loop runs over time, vectorized over (b, d, n).
+Everything is float64; the loop runs over time, vectorized over (b, d, n).  ``bwd`` is reverse
+mode of that loop written by hand, one operation of a step at a time, run backwards in time.
 """
 from __future__ import annotations
 
@@ -72,3 +73,86 @@ def fwd(u, delta, lam, A, B, C, D=None, z=None, bias=None, h0=None, u_prev=None,
         zz = _f64(z)
         y *= zz / (1.0 + np.exp(-zz))
     return y, h, cs
+
+
+def bwd(u, delta, lam, A, B, C, dout, D=None, z=None, bias=None, h0=None, u_prev=None,
+        B_prev=None, softplus=True):
+    """Gradients of sum(dout * out) for fwd(...): reverse mode of the forward loop, one step at
+    a time in reverse, each operation of the step differentiated by hand.  Returns a dict with
+    du, ddelta (w.r.t. the raw delta), dlam, dz, dA, dB, dC, dD, ddelta_bias, dh0, du_prev and
+    dB_prev (the inputs of the step before the first)."""
+    u, delta, lam, A, B, C, dout = map(_f64, (u, delta, lam, A, B, C, dout))
+    bsz, dim, L = u.shape
+    N = A.shape[1]
+    x = delta + (0.0 if bias is None else _f64(bias)[None, :, None])
+    dt = _softplus(x) if softplus else x
+    up0 = np.zeros((bsz, dim)) if u_prev is None else _f64(u_prev)
+    Bp0 = np.zeros((bsz, N)) if B_prev is None else _f64(B_prev)
+    # forward again, keeping every state
+    hs = np.zeros((L + 1, bsz, dim, N))
+    hs[0] = 0.0 if h0 is None else _f64(h0)
+    ys = np.zeros((bsz, dim, L))
+    for t in range(L):
+        up = up0 if t == 0 else u[:, :, t - 1]
+        Bp = Bp0 if t == 0 else B[:, :, t - 1]
+        a = np.exp(dt[:, :, t, None] * A[None])
+        right = lam[:, :, t, None] * B[:, None, :, t] * u[:, :, t, None]
+        left = (1.0 - lam[:, :, t, None]) * a * Bp[:, None, :] * up[:, :, None]
+        hs[t + 1] = a * hs[t] + dt[:, :, t, None] * (right + left)
+        ys[:, :, t] = np.sum(C[:, None, :, t] * hs[t + 1], axis=2)
+    if D is not None:
+        ys += _f64(D)[None, :, None] * u
+    g = {k: np.zeros_like(v) for k, v in (("du", u), ("dlam", lam), ("dB", B), ("dC", C))}
+    ddt = np.zeros_like(dt)
+    dA = np.zeros_like(A)
+    dup0 = np.zeros_like(up0)
+    dBp0 = np.zeros_like(Bp0)
+    # the gate
+    if z is not None:
+        zz = _f64(z)
+        sg = 1.0 / (1.0 + np.exp(-zz))
+        dy = dout * zz * sg
+        dz = dout * ys * sg * (1.0 + zz * (1.0 - sg))
+    else:
+        dy, dz = dout, None
+    dD = np.sum(dy * u, axis=(0, 2))
+    if D is not None:
+        g["du"] += _f64(D)[None, :, None] * dy
+    gh = np.zeros((bsz, dim, N))  # dL/dh_t, accumulated from the future
+    for t in range(L - 1, -1, -1):
+        up = up0 if t == 0 else u[:, :, t - 1]
+        Bp = Bp0 if t == 0 else B[:, :, t - 1]
+        h_old, h_new = hs[t], hs[t + 1]
+        a = np.exp(dt[:, :, t, None] * A[None])
+        # y_t = C_t . h_new
+        gh = gh + C[:, None, :, t] * dy[:, :, t, None]
+        g["dC"][:, :, t] += np.sum(dy[:, :, t, None] * h_new, axis=1)
+        # h_new = a h_old + dt (right + left)
+        lt = lam[:, :, t, None]
+        dtt = dt[:, :, t, None]
+        right = lt * B[:, None, :, t] * u[:, :, t, None]
+        left = (1.0 - lt) * a * Bp[:, None, :] * up[:, :, None]
+        d_a = gh * h_old + gh * dtt * (1.0 - lt) * Bp[:, None, :] * up[:, :, None]
+        ddt[:, :, t] += np.sum(gh * (right + left), axis=2)
+        # right = lam B_t u_t ; left = (1 - lam) a B_{t-1} u_{t-1}
+        g["dlam"][:, :, t] += np.sum(gh * dtt * (B[:, None, :, t] * u[:, :, t, None]
+                                                 - a * Bp[:, None, :] * up[:, :, None]), axis=2)
+        g["dB"][:, :, t] += np.sum(gh * dtt * lt * u[:, :, t, None], axis=1)
+        g["du"][:, :, t] += np.sum(gh * dtt * lt * B[:, None, :, t], axis=2)
+        dBp = np.sum(gh * dtt * (1.0 - lt) * a * up[:, :, None], axis=1)
+        dup = np.sum(gh * dtt * (1.0 - lt) * a * Bp[:, None, :], axis=2)
+        if t == 0:
+            dBp0 += dBp
+            dup0 += dup
+        else:
+            g["dB"][:, :, t - 1] += dBp
+            g["du"][:, :, t - 1] += dup
+        # a = exp(dt A)
+        ddt[:, :, t] += np.sum(d_a * A[None] * a, axis=2)
+        dA += np.sum(d_a * dtt * a, axis=0)
+        gh = gh * a
+    sig = 1.0 / (1.0 + np.exp(-x)) if softplus else np.ones_like(x)
+    ddelta = ddt * sig
+    return dict(du=g["du"], ddelta=ddelta, dlam=g["dlam"], dz=dz, dA=dA, dB=g["dB"],
+                dC=g["dC"], dD=dD, ddelta_bias=ddelta.sum(axis=(0, 2)), dh0=gh, du_prev=dup0,
+                dB_prev=dBp0)

@@ -154,3 +154,63 @@ def test_linearity_and_causality():
     a, b = f(p["u"], p["u_prev"]), f(u2, p["u_prev"])
     np.testing.assert_array_equal(a[:, :, :25], b[:, :, :25])
     assert not np.allclose(a[:, :, 25:], b[:, :, 25:])
+
+
+_GRADS = [("u", "du"), ("delta", "ddelta"), ("lam", "dlam"), ("A", "dA"), ("B", "dB"),
+          ("C", "dC"), ("D", "dD"), ("z", "dz"), ("bias", "ddelta_bias"), ("h0", "dh0"),
+          ("u_prev", "du_prev"), ("B_prev", "dB_prev")]
+
+
+def _fwd_args(q, softplus=True):
+    return (q["u"], q["delta"], q["lam"], q["A"], q["B"], q["C"], q["D"], q["z"], q["bias"],
+            q["h0"], q["u_prev"], q["B_prev"])
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+def test_bwd_matches_finite_differences(softplus):
+    p = _problem(bsz=2, dim=2, N=3, L=7, with_h0=True, with_prev=True, with_dout=True)
+    if not softplus:
+        p["delta"] = np.abs(p["delta"]) * 0.2
+        p["bias"] = np.abs(p["bias"]) * 0.01
+    g = trap.bwd(*_fwd_args(p)[:6], p["dout"], *_fwd_args(p)[6:], softplus=softplus)
+
+    def loss(**over):
+        q = dict(p)
+        q.update(over)
+        out, _, _ = trap.fwd(*_fwd_args(q), softplus=softplus)
+        return float(np.sum(p["dout"] * out))
+
+    eps = 1e-6
+    for name, gname in _GRADS:
+        base = p[name]
+        num = np.zeros_like(base)
+        for idx in np.ndindex(*base.shape):
+            hi, lo = base.copy(), base.copy()
+            hi[idx] += eps
+            lo[idx] -= eps
+            num[idx] = (loss(**{name: hi}) - loss(**{name: lo})) / (2 * eps)
+        assert g[gname].shape == base.shape, name
+        assert _rel(g[gname], num) < 1e-6, name
+
+
+def test_bwd_matches_torch_autograd():
+    torch = pytest.importorskip("torch")
+    p = _problem(bsz=2, dim=3, N=4, L=23, with_h0=True, with_prev=True, with_dout=True)
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=k != "dout") for k, v in p.items()}
+    x = t["delta"] + t["bias"][None, :, None]
+    dt = torch.nn.functional.softplus(x)
+    h, up, Bp = t["h0"], t["u_prev"], t["B_prev"]
+    ys = []
+    for s in range(23):
+        a = torch.exp(dt[:, :, s, None] * t["A"][None])
+        right = t["lam"][:, :, s, None] * t["B"][:, None, :, s] * t["u"][:, :, s, None]
+        left = (1 - t["lam"][:, :, s, None]) * a * Bp[:, None, :] * up[:, :, None]
+        h = a * h + dt[:, :, s, None] * (right + left)
+        ys.append((t["C"][:, None, :, s] * h).sum(dim=2))
+        up, Bp = t["u"][:, :, s], t["B"][:, :, s]
+    y = torch.stack(ys, dim=2) + t["D"][None, :, None] * t["u"]
+    out = y * torch.nn.functional.silu(t["z"])
+    (out * t["dout"]).sum().backward()
+    g = trap.bwd(*_fwd_args(p)[:6], p["dout"], *_fwd_args(p)[6:])
+    for name, gname in _GRADS:
+        assert _rel(g[gname], t[name].grad.numpy()) < 1e-12, name
