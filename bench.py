@@ -36,6 +36,7 @@ FLOPS_FWD = 7      # Delta*A, exp2, (Delta u)*B, h = a h + p, y += C h
 FLOPS_BWD = 20     # recompute h (5), adjoint (3), g = lam h a (2), dA, dDelta, du, dB, dC (10)
 FLOPS_BWD_Z = 2    # y += C h, rebuilt for dz when there is a gate
 FLOPS_TRAP = 10    # Delta*A, exp2, c*B_prev, (gamma u)*B, p = a*(c B_prev) + .., h, y
+FLOPS_TRAP_BWD = 31  # the backward's 20 + the previous/next-step input terms of the rule
 # per complex state (a pair of real states) and step: Delta*A_re, Delta*A_im, exp2, sin, cos,
 # the two products of the transition, (Delta u)*B for both parts, h = a h + p (4 fma), y (2 fma)
 FLOPS_COMPLEX_PAIR = 21
@@ -232,7 +233,24 @@ def main():
     tev[1].record()
     torch.cuda.synchronize()
     per["trap_fwd"] = tev[0].elapsed_time(tev[1]) / args.steps
-    del tsets
+    # its backward, from the chunk states of copy 0 (the call streams ~550 MB: no rotation)
+    trap_fwd(0)
+    trap_ws = torch.empty(msel.bwd_workspace_bytes(d["u"], d["A"], True), device=dev,
+                          dtype=torch.uint8)
+
+    def trap_bwd():
+        c = tsets[0]
+        msel.msel_scan_trap_bwd(c["u"], c["delta"], c["lam"], d["A"], d["B"], d["C"], d["dout"],
+                                trap_cs, d["D"], c["z"], d["bias"], True, workspace=trap_ws)
+    for _ in range(3):
+        trap_bwd()
+    tev[0].record()
+    for _ in range(args.steps):
+        trap_bwd()
+    tev[1].record()
+    torch.cuda.synchronize()
+    per["trap_bwd"] = tev[0].elapsed_time(tev[1]) / args.steps
+    del tsets, trap_ws
 
     # the complex-valued (rotational) forward at the same shape: dstate 16 = 8 complex states,
     # rates -1/2 + i pi j; calls alternate between the two input copies above
@@ -305,8 +323,11 @@ def main():
              "complex_fwd": FLOPS_COMPLEX_PAIR * upd // 2}
     alg["trap_fwd"] = alg["fwd"] + tc * (2 if w.dtype == "bf16" else 4)  # + lambda
     alg["complex_fwd"] = alg["fwd"]
+    # + lambda in, dlambda out
+    alg["trap_bwd"] = alg["bwd"] + 2 * tc * (2 if w.dtype == "bf16" else 4)
+    flops["trap_bwd"] = (FLOPS_TRAP_BWD + (FLOPS_BWD_Z if d.get("z") is not None else 0)) * upd
     kernels = {}
-    for n in ("fwd", "chunk_carry", "bwd_main", "bwd", "trap_fwd", "complex_fwd"):
+    for n in ("fwd", "chunk_carry", "bwd_main", "bwd", "trap_fwd", "trap_bwd", "complex_fwd"):
         sec = per[n] * 1e-3
         gbs = alg[n] / sec / 1e9
         kernels[n] = {"ms": round(per[n], 4), "alg_bytes": alg[n], "GB/s": round(gbs, 1),
@@ -315,6 +336,8 @@ def main():
         if n in flops:
             kernels[n]["TFLOP/s"] = round(flops[n] / sec / 1e12, 2)
     kernels["fwd"]["what"] = "scan_fwd_kernel (one launch)"
+    kernels["trap_bwd"]["what"] = ("the msel_scan_trap_bwd call (zero-fills, summary, link and "
+                                   "the trapezoidal gradient kernel), timed apart from the step")
     kernels["complex_fwd"]["what"] = ("scan_cplx_fwd_kernel: the complex-valued (rotational) "
                                       "forward, dstate 16 as 8 complex states, one launch, "
                                       "timed apart from the step")

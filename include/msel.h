@@ -207,10 +207,26 @@ msel_status msel_validate_trap_fwd(const msel_scan_args *args, const msel_trap_a
 
 /* Fused forward scan with the exponential-trapezoidal rule: the same single pass, outputs
  * (out, final_state, chunk_states) and conventions as msel_scan_fwd, reading lambda as one
- * more input stream.  seqlen == 1 is the decode step (state in place allowed).  The backward
- * and the chunk-carry pass of this variant are not part of the library. */
+ * more input stream.  seqlen == 1 is the decode step (state in place allowed).  Its backward
+ * is msel_scan_trap_bwd; its chunk-carry pass is not part of the library. */
 msel_status msel_scan_trap_fwd(const msel_scan_args *args, const msel_trap_args *trap,
                                hipStream_t stream);
+
+/* Host-only checks of msel_scan_trap_bwd's arguments (those of msel_validate_bwd, the
+ * trapezoidal inputs', chunk_states present, dlambda). */
+msel_status msel_validate_trap_bwd(const msel_scan_args *args, const msel_trap_args *trap,
+                                   const msel_scan_grads *grads, const void *dlambda,
+                                   const void *workspace, size_t workspace_bytes);
+
+/* Backward of msel_scan_trap_fwd with recomputation (page 1; page 4 Appendix D, Memory),
+ * the same three launches as msel_scan_bwd and the same outputs, plus dlambda
+ * ([batch, dim, seqlen], activation dtype, required, 16-byte aligned): the gradient w.r.t.
+ * lambda.  args->chunk_states is required and must hold msel_scan_trap_fwd's chunk states
+ * for the same inputs; the workspace is msel_scan_bwd_workspace_bytes(args).  The gradients
+ * w.r.t. u_prev and B_prev are not computed.  Same determinism as msel_scan_bwd. */
+msel_status msel_scan_trap_bwd(const msel_scan_args *args, const msel_trap_args *trap,
+                               const msel_scan_grads *grads, void *dlambda, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * The complex-valued (rotational) variant of the scan (Mamba-3).

@@ -123,6 +123,40 @@ msel::ConvParams to_conv_params(const msel_conv_args* a) {
     return p;
 }
 
+// The backward's launches after validation: zero-fills, then summary, link and gradient
+// kernels (the trapezoidal variant when `tr` is given).
+msel_status run_bwd(const msel_scan_args* a, const msel_scan_grads* g, const msel_trap_args* tr,
+                    void* dlam, void* workspace, hipStream_t stream, hipEvent_t ev_begin,
+                    hipEvent_t ev_end) {
+    const bool bf16 = a->dtype == MSEL_BF16;
+    msel::ScanParams p = to_params(a);
+    if (tr != nullptr) {
+        p.lam = tr->lambda;
+        p.u_prev = tr->u_prev;
+        p.B_prev = tr->B_prev;
+    }
+    const size_t DN = static_cast<size_t>(a->dim) * a->dstate;
+    const size_t BNL = static_cast<size_t>(a->batch) * a->dstate * a->seqlen;
+    const msel::FillList fill = {{g->dA, g->dB, g->dC, g->dD, g->ddelta_bias},
+                                 {DN, BNL, BNL, static_cast<size_t>(a->dim),
+                                  static_cast<size_t>(a->dim)}};
+    if (msel::launch_fill_zero(fill, stream) != hipSuccess) return MSEL_ERR_HIP;
+    msel::GradParams gp;
+    gp.dout = g->dout;
+    gp.du = g->du;
+    gp.ddelta = g->ddelta;
+    gp.dz = g->dz;
+    gp.dA = g->dA;
+    gp.dB = g->dB;
+    gp.dC = g->dC;
+    gp.dD = g->dD;
+    gp.dbias = g->ddelta_bias;
+    gp.dh0 = g->dh0;
+    gp.dlam = dlam;
+    return hip_status(msel::launch_scan_bwd(p, gp, a->chunk_states, workspace, bf16, stream,
+                                            ev_begin, ev_end));
+}
+
 }  // namespace
 
 extern "C" {
@@ -292,6 +326,33 @@ msel_status msel_conv1d_bwd(const msel_conv_args* a, const msel_conv_grads* g,
     return hip_status(msel::launch_conv_bwd(p, a->dtype == MSEL_BF16, stream));
 }
 
+msel_status msel_validate_trap_bwd(const msel_scan_args* a, const msel_trap_args* tr,
+                                   const msel_scan_grads* g, const void* dlam,
+                                   const void* workspace, size_t workspace_bytes) {
+    msel_status s = msel_validate_bwd(a, g, workspace, workspace_bytes);
+    if (s != MSEL_OK) return s;
+    if (a->chunk_states == nullptr || tr == nullptr || tr->lambda == nullptr || dlam == nullptr)
+        return MSEL_ERR_NULL;
+    const size_t e = a->dtype == MSEL_BF16 ? 2 : 4;
+    if (!aligned(tr->lambda, 16) || !aligned(dlam, 16) ||
+        (tr->u_prev != nullptr && !aligned(tr->u_prev, e)) ||
+        (tr->B_prev != nullptr && !aligned(tr->B_prev, e)))
+        return MSEL_ERR_ALIGN;
+    const void* ins[] = {tr->lambda, tr->u_prev, tr->B_prev};
+    const void* outs[] = {g->du, g->ddelta, g->dz, g->dA, g->dB, g->dC, g->dD, g->ddelta_bias,
+                          g->dh0, workspace};
+    for (const void* o : outs)
+        for (const void* i : ins)
+            if (o != nullptr && o == i) return MSEL_ERR_ALIAS;
+    if (same_as_input(a, dlam) || dlam == g->dout || dlam == a->chunk_states || dlam == workspace)
+        return MSEL_ERR_ALIAS;
+    for (const void* i : ins)
+        if (i == dlam) return MSEL_ERR_ALIAS;
+    for (const void* o : outs)
+        if (o == dlam) return MSEL_ERR_ALIAS;
+    return MSEL_OK;
+}
+
 msel_status msel_scan_fwd(const msel_scan_args* a, hipStream_t stream) {
     msel_status s = msel_validate_fwd(a);
     if (s != MSEL_OK) return s;
@@ -326,27 +387,15 @@ msel_status msel_scan_bwd_profiled(const msel_scan_args* a, const msel_scan_grad
                                    hipEvent_t ev_begin, hipEvent_t ev_end) {
     msel_status s = msel_validate_bwd(a, g, workspace, workspace_bytes);
     if (s != MSEL_OK) return s;
-    const bool bf16 = a->dtype == MSEL_BF16;
-    msel::ScanParams p = to_params(a);
-    const size_t DN = static_cast<size_t>(a->dim) * a->dstate;
-    const size_t BNL = static_cast<size_t>(a->batch) * a->dstate * a->seqlen;
-    const msel::FillList fill = {{g->dA, g->dB, g->dC, g->dD, g->ddelta_bias},
-                                 {DN, BNL, BNL, static_cast<size_t>(a->dim),
-                                  static_cast<size_t>(a->dim)}};
-    if (msel::launch_fill_zero(fill, stream) != hipSuccess) return MSEL_ERR_HIP;
-    msel::GradParams gp;
-    gp.dout = g->dout;
-    gp.du = g->du;
-    gp.ddelta = g->ddelta;
-    gp.dz = g->dz;
-    gp.dA = g->dA;
-    gp.dB = g->dB;
-    gp.dC = g->dC;
-    gp.dD = g->dD;
-    gp.dbias = g->ddelta_bias;
-    gp.dh0 = g->dh0;
-    return hip_status(msel::launch_scan_bwd(p, gp, a->chunk_states, workspace, bf16, stream,
-                                            ev_begin, ev_end));
+    return run_bwd(a, g, nullptr, nullptr, workspace, stream, ev_begin, ev_end);
+}
+
+msel_status msel_scan_trap_bwd(const msel_scan_args* a, const msel_trap_args* tr,
+                               const msel_scan_grads* g, void* dlam, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    msel_status s = msel_validate_trap_bwd(a, tr, g, dlam, workspace, workspace_bytes);
+    if (s != MSEL_OK) return s;
+    return run_bwd(a, g, tr, dlam, workspace, stream, nullptr, nullptr);
 }
 
 msel_status msel_scan_bwd(const msel_scan_args* a, const msel_scan_grads* g, void* workspace,

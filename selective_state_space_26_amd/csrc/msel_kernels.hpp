@@ -44,6 +44,7 @@ struct GradParams {
     float* dD;
     float* dbias;
     float* dh0;
+    void* dlam = nullptr;  // exponential-trapezoidal variant: gradient w.r.t. lambda
 };
 
 // All launchers enqueue on `stream` and return the hipGetLastError() after the launch.

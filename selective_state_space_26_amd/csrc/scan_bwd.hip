@@ -43,6 +43,11 @@ namespace msel {
 constexpr int kMaxN = 16;
 constexpr int kSumWaves = 4;
 constexpr int kMainWaves = 12;  // 3 per SIMD: the main kernel needs ~160 VGPRs
+// The trapezoidal variant keeps ~50 more values per lane (the previous and next step's input
+// terms and two more state sums): 2 wavefronts per SIMD.
+constexpr int kTrapWaves = 8;
+template <bool TRAP>
+constexpr int main_waves() { return TRAP ? kTrapWaves : kMainWaves; }
 
 struct BwdWork {
     float* H;       // [B*D*nch*N]: chunk-start states (may be the caller's chunk_states)
@@ -232,6 +237,7 @@ __global__ __launch_bounds__(256) void bwd_link_kernel(ScanParams p, GradParams 
 //  * B and C of the workgroup's (batch row, chunk) as fp32, [2 tensors][n][2][64 lanes][4]:
 //    lane l's 8 steps are two 16-byte vectors, consecutive lanes adjacent (conflict-free);
 //  * per-wave dA partials [wave][n][16]: sums over groups of four lanes, per state;
+//  * kMaxN floats: B of every state at the step before the chunk (trapezoidal variant);
 //  * (static) one int per (group, state): 1 + the global step of the last completed update
 //    of that state's accumulator rows (see the ring protocol in the kernel).
 constexpr int kAccKP = 65;
@@ -242,7 +248,8 @@ __host__ __device__ constexpr int acc_groups(int N, int W) { return (W + N - 1) 
 
 __host__ __device__ constexpr size_t main_lds_bytes(int N, int W) {
     return (2 * static_cast<size_t>(acc_groups(N, W)) * N * (kChunk / 64) * kAccKP +
-            2 * static_cast<size_t>(N) * kChunk + static_cast<size_t>(W) * N * kDaQuads) *
+            2 * static_cast<size_t>(N) * kChunk + static_cast<size_t>(W) * N * kDaQuads +
+            kMaxN) *
            sizeof(float);
 }
 
@@ -253,15 +260,29 @@ __host__ __device__ constexpr size_t main_lds_bytes_max(int W) {
     for (int n = 1; n <= kMaxN; ++n) m = main_lds_bytes(n, W) > m ? main_lds_bytes(n, W) : m;
     return m;
 }
-static_assert(main_lds_bytes_max(kMainWaves) + kMaxRingFlags * sizeof(int) <= 160 * 1024,
+static_assert(main_lds_bytes_max(kMainWaves) + kMaxRingFlags * sizeof(int) <= 160 * 1024 &&
+                  main_lds_bytes_max(kTrapWaves) + kMaxRingFlags * sizeof(int) <= 160 * 1024,
               "main kernel LDS exceeds a compute unit's 160 KB");
 static_assert(kMainWaves + kMaxN - 1 <= kMaxRingFlags, "ring flags do not fit");
 
-template <typename T, bool VEC, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p, GradParams g,
-                                                                   BwdWork w, int per_wave) {
+// TRAP: the exponential-trapezoidal rule, h_t = a_t (h_{t-1} + c_t B_{t-1}) + gam_t u_t B_t
+// with gam_t = lam_t Delta_t and c_t = (1 - lam_t) Delta_t u_{t-1}.  The adjoint recurrence
+// is unchanged; with at_t = a_{t+1} lam_{t+1} (the adjoint arriving from step t+1) the new
+// terms are
+//   dB_t += lam_t gam_t u_t + at_t c_{t+1}          g_t = lam_t a_t (h_{t-1} + c_t B_{t-1})
+//   du_t  = gam_t sum_n lam B + (1 - lam_{t+1}) Delta_{t+1} sum_n at B + D dy_t
+//   dlam_t = Delta_t (u_t sum_n lam B - u_{t-1} sum_n lam a B_{t-1})
+//   dDelta_t = sum_n g_t A + lam_t u_t sum_n lam B + (1 - lam_t) u_{t-1} sum_n lam a B_{t-1}
+// Step t-1's u and B come from the lane's registers, lane l-1, and for the chunk's first step
+// from HBM (u) or the LDS row staged for it (B); step t+1's lam and Delta likewise from lane
+// l+1 or the next chunk's first step.  The chunk states must be the trapezoidal forward's.
+template <typename T, bool VEC, bool HAS_Z, bool SOFTPLUS, bool TRAP>
+__global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanParams p,
+                                                                          GradParams g,
+                                                                          BwdWork w,
+                                                                          int per_wave) {
     constexpr int K = kChunk / 64;
-    constexpr int W = kMainWaves;
+    constexpr int W = main_waves<TRAP>();
     constexpr int KP = kAccKP;
     // bf16 rows are small enough that the next channel's u and delta can be fetched during
     // the current channel's last step, next to this channel's z and dout (for dz)
@@ -282,6 +303,7 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
     float* accC = acc + groups * tile;
     float* BCs = acc + 2 * groups * tile;                   // B rows, then C rows
     float* dAs = BCs + 2 * N * kChunk + wave * N * kDaQuads;  // this wave's dA partials
+    float* Bm1 = BCs + 2 * N * kChunk + W * N * kDaQuads;     // TRAP: B at step c*T - 1
     __shared__ int ring_flags[kMaxRingFlags];
     for (int i = tid; i < 2 * groups * tile; i += 64 * W) acc[i] = 0.0f;
     for (int i = tid; i < groups * N; i += 64 * W) ring_flags[i] = 0;
@@ -301,6 +323,16 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
             const int o = ((nn * 2 + (tl % K) / 4) * 64 + tl / K) * 4 + tl % 4;
             BCs[o] = vb;
             BCs[N * kChunk + o] = vc;
+        }
+        if constexpr (TRAP) {
+            if (tid < N) {
+                float v = 0.0f;
+                if (c > 0)
+                    v = Elem<T>::load1(Bg + static_cast<size_t>(tid) * L + c * kChunk - 1);
+                else if (p.B_prev != nullptr)
+                    v = Elem<T>::load1(static_cast<const T*>(p.B_prev) + static_cast<size_t>(b) * N + tid);
+                Bm1[tid] = v;
+            }
         }
     }
     __syncthreads();
@@ -330,15 +362,18 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
     const T* __restrict__ gd = static_cast<const T*>(p.delta);
     const T* __restrict__ gg_ = static_cast<const T*>(g.dout);
     const T* __restrict__ gz = static_cast<const T*>(p.z);
+    const T* __restrict__ gl = static_cast<const T*>(p.lam);
     auto chan_row = [&](int d) { return (static_cast<size_t>(b) * p.D + d) * L; };
 
     // raw input rows of the channel about to start, fetched ahead of time
     Raw<T, K> ru, rd, rg, rz;
+    Raw<T, K> rl;  // TRAP: lambda (unused otherwise)
     const int d_first = blockIdx.x * per_wave * W + wave;
     if (d_first < p.D) {
         const size_t row = chan_row(d_first);
         load_raw<T, K, VEC>(gu + row, t0, L, ru);
         load_raw<T, K, VEC>(gd + row, t0, L, rd);
+        if constexpr (TRAP) load_raw<T, K, VEC>(gl + row, t0, L, rl);
         load_raw<T, K, VEC>(gg_ + row, t0, L, rg);
         if constexpr (HAS_Z) load_raw<T, K, VEC>(gz + row, t0, L, rz);
     }
@@ -364,11 +399,30 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
         float dt[K], dtu[K], dy[K], sB[K], sgA[K];
         float y[HAS_Z ? K : 1];
         float sum_dt = 0.0f, dD_part = 0.0f;
+        // TRAP: u, lambda, c_t, (1 - lam_{t+1}) Delta_{t+1}, c_{t+1}, u before the chunk, and
+        // the sums of at B and of lam a B_{t-1}
+        constexpr int KT = TRAP ? K : 1;
+        float uT[KT], lm[KT], cp[KT], cnu[KT], cn[KT], sA[KT], sP[KT];
+        float u_before = 0.0f;
+        float cnu_after = 0.0f;  // (1 - lam) Delta at the next chunk's first step
+        if constexpr (TRAP) {
+            if (c > 0)
+                u_before = Elem<T>::load1(gu + row + c * kChunk - 1);
+            else if (p.u_prev != nullptr)
+                u_before = Elem<T>::load1(static_cast<const T*>(p.u_prev) + ch);
+            const int ta = (c + 1) * kChunk;
+            if (ta < L) {
+                const float x = Elem<T>::load1(gd + row + ta) + bias;
+                const float da = SOFTPLUS ? softplus_f(x) : x;
+                cnu_after = da - Elem<T>::load1(gl + row + ta) * da;
+            }
+        }
         {
             float uu[K], dd[K], go[K];
             unpack(ru, uu);
             unpack(rd, dd);
             unpack(rg, go);
+            if constexpr (TRAP) unpack(rl, lm);
             float zz[HAS_Z ? K : 1];
             if constexpr (HAS_Z) unpack(rz, zz);
 #pragma unroll
@@ -376,7 +430,14 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
                 const float x = dd[k] + bias;
                 const float v = SOFTPLUS ? softplus_f(x) : x;
                 dt[k] = (t0 + k < L) ? v : 0.0f;
-                dtu[k] = dt[k] * uu[k];
+                if constexpr (TRAP) {
+                    uT[k] = uu[k];
+                    dtu[k] = lm[k] * dt[k] * uu[k];
+                    sA[k] = 0.0f;
+                    sP[k] = 0.0f;
+                } else {
+                    dtu[k] = dt[k] * uu[k];
+                }
                 sum_dt += dt[k];
                 if constexpr (HAS_Z) {
                     dy[k] = go[k] * zz[k] * sigmoid_f(zz[k]);
@@ -387,6 +448,18 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
                 dD_part = fmaf(dy[k], uu[k], dD_part);
                 sB[k] = 0.0f;
                 sgA[k] = 0.0f;
+            }
+            if constexpr (TRAP) {
+                const float um1 = shift_up(uu[K - 1], u_before);
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    cp[k] = (dt[k] - lm[k] * dt[k]) * (k == 0 ? um1 : uu[k - 1]);
+                const float cnu_next = shift_down(dt[0] - lm[0] * dt[0], cnu_after);
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    cnu[k] = (k + 1 < K) ? dt[k + 1] - lm[k + 1] * dt[k + 1] : cnu_next;
+                    cn[k] = cnu[k] * uu[k];
+                }
             }
         }
         // sum of Delta over the steps whose a multiplies the adjoint inside this lane:
@@ -424,6 +497,7 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
                     if (next_active) {
                         load_raw<T, K, VEC>(gu + row_next, t0, L, ru);
                         load_raw<T, K, VEC>(gd + row_next, t0, L, rd);
+                        if constexpr (TRAP) load_raw<T, K, VEC>(gl + row_next, t0, L, rl);
                     }
                 }
             }
@@ -449,11 +523,16 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
                 const float Gn = readlane(Gv, nc);
                 // lane-local chains: states from a zero start, adjoint from a zero end
                 float a[K], bb[K], cd[K];
+                float bp0 = 0.0f;  // TRAP: B of state nc at the step before the lane's first
+                if constexpr (TRAP) bp0 = shift_up(bv[K - 1], Bm1[nc]);
                 float h = 0.0f;
 #pragma unroll
                 for (int k = 0; k < K; ++k) {
                     a[k] = exp2_hw(dt[k] * An2);
-                    bb[k] = dtu[k] * bv[k];
+                    if constexpr (TRAP)
+                        bb[k] = fmaf(a[k], cp[k] * (k == 0 ? bp0 : bv[k - 1]), dtu[k] * bv[k]);
+                    else
+                        bb[k] = dtu[k] * bv[k];
                     h = fmaf(a[k], h, bb[k]);
                     cd[k] = cv[k] * dy[k];
                 }
@@ -499,13 +578,28 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
                 float dA_part = 0.0f;
 #pragma unroll
                 for (int k = K - 1; k >= 0; --k) {
-                    lam = fmaf((k == K - 1) ? a_next : a[k + 1], lam, cd[k]);
-                    const float hprev = (k == 0) ? hin : hs[k - 1];
-                    const float gk = lam * hprev * a[k];
-                    dA_part = fmaf(gk, dt[k], dA_part);
-                    sgA[k] = fmaf(gk, An, sgA[k]);
-                    sB[k] = fmaf(lam, bv[k], sB[k]);
-                    ob[k] = fmaf(lam, dtu[k], ob[k]);
+                    if constexpr (TRAP) {
+                        const float at = ((k == K - 1) ? a_next : a[k + 1]) * lam;
+                        lam = at + cd[k];
+                        const float bpk = (k == 0) ? bp0 : bv[k - 1];
+                        const float hprev = fmaf(cp[k], bpk, (k == 0) ? hin : hs[k - 1]);
+                        const float la = lam * a[k];
+                        const float gk = la * hprev;
+                        dA_part = fmaf(gk, dt[k], dA_part);
+                        sgA[k] = fmaf(gk, An, sgA[k]);
+                        sB[k] = fmaf(lam, bv[k], sB[k]);
+                        sA[k] = fmaf(at, bv[k], sA[k]);
+                        sP[k] = fmaf(la, bpk, sP[k]);
+                        ob[k] = fmaf(lam, dtu[k], fmaf(at, cn[k], ob[k]));
+                    } else {
+                        lam = fmaf((k == K - 1) ? a_next : a[k + 1], lam, cd[k]);
+                        const float hprev = (k == 0) ? hin : hs[k - 1];
+                        const float gk = lam * hprev * a[k];
+                        dA_part = fmaf(gk, dt[k], dA_part);
+                        sgA[k] = fmaf(gk, An, sgA[k]);
+                        sB[k] = fmaf(lam, bv[k], sB[k]);
+                        ob[k] = fmaf(lam, dtu[k], ob[k]);
+                    }
                 }
 #pragma unroll
                 for (int k = 0; k < K; ++k) sBn[k * KP] = ob[k];
@@ -527,6 +621,7 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
             if constexpr (!kEarlyUD) {
                 load_raw<T, K, VEC>(gu + row_next, t0, L, ru);
                 load_raw<T, K, VEC>(gd + row_next, t0, L, rd);
+                if constexpr (TRAP) load_raw<T, K, VEC>(gl + row_next, t0, L, rl);
             }
             load_raw<T, K, VEC>(gg_ + row_next, t0, L, rg);
             if constexpr (HAS_Z) load_raw<T, K, VEC>(gz + row_next, t0, L, rz);
@@ -538,7 +633,21 @@ __global__ __launch_bounds__(64 * kMainWaves) void bwd_main_kernel(ScanParams p,
         // to 0 the sigmoid factor is 0 as well); without it u is read again (L2-resident).
         float o1[K], o2[K];
         float db_part = 0.0f;
-        {
+        if constexpr (TRAP) {
+            float o3[K];
+            const float um1_0 = shift_up(uT[K - 1], u_before);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const float um1 = (k == 0) ? um1_0 : uT[k - 1];
+                const float dsp = SOFTPLUS ? 1.0f - exp2_hw(-dt[k] * kLog2e) : 1.0f;
+                o1[k] = fmaf(sB[k], lm[k] * dt[k], fmaf(sA[k], cnu[k], dy[k] * Dd));     // du
+                const float dD_ = fmaf(sP[k], um1 - lm[k] * um1, fmaf(sB[k], lm[k] * uT[k], sgA[k]));
+                o2[k] = dD_ * dsp;                                                       // ddelta
+                o3[k] = dt[k] * fmaf(uT[k], sB[k], -um1 * sP[k]);                         // dlam
+                db_part += (t0 + k < L) ? o2[k] : 0.0f;
+            }
+            store_k<T, K, VEC>(static_cast<T*>(g.dlam) + row, t0, L, o3);
+        } else {
             float uu[K];
             if constexpr (SOFTPLUS) {
 #pragma unroll
@@ -648,13 +757,13 @@ int compute_units() {
     return cus;
 }
 
-int main_per_wave(const ScanParams& p) {
+int main_per_wave(const ScanParams& p, int waves) {
     static const int cus = compute_units();
     const long long slots = static_cast<long long>(p.B) * p.nchunks;
     const long long target = cus;
-    long long per = (static_cast<long long>(p.D) * slots + target * kMainWaves - 1) /
-                    (target * kMainWaves);
-    const long long max_per = (p.D + kMainWaves - 1) / kMainWaves;
+    long long per = (static_cast<long long>(p.D) * slots + target * waves - 1) /
+                    (target * waves);
+    const long long max_per = (p.D + waves - 1) / waves;
     if (per < 1) per = 1;
     if (per > max_per) per = max_per;
     return static_cast<int>(per);
@@ -664,9 +773,10 @@ struct Timing {
     hipEvent_t begin, end;
 };
 
-template <typename T, bool VEC, bool HAS_Z, bool SP>
+template <typename T, bool VEC, bool HAS_Z, bool SP, bool TRAP>
 hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hipStream_t s,
                   Timing tm) {
+    constexpr int W = main_waves<TRAP>();
     const int per_sum = w.want_fwd ? sum_channels<true>() : sum_channels<false>();
     const int sum_waves = p.B * p.nchunks * ((p.D + per_sum - 1) / per_sum);
     dim3 sgrid((sum_waves + kSumWaves - 1) / kSumWaves), sblock(64 * kSumWaves);
@@ -686,19 +796,18 @@ hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hi
         hipLaunchKernelGGL(bwd_link_kernel<false>, lgrid, lblock, 0, s, p, g, w);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int per_wave = main_per_wave(p);
-    const int cgroups = (p.D + per_wave * kMainWaves - 1) / (per_wave * kMainWaves);
-    const size_t lds = main_lds_bytes(p.N, kMainWaves);
+    const int per_wave = main_per_wave(p, W);
+    const int cgroups = (p.D + per_wave * W - 1) / (per_wave * W);
+    const size_t lds = main_lds_bytes(p.N, W);
     // the LDS exceeds the 64 KB default; allow the largest need over N <= kMaxN
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&bwd_main_kernel<T, VEC, HAS_Z, SP>),
-        hipFuncAttributeMaxDynamicSharedMemorySize,
-        static_cast<int>(main_lds_bytes_max(kMainWaves)));
+        reinterpret_cast<const void*>(&bwd_main_kernel<T, VEC, HAS_Z, SP, TRAP>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(main_lds_bytes_max(W)));
     if (attr != hipSuccess) return attr;
-    dim3 mgrid(cgroups, p.nchunks, p.B), mblock(64 * kMainWaves);
+    dim3 mgrid(cgroups, p.nchunks, p.B), mblock(64 * W);
     if (tm.begin != nullptr && (e = hipEventRecord(tm.begin, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_main_kernel<T, VEC, HAS_Z, SP>), mgrid, mblock, lds, s, p, g, w,
-                       per_wave);
+    hipLaunchKernelGGL((bwd_main_kernel<T, VEC, HAS_Z, SP, TRAP>), mgrid, mblock, lds, s, p, g,
+                       w, per_wave);
     e = hipGetLastError();
     if (e == hipSuccess && tm.end != nullptr) e = hipEventRecord(tm.end, s);
     return e;
@@ -710,8 +819,22 @@ hipError_t bwd_dispatch(const ScanParams& p, const GradParams& g, const BwdWork&
     const bool vec = (static_cast<size_t>(p.L) * sizeof(T)) % 16 == 0;
     const bool hz = p.z != nullptr;
     const bool sp = p.softplus != 0;
+    if (p.lam != nullptr) {  // the trapezoidal variant (chunk states given by its forward)
+#define MSEL_BWD_T(V, Z, S) \
+        if (vec == V && hz == Z && sp == S) return bwd_go<T, V, Z, S, true>(p, g, w, s, tm);
+        MSEL_BWD_T(true, true, true)
+        MSEL_BWD_T(true, true, false)
+        MSEL_BWD_T(true, false, true)
+        MSEL_BWD_T(true, false, false)
+        MSEL_BWD_T(false, true, true)
+        MSEL_BWD_T(false, true, false)
+        MSEL_BWD_T(false, false, true)
+        MSEL_BWD_T(false, false, false)
+#undef MSEL_BWD_T
+        return hipErrorInvalidValue;
+    }
 #define MSEL_BWD(V, Z, S) \
-    if (vec == V && hz == Z && sp == S) return bwd_go<T, V, Z, S>(p, g, w, s, tm);
+    if (vec == V && hz == Z && sp == S) return bwd_go<T, V, Z, S, false>(p, g, w, s, tm);
     MSEL_BWD(true, true, true)
     MSEL_BWD(true, true, false)
     MSEL_BWD(true, false, true)

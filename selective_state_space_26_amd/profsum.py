@@ -2,8 +2,8 @@
 
     python -m selective_state_space_26_amd.profsum stats KERNEL_STATS_CSV OUT.md --command "..."
     python -m selective_state_space_26_amd.profsum traffic FETCH_CSV WRITE_CSV OUT.txt \\
-        --kernel bwd_main_kernel --copy-mib 512 --workload NAME --command-fetch "..." \\
-        --command-write "..."
+        --kernel bwd_main_kernel [--match "bwd_main_kernel<msel::bf16_t, ..., false>"] \\
+        --copy-mib 512 --workload NAME --command-fetch "..." --command-write "..."
 
 `stats` turns a `--kernel-trace --stats` kernel_stats.csv into a short markdown table.
 
@@ -82,7 +82,8 @@ def _per_dispatch(csv_path: str, counter: str):
     return out
 
 
-def traffic(fetch_csv, write_csv, out, kernel, copy_mib, workload, cmd_fetch, cmd_write):
+def traffic(fetch_csv, write_csv, out, kernel, copy_mib, workload, cmd_fetch, cmd_write,
+            match=None):
     copy_bytes = copy_mib * (1 << 20)
     res = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -92,7 +93,8 @@ def traffic(fetch_csv, write_csv, out, kernel, copy_mib, workload, cmd_fetch, cm
             raise SystemExit(f"no copyBuffer dispatch in {path}")
         cal_kib = max(copies)
         factor = copy_bytes / (cal_kib * 1024.0)
-        mine = [v for name, vs in d.items() if kernel in name for v in vs]
+        sel = match or kernel
+        mine = [v for name, vs in d.items() if sel in name for v in vs]
         if not mine:
             raise SystemExit(f"no {kernel} dispatch in {path}")
         kib = statistics.mean(mine)
@@ -107,6 +109,7 @@ def traffic(fetch_csv, write_csv, out, kernel, copy_mib, workload, cmd_fetch, cm
         f"# is scaled by a plain {copy_mib} MiB device copy read by the same counter",
         f"workload = {workload}",
         f"kernel = {kernel}",
+        f"dispatch_name_contains = {match or kernel}",
         f"source_sha256 = {source_digest(sources_of(kernel))}",
     ]
     for c, r in res.items():
@@ -133,6 +136,9 @@ def main():
     t.add_argument("write_csv")
     t.add_argument("out")
     t.add_argument("--kernel", required=True)
+    t.add_argument("--match", default=None,
+                   help="substring that selects the dispatches (default: --kernel), e.g. one "
+                        "template instantiation")
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--workload", required=True)
     t.add_argument("--command-fetch", required=True)
@@ -142,7 +148,7 @@ def main():
         stats(a.csv, a.out, a.command)
     else:
         traffic(a.fetch_csv, a.write_csv, a.out, a.kernel, a.copy_mib, a.workload,
-                a.command_fetch, a.command_write)
+                a.command_fetch, a.command_write, a.match)
 
 
 if __name__ == "__main__":

@@ -476,3 +476,31 @@ def test_complex_validation(lib):
     assert lib.msel_validate_complex_fwd(ctypes.byref(a)) == 7
     assert lib.msel_validate_complex_fwd(None) == 1
     assert lib.msel_scan_complex_fwd(None, None) == 1
+
+
+def test_trap_bwd_validation(lib):
+    a, t = _good_args(L=1000), _trap()
+    g = _good_grads(a)
+    a.chunk_states = _addr()
+    ws, big, dl = _addr(), 1 << 20, _addr()
+    v = lambda: lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
+                                           dl, ws, big)
+    assert v() == 0
+    a.chunk_states = None                      # the forward's chunk states are required
+    assert v() == 1
+    assert lib.msel_scan_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g), dl, ws,
+                                  big, None) == 1
+    a.chunk_states = _addr()
+    assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g), None,
+                                      ws, big) == 1
+    assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
+                                      dl + 8, ws, big) == 4
+    assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
+                                      a.u, ws, big) == 7
+    assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
+                                      g.du, ws, big) == 7
+    g.dB = t.lambda_
+    assert v() == 7
+    g = _good_grads(a)
+    assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g), dl,
+                                      None, 0) == 6

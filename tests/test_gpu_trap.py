@@ -172,3 +172,80 @@ def test_trap_full_size_sampled_channels():
         assert_close("out", host(out[b:b + 1].index_select(1, di)), ro, "bf16")
         assert_close("final_state", host(fin[b:b + 1].index_select(1, di)), rf, "bf16")
         assert_close("chunk_states", host(cs[b:b + 1].index_select(1, di)), rcs, "bf16")
+
+
+BWD_CASES = [
+    # batch, dim, dstate, seqlen, dtype, z, softplus, D/bias, h0, prev
+    (2, 5, 16, 1100, "f32", True, True, True, True, True),     # 3 chunks, ragged tail
+    (2, 5, 16, 2500, "bf16", True, True, True, True, True),    # scalar path (2500 % 8)
+    (1, 3, 8, 1024, "bf16", False, False, True, False, False), # whole chunks, no z/softplus
+    (2, 13, 11, 700, "f32", True, True, True, False, True),    # odd dstate, 13 channels
+    (1, 4, 16, 300, "f32", False, True, False, True, True),    # one ragged chunk
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "x".join(map(str, c[:5])))
+def test_trap_bwd_matches_oracle(case):
+    bsz, dim, N, L, dtype, with_z, sp, with_db, with_h0, prev = case
+    log(f"trap bwd {case}")
+    t = _inputs(*case)
+    t2 = msel_inputs.make(bsz, dim, N, L, dtype, 654, with_dout=True)
+    t["dout"] = t2["dout"]
+    d = _dev(t)
+    _, _, cs = msel.msel_scan_trap_fwd(d["u"], d["delta"], d["lam"], d["A"], d["B"], d["C"],
+                                       d["D"], d["z"], d["bias"], sp, d["h0"], d.get("u_prev"),
+                                       d.get("B_prev"), return_chunk_states=True)
+    g = msel.msel_scan_trap_bwd(d["u"], d["delta"], d["lam"], d["A"], d["B"], d["C"], d["dout"],
+                                cs, d["D"], d["z"], d["bias"], sp, d["h0"], d.get("u_prev"),
+                                d.get("B_prev"), want_dh0=True)
+    torch.cuda.synchronize()
+    v = _vals(t)
+    r = otrap.bwd(v["u"], v["delta"], v["lam"], v["A"], v["B"], v["C"], v["dout"], v["D"],
+                  v["z"], v["bias"], v["h0"], v.get("u_prev"), v.get("B_prev"), softplus=sp)
+    for k in ("du", "ddelta", "dlam", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        assert_close(k, host(g[k]), r[k], dtype)
+    if with_z:
+        assert_close("dz", host(g["dz"]), r["dz"], dtype)
+
+
+def test_trap_bwd_lambda_one_matches_msel_scan_bwd():
+    log("trap bwd lambda=1 vs msel_scan_bwd")
+    t = _inputs(2, 5, 16, 1100, "f32", True, True, True, True, True)
+    t["dout"] = msel_inputs.make(2, 5, 16, 1100, "f32", 655, with_dout=True)["dout"]
+    d = _dev(t)
+    ones = torch.ones_like(d["lam"])
+    _, _, cs = msel.msel_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                  d["bias"], True, d["h0"], return_chunk_states=True)
+    a = msel.msel_scan_trap_bwd(d["u"], d["delta"], ones, d["A"], d["B"], d["C"], d["dout"], cs,
+                                d["D"], d["z"], d["bias"], True, d["h0"], d["u_prev"],
+                                d["B_prev"], want_dh0=True)
+    b = msel.msel_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dout"], d["D"],
+                           d["z"], d["bias"], True, d["h0"], chunk_states=cs, want_dh0=True)
+    torch.cuda.synchronize()
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        assert_close(k, host(a[k]), host(b[k]), "f32")
+
+
+def test_trap_bwd_full_size_one_batch_row():
+    """The workload-2 shape (batch 8, 1536 channels, dstate 16, seqlen 2048, bf16): dB and dC
+    of batch row 0 (sums over all its channels) and du, ddelta, dlam, dz of 8 channels."""
+    w = msel_inputs.WORKLOADS[2]
+    log("trap bwd full size workload-2 shape")
+    t = msel_inputs.make(w.batch, w.dim, w.dstate, w.seqlen, w.dtype, w.seed, with_lam=True,
+                         with_dout=True)
+    d = _dev(t)
+    _, _, cs = msel.msel_scan_trap_fwd(d["u"], d["delta"], d["lam"], d["A"], d["B"], d["C"],
+                                       d["D"], d["z"], d["bias"], True, return_chunk_states=True)
+    g = msel.msel_scan_trap_bwd(d["u"], d["delta"], d["lam"], d["A"], d["B"], d["C"], d["dout"],
+                                cs, d["D"], d["z"], d["bias"], True)
+    torch.cuda.synchronize()
+    v = _vals(t)
+    row = lambda k: v[k][0:1]
+    r = otrap.bwd(row("u"), row("delta"), row("lam"), v["A"], row("B"), row("C"), row("dout"),
+                  v["D"], row("z"), v["bias"])
+    assert_close("dB", host(g["dB"][0:1]), r["dB"], "bf16")
+    assert_close("dC", host(g["dC"][0:1]), r["dC"], "bf16")
+    ds = np.array([0, 1, 511, 767, 1024, 1300, 1534, 1535])
+    di = torch.as_tensor(ds, device=g["du"].device)
+    for k in ("du", "ddelta", "dlam", "dz"):
+        assert_close(k, host(g[k][0:1].index_select(1, di)), r[k][:, ds], "bf16")
