@@ -212,21 +212,32 @@ msel_status msel_validate_trap_fwd(const msel_scan_args *args, const msel_trap_a
 msel_status msel_scan_trap_fwd(const msel_scan_args *args, const msel_trap_args *trap,
                                hipStream_t stream);
 
-/* Host-only checks of msel_scan_trap_bwd's arguments (those of msel_validate_bwd, the
- * trapezoidal inputs', chunk_states present, dlambda). */
-msel_status msel_validate_trap_bwd(const msel_scan_args *args, const msel_trap_args *trap,
-                                   const msel_scan_grads *grads, const void *dlambda,
-                                   const void *workspace, size_t workspace_bytes);
+/* The trapezoidal variant's gradients beyond msel_scan_grads.  Overwritten, not
+ * accumulated. */
+typedef struct {
+    void *dlambda;          /* required [batch, dim, seqlen], activation dtype, 16-byte     */
+                            /* aligned: gradient w.r.t. lambda                             */
+    float *du_prev;         /* optional [batch, dim]: gradient w.r.t. u_prev                */
+    float *dB_prev;         /* optional [batch, dstate]: gradient w.r.t. B_prev             */
+} msel_trap_grads;
 
-/* Backward of msel_scan_trap_fwd with recomputation (page 1; page 4 Appendix D, Memory),
- * the same three launches as msel_scan_bwd and the same outputs, plus dlambda
- * ([batch, dim, seqlen], activation dtype, required, 16-byte aligned): the gradient w.r.t.
- * lambda.  args->chunk_states is required and must hold msel_scan_trap_fwd's chunk states
- * for the same inputs; the workspace is msel_scan_bwd_workspace_bytes(args).  The gradients
- * w.r.t. u_prev and B_prev are not computed.  Same determinism as msel_scan_bwd. */
+/* Host-only checks of msel_scan_trap_bwd's arguments (those of msel_validate_bwd, the
+ * trapezoidal inputs and gradients, chunk_states present, no output equal to an input, the
+ * workspace or another output). */
+msel_status msel_validate_trap_bwd(const msel_scan_args *args, const msel_trap_args *trap,
+                                   const msel_scan_grads *grads,
+                                   const msel_trap_grads *trap_grads, const void *workspace,
+                                   size_t workspace_bytes);
+
+/* Backward of msel_scan_trap_fwd with recomputation (page 1; page 4 Appendix D, Memory):
+ * the same three launches as msel_scan_bwd and the same outputs, plus trap_grads.
+ * args->chunk_states is required and must hold msel_scan_trap_fwd's chunk states for the
+ * same inputs; the workspace is msel_scan_bwd_workspace_bytes(args).  du_prev and dB_prev let
+ * a caller that split a sequence across calls carry the gradient into the earlier call.
+ * Same determinism as msel_scan_bwd (dB_prev is an fp32 atomic sum over channels). */
 msel_status msel_scan_trap_bwd(const msel_scan_args *args, const msel_trap_args *trap,
-                               const msel_scan_grads *grads, void *dlambda, void *workspace,
-                               size_t workspace_bytes, hipStream_t stream);
+                               const msel_scan_grads *grads, const msel_trap_grads *trap_grads,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * The complex-valued (rotational) variant of the scan (Mamba-3).

@@ -38,6 +38,10 @@ class TrapArgs(ctypes.Structure):
     _fields_ = [("lambda_", _P), ("u_prev", _P), ("B_prev", _P)]
 
 
+class TrapGrads(ctypes.Structure):
+    _fields_ = [("dlambda", _P), ("du_prev", _P), ("dB_prev", _P)]
+
+
 class ConvArgs(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_int32), ("batch", ctypes.c_int32),
                 ("dim", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("width", ctypes.c_int32),
@@ -101,11 +105,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.msel_scan_bwd.argtypes = [a, g, _P, ctypes.c_size_t, _P]
     lib.msel_scan_bwd_profiled.restype = ctypes.c_int
     lib.msel_scan_bwd_profiled.argtypes = [a, g, _P, ctypes.c_size_t, _P, _P, _P]
-    tap = ctypes.POINTER(TrapArgs)
+    tap, tgp = ctypes.POINTER(TrapArgs), ctypes.POINTER(TrapGrads)
     lib.msel_validate_trap_bwd.restype = ctypes.c_int
-    lib.msel_validate_trap_bwd.argtypes = [a, tap, g, _P, _P, ctypes.c_size_t]
+    lib.msel_validate_trap_bwd.argtypes = [a, tap, g, tgp, _P, ctypes.c_size_t]
     lib.msel_scan_trap_bwd.restype = ctypes.c_int
-    lib.msel_scan_trap_bwd.argtypes = [a, tap, g, _P, _P, ctypes.c_size_t, _P]
+    lib.msel_scan_trap_bwd.argtypes = [a, tap, g, tgp, _P, ctypes.c_size_t, _P]
     lib.msel_validate_complex_fwd.restype = ctypes.c_int
     lib.msel_validate_complex_fwd.argtypes = [a]
     lib.msel_scan_complex_fwd.restype = ctypes.c_int

@@ -126,8 +126,8 @@ msel::ConvParams to_conv_params(const msel_conv_args* a) {
 // The backward's launches after validation: zero-fills, then summary, link and gradient
 // kernels (the trapezoidal variant when `tr` is given).
 msel_status run_bwd(const msel_scan_args* a, const msel_scan_grads* g, const msel_trap_args* tr,
-                    void* dlam, void* workspace, hipStream_t stream, hipEvent_t ev_begin,
-                    hipEvent_t ev_end) {
+                    const msel_trap_grads* tg, void* workspace, hipStream_t stream,
+                    hipEvent_t ev_begin, hipEvent_t ev_end) {
     const bool bf16 = a->dtype == MSEL_BF16;
     msel::ScanParams p = to_params(a);
     if (tr != nullptr) {
@@ -137,9 +137,11 @@ msel_status run_bwd(const msel_scan_args* a, const msel_scan_grads* g, const mse
     }
     const size_t DN = static_cast<size_t>(a->dim) * a->dstate;
     const size_t BNL = static_cast<size_t>(a->batch) * a->dstate * a->seqlen;
-    const msel::FillList fill = {{g->dA, g->dB, g->dC, g->dD, g->ddelta_bias},
+    float* dB_prev = tg != nullptr ? tg->dB_prev : nullptr;
+    const msel::FillList fill = {{g->dA, g->dB, g->dC, g->dD, g->ddelta_bias, dB_prev},
                                  {DN, BNL, BNL, static_cast<size_t>(a->dim),
-                                  static_cast<size_t>(a->dim)}};
+                                  static_cast<size_t>(a->dim),
+                                  static_cast<size_t>(a->batch) * a->dstate}};
     if (msel::launch_fill_zero(fill, stream) != hipSuccess) return MSEL_ERR_HIP;
     msel::GradParams gp;
     gp.dout = g->dout;
@@ -152,7 +154,11 @@ msel_status run_bwd(const msel_scan_args* a, const msel_scan_grads* g, const mse
     gp.dD = g->dD;
     gp.dbias = g->ddelta_bias;
     gp.dh0 = g->dh0;
-    gp.dlam = dlam;
+    if (tg != nullptr) {
+        gp.dlam = tg->dlambda;
+        gp.du_prev = tg->du_prev;
+        gp.dB_prev = tg->dB_prev;
+    }
     return hip_status(msel::launch_scan_bwd(p, gp, a->chunk_states, workspace, bf16, stream,
                                             ev_begin, ev_end));
 }
@@ -319,37 +325,41 @@ msel_status msel_conv1d_bwd(const msel_conv_args* a, const msel_conv_grads* g,
     p.dw = g->dweight;
     p.dbias = g->dbias;
     p.dstate = a->width > 1 ? g->dstate_in : nullptr;
-    const msel::FillList fill = {{g->dweight, g->dbias, nullptr, nullptr, nullptr},
+    const msel::FillList fill = {{g->dweight, g->dbias, nullptr, nullptr, nullptr, nullptr},
                                  {static_cast<size_t>(a->dim) * a->width,
-                                  static_cast<size_t>(a->dim), 0, 0, 0}};
+                                  static_cast<size_t>(a->dim), 0, 0, 0, 0}};
     if (msel::launch_fill_zero(fill, stream) != hipSuccess) return MSEL_ERR_HIP;
     return hip_status(msel::launch_conv_bwd(p, a->dtype == MSEL_BF16, stream));
 }
 
 msel_status msel_validate_trap_bwd(const msel_scan_args* a, const msel_trap_args* tr,
-                                   const msel_scan_grads* g, const void* dlam,
+                                   const msel_scan_grads* g, const msel_trap_grads* tg,
                                    const void* workspace, size_t workspace_bytes) {
     msel_status s = msel_validate_bwd(a, g, workspace, workspace_bytes);
     if (s != MSEL_OK) return s;
-    if (a->chunk_states == nullptr || tr == nullptr || tr->lambda == nullptr || dlam == nullptr)
+    if (a->chunk_states == nullptr || tr == nullptr || tr->lambda == nullptr || tg == nullptr ||
+        tg->dlambda == nullptr)
         return MSEL_ERR_NULL;
     const size_t e = a->dtype == MSEL_BF16 ? 2 : 4;
-    if (!aligned(tr->lambda, 16) || !aligned(dlam, 16) ||
+    if (!aligned(tr->lambda, 16) || !aligned(tg->dlambda, 16) ||
         (tr->u_prev != nullptr && !aligned(tr->u_prev, e)) ||
-        (tr->B_prev != nullptr && !aligned(tr->B_prev, e)))
+        (tr->B_prev != nullptr && !aligned(tr->B_prev, e)) ||
+        (tg->du_prev != nullptr && !aligned(tg->du_prev, 4)) ||
+        (tg->dB_prev != nullptr && !aligned(tg->dB_prev, 4)))
         return MSEL_ERR_ALIGN;
-    const void* ins[] = {tr->lambda, tr->u_prev, tr->B_prev};
+    // every output distinct from every input, the workspace and each other
+    const void* ins[] = {a->u, a->delta, a->B, a->C, a->z, a->A, a->D, a->delta_bias, a->h0,
+                         a->chunk_states, g->dout, tr->lambda, tr->u_prev, tr->B_prev,
+                         workspace};
     const void* outs[] = {g->du, g->ddelta, g->dz, g->dA, g->dB, g->dC, g->dD, g->ddelta_bias,
-                          g->dh0, workspace};
-    for (const void* o : outs)
-        for (const void* i : ins)
-            if (o != nullptr && o == i) return MSEL_ERR_ALIAS;
-    if (same_as_input(a, dlam) || dlam == g->dout || dlam == a->chunk_states || dlam == workspace)
-        return MSEL_ERR_ALIAS;
-    for (const void* i : ins)
-        if (i == dlam) return MSEL_ERR_ALIAS;
-    for (const void* o : outs)
-        if (o == dlam) return MSEL_ERR_ALIAS;
+                          g->dh0, tg->dlambda, tg->du_prev, tg->dB_prev};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        if (outs[i] == nullptr) continue;
+        for (const void* in : ins)
+            if (in != nullptr && in == outs[i]) return MSEL_ERR_ALIAS;
+        for (size_t j = 0; j < i; ++j)
+            if (outs[j] == outs[i]) return MSEL_ERR_ALIAS;
+    }
     return MSEL_OK;
 }
 
@@ -391,11 +401,11 @@ msel_status msel_scan_bwd_profiled(const msel_scan_args* a, const msel_scan_grad
 }
 
 msel_status msel_scan_trap_bwd(const msel_scan_args* a, const msel_trap_args* tr,
-                               const msel_scan_grads* g, void* dlam, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
-    msel_status s = msel_validate_trap_bwd(a, tr, g, dlam, workspace, workspace_bytes);
+                               const msel_scan_grads* g, const msel_trap_grads* tg,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    msel_status s = msel_validate_trap_bwd(a, tr, g, tg, workspace, workspace_bytes);
     if (s != MSEL_OK) return s;
-    return run_bwd(a, g, tr, dlam, workspace, stream, nullptr, nullptr);
+    return run_bwd(a, g, tr, tg, workspace, stream, nullptr, nullptr);
 }
 
 msel_status msel_scan_bwd(const msel_scan_args* a, const msel_scan_grads* g, void* workspace,

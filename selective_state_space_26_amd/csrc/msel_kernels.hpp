@@ -44,7 +44,11 @@ struct GradParams {
     float* dD;
     float* dbias;
     float* dh0;
-    void* dlam = nullptr;  // exponential-trapezoidal variant: gradient w.r.t. lambda
+    // exponential-trapezoidal variant: gradients w.r.t. lambda [B, D, L] and the inputs of
+    // the step before the first, u_prev [B, D] and B_prev [B, N] (fp32, B_prev's summed)
+    void* dlam = nullptr;
+    float* du_prev = nullptr;
+    float* dB_prev = nullptr;
 };
 
 // All launchers enqueue on `stream` and return the hipGetLastError() after the launch.
@@ -61,7 +65,7 @@ hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float
                            void* workspace, bool bf16, hipStream_t stream,
                            hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 // Zero-fill of up to kFillSlots float buffers in one launch (null slots are skipped).
-constexpr int kFillSlots = 5;
+constexpr int kFillSlots = 6;
 struct FillList {
     float* p[kFillSlots];
     size_t n[kFillSlots];

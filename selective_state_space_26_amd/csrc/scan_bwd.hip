@@ -576,6 +576,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                     }
                 }
                 float dA_part = 0.0f;
+                float first_lac = 0.0f;  // TRAP: lam_0 a_0 c_0 of the lane's first step
 #pragma unroll
                 for (int k = K - 1; k >= 0; --k) {
                     if constexpr (TRAP) {
@@ -591,6 +592,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                         sA[k] = fmaf(at, bv[k], sA[k]);
                         sP[k] = fmaf(la, bpk, sP[k]);
                         ob[k] = fmaf(lam, dtu[k], fmaf(at, cn[k], ob[k]));
+                        if (k == 0) first_lac = la * cp[0];
                     } else {
                         lam = fmaf((k == K - 1) ? a_next : a[k + 1], lam, cd[k]);
                         const float hprev = (k == 0) ? hin : hs[k - 1];
@@ -603,6 +605,12 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 }
 #pragma unroll
                 for (int k = 0; k < K; ++k) sBn[k * KP] = ob[k];
+                // TRAP: dB_prev[b, n] sums lam_0 a_0 c_0 of the sequence's first step over
+                // channels (the B_prev term of h_0)
+                if constexpr (TRAP) {
+                    if (c == 0 && lane == 0 && g.dB_prev != nullptr)
+                        unsafeAtomicAdd(g.dB_prev + static_cast<size_t>(b) * N + nc, first_lac);
+                }
                 const float dq = quad_sum(dA_part);
                 if ((lane & 3) == 0) dAs[nc * kDaQuads + (lane >> 2)] = dq;
             }
@@ -647,6 +655,9 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 db_part += (t0 + k < L) ? o2[k] : 0.0f;
             }
             store_k<T, K, VEC>(static_cast<T*>(g.dlam) + row, t0, L, o3);
+            // the u_prev term of h_0: (1 - lam_0) Delta_0 sum_n lam_0 a_0 B_prev
+            if (c == 0 && lane == 0 && g.du_prev != nullptr)
+                g.du_prev[ch] = (dt[0] - lm[0] * dt[0]) * sP[0];
         } else {
             float uu[K];
             if constexpr (SOFTPLUS) {

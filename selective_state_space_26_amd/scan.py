@@ -203,9 +203,11 @@ def bwd_workspace_bytes(u, A, chunk_states_given=False) -> int:
 def msel_scan_trap_bwd(u, delta, lam, A, B, C, dout, chunk_states, D=None, z=None,
                        delta_bias=None, delta_softplus=True, h0=None, u_prev=None, B_prev=None,
                        want_dA=True, want_dB=True, want_dC=True, want_dD=True,
-                       want_ddelta_bias=True, want_dh0=False, workspace=None):
+                       want_ddelta_bias=True, want_dh0=False, want_dprev=False,
+                       workspace=None):
     """Backward of msel_scan_trap_fwd (chunk_states: that forward's).  Returns a dict of
-    gradients as msel_scan_bwd does, plus "dlam"."""
+    gradients as msel_scan_bwd does, plus "dlam" and, with want_dprev, "du_prev" [batch, dim]
+    and "dB_prev" [batch, dstate] (fp32)."""
     a, (bsz, dim, N, L) = _args(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
     dev, dt = u.device, u.dtype
     _need(lam, "lam", (bsz, dim, L), dt, dev)
@@ -226,11 +228,15 @@ def msel_scan_trap_bwd(u, delta, lam, A, B, C, dout, chunk_states, D=None, z=Non
         "dD": torch.empty((dim,), **f32) if want_dD else None,
         "ddelta_bias": torch.empty((dim,), **f32) if want_ddelta_bias else None,
         "dh0": torch.empty((bsz, dim, N), **f32) if want_dh0 else None,
+        "du_prev": torch.empty((bsz, dim), **f32) if want_dprev else None,
+        "dB_prev": torch.empty((bsz, N), **f32) if want_dprev else None,
     }
     g = _lib.ScanGrads()
     g.dout = _ptr(dout)
     for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
         setattr(g, k, _ptr(r[k]))
+    tg = _lib.TrapGrads()
+    tg.dlambda, tg.du_prev, tg.dB_prev = _ptr(r["dlam"]), _ptr(r["du_prev"]), _ptr(r["dB_prev"])
     tr = _lib.TrapArgs()
     tr.lambda_, tr.u_prev, tr.B_prev = _ptr(lam), _ptr(u_prev), _ptr(B_prev)
     lib = _lib.load()
@@ -241,7 +247,7 @@ def msel_scan_trap_bwd(u, delta, lam, A, B, C, dout, chunk_states, D=None, z=Non
     ws_bytes = workspace.numel() * workspace.element_size() if need > 0 else 0
     _lib.check("msel_scan_trap_bwd",
                lib.msel_scan_trap_bwd(ctypes.byref(a), ctypes.byref(tr), ctypes.byref(g),
-                                      _ptr(r["dlam"]), ws_ptr, ws_bytes, _stream(dev)))
+                                      ctypes.byref(tg), ws_ptr, ws_bytes, _stream(dev)))
     return r
 
 

@@ -48,6 +48,7 @@ def test_struct_layout_matches_header(tmp_path):
         + "".join(f"F(msel_conv_args, {f})\n" for f, _ in _lib.ConvArgs._fields_)
         + "".join(f"F(msel_conv_grads, {f})\n" for f, _ in _lib.ConvGrads._fields_)
         + "".join(f"F(msel_trap_args, {f.rstrip('_')})\n" for f, _ in _lib.TrapArgs._fields_)
+        + "".join(f"F(msel_trap_grads, {f})\n" for f, _ in _lib.TrapGrads._fields_)
         + "return 0; }\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o",
@@ -69,6 +70,8 @@ def test_struct_layout_matches_header(tmp_path):
     assert int(got["targs"]) == ctypes.sizeof(_lib.TrapArgs)
     for f, _ in _lib.TrapArgs._fields_:
         assert int(got[f"msel_trap_args.{f.rstrip('_')}"]) == getattr(_lib.TrapArgs, f).offset, f
+    for f, _ in _lib.TrapGrads._fields_:
+        assert int(got[f"msel_trap_grads.{f}"]) == getattr(_lib.TrapGrads, f).offset, f
 
 
 def test_constants(lib):
@@ -478,29 +481,51 @@ def test_complex_validation(lib):
     assert lib.msel_scan_complex_fwd(None, None) == 1
 
 
+def _trap_grads():
+    t = _lib.TrapGrads()
+    t.dlambda, t.du_prev, t.dB_prev = _addr(), _addr(), _addr()
+    return t
+
+
 def test_trap_bwd_validation(lib):
     a, t = _good_args(L=1000), _trap()
-    g = _good_grads(a)
+    g, tg = _good_grads(a), _trap_grads()
     a.chunk_states = _addr()
-    ws, big, dl = _addr(), 1 << 20, _addr()
+    ws, big = _addr(), 1 << 20
     v = lambda: lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
-                                           dl, ws, big)
+                                           ctypes.byref(tg), ws, big)
+    assert v() == 0
+    tg.du_prev = tg.dB_prev = None
     assert v() == 0
     a.chunk_states = None                      # the forward's chunk states are required
     assert v() == 1
-    assert lib.msel_scan_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g), dl, ws,
-                                  big, None) == 1
+    assert lib.msel_scan_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
+                                  ctypes.byref(tg), ws, big, None) == 1
     a.chunk_states = _addr()
     assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g), None,
                                       ws, big) == 1
-    assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
-                                      dl + 8, ws, big) == 4
-    assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
-                                      a.u, ws, big) == 7
-    assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
-                                      g.du, ws, big) == 7
+    tg = _trap_grads()
+    tg.dlambda = None
+    assert v() == 1
+    tg = _trap_grads()
+    tg.dlambda += 8
+    assert v() == 4
+    tg = _trap_grads()
+    tg.du_prev += 2
+    assert v() == 4
+    for target in (a.u, g.du, t.lambda_, ws, a.chunk_states):
+        tg = _trap_grads()
+        tg.dlambda = target
+        assert v() == 7
+    tg = _trap_grads()
+    tg.dB_prev = g.dB
+    assert v() == 7
+    tg = _trap_grads()
+    tg.du_prev = t.u_prev
+    assert v() == 7
+    tg = _trap_grads()
     g.dB = t.lambda_
     assert v() == 7
     g = _good_grads(a)
-    assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g), dl,
-                                      None, 0) == 6
+    assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
+                                      ctypes.byref(tg), None, 0) == 6

@@ -197,12 +197,13 @@ def test_trap_bwd_matches_oracle(case):
                                        d.get("B_prev"), return_chunk_states=True)
     g = msel.msel_scan_trap_bwd(d["u"], d["delta"], d["lam"], d["A"], d["B"], d["C"], d["dout"],
                                 cs, d["D"], d["z"], d["bias"], sp, d["h0"], d.get("u_prev"),
-                                d.get("B_prev"), want_dh0=True)
+                                d.get("B_prev"), want_dh0=True, want_dprev=True)
     torch.cuda.synchronize()
     v = _vals(t)
     r = otrap.bwd(v["u"], v["delta"], v["lam"], v["A"], v["B"], v["C"], v["dout"], v["D"],
                   v["z"], v["bias"], v["h0"], v.get("u_prev"), v.get("B_prev"), softplus=sp)
-    for k in ("du", "ddelta", "dlam", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+    for k in ("du", "ddelta", "dlam", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0", "du_prev",
+              "dB_prev"):
         assert_close(k, host(g[k]), r[k], dtype)
     if with_z:
         assert_close("dz", host(g["dz"]), r["dz"], dtype)
