@@ -21,7 +21,8 @@ layouts, rows 2j and 2j+1 being a pair's two components; the readout is the real
 of C and h, so with every A[d, 2j+1] = 0 the variant is the real scan with A[d, 2j+1] replaced
 by A[d, 2j].  h0, final states and chunk states hold (Re, Im) interleaved the same way.
 
-This is written with numpy complex128, a loop over time vectorized over (b, d, j).
+This is written with numpy complex128, a loop over time vectorized over (b, d, j); ``bwd`` is
+reverse mode of that loop by hand, run backwards in time.
 """
 from __future__ import annotations
 
@@ -76,3 +77,73 @@ def fwd(u, delta, A, B, C, D=None, z=None, bias=None, h0=None, softplus=True, ch
         zz = _f64(z)
         y *= zz / (1.0 + np.exp(-zz))
     return y, interleave(h), cs
+
+
+def bwd(u, delta, A, B, C, dout, D=None, z=None, bias=None, h0=None, softplus=True):
+    """Gradients of sum(dout * out) for fwd(...): reverse mode of the forward loop by hand, in
+    complex arithmetic.  With G = dL/dRe h + i dL/dIm h, a step h = a h' + p sends
+    G' = conj(a) G back to h', Re(conj(G) dp) to p's inputs and Re(conj(G) da) to a's.
+    Returns du, ddelta (w.r.t. the raw delta), dz, dA, dB, dC, dD, ddelta_bias, dh0; dA, dh0
+    interleaved (Re, Im) like A and h0."""
+    u, delta, A, B, C, dout = map(_f64, (u, delta, A, B, C, dout))
+    bsz, dim, L = u.shape
+    N = A.shape[1]
+    J = N // 2
+    Ac = A[:, 0::2] + 1j * A[:, 1::2]
+    Bc = B[:, 0::2, :] + 1j * B[:, 1::2, :]
+    x = delta + (0.0 if bias is None else _f64(bias)[None, :, None])
+    dt = _softplus(x) if softplus else x
+    hs = np.zeros((L + 1, bsz, dim, J), dtype=np.complex128)
+    if h0 is not None:
+        hh = _f64(h0)
+        hs[0] = hh[:, :, 0::2] + 1j * hh[:, :, 1::2]
+    ys = np.zeros((bsz, dim, L))
+    for t in range(L):
+        a = np.exp(dt[:, :, t, None] * Ac[None])
+        hs[t + 1] = a * hs[t] + (dt[:, :, t] * u[:, :, t])[:, :, None] * Bc[:, None, :, t]
+        ys[:, :, t] = np.sum(C[:, None, 0::2, t] * hs[t + 1].real
+                             + C[:, None, 1::2, t] * hs[t + 1].imag, axis=2)
+    if D is not None:
+        ys += _f64(D)[None, :, None] * u
+    if z is not None:
+        zz = _f64(z)
+        sg = 1.0 / (1.0 + np.exp(-zz))
+        dy = dout * zz * sg
+        dz = dout * ys * sg * (1.0 + zz * (1.0 - sg))
+    else:
+        dy, dz = dout, None
+    du = np.zeros_like(u) if D is None else _f64(D)[None, :, None] * dy
+    ddt = np.zeros_like(dt)
+    dAc = np.zeros((dim, J), dtype=np.complex128)
+    dB = np.zeros_like(B)
+    dC = np.zeros_like(C)
+    G = np.zeros((bsz, dim, J), dtype=np.complex128)
+    for t in range(L - 1, -1, -1):
+        h_new, h_old = hs[t + 1], hs[t]
+        # y_t = sum_j C_r Re h + C_i Im h
+        G = G + dy[:, :, t, None] * (C[:, None, 0::2, t] + 1j * C[:, None, 1::2, t])
+        dC[:, 0::2, t] += np.sum(dy[:, :, t, None] * h_new.real, axis=1)
+        dC[:, 1::2, t] += np.sum(dy[:, :, t, None] * h_new.imag, axis=1)
+        # h_new = a h_old + dt u Bc
+        a = np.exp(dt[:, :, t, None] * Ac[None])
+        gp = np.conj(G)                                     # Re(gp * d(.)) is the pullback
+        pin = dt[:, :, t, None] * u[:, :, t, None]
+        dB[:, 0::2, t] += np.sum((gp * pin).real, axis=1)   # d/dB_r: Re(conj(G) pin)
+        dB[:, 1::2, t] += np.sum((gp * 1j * pin).real, axis=1)
+        du[:, :, t] += np.sum((gp * dt[:, :, t, None] * Bc[:, None, :, t]).real, axis=2)
+        ddt[:, :, t] += np.sum((gp * u[:, :, t, None] * Bc[:, None, :, t]).real, axis=2)
+        X = gp * a * h_old                                   # conj(G) a h_old
+        ddt[:, :, t] += np.sum((X * Ac[None]).real, axis=2)
+        dAc += np.sum(X * dt[:, :, t, None], axis=0)        # Re part -> dA_r, Re(i X dt) -> dA_i
+        G = np.conj(a) * G
+    dD = np.sum(dy * u, axis=(0, 2))
+    sig = 1.0 / (1.0 + np.exp(-x)) if softplus else np.ones_like(x)
+    ddelta = ddt * sig
+    dA = np.empty((dim, N))
+    dA[:, 0::2] = dAc.real
+    dA[:, 1::2] = (1j * dAc).real                            # d/dA_i = Re(i conj(G) dt a h)
+    dh0 = np.empty((bsz, dim, N))
+    dh0[:, :, 0::2] = G.real
+    dh0[:, :, 1::2] = G.imag
+    return dict(du=du, ddelta=ddelta, dz=dz, dA=dA, dB=dB, dC=dC, dD=dD,
+                ddelta_bias=ddelta.sum(axis=(0, 2)), dh0=dh0)

@@ -111,3 +111,62 @@ def test_odd_dstate_is_rejected():
     with pytest.raises(ValueError):
         cplx.fwd(np.zeros((1, 1, 2)), np.zeros((1, 1, 2)), np.zeros((1, 3)), np.zeros((1, 3, 2)),
                  np.zeros((1, 3, 2)))
+
+
+_GRADS = [("u", "du"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC"), ("D", "dD"),
+          ("z", "dz"), ("bias", "ddelta_bias"), ("h0", "dh0")]
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+def test_bwd_matches_finite_differences(softplus):
+    p = _problem(bsz=2, dim=2, N=4, L=7, with_h0=True, with_dout=True)
+    if not softplus:
+        p["delta"] = np.abs(p["delta"]) * 0.2
+        p["bias"] = np.abs(p["bias"]) * 0.01
+    args = lambda q: (q["u"], q["delta"], q["A"], q["B"], q["C"])
+    g = cplx.bwd(*args(p), p["dout"], p["D"], p["z"], p["bias"], p["h0"], softplus=softplus)
+
+    def loss(**over):
+        q = dict(p)
+        q.update(over)
+        out, _, _ = cplx.fwd(*args(q), q["D"], q["z"], q["bias"], q["h0"], softplus=softplus)
+        return float(np.sum(p["dout"] * out))
+
+    eps = 1e-6
+    for name, gname in _GRADS:
+        base = p[name]
+        num = np.zeros_like(base)
+        for idx in np.ndindex(*base.shape):
+            hi, lo = base.copy(), base.copy()
+            hi[idx] += eps
+            lo[idx] -= eps
+            num[idx] = (loss(**{name: hi}) - loss(**{name: lo})) / (2 * eps)
+        assert g[gname].shape == base.shape, name
+        assert _rel(g[gname], num) < 1e-6, name
+
+
+def test_bwd_matches_torch_autograd_of_the_rotation_form():
+    """The same recurrence written with real 2x2 scale-rotations (the page's formulation),
+    differentiated by torch on the CPU in fp64."""
+    torch = pytest.importorskip("torch")
+    p = _problem(bsz=2, dim=3, N=6, L=21, with_h0=True, with_dout=True)
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=k != "dout") for k, v in p.items()}
+    dt = torch.nn.functional.softplus(t["delta"] + t["bias"][None, :, None])
+    Ar, Ai = t["A"][:, 0::2], t["A"][:, 1::2]
+    hr, hi = t["h0"][..., 0::2], t["h0"][..., 1::2]
+    ys = []
+    for s in range(21):
+        e = torch.exp(dt[:, :, s, None] * Ar[None])
+        ang = dt[:, :, s, None] * Ai[None]
+        c, sn = e * torch.cos(ang), e * torch.sin(ang)
+        pin = (dt[:, :, s] * t["u"][:, :, s])[:, :, None]
+        hr, hi = (c * hr - sn * hi + pin * t["B"][:, None, 0::2, s],
+                  sn * hr + c * hi + pin * t["B"][:, None, 1::2, s])
+        ys.append((t["C"][:, None, 0::2, s] * hr + t["C"][:, None, 1::2, s] * hi).sum(dim=2))
+    y = torch.stack(ys, dim=2) + t["D"][None, :, None] * t["u"]
+    out = y * torch.nn.functional.silu(t["z"])
+    (out * t["dout"]).sum().backward()
+    g = cplx.bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["dout"], p["D"], p["z"],
+                 p["bias"], p["h0"])
+    for name, gname in _GRADS:
+        assert _rel(g[gname], t[name].grad.numpy()) < 1e-12, name
