@@ -40,6 +40,9 @@ FLOPS_TRAP_BWD = 31  # the backward's 20 + the previous/next-step input terms of
 # per complex state (a pair of real states) and step: Delta*A_re, Delta*A_im, exp2, sin, cos,
 # the two products of the transition, (Delta u)*B for both parts, h = a h + p (4 fma), y (2 fma)
 FLOPS_COMPLEX_PAIR = 21
+# its backward per complex state and step: recompute h (17), the adjoint conj(a) G + C dy (12),
+# X = conj(G) a h (12), the dDelta, dA, du, dB and dC terms (18)
+FLOPS_COMPLEX_BWD_PAIR = 59
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, per kernel, of the default workload
 TRAFFIC_FILE = "profiles/{kernel}_d768x2_bf16_traffic.txt"
 CONV_WIDTH = 4     # taps of the short causal convolution before the scan
@@ -273,7 +276,24 @@ def main():
     cev[1].record()
     torch.cuda.synchronize()
     per["complex_fwd"] = cev[0].elapsed_time(cev[1]) / args.steps
-    del csets
+    # its backward, from the chunk states of copy 0
+    complex_fwd(0)
+    cws = torch.empty(msel.bwd_workspace_bytes(d["u"], d["A"], True), device=dev,
+                      dtype=torch.uint8)
+
+    def complex_bwd():
+        c = csets[0]
+        msel.msel_scan_complex_bwd(c["u"], c["delta"], cA, d["B"], d["C"], d["dout"], trap_cs,
+                                   d["D"], c["z"], d["bias"], True, workspace=cws)
+    for _ in range(3):
+        complex_bwd()
+    cev[0].record()
+    for _ in range(args.steps):
+        complex_bwd()
+    cev[1].record()
+    torch.cuda.synchronize()
+    per["complex_bwd"] = cev[0].elapsed_time(cev[1]) / args.steps
+    del csets, cws
 
     # the short causal convolution + SiLU that makes the scan's input, at the same batch,
     # channels, length and dtype, width 4, with bias and incoming state: forward, backward
@@ -325,9 +345,12 @@ def main():
     alg["complex_fwd"] = alg["fwd"]
     # + lambda in, dlambda out
     alg["trap_bwd"] = alg["bwd"] + 2 * tc * (2 if w.dtype == "bf16" else 4)
+    alg["complex_bwd"] = alg["bwd"]
+    flops["complex_bwd"] = FLOPS_COMPLEX_BWD_PAIR * upd // 2
     flops["trap_bwd"] = (FLOPS_TRAP_BWD + (FLOPS_BWD_Z if d.get("z") is not None else 0)) * upd
     kernels = {}
-    for n in ("fwd", "chunk_carry", "bwd_main", "bwd", "trap_fwd", "trap_bwd", "complex_fwd"):
+    for n in ("fwd", "chunk_carry", "bwd_main", "bwd", "trap_fwd", "trap_bwd", "complex_fwd",
+              "complex_bwd"):
         sec = per[n] * 1e-3
         gbs = alg[n] / sec / 1e9
         kernels[n] = {"ms": round(per[n], 4), "alg_bytes": alg[n], "GB/s": round(gbs, 1),
@@ -336,6 +359,9 @@ def main():
         if n in flops:
             kernels[n]["TFLOP/s"] = round(flops[n] / sec / 1e12, 2)
     kernels["fwd"]["what"] = "scan_fwd_kernel (one launch)"
+    kernels["complex_bwd"]["what"] = ("the msel_scan_complex_bwd call (zero-fills, summary, link "
+                                      "and the pair-per-wavefront gradient kernel), timed apart "
+                                      "from the step")
     kernels["trap_bwd"]["what"] = ("the msel_scan_trap_bwd call (zero-fills, summary, link and "
                                    "the trapezoidal gradient kernel), timed apart from the step")
     kernels["complex_fwd"]["what"] = ("scan_cplx_fwd_kernel: the complex-valued (rotational) "

@@ -254,11 +254,25 @@ msel_status msel_scan_trap_bwd(const msel_scan_args *args, const msel_trap_args 
  * The arguments, layouts and outputs are msel_scan_fwd's (h0, final_state and chunk_states
  * hold (Re, Im) pairs); dstate must be even (else MSEL_ERR_SHAPE).  With every A[d, 2j+1] = 0
  * this is msel_scan_fwd with A[d, 2j+1] = A[d, 2j].  seqlen == 1 is the decode step (state in
- * place allowed).  The backward and chunk-carry pass of this variant are not part of the
- * library.
+ * place allowed).  Its backward is msel_scan_complex_bwd; its chunk-carry pass is not
+ * part of the library.
  * ---------------------------------------------------------------------------------------- */
 msel_status msel_validate_complex_fwd(const msel_scan_args *args);
 msel_status msel_scan_complex_fwd(const msel_scan_args *args, hipStream_t stream);
+
+/* Host-only checks of msel_scan_complex_bwd's arguments: those of msel_validate_bwd, dstate
+ * even, and chunk_states present. */
+msel_status msel_validate_complex_bwd(const msel_scan_args *args, const msel_scan_grads *grads,
+                                      const void *workspace, size_t workspace_bytes);
+
+/* Backward of msel_scan_complex_fwd with recomputation (page 1; page 4 Appendix D, Memory):
+ * zero-fills, per-chunk adjoint summaries, their link across chunks (with conjugated
+ * transitions) and a gradient kernel with one wavefront per state pair.  args->chunk_states
+ * is required and must hold msel_scan_complex_fwd's chunk states for the same inputs; the
+ * workspace is msel_scan_bwd_workspace_bytes(args).  The outputs are msel_scan_grads' (dA and
+ * dh0 interleaved (Re, Im) like A and h0), with msel_scan_bwd's determinism. */
+msel_status msel_scan_complex_bwd(const msel_scan_args *args, const msel_scan_grads *grads,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * The short causal convolution and activation that produce the scan's input.

@@ -68,7 +68,8 @@ EXPORTS = ["msel_abi_version", "msel_chunk_len", "msel_num_chunks", "msel_status
            "msel_scan_bwd", "msel_scan_bwd_profiled", "msel_validate_conv_fwd",
            "msel_validate_conv_bwd", "msel_conv1d_fwd", "msel_conv1d_bwd",
            "msel_validate_trap_fwd", "msel_scan_trap_fwd", "msel_validate_complex_fwd",
-           "msel_scan_complex_fwd", "msel_validate_trap_bwd", "msel_scan_trap_bwd"]
+           "msel_scan_complex_fwd", "msel_validate_trap_bwd", "msel_scan_trap_bwd",
+           "msel_validate_complex_bwd", "msel_scan_complex_bwd"]
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
@@ -110,6 +111,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.msel_validate_trap_bwd.argtypes = [a, tap, g, tgp, _P, ctypes.c_size_t]
     lib.msel_scan_trap_bwd.restype = ctypes.c_int
     lib.msel_scan_trap_bwd.argtypes = [a, tap, g, tgp, _P, ctypes.c_size_t, _P]
+    lib.msel_validate_complex_bwd.restype = ctypes.c_int
+    lib.msel_validate_complex_bwd.argtypes = [a, g, _P, ctypes.c_size_t]
+    lib.msel_scan_complex_bwd.restype = ctypes.c_int
+    lib.msel_scan_complex_bwd.argtypes = [a, g, _P, ctypes.c_size_t, _P]
     lib.msel_validate_complex_fwd.restype = ctypes.c_int
     lib.msel_validate_complex_fwd.argtypes = [a]
     lib.msel_scan_complex_fwd.restype = ctypes.c_int

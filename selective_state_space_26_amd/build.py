@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["msel_api.cpp", "scan_fwd.hip", "chunk_carry.hip", "scan_bwd.hip", "conv1d.hip",
-           "scan_cplx.hip"]
+           "scan_cplx.hip", "scan_cplx_bwd.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -380,6 +380,40 @@ msel_status msel_scan_trap_fwd(const msel_scan_args* a, const msel_trap_args* tr
     return hip_status(msel::launch_scan_fwd(p, a->dtype == MSEL_BF16, stream));
 }
 
+msel_status msel_validate_complex_bwd(const msel_scan_args* a, const msel_scan_grads* g,
+                                      const void* workspace, size_t workspace_bytes) {
+    msel_status s = msel_validate_bwd(a, g, workspace, workspace_bytes);
+    if (s != MSEL_OK) return s;
+    if (a->dstate % 2 != 0) return MSEL_ERR_SHAPE;
+    if (a->chunk_states == nullptr) return MSEL_ERR_NULL;
+    return MSEL_OK;
+}
+
+msel_status msel_scan_complex_bwd(const msel_scan_args* a, const msel_scan_grads* g,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    msel_status s = msel_validate_complex_bwd(a, g, workspace, workspace_bytes);
+    if (s != MSEL_OK) return s;
+    const size_t DN = static_cast<size_t>(a->dim) * a->dstate;
+    const size_t BNL = static_cast<size_t>(a->batch) * a->dstate * a->seqlen;
+    const msel::FillList fill = {{g->dA, g->dB, g->dC, g->dD, g->ddelta_bias, nullptr},
+                                 {DN, BNL, BNL, static_cast<size_t>(a->dim),
+                                  static_cast<size_t>(a->dim), 0}};
+    if (msel::launch_fill_zero(fill, stream) != hipSuccess) return MSEL_ERR_HIP;
+    msel::GradParams gp;
+    gp.dout = g->dout;
+    gp.du = g->du;
+    gp.ddelta = g->ddelta;
+    gp.dz = g->dz;
+    gp.dA = g->dA;
+    gp.dB = g->dB;
+    gp.dC = g->dC;
+    gp.dD = g->dD;
+    gp.dbias = g->ddelta_bias;
+    gp.dh0 = g->dh0;
+    return hip_status(msel::launch_scan_cplx_bwd(to_params(a), gp, a->chunk_states, workspace,
+                                                 a->dtype == MSEL_BF16, stream));
+}
+
 msel_status msel_scan_complex_fwd(const msel_scan_args* a, hipStream_t stream) {
     msel_status s = msel_validate_complex_fwd(a);
     if (s != MSEL_OK) return s;

@@ -56,6 +56,11 @@ hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_chunk_carry(const ScanParams& p, bool bf16, hipStream_t stream);
 // The complex-valued (rotational) forward: state pairs (2j, 2j+1) are complex states; N even.
 hipError_t launch_scan_cplx_fwd(const ScanParams& p, bool bf16, hipStream_t stream);
+// Its backward from the forward's chunk states (required); the workspace is laid out as the
+// real backward's with chunk states given (bwd_workspace_bytes(..., false)).
+hipError_t launch_scan_cplx_bwd(const ScanParams& p, const GradParams& g,
+                                const float* chunk_states, void* workspace, bool bf16,
+                                hipStream_t stream);
 // Backward: the summary/link passes write into `workspace` (bwd_workspace_bytes), then the
 // chunk-parallel main kernel.  chunk_states may be NULL (rebuilt in the workspace).
 size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states);

@@ -200,6 +200,45 @@ def bwd_workspace_bytes(u, A, chunk_states_given=False) -> int:
     return int(_lib.load().msel_scan_bwd_workspace_bytes(ctypes.byref(a)))
 
 
+def msel_scan_complex_bwd(u, delta, A, B, C, dout, chunk_states, D=None, z=None,
+                          delta_bias=None, delta_softplus=True, h0=None, want_dA=True,
+                          want_dB=True, want_dC=True, want_dD=True, want_ddelta_bias=True,
+                          want_dh0=False, workspace=None):
+    """Backward of msel_scan_complex_fwd (chunk_states: that forward's).  Returns a dict of
+    gradients as msel_scan_bwd does (dA and dh0 interleaved (Re, Im))."""
+    a, (bsz, dim, N, L) = _args(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
+    dev = u.device
+    _need(dout, "dout", (bsz, dim, L), u.dtype, dev)
+    _need(chunk_states, "chunk_states", (bsz, dim, num_chunks(L), N), torch.float32, dev)
+    if chunk_states is None:
+        raise ValueError("chunk_states (from msel_scan_complex_fwd) are required")
+    a.chunk_states = _ptr(chunk_states)
+    f32 = dict(device=dev, dtype=torch.float32)
+    r = {
+        "du": torch.empty_like(u), "ddelta": torch.empty_like(u),
+        "dz": torch.empty_like(u) if z is not None else None,
+        "dA": torch.empty((dim, N), **f32) if want_dA else None,
+        "dB": torch.empty((bsz, N, L), **f32) if want_dB else None,
+        "dC": torch.empty((bsz, N, L), **f32) if want_dC else None,
+        "dD": torch.empty((dim,), **f32) if want_dD else None,
+        "ddelta_bias": torch.empty((dim,), **f32) if want_ddelta_bias else None,
+        "dh0": torch.empty((bsz, dim, N), **f32) if want_dh0 else None,
+    }
+    g = _lib.ScanGrads()
+    g.dout = _ptr(dout)
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        setattr(g, k, _ptr(r[k]))
+    lib = _lib.load()
+    need = int(lib.msel_scan_bwd_workspace_bytes(ctypes.byref(a)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    _lib.check("msel_scan_complex_bwd",
+               lib.msel_scan_complex_bwd(ctypes.byref(a), ctypes.byref(g), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream(dev)))
+    return r
+
+
 def msel_scan_trap_bwd(u, delta, lam, A, B, C, dout, chunk_states, D=None, z=None,
                        delta_bias=None, delta_softplus=True, h0=None, u_prev=None, B_prev=None,
                        want_dA=True, want_dB=True, want_dC=True, want_dD=True,

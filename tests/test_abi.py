@@ -529,3 +529,22 @@ def test_trap_bwd_validation(lib):
     g = _good_grads(a)
     assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
                                       ctypes.byref(tg), None, 0) == 6
+
+
+def test_complex_bwd_validation(lib):
+    a = _good_args(N=16, L=1000)
+    a.chunk_states = _addr()
+    g = _good_grads(a)
+    ws, big = _addr(), 1 << 20
+    v = lambda: lib.msel_validate_complex_bwd(ctypes.byref(a), ctypes.byref(g), ws, big)
+    assert v() == 0
+    a.dstate = 15
+    assert v() == 2
+    a.dstate = 16
+    a.chunk_states = None
+    assert v() == 1
+    assert lib.msel_scan_complex_bwd(ctypes.byref(a), ctypes.byref(g), ws, big, None) == 1
+    a.chunk_states = _addr()
+    assert lib.msel_validate_complex_bwd(ctypes.byref(a), ctypes.byref(g), None, 0) == 6
+    g.dC = a.C
+    assert v() == 7

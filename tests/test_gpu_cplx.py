@@ -156,3 +156,84 @@ def test_complex_full_size_sampled_channels():
         assert_close("out", host(out[b:b + 1].index_select(1, di)), ro, "bf16")
         assert_close("final_state", host(fin[b:b + 1].index_select(1, di)), rf, "bf16")
         assert_close("chunk_states", host(cs[b:b + 1].index_select(1, di)), rcs, "bf16")
+
+
+BWD_CASES = [
+    # batch, dim, dstate, seqlen, dtype, z, softplus, D/bias, h0
+    (2, 5, 16, 1100, "f32", True, True, True, True),     # 3 chunks, ragged tail, 8 pairs
+    (2, 5, 16, 2500, "bf16", True, True, True, True),    # scalar path (2500 % 8)
+    (1, 3, 8, 1024, "bf16", False, False, True, False),  # whole chunks, no z / softplus
+    (2, 7, 6, 700, "f32", True, True, True, True),       # 3 pairs
+    (1, 4, 2, 300, "f32", False, True, False, True),     # one pair, one ragged chunk
+    (2, 3, 16, 1, "f32", True, True, True, True),        # one step
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "x".join(map(str, c[:5])))
+def test_complex_bwd_matches_oracle(case):
+    bsz, dim, N, L, dtype, with_z, sp, with_db, with_h0 = case
+    log(f"complex bwd {case}")
+    t = _inputs(*case)
+    t["dout"] = msel_inputs.make(bsz, dim, N, L, dtype, 99, with_dout=True)["dout"]
+    d = to_device(t)
+    _, _, cs = msel.msel_scan_complex_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],
+                                          d["z"], d["bias"], sp, d["h0"],
+                                          return_chunk_states=True)
+    g = msel.msel_scan_complex_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dout"], cs,
+                                   d["D"], d["z"], d["bias"], sp, d["h0"], want_dh0=True)
+    torch.cuda.synchronize()
+    v = _vals(t)
+    r = ocplx.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
+                  v["bias"], v["h0"], softplus=sp)
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        assert_close(k, host(g[k]), r[k], dtype)
+    if with_z:
+        assert_close("dz", host(g["dz"]), r["dz"], dtype)
+
+
+def test_complex_bwd_without_rotation_equals_the_real_backward():
+    log("complex bwd with A_im = 0 vs msel_scan_bwd")
+    t = _inputs(2, 5, 16, 1100, "f32", True, True, True, True)
+    t["dout"] = msel_inputs.make(2, 5, 16, 1100, "f32", 98, with_dout=True)["dout"]
+    d = to_device(t)
+    A = d["A"].clone()
+    A[:, 1::2] = 0.0
+    Ar = A.clone()
+    Ar[:, 1::2] = A[:, 0::2]
+    _, _, cs = msel.msel_scan_complex_fwd(d["u"], d["delta"], A, d["B"], d["C"], d["D"], d["z"],
+                                          d["bias"], True, d["h0"], return_chunk_states=True)
+    a = msel.msel_scan_complex_bwd(d["u"], d["delta"], A, d["B"], d["C"], d["dout"], cs, d["D"],
+                                   d["z"], d["bias"], True, d["h0"], want_dh0=True)
+    b = msel.msel_scan_bwd(d["u"], d["delta"], Ar, d["B"], d["C"], d["dout"], d["D"], d["z"],
+                           d["bias"], True, d["h0"], chunk_states=cs, want_dh0=True)
+    torch.cuda.synchronize()
+    for k in ("du", "ddelta", "dz", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        assert_close(k, host(a[k]), host(b[k]), "f32")
+    # the real part of dA is the two real states' sum; the imaginary part is free
+    assert_close("dA_re", host(a["dA"][:, 0::2]),
+                 host(b["dA"][:, 0::2] + b["dA"][:, 1::2]), "f32")
+
+
+def test_complex_bwd_full_size_one_batch_row():
+    """The workload-2 shape as 8 complex states: dB and dC of batch row 0 (summed over all
+    1536 channels) and du, ddelta, dz of 8 channels against the oracle."""
+    w = msel_inputs.WORKLOADS[2]
+    log("complex bwd full size workload-2 shape")
+    t = msel_inputs.make(w.batch, w.dim, w.dstate, w.seqlen, w.dtype, w.seed, with_dout=True,
+                         complex_A=True)
+    d = to_device(t)
+    _, _, cs = msel.msel_scan_complex_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],
+                                          d["z"], d["bias"], True, return_chunk_states=True)
+    g = msel.msel_scan_complex_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dout"], cs,
+                                   d["D"], d["z"], d["bias"], True)
+    torch.cuda.synchronize()
+    v = _vals(t)
+    row = lambda k: v[k][0:1]
+    r = ocplx.bwd(row("u"), row("delta"), v["A"], row("B"), row("C"), row("dout"), v["D"],
+                  row("z"), v["bias"])
+    assert_close("dB", host(g["dB"][0:1]), r["dB"], "bf16")
+    assert_close("dC", host(g["dC"][0:1]), r["dC"], "bf16")
+    ds = np.array([0, 1, 511, 767, 1024, 1300, 1534, 1535])
+    di = torch.as_tensor(ds, device=g["du"].device)
+    for k in ("du", "ddelta", "dz"):
+        assert_close(k, host(g[k][0:1].index_select(1, di)), r[k][:, ds], "bf16")
