@@ -55,6 +55,8 @@ struct BwdWork {
     float* sdt;     // [B*D*nch]: sum of Delta over the chunk
     float* dfirst;  // [B*D*nch]: Delta at the chunk's first step
     int want_fwd;   // the summary/link passes also build H
+    int c0;         // first chunk summarised: chunk 0's adjoint summary feeds only dh0, so
+                    // it is skipped (c0 = 1) when neither dh0 nor the states are built here
 };
 
 // Channels per wavefront in the summary: B and C rows are read (and converted) once per state
@@ -79,12 +81,13 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nch = p.nchunks;
     const int dgroups = (p.D + R - 1) / R;
-    const int idx = blockIdx.x * kSumWaves + wave;  // ((b * nch) + c) * dgroups + dg
-    if (idx >= p.B * nch * dgroups) return;
+    const int nsum = nch - w.c0;  // chunks summarised
+    const int idx = blockIdx.x * kSumWaves + wave;  // ((b * nsum) + c - c0) * dgroups + dg
+    if (idx >= p.B * nsum * dgroups) return;
     const int dg = idx % dgroups;
     const int bc = idx / dgroups;
-    const int c = bc % nch;
-    const int b = bc / nch;
+    const int c = w.c0 + bc % nsum;
+    const int b = bc / nsum;
     const int L = p.L;
     const int N = p.N;
     const int t0 = c * kChunk + lane * K;
@@ -221,12 +224,13 @@ __global__ __launch_bounds__(256) void bwd_link_kernel(ScanParams p, GradParams 
         }
     }
     float G = 0.0f;
-    for (int c = nch - 1; c >= 0; --c) {
+    for (int c = nch - 1; c >= w.c0; --c) {
         float* slot = w.G + (base + c) * N + n;
         const float Sr = *slot;
         *slot = G;
         G = fmaf(exp2_hw(A2 * w.sdt[base + c]), G, exp2_hw(A2 * w.dfirst[base + c]) * Sr);
     }
+    if (w.c0 > 0) w.G[base * N + n] = G;  // the carry after chunk 0 (no summary of its own)
     if (g.dh0 != nullptr) g.dh0[static_cast<size_t>(ch) * N + n] = G;
 }
 
@@ -789,12 +793,12 @@ hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hi
                   Timing tm) {
     constexpr int W = main_waves<TRAP>();
     const int per_sum = w.want_fwd ? sum_channels<true>() : sum_channels<false>();
-    const int sum_waves = p.B * p.nchunks * ((p.D + per_sum - 1) / per_sum);
+    const int sum_waves = p.B * (p.nchunks - w.c0) * ((p.D + per_sum - 1) / per_sum);
     dim3 sgrid((sum_waves + kSumWaves - 1) / kSumWaves), sblock(64 * kSumWaves);
     if (w.want_fwd)
         hipLaunchKernelGGL((bwd_summary_kernel<T, VEC, HAS_Z, SP, true>), sgrid, sblock, 0, s, p,
                            g, w);
-    else
+    else if (sum_waves > 0)  // none with a single chunk and no dh0
         hipLaunchKernelGGL((bwd_summary_kernel<T, VEC, HAS_Z, SP, false>), sgrid, sblock, 0, s, p,
                            g, w);
     hipError_t e = hipGetLastError();
@@ -882,6 +886,7 @@ hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float
     w.sdt = reinterpret_cast<float*>(ws);
     ws += up(per_chunk);
     w.dfirst = reinterpret_cast<float*>(ws);
+    w.c0 = (!w.want_fwd && g.dh0 == nullptr) ? 1 : 0;
     const Timing tm{ev_begin, ev_end};
     if (bf16) return bwd_dispatch<bf16_t>(p, g, w, stream, tm);
     return bwd_dispatch<float>(p, g, w, stream, tm);

@@ -59,14 +59,21 @@ def test_fwd_full_size(wid):
     _check_fwd_samples(w, t, out, fin, cs, k=12 if wid == 3 else 24)
 
 
-@pytest.mark.parametrize("wid", [2, 4])
-def test_bwd_full_size(wid):
+@pytest.mark.parametrize("wid,given_states", [(2, True), (2, False), (4, False)])
+def test_bwd_full_size(wid, given_states):
+    """given_states: the chunk states come from the forward, as in the benchmark's step (the
+    summary then skips the first chunk, whose adjoint summary would feed only dh0)."""
     w = msel_inputs.WORKLOADS[wid]
-    log(f"bwd full {w}")
+    log(f"bwd full {w} given_states={given_states}")
     t = msel_inputs.make_workload(w, with_dout=True)
     dv = to_device(t)
+    cs = None
+    if given_states:
+        _, _, cs = msel.msel_scan_fwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"],
+                                      dv["z"], dv["bias"], True, return_final_state=False,
+                                      return_chunk_states=True)
     g = msel.msel_scan_bwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["dout"], dv["D"],
-                           dv["z"], dv["bias"], True, chunk_states=None)
+                           dv["z"], dv["bias"], True, chunk_states=cs)
     torch.cuda.synchronize()
     # one whole batch row: dB, dC and every per-channel gradient of that row
     b = w.batch // 2

@@ -97,11 +97,12 @@ BWD_CASES = [
 ]
 
 
-@pytest.mark.parametrize("given_states", [False, True])
+@pytest.mark.parametrize("given_states,want_dh0", [(False, True), (True, True), (True, False)])
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "x".join(map(str, c[:5])))
-def test_bwd_matches_oracle(case, given_states):
+def test_bwd_matches_oracle(case, given_states, want_dh0):
+    """With the chunk states given and no dh0 asked for, the first chunk is not summarised."""
     bsz, dim, N, L, dtype, with_z, sp, with_db, with_h0 = case
-    log(f"bwd {case} given_states={given_states}")
+    log(f"bwd {case} given_states={given_states} want_dh0={want_dh0}")
     t = _case_inputs(*case, dout=True)
     dv = to_device(t)
     cs = None
@@ -110,12 +111,17 @@ def test_bwd_matches_oracle(case, given_states):
                                       dv["z"], dv["bias"], sp, dv["h0"],
                                       return_final_state=False, return_chunk_states=True)
     g = msel.msel_scan_bwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["dout"], dv["D"],
-                           dv["z"], dv["bias"], sp, dv["h0"], chunk_states=cs, want_dh0=True)
+                           dv["z"], dv["bias"], sp, dv["h0"], chunk_states=cs,
+                           want_dh0=want_dh0)
     torch.cuda.synchronize()
     v = oracle_vals(t)
     r = oracle.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
                    v["bias"], v["h0"], softplus=sp)
-    names = ["du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"]
+    names = ["du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias"]
+    if want_dh0:
+        names.append("dh0")
+    else:
+        assert g["dh0"] is None
     if with_z:
         names.append("dz")
     for k in names:
