@@ -42,6 +42,8 @@ struct CWork {
     float* G;        // [B*D*nch*N]: per chunk the local adjoint, then the adjoint carry
     float* sdt;      // [B*D*nch]: sum of Delta over the chunk
     float* dfirst;   // [B*D*nch]: Delta at the chunk's first step
+    int c0;          // first chunk summarised: chunk 0's summary feeds only dh0, so it is
+                     // skipped (c0 = 1) when dh0 is not asked for
 };
 
 __device__ __forceinline__ float sin_rev(float r) {
@@ -101,11 +103,12 @@ __global__ __launch_bounds__(256) void cplx_summary_kernel(ScanParams p, GradPar
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int nch = p.nchunks;
-    const long long unit = static_cast<long long>(blockIdx.x) * 4 + wave;  // (b, c, d)
-    if (unit >= static_cast<long long>(p.B) * nch * p.D) return;
+    const int nsum = nch - w.c0;  // chunks summarised
+    const long long unit = static_cast<long long>(blockIdx.x) * 4 + wave;  // (b, c - c0, d)
+    if (unit >= static_cast<long long>(p.B) * nsum * p.D) return;
     const int d = static_cast<int>(unit % p.D);
-    const int c = static_cast<int>((unit / p.D) % nch);
-    const int b = static_cast<int>(unit / (static_cast<long long>(p.D) * nch));
+    const int c = w.c0 + static_cast<int>((unit / p.D) % nsum);
+    const int b = static_cast<int>(unit / (static_cast<long long>(p.D) * nsum));
     const int L = p.L, N = p.N;
     const size_t ch = static_cast<size_t>(b) * p.D + d;
     const size_t row = ch * L;
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(256) void cplx_link_kernel(ScanParams p, GradParams
     const float Ar = p.A[static_cast<size_t>(d) * p.N + 2 * j] * kLog2e;
     const float Ai = p.A[static_cast<size_t>(d) * p.N + 2 * j + 1] * kInv2Pi;
     float Gr = 0.0f, Gi = 0.0f;
-    for (int c = nch - 1; c >= 0; --c) {
+    for (int c = nch - 1; c >= w.c0; --c) {
         const size_t base = static_cast<size_t>(ch) * nch + c;
         float* slot = w.G + base * p.N + 2 * j;
         const float Sr = slot[0], Si = slot[1];
@@ -207,6 +210,11 @@ __global__ __launch_bounds__(256) void cplx_link_kernel(ScanParams p, GradParams
         cmul(cf, sf, Sr, Si, br, bi);
         Gr = ar + br;
         Gi = ai + bi;
+    }
+    if (w.c0 > 0) {  // the carry after chunk 0 (no summary of its own)
+        float* slot = w.G + static_cast<size_t>(ch) * nch * p.N + 2 * j;
+        slot[0] = Gr;
+        slot[1] = Gi;
     }
     if (g.dh0 != nullptr) {
         g.dh0[static_cast<size_t>(ch) * p.N + 2 * j] = Gr;
@@ -520,11 +528,14 @@ int cplx_compute_units() {
 template <typename T, bool VEC, bool HAS_Z, bool SP>
 hipError_t cplx_bwd_go(const ScanParams& p, const GradParams& g, const CWork& w,
                        hipStream_t s) {
-    const long long units = static_cast<long long>(p.B) * p.nchunks * p.D;
-    hipLaunchKernelGGL((cplx_summary_kernel<T, VEC, HAS_Z, SP>),
-                       dim3(static_cast<unsigned>((units + 3) / 4)), dim3(256), 0, s, p, g, w);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const long long units = static_cast<long long>(p.B) * (p.nchunks - w.c0) * p.D;
+    hipError_t e = hipSuccess;
+    if (units > 0) {  // none with a single chunk and no dh0
+        hipLaunchKernelGGL((cplx_summary_kernel<T, VEC, HAS_Z, SP>),
+                           dim3(static_cast<unsigned>((units + 3) / 4)), dim3(256), 0, s, p, g,
+                           w);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const long long links = static_cast<long long>(p.B) * p.D * (p.N / 2);
     hipLaunchKernelGGL(cplx_link_kernel, dim3(static_cast<unsigned>((links + 255) / 256)),
                        dim3(256), 0, s, p, g, w);
@@ -582,6 +593,7 @@ hipError_t launch_scan_cplx_bwd(const ScanParams& p, const GradParams& g,
     w.sdt = reinterpret_cast<float*>(ws);
     ws += up(per_chunk);
     w.dfirst = reinterpret_cast<float*>(ws);
+    w.c0 = g.dh0 == nullptr ? 1 : 0;
     return bf16 ? cplx_bwd_dispatch<bf16_t>(p, g, w, stream)
                 : cplx_bwd_dispatch<float>(p, g, w, stream);
 }

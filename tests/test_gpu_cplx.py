@@ -169,10 +169,12 @@ BWD_CASES = [
 ]
 
 
+@pytest.mark.parametrize("want_dh0", [True, False])
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "x".join(map(str, c[:5])))
-def test_complex_bwd_matches_oracle(case):
+def test_complex_bwd_matches_oracle(case, want_dh0):
+    """Without dh0 the first chunk is not summarised (its summary feeds only dh0)."""
     bsz, dim, N, L, dtype, with_z, sp, with_db, with_h0 = case
-    log(f"complex bwd {case}")
+    log(f"complex bwd {case} want_dh0={want_dh0}")
     t = _inputs(*case)
     t["dout"] = msel_inputs.make(bsz, dim, N, L, dtype, 99, with_dout=True)["dout"]
     d = to_device(t)
@@ -180,12 +182,17 @@ def test_complex_bwd_matches_oracle(case):
                                           d["z"], d["bias"], sp, d["h0"],
                                           return_chunk_states=True)
     g = msel.msel_scan_complex_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dout"], cs,
-                                   d["D"], d["z"], d["bias"], sp, d["h0"], want_dh0=True)
+                                   d["D"], d["z"], d["bias"], sp, d["h0"], want_dh0=want_dh0)
     torch.cuda.synchronize()
     v = _vals(t)
     r = ocplx.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
                   v["bias"], v["h0"], softplus=sp)
-    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+    names = ["du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias"]
+    if want_dh0:
+        names.append("dh0")
+    else:
+        assert g["dh0"] is None
+    for k in names:
         assert_close(k, host(g[k]), r[k], dtype)
     if with_z:
         assert_close("dz", host(g["dz"]), r["dz"], dtype)
