@@ -8,8 +8,10 @@
 // * Affine-pair scans over a 64-lane wavefront.  The recurrence h_t = a_t h_{t-1} + b_t is
 //   affine in h, so pairs compose associatively, (a2,b2) o (a1,b1) = (a2 a1, a2 b1 + b2);
 //   that is what makes the work-efficient parallel scan of page 1 possible.  The forward scan
-//   uses DPP row_shr 1/2/4/8 inside 16-lane rows and row_bcast 15/31 across rows; the
-//   reverse (suffix) scan uses DPP row_shl inside rows and ds_swizzle / readlane across rows.
+//   uses DPP row_shr 1/2/4/8 inside 16-lane rows and row_bcast 15/31 across rows.  DPP has
+//   no broadcast towards lower lanes, so a suffix scan over the wave runs as a forward scan in
+//   reversed lane order (ds_bpermute reverses the wave), or, in the complex kernels, as row_shl
+//   levels inside rows and readlane across rows.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -243,95 +245,7 @@ __device__ __forceinline__ float writelane(float v, int lane, float old) {
     return (static_cast<int>(__lane_id()) == lane) ? v : old;
 }
 
-// One Hillis-Steele step: element l absorbs element l-s (which precedes it in time).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void fwd_step(float& P, float& S) {
-    float Pp = dpp<CTRL, ROW_MASK>(1.0f, P);
-    float Sp = dpp<CTRL, ROW_MASK>(0.0f, S);
-    S = fmaf(P, Sp, S);
-    P = P * Pp;
-}
-
-// Inclusive scan over the 64 lanes of a wave, lane 0 first in time:
-// (P_l, S_l) <- (P_l,S_l) o (P_{l-1},S_{l-1}) o ... o (P_0,S_0).
-__device__ __forceinline__ void wave_scan_fwd(float& P, float& S) {
-    fwd_step<kRowShr1, 0xf>(P, S);
-    fwd_step<kRowShr2, 0xf>(P, S);
-    fwd_step<kRowShr4, 0xf>(P, S);
-    fwd_step<kRowShr8, 0xf>(P, S);
-    fwd_step<kRowBcast15, 0xa>(P, S);
-    fwd_step<kRowBcast31, 0xc>(P, S);
-}
-
-// Exclusive version of an inclusive forward scan: lane l gets lane l-1's value, lane 0 the
-// identity (1, 0).
-__device__ __forceinline__ void wave_shift_fwd(float P, float S, float& Pex, float& Sex) {
-    Pex = dpp<kWaveShr1, 0xf>(1.0f, P);
-    Sex = dpp<kWaveShr1, 0xf>(0.0f, S);
-}
-
-// One reverse step: element l absorbs element l+s (which follows it in time), for the
-// backward recurrence g_t = e_t g_{t+1} + c_t: (P_l,S_l) <- (P_l, S_l) o' (P_{l+s}, S_{l+s})
-// meaning g_l_in = P_{l+s} x + S_{l+s} is fed into lane l: S_l += P_l S_{l+s}, P_l *= P_{l+s}.
-template <int CTRL>
-__device__ __forceinline__ void rev_step(float& P, float& S) {
-    float Pp = dpp<CTRL, 0xf>(1.0f, P);
-    float Sp = dpp<CTRL, 0xf>(0.0f, S);
-    S = fmaf(P, Sp, S);
-    P = P * Pp;
-}
-
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
-
-// Inclusive suffix scan over 64 lanes, lane 63 last in time: lane l ends with the composition
-// of lanes l..63 (lane 63 applied first).
-__device__ __forceinline__ void wave_scan_rev(float& P, float& S) {
-    rev_step<kRowShl1>(P, S);
-    rev_step<kRowShl2>(P, S);
-    rev_step<kRowShl4>(P, S);
-    rev_step<kRowShl8>(P, S);
-    const int lane = lane_id();
-    // rows: lanes 0-15 absorb lane 16's row total, lanes 32-47 absorb lane 48's.
-    // ds_swizzle bit mode within 32-lane halves: and_mask 0, or_mask 16 -> every lane reads
-    // lane 16 of its half.
-    {
-        constexpr int pat = (0x00) | (0x10 << 5);
-        float Pp = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, P), pat));
-        float Sp = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, S), pat));
-        bool take = (lane & 16) == 0;
-        Pp = take ? Pp : 1.0f;
-        Sp = take ? Sp : 0.0f;
-        S = fmaf(P, Sp, S);
-        P = P * Pp;
-    }
-    // lanes 0-31 absorb lane 32's total (the suffix of lanes 32..63).
-    {
-        float Pp = readlane(P, 32);
-        float Sp = readlane(S, 32);
-        bool take = lane < 32;
-        Pp = take ? Pp : 1.0f;
-        Sp = take ? Sp : 0.0f;
-        S = fmaf(P, Sp, S);
-        P = P * Pp;
-    }
-}
-
-// Exclusive suffix: lane l gets lane l+1's inclusive suffix, lane 63 the identity.
-__device__ __forceinline__ void wave_shift_rev(float P, float S, float& Pex, float& Sex) {
-    Pex = dpp<kWaveShl1, 0xf>(1.0f, P);
-    Sex = dpp<kWaveShl1, 0xf>(0.0f, S);
-}
-
-// Sum over the 64 lanes; every lane gets the total.
-__device__ __forceinline__ float wave_sum(float v) {
-    v += dpp<kRowShr1, 0xf>(0.0f, v);
-    v += dpp<kRowShr2, 0xf>(0.0f, v);
-    v += dpp<kRowShr4, 0xf>(0.0f, v);
-    v += dpp<kRowShr8, 0xf>(0.0f, v);
-    v += dpp<kRowBcast15, 0xa>(0.0f, v);
-    v += dpp<kRowBcast31, 0xc>(0.0f, v);
-    return readlane(v, 63);
-}
 
 
 // ---------------------------------------------------------------------------------------
@@ -361,150 +275,30 @@ __device__ __forceinline__ void scan_fwd_fused(float& P, float& S) {
                  : [P] "+v"(P), [S] "+v"(S));
 }
 
-// Inclusive suffix scan over the 64 lanes (lane 63 last in time): the row levels are fused
-// DPP row_shl; the two cross-row levels use ds_swizzle and readlane.
-__device__ __forceinline__ void scan_rev_fused(float& P, float& S) {
+// Two independent inclusive forward scans over the 64 lanes in one instruction stream.  Each
+// DPP read comes at least three instructions after the write of its source, so the levels need
+// no wait states (only the first, after the inputs were written).
+__device__ __forceinline__ void scan_fwd2_fused(float& P, float& S, float& P2, float& S2) {
+#define MSEL_FWD2_LEVEL(CTRL, RMASK)                                                 \
+    "v_fmac_f32_dpp %[S], %[S], %[P] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"      \
+    "v_mul_f32_dpp %[P], %[P], %[P] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"       \
+    "v_fmac_f32_dpp %[S2], %[S2], %[P2] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"   \
+    "v_mul_f32_dpp %[P2], %[P2], %[P2] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"
     asm volatile("s_nop 1\n"
-                 MSEL_FWD_LEVEL("row_shl:1", "0xf")
-                 MSEL_FWD_LEVEL("row_shl:2", "0xf")
-                 MSEL_FWD_LEVEL("row_shl:4", "0xf")
-                 MSEL_FWD_LEVEL("row_shl:8", "0xf")
-                 : [P] "+v"(P), [S] "+v"(S));
-    const int lane = lane_id();
-    {
-        constexpr int pat = (0x10 << 5);  // every lane of a 32-lane half reads its lane 16
-        const float Pp = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, P), pat));
-        const float Sp = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, S), pat));
-        const bool take = (lane & 16) == 0;
-        S = take ? fmaf(P, Sp, S) : S;
-        P = take ? P * Pp : P;
-    }
-    {
-        const float Pp = readlane(P, 32);
-        const float Sp = readlane(S, 32);
-        const bool take = lane < 32;
-        S = take ? fmaf(P, Sp, S) : S;
-        P = take ? P * Pp : P;
-    }
+                 MSEL_FWD2_LEVEL("row_shr:1", "0xf")
+                 MSEL_FWD2_LEVEL("row_shr:2", "0xf")
+                 MSEL_FWD2_LEVEL("row_shr:4", "0xf")
+                 MSEL_FWD2_LEVEL("row_shr:8", "0xf")
+                 MSEL_FWD2_LEVEL("row_bcast:15", "0xa")
+                 MSEL_FWD2_LEVEL("row_bcast:31", "0xc")
+                 : [P] "+v"(P), [S] "+v"(S), [P2] "+v"(P2), [S2] "+v"(S2));
+#undef MSEL_FWD2_LEVEL
 }
 
-// The forward scan of (P, S) and the row levels of the suffix scan of (Pr, Sr) in one
-// instruction stream.  The two are independent, so each one's DPP reads come at least two
-// instructions after the other's writes and the row levels need no wait states; only the two
-// cross-row levels of the forward scan keep theirs.  On return (P, S) is the full inclusive
-// scan over the wave and (Pr, Sr) the suffix scan within each 16-lane row (finish it with
-// rev_rows_apply).
-__device__ __forceinline__ void scan_fwd_and_rev_rows(float& P, float& S, float& Pr, float& Sr) {
-#define MSEL_PAIR_LEVEL(CF, CR)                                                         \
-    "v_fmac_f32_dpp %[S], %[S], %[P] " CF " row_mask:0xf bank_mask:0xf\n"              \
-    "v_mul_f32_dpp %[P], %[P], %[P] " CF " row_mask:0xf bank_mask:0xf\n"               \
-    "v_fmac_f32_dpp %[Sr], %[Sr], %[Pr] " CR " row_mask:0xf bank_mask:0xf\n"           \
-    "v_mul_f32_dpp %[Pr], %[Pr], %[Pr] " CR " row_mask:0xf bank_mask:0xf\n"
-    asm volatile("s_nop 1\n"
-                 MSEL_PAIR_LEVEL("row_shr:1", "row_shl:1")
-                 MSEL_PAIR_LEVEL("row_shr:2", "row_shl:2")
-                 MSEL_PAIR_LEVEL("row_shr:4", "row_shl:4")
-                 MSEL_PAIR_LEVEL("row_shr:8", "row_shl:8")
-                 MSEL_FWD_LEVEL("row_bcast:15", "0xa")
-                 MSEL_FWD_LEVEL("row_bcast:31", "0xc")
-                 : [P] "+v"(P), [S] "+v"(S), [Pr] "+v"(Pr), [Sr] "+v"(Sr));
-#undef MSEL_PAIR_LEVEL
-}
-
-// Row levels (16-lane rows) of four independent scans in one instruction stream: (P1, S1) and
-// (P2, S2) forward (row_shr), (Q1, R1) and (Q2, R2) suffix (row_shl).  Each DPP read comes at
-// least three instructions after the write of its source, so no wait states are needed.
-__device__ __forceinline__ void scan_rows4(float& P1, float& S1, float& Q1, float& R1, float& P2,
-                                           float& S2, float& Q2, float& R2) {
-#define MSEL_ROW4(CF, CR)                                                            \
-    "v_fmac_f32_dpp %[S1], %[S1], %[P1] " CF " row_mask:0xf bank_mask:0xf\n"         \
-    "v_mul_f32_dpp %[P1], %[P1], %[P1] " CF " row_mask:0xf bank_mask:0xf\n"          \
-    "v_fmac_f32_dpp %[R1], %[R1], %[Q1] " CR " row_mask:0xf bank_mask:0xf\n"         \
-    "v_mul_f32_dpp %[Q1], %[Q1], %[Q1] " CR " row_mask:0xf bank_mask:0xf\n"          \
-    "v_fmac_f32_dpp %[S2], %[S2], %[P2] " CF " row_mask:0xf bank_mask:0xf\n"         \
-    "v_mul_f32_dpp %[P2], %[P2], %[P2] " CF " row_mask:0xf bank_mask:0xf\n"          \
-    "v_fmac_f32_dpp %[R2], %[R2], %[Q2] " CR " row_mask:0xf bank_mask:0xf\n"         \
-    "v_mul_f32_dpp %[Q2], %[Q2], %[Q2] " CR " row_mask:0xf bank_mask:0xf\n"
-    asm volatile("s_nop 1\n"
-                 MSEL_ROW4("row_shr:1", "row_shl:1")
-                 MSEL_ROW4("row_shr:2", "row_shl:2")
-                 MSEL_ROW4("row_shr:4", "row_shl:4")
-                 MSEL_ROW4("row_shr:8", "row_shl:8")
-                 : [P1] "+v"(P1), [S1] "+v"(S1), [Q1] "+v"(Q1), [R1] "+v"(R1),
-                   [P2] "+v"(P2), [S2] "+v"(S2), [Q2] "+v"(Q2), [R2] "+v"(R2));
-#undef MSEL_ROW4
-}
-
-// Row levels of two independent suffix scans (row_shl), interleaved; the DPP reads come two
-// instructions after the writes of their sources, which is the wait the hardware needs.
-__device__ __forceinline__ void scan_rows2_rev(float& Q1, float& R1, float& Q2, float& R2) {
-#define MSEL_ROW2(CR)                                                                \
-    "v_fmac_f32_dpp %[R1], %[R1], %[Q1] " CR " row_mask:0xf bank_mask:0xf\n"         \
-    "v_mul_f32_dpp %[Q1], %[Q1], %[Q1] " CR " row_mask:0xf bank_mask:0xf\n"          \
-    "v_fmac_f32_dpp %[R2], %[R2], %[Q2] " CR " row_mask:0xf bank_mask:0xf\n"         \
-    "v_mul_f32_dpp %[Q2], %[Q2], %[Q2] " CR " row_mask:0xf bank_mask:0xf\n"
-    asm volatile("s_nop 1\n"
-                 MSEL_ROW2("row_shl:1")
-                 MSEL_ROW2("row_shl:2")
-                 MSEL_ROW2("row_shl:4")
-                 MSEL_ROW2("row_shl:8")
-                 : [Q1] "+v"(Q1), [R1] "+v"(R1), [Q2] "+v"(Q2), [R2] "+v"(R2));
-#undef MSEL_ROW2
-}
-
-// Row levels of four independent suffix scans (row_shl), interleaved.
-__device__ __forceinline__ void scan_rows4_rev(float& Q1, float& R1, float& Q2, float& R2,
-                                               float& Q3, float& R3, float& Q4, float& R4) {
-#define MSEL_ROWR4(CR)                                                               \
-    "v_fmac_f32_dpp %[R1], %[R1], %[Q1] " CR " row_mask:0xf bank_mask:0xf\n"         \
-    "v_mul_f32_dpp %[Q1], %[Q1], %[Q1] " CR " row_mask:0xf bank_mask:0xf\n"          \
-    "v_fmac_f32_dpp %[R2], %[R2], %[Q2] " CR " row_mask:0xf bank_mask:0xf\n"         \
-    "v_mul_f32_dpp %[Q2], %[Q2], %[Q2] " CR " row_mask:0xf bank_mask:0xf\n"          \
-    "v_fmac_f32_dpp %[R3], %[R3], %[Q3] " CR " row_mask:0xf bank_mask:0xf\n"         \
-    "v_mul_f32_dpp %[Q3], %[Q3], %[Q3] " CR " row_mask:0xf bank_mask:0xf\n"          \
-    "v_fmac_f32_dpp %[R4], %[R4], %[Q4] " CR " row_mask:0xf bank_mask:0xf\n"         \
-    "v_mul_f32_dpp %[Q4], %[Q4], %[Q4] " CR " row_mask:0xf bank_mask:0xf\n"
-    asm volatile("s_nop 1\n"
-                 MSEL_ROWR4("row_shl:1")
-                 MSEL_ROWR4("row_shl:2")
-                 MSEL_ROWR4("row_shl:4")
-                 MSEL_ROWR4("row_shl:8")
-                 : [Q1] "+v"(Q1), [R1] "+v"(R1), [Q2] "+v"(Q2), [R2] "+v"(R2),
-                   [Q3] "+v"(Q3), [R3] "+v"(R3), [Q4] "+v"(Q4), [R4] "+v"(R4));
-#undef MSEL_ROWR4
-}
-
-// Totals of scans whose row levels are done (wave-uniform results):
-//  forward: the composition of all 64 lanes, from the last lane of each row;
-//  suffix:  the composition of all 64 lanes, from the first lane of each row.
-// Only the S part is returned (the end state from a zero start, resp. the value at lane 0
-// from a zero carry).
-__device__ __forceinline__ float fwd_rows_total(float P, float S) {
-    float t = readlane(S, 15);
-    t = fmaf(readlane(P, 31), t, readlane(S, 31));
-    t = fmaf(readlane(P, 47), t, readlane(S, 47));
-    return fmaf(readlane(P, 63), t, readlane(S, 63));
-}
-__device__ __forceinline__ float rev_rows_total(float P, float S) {
-    float t = readlane(S, 48);
-    t = fmaf(readlane(P, 32), t, readlane(S, 32));
-    t = fmaf(readlane(P, 16), t, readlane(S, 16));
-    return fmaf(readlane(P, 0), t, readlane(S, 0));
-}
-
-// Finishes a suffix scan whose row levels are done: (P, S) of lane l compose lanes l..15 of
-// its row.  `carry` is the value entering from beyond lane 63 (wave-uniform).  Returns, in
-// every lane, the suffix composition of lanes l..63 applied to `carry`:
-//   V_l = S_l + P_l R(row),  R(3) = carry,  R(r) = S_{16(r+1)} + P_{16(r+1)} R(r+1),
-// read from the first lane of each following row (no LDS round trip).
-__device__ __forceinline__ float rev_rows_apply(float P, float S, float carry) {
-    const float R3 = carry;
-    const float R2 = fmaf(readlane(P, 48), R3, readlane(S, 48));
-    const float R1 = fmaf(readlane(P, 32), R2, readlane(S, 32));
-    const float R0 = fmaf(readlane(P, 16), R1, readlane(S, 16));
-    const int row = lane_id() >> 4;
-    const float R = row == 0 ? R0 : (row == 1 ? R1 : (row == 2 ? R2 : R3));
-    return fmaf(P, R, S);
+// The value of lane 63 - l in lane l (a whole-wave reversal through the LDS crossbar, no LDS
+// memory); rev_addr is (63 - lane) * 4.
+__device__ __forceinline__ float rev_lanes(float v, int rev_addr) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(rev_addr, __builtin_bit_cast(int, v)));
 }
 
 // Sum over each group of four consecutive lanes (every lane of the group gets it).

@@ -360,6 +360,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     float* myC = accC + grp * tile;
 
     const int t0 = c * kChunk + lane * K;
+    const int rev_addr = (63 - lane) << 2;
     const f32x4* __restrict__ B4 = reinterpret_cast<const f32x4*>(BCs);
     const f32x4* __restrict__ C4 = reinterpret_cast<const f32x4*>(BCs + N * kChunk);
     const T* __restrict__ gu = static_cast<const T*>(p.u);
@@ -466,9 +467,6 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 }
             }
         }
-        // sum of Delta over the steps whose a multiplies the adjoint inside this lane:
-        // a_{t+1} for t in the lane, i.e. this lane's steps 1..K-1 and the next lane's first
-        const float rsum_dt = sum_dt - dt[0] + shift_down(dt[0], 0.0f);
         // this channel's z and dout, fetched during the last step for dz
         Raw<T, K> cz, cg;
 
@@ -540,17 +538,23 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                     h = fmaf(a[k], h, bb[k]);
                     cd[k] = cv[k] * dy[k];
                 }
-                const float a_next = shift_down(a[0], 1.0f);
-                float rr = 0.0f;
+                // the lane's adjoint chain from a zero input on its right
+                float rr = cd[K - 1];
 #pragma unroll
-                for (int k = K - 1; k >= 0; --k)
-                    rr = fmaf((k == K - 1) ? a_next : a[k + 1], rr, cd[k]);
+                for (int k = K - 2; k >= 0; --k) rr = fmaf(a[k + 1], rr, cd[k]);
+                // Lane maps.  States: x -> P x + S with P = a_{K-1} ... a_0.  Adjoints: from the
+                // one arriving on the lane's right (carried into its last step) to the one
+                // leaving on its left (carried into the previous lane's last step),
+                // x -> P x + a_0 rr, the same P.  The adjoint maps are scanned forward in
+                // reversed lane order, next to the states' scan.
                 float P = exp2_hw(An2 * sum_dt), S = h;
-                float Pr = exp2_hw(An2 * rsum_dt), Sr = rr;
-                scan_fwd_and_rev_rows(P, S, Pr, Sr);
-                // state entering the lane (from H_c), adjoint entering it from the right (G_c)
+                float Pr = rev_lanes(P, rev_addr), Sr = rev_lanes(a[0] * rr, rev_addr);
+                scan_fwd2_fused(P, S, Pr, Sr);
+                // state entering the lane (from H_c)
                 const float hin = shift_up(fmaf(P, Hn, S), Hn);
-                float lam = shift_down(rev_rows_apply(Pr, Sr, Gn), Gn);
+                // reversed lane 63 - l now maps G_c to the adjoint leaving lane l on its left;
+                // lane l receives lane l + 1's (G_c for lane 63), carried into its last step
+                float lam = rev_lanes(shift_up(fmaf(Pr, Gn, Sr), Gn), rev_addr);
                 float hs[K];
                 h = hin;
 #pragma unroll
@@ -584,7 +588,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
 #pragma unroll
                 for (int k = K - 1; k >= 0; --k) {
                     if constexpr (TRAP) {
-                        const float at = ((k == K - 1) ? a_next : a[k + 1]) * lam;
+                        const float at = (k == K - 1) ? lam : a[k + 1] * lam;
                         lam = at + cd[k];
                         const float bpk = (k == 0) ? bp0 : bv[k - 1];
                         const float hprev = fmaf(cp[k], bpk, (k == 0) ? hin : hs[k - 1]);
@@ -598,7 +602,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                         ob[k] = fmaf(lam, dtu[k], fmaf(at, cn[k], ob[k]));
                         if (k == 0) first_lac = la * cp[0];
                     } else {
-                        lam = fmaf((k == K - 1) ? a_next : a[k + 1], lam, cd[k]);
+                        lam = (k == K - 1) ? lam + cd[k] : fmaf(a[k + 1], lam, cd[k]);
                         const float hprev = (k == 0) ? hin : hs[k - 1];
                         const float gk = lam * hprev * a[k];
                         dA_part = fmaf(gk, dt[k], dA_part);
