@@ -7,6 +7,9 @@
 
 `stats` turns a `--kernel-trace --stats` kernel_stats.csv into a short markdown table.
 
+`counters` turns `--pmc SQ_...` counter_collection.csv files (one per pass) into a per-kernel
+table: the mean per dispatch of each counter and the ratios that say what bounds a kernel.
+
 `traffic` reads two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` counter_collection.csv files (KiB
 per dispatch), takes the largest `copyBuffer` dispatch of the run (a plain device-to-device
 copy of --copy-mib MiB that the bench makes before its steps) as the calibration of each
@@ -124,6 +127,59 @@ def traffic(fetch_csv, write_csv, out, kernel, copy_mib, workload, cmd_fetch, cm
         fh.write("\n".join(lines) + "\n")
 
 
+def counters(csv_paths, out, selects, commands, clock_ghz=2.4, simds=1024):
+    """Per selected kernel: mean per dispatch of every counter, and derived ratios.  SQ cycle
+    counters are in quad-cycles (4 clocks), summed over the wavefronts; `simds` and
+    `clock_ghz` turn them into a share of the SIMDs' time over the dispatch's duration."""
+    vals = {n: defaultdict(lambda: defaultdict(float)) for n, _ in selects}
+    durs = {n: {} for n, _ in selects}
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            name = next((n for n, sub in selects if sub in r["Kernel_Name"]), None)
+            if name is None:
+                continue
+            key = (path, r["Dispatch_Id"])
+            vals[name][r["Counter_Name"]][key] += float(r["Counter_Value"])
+            durs[name][key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    lines = [f"# rocprofv3 SQ counters: {os.path.basename(out)}", "",
+             "Commands (from the repository root on the GPU host), one pass each:", "", "```",
+             *commands, "```", "",
+             "Mean per dispatch.  Cycle counters are quad-cycles summed over the wavefronts; "
+             f"the SIMD shares assume {simds} SIMDs at {clock_ghz} GHz over the profiled "
+             "dispatch's duration (which the profiler lengthens a little).", ""]
+    for name, sub in selects:
+        v = {c: statistics.mean(d.values()) for c, d in vals[name].items()}
+        if not v:
+            continue
+        dur = statistics.mean(durs[name].values())
+        lines += [f"## {name}", "", f"dispatches matching `{sub}`, mean duration "
+                  f"{dur * 1e6:.1f} us", "", "| counter | per dispatch |", "|---|---:|"]
+        lines += [f"| {c} | {x:.4g} |" for c, x in sorted(v.items())]
+        waves = v.get("SQ_WAVES")
+        quad = simds * dur * clock_ghz * 1e9 / 4.0
+        derived = []
+        if waves and "SQ_INSTS_VALU" in v:
+            derived.append(("VALU instructions per wavefront", v["SQ_INSTS_VALU"] / waves))
+        if "SQ_ACTIVE_INST_VALU" in v and "SQ_INSTS_VALU" in v:
+            derived.append(("quad-cycles per VALU instruction",
+                            v["SQ_ACTIVE_INST_VALU"] / v["SQ_INSTS_VALU"]))
+        if "SQ_ACTIVE_INST_VALU" in v:
+            derived.append(("share of SIMD time issuing VALU", v["SQ_ACTIVE_INST_VALU"] / quad))
+        if "SQ_ACTIVE_INST_VALU2" in v:
+            derived.append(("share of SIMD time dual-issuing VALU",
+                            v["SQ_ACTIVE_INST_VALU2"] / quad))
+        for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_LDS"):
+            if c in v and v.get("SQ_WAVE_CYCLES"):
+                derived.append((f"{c} / SQ_WAVE_CYCLES", v[c] / v["SQ_WAVE_CYCLES"]))
+        if derived:
+            lines += ["", "| derived | value |", "|---|---:|"]
+            lines += [f"| {k} | {x:.3f} |" if x < 100 else f"| {k} | {x:.0f} |"
+                      for k, x in derived]
+        lines.append("")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -143,8 +199,17 @@ def main():
     t.add_argument("--workload", required=True)
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
+    k = sub.add_parser("counters")
+    k.add_argument("csv", nargs="+")
+    k.add_argument("--out", required=True)
+    k.add_argument("--select", action="append", required=True,
+                   help="NAME=SUBSTRING of the dispatch names to summarise (repeatable)")
+    k.add_argument("--command", action="append", required=True,
+                   help="the command of each pass (repeatable)")
     a = ap.parse_args()
-    if a.cmd == "stats":
+    if a.cmd == "counters":
+        counters(a.csv, a.out, [tuple(x.split("=", 1)) for x in a.select], a.command)
+    elif a.cmd == "stats":
         stats(a.csv, a.out, a.command)
     else:
         traffic(a.fetch_csv, a.write_csv, a.out, a.kernel, a.copy_mib, a.workload,
