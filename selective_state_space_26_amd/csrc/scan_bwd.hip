@@ -296,8 +296,12 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int b = blockIdx.z;
-    const int c = blockIdx.y;
+    // one-dimensional grid over (batch row, chunk, channel group), channel groups fastest
+    const int cgroups = static_cast<int>(gridDim.x) / (p.B * p.nchunks);
+    const int bc_ = static_cast<int>(blockIdx.x) / cgroups;
+    const int cgrp = static_cast<int>(blockIdx.x) - bc_ * cgroups;
+    const int b = bc_ / p.nchunks;
+    const int c = bc_ - b * p.nchunks;
     const int N = p.N;
     const int L = p.L;
     const int nch = p.nchunks;
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     // raw input rows of the channel about to start, fetched ahead of time
     Raw<T, K> ru, rd, rg, rz;
     Raw<T, K> rl;  // TRAP: lambda (unused otherwise)
-    const int d_first = blockIdx.x * per_wave * W + wave;
+    const int d_first = cgrp * per_wave * W + wave;
     if (d_first < p.D) {
         const size_t row = chan_row(d_first);
         load_raw<T, K, VEC>(gu + row, t0, L, ru);
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     }
 
     for (int r = 0; r < per_wave; ++r) {
-        const int d = (blockIdx.x * per_wave + r) * W + wave;
+        const int d = (cgrp * per_wave + r) * W + wave;
         const bool active = d < p.D;  // wave-uniform; inactive waves still run the protocol
         const bool next_active = (r + 1 < per_wave) && (d + W < p.D);
         const int dd_ = active ? d : 0;
@@ -823,7 +827,9 @@ hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hi
         reinterpret_cast<const void*>(&bwd_main_kernel<T, VEC, HAS_Z, SP, TRAP>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(main_lds_bytes_max(W)));
     if (attr != hipSuccess) return attr;
-    dim3 mgrid(cgroups, p.nchunks, p.B), mblock(64 * W);
+    const long long mblocks = static_cast<long long>(cgroups) * p.nchunks * p.B;
+    if (mblocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    dim3 mgrid(static_cast<unsigned>(mblocks)), mblock(64 * W);
     if (tm.begin != nullptr && (e = hipEventRecord(tm.begin, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_main_kernel<T, VEC, HAS_Z, SP, TRAP>), mgrid, mblock, lds, s, p, g,
                        w, per_wave);

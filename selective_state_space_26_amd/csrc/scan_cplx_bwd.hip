@@ -291,8 +291,12 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
     const int lane = lane_id();
     const int W = static_cast<int>(blockDim.x >> 6);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int b = blockIdx.z;
-    const int c = blockIdx.y;
+    // one-dimensional grid over (batch row, chunk, channel group), channel groups fastest
+    const int cgroups = static_cast<int>(gridDim.x) / (p.B * p.nchunks);
+    const int bc_ = static_cast<int>(blockIdx.x) / cgroups;
+    const int cgrp = static_cast<int>(blockIdx.x) - bc_ * cgroups;
+    const int b = bc_ / p.nchunks;
+    const int c = bc_ - b * p.nchunks;
     const int N = p.N;
     const int J = N / 2;
     const int L = p.L;
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
 
     // raw input rows of the channel about to start, fetched ahead of time
     Raw<T, K> ru, rd, rg, rz;
-    const int d_first = blockIdx.x * per_wave * W + wave;
+    const int d_first = cgrp * per_wave * W + wave;
     if (d_first < p.D) {
         const size_t row = chan_row(d_first);
         load_raw<T, K, VEC>(gu + row, t0, L, ru);
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
     }
 
     for (int r = 0; r < per_wave; ++r) {
-        const int d = (blockIdx.x * per_wave + r) * W + wave;
+        const int d = (cgrp * per_wave + r) * W + wave;
         const bool active = d < p.D;  // wave-uniform; inactive waves still run the protocol
         const bool next_active = (r + 1 < per_wave) && (d + W < p.D);
         const int dd_ = active ? d : 0;
@@ -729,7 +733,9 @@ hipError_t cplx_bwd_go(const ScanParams& p, const GradParams& g, const CWork& w,
         reinterpret_cast<const void*>(&cplx_main_kernel<T, VEC, HAS_Z, SP>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ring_lds_bytes_max()));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((cplx_main_kernel<T, VEC, HAS_Z, SP>), dim3(cgroups, p.nchunks, p.B),
+    const long long mblocks = static_cast<long long>(cgroups) * p.nchunks * p.B;
+    if (mblocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((cplx_main_kernel<T, VEC, HAS_Z, SP>), dim3(static_cast<unsigned>(mblocks)),
                        dim3(64 * W), ring_lds_bytes(p.N), s, p, g, w, static_cast<int>(per));
     return hipGetLastError();
 }
