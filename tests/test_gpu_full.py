@@ -113,3 +113,55 @@ def test_tiny_workload_exact_oracle():
                    v["bias"])
     for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias"):
         assert_close(k, host(g[k]), r[k], "f32")
+
+
+def _time_window(t, lo, hi):
+    """float32 values of the problem restricted to steps [lo, hi), from a zero state."""
+    sub = {}
+    for name in ("u", "delta", "z", "dout", "B", "C"):
+        v = t.get(name)
+        sub[name] = None if v is None else msel_inputs.bf16_bits_to_f32(v[..., lo:hi]) \
+            if v.dtype == np.uint16 else v[..., lo:hi]
+    for name in ("A", "D", "bias"):
+        sub[name] = t.get(name)
+    return sub
+
+
+def test_sequence_beyond_65535_chunks():
+    """Batch 1, 2 channels, dstate 2, 65536 whole chunks and a ragged one: the chunk index runs
+    past the 65535 limit of a y or z grid dimension, in the launch configuration of the
+    benchmark (chunk states from the forward, no dh0).  With Delta near 2 and A = -(n+1) a
+    state forgets its past within a few dozen steps (a factor below 0.4 per step), so the
+    oracle run on a window with a margin of 128 steps on each side, from a zero state, gives
+    the outputs and gradients inside the window to far below the tolerance.  Windows sit at
+    the start, around chunks 65535 and 65536 and at the end.  dD, a sum over every step, is
+    checked against its definition sum_t dout_t silu(z_t) u_t over the whole sequence."""
+    L = 65536 * T + 300
+    log(f"long sequence L={L}")
+    t = msel_inputs.make(1, 2, 2, L, "bf16", 77, with_dout=True)
+    t["bias"] = np.full(2, 2.0, dtype=np.float32)
+    dv = to_device(t)
+    out, fin, cs = msel.msel_scan_fwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["D"],
+                                      dv["z"], dv["bias"], True, return_chunk_states=True)
+    g = msel.msel_scan_bwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["dout"], dv["D"],
+                           dv["z"], dv["bias"], True, chunk_states=cs)
+    torch.cuda.synchronize()
+    M = 128
+    for s, e in ((0, 1024), (65535 * T - 700, 65536 * T + 700), (L - 1200, L)):
+        lo, hi = max(0, s - M), min(L, e + M)
+        w = _time_window(t, lo, hi)
+        ro, rf = oracle.fwd(w["u"], w["delta"], w["A"], w["B"], w["C"], w["D"], w["z"],
+                            w["bias"])
+        r = oracle.bwd(w["u"], w["delta"], w["A"], w["B"], w["C"], w["dout"], w["D"], w["z"],
+                       w["bias"])
+        i0, i1 = s - lo, e - lo
+        assert_close(f"out[{s}:{e}]", host(out[..., s:e]), ro[..., i0:i1], "bf16")
+        for k in ("du", "ddelta", "dz", "dB", "dC"):
+            assert_close(f"{k}[{s}:{e}]", host(g[k][..., s:e]), r[k][..., i0:i1], "bf16")
+        if e == L:
+            assert_close("final_state", host(fin), rf, "bf16")
+    u = msel_inputs.bf16_bits_to_f32(t["u"]).astype(np.float64)
+    z = msel_inputs.bf16_bits_to_f32(t["z"]).astype(np.float64)
+    go = msel_inputs.bf16_bits_to_f32(t["dout"]).astype(np.float64)
+    dD = np.sum(go * z / (1.0 + np.exp(-z)) * u, axis=(0, 2))
+    assert_close("dD", host(g["dD"]), dD, "bf16")
