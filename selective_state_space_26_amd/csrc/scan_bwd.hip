@@ -16,10 +16,10 @@
 //
 // Three launches, all parallel over chunks:
 //  1. summary: one wavefront per (batch, chunk, few channels).  For every state n it forms
-//     the chunk's local end state from a zero start (forward) and the adjoint at the chunk's
-//     first step from a zero adjoint beyond the chunk (reverse), both with lane-local chains
-//     and DPP row scans finished through readlane, plus sum(Delta) and Delta at the first
-//     step.
+//     the chunk's local end state from a zero start and the adjoint at the chunk's first step
+//     from a zero adjoint beyond the chunk, in closed form from prefix sums of Delta (see the
+//     kernel), plus sum(Delta) and Delta at the first step.  With the chunk states given only
+//     the adjoint is formed, and chunk 0 is skipped unless dh0 is asked for.
 //  2. link: one thread per (batch, channel, state) walks the chunks:
 //       H_{c+1} = exp(A sum Delta_c) H_c + S_c                      (H_0 = h0)
 //       G_{c-1} = exp(A sum Delta_c) G_c + exp(A Delta_first_c) Sr_c (G_last = 0)
@@ -28,8 +28,9 @@
 //     run once forward for the states and once backward for the adjoint.)
 //  3. main: about one workgroup per compute unit, each on one (batch row, chunk) and a range
 //     of channels; B and C of that chunk are staged in LDS once.  Each wavefront takes one
-//     channel at a time: the states inside the chunk are rebuilt from H_c, the adjoint from
-//     G_c, and every gradient term is formed in registers.  dB and dC, which sum over
+//     channel at a time: the states inside the chunk are rebuilt from H_c (lane chains and a
+//     forward DPP scan), the adjoint from G_c (lane chains and the same scan in reversed lane
+//     order), and every gradient term is formed in registers.  dB and dC, which sum over
 //     channels, are accumulated over all the workgroup's channels in LDS and written to HBM
 //     once per workgroup with fp32 global atomics.  LDS float atomics are avoided (they run at
 //     a small fraction of the plain LDS rate on this chip): the wavefronts visit the states

@@ -70,25 +70,6 @@ __device__ __forceinline__ void cplx_level(float& Pr, float& Pi, float& Sr, floa
     Si = nSi;
 }
 
-// Inclusive prefix composition over the 64 lanes (lane 0 applied first).
-__device__ __forceinline__ void cplx_scan_fwd(float& Pr, float& Pi, float& Sr, float& Si) {
-    cplx_level<kRowShr1, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowShr2, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowShr4, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowShr8, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowBcast15, 0xa>(Pr, Pi, Sr, Si);
-    cplx_level<kRowBcast31, 0xc>(Pr, Pi, Sr, Si);
-}
-
-// Inclusive suffix composition inside each 16-lane row (the row's last lane applied first):
-// afterwards lane 16r holds the composition of its whole row.
-__device__ __forceinline__ void cplx_scan_rev_rows(float& Pr, float& Pi, float& Sr, float& Si) {
-    cplx_level<kRowShl1, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowShl2, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowShl4, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowShl8, 0xf>(Pr, Pi, Sr, Si);
-}
-
 __device__ __forceinline__ void cmul(float ar, float ai, float br, float bi, float& r, float& i) {
     r = fmaf(ar, br, -ai * bi);
     i = fmaf(ar, bi, ai * br);

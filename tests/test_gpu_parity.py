@@ -94,6 +94,7 @@ BWD_CASES = [
     (2, 13, 11, 700, "f32", True, True, True, True),    # dstate 11: the largest LDS need
     (1, 25, 10, 1030, "bf16", True, True, True, False), # two accumulator groups, ragged tail
     (2, 7, 16, 1000, "bf16", True, True, True, True),   # 16-byte rows, ragged last chunk
+    (1, 1, 1, 777, "bf16", True, True, True, True),     # dstate 1, one channel: 12 ring groups
 ]
 
 
@@ -357,3 +358,20 @@ def test_decode_step_replays_from_a_hip_graph():
         _ = host(out).sum()  # host work between replays
         assert torch.equal(out, eager_outs[k]), k
     assert torch.equal(state, eager_state)
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 0), (1, 0, 8), (0, 2, 8)])
+def test_empty_problem_is_an_error(shape):
+    """No steps, no channels or no batch rows: the library rejects the call before any launch
+    (an empty problem is a shape error, not a silent no-op), and the binding raises."""
+    log(f"empty {shape}")
+    bsz, dim, L = shape
+    N = 4
+    dev = torch.device("cuda")
+    u = torch.zeros(shape, device=dev)
+    A = -torch.ones(dim, N, device=dev)
+    Bm = torch.zeros(bsz, N, L, device=dev)
+    with pytest.raises((ValueError, RuntimeError)):
+        msel.msel_scan_fwd(u, u.clone(), A, Bm, Bm.clone(), None, None, None, True)
+    with pytest.raises((ValueError, RuntimeError)):
+        msel.msel_scan_bwd(u, u.clone(), A, Bm, Bm.clone(), u.clone(), None, None, None, True)
