@@ -1,0 +1,108 @@
+"""Every forward + backward pair only enqueues kernels (zero-fills included, no allocation
+and no host synchronisation inside the library), so a whole training step of each variant can
+be captured in a HIP graph.  Three replays, each after the outputs were overwritten with NaN
+and followed by host work and a synchronisation, must match the eager step: bit for bit where
+each output element is written by one thread, and to fp32 rounding where fp32 atomics sum
+over channels or time (their order varies from run to run)."""
+import numpy as np
+import pytest
+
+import msel_inputs
+from helpers import host, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import selective_state_space_26_amd as msel  # noqa: E402
+
+SHAPE = (2, 6, 16, 1100)  # three chunks, ragged tail
+
+
+def _scan():
+    t = msel_inputs.make(*SHAPE, "bf16", 31, with_dout=True)
+    d = to_device(t)
+    a = (d["u"], d["delta"], d["A"], d["B"], d["C"])
+    o = (d["D"], d["z"], d["bias"], True)
+
+    def step():
+        out, fin, cs = msel.msel_scan_fwd(*a, *o, return_chunk_states=True)
+        g = msel.msel_scan_bwd(*a, d["dout"], *o, chunk_states=cs)
+        return dict(out=out, fin=fin, **g)
+    return step, ("out", "fin", "du", "ddelta", "dz"), ("dA", "dB", "dC", "dD", "ddelta_bias")
+
+
+def _trap():
+    t = msel_inputs.make(*SHAPE, "bf16", 32, with_dout=True, with_lam=True, with_prev=True,
+                         with_h0=True)
+    d = to_device(t)
+    a = (d["u"], d["delta"], d["lam"], d["A"], d["B"], d["C"])
+    o = (d["D"], d["z"], d["bias"], True, d["h0"], d["u_prev"], d["B_prev"])
+
+    def step():
+        out, fin, cs = msel.msel_scan_trap_fwd(*a, *o, return_chunk_states=True)
+        g = msel.msel_scan_trap_bwd(*a, d["dout"], cs, *o, want_dh0=True, want_dprev=True)
+        return dict(out=out, fin=fin, **g)
+    return (step, ("out", "fin", "du", "ddelta", "dz", "dlam", "dh0", "du_prev"),
+            ("dA", "dB", "dC", "dD", "ddelta_bias", "dB_prev"))
+
+
+def _complex():
+    t = msel_inputs.make(*SHAPE, "bf16", 33, with_dout=True, complex_A=True)
+    d = to_device(t)
+    a = (d["u"], d["delta"], d["A"], d["B"], d["C"])
+    o = (d["D"], d["z"], d["bias"], True)
+
+    def step():
+        out, fin, cs = msel.msel_scan_complex_fwd(*a, *o, return_chunk_states=True)
+        g = msel.msel_scan_complex_bwd(*a, d["dout"], cs, *o)
+        return dict(out=out, fin=fin, **g)
+    return step, ("out", "fin", "du", "ddelta", "dz"), ("dA", "dB", "dC", "dD", "ddelta_bias")
+
+
+def _conv():
+    t = msel_inputs.make_conv(2, 6, 1100, 4, "bf16", 34, with_state=True, with_dout=True)
+    d = to_device(t)
+
+    def step():
+        out, st = msel.msel_conv1d_fwd(d["x"], d["weight"], d["bias"], d["state"], True,
+                                       return_state=True)
+        g = msel.msel_conv1d_bwd(d["x"], d["weight"], d["dout"], d["bias"], d["state"], True,
+                                 want_dstate=True)
+        return dict(out=out, state_out=st, **g)
+    return step, ("out", "state_out", "dx", "dstate"), ("dweight", "dbias")
+
+
+@pytest.mark.parametrize("variant", ["scan", "trap", "complex", "conv"])
+def test_training_step_replays_from_a_hip_graph(variant):
+    log(f"graph {variant}")
+    step, exact, summed = {"scan": _scan, "trap": _trap, "complex": _complex, "conv": _conv}[variant]()
+    eager = step()
+    torch.cuda.synchronize()
+    for n in exact + summed:
+        assert eager[n] is not None, n
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        step()  # warm up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            cap = step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for k in range(3):
+        for n in exact + summed:
+            cap[n].fill_(float("nan"))  # every replay must write all of it again
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = host(cap[exact[0]]).sum()  # host work between replays
+        for n in exact:
+            assert torch.equal(cap[n], eager[n]), (k, n)
+        for n in summed:
+            a, b = host(cap[n]), host(eager[n])
+            assert np.all(np.isfinite(a)), (k, n)
+            assert np.max(np.abs(a - b)) <= 1e-5 * np.max(np.abs(b)), (k, n)
