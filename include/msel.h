@@ -28,7 +28,8 @@
  *    calls, is re-entrant, and never synchronizes: work is enqueued on `stream` and the
  *    call returns.  Errors in the arguments are detected on the host before anything is
  *    enqueued; the return value is then not MSEL_OK and no device memory is touched.
- *  - Inputs are read-only.  Outputs must not be the same pointer as any input (checked).
+ *  - Inputs are read-only.  Outputs must not be the same pointer as any input (checked),
+ *    except where a field says otherwise (a state updated in place).
  *  - Layouts:
  *      u, delta, z, out                  [batch, dim, seqlen]     activation dtype
  *      B, C                              [batch, dstate, seqlen]  activation dtype
