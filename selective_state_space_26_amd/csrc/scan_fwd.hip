@@ -35,14 +35,46 @@
 
 namespace msel {
 
+// Channels of one batch row per workgroup: with the stage (below), the more share it, the
+// fewer conversions and L2 reads of B and C per channel.
+constexpr int kFwdStageWaves = 4;
+template <typename T, bool TRAP>
+__host__ __device__ constexpr int fwd_waves() { return sizeof(T) == 2 && !TRAP ? kFwdStageWaves : 4; }
+
+// STAGE (bf16 rows, plain rule): a state's B and C rows over a tile are converted to fp32 once
+// per workgroup, into LDS, and read by each of its wavefronts, instead of being converted by
+// every wavefront: [2 tensors][K/4 words][64 lanes] of 16-byte words, so that a lane's K
+// steps are K/4 words of its own column and the 64 lanes read consecutive words.  Two
+// buffers: the next state's rows are staged while the current one is computed, with one
+// barrier per state.  (The trapezoidal rule and fp32 rows load B and C per wavefront: the
+// fp32 rows would hold twice the registers, and these instantiations have none to spare.)
 template <typename T, int K, bool VEC, bool HAS_Z, bool SOFTPLUS, bool TRAP>
-__global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
+__global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(ScanParams p) {
+    constexpr bool STAGE = sizeof(T) == 2 && !TRAP;
+    constexpr int kFwdWaves = fwd_waves<T, TRAP>();
+    constexpr int QW = K / 4;                           // 16-byte words per lane and row
+    constexpr int VW = Elem<T>::kPerVec;                // elements per 16-byte vector
+    constexpr int NTH = 64 * kFwdWaves;
+    constexpr int NVEC = 2 * 64 * K / VW;               // staged vectors per state (B and C)
+    constexpr int G = STAGE ? (NVEC + NTH - 1) / NTH : 1;  // per thread (the last round of a
+                                                           // workgroup wider than NVEC is partial)
+    static_assert(!STAGE || (K % VW == 0 && (64 * K / VW) % 64 == 0 && NVEC % 64 == 0),
+                  "a row of the stage must split over whole wavefronts");
+    __shared__ f32x4 stage[STAGE ? 2 : 1][STAGE ? 2 * QW * 64 : 1];
+    const int tid = threadIdx.x;
     const int lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int ch = blockIdx.x * (blockDim.x >> 6) + wave;  // b * D + d
-    if (ch >= p.B * p.D) return;  // whole wavefront leaves; this kernel has no barriers
-    const int b = ch / p.D;
-    const int d = ch - b * p.D;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // one-dimensional grid over (batch row, group of channels), channel groups fastest
+    const int ngrp = (p.D + kFwdWaves - 1) / kFwdWaves;
+    const int b = static_cast<int>(blockIdx.x) / ngrp;
+    const int dw = (static_cast<int>(blockIdx.x) - b * ngrp) * kFwdWaves + wave;
+    // wave-uniform.  Without the stage a wavefront past the last channel leaves (no barriers
+    // then); with it, it computes channel D-1 again (its addresses stay valid), takes part in
+    // the staging and the barriers, and stores nothing.
+    const bool active = dw < p.D;
+    if (!STAGE && !active) return;
+    const int d = active ? dw : p.D - 1;
+    const int ch = b * p.D + d;
     const int L = p.L;
     const int N = p.N;
     const size_t row = static_cast<size_t>(ch) * L;
@@ -69,6 +101,56 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
 
     constexpr int TILE = 64 * K;
     static_assert(TILE % kChunk == 0, "a tile must hold whole chunks");
+
+    // staging: thread tid moves vectors v = tid + i * NTH of the state's [B row, C row] over
+    // the tile (TILE / VW vectors per row)
+    Raw<T, VW> nxt[G];
+    auto stage_load = [&](int tile, int n) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int v = tid + i * NTH;
+            if (NVEC % NTH != 0 && v >= NVEC) break;  // wave-uniform (NVEC, NTH: multiples of 64)
+            // B or C: the same for the whole wavefront (a row is a multiple of 64 vectors)
+            const int x = __builtin_amdgcn_readfirstlane(v / (TILE / VW));
+            const int tl = (v - x * (TILE / VW)) * VW;
+            load_raw<T, VW, VEC>((x == 0 ? Bb : Cb) + static_cast<size_t>(n) * L, tile + tl, L,
+                                 nxt[i]);
+        }
+    };
+    auto stage_store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int v = tid + i * NTH;
+            if (NVEC % NTH != 0 && v >= NVEC) break;
+            const int x = v / (TILE / VW);
+            const int tl = (v - x * (TILE / VW)) * VW;
+            float f[VW];
+            unpack<T, VW>(nxt[i], f);
+            const int l = tl / K, q0 = (tl - l * K) / 4;
+#pragma unroll
+            for (int j = 0; j < VW / 4; ++j)
+                stage[buf][(x * QW + q0 + j) * 64 + l] =
+                    f32x4{f[4 * j], f[4 * j + 1], f[4 * j + 2], f[4 * j + 3]};
+        }
+    };
+    // a state's row of B (x = 0) or C (x = 1) for the lane's K steps
+    auto stage_read = [&](int buf, int x, float (&r)[K]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < QW; ++q) {
+            const f32x4 w4 = stage[buf][(x * QW + q) * 64 + lane];
+            r[4 * q] = w4[0];
+            r[4 * q + 1] = w4[1];
+            r[4 * q + 2] = w4[2];
+            r[4 * q + 3] = w4[3];
+        }
+    };
+    int buf = 0;
+    if constexpr (STAGE) {
+        stage_load(0, 0);
+        stage_store(0);
+        __syncthreads();
+    }
+
     for (int tile = 0; tile < L; tile += TILE) {
         const int t0 = tile + lane * K;
         float dt[K], du[K], y[K];
@@ -107,9 +189,13 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
         for (int q = 0; q < kCpt; ++q) csv[q] = 0.0f;
 
         for (int n = 0; n < N; ++n) {
+            // the next state's rows (the next tile's first state after the last one)
+            const bool more = STAGE && ((n + 1 < N) || (tile + TILE < L));
+            if (more) stage_load(n + 1 < N ? tile : tile + TILE, n + 1 < N ? n + 1 : 0);
             const float An = readlane(Av, n);
             float a[K], bb[K], bc[K];
-            load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, bc);
+            if constexpr (STAGE) stage_read(buf, 0, bc);
+            else load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, bc);
             float bprev0 = 0.0f;  // TRAP: B_{n} of the step before the lane's first
             if constexpr (TRAP) {
                 bprev0 = shift_up(bc[K - 1], readlane(B_last, n));
@@ -136,12 +222,18 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
             for (int q = 0; q < kCpt; ++q)
                 csv[q] = writelane(readlane(hin, q * (kChunk / K)), n, csv[q]);
 
-            load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n) * L, t0, L, bc);
+            if constexpr (STAGE) stage_read(buf, 1, bc);
+            else load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n) * L, t0, L, bc);
             h = hin;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 h = fmaf(a[k], h, bb[k]);
                 y[k] = fmaf(bc[k], h, y[k]);
+            }
+            if constexpr (STAGE) {
+                if (more) stage_store(buf ^ 1);
+                __syncthreads();
+                buf ^= 1;
             }
         }
         if constexpr (HAS_Z) {
@@ -150,8 +242,8 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
 #pragma unroll
             for (int k = 0; k < K; ++k) y[k] *= zz[k] * sigmoid_f(zz[k]);
         }
-        store_k<T, K, VEC, false>(out, t0, L, y);
-        if (p.chunk_states != nullptr && lane < N) {
+        if (active) store_k<T, K, VEC, false>(out, t0, L, y);
+        if (active && p.chunk_states != nullptr && lane < N) {
 #pragma unroll
             for (int q = 0; q < kCpt; ++q) {
                 const int cidx = tile / kChunk + q;
@@ -161,7 +253,7 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanParams p) {
             }
         }
     }
-    if (p.final_state != nullptr && lane < N)
+    if (active && p.final_state != nullptr && lane < N)
         p.final_state[static_cast<size_t>(ch) * N + lane] = carry;
 }
 
@@ -231,17 +323,20 @@ __global__ __launch_bounds__(256) void scan_step_kernel(ScanParams p) {
 
 namespace {
 
-constexpr int kFwdWaves = 4;
+template <typename T, int K, bool VEC, bool HAS_Z, bool SP, bool TRAP>
+hipError_t fwd_launch(const ScanParams& p, hipStream_t s) {
+    // a workgroup per (batch row, W channels): its wavefronts share B and C
+    constexpr int W = fwd_waves<T, TRAP>();
+    const long long groups = static_cast<long long>(p.B) * ((p.D + W - 1) / W);
+    hipLaunchKernelGGL((scan_fwd_kernel<T, K, VEC, HAS_Z, SP, TRAP>),
+                       dim3(static_cast<unsigned>(groups)), dim3(64 * W), 0, s, p);
+    return hipGetLastError();
+}
 
 template <typename T, int K, bool VEC, bool HAS_Z, bool SP>
 hipError_t fwd_go(const ScanParams& p, hipStream_t s) {
-    const int ch = p.B * p.D;
-    dim3 grid((ch + kFwdWaves - 1) / kFwdWaves), block(64 * kFwdWaves);
-    if (p.lam != nullptr)
-        hipLaunchKernelGGL((scan_fwd_kernel<T, K, VEC, HAS_Z, SP, true>), grid, block, 0, s, p);
-    else
-        hipLaunchKernelGGL((scan_fwd_kernel<T, K, VEC, HAS_Z, SP, false>), grid, block, 0, s, p);
-    return hipGetLastError();
+    if (p.lam != nullptr) return fwd_launch<T, K, VEC, HAS_Z, SP, true>(p, s);
+    return fwd_launch<T, K, VEC, HAS_Z, SP, false>(p, s);
 }
 
 template <typename T, int K>
