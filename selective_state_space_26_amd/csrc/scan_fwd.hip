@@ -17,6 +17,10 @@
 //     pass 2  replay the chain from that state, y_k += C_{n,k} h_k
 //   epilogue: y += D u (initialised up front), out = y * silu(z), one store.
 //
+// A workgroup holds four channels of one batch row, which share B and C: in bf16 their rows of
+// each state are converted to fp32 once per workgroup into a double-buffered LDS stage (see the
+// kernel) and read from there by every wavefront.
+//
 // The state never leaves registers: the carried state of all N states lives in one VGPR
 // (lane n holds h_n), so long sequences are handled by the tile loop with the state carried
 // across tiles (page 4, Appendix D: split the sequence into chunks, continue the scan from the
