@@ -221,6 +221,67 @@ __device__ __forceinline__ void unpack(const Raw<T, K>& r, float (&v)[K]) {
     for (int j = 0; j < Raw<T, K>::kVecs; ++j) unpack_vec<T, K>(r.v[j], j, v);
 }
 
+// Rows of one tile (64*K steps) staged in LDS as fp32 by a whole workgroup of NTH threads and
+// read by each of its wavefronts: for rows shared by the workgroup's channels (B and C of one
+// batch row), which are then loaded and converted once per workgroup instead of once per
+// wavefront.  A buffer is [ROWS rows][K/4 words][64 lanes] of 16-byte words, so that lane l
+// reads its K steps of a row as K/4 words of its own column, the 64 lanes consecutive words.
+// load() issues the global loads of one set of rows into registers (thread tid moves vectors
+// tid, tid + NTH, ...; a row is a whole number of wavefronts' vectors, so which row a vector
+// belongs to is wave-uniform); store() converts them into a buffer; read() gives a lane its K
+// values of one row.  The caller separates a store and the reads of the same buffer by a
+// workgroup barrier.
+template <typename T, int K, int ROWS, int NTH, bool VEC>
+struct TileStage {
+    static constexpr int QW = K / 4;                 // 16-byte words per lane and row
+    static constexpr int VW = Elem<T>::kPerVec;      // elements per 16-byte vector
+    static constexpr int RV = 64 * K / VW;           // vectors per row
+    static constexpr int NVEC = ROWS * RV;
+    static constexpr int G = (NVEC + NTH - 1) / NTH; // vectors per thread (the last partial)
+    static constexpr int kWords = ROWS * QW * 64;    // 16-byte words per buffer
+    static_assert(K % VW == 0 && K % 4 == 0 && RV % 64 == 0 && NTH % 64 == 0,
+                  "a row must split over whole wavefronts");
+    Raw<T, VW> nxt[G];
+
+    // row(x): the global row that staged row x comes from; t_tile: the tile's first step
+    template <typename RowFn>
+    __device__ __forceinline__ void load(int tid, RowFn row, int t_tile, int L) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int v = tid + i * NTH;
+            if (NVEC % NTH != 0 && v >= NVEC) break;  // wave-uniform
+            const int x = __builtin_amdgcn_readfirstlane(v / RV);
+            load_raw<T, VW, VEC>(row(x), t_tile + (v - x * RV) * VW, L, nxt[i]);
+        }
+    }
+    __device__ __forceinline__ void store(int tid, f32x4* __restrict__ buf) const {
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int v = tid + i * NTH;
+            if (NVEC % NTH != 0 && v >= NVEC) break;
+            const int x = v / RV;
+            const int tl = (v - x * RV) * VW;
+            float f[VW];
+            unpack<T, VW>(nxt[i], f);
+            const int l = tl / K, q0 = (tl - l * K) / 4;
+#pragma unroll
+            for (int j = 0; j < VW / 4; ++j)
+                buf[(x * QW + q0 + j) * 64 + l] = f32x4{f[4 * j], f[4 * j + 1], f[4 * j + 2], f[4 * j + 3]};
+        }
+    }
+    __device__ __forceinline__ static void read(const f32x4* __restrict__ buf, int x, int lane,
+                                                float (&r)[K]) {
+#pragma unroll
+        for (int q = 0; q < QW; ++q) {
+            const f32x4 w4 = buf[(x * QW + q) * 64 + lane];
+            r[4 * q] = w4[0];
+            r[4 * q + 1] = w4[1];
+            r[4 * q + 2] = w4[2];
+            r[4 * q + 3] = w4[3];
+        }
+    }
+};
+
 // ---------------------------------------------------------------------------------------
 // Cross-lane moves.
 

@@ -56,15 +56,8 @@ template <typename T, int K, bool VEC, bool HAS_Z, bool SOFTPLUS, bool TRAP>
 __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(ScanParams p) {
     constexpr bool STAGE = sizeof(T) == 2 && !TRAP;
     constexpr int kFwdWaves = fwd_waves<T, TRAP>();
-    constexpr int QW = K / 4;                           // 16-byte words per lane and row
-    constexpr int VW = Elem<T>::kPerVec;                // elements per 16-byte vector
-    constexpr int NTH = 64 * kFwdWaves;
-    constexpr int NVEC = 2 * 64 * K / VW;               // staged vectors per state (B and C)
-    constexpr int G = STAGE ? (NVEC + NTH - 1) / NTH : 1;  // per thread (the last round of a
-                                                           // workgroup wider than NVEC is partial)
-    static_assert(!STAGE || (K % VW == 0 && (64 * K / VW) % 64 == 0 && NVEC % 64 == 0),
-                  "a row of the stage must split over whole wavefronts");
-    __shared__ f32x4 stage[STAGE ? 2 : 1][STAGE ? 2 * QW * 64 : 1];
+    using Stage = TileStage<T, K, 2, 64 * kFwdWaves, VEC>;  // rows: B, C of one state
+    __shared__ f32x4 stage[STAGE ? 2 : 1][STAGE ? Stage::kWords : 1];
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -106,52 +99,14 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
     constexpr int TILE = 64 * K;
     static_assert(TILE % kChunk == 0, "a tile must hold whole chunks");
 
-    // staging: thread tid moves vectors v = tid + i * NTH of the state's [B row, C row] over
-    // the tile (TILE / VW vectors per row)
-    Raw<T, VW> nxt[G];
-    auto stage_load = [&](int tile, int n) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const int v = tid + i * NTH;
-            if (NVEC % NTH != 0 && v >= NVEC) break;  // wave-uniform (NVEC, NTH: multiples of 64)
-            // B or C: the same for the whole wavefront (a row is a multiple of 64 vectors)
-            const int x = __builtin_amdgcn_readfirstlane(v / (TILE / VW));
-            const int tl = (v - x * (TILE / VW)) * VW;
-            load_raw<T, VW, VEC>((x == 0 ? Bb : Cb) + static_cast<size_t>(n) * L, tile + tl, L,
-                                 nxt[i]);
-        }
-    };
-    auto stage_store = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const int v = tid + i * NTH;
-            if (NVEC % NTH != 0 && v >= NVEC) break;
-            const int x = v / (TILE / VW);
-            const int tl = (v - x * (TILE / VW)) * VW;
-            float f[VW];
-            unpack<T, VW>(nxt[i], f);
-            const int l = tl / K, q0 = (tl - l * K) / 4;
-#pragma unroll
-            for (int j = 0; j < VW / 4; ++j)
-                stage[buf][(x * QW + q0 + j) * 64 + l] =
-                    f32x4{f[4 * j], f[4 * j + 1], f[4 * j + 2], f[4 * j + 3]};
-        }
-    };
-    // a state's row of B (x = 0) or C (x = 1) for the lane's K steps
-    auto stage_read = [&](int buf, int x, float (&r)[K]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int q = 0; q < QW; ++q) {
-            const f32x4 w4 = stage[buf][(x * QW + q) * 64 + lane];
-            r[4 * q] = w4[0];
-            r[4 * q + 1] = w4[1];
-            r[4 * q + 2] = w4[2];
-            r[4 * q + 3] = w4[3];
-        }
+    Stage st;
+    auto rows = [&](int n) {  // staged row x of state n: B (x = 0) or C (x = 1)
+        return [=](int x) { return (x == 0 ? Bb : Cb) + static_cast<size_t>(n) * L; };
     };
     int buf = 0;
     if constexpr (STAGE) {
-        stage_load(0, 0);
-        stage_store(0);
+        st.load(tid, rows(0), 0, L);
+        st.store(tid, stage[0]);
         __syncthreads();
     }
 
@@ -195,10 +150,10 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
         for (int n = 0; n < N; ++n) {
             // the next state's rows (the next tile's first state after the last one)
             const bool more = STAGE && ((n + 1 < N) || (tile + TILE < L));
-            if (more) stage_load(n + 1 < N ? tile : tile + TILE, n + 1 < N ? n + 1 : 0);
+            if (more) st.load(tid, rows(n + 1 < N ? n + 1 : 0), n + 1 < N ? tile : tile + TILE, L);
             const float An = readlane(Av, n);
             float a[K], bb[K], bc[K];
-            if constexpr (STAGE) stage_read(buf, 0, bc);
+            if constexpr (STAGE) Stage::read(stage[buf], 0, lane, bc);
             else load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, bc);
             float bprev0 = 0.0f;  // TRAP: B_{n} of the step before the lane's first
             if constexpr (TRAP) {
@@ -226,7 +181,7 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
             for (int q = 0; q < kCpt; ++q)
                 csv[q] = writelane(readlane(hin, q * (kChunk / K)), n, csv[q]);
 
-            if constexpr (STAGE) stage_read(buf, 1, bc);
+            if constexpr (STAGE) Stage::read(stage[buf], 1, lane, bc);
             else load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n) * L, t0, L, bc);
             h = hin;
 #pragma unroll
@@ -235,7 +190,7 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
                 y[k] = fmaf(bc[k], h, y[k]);
             }
             if constexpr (STAGE) {
-                if (more) stage_store(buf ^ 1);
+                if (more) st.store(tid, stage[buf ^ 1]);
                 __syncthreads();
                 buf ^= 1;
             }
