@@ -434,9 +434,12 @@ def main():
         "metric": METRIC, "value": float(f"{tc / (ms_per_step * 1e-3):.5g}"),
         "unit": "token*channels/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        # dtype: the arithmetic type of every step (state, transitions, sums); the activations
+        # are stored in io_dtype
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
-                   "seqlen": w.seqlen, "step": "fwd (with chunk-boundary states) + bwd"},
+                   "seqlen": w.seqlen, "io_dtype": w.dtype,
+                   "step": "fwd (with chunk-boundary states) + bwd"},
         "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
