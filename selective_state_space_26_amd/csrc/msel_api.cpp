@@ -142,7 +142,6 @@ msel_status run_bwd(const msel_scan_args* a, const msel_scan_grads* g, const mse
                                  {DN, BNL, BNL, static_cast<size_t>(a->dim),
                                   static_cast<size_t>(a->dim),
                                   static_cast<size_t>(a->batch) * a->dstate}};
-    if (msel::launch_fill_zero(fill, stream) != hipSuccess) return MSEL_ERR_HIP;
     msel::GradParams gp;
     gp.dout = g->dout;
     gp.du = g->du;
@@ -159,8 +158,8 @@ msel_status run_bwd(const msel_scan_args* a, const msel_scan_grads* g, const mse
         gp.du_prev = tg->du_prev;
         gp.dB_prev = tg->dB_prev;
     }
-    return hip_status(msel::launch_scan_bwd(p, gp, a->chunk_states, workspace, bf16, stream,
-                                            ev_begin, ev_end));
+    return hip_status(msel::launch_scan_bwd(p, gp, a->chunk_states, workspace, bf16, fill,
+                                            stream, ev_begin, ev_end));
 }
 
 }  // namespace
@@ -398,7 +397,6 @@ msel_status msel_scan_complex_bwd(const msel_scan_args* a, const msel_scan_grads
     const msel::FillList fill = {{g->dA, g->dB, g->dC, g->dD, g->ddelta_bias, nullptr},
                                  {DN, BNL, BNL, static_cast<size_t>(a->dim),
                                   static_cast<size_t>(a->dim), 0}};
-    if (msel::launch_fill_zero(fill, stream) != hipSuccess) return MSEL_ERR_HIP;
     msel::GradParams gp;
     gp.dout = g->dout;
     gp.du = g->du;
@@ -411,7 +409,7 @@ msel_status msel_scan_complex_bwd(const msel_scan_args* a, const msel_scan_grads
     gp.dbias = g->ddelta_bias;
     gp.dh0 = g->dh0;
     return hip_status(msel::launch_scan_cplx_bwd(to_params(a), gp, a->chunk_states, workspace,
-                                                 a->dtype == MSEL_BF16, stream));
+                                                 a->dtype == MSEL_BF16, fill, stream));
 }
 
 msel_status msel_scan_complex_fwd(const msel_scan_args* a, hipStream_t stream) {

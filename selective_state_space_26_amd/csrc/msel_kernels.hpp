@@ -56,25 +56,43 @@ hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_chunk_carry(const ScanParams& p, bool bf16, hipStream_t stream);
 // The complex-valued (rotational) forward: state pairs (2j, 2j+1) are complex states; N even.
 hipError_t launch_scan_cplx_fwd(const ScanParams& p, bool bf16, hipStream_t stream);
-// Its backward from the forward's chunk states (required); the workspace is laid out as the
-// real backward's with chunk states given (bwd_workspace_bytes(..., false)).
-hipError_t launch_scan_cplx_bwd(const ScanParams& p, const GradParams& g,
-                                const float* chunk_states, void* workspace, bool bf16,
-                                hipStream_t stream);
-// Backward: the summary/link passes write into `workspace` (bwd_workspace_bytes), then the
-// chunk-parallel main kernel.  chunk_states may be NULL (rebuilt in the workspace).
-size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states);
-// ev_begin / ev_end (either may be null) are recorded on `stream` right before and after the
-// gradient kernel, so that a caller can time it alone.
-hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float* chunk_states,
-                           void* workspace, bool bf16, hipStream_t stream,
-                           hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
-// Zero-fill of up to kFillSlots float buffers in one launch (null slots are skipped).
+// Buffers to zero before a backward's atomics (null slots are skipped).
 constexpr int kFillSlots = 6;
 struct FillList {
     float* p[kFillSlots];
     size_t n[kFillSlots];
 };
+// Grid-stride zero-fill of every slot by the threads of a launch (thread `tid` of `threads`).
+__device__ __forceinline__ void zero_fill(const FillList& f, size_t tid, size_t threads) {
+    for (int s = 0; s < kFillSlots; ++s) {
+        float* __restrict__ p = f.p[s];
+        if (p == nullptr) continue;
+        for (size_t i = tid; i < f.n[s]; i += threads) p[i] = 0.0f;
+    }
+}
+// Blocks of 256 threads for a grid-stride fill of `f` (at most 2048; 0 when there is nothing).
+inline unsigned fill_blocks(const FillList& f) {
+    size_t total = 0;
+    for (int s = 0; s < kFillSlots; ++s)
+        if (f.p[s] != nullptr) total += f.n[s];
+    const size_t b = (total + 255) / 256;
+    return static_cast<unsigned>(b > 2048 ? 2048 : b);
+}
+// Its backward from the forward's chunk states (required); the workspace is laid out as the
+// real backward's with chunk states given (bwd_workspace_bytes(..., false)).
+hipError_t launch_scan_cplx_bwd(const ScanParams& p, const GradParams& g,
+                                const float* chunk_states, void* workspace, bool bf16,
+                                const FillList& fill, hipStream_t stream);
+// Backward: the summary/link passes write into `workspace` (bwd_workspace_bytes), then the
+// chunk-parallel main kernel.  chunk_states may be NULL (rebuilt in the workspace).
+size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states);
+// ev_begin / ev_end (either may be null) are recorded on `stream` right before and after the
+// gradient kernel, so that a caller can time it alone.
+// `fill`: the reduction targets the gradient kernel adds into, zeroed by the link launch.
+hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float* chunk_states,
+                           void* workspace, bool bf16, const FillList& fill, hipStream_t stream,
+                           hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
+// Zero-fill of up to kFillSlots float buffers in one launch (null slots are skipped).
 hipError_t launch_fill_zero(const FillList& f, hipStream_t stream);
 
 // Division of a 31-bit unsigned value by a fixed divisor d >= 1 with one multiply-high, an add

@@ -25,7 +25,8 @@
 //       G_{c-1} = exp(A sum Delta_c) G_c + exp(A Delta_first_c) Sr_c (G_last = 0)
 //     H_c is the state entering chunk c, G_c = a lam at the first step after chunk c; the
 //     walk ends with G = a_0 lam_0 = dh0.  (This is the chunk carry of page 4, Appendix D,
-//     run once forward for the states and once backward for the adjoint.)
+//     run once forward for the states and once backward for the adjoint.)  The same launch
+//     zeroes the buffers that the main kernel adds into (dA, dB, dC, dD, dbias).
 //  3. main: about one workgroup per compute unit, each on one (batch row, chunk) and a range
 //     of channels; B and C of that chunk are staged in LDS once.  Each wavefront takes one
 //     channel at a time: the states inside the chunk are rebuilt from H_c (lane chains and a
@@ -58,6 +59,7 @@ struct BwdWork {
     int want_fwd;   // the summary/link passes also build H
     int c0;         // first chunk summarised: chunk 0's adjoint summary feeds only dh0, so
                     // it is skipped (c0 = 1) when neither dh0 nor the states are built here
+    FillList fill;  // the gradient kernel's reduction targets, zeroed by the link launch
 };
 
 // Channels per wavefront in the summary: B and C rows are read (and converted) once per state
@@ -204,11 +206,15 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
     }
 }
 
+// One thread per (batch, channel, state) links the chunks; the launch also zeroes the gradient
+// kernel's reduction targets (its grid may be wider than the links for that).
 template <bool FWD>
 __global__ __launch_bounds__(256) void bwd_link_kernel(ScanParams p, GradParams g, BwdWork w) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t tid = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    zero_fill(w.fill, tid, static_cast<size_t>(gridDim.x) * blockDim.x);
+    const int i = static_cast<int>(tid);
     const int N = p.N;
-    if (i >= p.B * p.D * N) return;
+    if (tid >= static_cast<size_t>(p.B) * p.D * N) return;
     const int ch = i / N;
     const int n = i - ch * N;
     const int d = ch % p.D;
@@ -736,27 +742,17 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     }
 }
 
-// Zeroes up to kFillSlots buffers in one launch (the reduction targets of the backward).
+// Zeroes up to kFillSlots buffers in one launch (for reductions with no launch of their own
+// before them to do it, such as the convolution backward's).
 __global__ void fill_zero_kernel(FillList f) {
-    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-    for (int s = 0; s < kFillSlots; ++s) {
-        float* __restrict__ p = f.p[s];
-        if (p == nullptr) continue;
-        for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < f.n[s];
-             i += stride)
-            p[i] = 0.0f;
-    }
+    zero_fill(f, static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x,
+              static_cast<size_t>(gridDim.x) * blockDim.x);
 }
 
 hipError_t launch_fill_zero(const FillList& f, hipStream_t stream) {
-    size_t total = 0;
-    for (int s = 0; s < kFillSlots; ++s)
-        if (f.p[s] != nullptr) total += f.n[s];
-    if (total == 0) return hipSuccess;
-    size_t blocks = (total + 255) / 256;
-    if (blocks > 2048) blocks = 2048;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                       stream, f);
+    const unsigned blocks = fill_blocks(f);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream, f);
     return hipGetLastError();
 }
 
@@ -813,7 +809,8 @@ hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hi
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int links = p.B * p.D * p.N;
-    dim3 lgrid((links + 255) / 256), lblock(256);
+    const unsigned fb = fill_blocks(w.fill);
+    dim3 lgrid(std::max(static_cast<unsigned>((links + 255) / 256), fb)), lblock(256);
     if (w.want_fwd)
         hipLaunchKernelGGL(bwd_link_kernel<true>, lgrid, lblock, 0, s, p, g, w);
     else
@@ -876,8 +873,8 @@ hipError_t bwd_dispatch(const ScanParams& p, const GradParams& g, const BwdWork&
 }  // namespace
 
 hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float* chunk_states,
-                           void* workspace, bool bf16, hipStream_t stream, hipEvent_t ev_begin,
-                           hipEvent_t ev_end) {
+                           void* workspace, bool bf16, const FillList& fill, hipStream_t stream,
+                           hipEvent_t ev_begin, hipEvent_t ev_end) {
     if (p.N > kMaxN) return hipErrorInvalidValue;
     const size_t nch = static_cast<size_t>(p.nchunks);
     const size_t states = static_cast<size_t>(p.B) * p.D * nch * p.N * sizeof(float);
@@ -898,6 +895,7 @@ hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float
     ws += up(per_chunk);
     w.dfirst = reinterpret_cast<float*>(ws);
     w.c0 = (!w.want_fwd && g.dh0 == nullptr) ? 1 : 0;
+    w.fill = fill;
     const Timing tm{ev_begin, ev_end};
     if (bf16) return bwd_dispatch<bf16_t>(p, g, w, stream, tm);
     return bwd_dispatch<float>(p, g, w, stream, tm);

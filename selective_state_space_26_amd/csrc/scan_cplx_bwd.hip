@@ -44,6 +44,7 @@ struct CWork {
     float* dfirst;   // [B*D*nch]: Delta at the chunk's first step
     int c0;          // first chunk summarised: chunk 0's summary feeds only dh0, so it is
                      // skipped (c0 = 1) when dh0 is not asked for
+    FillList fill;   // the gradient kernel's reduction targets, zeroed by the link launch
 };
 
 __device__ __forceinline__ float sin_rev(float r) {
@@ -164,9 +165,12 @@ __global__ __launch_bounds__(256) void cplx_summary_kernel(ScanParams p, GradPar
 // ---------------------------------------------------------------------------------------
 // 2. link
 
+// One thread per (batch, channel, pair); the launch also zeroes the gradient kernel's reduction
+// targets (its grid may be wider than the links for that).
 __global__ __launch_bounds__(256) void cplx_link_kernel(ScanParams p, GradParams g, CWork w) {
     const int J = p.N / 2;
     const long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    zero_fill(w.fill, static_cast<size_t>(i), static_cast<size_t>(gridDim.x) * blockDim.x);
     if (i >= static_cast<long long>(p.B) * p.D * J) return;
     const long long ch = i / J;
     const int j = static_cast<int>(i - ch * J);
@@ -695,7 +699,9 @@ hipError_t cplx_bwd_go(const ScanParams& p, const GradParams& g, const CWork& w,
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const long long links = static_cast<long long>(p.B) * p.D * (p.N / 2);
-    hipLaunchKernelGGL(cplx_link_kernel, dim3(static_cast<unsigned>((links + 255) / 256)),
+    hipLaunchKernelGGL(cplx_link_kernel,
+                       dim3(std::max(static_cast<unsigned>((links + 255) / 256),
+                                     fill_blocks(w.fill))),
                        dim3(256), 0, s, p, g, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // channels per wavefront: about one workgroup per compute unit over (batch, chunk,
@@ -744,7 +750,7 @@ hipError_t cplx_bwd_dispatch(const ScanParams& p, const GradParams& g, const CWo
 
 hipError_t launch_scan_cplx_bwd(const ScanParams& p, const GradParams& g,
                                 const float* chunk_states, void* workspace, bool bf16,
-                                hipStream_t stream) {
+                                const FillList& fill, hipStream_t stream) {
     if (p.N % 2 != 0 || p.N > 2 * kMaxPairs || chunk_states == nullptr)
         return hipErrorInvalidValue;
     const size_t nch = static_cast<size_t>(p.nchunks);
@@ -760,6 +766,7 @@ hipError_t launch_scan_cplx_bwd(const ScanParams& p, const GradParams& g,
     ws += up(per_chunk);
     w.dfirst = reinterpret_cast<float*>(ws);
     w.c0 = g.dh0 == nullptr ? 1 : 0;
+    w.fill = fill;
     return bf16 ? cplx_bwd_dispatch<bf16_t>(p, g, w, stream)
                 : cplx_bwd_dispatch<float>(p, g, w, stream);
 }
