@@ -655,9 +655,9 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
         }
         if (!active) continue;
 
-        // du and ddelta.  With the softplus, sigmoid(delta + bias) = 1 - exp(-Delta) and
-        // u = (Delta u) / Delta come from values already in registers (where Delta underflows
-        // to 0 the sigmoid factor is 0 as well); without it u is read again (L2-resident).
+        // du and ddelta.  With the softplus, sigmoid(delta + bias) = 1 - exp(-Delta) comes from
+        // Delta, already in registers; u is read again (this channel's row, still in L2): one
+        // load costs fewer instructions than forming (Delta u) / Delta.
         float o1[K], o2[K];
         float db_part = 0.0f;
         if constexpr (TRAP) {
@@ -679,12 +679,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 g.du_prev[ch] = (dt[0] - lm[0] * dt[0]) * sP[0];
         } else {
             float uu[K];
-            if constexpr (SOFTPLUS) {
-#pragma unroll
-                for (int k = 0; k < K; ++k) uu[k] = dt[k] > 1e-30f ? dtu[k] * rcp_hw(dt[k]) : 0.0f;
-            } else {
-                load_k_cached<T, K, VEC>(gu + row, t0, L, uu);
-            }
+            load_k_cached<T, K, VEC>(gu + row, t0, L, uu);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float dsp = SOFTPLUS ? 1.0f - exp2_hw(-dt[k] * kLog2e) : 1.0f;
