@@ -5,7 +5,41 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace msel {
+
+// Raises kernel Fn's dynamic-LDS limit to `bytes` on the current device.  The limit is a
+// per-device setting, so it is made once per device (a failed attempt is retried next call).
+template <auto Fn>
+hipError_t allow_dynamic_lds(int bytes) {
+    constexpr int kDevices = 64;
+    static std::atomic<bool> done[kDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < kDevices;
+    if (cached && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(Fn),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && cached) done[dev].store(true, std::memory_order_release);
+    return e;
+}
+
+// Compute units of the current device (256 if the query fails), looked up once per device.
+inline int device_compute_units() {
+    constexpr int kDevices = 64;
+    static std::atomic<int> known[kDevices] = {};
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    const bool cached = dev >= 0 && dev < kDevices;
+    if (cached && (cus = known[dev].load(std::memory_order_relaxed)) > 0) return cus;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 256;
+    if (cached) known[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
 
 // Chunk length of the scan: 64 lanes x 8 time steps.  chunk_states hold the state before
 // every multiple of it; the backward and the chunk-carry pass work one chunk per wave step.

@@ -212,11 +212,10 @@ template <bool FWD>
 __global__ __launch_bounds__(256) void bwd_link_kernel(ScanParams p, GradParams g, BwdWork w) {
     const size_t tid = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     zero_fill(w.fill, tid, static_cast<size_t>(gridDim.x) * blockDim.x);
-    const int i = static_cast<int>(tid);
     const int N = p.N;
     if (tid >= static_cast<size_t>(p.B) * p.D * N) return;
-    const int ch = i / N;
-    const int n = i - ch * N;
+    const int ch = static_cast<int>(tid / N);  // < batch * dim, which fits an int
+    const int n = static_cast<int>(tid - static_cast<size_t>(ch) * N);
     const int d = ch % p.D;
     const int nch = p.nchunks;
     const float A2 = p.A[static_cast<size_t>(d) * N + n] * kLog2e;
@@ -763,17 +762,8 @@ namespace {
 
 // Channels per wavefront in the main kernel: about one workgroup per compute unit, so that
 // each workgroup walks many channels of one (batch row, chunk) and flushes its dB/dC sums once.
-int compute_units() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = 256;
-    return cus;
-}
-
 int main_per_wave(const ScanParams& p, int waves) {
-    static const int cus = compute_units();
+    const int cus = device_compute_units();
     const long long slots = static_cast<long long>(p.B) * p.nchunks;
     const long long target = cus;
     long long per = (static_cast<long long>(p.D) * slots + target * waves - 1) /
@@ -803,7 +793,7 @@ hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hi
                            g, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int links = p.B * p.D * p.N;
+    const long long links = static_cast<long long>(p.B) * p.D * p.N;  // may exceed an int
     const unsigned fb = fill_blocks(w.fill);
     dim3 lgrid(std::max(static_cast<unsigned>((links + 255) / 256), fb)), lblock(256);
     if (w.want_fwd)
@@ -816,10 +806,9 @@ hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hi
     const int cgroups = (p.D + per_wave * W - 1) / (per_wave * W);
     const size_t lds = main_lds_bytes(p.N, W);
     // the LDS exceeds the 64 KB default; allow the largest need over N <= kMaxN
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&bwd_main_kernel<T, VEC, HAS_Z, SP, TRAP>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(main_lds_bytes_max(W)));
-    if (attr != hipSuccess) return attr;
+    e = allow_dynamic_lds<&bwd_main_kernel<T, VEC, HAS_Z, SP, TRAP>>(
+        static_cast<int>(main_lds_bytes_max(W)));
+    if (e != hipSuccess) return e;
     const long long mblocks = static_cast<long long>(cgroups) * p.nchunks * p.B;
     if (mblocks > 0x7fffffffLL) return hipErrorInvalidValue;
     dim3 mgrid(static_cast<unsigned>(mblocks)), mblock(64 * W);

@@ -678,15 +678,6 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
     }
 }
 
-int cplx_compute_units() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = 256;
-    return cus;
-}
-
 template <typename T, bool VEC, bool HAS_Z, bool SP>
 hipError_t cplx_bwd_go(const ScanParams& p, const GradParams& g, const CWork& w,
                        hipStream_t s) {
@@ -706,7 +697,7 @@ hipError_t cplx_bwd_go(const ScanParams& p, const GradParams& g, const CWork& w,
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // channels per wavefront: about one workgroup per compute unit over (batch, chunk,
     // channel ranges), so that each flushes its dB / dC sums once for many channels
-    static const int cus = cplx_compute_units();
+    const int cus = device_compute_units();
     const int W = ring_waves(p.N / 2);
     const long long slots = static_cast<long long>(p.B) * p.nchunks;
     long long per = (static_cast<long long>(p.D) * slots + static_cast<long long>(cus) * W - 1) /
@@ -716,9 +707,8 @@ hipError_t cplx_bwd_go(const ScanParams& p, const GradParams& g, const CWork& w,
     if (per > max_per) per = max_per;
     const int cgroups = static_cast<int>((p.D + per * W - 1) / (per * W));
     // the LDS exceeds the 64 KB default; allow the largest need over the pair counts
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&cplx_main_kernel<T, VEC, HAS_Z, SP>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ring_lds_bytes_max()));
+    const hipError_t attr = allow_dynamic_lds<&cplx_main_kernel<T, VEC, HAS_Z, SP>>(
+        static_cast<int>(ring_lds_bytes_max()));
     if (attr != hipSuccess) return attr;
     const long long mblocks = static_cast<long long>(cgroups) * p.nchunks * p.B;
     if (mblocks > 0x7fffffffLL) return hipErrorInvalidValue;

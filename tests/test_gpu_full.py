@@ -165,3 +165,31 @@ def test_sequence_beyond_65535_chunks():
     go = msel_inputs.bf16_bits_to_f32(t["dout"]).astype(np.float64)
     dD = np.sum(go * z / (1.0 + np.exp(-z)) * u, axis=(0, 2))
     assert_close("dD", host(g["dD"]), dD, "bf16")
+
+
+def test_link_count_beyond_int_range():
+    """Batch 8193, 16384 channels, dstate 16, one step: batch * dim * dstate = 2^31 + 2^18
+    (batch, channel, state) links, one thread each, so the last batch row's link threads have
+    indices past the int range.  Recomputed chunk states (the link then runs both its loops).
+    The first and last batch rows are checked whole (every per-channel gradient, dB, dC);
+    dA, dD and ddelta_bias on sampled channels over every batch row."""
+    bsz, dim, N = 8193, 16384, 16
+    log(f"link count beyond int range: batch={bsz} dim={dim} dstate={N}")
+    t = msel_inputs.make(bsz, dim, N, 1, "bf16", 91, with_dout=True)
+    dv = to_device(t)
+    g = msel.msel_scan_bwd(dv["u"], dv["delta"], dv["A"], dv["B"], dv["C"], dv["dout"], dv["D"],
+                           dv["z"], dv["bias"], True)
+    torch.cuda.synchronize()
+    del dv
+    for b in (0, bsz - 1):
+        s = msel_inputs.channel_slice(t, b, np.arange(dim))
+        r = oracle.bwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["dout"], s["D"], s["z"],
+                       s["bias"])
+        for k in ("du", "ddelta", "dz", "dB", "dC"):
+            assert_close(f"{k}[{b}]", host(g[k][b]), r[k][0], "bf16")
+    ds = sorted({0, dim - 1, *np.random.default_rng(91).integers(dim, size=6).tolist()})
+    sub = {k: (None if t.get(k) is None else t.values(k)) for k in t}
+    r2 = oracle.bwd(sub["u"][:, ds], sub["delta"][:, ds], t["A"][ds], sub["B"], sub["C"],
+                    sub["dout"][:, ds], t["D"][ds], sub["z"][:, ds], t["bias"][ds])
+    for k in ("dA", "dD", "ddelta_bias"):
+        assert_close(k, host(g[k][ds]), r2[k], "bf16")
