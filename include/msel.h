@@ -25,8 +25,8 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers on the current HIP device, contiguous, row-major.
  *  - The caller owns every buffer.  The library allocates nothing, keeps no state between
- *    calls, is re-entrant, and never synchronizes: work is enqueued on `stream` and the
- *    call returns.  Errors in the arguments are detected on the host before anything is
+ *    calls (but for the ring-wait counter of msel_ring_timeouts), is re-entrant, and never
+ *    synchronizes: work is enqueued on `stream` and the call returns.  Errors in the arguments are detected on the host before anything is
  *    enqueued; the return value is then not MSEL_OK and no device memory is touched.
  *  - Inputs are read-only.  Outputs must not be the same pointer as any input (checked),
  *    except where a field says otherwise (a state updated in place).
@@ -181,6 +181,23 @@ msel_status msel_scan_bwd(const msel_scan_args *args, const msel_scan_grads *gra
 msel_status msel_scan_bwd_profiled(const msel_scan_args *args, const msel_scan_grads *grads,
                                    void *workspace, size_t workspace_bytes, hipStream_t stream,
                                    hipEvent_t ev_begin, hipEvent_t ev_end);
+
+/* The backward gradient kernels (msel_scan_bwd, msel_scan_trap_bwd, msel_scan_complex_bwd)
+ * hand the rows of their dB/dC accumulators from wavefront to wavefront through flags in LDS.
+ * Each wait on such a flag is bounded: after a poll limit it gives up, so that a fault in the
+ * hand-over ends the kernel instead of hanging the device, and it is counted.
+ * msel_ring_timeouts waits for the current device to finish its work, stores in *count the
+ * number of waits that gave up on that device since the last call (0 in any correct run; a
+ * call with a nonzero count may have wrong dB and dC), and clears the count.  It is the one
+ * place where the library keeps state: a counter per device.  MSEL_ERR_NULL if count is NULL,
+ * MSEL_ERR_HIP if the runtime fails. */
+msel_status msel_ring_timeouts(unsigned long long *count);
+
+/* Sets the poll limit of those waits for calls made after it in this process: `polls`
+ * polls, each after a sleep of about 64 clocks; 0 restores the default of 2^22 polls (about
+ * 0.1 s).  For tests of the timeout path, which set a tiny limit so that waits give up while
+ * every kernel still ends normally.  Not thread-safe against concurrent backward calls. */
+void msel_set_ring_spin_limit(uint32_t polls);
 
 /* ------------------------------------------------------------------------------------------
  * The exponential-trapezoidal variant of the scan (Mamba-3).

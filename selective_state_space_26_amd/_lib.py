@@ -69,7 +69,8 @@ EXPORTS = ["msel_abi_version", "msel_chunk_len", "msel_num_chunks", "msel_status
            "msel_validate_conv_bwd", "msel_conv1d_fwd", "msel_conv1d_bwd",
            "msel_validate_trap_fwd", "msel_scan_trap_fwd", "msel_validate_complex_fwd",
            "msel_scan_complex_fwd", "msel_validate_trap_bwd", "msel_scan_trap_bwd",
-           "msel_validate_complex_bwd", "msel_scan_complex_bwd"]
+           "msel_validate_complex_bwd", "msel_scan_complex_bwd", "msel_ring_timeouts",
+           "msel_set_ring_spin_limit"]
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
@@ -133,6 +134,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.msel_conv1d_fwd.argtypes = [ca, _P]
     lib.msel_conv1d_bwd.restype = ctypes.c_int
     lib.msel_conv1d_bwd.argtypes = [ca, cg, _P]
+    lib.msel_ring_timeouts.restype = ctypes.c_int
+    lib.msel_ring_timeouts.argtypes = [ctypes.POINTER(ctypes.c_ulonglong)]
+    lib.msel_set_ring_spin_limit.restype = None
+    lib.msel_set_ring_spin_limit.argtypes = [ctypes.c_uint32]
     if lib.msel_abi_version() != ABI_VERSION:
         raise RuntimeError("libmsel.so ABI version mismatch")
     if path is None:

@@ -12,9 +12,12 @@
 // F'_t = the sum of Delta over the chunk's steps after t, the product of a = exp(Delta A) over
 // those steps is exp(A F'_t), and
 //   S_c = sum_t exp(A F'_t) Delta_t u_t B_t,   P_c = exp(A * the chunk's sum of Delta).
-// One prefix sum of Delta per chunk serves all states; every term is independent, and the
-// 64-lane sums are done four at a time.  The link runs on all states at once (lane n holds
-// state n).  It reads u, delta and B only.
+// One suffix sum of Delta per chunk serves all states; every term is independent, and the
+// 64-lane sums are done four at a time.  F'_t is summed from the steps it covers (a reversed
+// lane scan), not taken as total - prefix: a selective model may reset its state with one
+// huge Delta (page 1, the model forgets depending on the current token), and next to it such
+// a difference would keep only a few bits of F'_t.  The link runs on all states at once (lane
+// n holds state n).  It reads u, delta and B only.
 #include "msel_device.hpp"
 #include "msel_kernels.hpp"
 
@@ -27,6 +30,7 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
     constexpr int K = kChunk / 64;
     constexpr int R = kCcChannels;
     const int lane = lane_id();
+    const int rev_addr = (63 - lane) << 2;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int dgroups = (p.D + R - 1) / R;
     const int idx = blockIdx.x * (blockDim.x >> 6) + wave;  // b * dgroups + dg
@@ -68,21 +72,26 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
             float uu[K], dd[K];
             load_k_cached<T, K, VEC>(u[r], t0, L, uu);
             load_k_cached<T, K, VEC>(dl[r], t0, L, dd);
-            float run = 0.0f;
+            float dt[K];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float x = dd[k] + bias[r];
                 const float v = SOFTPLUS ? softplus_f(x) : x;
-                const float dt = (t0 + k < L) ? v : 0.0f;
-                du[r][k] = dt * uu[k];
-                run += dt;
-                Fs[r][k] = run;
+                dt[k] = (t0 + k < L) ? v : 0.0f;
+                du[r][k] = dt[k] * uu[k];
             }
-            const float incl = wave_incl_sum(run);
-            const float before = shift_up(incl, 0.0f);
-            total[r] = readlane(incl, 63);
+            // suffix sums, each a sum of the steps it covers (never total - prefix: next to a
+            // reset step's huge Delta that difference would lose the remainder)
+            float suf = 0.0f;
 #pragma unroll
-            for (int k = 0; k < K; ++k) Fs[r][k] = total[r] - (before + Fs[r][k]);
+            for (int k = K - 1; k >= 0; --k) {
+                Fs[r][k] = suf;
+                suf += dt[k];
+            }
+            const float after = wave_excl_suffix_sum(suf, rev_addr);  // lanes after this one
+            total[r] = readlane(after, 0) + readlane(suf, 0);
+#pragma unroll
+            for (int k = 0; k < K; ++k) Fs[r][k] += after;
         }
         // local end state of every state from a zero start, two states at a time; lane n
         // collects state n's total

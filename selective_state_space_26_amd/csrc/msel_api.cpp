@@ -2,7 +2,8 @@
 //
 // Every entry point first validates its arguments on the host (no HIP call, no device memory
 // touched) and only then enqueues kernels on the caller's stream.  The library never
-// allocates, never synchronizes and keeps no state.
+// allocates and never synchronizes; its only state is the ring-wait timeout count and limit
+// (msel_ring_timeouts, msel_set_ring_spin_limit), whose reader synchronizes.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -439,6 +440,19 @@ msel_status msel_scan_trap_bwd(const msel_scan_args* a, const msel_trap_args* tr
     if (s != MSEL_OK) return s;
     return run_bwd(a, g, tr, tg, workspace, stream, nullptr, nullptr);
 }
+
+msel_status msel_ring_timeouts(unsigned long long* count) {
+    if (count == nullptr) return MSEL_ERR_NULL;
+    *count = 0;
+    if (hipDeviceSynchronize() != hipSuccess) return MSEL_ERR_HIP;
+    unsigned long long a = 0, b = 0;
+    if (msel::take_ring_timeouts_bwd(&a) != hipSuccess) return MSEL_ERR_HIP;
+    if (msel::take_ring_timeouts_cplx(&b) != hipSuccess) return MSEL_ERR_HIP;
+    *count = a + b;
+    return MSEL_OK;
+}
+
+void msel_set_ring_spin_limit(uint32_t polls) { msel::set_ring_spin_limit(polls); }
 
 msel_status msel_scan_bwd(const msel_scan_args* a, const msel_scan_grads* g, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {

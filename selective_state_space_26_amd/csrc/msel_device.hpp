@@ -38,6 +38,14 @@ __device__ __forceinline__ float softplus_f(float x) {
 
 __device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
 
+// The softplus's derivative sigmoid(x), given x and its softplus sp = log(1 + e^x):
+// sigmoid(x) = e^x / (1 + e^x) = exp(x - sp), one exp.  (The other one-exp form, 1 - exp(-sp),
+// cancels for small sp: at sp = 1e-4 it keeps only ~4 significant digits.)  x - sp = -log(1 +
+// e^-x) is exact where it is large, and where it is tiny (x large) the sigmoid is ~1 anyway.
+__device__ __forceinline__ float softplus_grad_f(float x, float sp) {
+    return exp2_hw((x - sp) * kLog2e);
+}
+
 // ---------------------------------------------------------------------------------------
 // dtype traits: float rows, or bf16 rows stored as uint16_t.
 
@@ -423,6 +431,18 @@ __device__ __forceinline__ float wave_incl_sum(float v) {
                  "v_add_f32_dpp %[v], %[v], %[v] row_bcast:31 row_mask:0xc bank_mask:0xf\n"
                  : [v] "+v"(v));
     return v;
+}
+
+// Sum of v over the lanes before this one (lane 0 gets 0).
+__device__ __forceinline__ float wave_excl_sum(float v) { return shift_up(wave_incl_sum(v), 0.0f); }
+
+// Sum of v over the lanes after this one (lane 63 gets 0): the exclusive prefix sum in
+// reversed lane order (rev_addr = (63 - lane) * 4).  Partial sums of step sizes are always
+// formed this way, as sums of the terms they cover: a difference of two totals, such as
+// total - prefix, loses the small remainder next to one huge step (a state reset, whose
+// Delta * A is hundreds), and exp(A * remainder) then carries that error.
+__device__ __forceinline__ float wave_excl_suffix_sum(float v, int rev_addr) {
+    return rev_lanes(wave_excl_sum(rev_lanes(v, rev_addr)), rev_addr);
 }
 
 // Four independent 64-lane sums, interleaved so that no wait states are needed; lane 63 of

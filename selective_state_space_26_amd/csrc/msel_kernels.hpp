@@ -85,6 +85,16 @@ struct GradParams {
     float* dB_prev = nullptr;
 };
 
+// The gradient kernels' LDS ring waits (scan_bwd.hip, scan_cplx_bwd.hip) are bounded: a wait
+// that has polled its flag ring_spin_limit() times (each poll after an s_sleep of ~64 clocks)
+// gives up, so that a protocol slip ends the kernel instead of hanging the device, and counts
+// the event in a device counter of its source file, which take_ring_timeouts_* read and clear.
+constexpr unsigned kRingSpinDefault = 1u << 22;  // ~0.1 s of polls at 2.4 GHz
+unsigned ring_spin_limit();
+void set_ring_spin_limit(unsigned polls);  // 0: the default
+hipError_t take_ring_timeouts_bwd(unsigned long long* count);
+hipError_t take_ring_timeouts_cplx(unsigned long long* count);
+
 // All launchers enqueue on `stream` and return the hipGetLastError() after the launch.
 hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_chunk_carry(const ScanParams& p, bool bf16, hipStream_t stream);

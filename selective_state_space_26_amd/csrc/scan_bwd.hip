@@ -60,7 +60,31 @@ struct BwdWork {
     int c0;         // first chunk summarised: chunk 0's adjoint summary feeds only dh0, so
                     // it is skipped (c0 = 1) when neither dh0 nor the states are built here
     FillList fill;  // the gradient kernel's reduction targets, zeroed by the link launch
+    unsigned spin_limit;  // polls after which a ring wait gives up (ring_spin_limit())
 };
+
+// Ring waits of this file's gradient kernel that gave up (see ring_spin_limit).
+__device__ unsigned long long g_ring_timeouts_bwd;
+
+std::atomic<unsigned> g_ring_spin_limit{kRingSpinDefault};
+
+unsigned ring_spin_limit() { return g_ring_spin_limit.load(std::memory_order_relaxed); }
+
+void set_ring_spin_limit(unsigned polls) {
+    g_ring_spin_limit.store(polls != 0 ? polls : kRingSpinDefault, std::memory_order_relaxed);
+}
+
+hipError_t take_ring_timeouts_bwd(unsigned long long* count) {
+    unsigned long long v = 0;
+    const unsigned long long zero = 0;
+    hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_ring_timeouts_bwd), sizeof(v), 0,
+                                       hipMemcpyDeviceToHost);
+    if (e == hipSuccess)
+        e = hipMemcpyToSymbol(HIP_SYMBOL(g_ring_timeouts_bwd), &zero, sizeof(zero), 0,
+                              hipMemcpyHostToDevice);
+    *count = v;
+    return e;
+}
 
 // Channels per wavefront in the summary: B and C rows are read (and converted) once per state
 // and used for all of them.
@@ -119,6 +143,10 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
         const float a_ = p.A[static_cast<size_t>(dch[r]) * N + (lane < N ? lane : N - 1)];
         Av[r] = (lane < N) ? a_ * kLog2e : 0.0f;
     }
+    // E_t and F'_t are each summed from the steps they cover (the chunk's first step left
+    // out of E; F'_t by a reversed lane scan), never as a difference of two sums: next to a
+    // reset step's huge Delta such a difference would keep only a few bits of the remainder.
+    const int rev_addr = (63 - lane) << 2;
     float tot[R], fst[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -138,18 +166,25 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
             if constexpr (HAS_Z) dy[r][k] = gg[k] * zz[k] * sigmoid_f(zz[k]);
             else dy[r][k] = gg[k];
             if constexpr (FWD) du[r][k] = dt[k] * uu[k];
-            run += dt[k];
+            run += (k == 0 && lane == 0) ? 0.0f : dt[k];  // the chunk's first step left out
             E[r][k] = run;  // inclusive within the lane for now
         }
         const float incl = wave_incl_sum(run);
         const float before = shift_up(incl, 0.0f);  // Delta summed over the earlier lanes
-        tot[r] = readlane(incl, 63);
         fst[r] = readlane(dt[0], 0);
+        tot[r] = readlane(incl, 63) + fst[r];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const float F = before + E[r][k];  // sum of Delta from the chunk start to t
-            if constexpr (FWD) Fs[r][k] = tot[r] - F;
-            E[r][k] = F - fst[r];
+        for (int k = 0; k < K; ++k) E[r][k] += before;  // sum of Delta over steps 1..t
+        if constexpr (FWD) {
+            float suf = 0.0f;
+#pragma unroll
+            for (int k = K - 1; k >= 0; --k) {
+                Fs[r][k] = suf;
+                suf += dt[k];
+            }
+            const float after = wave_excl_suffix_sum(suf, rev_addr);
+#pragma unroll
+            for (int k = 0; k < K; ++k) Fs[r][k] += after;  // sum of Delta after t
         }
     }
     if (lane == 0) {
@@ -516,9 +551,17 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
             // wait until the previous update of state nc (step gstep - kp) is complete
             const int need = gstep - kp + 1;
             if (need > 0) {
+                unsigned polls = 0;
                 while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                           gflags + nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < need)
+                           gflags + nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < need) {
+                    if (++polls >= w.spin_limit) {  // give up: counted, never a hang
+                        if (lane == 0)
+                            __hip_atomic_fetch_add(&g_ring_timeouts_bwd, 1ull, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
                     __builtin_amdgcn_s_sleep(1);
+                }
             }
             asm volatile("" ::: "memory");
             if (active) {
@@ -654,18 +697,24 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
         }
         if (!active) continue;
 
-        // du and ddelta.  With the softplus, sigmoid(delta + bias) = 1 - exp(-Delta) comes from
-        // Delta, already in registers; u is read again (this channel's row, still in L2): one
-        // load costs fewer instructions than forming (Delta u) / Delta.
+        // du and ddelta.  With the softplus, ddelta = dDelta * sigmoid(delta + bias), formed
+        // from delta + bias and Delta (softplus_grad_f); delta, and u, are read again (this
+        // channel's rows, still in L2): one load costs fewer instructions than keeping them.
         float o1[K], o2[K];
         float db_part = 0.0f;
+        float xs[SOFTPLUS ? K : 1];  // delta + bias
+        if constexpr (SOFTPLUS) {
+            load_k_cached<T, K, VEC>(gd + row, t0, L, xs);
+#pragma unroll
+            for (int k = 0; k < K; ++k) xs[k] += bias;
+        }
         if constexpr (TRAP) {
             float o3[K];
             const float um1_0 = shift_up(uT[K - 1], u_before);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float um1 = (k == 0) ? um1_0 : uT[k - 1];
-                const float dsp = SOFTPLUS ? 1.0f - exp2_hw(-dt[k] * kLog2e) : 1.0f;
+                const float dsp = SOFTPLUS ? softplus_grad_f(xs[k], dt[k]) : 1.0f;
                 o1[k] = fmaf(sB[k], lm[k] * dt[k], fmaf(sA[k], cnu[k], dy[k] * Dd));     // du
                 const float dD_ = fmaf(sP[k], um1 - lm[k] * um1, fmaf(sB[k], lm[k] * uT[k], sgA[k]));
                 o2[k] = dD_ * dsp;                                                       // ddelta
@@ -681,7 +730,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
             load_k_cached<T, K, VEC>(gu + row, t0, L, uu);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                const float dsp = SOFTPLUS ? 1.0f - exp2_hw(-dt[k] * kLog2e) : 1.0f;
+                const float dsp = SOFTPLUS ? softplus_grad_f(xs[k], dt[k]) : 1.0f;
                 o1[k] = fmaf(sB[k], dt[k], dy[k] * Dd);            // du
                 o2[k] = fmaf(sB[k], uu[k], sgA[k]) * dsp;         // ddelta
                 db_part += (t0 + k < L) ? o2[k] : 0.0f;
@@ -880,6 +929,7 @@ hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float
     w.dfirst = reinterpret_cast<float*>(ws);
     w.c0 = (!w.want_fwd && g.dh0 == nullptr) ? 1 : 0;
     w.fill = fill;
+    w.spin_limit = ring_spin_limit();
     const Timing tm{ev_begin, ev_end};
     if (bf16) return bwd_dispatch<bf16_t>(p, g, w, stream, tm);
     return bwd_dispatch<float>(p, g, w, stream, tm);

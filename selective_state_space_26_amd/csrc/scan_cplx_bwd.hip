@@ -45,7 +45,11 @@ struct CWork {
     int c0;          // first chunk summarised: chunk 0's summary feeds only dh0, so it is
                      // skipped (c0 = 1) when dh0 is not asked for
     FillList fill;   // the gradient kernel's reduction targets, zeroed by the link launch
+    unsigned spin_limit;  // polls after which a ring wait gives up (ring_spin_limit())
 };
+
+// Ring waits of this file's gradient kernel that gave up (see ring_spin_limit).
+__device__ unsigned long long g_ring_timeouts_cplx;
 
 __device__ __forceinline__ float sin_rev(float r) {
     return __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(r));
@@ -112,20 +116,22 @@ __global__ __launch_bounds__(256) void cplx_summary_kernel(ScanParams p, GradPar
             dy[k] = HAS_Z ? go[k] * zz[k] * sigmoid_f(zz[k]) : go[k];
         }
     }
-    // E_t: sum of Delta over the chunk's steps 1..t
+    // E_t: sum of Delta over the chunk's steps 1..t, summed from those steps alone (the first
+    // step left out of the running sum, not subtracted: next to a reset step's huge Delta a
+    // difference of two sums would keep only a few bits of E_t)
     float E[K];
     float run = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        run += dt[k];
+        run += (k == 0 && lane == 0) ? 0.0f : dt[k];
         E[k] = run;
     }
     const float incl = wave_incl_sum(run);
-    const float before = incl - run;                 // Delta of the lanes before this one
+    const float before = shift_up(incl, 0.0f);      // Delta of the lanes before this one
     const float first = readlane(dt[0], 0);          // Delta at the chunk's first step
-    const float total = readlane(incl, 63);
+    const float total = readlane(incl, 63) + first;
 #pragma unroll
-    for (int k = 0; k < K; ++k) E[k] += before - first;
+    for (int k = 0; k < K; ++k) E[k] += before;
 
     const T* __restrict__ Cg = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
     const float* Ad = p.A + static_cast<size_t>(d) * N;
@@ -430,9 +436,17 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
             }
             // wait until the previous update of pair jc (one step earlier) is complete
             if (gstep > 0) {
+                unsigned polls = 0;
                 while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                           gflags + jc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < gstep)
+                           gflags + jc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < gstep) {
+                    if (++polls >= w.spin_limit) {  // give up: counted, never a hang
+                        if (lane == 0)
+                            __hip_atomic_fetch_add(&g_ring_timeouts_cplx, 1ull, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
                     __builtin_amdgcn_s_sleep(1);
+                }
             }
             asm volatile("" ::: "memory");
             if (active) {
@@ -598,21 +612,22 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
         }
         if (!active) continue;
 
-        // du, ddelta and dz.  With the softplus, sigmoid(delta + bias) = 1 - exp(-Delta) and
-        // u = (Delta u) / Delta come from registers (where Delta underflows to 0 the sigmoid
-        // factor is 0 as well); without it u is read again.
+        // du, ddelta and dz.  u and delta are read again (this channel's rows, still in L2);
+        // with the softplus, ddelta = dDelta * sigmoid(delta + bias), formed from delta + bias
+        // and Delta (softplus_grad_f).
         float uu[K];
+        load_k_cached<T, K, VEC>(gu + row, t0, L, uu);
+        float xs[SOFTPLUS ? K : 1];  // delta + bias
         if constexpr (SOFTPLUS) {
+            load_k_cached<T, K, VEC>(gd + row, t0, L, xs);
 #pragma unroll
-            for (int k = 0; k < K; ++k) uu[k] = dt[k] > 1e-30f ? dtu[k] * rcp_hw(dt[k]) : 0.0f;
-        } else {
-            load_k_cached<T, K, VEC>(gu + row, t0, L, uu);
+            for (int k = 0; k < K; ++k) xs[k] += bias;
         }
         float o1[K], o2[K];
         float db_part = 0.0f;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const float dsp = SOFTPLUS ? 1.0f - exp2_hw(-dt[k] * kLog2e) : 1.0f;
+            const float dsp = SOFTPLUS ? softplus_grad_f(xs[k], dt[k]) : 1.0f;
             o1[k] = fmaf(sB[k], dt[k], dy[k] * Dd);        // du
             o2[k] = fmaf(sB[k], uu[k], sgA[k]) * dsp;     // ddelta
             db_part += (t0 + k < L) ? o2[k] : 0.0f;
@@ -738,6 +753,18 @@ hipError_t cplx_bwd_dispatch(const ScanParams& p, const GradParams& g, const CWo
 
 }  // namespace
 
+hipError_t take_ring_timeouts_cplx(unsigned long long* count) {
+    unsigned long long v = 0;
+    const unsigned long long zero = 0;
+    hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_ring_timeouts_cplx), sizeof(v), 0,
+                                       hipMemcpyDeviceToHost);
+    if (e == hipSuccess)
+        e = hipMemcpyToSymbol(HIP_SYMBOL(g_ring_timeouts_cplx), &zero, sizeof(zero), 0,
+                              hipMemcpyHostToDevice);
+    *count = v;
+    return e;
+}
+
 hipError_t launch_scan_cplx_bwd(const ScanParams& p, const GradParams& g,
                                 const float* chunk_states, void* workspace, bool bf16,
                                 const FillList& fill, hipStream_t stream) {
@@ -757,6 +784,7 @@ hipError_t launch_scan_cplx_bwd(const ScanParams& p, const GradParams& g,
     w.dfirst = reinterpret_cast<float*>(ws);
     w.c0 = g.dh0 == nullptr ? 1 : 0;
     w.fill = fill;
+    w.spin_limit = ring_spin_limit();
     return bf16 ? cplx_bwd_dispatch<bf16_t>(p, g, w, stream)
                 : cplx_bwd_dispatch<float>(p, g, w, stream);
 }

@@ -228,9 +228,11 @@ template <typename T, bool HAS_Z, bool SOFTPLUS, bool TRAP>
 __global__ __launch_bounds__(256) void scan_step_kernel(ScanParams p) {
     const int lane = lane_id();
     const int n = lane & 15;
-    const int ch = (blockIdx.x * blockDim.x + threadIdx.x) >> 4;  // b * D + d
-    const bool in = ch < p.B * p.D;
-    const int chc = in ? ch : 0;
+    // b * D + d, formed in 64 bits: 16 * batch * dim threads may pass 2^32
+    const long long ch =
+        (static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x) >> 4;
+    const bool in = ch < static_cast<long long>(p.B) * p.D;
+    const int chc = in ? static_cast<int>(ch) : 0;
     const int b = chc / p.D;
     const int d = chc - b * p.D;
     const int N = p.N;

@@ -336,3 +336,18 @@ def msel_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
                    lib.msel_scan_bwd_profiled(ctypes.byref(a), ctypes.byref(g), ws_ptr, ws_bytes,
                                               _stream(dev), ev[0], ev[1]))
     return r
+
+
+def ring_timeouts() -> int:
+    """Waits of the backward gradient kernels' LDS ring that gave up on the current device since
+    the last call (0 in a correct run), then clears the count (msel_ring_timeouts).  Waits for
+    the device to finish its work."""
+    n = ctypes.c_ulonglong(0)
+    _lib.check("msel_ring_timeouts", _lib.load().msel_ring_timeouts(ctypes.byref(n)))
+    return int(n.value)
+
+
+def set_ring_spin_limit(polls: int) -> None:
+    """Poll limit of those waits for later calls (0: the default); for tests of the timeout
+    path (msel_set_ring_spin_limit)."""
+    _lib.load().msel_set_ring_spin_limit(int(polls))

@@ -59,3 +59,33 @@ def assert_close(name, got, ref, dtype):
 
 def oracle_vals(t: msel_inputs.Tensors) -> dict:
     return {k: t.values(k) for k in ("u", "delta", "z", "B", "C", "A", "D", "bias", "h0", "dout")}
+
+
+class MaxErr:
+    """max|got - ref| and max|ref| of one tensor accumulated over slices, so that a tensor too
+    large for one oracle call is still held to the per-tensor bar as a whole."""
+
+    def __init__(self, name: str, dtype: str):
+        self.name, self.dtype = name, dtype
+        self.err = 0.0
+        self.scale = 0.0
+        self.count = 0
+
+    def add(self, got, ref) -> None:
+        got = np.asarray(got, np.float64)
+        ref = np.asarray(ref, np.float64)
+        assert got.shape == ref.shape, (self.name, got.shape, ref.shape)
+        assert np.all(np.isfinite(got)), f"{self.name}: non-finite values in GPU output"
+        if got.size:
+            self.err = max(self.err, float(np.max(np.abs(got - ref))))
+            self.scale = max(self.scale, float(np.max(np.abs(ref))))
+        self.count += got.size
+
+    def check(self, expect_count=None) -> float:
+        if expect_count is not None:
+            assert self.count == expect_count, (self.name, self.count, expect_count)
+        e = self.err / self.scale if self.scale > 0 else self.err
+        log(f"{self.name}: {self.count} elements, max|err|/max|ref| = {e:.3e}")
+        assert e <= tol(self.dtype), \
+            f"{self.name}: max|err|/max|ref| = {e:.3e} > {tol(self.dtype):.0e}"
+        return e

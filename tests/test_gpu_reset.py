@@ -1,0 +1,202 @@
+"""GPU parity next to a state reset, and of ddelta where every step is tiny.
+
+A selective model forgets its state when one token's step is large (page 1, "A Secret Weapon
+For mamba paper": the parameters depend on the current token, so the model can keep or forget
+state).  A step with Delta * A below -746 makes exp(Delta A) = 0 in fp32 and in fp64 alike.
+The closed-form chunk totals (the chunk-carry pass, the backward's summaries) sum Delta over
+runs of steps; a run that sits next to such a step must still be summed to full relative
+precision, or exp(A * run) inherits the rounding of the huge step.  The cases put one reset
+inside a chunk and one on a chunk's first step, on every path that forms such sums:
+msel_scan_chunk_carry, msel_scan_fwd's chunk states, msel_scan_bwd with rebuilt and with given
+chunk states (with and without dh0), and the trapezoidal and complex backwards.
+
+The bar is the parity bar of every other test: max|gpu - oracle| <= tol * max|oracle| per
+tensor (1e-4 fp32 inputs, 1e-2 bf16).
+"""
+import numpy as np
+import pytest
+
+import msel_inputs
+import oracle
+from helpers import assert_close, host, log, oracle_vals, to_device
+from oracle import cplx as ocplx
+from oracle import trap as otrap
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import selective_state_space_26_amd as msel  # noqa: E402
+
+T = msel.chunk_len()
+# exact in bf16; softplus(1504 + bias) * A_re < -745.2 for every real rate A_re <= -1/2 (the
+# complex inputs' rate), so exp underflows to 0 in fp64 as well as in fp32
+RESET_DELTA = 1504.0
+
+CASES = [
+    # batch, dim, dstate, seqlen, dtype, reset steps, zero u at the resets, softplus
+    (2, 3, 16, 2000, "f32", (700, 2 * T), True, True),      # inside chunk 1; chunk 2's start
+    (2, 3, 16, 2000, "f32", (700, 2 * T), False, True),     # the reset step's own input kept
+    (1, 4, 16, 3 * T + 37, "f32", (0, T, 3 * T + 36), True, True),  # first and last steps
+    (2, 3, 16, 2000, "bf16", (700, 2 * T), True, True),
+    (1, 5, 7, 1600, "f32", (T + 1, 2 * T - 1), True, False),  # no softplus, dstate 7
+]
+
+
+def _reset_inputs(bsz, dim, N, L, dtype, resets, zero_u, sp, seed=311, complex_A=False):
+    t = msel_inputs.make(bsz, dim, N, L, dtype, seed, with_h0=True, with_dout=True,
+                         complex_A=complex_A)
+    delta = t.values("delta").copy()
+    u = t.values("u").copy()
+    if not sp:  # a small positive step, as a learned one is
+        delta = np.abs(delta) * np.float32(0.2)
+        t["bias"] = (np.abs(t["bias"]) * np.float32(0.01)).astype(np.float32)
+    for r in resets:
+        delta[:, :, r] = RESET_DELTA
+        if zero_u:
+            u[:, :, r] = 0.0
+    enc = (lambda v: msel_inputs.f32_to_bf16_bits(v)) if dtype == "bf16" else (lambda v: v)
+    t["delta"] = enc(delta.astype(np.float32))
+    t["u"] = enc(u.astype(np.float32))
+    return t
+
+
+def _ids(c):
+    return f"{c[4]}-L{c[3]}-N{c[2]}-r{'_'.join(map(str, c[5]))}-{'u0' if c[6] else 'u'}" + \
+        ("" if c[7] else "-nosp")
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_chunk_carry_next_to_reset(case):
+    bsz, dim, N, L, dtype, resets, zero_u, sp = case
+    log(f"chunk_carry reset {case}")
+    t = _reset_inputs(*case)
+    d = to_device(t)
+    cs, fin = msel.msel_scan_chunk_carry(d["u"], d["delta"], d["A"], d["B"], d["bias"], sp,
+                                         d["h0"])
+    out, ffin, fcs = msel.msel_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],
+                                        d["z"], d["bias"], sp, d["h0"], return_chunk_states=True)
+    torch.cuda.synchronize()
+    v = oracle_vals(t)
+    ro, rf, rcs = oracle.fwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"],
+                             v["bias"], v["h0"], softplus=sp, chunk_len=T)
+    fcs_, ffin_ = oracle.chunk_states_formula(v["u"], v["delta"], v["A"], v["B"], T, h0=v["h0"],
+                                              bias=v["bias"], softplus=sp)
+    assert_close("oracle: chunk formula vs loop", fcs_, rcs, "f32")
+    assert_close("chunk_carry chunk_states", host(cs), rcs, dtype)
+    assert_close("chunk_carry final_state", host(fin), rf, dtype)
+    assert_close("fwd out", host(out), ro, dtype)
+    assert_close("fwd final_state", host(ffin), rf, dtype)
+    assert_close("fwd chunk_states", host(fcs), rcs, dtype)
+    # the two passes that produce chunk states agree with each other too
+    assert_close("fwd vs chunk_carry", host(fcs), host(cs), dtype)
+
+
+@pytest.mark.parametrize("given_states,want_dh0", [(False, True), (True, True), (True, False)])
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_bwd_next_to_reset(case, given_states, want_dh0):
+    bsz, dim, N, L, dtype, resets, zero_u, sp = case
+    log(f"bwd reset {case} given_states={given_states} want_dh0={want_dh0}")
+    t = _reset_inputs(*case)
+    d = to_device(t)
+    cs = None
+    if given_states:
+        _, _, cs = msel.msel_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],
+                                      d["z"], d["bias"], sp, d["h0"], return_final_state=False,
+                                      return_chunk_states=True)
+    g = msel.msel_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dout"], d["D"],
+                           d["z"], d["bias"], sp, d["h0"], chunk_states=cs, want_dh0=want_dh0)
+    torch.cuda.synchronize()
+    v = oracle_vals(t)
+    r = oracle.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
+                   v["bias"], v["h0"], softplus=sp)
+    names = ["du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias"]
+    if want_dh0:
+        names.append("dh0")
+    for k in names:
+        assert_close(k, host(g[k]), r[k], dtype)
+
+
+@pytest.mark.parametrize("want_dh0", [True, False])
+@pytest.mark.parametrize("case", CASES[:4], ids=_ids)
+def test_complex_bwd_next_to_reset(case, want_dh0):
+    bsz, dim, N, L, dtype, resets, zero_u, sp = case
+    log(f"complex bwd reset {case} want_dh0={want_dh0}")
+    t = _reset_inputs(*case, complex_A=True)
+    d = to_device(t)
+    out, fin, cs = msel.msel_scan_complex_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"],
+                                              d["D"], d["z"], d["bias"], sp, d["h0"],
+                                              return_chunk_states=True)
+    g = msel.msel_scan_complex_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dout"], cs,
+                                   d["D"], d["z"], d["bias"], sp, d["h0"], want_dh0=want_dh0)
+    torch.cuda.synchronize()
+    v = oracle_vals(t)
+    ro, rf, _ = ocplx.fwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"],
+                          v["bias"], v["h0"], softplus=sp)
+    assert_close("out", host(out), ro, dtype)
+    assert_close("final_state", host(fin), rf, dtype)
+    r = ocplx.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
+                  v["bias"], v["h0"], softplus=sp)
+    names = ["du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias"]
+    if want_dh0:
+        names.append("dh0")
+    for k in names:
+        assert_close(k, host(g[k]), r[k], dtype)
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[3]], ids=_ids)
+def test_trap_bwd_next_to_reset(case):
+    bsz, dim, N, L, dtype, resets, zero_u, sp = case
+    log(f"trap bwd reset {case}")
+    t = _reset_inputs(*case)
+    t["lam"] = msel_inputs.make(bsz, dim, N, L, dtype, 312, with_lam=True)["lam"]
+    d = to_device(t)
+    lam_d = d["lam"]
+    _, _, cs = msel.msel_scan_trap_fwd(d["u"], d["delta"], lam_d, d["A"], d["B"], d["C"],
+                                       d["D"], d["z"], d["bias"], sp, d["h0"],
+                                       return_chunk_states=True)
+    g = msel.msel_scan_trap_bwd(d["u"], d["delta"], lam_d, d["A"], d["B"], d["C"], d["dout"],
+                                cs, d["D"], d["z"], d["bias"], sp, d["h0"], want_dh0=True)
+    torch.cuda.synchronize()
+    v = oracle_vals(t)
+    r = otrap.bwd(v["u"], v["delta"], t.values("lam"), v["A"], v["B"], v["C"], v["dout"],
+                  v["D"], v["z"], v["bias"], v["h0"], softplus=sp)
+    for k in ("du", "ddelta", "dlam", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        assert_close(k, host(g[k]), r[k], dtype)
+
+
+@pytest.mark.parametrize("variant", ["real", "complex"])
+def test_ddelta_with_tiny_steps(variant):
+    """Every step has Delta = softplus(delta + bias) near 1e-4 (delta + bias near -9.2, the
+    lower tail of the input recipe).  ddelta = dDelta * sigmoid(delta + bias): a sigmoid formed
+    as 1 - exp(-Delta) would keep only ~4 digits there, so the whole tensor, whose scale is set
+    by such steps alone, is held to the fp32 bar."""
+    bsz, dim, N, L = 2, 4, 16, 1300
+    log(f"ddelta tiny steps {variant}")
+    t = msel_inputs.make(bsz, dim, N, L, "f32", 313, with_dout=True, with_h0=True,
+                         complex_A=variant == "complex")
+    t["delta"] = (t.values("delta") * np.float32(0.2) - np.float32(9.2) -
+                  t["bias"][None, :, None]).astype(np.float32)
+    d = to_device(t)
+    v = oracle_vals(t)
+    if variant == "real":
+        g = msel.msel_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dout"], d["D"],
+                               d["z"], d["bias"], True, d["h0"])
+        r = oracle.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
+                       v["bias"], v["h0"])
+    else:
+        _, _, cs = msel.msel_scan_complex_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"],
+                                              d["D"], d["z"], d["bias"], True, d["h0"],
+                                              return_chunk_states=True)
+        g = msel.msel_scan_complex_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dout"],
+                                       cs, d["D"], d["z"], d["bias"], True, d["h0"])
+        r = ocplx.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
+                      v["bias"], v["h0"])
+    torch.cuda.synchronize()
+    x = v["delta"].astype(np.float64) + v["bias"][None, :, None]
+    sp = np.log1p(np.exp(x))
+    assert 5e-5 < sp.min() and sp.max() < 4e-4, (sp.min(), sp.max())
+    for k in ("ddelta", "ddelta_bias", "du"):
+        assert_close(k, host(g[k]), r[k], "f32")
