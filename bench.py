@@ -1,19 +1,27 @@
 """Benchmark of the selective scan on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu] [--no-extra]
 
 A step is one pass of the whole hot path over one batch of synthetic input resident in HBM:
 the fused forward scan (out, final state and the state at every chunk boundary), then the
 backward with recomputation (all gradients): it rebuilds every state inside the chunks from
-those boundary states and runs the chunk carry backward for the adjoint.  The standalone
-chunk-carry entry point is timed separately, and so are the recurrent (decode) step and
-the short causal convolution + SiLU that produces the scan's input (forward, backward and its
-decode step, width 4, at the same batch, channels, length and dtype).  The
-default workload is batch 8, d_model 768 x expand 2 = 1536 channels, dstate 16, seqlen 2048,
-bf16 activations with fp32 state -- the workload that runs both the forward and the backward.
+those boundary states and runs the chunk carry backward for the adjoint.  Consecutive steps
+take consecutive copies of the inputs, from a ring of copies larger than the chip's 256 MB
+last-level cache (MALL), so that each step's forward reads its inputs from HBM.  The default
+workload is batch 8, d_model 768 x expand 2 = 1536 channels, dstate 16, seqlen 2048, bf16
+activations with fp32 state -- the workload that runs both the forward and the backward.
 
-Prints one JSON line: the whole-step throughput in token*channels/s, the roofline of the
-dominant kernel (from HIP events on the launch stream over the timed steps), per-kernel
+Besides the step it measures, each with a cold last-level cache (a 512 MiB copy before every
+launch) and reported as median / p10 / p90 over the launches:
+  * the forward, the gradient kernel and the chunk-carry pass of the step's workload alone;
+  * the same passes at the other workloads' full sizes: the selective-copying shape (fp32
+    forward), the 64k-step bf16 forward (chunk carry across 128 chunks) and the fp32 backward
+    with recomputed chunk states;
+  * the variants at the step's shape: the recurrent (decode) step, the exponential-trapezoidal
+    and complex forwards and backwards, and the short causal convolution + SiLU (width 4).
+
+Prints one JSON line: the whole-step throughput in token*channels/s, the HBM roofline of the
+dominant kernel (from HIP events on its launch stream over the timed steps), per-kernel
 figures, and the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -28,46 +36,48 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector: 256 CUs x 256 flop/clk x 2.4 GHz
+# VALU issue of the chip: one wave64 instruction per SIMD every 4 clocks (16 lanes per clock),
+# 1024 SIMDs at 2.4 GHz = 39.3 T lane-instructions/s; the scan kernels issue VALU
+# instructions one at a time (their dual-issue share is ~13% by the SQ counters)
+VALU_ISSUE_PEAK = 1024 * 16 * 2.4e9
 METRIC = "selective-scan fwd/bwd tokens·channels/s and achieved HBM GB/s (% of peak)"
-# fp32 flops per (batch, channel, time, state) update, FMA = 2, exp2 = 1 (the arithmetic of
-# the recurrence itself; the parallel scan's replay and combine steps are not counted)
-FLOPS_FWD = 7      # Delta*A, exp2, (Delta u)*B, h = a h + p, y += C h
-FLOPS_BWD = 20     # recompute h (5), adjoint (3), g = lam h a (2), dA, dDelta, du, dB, dC (10)
-FLOPS_BWD_Z = 2    # y += C h, rebuilt for dz when there is a gate
-FLOPS_TRAP = 10    # Delta*A, exp2, c*B_prev, (gamma u)*B, p = a*(c B_prev) + .., h, y
-FLOPS_TRAP_BWD = 31  # the backward's 20 + the previous/next-step input terms of the rule
-# per complex state (a pair of real states) and step: Delta*A_re, Delta*A_im, exp2, sin, cos,
-# the two products of the transition, (Delta u)*B for both parts, h = a h + p (4 fma), y (2 fma)
-FLOPS_COMPLEX_PAIR = 21
-# its backward per complex state and step: recompute h (17), the adjoint conj(a) G + C dy (12),
-# X = conj(G) a h (12), the dDelta, dA, du, dB and dC terms (18)
-FLOPS_COMPLEX_BWD_PAIR = 59
+# The least VALU work per (batch, channel, time, state) update that the recurrence itself
+# needs, in instructions (each exp is one instruction): the forward Delta*A, exp, (Delta u)*B,
+# h = a h + p, y += C h; the backward recomputes h (4), runs the adjoint lam = a lam + C dy (2),
+# forms g = lam h a (2), and adds into dA, dDelta, sum(lam B), dB, dC (5), plus y += C h for
+# the gate's dz (1).
+VALU_FLOOR_FWD = 5
+VALU_FLOOR_BWD = 13
+VALU_FLOOR_BWD_Z = 1
+CONV_WIDTH = 4     # taps of the short causal convolution before the scan
+CACHE_BYTES = 256 << 20   # MI355X last-level cache (MALL)
+FLUSH_MIB = 512           # a copy of this size before every cold launch evicts it
+COLD_REPS = 10
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, per kernel, of the default workload
 TRAFFIC_FILE = "profiles/{kernel}_d768x2_bf16_traffic.txt"
-CONV_WIDTH = 4     # taps of the short causal convolution before the scan
-CONV_SETS = 4      # input copies the convolution timing cycles through (> last-level cache)
 
 
-def algorithmic_bytes(w, nchunks):
+def algorithmic_bytes(w, nchunks, dtype_bytes=None):
     """Bytes each pass must move at least once between HBM and the chip."""
-    s = 2 if w.dtype == "bf16" else 4
+    s = dtype_bytes or (2 if w.dtype == "bf16" else 4)
     tc = w.batch * w.dim * w.seqlen
     bnl = w.batch * w.dstate * w.seqlen
     states = w.batch * w.dim * nchunks * w.dstate * 4
     dn, d = w.dim * w.dstate, w.dim
-    fwd = 4 * tc * s + 2 * bnl * s + states + w.batch * w.dim * w.dstate * 4 + dn * 4 + 2 * d * 4
+    # u, delta, z in, out out; B, C in; final state out; A, D, bias in.  The chunk states the
+    # forward also writes are implementation overhead (0.4-3% of it) and are not counted.
+    fwd = 4 * tc * s + 2 * bnl * s + w.batch * w.dim * w.dstate * 4 + dn * 4 + 2 * d * 4
+    # u, delta in; B in; A, bias in; chunk states out (the pass's product)
     cc = 2 * tc * s + bnl * s + states + dn * 4 + d * 4
-    # the gradient kernel: u, delta, dout, z in; du, ddelta, dz out; B, C in; dB, dC out
-    # (fp32); chunk-start states and adjoint carries in; A, D, bias in; dA, dD, dbias out
-    bwd_main = 7 * tc * s + 2 * bnl * s + 2 * bnl * 4 + 2 * states + 2 * (dn + 2 * d) * 4
-    # the whole msel_scan_bwd call: the same tensors once (its summary pass reads delta, dout
-    # and z a second time; that re-read is not counted)
+    # the whole backward: u, delta, dout, z in; du, ddelta, dz out; B, C in; dB, dC out
+    # (fp32); A, D, bias in; dA, dD, dbias out.  The gradient kernel alone moves the same
+    # tensors, plus the chunk-start states and adjoint carries it reads (counted for it).
     bwd = 7 * tc * s + 2 * bnl * s + 2 * bnl * 4 + 2 * dn * 4 + 4 * d * 4
+    bwd_main = bwd + 2 * states
     return {"fwd": fwd, "chunk_carry": cc, "bwd_main": bwd_main, "bwd": bwd}
 
 
-def measured_traffic(workload_name, kernel="bwd_main_kernel"):
+def measured_traffic(workload_name, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summary, or None when there is none for this workload or the kernel's sources have changed
     since the counters were taken."""
@@ -97,12 +107,91 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only the step (no cold per-kernel, variant or other-workload "
+                         "timings): for profiler runs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle over the whole workload for at least this long")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB once (a plain copy "
                          "kernel of known size that scales the HBM byte counters)")
     return ap.parse_args()
+
+
+def summary(ms):
+    """mean / median / p10 / p90 of a list of per-launch times in ms."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)),
+            "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "n": int(a.size)}
+
+
+def entry(st, alg_bytes, tcs, what, updates=None, valu_floor=None, basis="median"):
+    """A kernels[...] record: times, and the algorithmic GB/s and tc/s at the `basis` time."""
+    ms = st[basis]
+    sec = ms * 1e-3
+    gbs = alg_bytes / sec / 1e9
+    e = {"ms": round(ms, 4), "ms_basis": basis,
+         "ms_stats": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in st.items()},
+         "alg_bytes": int(alg_bytes), "GB/s": round(gbs, 1),
+         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "tc_per_s": float(f"{tcs / sec:.4g}"),
+         "what": what}
+    if updates is not None and valu_floor is not None:
+        floor_s = updates * valu_floor / VALU_ISSUE_PEAK
+        e["valu_issue"] = {"floor_instr_per_update": valu_floor, "floor_ms": round(floor_s * 1e3, 4),
+                           "frac": round(floor_s / sec, 4)}
+    return e
+
+
+class Ctx:
+    """Device, dtype and the helpers every timing below uses."""
+
+    def __init__(self, torch, np, dev):
+        self.torch, self.np, self.dev = torch, np, dev
+        n = FLUSH_MIB * (1 << 20) // 4
+        self.flush_src = torch.ones(n, device=dev, dtype=torch.float32)
+        self.flush_dst = torch.empty_like(self.flush_src)
+
+    def put(self, v, dt):
+        torch, np = self.torch, self.np
+        if v is None:
+            return None
+        if v.dtype == np.uint16:
+            return torch.from_numpy(v.view(np.int16)).to(self.dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(v)).to(device=self.dev, dtype=dt)
+
+    def device_inputs(self, t, dtype):
+        torch = self.torch
+        act = torch.bfloat16 if dtype == "bf16" else torch.float32
+        return {k: self.put(v, act if k in ("u", "delta", "z", "B", "C", "dout", "lam")
+                            else torch.float32) for k, v in t.items()}
+
+    def flush(self):
+        """Evict the last-level cache: a 512 MiB copy (reads and writes twice its size)."""
+        self.flush_dst.copy_(self.flush_src)
+
+    def cold(self, fn, reps=COLD_REPS, events=None):
+        """Per-launch ms of fn() (which enqueues on the current stream), each launch after a
+        cache flush.  events(): optional pair of events fn records itself (the gradient
+        kernel's), else the events bracket the whole call."""
+        torch = self.torch
+        fn()  # warm the code path
+        out = []
+        for _ in range(reps):
+            self.flush()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            if events is None:
+                ev[0].record()
+                fn()
+                ev[1].record()
+            else:
+                for e in ev:
+                    e.record()
+                fn(ev)
+            torch.cuda.synchronize()
+            out.append(ev[0].elapsed_time(ev[1]))
+        return summary(out)
 
 
 def main():
@@ -121,20 +210,26 @@ def main():
     w = msel_inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    cx = Ctx(torch, np, dev)
     t = msel_inputs.make_workload(w, with_dout=True)
-    act = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-
-    def put(v, dt):
-        if v is None:
-            return None
-        if v.dtype == np.uint16:
-            return torch.from_numpy(v.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(v)).to(device=dev, dtype=dt)
-
-    d = {k: put(v, act if k in ("u", "delta", "z", "B", "C", "dout") else torch.float32)
-         for k, v in t.items()}
+    d0 = cx.device_inputs(t, w.dtype)
     nch = msel.num_chunks(w.seqlen)
-    ws = torch.empty(msel.bwd_workspace_bytes(d["u"], d["A"], True), device=dev,
+    s_ = 2 if w.dtype == "bf16" else 4
+    tc = w.batch * w.dim * w.seqlen
+    upd = tc * w.dstate
+    alg = algorithmic_bytes(w, nch)
+
+    # a ring of input copies, together more than twice the last-level cache
+    streamed = ("u", "delta", "z", "dout", "B", "C")
+    set_bytes = sum(d0[k].numel() * d0[k].element_size() for k in streamed if d0[k] is not None)
+    nsets = max(2, min(8, -(-3 * CACHE_BYTES // set_bytes)))
+    sets = [d0] + [{k: (v.clone() if k in streamed and v is not None else v)
+                    for k, v in d0.items()} for _ in range(nsets - 1)]
+    for s in sets:
+        s["out"] = torch.empty_like(d0["u"])
+        s["fin"] = torch.empty(w.batch, w.dim, w.dstate, device=dev, dtype=torch.float32)
+        s["cs"] = torch.empty(w.batch, w.dim, nch, w.dstate, device=dev, dtype=torch.float32)
+    ws = torch.empty(msel.bwd_workspace_bytes(d0["u"], d0["A"], True), device=dev,
                      dtype=torch.uint8)
 
     if args.calib_copy_mib > 0:
@@ -146,285 +241,92 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    def fwd(s):
+        return msel.msel_scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"],
+                                  s["bias"], True, out=s["out"], final_state=s["fin"],
+                                  chunk_states=s["cs"], return_chunk_states=True)
+
+    def bwd(s, main_events=None, states=True):
+        return msel.msel_scan_bwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["dout"], s["D"],
+                                  s["z"], s["bias"], True, chunk_states=s["cs"] if states else None,
+                                  workspace=ws, main_events=main_events)
+
     def new_events(k):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
         for e in ev:   # the library records the gradient-kernel events itself: create them
             e.record()
         return ev
 
-    def step(ev=None):
+    def step(k, ev=None):
         """fwd (out, final state, one state per chunk) then bwd, which recomputes every state
-        inside the chunks and runs the chunk carry backward for the adjoint.  All launches go
-        to torch's current stream, on which the events are recorded."""
+        inside the chunks and runs the chunk carry backward for the adjoint, on input copy
+        k mod nsets.  All launches go to torch's current stream, on which the events are
+        recorded."""
+        s = sets[k % nsets]
         if ev is not None:
             ev[0].record()
-        out, fin, cs = msel.msel_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],
-                                          d["z"], d["bias"], True, return_chunk_states=True)
+        fwd(s)
         if ev is not None:
             ev[1].record()
-        g = msel.msel_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dout"], d["D"],
-                               d["z"], d["bias"], True, chunk_states=cs, workspace=ws,
-                               main_events=None if ev is None else (ev[3], ev[4]))
+        g = bwd(s, None if ev is None else (ev[3], ev[4]))
         if ev is not None:
             ev[2].record()
-        return out, fin, g
+        return g
 
-    for _ in range(args.warmup):
-        step()
+    for k in range(args.warmup):
+        step(k)
     torch.cuda.synchronize()
     evs = [new_events(5) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(evs[k])
+        step(args.warmup + k, evs[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    per = {
-        "fwd": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
-        "bwd": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
-        "bwd_main": float(np.mean([e[3].elapsed_time(e[4]) for e in evs])),
+    step_ms = {
+        "fwd": summary([e[0].elapsed_time(e[1]) for e in evs]),
+        "bwd": summary([e[1].elapsed_time(e[2]) for e in evs]),
+        "bwd_main": summary([e[3].elapsed_time(e[4]) for e in evs]),
     }
-
-    tc = w.batch * w.dim * w.seqlen
-    upd = tc * w.dstate
-    alg = algorithmic_bytes(w, nch)
-    # the standalone chunk-carry pass, timed on its own after the steps
-    cc_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for _ in range(3):
-        msel.msel_scan_chunk_carry(d["u"], d["delta"], d["A"], d["B"], d["bias"], True)
-    cc_ev[0].record()
-    for _ in range(args.steps):
-        msel.msel_scan_chunk_carry(d["u"], d["delta"], d["A"], d["B"], d["bias"], True)
-    cc_ev[1].record()
-    torch.cuda.synchronize()
-    per["chunk_carry"] = cc_ev[0].elapsed_time(cc_ev[1]) / args.steps
-
-    # the recurrent (decode) step at the same batch and channels: seqlen 1, state in place
-    st = {k: (None if v is None else (v[..., :1].contiguous() if k in ("u", "delta", "z", "B", "C")
-                                        else v)) for k, v in d.items()}
-    state = torch.zeros(w.batch, w.dim, w.dstate, device=dev, dtype=torch.float32)
-    dec_out = torch.empty_like(st["u"])
-    def decode():
-        msel.msel_scan_fwd(st["u"], st["delta"], st["A"], st["B"], st["C"], st["D"], st["z"],
-                           st["bias"], True, state, out=dec_out, final_state=state)
-    dec_per_graph, dec_reps = 32, 10
-    per["decode_step"] = graph_time(decode, dec_per_graph, dec_reps)
-
-    # the exponential-trapezoidal forward at the same shape: one more input stream (lambda);
-    # calls alternate between two copies of the streamed inputs (~400 MB, more than the
-    # last-level cache)
-    lam = put(msel_inputs.make(w.batch, w.dim, w.dstate, w.seqlen, w.dtype, w.seed,
-                               with_lam=True)["lam"], act)
-    tsets = [{k: (d[k] if i == 0 else d[k].clone()) for k in ("u", "delta", "z")} |
-             {"lam": lam if i == 0 else lam.clone(), "out": torch.empty_like(d["u"])}
-             for i in range(2)]
-    trap_cs = torch.empty(w.batch, w.dim, nch, w.dstate, device=dev, dtype=torch.float32)
-    trap_fin = torch.empty(w.batch, w.dim, w.dstate, device=dev, dtype=torch.float32)
-
-    def trap_fwd(i):
-        c = tsets[i % 2]
-        msel.msel_scan_trap_fwd(c["u"], c["delta"], c["lam"], d["A"], d["B"], d["C"], d["D"],
-                                c["z"], d["bias"], True, out=c["out"], final_state=trap_fin,
-                                chunk_states=trap_cs)
-    for i in range(4):
-        trap_fwd(i)
-    tev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    tev[0].record()
-    for i in range(args.steps):
-        trap_fwd(i)
-    tev[1].record()
-    torch.cuda.synchronize()
-    per["trap_fwd"] = tev[0].elapsed_time(tev[1]) / args.steps
-    # its backward, from the chunk states of copy 0 (the call streams ~550 MB: no rotation)
-    trap_fwd(0)
-    trap_ws = torch.empty(msel.bwd_workspace_bytes(d["u"], d["A"], True), device=dev,
-                          dtype=torch.uint8)
-
-    def trap_bwd():
-        c = tsets[0]
-        msel.msel_scan_trap_bwd(c["u"], c["delta"], c["lam"], d["A"], d["B"], d["C"], d["dout"],
-                                trap_cs, d["D"], c["z"], d["bias"], True, workspace=trap_ws)
-    for _ in range(3):
-        trap_bwd()
-    tev[0].record()
-    for _ in range(args.steps):
-        trap_bwd()
-    tev[1].record()
-    torch.cuda.synchronize()
-    per["trap_bwd"] = tev[0].elapsed_time(tev[1]) / args.steps
-    del tsets, trap_ws
-
-    # the complex-valued (rotational) forward at the same shape: dstate 16 = 8 complex states,
-    # rates -1/2 + i pi j; calls alternate between the two input copies above
-    cA = put(msel_inputs.make(1, w.dim, w.dstate, 1, "f32", w.seed, complex_A=True)["A"],
-             torch.float32)
-    csets = [{k: (d[k] if i == 0 else d[k].clone()) for k in ("u", "delta", "z")} |
-             {"out": torch.empty_like(d["u"])} for i in range(2)]
-
-    def complex_fwd(i):
-        c = csets[i % 2]
-        msel.msel_scan_complex_fwd(c["u"], c["delta"], cA, d["B"], d["C"], d["D"], c["z"],
-                                   d["bias"], True, out=c["out"], final_state=trap_fin,
-                                   chunk_states=trap_cs)
-    for i in range(4):
-        complex_fwd(i)
-    cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    cev[0].record()
-    for i in range(args.steps):
-        complex_fwd(i)
-    cev[1].record()
-    torch.cuda.synchronize()
-    per["complex_fwd"] = cev[0].elapsed_time(cev[1]) / args.steps
-    # its backward, from the chunk states of copy 0
-    complex_fwd(0)
-    cws = torch.empty(msel.bwd_workspace_bytes(d["u"], d["A"], True), device=dev,
-                      dtype=torch.uint8)
-
-    def complex_bwd():
-        c = csets[0]
-        msel.msel_scan_complex_bwd(c["u"], c["delta"], cA, d["B"], d["C"], d["dout"], trap_cs,
-                                   d["D"], c["z"], d["bias"], True, workspace=cws)
-    for _ in range(3):
-        complex_bwd()
-    cev[0].record()
-    for _ in range(args.steps):
-        complex_bwd()
-    cev[1].record()
-    torch.cuda.synchronize()
-    per["complex_bwd"] = cev[0].elapsed_time(cev[1]) / args.steps
-    del csets, cws
-
-    # the short causal convolution + SiLU that makes the scan's input, at the same batch,
-    # channels, length and dtype, width 4, with bias and incoming state: forward, backward
-    # (zero-fill + one kernel) and the decode step (seqlen 1, state updated in place)
-    cv = {k: put(v, act if k in ("x", "state", "dout") else torch.float32)
-          for k, v in msel_inputs.make_conv(w.batch, w.dim, w.seqlen, CONV_WIDTH, w.dtype,
-                                            w.seed, with_state=True, with_dout=True).items()}
-    # consecutive calls cycle through CONV_SETS copies of the streamed tensors, more than the
-    # chip's 256 MB last-level cache holds, so that each call reads its inputs from HBM
-    sets = [{"x": cv["x"] if i == 0 else cv["x"].clone(),
-             "dout": cv["dout"] if i == 0 else cv["dout"].clone(),
-             "out": torch.empty_like(cv["x"]), "state_out": torch.empty_like(cv["state"])}
-            for i in range(CONV_SETS)]
-
-    def conv_fwd(i):
-        c = sets[i % CONV_SETS]
-        msel.msel_conv1d_fwd(c["x"], cv["weight"], cv["bias"], cv["state"], out=c["out"],
-                             state_out=c["state_out"])
-
-    def conv_bwd(i):
-        c = sets[i % CONV_SETS]
-        msel.msel_conv1d_bwd(c["x"], cv["weight"], c["dout"], cv["bias"], cv["state"],
-                             want_dstate=True)
-
-    for name, fn in (("conv_fwd", conv_fwd), ("conv_bwd", conv_bwd)):
-        for i in range(CONV_SETS):
-            fn(i)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record()
-        for i in range(args.steps):
-            fn(i)
-        ev[1].record()
-        torch.cuda.synchronize()
-        per[name] = ev[0].elapsed_time(ev[1]) / args.steps
-    del sets
-    cx1 = cv["x"][..., :1].contiguous()
-    cache = cv["state"].clone()
-    conv_dec_out = torch.empty_like(cx1)
-
-    def conv_decode():
-        msel.msel_conv1d_fwd(cx1, cv["weight"], cv["bias"], cache, out=conv_dec_out,
-                             state_out=cache)
-    per["conv_decode_step"] = graph_time(conv_decode, dec_per_graph, dec_reps)
-
-    fl_bwd = FLOPS_BWD + (FLOPS_BWD_Z if d.get("z") is not None else 0)
-    flops = {"fwd": FLOPS_FWD * upd, "bwd_main": fl_bwd * upd, "trap_fwd": FLOPS_TRAP * upd,
-             "complex_fwd": FLOPS_COMPLEX_PAIR * upd // 2}
-    alg["trap_fwd"] = alg["fwd"] + tc * (2 if w.dtype == "bf16" else 4)  # + lambda
-    alg["complex_fwd"] = alg["fwd"]
-    # + lambda in, dlambda out
-    alg["trap_bwd"] = alg["bwd"] + 2 * tc * (2 if w.dtype == "bf16" else 4)
-    alg["complex_bwd"] = alg["bwd"]
-    flops["complex_bwd"] = FLOPS_COMPLEX_BWD_PAIR * upd // 2
-    flops["trap_bwd"] = (FLOPS_TRAP_BWD + (FLOPS_BWD_Z if d.get("z") is not None else 0)) * upd
-    kernels = {}
-    for n in ("fwd", "chunk_carry", "bwd_main", "bwd", "trap_fwd", "trap_bwd", "complex_fwd",
-              "complex_bwd"):
-        sec = per[n] * 1e-3
-        gbs = alg[n] / sec / 1e9
-        kernels[n] = {"ms": round(per[n], 4), "alg_bytes": alg[n], "GB/s": round(gbs, 1),
-                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                      "tc_per_s": float(f"{tc / sec:.4g}")}
-        if n in flops:
-            kernels[n]["TFLOP/s"] = round(flops[n] / sec / 1e12, 2)
-    kernels["fwd"]["what"] = "scan_fwd_kernel (one launch)"
-    kernels["complex_bwd"]["what"] = ("the msel_scan_complex_bwd call (zero-fills, summary, link "
-                                      "and the pair-per-wavefront gradient kernel), timed apart "
-                                      "from the step")
-    kernels["trap_bwd"]["what"] = ("the msel_scan_trap_bwd call (zero-fills, summary, link and "
-                                   "the trapezoidal gradient kernel), timed apart from the step")
-    kernels["complex_fwd"]["what"] = ("scan_cplx_fwd_kernel: the complex-valued (rotational) "
-                                      "forward, dstate 16 as 8 complex states, one launch, "
-                                      "timed apart from the step")
-    kernels["trap_fwd"]["what"] = ("scan_fwd_kernel with the exponential-trapezoidal rule "
-                                   "(msel_scan_trap_fwd, lambda as one more input), one launch, "
-                                   "timed apart from the step")
-    kernels["chunk_carry"]["what"] = "chunk_carry_kernel (one launch), timed apart from the step"
-    kernels["bwd_main"]["what"] = "bwd_main_kernel, the chunk-parallel gradient kernel"
-    kernels["bwd"]["what"] = ("the msel_scan_bwd call: zero-fills, summary, link and "
-                              "bwd_main_kernel")
-    s_ = 2 if w.dtype == "bf16" else 4
-    dec_bytes = (2 * w.batch * w.dim * w.dstate * 4 + 4 * w.batch * w.dim * s_ +
-                 2 * w.batch * w.dstate * s_ + w.dim * w.dstate * 4 + 2 * w.dim * 4)
-    dsec = per["decode_step"] * 1e-3
-    kernels["decode_step"] = {
-        "ms": round(per["decode_step"], 4), "alg_bytes": dec_bytes,
-        "GB/s": round(dec_bytes / dsec / 1e9, 1),
-        "hbm_frac": round(dec_bytes / dsec / 1e9 / HBM_PEAK_GBS, 4),
-        "tc_per_s": float(f"{w.batch * w.dim / dsec:.4g}"),
-        "what": "scan_step_kernel: one recurrent step (seqlen 1) of every channel, state "
-                "updated in place; steps replayed from a HIP graph"}
-
-    rows = w.batch * w.dim
-    H = CONV_WIDTH - 1
-    conv_bytes = {
-        # x in, out out; state in and out; taps and bias in
-        "conv_fwd": 2 * tc * s_ + 2 * rows * H * s_ + w.dim * (CONV_WIDTH + 1) * 4,
-        # x, dout in, dx out; state in, its fp32 gradient out; taps, bias in, their grads out
-        "conv_bwd": 3 * tc * s_ + rows * H * (s_ + 4) + 2 * w.dim * (CONV_WIDTH + 1) * 4,
-        "conv_decode_step": 2 * rows * s_ + 2 * rows * H * s_ + w.dim * (CONV_WIDTH + 1) * 4,
+    vf_bwd = VALU_FLOOR_BWD + (VALU_FLOOR_BWD_Z if d0.get("z") is not None else 0)
+    kernels = {
+        "fwd": entry(step_ms["fwd"], alg["fwd"], tc, "scan_fwd_kernel in the step (one launch)",
+                     upd, VALU_FLOOR_FWD),
+        "bwd": entry(step_ms["bwd"], alg["bwd"], tc, "the msel_scan_bwd call in the step: "
+                     "zero-fills, summary, link and bwd_main_kernel"),
+        "bwd_main": entry(step_ms["bwd_main"], alg["bwd_main"], tc,
+                          "bwd_main_kernel in the step, the chunk-parallel gradient kernel",
+                          upd, vf_bwd),
     }
-    what = {"conv_fwd": "conv_fwd_kernel: causal depthwise conv (width 4) + bias + SiLU, "
-                        "state in and out (one launch)",
-            "conv_bwd": "the msel_conv1d_bwd call: zero-fill of the tap/bias gradients and "
-                        "conv_bwd_kernel (recomputes the activation)",
-            "conv_decode_step": "conv_step_kernel: msel_conv1d_fwd at seqlen 1 with the state "
-                                "updated in place; steps replayed from a HIP graph"}
-    for n, nb in conv_bytes.items():
-        sec = per[n] * 1e-3
-        toks = rows if n == "conv_decode_step" else tc
-        kernels[n] = {"ms": round(per[n], 4), "alg_bytes": nb, "GB/s": round(nb / sec / 1e9, 1),
-                      "hbm_frac": round(nb / sec / 1e9 / HBM_PEAK_GBS, 4),
-                      "tc_per_s": float(f"{toks / sec:.4g}"), "what": what[n]}
-        if n in ("conv_fwd", "conv_bwd"):
-            kernels[n]["traffic"] = measured_traffic(w.name, n + "_kernel")
+    for k in ("fwd", "bwd_main"):
+        kernels[k]["traffic"] = measured_traffic(
+            w.name, "scan_fwd_kernel" if k == "fwd" else "bwd_main_kernel")
 
-    # the dominant kernel: the gradient kernel, bound by VALU arithmetic (an exp2 per update
-    # and ~20 flops), measured with the library's events on the launch stream
-    sec = per["bwd_main"] * 1e-3
-    ach = flops["bwd_main"] / sec / 1e12
+    # the dominant kernel of the step: its HBM roofline from the timed steps' mean launch
+    # duration (the figure rocprofv3's kernel-trace average is compared with)
+    dom = max(("fwd", "bwd_main"), key=lambda k: step_ms[k]["mean"])
+    dsec = step_ms[dom]["mean"] * 1e-3
+    dbytes = alg[dom]
+    ach = dbytes / dsec / 1e9
+    vfloor = VALU_FLOOR_FWD if dom == "fwd" else vf_bwd
     roofline = {
-        "kernel": "bwd_main_kernel", "bound": "alu", "achieved": round(ach, 2),
-        "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(ach / FP32_VECTOR_PEAK_TFLOPS, 4),
-        "traffic": measured_traffic(w.name),
-        "flops_per_launch": flops["bwd_main"],
-        "flops_per_update": fl_bwd, "updates_per_launch": upd,
-        "alg_bytes_per_launch": alg["bwd_main"],
-        "hbm_GBs": kernels["bwd_main"]["GB/s"], "hbm_frac": kernels["bwd_main"]["hbm_frac"],
-        "ms_per_launch": round(per["bwd_main"], 4),
+        "kernel": "scan_fwd_kernel" if dom == "fwd" else "bwd_main_kernel",
+        "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(ach / HBM_PEAK_GBS, 4),
+        "traffic": kernels[dom]["traffic"],
+        "alg_bytes_per_launch": dbytes, "ms_per_launch_mean": round(step_ms[dom]["mean"], 4),
+        "ms_per_launch_median": round(step_ms[dom]["median"], 4),
+        "valu_issue": {"floor_instr_per_update": vfloor, "updates_per_launch": upd,
+                       "peak_lane_instr_per_s": VALU_ISSUE_PEAK,
+                       "frac": round(upd * vfloor / VALU_ISSUE_PEAK / dsec, 4)},
     }
+
+    extra = {}
+    if not args.no_extra:
+        extra = extra_timings(cx, msel, msel_inputs, w, sets, nsets, alg, tc, upd, vf_bwd, ws,
+                              fwd, bwd, args)
+    kernels.update(extra)
 
     cpu = None
     if not args.no_cpu:
@@ -439,16 +341,227 @@ def main():
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
                    "seqlen": w.seqlen, "io_dtype": w.dtype,
-                   "step": "fwd (with chunk-boundary states) + bwd"},
+                   "step": "fwd (with chunk-boundary states) + bwd",
+                   "input_copies": nsets, "input_copy_bytes": int(set_bytes)},
         "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
 
-def graph_time(fn, per_graph, reps):
+def extra_timings(cx, msel, msel_inputs, w, sets, nsets, alg, tc, upd, vf_bwd, ws, fwd, bwd,
+                  args):
+    """Cold-cache per-kernel timings of the step's passes, the other workloads and the
+    variants."""
+    torch, np = cx.torch, cx.np
+    dev = cx.dev
+    s_ = 2 if w.dtype == "bf16" else 4
+    nch = msel.num_chunks(w.seqlen)
+    k = {}
+    s = sets[0]
+    k["fwd_cold"] = entry(cx.cold(lambda: fwd(s)), alg["fwd"], tc,
+                          "scan_fwd_kernel, one launch after a 512 MiB cache flush", upd,
+                          VALU_FLOOR_FWD)
+    k["bwd_main_cold"] = entry(cx.cold(lambda ev=None: bwd(s, None if ev is None else ev),
+                                       events=True),
+                               alg["bwd_main"], tc, "bwd_main_kernel, one launch after a "
+                               "512 MiB cache flush", upd, vf_bwd)
+    k["chunk_carry_cold"] = entry(
+        cx.cold(lambda: msel.msel_scan_chunk_carry(s["u"], s["delta"], s["A"], s["B"], s["bias"],
+                                                   True, chunk_states=s["cs"],
+                                                   final_state=s["fin"])),
+        alg["chunk_carry"], tc, "chunk_carry_kernel (one launch) after a cache flush")
+
+    # the other workloads at their full sizes
+    for wid, passes in ((1, ("fwd", "chunk_carry", "bwd")), (3, ("fwd", "chunk_carry", "bwd")),
+                        (4, ("fwd", "bwd"))):
+        if wid == args.workload:
+            continue
+        ow = msel_inputs.WORKLOADS[wid]
+        od = device_workload(torch, ow, dev)
+        onch = msel.num_chunks(ow.seqlen)
+        otc = ow.batch * ow.dim * ow.seqlen
+        oupd = otc * ow.dstate
+        oalg = algorithmic_bytes(ow, onch)
+        od["out"] = torch.empty_like(od["u"])
+        od["fin"] = torch.empty(ow.batch, ow.dim, ow.dstate, device=dev, dtype=torch.float32)
+        od["cs"] = torch.empty(ow.batch, ow.dim, onch, ow.dstate, device=dev,
+                               dtype=torch.float32)
+        ows = torch.empty(msel.bwd_workspace_bytes(od["u"], od["A"], False), device=dev,
+                          dtype=torch.uint8)
+        tag = f"w{wid}"
+        shape = f"{ow.batch}x{ow.dim}x{ow.dstate}x{ow.seqlen} {ow.dtype}"
+
+        def ofwd():
+            msel.msel_scan_fwd(od["u"], od["delta"], od["A"], od["B"], od["C"], od["D"],
+                               od["z"], od["bias"], True, out=od["out"], final_state=od["fin"],
+                               chunk_states=od["cs"], return_chunk_states=True)
+        k[f"fwd_{tag}"] = entry(cx.cold(ofwd), oalg["fwd"], otc,
+                                f"scan_fwd_kernel at workload {wid} ({ow.name}, {shape}), "
+                                "cold cache", oupd, VALU_FLOOR_FWD)
+        k[f"fwd_{tag}"]["workload"] = ow.name
+        if "chunk_carry" in passes:
+            k[f"chunk_carry_{tag}"] = entry(
+                cx.cold(lambda: msel.msel_scan_chunk_carry(
+                    od["u"], od["delta"], od["A"], od["B"], od["bias"], True,
+                    chunk_states=od["cs"], final_state=od["fin"])),
+                oalg["chunk_carry"], otc, f"chunk_carry_kernel at workload {wid}, cold cache")
+        # the backward as that workload's description asks: chunk states rebuilt by the
+        # backward (workload 4: "no stored intermediate states"), else the forward's
+        given = wid != 4
+        ofwd()
+
+        def obwd(ev=None):
+            msel.msel_scan_bwd(od["u"], od["delta"], od["A"], od["B"], od["C"], od["dout"],
+                               od["D"], od["z"], od["bias"], True,
+                               chunk_states=od["cs"] if given else None, workspace=ows,
+                               main_events=ev)
+        vfb = VALU_FLOOR_BWD + VALU_FLOOR_BWD_Z
+        k[f"bwd_main_{tag}"] = entry(cx.cold(obwd, events=True), oalg["bwd_main"], otc,
+                                     f"bwd_main_kernel at workload {wid}, cold cache", oupd, vfb)
+        k[f"bwd_{tag}"] = entry(cx.cold(obwd), oalg["bwd"], otc,
+                                f"the msel_scan_bwd call at workload {wid}, chunk states "
+                                f"{'from the forward' if given else 'rebuilt (none stored)'}, "
+                                "cold cache")
+        del od, ows
+        torch.cuda.empty_cache()
+
+    # the recurrent (decode) step at the same batch and channels: seqlen 1, state in place
+    d = sets[0]
+    st = {k_: (None if v is None else (v[..., :1].contiguous() if k_ in ("u", "delta", "z", "B", "C")
+                                        else v)) for k_, v in d.items()
+          if k_ not in ("out", "fin", "cs")}
+    state = torch.zeros(w.batch, w.dim, w.dstate, device=dev, dtype=torch.float32)
+    dec_out = torch.empty_like(st["u"])
+
+    def decode():
+        msel.msel_scan_fwd(st["u"], st["delta"], st["A"], st["B"], st["C"], st["D"], st["z"],
+                           st["bias"], True, state, out=dec_out, final_state=state)
+    dec_ms = graph_time(torch, decode, 32, 10)
+    dec_bytes = (2 * w.batch * w.dim * w.dstate * 4 + 4 * w.batch * w.dim * s_ +
+                 2 * w.batch * w.dstate * s_ + w.dim * w.dstate * 4 + 2 * w.dim * 4)
+    k["decode_step"] = entry({"mean": dec_ms, "median": dec_ms, "p10": dec_ms, "p90": dec_ms,
+                              "n": 320}, dec_bytes, w.batch * w.dim,
+                             "scan_step_kernel: one recurrent step (seqlen 1) of every channel, "
+                             "state updated in place; mean over 320 steps replayed from HIP "
+                             "graphs")
+
+    # the exponential-trapezoidal and complex variants at the same shape, cold cache
+    lam = cx.put(msel_inputs.make(w.batch, w.dim, w.dstate, w.seqlen, w.dtype, w.seed,
+                                  with_lam=True)["lam"],
+                 torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+    cs2 = torch.empty_like(d["cs"])
+    fin2 = torch.empty_like(d["fin"])
+    out2 = torch.empty_like(d["u"])
+    vws = torch.empty(msel.bwd_workspace_bytes(d["u"], d["A"], True), device=dev,
+                      dtype=torch.uint8)
+
+    def trap_fwd():
+        msel.msel_scan_trap_fwd(d["u"], d["delta"], lam, d["A"], d["B"], d["C"], d["D"], d["z"],
+                                d["bias"], True, out=out2, final_state=fin2, chunk_states=cs2)
+
+    def trap_bwd():
+        msel.msel_scan_trap_bwd(d["u"], d["delta"], lam, d["A"], d["B"], d["C"], d["dout"], cs2,
+                                d["D"], d["z"], d["bias"], True, workspace=vws)
+    k["trap_fwd"] = entry(cx.cold(trap_fwd), alg["fwd"] + tc * s_, tc,
+                          "scan_fwd_kernel with the exponential-trapezoidal rule "
+                          "(msel_scan_trap_fwd, lambda as one more input), cold cache")
+    trap_fwd()
+    k["trap_bwd"] = entry(cx.cold(trap_bwd), alg["bwd"] + 2 * tc * s_, tc,
+                          "the msel_scan_trap_bwd call (zero-fills, summary, link and the "
+                          "trapezoidal gradient kernel), cold cache")
+    cA = cx.put(msel_inputs.make(1, w.dim, w.dstate, 1, "f32", w.seed, complex_A=True)["A"],
+                torch.float32)
+
+    def complex_fwd():
+        msel.msel_scan_complex_fwd(d["u"], d["delta"], cA, d["B"], d["C"], d["D"], d["z"],
+                                   d["bias"], True, out=out2, final_state=fin2,
+                                   chunk_states=cs2)
+
+    def complex_bwd():
+        msel.msel_scan_complex_bwd(d["u"], d["delta"], cA, d["B"], d["C"], d["dout"], cs2,
+                                   d["D"], d["z"], d["bias"], True, workspace=vws)
+    k["complex_fwd"] = entry(cx.cold(complex_fwd), alg["fwd"], tc,
+                             "scan_cplx_fwd_kernel: the complex-valued (rotational) forward, "
+                             "dstate 16 as 8 complex states, cold cache")
+    complex_fwd()
+    k["complex_bwd"] = entry(cx.cold(complex_bwd), alg["bwd"], tc,
+                             "the msel_scan_complex_bwd call (zero-fills, summary, link and the "
+                             "pair-ring gradient kernel), cold cache")
+    del vws, out2
+
+    # the short causal convolution + SiLU that makes the scan's input, at the same batch,
+    # channels, length and dtype, width 4, with bias and incoming state
+    cv = {k_: cx.put(v, (torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+                     if k_ in ("x", "state", "dout") else torch.float32)
+          for k_, v in msel_inputs.make_conv(w.batch, w.dim, w.seqlen, CONV_WIDTH, w.dtype,
+                                             w.seed, with_state=True, with_dout=True).items()}
+    cout = torch.empty_like(cv["x"])
+    cst = torch.empty_like(cv["state"])
+    rows = w.batch * w.dim
+    H = CONV_WIDTH - 1
+
+    def conv_fwd():
+        msel.msel_conv1d_fwd(cv["x"], cv["weight"], cv["bias"], cv["state"], out=cout,
+                             state_out=cst)
+
+    def conv_bwd():
+        msel.msel_conv1d_bwd(cv["x"], cv["weight"], cv["dout"], cv["bias"], cv["state"],
+                             want_dstate=True)
+    conv_bytes = {
+        "conv_fwd": 2 * tc * s_ + 2 * rows * H * s_ + w.dim * (CONV_WIDTH + 1) * 4,
+        "conv_bwd": 3 * tc * s_ + rows * H * (s_ + 4) + 2 * w.dim * (CONV_WIDTH + 1) * 4,
+        "conv_decode_step": 2 * rows * s_ + 2 * rows * H * s_ + w.dim * (CONV_WIDTH + 1) * 4,
+    }
+    k["conv_fwd"] = entry(cx.cold(conv_fwd), conv_bytes["conv_fwd"], tc,
+                          "conv_fwd_kernel: causal depthwise conv (width 4) + bias + SiLU, "
+                          "state in and out (one launch), cold cache")
+    k["conv_bwd"] = entry(cx.cold(conv_bwd), conv_bytes["conv_bwd"], tc,
+                          "the msel_conv1d_bwd call: zero-fill of the tap/bias gradients and "
+                          "conv_bwd_kernel (recomputes the activation), cold cache")
+    for n in ("conv_fwd", "conv_bwd"):
+        k[n]["traffic"] = measured_traffic(w.name, n + "_kernel")
+    cx1 = cv["x"][..., :1].contiguous()
+    cache = cv["state"].clone()
+    conv_dec_out = torch.empty_like(cx1)
+
+    def conv_decode():
+        msel.msel_conv1d_fwd(cx1, cv["weight"], cv["bias"], cache, out=conv_dec_out,
+                             state_out=cache)
+    cd_ms = graph_time(torch, conv_decode, 32, 10)
+    k["conv_decode_step"] = entry({"mean": cd_ms, "median": cd_ms, "p10": cd_ms, "p90": cd_ms,
+                                   "n": 320}, conv_bytes["conv_decode_step"], rows,
+                                  "conv_step_kernel: msel_conv1d_fwd at seqlen 1 with the state "
+                                  "updated in place; mean over 320 steps replayed from HIP "
+                                  "graphs")
+    return k
+
+
+def device_workload(torch, w, dev):
+    """A workload's inputs drawn on the device with a seeded torch generator, in the input
+    recipe's distributions (u, z, dout, B, C, D ~ N(0,1); delta = 0.5 N(0,1); bias =
+    log(expm1(U[1e-3, 1e-1])); A[d, n] = -(n+1)), rounded to nearest-even bf16 where the
+    workload is bf16.  For timing only: the kernels' work does not depend on the values, and
+    drawing the 64k-step workload on the host would take half a minute."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000 + w.seed)
+    act = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    f32 = dict(device=dev, dtype=torch.float32, generator=g)
+
+    def normal(shape, scale=1.0):
+        return (torch.randn(shape, **f32) * scale).to(act)
+    x = {"u": normal((w.batch, w.dim, w.seqlen)), "delta": normal((w.batch, w.dim, w.seqlen), 0.5),
+         "z": normal((w.batch, w.dim, w.seqlen)), "dout": normal((w.batch, w.dim, w.seqlen)),
+         "B": normal((w.batch, w.dstate, w.seqlen)), "C": normal((w.batch, w.dstate, w.seqlen))}
+    x["D"] = torch.randn(w.dim, **f32)
+    x["bias"] = torch.log(torch.expm1(torch.rand(w.dim, **f32) * (1e-1 - 1e-3) + 1e-3))
+    x["A"] = (-(torch.arange(w.dstate, device=dev, dtype=torch.float32) + 1.0)).expand(
+        w.dim, w.dstate).contiguous()
+    return x
+
+
+def graph_time(torch, fn, per_graph, reps):
     """ms per call of `fn` (which only enqueues kernels): one call costs more host time than
     GPU time, so `per_graph` calls are captured in a HIP graph that is replayed `reps` times."""
-    import torch
     for _ in range(5):
         fn()
     torch.cuda.synchronize()
@@ -471,26 +584,59 @@ def graph_time(fn, per_graph, reps):
     return ev[0].elapsed_time(ev[1]) / (per_graph * reps)
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, t, min_seconds):
     """The fp64 oracle, as it stands: forward then backward over the whole workload, repeated
-    until at least `min_seconds` have passed, on at most 16 of this host's cores."""
+    until at least `min_seconds` have passed, on the host threads this process may use (at most
+    16, the host share of one GPU on the GPU hosts); and the same on one thread over a slice of
+    the workload (one batch row, a sixteenth of its channels), scaled by token*channels."""
     import oracle
     v = {k: (None if t.get(k) is None else t.values(k)) for k in t}
     nthreads = min(16, oracle.default_threads())
-    reps, el = 0, 0.0
-    s = time.perf_counter()
-    while el < min_seconds:
-        oracle.fwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"], v["bias"],
-                   nthreads=nthreads)
-        oracle.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
-                   v["bias"], nthreads=nthreads)
-        reps += 1
-        el = time.perf_counter() - s
+
+    def run(vv, threads, secs):
+        reps, el = 0, 0.0
+        s = time.perf_counter()
+        while el < secs:
+            oracle.fwd(vv["u"], vv["delta"], vv["A"], vv["B"], vv["C"], vv["D"], vv["z"],
+                       vv["bias"], nthreads=threads)
+            oracle.bwd(vv["u"], vv["delta"], vv["A"], vv["B"], vv["C"], vv["dout"], vv["D"],
+                       vv["z"], vv["bias"], nthreads=threads)
+            reps += 1
+            el = time.perf_counter() - s
+        return reps, el
+
+    reps, el = run(v, nthreads, min_seconds)
     tcs = reps * w.batch * w.dim * w.seqlen
+    nd = max(1, w.dim // 16)
+    sl = {k: (None if x is None else x) for k, x in v.items()}
+    for k in ("u", "delta", "z", "dout"):
+        sl[k] = v[k][:1, :nd]
+    for k in ("B", "C"):
+        sl[k] = v[k][:1]
+    for k in ("A", "D", "bias"):
+        sl[k] = None if v[k] is None else v[k][:nd]
+    r1, e1 = run(sl, 1, min(3.0, min_seconds))
+    tc1 = r1 * nd * w.seqlen
     return {"value": float(f"{tcs / el:.4g}"), "unit": "token*channels/s", "cores": nthreads,
             "kind": "oracle", "seconds": round(el, 3),
             "sample": f"{reps} x (fwd + bwd) over the whole workload: all {w.batch} batch rows, "
-                      f"{w.dim} channels, seqlen {w.seqlen}, fp64"}
+                      f"{w.dim} channels, seqlen {w.seqlen}, fp64",
+            "host_cpus_visible": os.cpu_count(), "cpu_model": _cpu_model(),
+            "one_thread": {"value": float(f"{tc1 / e1:.4g}"), "unit": "token*channels/s",
+                           "seconds": round(e1, 3),
+                           "sample": f"{r1} x (fwd + bwd) over batch row 0, channels 0..{nd - 1},"
+                                     f" seqlen {w.seqlen}, fp64, one thread"}}
 
 
 if __name__ == "__main__":

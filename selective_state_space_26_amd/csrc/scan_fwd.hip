@@ -17,9 +17,9 @@
 //     pass 2  replay the chain from that state, y_k += C_{n,k} h_k
 //   epilogue: y += D u (initialised up front), out = y * silu(z), one store.
 //
-// A workgroup holds four channels of one batch row, which share B and C: in bf16 their rows of
-// each state are converted to fp32 once per workgroup into a double-buffered LDS stage (see the
-// kernel) and read from there by every wavefront.
+// A workgroup holds four channels of one batch row, which share B and C: their rows of each
+// state are read (and, in bf16, converted to fp32) once per workgroup into a double-buffered
+// LDS stage (see the kernel) and read from there by every wavefront.
 //
 // The state never leaves registers: the carried state of all N states lives in one VGPR
 // (lane n holds h_n), so long sequences are handled by the tile loop with the state carried
@@ -40,21 +40,24 @@
 namespace msel {
 
 // Channels of one batch row per workgroup: with the stage (below), the more share it, the
-// fewer conversions and L2 reads of B and C per channel.
+// fewer conversions and L2 reads of B and C per channel.  (8 and 16 were slower: each state
+// then waits at a wider barrier.)
 constexpr int kFwdStageWaves = 4;
 template <typename T, bool TRAP>
-__host__ __device__ constexpr int fwd_waves() { return sizeof(T) == 2 && !TRAP ? kFwdStageWaves : 4; }
+__host__ __device__ constexpr int fwd_waves() { return !TRAP ? kFwdStageWaves : 4; }
 
-// STAGE (bf16 rows, plain rule): a state's B and C rows over a tile are converted to fp32 once
-// per workgroup, into LDS, and read by each of its wavefronts, instead of being converted by
-// every wavefront: [2 tensors][K/4 words][64 lanes] of 16-byte words, so that a lane's K
-// steps are K/4 words of its own column and the 64 lanes read consecutive words.  Two
+// STAGE (plain rule): a state's B and C rows over a tile are read from L2 once per workgroup
+// (bf16 converted to fp32 on the way), into LDS, and read by each of its wavefronts, instead
+// of by every wavefront: [2 tensors][K/4 words][64 lanes] of 16-byte words, so that a lane's
+// K steps are K/4 words of its own column and the 64 lanes read consecutive words.  Two
 // buffers: the next state's rows are staged while the current one is computed, with one
-// barrier per state.  (The trapezoidal rule and fp32 rows load B and C per wavefront: the
-// fp32 rows would hold twice the registers, and these instantiations have none to spare.)
+// barrier per state.  Without the stage an fp32 wavefront streams 8 KB of B and C rows per
+// state and tile through L2, eight times the HBM bytes it reads.  (The trapezoidal rule loads
+// B and C per wavefront: with the stage it needs 143 VGPRs, 3 wavefronts per SIMD, and ran
+// slower.)
 template <typename T, int K, bool VEC, bool HAS_Z, bool SOFTPLUS, bool TRAP>
 __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(ScanParams p) {
-    constexpr bool STAGE = sizeof(T) == 2 && !TRAP;
+    constexpr bool STAGE = !TRAP;
     constexpr int kFwdWaves = fwd_waves<T, TRAP>();
     using Stage = TileStage<T, K, 2, 64 * kFwdWaves, VEC>;  // rows: B, C of one state
     __shared__ f32x4 stage[STAGE ? 2 : 1][STAGE ? Stage::kWords : 1];

@@ -35,9 +35,23 @@ CONV_SOURCES = ("selective_state_space_26_amd/csrc/conv1d.hip",
                 "selective_state_space_26_amd/csrc/msel_kernels.hpp")
 
 
+FWD_SOURCES = ("selective_state_space_26_amd/csrc/scan_fwd.hip",
+               "selective_state_space_26_amd/csrc/msel_device.hpp",
+               "selective_state_space_26_amd/csrc/msel_kernels.hpp")
+CC_SOURCES = ("selective_state_space_26_amd/csrc/chunk_carry.hip",
+              "selective_state_space_26_amd/csrc/msel_device.hpp",
+              "selective_state_space_26_amd/csrc/msel_kernels.hpp")
+
+
 def sources_of(kernel: str):
     """The sources a kernel is built from (their digest goes into its traffic file)."""
-    return CONV_SOURCES if kernel.startswith("conv_") else BWD_SOURCES
+    if kernel.startswith("conv_"):
+        return CONV_SOURCES
+    if kernel.startswith("scan_fwd"):
+        return FWD_SOURCES
+    if kernel.startswith("chunk_carry"):
+        return CC_SOURCES
+    return BWD_SOURCES
 
 
 def source_digest(files=BWD_SOURCES) -> str:
