@@ -71,7 +71,9 @@ typedef enum {
     MSEL_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than msel_scan_bwd_workspace_bytes */
     MSEL_ERR_ALIAS = 7,       /* an output pointer equals an input pointer                 */
     MSEL_ERR_HIP = 8,         /* the HIP runtime reported an error at launch               */
-    MSEL_ERR_VERSION = 9      /* args->abi_version != MSEL_ABI_VERSION                     */
+    MSEL_ERR_VERSION = 9,     /* args->abi_version != MSEL_ABI_VERSION                     */
+    MSEL_ERR_TOO_LARGE = 10   /* msel_scan_bwd_noalloc: the problem's workspace would exceed */
+                              /* MSEL_NOALLOC_SCRATCH_BYTES                                 */
 } msel_status;
 
 typedef enum { MSEL_F32 = 0, MSEL_BF16 = 1 } msel_dtype;
@@ -172,6 +174,23 @@ size_t msel_scan_bwd_workspace_bytes(const msel_scan_args *args);
  * du, ddelta, dz and dh0 are deterministic. */
 msel_status msel_scan_bwd(const msel_scan_args *args, const msel_scan_grads *grads,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  msel_scan_bwd without the workspace
+ * argument: the same launches and results, with the workspace taken from a static device
+ * array of MSEL_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
+ * until the process ends.  The call allocates nothing (no hipMalloc, no allocating library
+ * routine); on its first call on a device it looks up that device's address of the array.
+ * Problems whose msel_scan_bwd_workspace_bytes exceed MSEL_NOALLOC_SCRATCH_BYTES are refused
+ * with MSEL_ERR_TOO_LARGE before anything is enqueued (with chunk_states given, the workspace
+ * is about 4 * batch * dim * n_chunks * (dstate + 2) bytes; rebuilt, twice the state part).
+ * Every call on a device shares that device's array: calls that overlap on one device (on
+ * different streams, or from different threads) race and give wrong results; calls in one
+ * stream's order are safe.  The workspace needs no clearing between calls: the backward
+ * writes every value of it before reading it. */
+#define MSEL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+msel_status msel_scan_bwd_noalloc(const msel_scan_args *args, const msel_scan_grads *grads,
+                                  hipStream_t stream);
 
 /* msel_scan_bwd for profiling: the same launches and results, and in addition the caller's
  * events ev_begin and ev_end (hipEvent_t created by the caller; either may be NULL) are

@@ -14,7 +14,8 @@ ABI_VERSION = 1
 MSEL_F32, MSEL_BF16 = 0, 1
 STATUS = {0: "MSEL_OK", 1: "MSEL_ERR_NULL", 2: "MSEL_ERR_SHAPE", 3: "MSEL_ERR_DTYPE",
           4: "MSEL_ERR_ALIGN", 5: "MSEL_ERR_UNSUPPORTED", 6: "MSEL_ERR_WORKSPACE",
-          7: "MSEL_ERR_ALIAS", 8: "MSEL_ERR_HIP", 9: "MSEL_ERR_VERSION"}
+          7: "MSEL_ERR_ALIAS", 8: "MSEL_ERR_HIP", 9: "MSEL_ERR_VERSION", 10: "MSEL_ERR_TOO_LARGE"}
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MSEL_NOALLOC_SCRATCH_BYTES
 
 _P = ctypes.c_void_p
 
@@ -70,7 +71,7 @@ EXPORTS = ["msel_abi_version", "msel_chunk_len", "msel_num_chunks", "msel_status
            "msel_validate_trap_fwd", "msel_scan_trap_fwd", "msel_validate_complex_fwd",
            "msel_scan_complex_fwd", "msel_validate_trap_bwd", "msel_scan_trap_bwd",
            "msel_validate_complex_bwd", "msel_scan_complex_bwd", "msel_ring_timeouts",
-           "msel_set_ring_spin_limit"]
+           "msel_set_ring_spin_limit", "msel_scan_bwd_noalloc"]
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
@@ -105,6 +106,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.msel_scan_bwd_workspace_bytes.argtypes = [a]
     lib.msel_scan_bwd.restype = ctypes.c_int
     lib.msel_scan_bwd.argtypes = [a, g, _P, ctypes.c_size_t, _P]
+    lib.msel_scan_bwd_noalloc.restype = ctypes.c_int
+    lib.msel_scan_bwd_noalloc.argtypes = [a, g, _P]
     lib.msel_scan_bwd_profiled.restype = ctypes.c_int
     lib.msel_scan_bwd_profiled.argtypes = [a, g, _P, ctypes.c_size_t, _P, _P, _P]
     tap, tgp = ctypes.POINTER(TrapArgs), ctypes.POINTER(TrapGrads)

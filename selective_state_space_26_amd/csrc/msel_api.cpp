@@ -8,6 +8,9 @@
 
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "msel.h"  // include/ is on the include path
 #include "msel_kernels.hpp"
 
@@ -188,6 +191,9 @@ const char* msel_status_string(msel_status s) {
         case MSEL_ERR_ALIAS: return "MSEL_ERR_ALIAS: an output aliases an input";
         case MSEL_ERR_HIP: return "MSEL_ERR_HIP: the HIP runtime reported an error";
         case MSEL_ERR_VERSION: return "MSEL_ERR_VERSION: ABI version or reserved field mismatch";
+        case MSEL_ERR_TOO_LARGE:
+            return "MSEL_ERR_TOO_LARGE: the problem needs more than the library's static scratch "
+                   "(MSEL_NOALLOC_SCRATCH_BYTES)";
     }
     return "MSEL_ERR_UNKNOWN";
 }
@@ -244,8 +250,12 @@ size_t msel_scan_bwd_workspace_bytes(const msel_scan_args* a) {
                                      a->chunk_states == nullptr);
 }
 
-msel_status msel_validate_bwd(const msel_scan_args* a, const msel_scan_grads* g,
-                              const void* workspace, size_t workspace_bytes) {
+}  // extern "C"
+
+namespace {
+
+// The backward's checks that do not involve the workspace.
+msel_status check_bwd(const msel_scan_args* a, const msel_scan_grads* g) {
     msel_status s = check_common(a);
     if (s != MSEL_OK) return s;
     if (a->C == nullptr || g == nullptr || g->dout == nullptr || g->du == nullptr ||
@@ -263,6 +273,49 @@ msel_status msel_validate_bwd(const msel_scan_args* a, const msel_scan_grads* g,
     for (const void* o : outs)
         if (same_as_input(a, o) || (o != nullptr && (o == g->dout || o == a->chunk_states)))
             return MSEL_ERR_ALIAS;
+    return MSEL_OK;
+}
+
+// ---- the backward without a workspace argument ------------------------------------------
+//
+// For callers that cannot allocate: the workspace is a file-scope device array of fixed size.
+// In host code `scratch` only names the symbol; its device address, one per device, comes
+// from hipGetSymbolAddress on the entry point's first call on that device.
+constexpr size_t kScratchBytes = MSEL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, or null if the device cannot be queried.
+void* scratch_on_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p != nullptr) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+        void* q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr)
+            return nullptr;
+        g_scratch_ptr[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+msel_status msel_validate_bwd(const msel_scan_args* a, const msel_scan_grads* g,
+                              const void* workspace, size_t workspace_bytes) {
+    msel_status s = check_bwd(a, g);
+    if (s != MSEL_OK) return s;
+    const void* outs[] = {g->du, g->ddelta, g->dz, g->dA, g->dB, g->dC, g->dD, g->ddelta_bias,
+                          g->dh0};
     const size_t need = msel_scan_bwd_workspace_bytes(a);
     if (workspace == nullptr || workspace_bytes < need) return MSEL_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return MSEL_ERR_ALIGN;
@@ -453,6 +506,16 @@ msel_status msel_ring_timeouts(unsigned long long* count) {
 }
 
 void msel_set_ring_spin_limit(uint32_t polls) { msel::set_ring_spin_limit(polls); }
+
+msel_status msel_scan_bwd_noalloc(const msel_scan_args* a, const msel_scan_grads* g,
+                                  hipStream_t stream) {
+    msel_status s = check_bwd(a, g);
+    if (s != MSEL_OK) return s;
+    if (msel_scan_bwd_workspace_bytes(a) > kScratchBytes) return MSEL_ERR_TOO_LARGE;
+    void* ws = scratch_on_current_device();
+    if (ws == nullptr) return MSEL_ERR_HIP;
+    return run_bwd(a, g, nullptr, nullptr, ws, stream, nullptr, nullptr);
+}
 
 msel_status msel_scan_bwd(const msel_scan_args* a, const msel_scan_grads* g, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {

@@ -338,6 +338,45 @@ def msel_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
     return r
 
 
+def msel_scan_bwd_noalloc(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
+                          delta_softplus=True, h0=None, chunk_states=None, grads=None,
+                          want_dA=True, want_dB=True, want_dC=True, want_dD=True,
+                          want_ddelta_bias=True, want_dh0=False):
+    """msel_scan_bwd with the library's static scratch as the workspace (for callers that
+    cannot allocate; msel_scan_bwd_noalloc).  grads: optional dict of preallocated outputs
+    (the keys msel_scan_bwd returns); missing ones are allocated here, on the caller's side of
+    the C entry point, which itself allocates nothing.  Returns the dict of gradients."""
+    a, (bsz, dim, N, L) = _args(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
+    dev, dt = u.device, u.dtype
+    _need(dout, "dout", (bsz, dim, L), dt, dev)
+    _need(chunk_states, "chunk_states", (bsz, dim, num_chunks(L), N), torch.float32, dev)
+    a.chunk_states = _ptr(chunk_states)
+    f32 = dict(device=dev, dtype=torch.float32)
+    given = dict(grads or {})
+    shapes = {"du": (bsz, dim, L), "ddelta": (bsz, dim, L), "dz": (bsz, dim, L),
+              "dA": (dim, N), "dB": (bsz, N, L), "dC": (bsz, N, L), "dD": (dim,),
+              "ddelta_bias": (dim,), "dh0": (bsz, dim, N)}
+    want = {"du": True, "ddelta": True, "dz": z is not None, "dA": want_dA, "dB": want_dB,
+            "dC": want_dC, "dD": want_dD, "ddelta_bias": want_ddelta_bias, "dh0": want_dh0}
+    r = {}
+    for k, shp in shapes.items():
+        if not want[k]:
+            r[k] = None
+            continue
+        kdt = dt if k in ("du", "ddelta", "dz") else torch.float32
+        if given.get(k) is not None:
+            r[k] = _need(given[k], k, shp, kdt, dev)
+        else:
+            r[k] = torch.empty(shp, device=dev, dtype=kdt)
+    g = _lib.ScanGrads()
+    g.dout = _ptr(dout)
+    for k in shapes:
+        setattr(g, k, _ptr(r[k]))
+    _lib.check("msel_scan_bwd_noalloc",
+               _lib.load().msel_scan_bwd_noalloc(ctypes.byref(a), ctypes.byref(g), _stream(dev)))
+    return r
+
+
 def ring_timeouts() -> int:
     """Waits of the backward gradient kernels' LDS ring that gave up on the current device since
     the last call (0 in a correct run), then clears the count (msel_ring_timeouts).  Waits for

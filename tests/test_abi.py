@@ -239,6 +239,28 @@ def test_bwd_workspace_rules(lib):
     assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), a.chunk_states, need2) == 7
 
 
+def test_bwd_noalloc_checks_before_any_launch(lib):
+    """msel_scan_bwd_noalloc refuses bad arguments, and a problem whose workspace would exceed
+    its static scratch, on the host (these calls make no HIP call)."""
+    a = _good_args(bsz=1, dim=4096, N=16, L=65536)  # rebuilt states: 2 x 33.5 MB + 2 x 2 MB
+    g = _good_grads(a)
+    need = lib.msel_scan_bwd_workspace_bytes(ctypes.byref(a))
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.msel_scan_bwd_noalloc(ctypes.byref(a), ctypes.byref(g), None) == 10
+    # with the forward's chunk states the same problem fits (the states are not rebuilt)
+    a.chunk_states = _addr()
+    assert lib.msel_scan_bwd_workspace_bytes(ctypes.byref(a)) <= _lib.NOALLOC_SCRATCH_BYTES
+    g.du = None
+    assert lib.msel_scan_bwd_noalloc(ctypes.byref(a), ctypes.byref(g), None) == 1
+    g.du = g.dout
+    assert lib.msel_scan_bwd_noalloc(ctypes.byref(a), ctypes.byref(g), None) == 7
+    a.seqlen = 0
+    assert lib.msel_scan_bwd_noalloc(ctypes.byref(a), ctypes.byref(g), None) == 2
+    assert lib.msel_scan_bwd_noalloc(None, ctypes.byref(g), None) == 1
+    text = open(HEADER).read()
+    assert "#define MSEL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+
+
 @pytest.mark.parametrize("field,code", [("dout", 1), ("du", 1), ("ddelta", 1), ("dz", 1)])
 def test_bwd_required_grads(lib, field, code):
     a = _good_args()
