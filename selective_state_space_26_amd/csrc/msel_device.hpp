@@ -468,4 +468,42 @@ __device__ __forceinline__ void wave_sum4(float& a, float& b, float& c, float& d
     d = readlane(d, 63);
 }
 
+// ---------------------------------------------------------------------------------------
+// Complex states as (Re, Im) pairs of fp32 (the rotational variant).
+
+constexpr float kInv2Pi = 0.15915494309189535f;
+
+// sin and cos of an angle given in revolutions: v_sin_f32 / v_cos_f32 take revolutions, and
+// reducing to [0, 1) first keeps any step size inside their input range.
+__device__ __forceinline__ float sin_rev(float r) {
+    return __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(r));
+}
+__device__ __forceinline__ float cos_rev(float r) {
+    return __builtin_amdgcn_cosf(__builtin_amdgcn_fractf(r));
+}
+
+// r + i i = (ar + i ai)(br + i bi)
+__device__ __forceinline__ void cmul(float ar, float ai, float br, float bi, float& r, float& i) {
+    r = fmaf(ar, br, -ai * bi);
+    i = fmaf(ar, bi, ai * br);
+}
+
+// One level of a 64-lane scan of complex affine pairs: (P, S) <- (P Q, P T + S), (Q, T) the
+// pair of the DPP source lane; lanes without one take the identity (1, 0), (0, 0).
+template <int CTRL, int RM>
+__device__ __forceinline__ void cplx_level(float& Pr, float& Pi, float& Sr, float& Si) {
+    const float qr = dpp<CTRL, RM>(1.0f, Pr);
+    const float qi = dpp<CTRL, RM>(0.0f, Pi);
+    const float tr = dpp<CTRL, RM>(0.0f, Sr);
+    const float ti = dpp<CTRL, RM>(0.0f, Si);
+    const float nSr = fmaf(Pr, tr, fmaf(-Pi, ti, Sr));
+    const float nSi = fmaf(Pr, ti, fmaf(Pi, tr, Si));
+    const float nPr = fmaf(Pr, qr, -Pi * qi);
+    const float nPi = fmaf(Pr, qi, Pi * qr);
+    Pr = nPr;
+    Pi = nPi;
+    Sr = nSr;
+    Si = nSi;
+}
+
 }  // namespace msel

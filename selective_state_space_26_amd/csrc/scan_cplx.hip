@@ -26,41 +26,14 @@ namespace msel {
 
 namespace {
 
-constexpr float kInv2Pi = 0.15915494309189535f;
-
-__device__ __forceinline__ float sin_rev(float r) {
-    return __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(r));
-}
-__device__ __forceinline__ float cos_rev(float r) {
-    return __builtin_amdgcn_cosf(__builtin_amdgcn_fractf(r));
-}
-
-// One level of the complex affine scan: (P, S) <- (P Q, P T + S), (Q, T) the pair of the
-// source lane; lanes without one take the identity (1, 0), (0, 0).
-template <int CTRL, int RM>
-__device__ __forceinline__ void cscan_level(float& Pr, float& Pi, float& Sr, float& Si) {
-    const float qr = dpp<CTRL, RM>(1.0f, Pr);
-    const float qi = dpp<CTRL, RM>(0.0f, Pi);
-    const float tr = dpp<CTRL, RM>(0.0f, Sr);
-    const float ti = dpp<CTRL, RM>(0.0f, Si);
-    const float nSr = fmaf(Pr, tr, fmaf(-Pi, ti, Sr));
-    const float nSi = fmaf(Pr, ti, fmaf(Pi, tr, Si));
-    const float nPr = fmaf(Pr, qr, -Pi * qi);
-    const float nPi = fmaf(Pr, qi, Pi * qr);
-    Pr = nPr;
-    Pi = nPi;
-    Sr = nSr;
-    Si = nSi;
-}
-
 // Inclusive scan over the 64 lanes, lane 0 first.
 __device__ __forceinline__ void cscan(float& Pr, float& Pi, float& Sr, float& Si) {
-    cscan_level<kRowShr1, 0xf>(Pr, Pi, Sr, Si);
-    cscan_level<kRowShr2, 0xf>(Pr, Pi, Sr, Si);
-    cscan_level<kRowShr4, 0xf>(Pr, Pi, Sr, Si);
-    cscan_level<kRowShr8, 0xf>(Pr, Pi, Sr, Si);
-    cscan_level<kRowBcast15, 0xa>(Pr, Pi, Sr, Si);
-    cscan_level<kRowBcast31, 0xc>(Pr, Pi, Sr, Si);
+    cplx_level<kRowShr1, 0xf>(Pr, Pi, Sr, Si);
+    cplx_level<kRowShr2, 0xf>(Pr, Pi, Sr, Si);
+    cplx_level<kRowShr4, 0xf>(Pr, Pi, Sr, Si);
+    cplx_level<kRowShr8, 0xf>(Pr, Pi, Sr, Si);
+    cplx_level<kRowBcast15, 0xa>(Pr, Pi, Sr, Si);
+    cplx_level<kRowBcast31, 0xc>(Pr, Pi, Sr, Si);
 }
 
 template <typename T, int K, bool VEC, bool HAS_Z, bool SOFTPLUS>

@@ -33,7 +33,6 @@ namespace msel {
 
 namespace {
 
-constexpr float kInv2Pi = 0.15915494309189535f;
 constexpr int kK = kChunk / 64;  // steps per lane
 constexpr int kMaxPairs = 8;
 
@@ -50,35 +49,6 @@ struct CWork {
 
 // Ring waits of this file's gradient kernel that gave up (see ring_spin_limit).
 __device__ unsigned long long g_ring_timeouts_cplx;
-
-__device__ __forceinline__ float sin_rev(float r) {
-    return __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(r));
-}
-__device__ __forceinline__ float cos_rev(float r) {
-    return __builtin_amdgcn_cosf(__builtin_amdgcn_fractf(r));
-}
-
-// (P, S) <- (P Q, P T + S) with (Q, T) from the DPP source lane, identity where there is none.
-template <int CTRL, int RM>
-__device__ __forceinline__ void cplx_level(float& Pr, float& Pi, float& Sr, float& Si) {
-    const float qr = dpp<CTRL, RM>(1.0f, Pr);
-    const float qi = dpp<CTRL, RM>(0.0f, Pi);
-    const float tr = dpp<CTRL, RM>(0.0f, Sr);
-    const float ti = dpp<CTRL, RM>(0.0f, Si);
-    const float nSr = fmaf(Pr, tr, fmaf(-Pi, ti, Sr));
-    const float nSi = fmaf(Pr, ti, fmaf(Pi, tr, Si));
-    const float nPr = fmaf(Pr, qr, -Pi * qi);
-    const float nPi = fmaf(Pr, qi, Pi * qr);
-    Pr = nPr;
-    Pi = nPi;
-    Sr = nSr;
-    Si = nSi;
-}
-
-__device__ __forceinline__ void cmul(float ar, float ai, float br, float bi, float& r, float& i) {
-    r = fmaf(ar, br, -ai * bi);
-    i = fmaf(ar, bi, ai * br);
-}
 
 // ---------------------------------------------------------------------------------------
 // 1. summary
