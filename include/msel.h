@@ -106,7 +106,7 @@ typedef struct {
     float *final_state;     /* fwd / chunk_carry: optional output, state after step L-1;
                                may equal h0 (the state is then updated in place)          */
     float *chunk_states;    /* fwd: optional output; chunk_carry: required output;          */
-                            /* bwd: optional input (recomputed into the workspace if NULL) */
+                            /* bwds: optional input (rebuilt into the workspace if NULL)   */
 } msel_scan_args;
 
 /* Gradients of a scalar loss given dL/dout.  Every output is overwritten, not accumulated. */
@@ -245,9 +245,23 @@ msel_status msel_validate_trap_fwd(const msel_scan_args *args, const msel_trap_a
 /* Fused forward scan with the exponential-trapezoidal rule: the same single pass, outputs
  * (out, final_state, chunk_states) and conventions as msel_scan_fwd, reading lambda as one
  * more input stream.  seqlen == 1 is the decode step (state in place allowed).  Its backward
- * is msel_scan_trap_bwd; its chunk-carry pass is not part of the library. */
+ * is msel_scan_trap_bwd, its chunk-carry pass msel_scan_trap_chunk_carry. */
 msel_status msel_scan_trap_fwd(const msel_scan_args *args, const msel_trap_args *trap,
                                hipStream_t stream);
+
+/* Host-only checks of msel_scan_trap_chunk_carry's arguments (those of
+ * msel_validate_chunk_carry, and the trapezoidal inputs'). */
+msel_status msel_validate_trap_chunk_carry(const msel_scan_args *args,
+                                           const msel_trap_args *trap);
+
+/* Chunk-carry pass of the exponential-trapezoidal rule (page 4, Appendix D, Speed: the scan
+ * continues chunk by chunk from the intermediate state; page 5, the rule): chunk_states
+ * (required) and final_state (optional) equal to msel_scan_trap_fwd's for the same inputs,
+ * from u, delta, lambda, B, A, delta_bias, h0, u_prev and B_prev alone (C, z, D unread).
+ * Per chunk, the transition and the local end state in closed form, where each step's input
+ * also reaches back to the previous step's B and u; then the link. */
+msel_status msel_scan_trap_chunk_carry(const msel_scan_args *args, const msel_trap_args *trap,
+                                       hipStream_t stream);
 
 /* The trapezoidal variant's gradients beyond msel_scan_grads.  Overwritten, not
  * accumulated. */
@@ -259,7 +273,7 @@ typedef struct {
 } msel_trap_grads;
 
 /* Host-only checks of msel_scan_trap_bwd's arguments (those of msel_validate_bwd, the
- * trapezoidal inputs and gradients, chunk_states present, no output equal to an input, the
+ * trapezoidal inputs and gradients, no output equal to an input, the
  * workspace or another output). */
 msel_status msel_validate_trap_bwd(const msel_scan_args *args, const msel_trap_args *trap,
                                    const msel_scan_grads *grads,
@@ -268,8 +282,9 @@ msel_status msel_validate_trap_bwd(const msel_scan_args *args, const msel_trap_a
 
 /* Backward of msel_scan_trap_fwd with recomputation (page 1; page 4 Appendix D, Memory):
  * the same three launches as msel_scan_bwd and the same outputs, plus trap_grads.
- * args->chunk_states is required and must hold msel_scan_trap_fwd's chunk states for the
- * same inputs; the workspace is msel_scan_bwd_workspace_bytes(args).  du_prev and dB_prev let
+ * args->chunk_states holds msel_scan_trap_fwd's chunk states for the same inputs, or is NULL:
+ * then msel_scan_trap_chunk_carry's pass rebuilds them into the front of the workspace first.
+ * The workspace is msel_scan_bwd_workspace_bytes(args).  du_prev and dB_prev let
  * a caller that split a sequence across calls carry the gradient into the earlier call.
  * Same determinism as msel_scan_bwd (dB_prev is an fp32 atomic sum over channels). */
 msel_status msel_scan_trap_bwd(const msel_scan_args *args, const msel_trap_args *trap,
@@ -291,22 +306,34 @@ msel_status msel_scan_trap_bwd(const msel_scan_args *args, const msel_trap_args 
  * The arguments, layouts and outputs are msel_scan_fwd's (h0, final_state and chunk_states
  * hold (Re, Im) pairs); dstate must be even (else MSEL_ERR_SHAPE).  With every A[d, 2j+1] = 0
  * this is msel_scan_fwd with A[d, 2j+1] = A[d, 2j].  seqlen == 1 is the decode step (state in
- * place allowed).  Its backward is msel_scan_complex_bwd; its chunk-carry pass is not
- * part of the library.
+ * place allowed).  Its backward is msel_scan_complex_bwd, its chunk-carry pass
+ * msel_scan_complex_chunk_carry.
  * ---------------------------------------------------------------------------------------- */
 msel_status msel_validate_complex_fwd(const msel_scan_args *args);
 msel_status msel_scan_complex_fwd(const msel_scan_args *args, hipStream_t stream);
 
-/* Host-only checks of msel_scan_complex_bwd's arguments: those of msel_validate_bwd, dstate
- * even, and chunk_states present. */
+/* Host-only checks of msel_scan_complex_chunk_carry's arguments (those of
+ * msel_validate_chunk_carry, and dstate even). */
+msel_status msel_validate_complex_chunk_carry(const msel_scan_args *args);
+
+/* Chunk-carry pass of the complex-valued scan (page 4, Appendix D, Speed; page 5, the complex
+ * state as a scaling and a rotation): chunk_states (required) and final_state (optional)
+ * equal to msel_scan_complex_fwd's for the same inputs, from u, delta, A, B, delta_bias and h0
+ * alone.  Per chunk, the complex transition exp(A * sum of Delta) and the local end state in
+ * closed form; then the link, a complex product per state pair. */
+msel_status msel_scan_complex_chunk_carry(const msel_scan_args *args, hipStream_t stream);
+
+/* Host-only checks of msel_scan_complex_bwd's arguments: those of msel_validate_bwd and
+ * dstate even. */
 msel_status msel_validate_complex_bwd(const msel_scan_args *args, const msel_scan_grads *grads,
                                       const void *workspace, size_t workspace_bytes);
 
 /* Backward of msel_scan_complex_fwd with recomputation (page 1; page 4 Appendix D, Memory):
  * zero-fills, per-chunk adjoint summaries, their link across chunks (with conjugated
  * transitions) and a gradient kernel with one wavefront per state pair.  args->chunk_states
- * is required and must hold msel_scan_complex_fwd's chunk states for the same inputs; the
- * workspace is msel_scan_bwd_workspace_bytes(args).  The outputs are msel_scan_grads' (dA and
+ * holds msel_scan_complex_fwd's chunk states for the same inputs, or is NULL: then
+ * msel_scan_complex_chunk_carry's pass rebuilds them into the front of the workspace first.
+ * The workspace is msel_scan_bwd_workspace_bytes(args).  The outputs are msel_scan_grads' (dA and
  * dh0 interleaved (Re, Im) like A and h0), with msel_scan_bwd's determinism. */
 msel_status msel_scan_complex_bwd(const msel_scan_args *args, const msel_scan_grads *grads,
                                   void *workspace, size_t workspace_bytes, hipStream_t stream);

@@ -71,7 +71,9 @@ EXPORTS = ["msel_abi_version", "msel_chunk_len", "msel_num_chunks", "msel_status
            "msel_validate_trap_fwd", "msel_scan_trap_fwd", "msel_validate_complex_fwd",
            "msel_scan_complex_fwd", "msel_validate_trap_bwd", "msel_scan_trap_bwd",
            "msel_validate_complex_bwd", "msel_scan_complex_bwd", "msel_ring_timeouts",
-           "msel_set_ring_spin_limit", "msel_scan_bwd_noalloc"]
+           "msel_set_ring_spin_limit", "msel_scan_bwd_noalloc", "msel_validate_trap_chunk_carry",
+           "msel_scan_trap_chunk_carry", "msel_validate_complex_chunk_carry",
+           "msel_scan_complex_chunk_carry"]
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
@@ -128,6 +130,14 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.msel_validate_trap_fwd.argtypes = [a, ta]
     lib.msel_scan_trap_fwd.restype = ctypes.c_int
     lib.msel_scan_trap_fwd.argtypes = [a, ta, _P]
+    lib.msel_validate_trap_chunk_carry.restype = ctypes.c_int
+    lib.msel_validate_trap_chunk_carry.argtypes = [a, ta]
+    lib.msel_scan_trap_chunk_carry.restype = ctypes.c_int
+    lib.msel_scan_trap_chunk_carry.argtypes = [a, ta, _P]
+    lib.msel_validate_complex_chunk_carry.restype = ctypes.c_int
+    lib.msel_validate_complex_chunk_carry.argtypes = [a]
+    lib.msel_scan_complex_chunk_carry.restype = ctypes.c_int
+    lib.msel_scan_complex_chunk_carry.argtypes = [a, _P]
     ca, cg = ctypes.POINTER(ConvArgs), ctypes.POINTER(ConvGrads)
     lib.msel_validate_conv_fwd.restype = ctypes.c_int
     lib.msel_validate_conv_fwd.argtypes = [ca]

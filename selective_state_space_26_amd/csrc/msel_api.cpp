@@ -127,8 +127,16 @@ msel::ConvParams to_conv_params(const msel_conv_args* a) {
     return p;
 }
 
+// Bytes of one set of chunk states, rounded up as the backward's workspace pieces are.
+size_t states_bytes_aligned(const msel_scan_args* a) {
+    const size_t s = static_cast<size_t>(a->batch) * a->dim * msel_num_chunks(a->seqlen) *
+                     a->dstate * sizeof(float);
+    return (s + 255) & ~static_cast<size_t>(255);
+}
+
 // The backward's launches after validation: zero-fills, then summary, link and gradient
-// kernels (the trapezoidal variant when `tr` is given).
+// kernels (the trapezoidal variant when `tr` is given; with no chunk states given, its
+// chunk-carry pass rebuilds them first).
 msel_status run_bwd(const msel_scan_args* a, const msel_scan_grads* g, const msel_trap_args* tr,
                     const msel_trap_grads* tg, void* workspace, hipStream_t stream,
                     hipEvent_t ev_begin, hipEvent_t ev_end) {
@@ -162,8 +170,20 @@ msel_status run_bwd(const msel_scan_args* a, const msel_scan_grads* g, const mse
         gp.du_prev = tg->du_prev;
         gp.dB_prev = tg->dB_prev;
     }
-    return hip_status(msel::launch_scan_bwd(p, gp, a->chunk_states, workspace, bf16, fill,
-                                            stream, ev_begin, ev_end));
+    const float* states = a->chunk_states;
+    if (tr != nullptr && states == nullptr) {
+        // the trapezoidal forward's chunk states, rebuilt by its chunk-carry pass into the
+        // front of the workspace; the rest is laid out as with the states given
+        float* H = static_cast<float*>(workspace);
+        msel::ScanParams pc = p;
+        pc.chunk_states = H;
+        pc.final_state = nullptr;
+        if (msel::launch_chunk_carry(pc, bf16, false, stream) != hipSuccess) return MSEL_ERR_HIP;
+        states = H;
+        workspace = static_cast<char*>(workspace) + states_bytes_aligned(a);
+    }
+    return hip_status(msel::launch_scan_bwd(p, gp, states, workspace, bf16, fill, stream,
+                                            ev_begin, ev_end));
 }
 
 }  // namespace
@@ -390,8 +410,7 @@ msel_status msel_validate_trap_bwd(const msel_scan_args* a, const msel_trap_args
                                    const void* workspace, size_t workspace_bytes) {
     msel_status s = msel_validate_bwd(a, g, workspace, workspace_bytes);
     if (s != MSEL_OK) return s;
-    if (a->chunk_states == nullptr || tr == nullptr || tr->lambda == nullptr || tg == nullptr ||
-        tg->dlambda == nullptr)
+    if (tr == nullptr || tr->lambda == nullptr || tg == nullptr || tg->dlambda == nullptr)
         return MSEL_ERR_NULL;
     const size_t e = a->dtype == MSEL_BF16 ? 2 : 4;
     if (!aligned(tr->lambda, 16) || !aligned(tg->dlambda, 16) ||
@@ -438,7 +457,6 @@ msel_status msel_validate_complex_bwd(const msel_scan_args* a, const msel_scan_g
     msel_status s = msel_validate_bwd(a, g, workspace, workspace_bytes);
     if (s != MSEL_OK) return s;
     if (a->dstate % 2 != 0) return MSEL_ERR_SHAPE;
-    if (a->chunk_states == nullptr) return MSEL_ERR_NULL;
     return MSEL_OK;
 }
 
@@ -462,8 +480,21 @@ msel_status msel_scan_complex_bwd(const msel_scan_args* a, const msel_scan_grads
     gp.dD = g->dD;
     gp.dbias = g->ddelta_bias;
     gp.dh0 = g->dh0;
-    return hip_status(msel::launch_scan_cplx_bwd(to_params(a), gp, a->chunk_states, workspace,
-                                                 a->dtype == MSEL_BF16, fill, stream));
+    const bool bf16 = a->dtype == MSEL_BF16;
+    const msel::ScanParams p = to_params(a);
+    const float* states = a->chunk_states;
+    if (states == nullptr) {
+        // the complex forward's chunk states, rebuilt by its chunk-carry pass into the front
+        // of the workspace; the rest is laid out as with the states given
+        float* H = static_cast<float*>(workspace);
+        msel::ScanParams pc = p;
+        pc.chunk_states = H;
+        pc.final_state = nullptr;
+        if (msel::launch_chunk_carry(pc, bf16, true, stream) != hipSuccess) return MSEL_ERR_HIP;
+        states = H;
+        workspace = static_cast<char*>(workspace) + states_bytes_aligned(a);
+    }
+    return hip_status(msel::launch_scan_cplx_bwd(p, gp, states, workspace, bf16, fill, stream));
 }
 
 msel_status msel_scan_complex_fwd(const msel_scan_args* a, hipStream_t stream) {
@@ -475,7 +506,49 @@ msel_status msel_scan_complex_fwd(const msel_scan_args* a, hipStream_t stream) {
 msel_status msel_scan_chunk_carry(const msel_scan_args* a, hipStream_t stream) {
     msel_status s = msel_validate_chunk_carry(a);
     if (s != MSEL_OK) return s;
-    return hip_status(msel::launch_chunk_carry(to_params(a), a->dtype == MSEL_BF16, stream));
+    return hip_status(
+        msel::launch_chunk_carry(to_params(a), a->dtype == MSEL_BF16, false, stream));
+}
+
+msel_status msel_validate_trap_chunk_carry(const msel_scan_args* a, const msel_trap_args* tr) {
+    msel_status s = msel_validate_chunk_carry(a);
+    if (s != MSEL_OK) return s;
+    if (tr == nullptr || tr->lambda == nullptr) return MSEL_ERR_NULL;
+    if (!aligned(tr->lambda, 16)) return MSEL_ERR_ALIGN;
+    const size_t e = a->dtype == MSEL_BF16 ? 2 : 4;
+    if ((tr->u_prev != nullptr && !aligned(tr->u_prev, e)) ||
+        (tr->B_prev != nullptr && !aligned(tr->B_prev, e)))
+        return MSEL_ERR_ALIGN;
+    const void* outs[] = {a->final_state, a->chunk_states};
+    for (const void* o : outs)
+        if (o != nullptr && (o == tr->lambda || o == tr->u_prev || o == tr->B_prev))
+            return MSEL_ERR_ALIAS;
+    return MSEL_OK;
+}
+
+msel_status msel_scan_trap_chunk_carry(const msel_scan_args* a, const msel_trap_args* tr,
+                                       hipStream_t stream) {
+    msel_status s = msel_validate_trap_chunk_carry(a, tr);
+    if (s != MSEL_OK) return s;
+    msel::ScanParams p = to_params(a);
+    p.lam = tr->lambda;
+    p.u_prev = tr->u_prev;
+    p.B_prev = tr->B_prev;
+    return hip_status(msel::launch_chunk_carry(p, a->dtype == MSEL_BF16, false, stream));
+}
+
+msel_status msel_validate_complex_chunk_carry(const msel_scan_args* a) {
+    msel_status s = msel_validate_chunk_carry(a);
+    if (s != MSEL_OK) return s;
+    if (a->dstate % 2 != 0) return MSEL_ERR_SHAPE;  // states come in (Re, Im) pairs
+    return MSEL_OK;
+}
+
+msel_status msel_scan_complex_chunk_carry(const msel_scan_args* a, hipStream_t stream) {
+    msel_status s = msel_validate_complex_chunk_carry(a);
+    if (s != MSEL_OK) return s;
+    return hip_status(
+        msel::launch_chunk_carry(to_params(a), a->dtype == MSEL_BF16, true, stream));
 }
 
 msel_status msel_scan_bwd_profiled(const msel_scan_args* a, const msel_scan_grads* g,

@@ -97,7 +97,9 @@ hipError_t take_ring_timeouts_cplx(unsigned long long* count);
 
 // All launchers enqueue on `stream` and return the hipGetLastError() after the launch.
 hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, hipStream_t stream);
-hipError_t launch_chunk_carry(const ScanParams& p, bool bf16, hipStream_t stream);
+// The chunk-carry pass: the plain rule, the exponential-trapezoidal rule when p.lam is set, or
+// the complex-valued state when cplx (N even).
+hipError_t launch_chunk_carry(const ScanParams& p, bool bf16, bool cplx, hipStream_t stream);
 // The complex-valued (rotational) forward: state pairs (2j, 2j+1) are complex states; N even.
 hipError_t launch_scan_cplx_fwd(const ScanParams& p, bool bf16, hipStream_t stream);
 // Buffers to zero before a backward's atomics (null slots are skipped).

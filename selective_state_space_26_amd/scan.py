@@ -185,6 +185,68 @@ def msel_scan_chunk_carry(u, delta, A, B, delta_bias=None, delta_softplus=True, 
     return chunk_states, final_state
 
 
+def _chunk_carry_out(u, A, chunk_states, final_state, return_final_state):
+    bsz, dim, L = u.shape
+    N = A.shape[1]
+    dev = u.device
+    if chunk_states is None:
+        chunk_states = torch.empty((bsz, dim, num_chunks(L), N), device=dev,
+                                   dtype=torch.float32)
+    if return_final_state and final_state is None:
+        final_state = torch.empty((bsz, dim, N), device=dev, dtype=torch.float32)
+    _need(chunk_states, "chunk_states", (bsz, dim, num_chunks(L), N), torch.float32, dev)
+    _need(final_state, "final_state", (bsz, dim, N), torch.float32, dev)
+    return chunk_states, final_state
+
+
+def msel_scan_trap_chunk_carry(u, delta, lam, A, B, delta_bias=None, delta_softplus=True,
+                               h0=None, u_prev=None, B_prev=None, return_final_state=True,
+                               chunk_states=None, final_state=None):
+    """Chunk-carry pass of the exponential-trapezoidal rule.  Returns (chunk_states,
+    final_state or None), those msel_scan_trap_fwd gives for the same inputs."""
+    if u.dim() != 3 or A.dim() != 2:
+        raise ValueError("u must be [batch, dim, seqlen] and A [dim, dstate]")
+    bsz, dim, L = u.shape
+    N = A.shape[1]
+    dev, dt = u.device, u.dtype
+    _need(B, "B", (bsz, N, L), dt, dev)
+    _need(lam, "lam", (bsz, dim, L), dt, dev)
+    _need(u_prev, "u_prev", (bsz, dim), dt, dev)
+    _need(B_prev, "B_prev", (bsz, N), dt, dev)
+    if lam is None:
+        raise ValueError("lam is required")
+    a, _ = _args(u, delta, A, B, B, None, None, delta_bias, h0, delta_softplus)
+    a.C = None
+    chunk_states, final_state = _chunk_carry_out(u, A, chunk_states, final_state,
+                                                 return_final_state)
+    a.chunk_states, a.final_state = _ptr(chunk_states), _ptr(final_state)
+    tr = _lib.TrapArgs()
+    tr.lambda_, tr.u_prev, tr.B_prev = _ptr(lam), _ptr(u_prev), _ptr(B_prev)
+    _lib.check("msel_scan_trap_chunk_carry",
+               _lib.load().msel_scan_trap_chunk_carry(ctypes.byref(a), ctypes.byref(tr),
+                                                      _stream(dev)))
+    return chunk_states, final_state
+
+
+def msel_scan_complex_chunk_carry(u, delta, A, B, delta_bias=None, delta_softplus=True, h0=None,
+                                  return_final_state=True, chunk_states=None, final_state=None):
+    """Chunk-carry pass of the complex-valued scan (A interleaved (Re, Im), dstate even).
+    Returns (chunk_states, final_state or None), those msel_scan_complex_fwd gives."""
+    if u.dim() != 3 or A.dim() != 2:
+        raise ValueError("u must be [batch, dim, seqlen] and A [dim, dstate]")
+    bsz, dim, L = u.shape
+    N = A.shape[1]
+    _need(B, "B", (bsz, N, L), u.dtype, u.device)
+    a, _ = _args(u, delta, A, B, B, None, None, delta_bias, h0, delta_softplus)
+    a.C = None
+    chunk_states, final_state = _chunk_carry_out(u, A, chunk_states, final_state,
+                                                 return_final_state)
+    a.chunk_states, a.final_state = _ptr(chunk_states), _ptr(final_state)
+    _lib.check("msel_scan_complex_chunk_carry",
+               _lib.load().msel_scan_complex_chunk_carry(ctypes.byref(a), _stream(u.device)))
+    return chunk_states, final_state
+
+
 def bwd_workspace_bytes(u, A, chunk_states_given=False) -> int:
     """Bytes of workspace msel_scan_bwd needs for this problem (msel_scan_bwd_workspace_bytes)."""
     bsz, dim, L = u.shape
@@ -200,18 +262,17 @@ def bwd_workspace_bytes(u, A, chunk_states_given=False) -> int:
     return int(_lib.load().msel_scan_bwd_workspace_bytes(ctypes.byref(a)))
 
 
-def msel_scan_complex_bwd(u, delta, A, B, C, dout, chunk_states, D=None, z=None,
+def msel_scan_complex_bwd(u, delta, A, B, C, dout, chunk_states=None, D=None, z=None,
                           delta_bias=None, delta_softplus=True, h0=None, want_dA=True,
                           want_dB=True, want_dC=True, want_dD=True, want_ddelta_bias=True,
                           want_dh0=False, workspace=None):
-    """Backward of msel_scan_complex_fwd (chunk_states: that forward's).  Returns a dict of
-    gradients as msel_scan_bwd does (dA and dh0 interleaved (Re, Im))."""
+    """Backward of msel_scan_complex_fwd (chunk_states: that forward's, or None: rebuilt by the
+    library).  Returns a dict of gradients as msel_scan_bwd does (dA and dh0 interleaved
+    (Re, Im))."""
     a, (bsz, dim, N, L) = _args(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
     dev = u.device
     _need(dout, "dout", (bsz, dim, L), u.dtype, dev)
     _need(chunk_states, "chunk_states", (bsz, dim, num_chunks(L), N), torch.float32, dev)
-    if chunk_states is None:
-        raise ValueError("chunk_states (from msel_scan_complex_fwd) are required")
     a.chunk_states = _ptr(chunk_states)
     f32 = dict(device=dev, dtype=torch.float32)
     r = {
@@ -239,14 +300,14 @@ def msel_scan_complex_bwd(u, delta, A, B, C, dout, chunk_states, D=None, z=None,
     return r
 
 
-def msel_scan_trap_bwd(u, delta, lam, A, B, C, dout, chunk_states, D=None, z=None,
+def msel_scan_trap_bwd(u, delta, lam, A, B, C, dout, chunk_states=None, D=None, z=None,
                        delta_bias=None, delta_softplus=True, h0=None, u_prev=None, B_prev=None,
                        want_dA=True, want_dB=True, want_dC=True, want_dD=True,
                        want_ddelta_bias=True, want_dh0=False, want_dprev=False,
                        workspace=None):
-    """Backward of msel_scan_trap_fwd (chunk_states: that forward's).  Returns a dict of
-    gradients as msel_scan_bwd does, plus "dlam" and, with want_dprev, "du_prev" [batch, dim]
-    and "dB_prev" [batch, dstate] (fp32)."""
+    """Backward of msel_scan_trap_fwd (chunk_states: that forward's, or None: rebuilt by the
+    library).  Returns a dict of gradients as msel_scan_bwd does, plus "dlam" and, with
+    want_dprev, "du_prev" [batch, dim] and "dB_prev" [batch, dstate] (fp32)."""
     a, (bsz, dim, N, L) = _args(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
     dev, dt = u.device, u.dtype
     _need(lam, "lam", (bsz, dim, L), dt, dev)
@@ -254,8 +315,8 @@ def msel_scan_trap_bwd(u, delta, lam, A, B, C, dout, chunk_states, D=None, z=Non
     _need(B_prev, "B_prev", (bsz, N), dt, dev)
     _need(dout, "dout", (bsz, dim, L), dt, dev)
     _need(chunk_states, "chunk_states", (bsz, dim, num_chunks(L), N), torch.float32, dev)
-    if lam is None or chunk_states is None:
-        raise ValueError("lam and chunk_states are required")
+    if lam is None:
+        raise ValueError("lam is required")
     a.chunk_states = _ptr(chunk_states)
     f32 = dict(device=dev, dtype=torch.float32)
     r = {

@@ -519,10 +519,15 @@ def test_trap_bwd_validation(lib):
     assert v() == 0
     tg.du_prev = tg.dB_prev = None
     assert v() == 0
-    a.chunk_states = None                      # the forward's chunk states are required
-    assert v() == 1
+    # without the forward's chunk states they are rebuilt: the workspace must hold them too
+    a.chunk_states = None
+    need = lib.msel_scan_bwd_workspace_bytes(ctypes.byref(a))
+    assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
+                                      ctypes.byref(tg), ws, need) == 0
+    assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
+                                      ctypes.byref(tg), ws, need - 1) == 6
     assert lib.msel_scan_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
-                                  ctypes.byref(tg), ws, big, None) == 1
+                                  ctypes.byref(tg), ws, need - 1, None) == 6
     a.chunk_states = _addr()
     assert lib.msel_validate_trap_bwd(ctypes.byref(a), ctypes.byref(t), ctypes.byref(g), None,
                                       ws, big) == 1
@@ -563,10 +568,39 @@ def test_complex_bwd_validation(lib):
     a.dstate = 15
     assert v() == 2
     a.dstate = 16
+    # without the forward's chunk states they are rebuilt: the workspace must hold them too
     a.chunk_states = None
-    assert v() == 1
-    assert lib.msel_scan_complex_bwd(ctypes.byref(a), ctypes.byref(g), ws, big, None) == 1
+    need = lib.msel_scan_bwd_workspace_bytes(ctypes.byref(a))
+    assert lib.msel_validate_complex_bwd(ctypes.byref(a), ctypes.byref(g), ws, need) == 0
+    assert lib.msel_validate_complex_bwd(ctypes.byref(a), ctypes.byref(g), ws, need - 1) == 6
+    assert lib.msel_scan_complex_bwd(ctypes.byref(a), ctypes.byref(g), ws, need - 1, None) == 6
     a.chunk_states = _addr()
     assert lib.msel_validate_complex_bwd(ctypes.byref(a), ctypes.byref(g), None, 0) == 6
     g.dC = a.C
     assert v() == 7
+
+
+def test_variant_chunk_carry_validation(lib):
+    a = _good_args(N=16, L=1000)
+    a.chunk_states = _addr()
+    t = _trap()
+    assert lib.msel_validate_trap_chunk_carry(ctypes.byref(a), ctypes.byref(t)) == 0
+    assert lib.msel_validate_complex_chunk_carry(ctypes.byref(a)) == 0
+    assert lib.msel_validate_trap_chunk_carry(ctypes.byref(a), None) == 1
+    t2 = _trap()
+    t2.lambda_ = None
+    assert lib.msel_validate_trap_chunk_carry(ctypes.byref(a), ctypes.byref(t2)) == 1
+    assert lib.msel_scan_trap_chunk_carry(ctypes.byref(a), ctypes.byref(t2), None) == 1
+    t2 = _trap()
+    t2.lambda_ += 8
+    assert lib.msel_validate_trap_chunk_carry(ctypes.byref(a), ctypes.byref(t2)) == 4
+    t2 = _trap()
+    t2.lambda_ = a.chunk_states
+    assert lib.msel_validate_trap_chunk_carry(ctypes.byref(a), ctypes.byref(t2)) == 7
+    a.dstate = 15
+    assert lib.msel_validate_complex_chunk_carry(ctypes.byref(a)) == 2
+    assert lib.msel_scan_complex_chunk_carry(ctypes.byref(a), None) == 2
+    a.dstate = 16
+    a.chunk_states = None  # required: the pass's product
+    assert lib.msel_validate_trap_chunk_carry(ctypes.byref(a), ctypes.byref(t)) == 1
+    assert lib.msel_validate_complex_chunk_carry(ctypes.byref(a)) == 1

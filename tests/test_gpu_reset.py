@@ -200,3 +200,57 @@ def test_ddelta_with_tiny_steps(variant):
     assert 5e-5 < sp.min() and sp.max() < 4e-4, (sp.min(), sp.max())
     for k in ("ddelta", "ddelta_bias", "du"):
         assert_close(k, host(g[k]), r[k], "f32")
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[3]], ids=_ids)
+def test_variant_chunk_carry_next_to_reset(case):
+    """The trapezoidal and complex chunk-carry passes form the same suffix sums."""
+    bsz, dim, N, L, dtype, resets, zero_u, sp = case
+    log(f"variant chunk carry reset {case}")
+    t = _reset_inputs(*case)
+    t["lam"] = msel_inputs.make(bsz, dim, N, L, dtype, 313, with_lam=True)["lam"]
+    d = to_device(t)
+    cs, fin = msel.msel_scan_trap_chunk_carry(d["u"], d["delta"], d["lam"], d["A"], d["B"],
+                                              d["bias"], sp, d["h0"])
+    tc = _reset_inputs(*case, complex_A=True)
+    dc = to_device(tc)
+    ccs, cfin = msel.msel_scan_complex_chunk_carry(dc["u"], dc["delta"], dc["A"], dc["B"],
+                                                   dc["bias"], sp, dc["h0"])
+    torch.cuda.synchronize()
+    v = oracle_vals(t)
+    _, rf, rcs = otrap.fwd(v["u"], v["delta"], t.values("lam"), v["A"], v["B"], v["C"], v["D"],
+                           v["z"], v["bias"], v["h0"], softplus=sp, chunk_len=T)
+    assert_close("trap chunk_states", host(cs), rcs, dtype)
+    assert_close("trap final_state", host(fin), rf, dtype)
+    vc = oracle_vals(tc)
+    _, crf, crcs = ocplx.fwd(vc["u"], vc["delta"], vc["A"], vc["B"], vc["C"], vc["D"], vc["z"],
+                             vc["bias"], vc["h0"], softplus=sp, chunk_len=T)
+    assert_close("complex chunk_states", host(ccs), crcs, dtype)
+    assert_close("complex final_state", host(cfin), crf, dtype)
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[3]], ids=_ids)
+def test_variant_bwd_with_rebuilt_states_next_to_reset(case):
+    bsz, dim, N, L, dtype, resets, zero_u, sp = case
+    log(f"variant bwd rebuilt states reset {case}")
+    t = _reset_inputs(*case)
+    t["lam"] = msel_inputs.make(bsz, dim, N, L, dtype, 314, with_lam=True)["lam"]
+    d = to_device(t)
+    g = msel.msel_scan_trap_bwd(d["u"], d["delta"], d["lam"], d["A"], d["B"], d["C"], d["dout"],
+                                None, d["D"], d["z"], d["bias"], sp, d["h0"], want_dh0=True)
+    tc = _reset_inputs(*case, complex_A=True)
+    dc = to_device(tc)
+    gc = msel.msel_scan_complex_bwd(dc["u"], dc["delta"], dc["A"], dc["B"], dc["C"], dc["dout"],
+                                    None, dc["D"], dc["z"], dc["bias"], sp, dc["h0"],
+                                    want_dh0=True)
+    torch.cuda.synchronize()
+    v = oracle_vals(t)
+    r = otrap.bwd(v["u"], v["delta"], t.values("lam"), v["A"], v["B"], v["C"], v["dout"],
+                  v["D"], v["z"], v["bias"], v["h0"], softplus=sp)
+    for k in ("du", "ddelta", "dlam", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        assert_close(f"trap {k}", host(g[k]), r[k], dtype)
+    vc = oracle_vals(tc)
+    rc = ocplx.bwd(vc["u"], vc["delta"], vc["A"], vc["B"], vc["C"], vc["dout"], vc["D"],
+                   vc["z"], vc["bias"], vc["h0"], softplus=sp)
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        assert_close(f"complex {k}", host(gc[k]), rc[k], dtype)
