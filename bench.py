@@ -326,6 +326,16 @@ def main():
     if not args.no_extra:
         extra = extra_timings(cx, msel, msel_inputs, w, sets, nsets, alg, tc, upd, vf_bwd, ws,
                               fwd, bwd, args)
+    else:  # the chunk-carry pass alone, a few launches (profiler runs count its bytes too)
+        s0 = sets[0]
+        extra["chunk_carry_cold"] = entry(
+            cx.cold(lambda: msel.msel_scan_chunk_carry(s0["u"], s0["delta"], s0["A"], s0["B"],
+                                                       s0["bias"], True, chunk_states=s0["cs"],
+                                                       final_state=s0["fin"]), reps=3),
+            alg["chunk_carry"], tc, "chunk_carry_kernel (one launch) after a cache flush")
+    for k in ("chunk_carry_cold",):
+        if k in extra:
+            extra[k]["traffic"] = measured_traffic(w.name, "chunk_carry_kernel")
     kernels.update(extra)
 
     cpu = None

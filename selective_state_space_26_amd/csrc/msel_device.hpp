@@ -309,9 +309,13 @@ constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 __device__ __forceinline__ float readlane(float v, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
-// Lane `lane` of the result is v, the other lanes keep old (lane is wave-uniform).
+// Lane `lane` of the result is v, the other lanes keep old: one v_writelane_b32.  v and lane
+// must be wave-uniform (every caller passes a readlane result or a wave-wide sum).  gfx9
+// reads at most one SGPR per VALU instruction through the constant bus, so the lane select
+// goes in M0.
 __device__ __forceinline__ float writelane(float v, int lane, float old) {
-    return (static_cast<int>(__lane_id()) == lane) ? v : old;
+    asm("v_writelane_b32 %0, %1, m0" : "+v"(old) : "s"(v), "{m0}"(lane));
+    return old;
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

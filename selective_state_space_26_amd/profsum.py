@@ -5,7 +5,8 @@
         --kernel bwd_main_kernel [--match "bwd_main_kernel<msel::bf16_t, ..., false>"] \\
         --copy-mib 512 --workload NAME --command-fetch "..." --command-write "..."
 
-`stats` turns a `--kernel-trace --stats` kernel_stats.csv into a short markdown table.
+`stats` turns a `--kernel-trace --stats` kernel_stats.csv into a short markdown table (with
+`--trace KERNEL_TRACE_CSV`, also the busiest kernels split by launch grid).
 
 `counters` turns `--pmc SQ_...` counter_collection.csv files (one per pass) into a per-kernel
 table: the mean per dispatch of each counter and the ratios that say what bounds a kernel.
@@ -69,7 +70,11 @@ def short_name(name: str) -> str:
     return n.split("(")[0]
 
 
-def stats(csv_path: str, out: str, command: str) -> None:
+def stats(csv_path: str, out: str, command: str, trace_csv: str | None = None,
+          top: int = 12) -> None:
+    """The --stats table; with the kernel trace of the same run, also each of the `top`
+    busiest kernels split by launch grid (one kernel serves several problem sizes in one run,
+    and its per-size durations are what per-launch timings compare with)."""
     rows = list(csv.DictReader(open(csv_path)))
     lines = [f"# rocprofv3 kernel statistics: {os.path.basename(out)}", "",
              "Command (from the repository root on the GPU host):", "", "```", command, "```",
@@ -79,6 +84,23 @@ def stats(csv_path: str, out: str, command: str) -> None:
         lines.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | "
                      f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    if trace_csv is not None:
+        busiest = [r["Name"] for r in rows[:top]]
+        groups = defaultdict(list)
+        for r in csv.DictReader(open(trace_csv)):
+            if r["Kernel_Name"] not in busiest:
+                continue
+            key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+        lines += ["", "The same run from its kernel trace, split by launch grid (threads in x, "
+                  "workgroup size): one line per kernel and problem size.", "",
+                  "| kernel | grid x | workgroup | calls | avg us | median us | min us | max us |",
+                  "|---|---:|---:|---:|---:|---:|---:|---:|"]
+        for name in busiest:
+            for (n, gx, wx), us in sorted((k, v) for k, v in groups.items() if k[0] == name):
+                lines.append(f"| `{short_name(n)}` | {gx} | {wx} | {len(us)} | "
+                             f"{statistics.mean(us):.1f} | {statistics.median(us):.1f} | "
+                             f"{min(us):.1f} | {max(us):.1f} |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -201,6 +223,7 @@ def main():
     s.add_argument("csv")
     s.add_argument("out")
     s.add_argument("--command", required=True)
+    s.add_argument("--trace", default=None, help="the run's kernel_trace.csv")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_csv")
     t.add_argument("write_csv")
@@ -224,7 +247,7 @@ def main():
     if a.cmd == "counters":
         counters(a.csv, a.out, [tuple(x.split("=", 1)) for x in a.select], a.command)
     elif a.cmd == "stats":
-        stats(a.csv, a.out, a.command)
+        stats(a.csv, a.out, a.command, a.trace)
     else:
         traffic(a.fetch_csv, a.write_csv, a.out, a.kernel, a.copy_mib, a.workload,
                 a.command_fetch, a.command_write, a.match)
