@@ -250,16 +250,25 @@ struct TileStage {
     static_assert(K % VW == 0 && K % 4 == 0 && RV % 64 == 0 && NTH % 64 == 0,
                   "a row must split over whole wavefronts");
     Raw<T, VW> nxt[G];
+    int xr[G];    // staged row of this thread's i-th vector (wave-uniform)
+    int toff[G];  // its first step within the tile
+
+    __device__ __forceinline__ explicit TileStage(int tid) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int v = tid + i * NTH;
+            xr[i] = __builtin_amdgcn_readfirstlane(v / RV);
+            toff[i] = (v - xr[i] * RV) * VW;
+        }
+    }
 
     // row(x): the global row that staged row x comes from; t_tile: the tile's first step
     template <typename RowFn>
     __device__ __forceinline__ void load(int tid, RowFn row, int t_tile, int L) {
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const int v = tid + i * NTH;
-            if (NVEC % NTH != 0 && v >= NVEC) break;  // wave-uniform
-            const int x = __builtin_amdgcn_readfirstlane(v / RV);
-            load_raw<T, VW, VEC>(row(x), t_tile + (v - x * RV) * VW, L, nxt[i]);
+            if (NVEC % NTH != 0 && tid + i * NTH >= NVEC) break;  // wave-uniform
+            load_raw<T, VW, VEC>(row(xr[i]), t_tile + toff[i], L, nxt[i]);
         }
     }
     __device__ __forceinline__ void store(int tid, f32x4* __restrict__ buf) const {

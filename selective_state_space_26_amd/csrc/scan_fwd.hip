@@ -102,7 +102,7 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
     constexpr int TILE = 64 * K;
     static_assert(TILE % kChunk == 0, "a tile must hold whole chunks");
 
-    Stage st;
+    Stage st(tid);
     auto rows = [&](int n) {  // staged row x of state n: B (x = 0) or C (x = 1)
         return [=](int x) { return (x == 0 ? Bb : Cb) + static_cast<size_t>(n) * L; };
     };
@@ -151,9 +151,12 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
         for (int q = 0; q < kCpt; ++q) csv[q] = 0.0f;
 
         for (int n = 0; n < N; ++n) {
-            // the next state's rows (the next tile's first state after the last one)
-            const bool more = STAGE && ((n + 1 < N) || (tile + TILE < L));
-            if (more) st.load(tid, rows(n + 1 < N ? n + 1 : 0), n + 1 < N ? tile : tile + TILE, L);
+            // the next state's rows (the next tile's first state after the last one); one
+            // compare of scalars (an || of two compares would be carried through a VGPR)
+            const int n_next = (n + 1 < N) ? n + 1 : 0;
+            const int t_next = (n + 1 < N) ? tile : tile + TILE;
+            const bool more = STAGE && t_next < L;
+            if (more) st.load(tid, rows(n_next), t_next, L);
             const float An = readlane(Av, n);
             float a[K], bb[K], bc[K];
             if constexpr (STAGE) Stage::read(stage[buf], 0, lane, bc);
@@ -171,7 +174,7 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
                     bb[k] = fmaf(a[k], cp[k] * (k == 0 ? bprev0 : bc[k - 1]), du[k] * bc[k]);
                 else
                     bb[k] = du[k] * bc[k];
-                h = fmaf(a[k], h, bb[k]);
+                h = k == 0 ? bb[0] : fmaf(a[k], h, bb[k]);  // the chain from a zero state
             }
             float P = exp2_hw(An * sum_dt);
             float S = h;
