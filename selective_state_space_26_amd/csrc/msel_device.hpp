@@ -232,8 +232,9 @@ __device__ __forceinline__ void unpack(const Raw<T, K>& r, float (&v)[K]) {
 // Rows of one tile (64*K steps) staged in LDS as fp32 by a whole workgroup of NTH threads and
 // read by each of its wavefronts: for rows shared by the workgroup's channels (B and C of one
 // batch row), which are then loaded and converted once per workgroup instead of once per
-// wavefront.  A buffer is [ROWS rows][K/4 words][64 lanes] of 16-byte words, so that lane l
-// reads its K steps of a row as K/4 words of its own column, the 64 lanes consecutive words.
+// wavefront.  A buffer is [ROWS rows][K/4 words][64 lanes (+2 padding)] of 16-byte words, so
+// that lane l reads its K steps of a row as K/4 words of its own column, the 64 lanes
+// consecutive words.
 // load() issues the global loads of one set of rows into registers (thread tid moves vectors
 // tid, tid + NTH, ...; a row is a whole number of wavefronts' vectors, so which row a vector
 // belongs to is wave-uniform); store() converts them into a buffer; read() gives a lane its K
@@ -246,7 +247,13 @@ struct TileStage {
     static constexpr int RV = 64 * K / VW;           // vectors per row
     static constexpr int NVEC = ROWS * RV;
     static constexpr int G = (NVEC + NTH - 1) / NTH; // vectors per thread (the last partial)
-    static constexpr int kWords = ROWS * QW * 64;    // 16-byte words per buffer
+    // 16-byte words from one (row, word) line of 64 lanes to the next: 66, not 64.  A store
+    // pass (8 lanes, 128 bytes) puts neighbouring threads' vectors in different lines of the
+    // same lane (fp32: 4 lines of one lane; bf16: 2 lines of each of 4 lanes); with lines
+    // 2 words (32 bytes) apart modulo 128 bytes, those 8 vectors fill 8 different bank groups.
+    // Reads stay 64 consecutive words of one line.
+    static constexpr int kLine = 64 + 2;
+    static constexpr int kWords = ROWS * QW * kLine; // 16-byte words per buffer
     static_assert(K % VW == 0 && K % 4 == 0 && RV % 64 == 0 && NTH % 64 == 0,
                   "a row must split over whole wavefronts");
     Raw<T, VW> nxt[G];
@@ -283,14 +290,15 @@ struct TileStage {
             const int l = tl / K, q0 = (tl - l * K) / 4;
 #pragma unroll
             for (int j = 0; j < VW / 4; ++j)
-                buf[(x * QW + q0 + j) * 64 + l] = f32x4{f[4 * j], f[4 * j + 1], f[4 * j + 2], f[4 * j + 3]};
+                buf[(x * QW + q0 + j) * kLine + l] =
+                    f32x4{f[4 * j], f[4 * j + 1], f[4 * j + 2], f[4 * j + 3]};
         }
     }
     __device__ __forceinline__ static void read(const f32x4* __restrict__ buf, int x, int lane,
                                                 float (&r)[K]) {
 #pragma unroll
         for (int q = 0; q < QW; ++q) {
-            const f32x4 w4 = buf[(x * QW + q) * 64 + lane];
+            const f32x4 w4 = buf[(x * QW + q) * kLine + lane];
             r[4 * q] = w4[0];
             r[4 * q + 1] = w4[1];
             r[4 * q + 2] = w4[2];

@@ -48,8 +48,8 @@ __host__ __device__ constexpr int fwd_waves() { return !TRAP ? kFwdStageWaves : 
 
 // STAGE (plain rule): a state's B and C rows over a tile are read from L2 once per workgroup
 // (bf16 converted to fp32 on the way), into LDS, and read by each of its wavefronts, instead
-// of by every wavefront: [2 tensors][K/4 words][64 lanes] of 16-byte words, so that a lane's
-// K steps are K/4 words of its own column and the 64 lanes read consecutive words.  Two
+// of by every wavefront: [2 tensors][K/4 words][64 lanes + 2] of 16-byte words, so that a
+// lane's K steps are K/4 words of its own column and the 64 lanes read consecutive words.  Two
 // buffers: the next state's rows are staged while the current one is computed, with one
 // barrier per state.  Without the stage an fp32 wavefront streams 8 KB of B and C rows per
 // state and tile through L2, eight times the HBM bytes it reads.  (The trapezoidal rule loads
