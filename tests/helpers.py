@@ -1,6 +1,7 @@
 """Shared helpers of the GPU tests: seeded inputs on the device and oracle comparisons."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -51,8 +52,19 @@ def rel_err(got, ref) -> float:
     return float(np.max(np.abs(got - ref)) / scale)
 
 
+def _record_margin(name, e, dtype):
+    """With MSEL_MARGINS_LOG set to a file, append 'test | tensor | err/tol' to it: the
+    parity margins of a whole run, for the design notes."""
+    path = os.environ.get("MSEL_MARGINS_LOG")
+    if path:
+        test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+        with open(path, "a") as fh:
+            fh.write(f"{test} | {name} | {dtype} | {e:.4e} | {e / tol(dtype):.4f}\n")
+
+
 def assert_close(name, got, ref, dtype):
     e = rel_err(got, ref)
+    _record_margin(name, e, dtype)
     assert e <= tol(dtype), f"{name}: max|err|/max|ref| = {e:.3e} > {tol(dtype):.0e}"
     return e
 
@@ -86,6 +98,7 @@ class MaxErr:
             assert self.count == expect_count, (self.name, self.count, expect_count)
         e = self.err / self.scale if self.scale > 0 else self.err
         log(f"{self.name}: {self.count} elements, max|err|/max|ref| = {e:.3e}")
+        _record_margin(self.name, e, self.dtype)
         assert e <= tol(self.dtype), \
             f"{self.name}: max|err|/max|ref| = {e:.3e} > {tol(self.dtype):.0e}"
         return e
