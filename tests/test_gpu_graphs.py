@@ -62,6 +62,44 @@ def _complex():
     return step, ("out", "fin", "du", "ddelta", "dz"), ("dA", "dB", "dC", "dD", "ddelta_bias")
 
 
+def _noalloc():
+    """The backward that allocates nothing (its workspace is the library's static array), with
+    chunk states rebuilt: the path for callers under graph capture."""
+    t = msel_inputs.make(*SHAPE, "bf16", 35, with_dout=True, with_h0=True)
+    d = to_device(t)
+    a = (d["u"], d["delta"], d["A"], d["B"], d["C"])
+    o = (d["D"], d["z"], d["bias"], True, d["h0"])
+
+    def step():
+        out, fin, _ = msel.msel_scan_fwd(*a, *o)
+        g = msel.msel_scan_bwd_noalloc(*a, d["dout"], *o, want_dh0=True)
+        return dict(out=out, fin=fin, **g)
+    return (step, ("out", "fin", "du", "ddelta", "dz", "dh0"),
+            ("dA", "dB", "dC", "dD", "ddelta_bias"))
+
+
+def _variants_rebuilt():
+    """The trapezoidal and complex backwards with their chunk states rebuilt by their own
+    chunk-carry passes inside the call."""
+    t = msel_inputs.make(*SHAPE, "bf16", 36, with_dout=True, with_lam=True)
+    d = to_device(t)
+    tc = msel_inputs.make(*SHAPE, "bf16", 37, with_dout=True, complex_A=True)
+    dc = to_device(tc)
+
+    def step():
+        g = msel.msel_scan_trap_bwd(d["u"], d["delta"], d["lam"], d["A"], d["B"], d["C"],
+                                    d["dout"], None, d["D"], d["z"], d["bias"], True)
+        gc = msel.msel_scan_complex_bwd(dc["u"], dc["delta"], dc["A"], dc["B"], dc["C"],
+                                        dc["dout"], None, dc["D"], dc["z"], dc["bias"], True)
+        r = {f"trap_{k}": v for k, v in g.items()}
+        r.update({f"cplx_{k}": v for k, v in gc.items()})
+        return r
+    exact = ("trap_du", "trap_ddelta", "trap_dz", "trap_dlam", "cplx_du", "cplx_ddelta",
+             "cplx_dz")
+    summed = ("trap_dA", "trap_dB", "trap_dC", "cplx_dA", "cplx_dB", "cplx_dC")
+    return step, exact, summed
+
+
 def _conv():
     t = msel_inputs.make_conv(2, 6, 1100, 4, "bf16", 34, with_state=True, with_dout=True)
     d = to_device(t)
@@ -75,10 +113,14 @@ def _conv():
     return step, ("out", "state_out", "dx", "dstate"), ("dweight", "dbias")
 
 
-@pytest.mark.parametrize("variant", ["scan", "trap", "complex", "conv"])
+STEPS = {"scan": _scan, "trap": _trap, "complex": _complex, "conv": _conv, "noalloc": _noalloc,
+         "variants_rebuilt": _variants_rebuilt}
+
+
+@pytest.mark.parametrize("variant", list(STEPS))
 def test_training_step_replays_from_a_hip_graph(variant):
     log(f"graph {variant}")
-    step, exact, summed = {"scan": _scan, "trap": _trap, "complex": _complex, "conv": _conv}[variant]()
+    step, exact, summed = STEPS[variant]()
     eager = step()
     torch.cuda.synchronize()
     for n in exact + summed:

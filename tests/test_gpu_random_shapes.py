@@ -1,9 +1,11 @@
 """Seeded random shapes for every variant against the fp64 oracles: batch 1-3, dim 1-13 (most
 not a multiple of a workgroup's channels), every dstate the variant allows, lengths from one
-step to a few chunks with ragged tails, both dtypes, and random optional inputs.  The shapes are
-drawn once from a fixed seed, so a failure names a case that can be run again by itself.
-The bar is the parity bar of the other tests: max|gpu - oracle| <= tol * max|oracle| (1e-4
-fp32, 1e-2 bf16 inputs; the convolution's fp32 sums at 1e-4)."""
+step to a few chunks with ragged tails, both dtypes, and random optional inputs.  The
+chunk-carry passes are checked against the oracles' chunk states too, and every other case's
+backward runs with chunk states that the library rebuilds.  The shapes are drawn once from a
+fixed seed, so a failure names a case that can be run again by itself.  The bar is the parity
+bar of the other tests: max|gpu - oracle| <= tol * max|oracle| (1e-4 fp32, 1e-2 bf16 inputs;
+the convolution's fp32 sums at 1e-4)."""
 import numpy as np
 import pytest
 
@@ -66,6 +68,13 @@ def _vals(t):
     return {k: (None if t.get(k) is None else t.values(k)) for k in t}
 
 
+def _check_states(cs, ccs, cfin, rcs, rf, dtype):
+    """The forward's chunk states and the chunk-carry pass's against the oracle's."""
+    assert_close("chunk_states", host(cs), rcs, dtype)
+    assert_close("chunk_carry chunk_states", host(ccs), rcs, dtype)
+    assert_close("chunk_carry final_state", host(cfin), rf, dtype)
+
+
 @pytest.mark.parametrize("case", CASES, ids=_ids)
 def test_random_shape_matches_oracle(case):
     kind, k = case
@@ -103,6 +112,8 @@ def test_random_shape_matches_oracle(case):
         a = (d["u"], d["delta"], d["A"], d["B"], d["C"])
         o = (d["D"], d["z"], d["bias"], sp, d["h0"])
         out, fin, cs = msel.msel_scan_fwd(*a, *o, return_chunk_states=True)
+        ccs, cfin = msel.msel_scan_chunk_carry(d["u"], d["delta"], d["A"], d["B"], d["bias"],
+                                               sp, d["h0"])
         g = msel.msel_scan_bwd(*a, d["dout"], *o, chunk_states=cs if extra else None,
                                want_dh0=with_h0)
         torch.cuda.synchronize()
@@ -111,7 +122,7 @@ def test_random_shape_matches_oracle(case):
                                  v["bias"], v["h0"], softplus=sp, chunk_len=msel.chunk_len())
         r = oracle.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
                        v["bias"], v["h0"], softplus=sp)
-        assert_close("chunk_states", host(cs), rcs, dtype)
+        _check_states(cs, ccs, cfin, rcs, rf, dtype)
         names = ["du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias"]
     elif kind == "trap":
         t = _scan_inputs(msel_inputs.make(bsz, dim, N, L, dtype, seed, with_lam=True,
@@ -120,15 +131,20 @@ def test_random_shape_matches_oracle(case):
         a = (d["u"], d["delta"], d["lam"], d["A"], d["B"], d["C"])
         o = (d["D"], d["z"], d["bias"], sp, d["h0"], d.get("u_prev"), d.get("B_prev"))
         out, fin, cs = msel.msel_scan_trap_fwd(*a, *o, return_chunk_states=True)
-        g = msel.msel_scan_trap_bwd(*a, d["dout"], cs, *o, want_dh0=with_h0, want_dprev=extra)
+        ccs, cfin = msel.msel_scan_trap_chunk_carry(d["u"], d["delta"], d["lam"], d["A"], d["B"],
+                                                    d["bias"], sp, d["h0"], d.get("u_prev"),
+                                                    d.get("B_prev"))
+        g = msel.msel_scan_trap_bwd(*a, d["dout"], cs if k % 2 else None, *o, want_dh0=with_h0,
+                                    want_dprev=extra)
         torch.cuda.synchronize()
         v = _vals(t)
-        ro, rf, _ = otrap.fwd(v["u"], v["delta"], v["lam"], v["A"], v["B"], v["C"], v["D"],
+        ro, rf, rcs = otrap.fwd(v["u"], v["delta"], v["lam"], v["A"], v["B"], v["C"], v["D"],
                               v["z"], v["bias"], v["h0"], v.get("u_prev"), v.get("B_prev"),
                               softplus=sp, chunk_len=msel.chunk_len())
         r = otrap.bwd(v["u"], v["delta"], v["lam"], v["A"], v["B"], v["C"], v["dout"], v["D"],
                       v["z"], v["bias"], v["h0"], v.get("u_prev"), v.get("B_prev"), softplus=sp)
         names = ["du", "ddelta", "dlam", "dA", "dB", "dC", "dD", "ddelta_bias"]
+        _check_states(cs, ccs, cfin, rcs, rf, dtype)
         if extra:
             names += ["du_prev", "dB_prev"]
     else:
@@ -138,14 +154,18 @@ def test_random_shape_matches_oracle(case):
         a = (d["u"], d["delta"], d["A"], d["B"], d["C"])
         o = (d["D"], d["z"], d["bias"], sp, d["h0"])
         out, fin, cs = msel.msel_scan_complex_fwd(*a, *o, return_chunk_states=True)
-        g = msel.msel_scan_complex_bwd(*a, d["dout"], cs, *o, want_dh0=with_h0)
+        ccs, cfin = msel.msel_scan_complex_chunk_carry(d["u"], d["delta"], d["A"], d["B"],
+                                                       d["bias"], sp, d["h0"])
+        g = msel.msel_scan_complex_bwd(*a, d["dout"], cs if k % 2 else None, *o,
+                                       want_dh0=with_h0)
         torch.cuda.synchronize()
         v = _vals(t)
-        ro, rf, _ = ocplx.fwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"],
+        ro, rf, rcs = ocplx.fwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"],
                               v["bias"], v["h0"], softplus=sp, chunk_len=msel.chunk_len())
         r = ocplx.bwd(v["u"], v["delta"], v["A"], v["B"], v["C"], v["dout"], v["D"], v["z"],
                       v["bias"], v["h0"], softplus=sp)
         names = ["du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias"]
+        _check_states(cs, ccs, cfin, rcs, rf, dtype)
     assert_close("out", host(out), ro, dtype)
     assert_close("final_state", host(fin), rf, dtype)
     if with_h0:
