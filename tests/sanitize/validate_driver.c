@@ -145,7 +145,11 @@ static void scan_checks(void) {
     EXPECT(msel_validate_complex_fwd(&c), MSEL_ERR_SHAPE);
     c.dstate = 8;
     EXPECT(msel_validate_complex_fwd(&c), MSEL_OK);
-    EXPECT(msel_scan_complex_bwd(&c, &g, ws, need, NULL), MSEL_ERR_NULL);  /* chunk_states */
+    /* chunk_states NULL: rebuilt into the front of a workspace sized for that */
+    size_t need_c = msel_scan_bwd_workspace_bytes(&c);
+    EXPECT(msel_validate_complex_bwd(&c, &g, ws, need_c), MSEL_OK);
+    EXPECT(msel_validate_complex_bwd(&c, &g, ws, need_c - 1), MSEL_ERR_WORKSPACE);
+    EXPECT(msel_scan_complex_bwd(&c, &g, ws, need_c - 1, NULL), MSEL_ERR_WORKSPACE);
 }
 
 static void conv_checks(void) {
