@@ -25,7 +25,8 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers on the current HIP device, contiguous, row-major.
  *  - The caller owns every buffer.  The library allocates nothing, keeps no state between
- *    calls (but for the ring-wait counter of msel_ring_timeouts), is re-entrant, and never
+ *    calls (but for the device counters read by msel_ring_timeouts and, in the checked build,
+ *    msel_bound_violations), is re-entrant, and never
  *    synchronizes: work is enqueued on `stream` and the call returns.  Errors in the arguments are detected on the host before anything is
  *    enqueued; the return value is then not MSEL_OK and no device memory is touched.
  *  - Inputs are read-only.  Outputs must not be the same pointer as any input (checked),
@@ -217,6 +218,32 @@ msel_status msel_ring_timeouts(unsigned long long *count);
  * 0.1 s).  For tests of the timeout path, which set a tiny limit so that waits give up while
  * every kernel still ends normally.  Not thread-safe against concurrent backward calls. */
 void msel_set_ring_spin_limit(uint32_t polls);
+
+/* ------------------------------------------------------------------------------------------
+ * The checked build.  libmsel_checked.so is the same library compiled with MSEL_CHECKED: every
+ * index that a kernel forms into a global buffer or an LDS array is compared with the extent
+ * of what it indexes.  An index out of range is counted in a device record of its source file
+ * and replaced by 0, so the access stays inside the buffer and the kernel ends normally (a
+ * failed check never traps, faults or hangs).  Outputs are those of the release build; the
+ * kernels are slower.  For tests and debugging (these checks are not from the pages).
+ */
+
+/* 1 in the checked build, 0 in the release build. */
+int msel_checked_build(void);
+
+/* Waits for the current device to finish its work, then stores the number of out-of-range
+ * indexes that the kernels met on that device since the last call in *count and, when the
+ * count is nonzero, where the first one was: *file (1 scan_fwd.hip, 2 chunk_carry.hip,
+ * 3 scan_bwd.hip, 4 conv1d.hip, 5 scan_cplx.hip, 6 scan_cplx_bwd.hip; the first file with a
+ * nonzero count) and *line (its source line); 0 and 0 otherwise.  Clears the records.  The
+ * release build always reports 0.  MSEL_ERR_NULL if a pointer is NULL, MSEL_ERR_HIP if the
+ * runtime fails. */
+msel_status msel_bound_violations(unsigned long long *count, uint32_t *file, uint32_t *line);
+
+/* Checked build: enqueues on `stream` one kernel that forms index 1 of a one-element device
+ * array, which its check must count (file 1) and redirect to element 0.  The release build
+ * returns MSEL_ERR_UNSUPPORTED and enqueues nothing. */
+msel_status msel_bounds_selftest(hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * The exponential-trapezoidal variant of the scan (Mamba-3).

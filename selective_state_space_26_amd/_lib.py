@@ -4,11 +4,14 @@ There is no fallback of any kind: if the library is not built, every call raises
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmsel.so")
+# the same sources built with every kernel index range-checked (msel_checked_build)
+LIB_CHECKED_PATH = os.path.join(HERE, "libmsel_checked.so")
 
 ABI_VERSION = 1
 MSEL_F32, MSEL_BF16 = 0, 1
@@ -73,15 +76,26 @@ EXPORTS = ["msel_abi_version", "msel_chunk_len", "msel_num_chunks", "msel_status
            "msel_validate_complex_bwd", "msel_scan_complex_bwd", "msel_ring_timeouts",
            "msel_set_ring_spin_limit", "msel_scan_bwd_noalloc", "msel_validate_trap_chunk_carry",
            "msel_scan_trap_chunk_carry", "msel_validate_complex_chunk_carry",
-           "msel_scan_complex_chunk_carry"]
+           "msel_scan_complex_chunk_carry", "msel_checked_build", "msel_bound_violations",
+           "msel_bounds_selftest"]
+
+
+def default_path() -> str:
+    """The library load() uses: MSEL_LIBRARY=checked selects libmsel_checked.so, any other
+    non-empty value is taken as a path; by default the in-tree libmsel.so."""
+    v = os.environ.get("MSEL_LIBRARY", "")
+    if v == "checked":
+        return LIB_CHECKED_PATH
+    return v or LIB_PATH
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
-    """Load libmsel.so (once).  Raises if it is missing: the product has no other path."""
+    """Load the library (once; default_path() unless `path` is given).  Raises if it is
+    missing: the product has no other path."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or default_path()
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is not built; run `python -m selective_state_space_26_amd.build`"
                            " (or __graft_entry__.build())")
@@ -151,11 +165,32 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.msel_ring_timeouts.argtypes = [ctypes.POINTER(ctypes.c_ulonglong)]
     lib.msel_set_ring_spin_limit.restype = None
     lib.msel_set_ring_spin_limit.argtypes = [ctypes.c_uint32]
+    lib.msel_checked_build.restype = ctypes.c_int
+    lib.msel_checked_build.argtypes = []
+    lib.msel_bound_violations.restype = ctypes.c_int
+    lib.msel_bound_violations.argtypes = [ctypes.POINTER(ctypes.c_ulonglong),
+                                          ctypes.POINTER(ctypes.c_uint32),
+                                          ctypes.POINTER(ctypes.c_uint32)]
+    lib.msel_bounds_selftest.restype = ctypes.c_int
+    lib.msel_bounds_selftest.argtypes = [_P]
     if lib.msel_abi_version() != ABI_VERSION:
         raise RuntimeError("libmsel.so ABI version mismatch")
     if path is None:
         _lib = lib
     return lib
+
+
+@contextlib.contextmanager
+def using(path: str):
+    """Inside the block every call of the binding goes to the library at `path` (for example
+    LIB_CHECKED_PATH); the one loaded before is restored after it."""
+    global _lib
+    prev = _lib
+    _lib = load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
 
 
 def check(fn: str, code: int) -> None:

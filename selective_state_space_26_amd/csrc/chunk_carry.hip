@@ -56,7 +56,9 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
     const int dg = idx - b * dgroups;
     const int L = p.L;
     const int N = p.N;
-    const T* __restrict__ Bb = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
+    const T* __restrict__ Bb =
+        static_cast<const T*>(p.Bm) + static_cast<size_t>(MSEL_IDX(b, p.B)) * N * L;
+    [[maybe_unused]] const size_t BDN = static_cast<size_t>(p.B) * p.D * N;
 
     int dch[R];
     bool live[R];
@@ -71,22 +73,25 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
         const int d = dg * R + r;
         live[r] = d < p.D;
         dch[r] = live[r] ? d : p.D - 1;
-        const size_t ch = static_cast<size_t>(b) * p.D + dch[r];
+        const size_t ch = MSEL_IDX(static_cast<size_t>(b) * p.D + dch[r],
+                                   static_cast<size_t>(p.B) * p.D);
         u[r] = static_cast<const T*>(p.u) + ch * L;
         dl[r] = static_cast<const T*>(p.delta) + ch * L;
         lm[r] = TRAP ? static_cast<const T*>(p.lam) + ch * L : nullptr;
-        bias[r] = p.bias ? p.bias[dch[r]] : 0.0f;
-        const float* Ad = p.A + static_cast<size_t>(dch[r]) * N;
+        bias[r] = p.bias ? p.bias[MSEL_IDX(dch[r], p.D)] : 0.0f;
+        const float* Ad = p.A + static_cast<size_t>(MSEL_IDX(dch[r], p.D)) * N;
         // lane n holds A[d, n] * log2(e) (CPLX: lane 2j+1 holds A_im / (2 pi), in revolutions)
         // and the state h_n entering the current chunk
         if constexpr (CPLX) {
-            Av[r] = (lane < N) ? ((lane & 1) ? Ad[lane] * kInv2Pi : Ad[lane] * kLog2e) : 0.0f;
-            Are[r] = (lane < N) ? Ad[lane & ~1] * kLog2e : 0.0f;
-            Aim[r] = (lane < N) ? Ad[lane | 1] * kInv2Pi : 0.0f;
+            Av[r] = (lane < N) ? ((lane & 1) ? Ad[MSEL_IDX(lane, N)] * kInv2Pi
+                                             : Ad[MSEL_IDX(lane, N)] * kLog2e)
+                               : 0.0f;
+            Are[r] = (lane < N) ? Ad[MSEL_IDX(lane & ~1, N)] * kLog2e : 0.0f;
+            Aim[r] = (lane < N) ? Ad[MSEL_IDX(lane | 1, N)] * kInv2Pi : 0.0f;
         } else {
-            Av[r] = (lane < N) ? Ad[lane < N ? lane : 0] * kLog2e : 0.0f;
+            Av[r] = (lane < N) ? Ad[MSEL_IDX(lane < N ? lane : 0, N)] * kLog2e : 0.0f;
         }
-        carry[r] = (p.h0 != nullptr && lane < N) ? p.h0[ch * N + lane] : 0.0f;
+        carry[r] = (p.h0 != nullptr && lane < N) ? p.h0[MSEL_IDX(ch * N + lane, BDN)] : 0.0f;
         u_last[r] = 0.0f;
         if constexpr (TRAP)
             if (p.u_prev != nullptr) u_last[r] = Elem<T>::load1(static_cast<const T*>(p.u_prev) + ch);
@@ -95,7 +100,9 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
     float B_last = 0.0f;
     if constexpr (TRAP)
         if (p.B_prev != nullptr && lane < N)
-            B_last = Elem<T>::load1(static_cast<const T*>(p.B_prev) + static_cast<size_t>(b) * N + lane);
+            B_last = Elem<T>::load1(static_cast<const T*>(p.B_prev) +
+                                    MSEL_IDX(static_cast<size_t>(b) * N + lane,
+                                             static_cast<size_t>(p.B) * N));
 
     for (int c = 0; c < p.nchunks; ++c) {
         const int t0 = c * kChunk + lane * K;
@@ -106,8 +113,9 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             if (live[r] && lane < N)
-                p.chunk_states[((static_cast<size_t>(b) * p.D + dch[r]) * p.nchunks + c) * N +
-                               lane] = carry[r];
+                p.chunk_states[MSEL_IDX(
+                    ((static_cast<size_t>(b) * p.D + dch[r]) * p.nchunks + c) * N + lane,
+                    BDN * p.nchunks)] = carry[r];
             float uu[K], dd[K], ll[TRAP ? K : 1];
             load_k_cached<T, K, VEC>(u[r], t0, L, uu);
             load_k_cached<T, K, VEC>(dl[r], t0, L, dd);
@@ -156,16 +164,17 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
         float B_next = B_last;  // TRAP: B of every state at this chunk's last step
         Raw<T, K> B1, B2;
         load_raw<T, K, VEC>(Bb, t0, L, B1);
-        load_raw<T, K, VEC>(Bb + static_cast<size_t>(N > 1 ? 1 : 0) * L, t0, L, B2);
+        load_raw<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(N > 1 ? 1 : 0, N)) * L, t0, L, B2);
         for (int n = 0; n < N; n += 2) {
             const int n2 = (n + 1 < N) ? n + 1 : n;
             float bv1[K], bv2[K];
             unpack(B1, bv1);
             unpack(B2, bv2);
             if (n + 2 < N) {
-                load_raw<T, K, VEC>(Bb + static_cast<size_t>(n + 2) * L, t0, L, B1);
-                load_raw<T, K, VEC>(Bb + static_cast<size_t>(n + 3 < N ? n + 3 : n + 2) * L, t0,
-                                    L, B2);
+                load_raw<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(n + 2, N)) * L, t0, L, B1);
+                load_raw<T, K, VEC>(
+                    Bb + static_cast<size_t>(MSEL_IDX(n + 3 < N ? n + 3 : n + 2, N)) * L, t0, L,
+                    B2);
             }
             if constexpr (TRAP) {
                 B_next = writelane(readlane(bv1[K - 1], 63), n, B_next);
@@ -223,7 +232,8 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
         if (p.final_state != nullptr && live[r] && lane < N)
-            p.final_state[(static_cast<size_t>(b) * p.D + dch[r]) * N + lane] = carry[r];
+            p.final_state[MSEL_IDX((static_cast<size_t>(b) * p.D + dch[r]) * N + lane, BDN)] =
+                carry[r];
 }
 
 namespace {
@@ -261,5 +271,7 @@ hipError_t launch_chunk_carry(const ScanParams& p, bool bf16, bool cplx, hipStre
     if (bf16) return cc_rule<bf16_t>(p, cplx, stream);
     return cc_rule<float>(p, cplx, stream);
 }
+
+MSEL_BOUNDS_TAKER(take_bounds_chunk_carry)
 
 }  // namespace msel

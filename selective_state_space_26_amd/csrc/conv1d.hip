@@ -67,9 +67,10 @@ __device__ __forceinline__ bool seg_of(const ConvParams& p, Seg& s) {
     const uint32_t wave = blockIdx.x * kConvWaves + wid;  // < 2^31: checked on the host
     if (wave >= static_cast<uint32_t>(p.rows) * static_cast<uint32_t>(p.segs)) return false;
     const uint32_t row = div_by(wave, p.segs_div);
-    s.row = row;
+    s.row = MSEL_IDX(static_cast<int64_t>(row), p.rows);
     s.seg = static_cast<int>(wave - row * static_cast<uint32_t>(p.segs));
-    s.d = static_cast<int>(row - div_by(row, p.dim_div) * static_cast<uint32_t>(p.D));
+    s.d = MSEL_IDX(static_cast<int>(row - div_by(row, p.dim_div) * static_cast<uint32_t>(p.D)),
+                   p.D);
     s.tile0 = s.seg * p.seg_tiles;
     s.ntiles = min(p.seg_tiles, p.tiles - s.tile0);
     return true;
@@ -80,7 +81,7 @@ __device__ __forceinline__ bool seg_of(const ConvParams& p, Seg& s) {
 template <typename T, int H>
 __device__ __forceinline__ float input_at(const T* __restrict__ xr, const T* st, int t) {
     if (t >= 0) return Elem<T>::load1(xr + t);
-    return st != nullptr ? Elem<T>::load1(st + H + t) : 0.0f;
+    return st != nullptr ? Elem<T>::load1(st + H + (MSEL_IDX(H + t, H) - H)) : 0.0f;
 }
 
 // pre-activation of lane step k from the window [prev[0..H), v[0..K)]
@@ -116,7 +117,8 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_fwd_kernel(ConvParams p)
     load_k_cached<T, K, VEC>(xr, t0, L, v);
     float wk[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) wk[i] = p.w[static_cast<size_t>(sg.d) * W + i];
+    for (int i = 0; i < W; ++i)
+        wk[i] = p.w[MSEL_IDX(static_cast<size_t>(sg.d) * W + i, static_cast<size_t>(p.D) * W)];
     const float b = p.bias != nullptr ? p.bias[sg.d] : 0.0f;
 
     // the H inputs before each lane's first step, oldest first
@@ -137,10 +139,10 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_fwd_kernel(ConvParams p)
         const int t = L - H + lane;
         float s = 0.0f;
         if (t >= 0)
-            s = Elem<T>::load1(xr + t);
+            s = Elem<T>::load1(xr + MSEL_IDX(t, L));
         else if (st != nullptr)
-            s = Elem<T>::load1(st + H + t);
-        Elem<T>::store1(static_cast<T*>(p.state_out) + sg.row * H + lane, s);
+            s = Elem<T>::load1(st + H + (MSEL_IDX(H + t, H) - H));
+        Elem<T>::store1(static_cast<T*>(p.state_out) + sg.row * H + MSEL_IDX(lane, H), s);
     }
 }
 
@@ -166,7 +168,8 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_bwd_kernel(ConvParams p)
     load_raw<T, K, VEC>(gr, t0, L, cg);
     float wk[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) wk[i] = p.w[static_cast<size_t>(sg.d) * W + i];
+    for (int i = 0; i < W; ++i)
+        wk[i] = p.w[MSEL_IDX(static_cast<size_t>(sg.d) * W + i, static_cast<size_t>(p.D) * W)];
     const float b = p.bias != nullptr ? p.bias[sg.d] : 0.0f;
     float halo[HA];
 #pragma unroll
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_bwd_kernel(ConvParams p)
                     float acc = 0.0f;
 #pragma unroll
                     for (int m = 0; m <= j; ++m) acc = fmaf(wk[j - m], d0[m], acc);
-                    p.dstate[sg.row * H + j] = acc;
+                    p.dstate[sg.row * H + MSEL_IDX(j, H)] = acc;
                 }
             }
         }
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_bwd_kernel(ConvParams p)
 #pragma unroll
         for (int q = 0; q < W; ++q)
             if (lane == q && p.dw != nullptr) {
-                dst = p.dw + static_cast<size_t>(sg.d) * W + q;
+                dst = p.dw + MSEL_IDX(static_cast<size_t>(sg.d) * W + q, static_cast<size_t>(p.D) * W);
                 val = tot[q];
             }
         if (lane == 63 && p.dbias != nullptr) {
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(256) void conv_step_kernel(ConvParams p) {
     constexpr int H = W - 1;
     const int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (row >= p.rows) return;
-    const int d = static_cast<int>(row % p.D);
+    const int d = MSEL_IDX(static_cast<int>(row % p.D), p.D);
     const T* st = (H > 0 && p.state_in != nullptr)
                       ? static_cast<const T*>(p.state_in) + row * H : nullptr;
     float win[W];  // [state, x]
@@ -308,7 +311,9 @@ __global__ __launch_bounds__(256) void conv_step_kernel(ConvParams p) {
     win[H] = Elem<T>::load1(static_cast<const T*>(p.x) + row);
     float pre = p.bias != nullptr ? p.bias[d] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < W; ++i) pre = fmaf(p.w[static_cast<size_t>(d) * W + i], win[i], pre);
+    for (int i = 0; i < W; ++i)
+        pre = fmaf(p.w[MSEL_IDX(static_cast<size_t>(d) * W + i, static_cast<size_t>(p.D) * W)],
+                   win[i], pre);
     Elem<T>::store1(static_cast<T*>(p.out) + row, SILU ? pre * sigmoid_f(pre) : pre);
     if (H > 0 && p.state_out != nullptr) {
         T* so = static_cast<T*>(p.state_out) + row * H;
@@ -390,5 +395,7 @@ hipError_t launch_conv_fwd(const ConvParams& p, bool bf16, hipStream_t stream) {
 hipError_t launch_conv_bwd(const ConvParams& p, bool bf16, hipStream_t stream) {
     return bf16 ? conv_dispatch<bf16_t>(p, true, stream) : conv_dispatch<float>(p, true, stream);
 }
+
+MSEL_BOUNDS_TAKER(take_bounds_conv)
 
 }  // namespace msel

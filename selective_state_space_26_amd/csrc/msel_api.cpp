@@ -580,6 +580,46 @@ msel_status msel_ring_timeouts(unsigned long long* count) {
 
 void msel_set_ring_spin_limit(uint32_t polls) { msel::set_ring_spin_limit(polls); }
 
+int msel_checked_build(void) {
+#ifdef MSEL_CHECKED
+    return 1;
+#else
+    return 0;
+#endif
+}
+
+msel_status msel_bound_violations(unsigned long long* count, uint32_t* file, uint32_t* line) {
+    if (count == nullptr || file == nullptr || line == nullptr) return MSEL_ERR_NULL;
+    *count = 0;
+    *file = 0;
+    *line = 0;
+    if (hipDeviceSynchronize() != hipSuccess) return MSEL_ERR_HIP;
+    using Taker = hipError_t (*)(msel::BoundsRecord*);
+    // in the order of the file numbers of msel.h
+    const Taker takers[] = {msel::take_bounds_fwd,  msel::take_bounds_chunk_carry,
+                            msel::take_bounds_bwd,  msel::take_bounds_conv,
+                            msel::take_bounds_cplx, msel::take_bounds_cplx_bwd};
+    msel_status s = MSEL_OK;
+    for (uint32_t i = 0; i < sizeof(takers) / sizeof(takers[0]); ++i) {
+        msel::BoundsRecord r{};
+        if (takers[i](&r) != hipSuccess) {
+            s = MSEL_ERR_HIP;  // the other records are still read and cleared
+            continue;
+        }
+        if (r.count != 0 && *count == 0) {
+            *file = i + 1;
+            *line = r.line;
+        }
+        *count += r.count;
+    }
+    return s;
+}
+
+msel_status msel_bounds_selftest(hipStream_t stream) {
+    if (!msel_checked_build()) return MSEL_ERR_UNSUPPORTED;
+    return msel::launch_bounds_selftest(1, stream) == hipSuccess ? MSEL_OK : MSEL_ERR_HIP;
+}
+
 msel_status msel_scan_bwd_noalloc(const msel_scan_args* a, const msel_scan_grads* g,
                                   hipStream_t stream) {
     msel_status s = check_bwd(a, g);

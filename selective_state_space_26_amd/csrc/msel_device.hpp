@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "msel_kernels.hpp"
+
 namespace msel {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -35,6 +37,47 @@ __device__ __forceinline__ float softplus_f(float x) {
     float l = (w == 1.0f) ? e : log2_hw(w) * kLn2 * (e * rcp_hw(w - 1.0f));
     return fmaxf(x, 0.0f) + l;
 }
+
+// ---------------------------------------------------------------------------------------
+// Bounds checks of the checked build.  Built with -DMSEL_CHECKED (libmsel_checked.so), every
+// index that a kernel forms into a global buffer or an LDS array goes through MSEL_IDX(i, n),
+// n being the extent of what it indexes (for a row, the number of rows).  An index outside
+// [0, n) is counted in its source file's device record (with the source line of the first one),
+// which the host reads and clears, and is replaced by 0: the access then stays inside the
+// buffer and the kernel ends normally, so a failed check never traps, faults or hangs.
+// Without MSEL_CHECKED, MSEL_IDX(i, n) is i, and MSEL_BOUNDS_TAKER defines a reader of an
+// empty record.  Row accesses through buffer resources are range-checked by the hardware
+// within the row; their row index is what MSEL_IDX checks.
+#ifdef MSEL_CHECKED
+static __device__ BoundsRecord g_bounds;  // one per source file
+
+template <typename I>
+__device__ __forceinline__ I checked_index(I i, unsigned long long n, unsigned int line) {
+    if (static_cast<long long>(i) >= 0 && static_cast<unsigned long long>(i) < n) return i;
+    if (__hip_atomic_fetch_add(&g_bounds.count, 1ull, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) == 0)
+        __hip_atomic_store(&g_bounds.line, line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return I(0);
+}
+#define MSEL_IDX(i, n) ::msel::checked_index((i), static_cast<unsigned long long>(n), __LINE__)
+#define MSEL_BOUNDS_TAKER(fn)                                                                  \
+    hipError_t fn(::msel::BoundsRecord* out) {                                                 \
+        const ::msel::BoundsRecord zero{};                                                     \
+        hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(::msel::g_bounds), sizeof(*out), 0, \
+                                           hipMemcpyDeviceToHost);                             \
+        if (e == hipSuccess)                                                                   \
+            e = hipMemcpyToSymbol(HIP_SYMBOL(::msel::g_bounds), &zero, sizeof(zero), 0,        \
+                                  hipMemcpyHostToDevice);                                      \
+        return e;                                                                              \
+    }
+#else
+#define MSEL_IDX(i, n) (i)
+#define MSEL_BOUNDS_TAKER(fn)                      \
+    hipError_t fn(::msel::BoundsRecord* out) {     \
+        *out = ::msel::BoundsRecord{};             \
+        return hipSuccess;                         \
+    }
+#endif
 
 __device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
 
@@ -290,7 +333,7 @@ struct TileStage {
             const int l = tl / K, q0 = (tl - l * K) / 4;
 #pragma unroll
             for (int j = 0; j < VW / 4; ++j)
-                buf[(x * QW + q0 + j) * kLine + l] =
+                buf[MSEL_IDX((x * QW + q0 + j) * kLine + l, kWords)] =
                     f32x4{f[4 * j], f[4 * j + 1], f[4 * j + 2], f[4 * j + 3]};
         }
     }
@@ -298,7 +341,7 @@ struct TileStage {
                                                 float (&r)[K]) {
 #pragma unroll
         for (int q = 0; q < QW; ++q) {
-            const f32x4 w4 = buf[(x * QW + q) * kLine + lane];
+            const f32x4 w4 = buf[MSEL_IDX((x * QW + q) * kLine + lane, kWords)];
             r[4 * q] = w4[0];
             r[4 * q + 1] = w4[1];
             r[4 * q + 2] = w4[2];

@@ -95,6 +95,24 @@ void set_ring_spin_limit(unsigned polls);  // 0: the default
 hipError_t take_ring_timeouts_bwd(unsigned long long* count);
 hipError_t take_ring_timeouts_cplx(unsigned long long* count);
 
+// Out-of-range indexes met by the kernels of the checked build (MSEL_IDX in msel_device.hpp),
+// one record per source file; each take_bounds_* reads its file's record and clears it (the
+// release build's records are always empty).
+struct BoundsRecord {
+    unsigned long long count;  // indexes out of range since the last read
+    unsigned int line;         // source line of the first one
+    unsigned int pad;
+};
+hipError_t take_bounds_fwd(BoundsRecord* r);
+hipError_t take_bounds_chunk_carry(BoundsRecord* r);
+hipError_t take_bounds_bwd(BoundsRecord* r);
+hipError_t take_bounds_conv(BoundsRecord* r);
+hipError_t take_bounds_cplx(BoundsRecord* r);
+hipError_t take_bounds_cplx_bwd(BoundsRecord* r);
+// Checked build: one kernel that forms index i of a one-element array (out of range unless
+// i == 0).  The release build returns hipErrorNotSupported and launches nothing.
+hipError_t launch_bounds_selftest(int i, hipStream_t stream);
+
 // All launchers enqueue on `stream` and return the hipGetLastError() after the launch.
 hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, hipStream_t stream);
 // The chunk-carry pass: the plain rule, the exponential-trapezoidal rule when p.lam is set, or

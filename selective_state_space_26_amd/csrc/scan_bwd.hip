@@ -118,8 +118,11 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
     const int L = p.L;
     const int N = p.N;
     const int t0 = c * kChunk + lane * K;
-    const T* __restrict__ Bg = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
-    const T* __restrict__ Cg = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
+    const T* __restrict__ Bg =
+        static_cast<const T*>(p.Bm) + static_cast<size_t>(MSEL_IDX(b, p.B)) * N * L;
+    const T* __restrict__ Cg =
+        static_cast<const T*>(p.Cm) + static_cast<size_t>(MSEL_IDX(b, p.B)) * N * L;
+    [[maybe_unused]] const size_t BD = static_cast<size_t>(p.B) * p.D;
 
     // A slot past the last channel repeats channel D-1 exactly, so its results equal that
     // channel's and may be stored over them: every store is then unconditional, which keeps
@@ -135,12 +138,13 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
     for (int r = 0; r < R; ++r) {
         const int d = dg * R + r;
         dch[r] = d < p.D ? d : p.D - 1;
-        const size_t row = (static_cast<size_t>(b) * p.D + dch[r]) * L;
+        const size_t row = MSEL_IDX(static_cast<size_t>(b) * p.D + dch[r], BD) * L;
         load_raw<T, K, VEC>(static_cast<const T*>(p.delta) + row, t0, L, rd[r]);
         load_raw<T, K, VEC>(static_cast<const T*>(g.dout) + row, t0, L, rg[r]);
         if constexpr (HAS_Z) load_raw<T, K, VEC>(static_cast<const T*>(p.z) + row, t0, L, rz[r]);
         if constexpr (FWD) load_raw<T, K, VEC>(static_cast<const T*>(p.u) + row, t0, L, ru[r]);
-        const float a_ = p.A[static_cast<size_t>(dch[r]) * N + (lane < N ? lane : N - 1)];
+        const float a_ = p.A[MSEL_IDX(static_cast<size_t>(dch[r]) * N + (lane < N ? lane : N - 1),
+                                      static_cast<size_t>(p.D) * N)];
         Av[r] = (lane < N) ? a_ * kLog2e : 0.0f;
     }
     // E_t and F'_t are each summed from the steps they cover (the chunk's first step left
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
     float tot[R], fst[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const float bias = p.bias ? p.bias[dch[r]] : 0.0f;
+        const float bias = p.bias ? p.bias[MSEL_IDX(dch[r], p.D)] : 0.0f;
         float dd[K], gg[K], dt[K];
         unpack(rd[r], dd);
         unpack(rg[r], gg);
@@ -190,7 +194,8 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
     if (lane == 0) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const size_t slot = (static_cast<size_t>(b) * p.D + dch[r]) * nch + c;
+            const size_t slot = MSEL_IDX((static_cast<size_t>(b) * p.D + dch[r]) * nch + c,
+                                         BD * nch);
             w.sdt[slot] = tot[r];
             w.dfirst[slot] = fst[r];
         }
@@ -208,8 +213,9 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
         unpack(Cn, cv);
         {  // the next state's rows (the last state fetches its own again: no branch)
             const int nn = (n + 1 < N) ? n + 1 : n;
-            if constexpr (FWD) load_raw<T, K, VEC>(Bg + static_cast<size_t>(nn) * L, t0, L, Bn);
-            load_raw<T, K, VEC>(Cg + static_cast<size_t>(nn) * L, t0, L, Cn);
+            if constexpr (FWD)
+                load_raw<T, K, VEC>(Bg + static_cast<size_t>(MSEL_IDX(nn, N)) * L, t0, L, Bn);
+            load_raw<T, K, VEC>(Cg + static_cast<size_t>(MSEL_IDX(nn, N)) * L, t0, L, Cn);
         }
         float acc[4];
 #pragma unroll
@@ -234,7 +240,8 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_kernel(ScanParams 
     if (lane < N) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const size_t slot = ((static_cast<size_t>(b) * p.D + dch[r]) * nch + c) * N + lane;
+            const size_t slot = MSEL_IDX(
+                ((static_cast<size_t>(b) * p.D + dch[r]) * nch + c) * N + lane, BD * nch * N);
             w.G[slot] = Gv[r];
             if constexpr (FWD) w.H[slot] = Hv[r];
         }
@@ -253,26 +260,31 @@ __global__ __launch_bounds__(256) void bwd_link_kernel(ScanParams p, GradParams 
     const int n = static_cast<int>(tid - static_cast<size_t>(ch) * N);
     const int d = ch % p.D;
     const int nch = p.nchunks;
-    const float A2 = p.A[static_cast<size_t>(d) * N + n] * kLog2e;
+    [[maybe_unused]] const size_t BDN = static_cast<size_t>(p.B) * p.D * N;
+    [[maybe_unused]] const size_t BDC = static_cast<size_t>(p.B) * p.D * nch;
+    const float A2 = p.A[MSEL_IDX(static_cast<size_t>(d) * N + n, static_cast<size_t>(p.D) * N)] *
+                     kLog2e;
     const size_t base = static_cast<size_t>(ch) * nch;
     if (FWD) {
-        float H = p.h0 ? p.h0[static_cast<size_t>(ch) * N + n] : 0.0f;
+        float H = p.h0 ? p.h0[MSEL_IDX(static_cast<size_t>(ch) * N + n, BDN)] : 0.0f;
         for (int c = 0; c < nch; ++c) {
-            float* slot = w.H + (base + c) * N + n;
+            float* slot = w.H + MSEL_IDX((base + c) * N + n, BDC * N);
             const float S = *slot;
             *slot = H;
-            H = fmaf(exp2_hw(A2 * w.sdt[base + c]), H, S);
+            H = fmaf(exp2_hw(A2 * w.sdt[MSEL_IDX(base + c, BDC)]), H, S);
         }
     }
     float G = 0.0f;
     for (int c = nch - 1; c >= w.c0; --c) {
-        float* slot = w.G + (base + c) * N + n;
+        float* slot = w.G + MSEL_IDX((base + c) * N + n, BDC * N);
         const float Sr = *slot;
         *slot = G;
-        G = fmaf(exp2_hw(A2 * w.sdt[base + c]), G, exp2_hw(A2 * w.dfirst[base + c]) * Sr);
+        G = fmaf(exp2_hw(A2 * w.sdt[MSEL_IDX(base + c, BDC)]), G,
+                 exp2_hw(A2 * w.dfirst[MSEL_IDX(base + c, BDC)]) * Sr);
     }
-    if (w.c0 > 0) w.G[base * N + n] = G;  // the carry after chunk 0 (no summary of its own)
-    if (g.dh0 != nullptr) g.dh0[static_cast<size_t>(ch) * N + n] = G;
+    // the carry after chunk 0 (no summary of its own)
+    if (w.c0 > 0) w.G[MSEL_IDX(base * N + n, BDC * N)] = G;
+    if (g.dh0 != nullptr) g.dh0[MSEL_IDX(static_cast<size_t>(ch) * N + n, BDN)] = G;
 }
 
 // LDS layout of the main kernel:
@@ -354,12 +366,16 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     float* dAs = BCs + 2 * N * kChunk + wave * N * kDaQuads;  // this wave's dA partials
     float* Bm1 = BCs + 2 * N * kChunk + W * N * kDaQuads;     // TRAP: B at step c*T - 1
     __shared__ int ring_flags[kMaxRingFlags];
+    [[maybe_unused]] const size_t BD = static_cast<size_t>(p.B) * p.D;
+    [[maybe_unused]] const size_t DN = static_cast<size_t>(p.D) * N;
     for (int i = tid; i < 2 * groups * tile; i += 64 * W) acc[i] = 0.0f;
-    for (int i = tid; i < groups * N; i += 64 * W) ring_flags[i] = 0;
+    for (int i = tid; i < groups * N; i += 64 * W) ring_flags[MSEL_IDX(i, kMaxRingFlags)] = 0;
     {
         // B and C of this (batch row, chunk), read once per workgroup, zero past the end
-        const T* __restrict__ Bg = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
-        const T* __restrict__ Cg = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
+        const T* __restrict__ Bg =
+            static_cast<const T*>(p.Bm) + static_cast<size_t>(MSEL_IDX(b, p.B)) * N * L;
+        const T* __restrict__ Cg =
+            static_cast<const T*>(p.Cm) + static_cast<size_t>(MSEL_IDX(b, p.B)) * N * L;
         for (int i = tid; i < N * kChunk; i += 64 * W) {
             const int nn = i / kChunk;
             const int tl = i - nn * kChunk;
@@ -369,7 +385,8 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 vb = Elem<T>::load1(Bg + static_cast<size_t>(nn) * L + t);
                 vc = Elem<T>::load1(Cg + static_cast<size_t>(nn) * L + t);
             }
-            const int o = ((nn * 2 + (tl % K) / 4) * 64 + tl / K) * 4 + tl % 4;
+            const int o = MSEL_IDX(((nn * 2 + (tl % K) / 4) * 64 + tl / K) * 4 + tl % 4,
+                                   N * kChunk);
             BCs[o] = vb;
             BCs[N * kChunk + o] = vc;
         }
@@ -379,8 +396,10 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 if (c > 0)
                     v = Elem<T>::load1(Bg + static_cast<size_t>(tid) * L + c * kChunk - 1);
                 else if (p.B_prev != nullptr)
-                    v = Elem<T>::load1(static_cast<const T*>(p.B_prev) + static_cast<size_t>(b) * N + tid);
-                Bm1[tid] = v;
+                    v = Elem<T>::load1(static_cast<const T*>(p.B_prev) +
+                                       MSEL_IDX(static_cast<size_t>(b) * N + tid,
+                                                static_cast<size_t>(p.B) * N));
+                Bm1[MSEL_IDX(tid, kMaxN)] = v;
             }
         }
     }
@@ -399,7 +418,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     const int rot = wave - grp * N;
     const int Wg = (W - grp * N < N) ? W - grp * N : N;  // waves sharing this group's rows
     const int kp = (rot + 1 < Wg) ? 1 : N - rot;
-    int* gflags = ring_flags + grp * N;
+    int* gflags = ring_flags + MSEL_IDX(grp * N, kMaxRingFlags);
     int gstep = 0;
     float* myB = accB + grp * tile;
     float* myC = accC + grp * tile;
@@ -413,7 +432,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     const T* __restrict__ gg_ = static_cast<const T*>(g.dout);
     const T* __restrict__ gz = static_cast<const T*>(p.z);
     const T* __restrict__ gl = static_cast<const T*>(p.lam);
-    auto chan_row = [&](int d) { return (static_cast<size_t>(b) * p.D + d) * L; };
+    auto chan_row = [&](int d) { return MSEL_IDX(static_cast<size_t>(b) * p.D + d, BD) * L; };
 
     // raw input rows of the channel about to start, fetched ahead of time
     Raw<T, K> ru, rd, rg, rz;
@@ -433,16 +452,16 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
         const bool active = d < p.D;  // wave-uniform; inactive waves still run the protocol
         const bool next_active = (r + 1 < per_wave) && (d + W < p.D);
         const int dd_ = active ? d : 0;
-        const size_t ch = static_cast<size_t>(b) * p.D + dd_;
+        const size_t ch = MSEL_IDX(static_cast<size_t>(b) * p.D + dd_, BD);
         const size_t row = ch * L;
         const size_t row_next = chan_row(next_active ? d + W : 0);
-        const float bias = p.bias ? p.bias[dd_] : 0.0f;
-        const float Dd = p.Dv ? p.Dv[dd_] : 0.0f;
+        const float bias = p.bias ? p.bias[MSEL_IDX(dd_, p.D)] : 0.0f;
+        const float Dd = p.Dv ? p.Dv[MSEL_IDX(dd_, p.D)] : 0.0f;
         // per-channel rows of A, H_c and G_c, one value per lane (lane n holds state n)
         const size_t hg = (ch * nch + c) * N;
-        const float Av = (lane < N) ? p.A[static_cast<size_t>(dd_) * N + lane] : 0.0f;
-        const float Hv = (lane < N) ? w.H[hg + lane] : 0.0f;
-        const float Gv = (lane < N) ? w.G[hg + lane] : 0.0f;
+        const float Av = (lane < N) ? p.A[MSEL_IDX(static_cast<size_t>(dd_) * N + lane, DN)] : 0.0f;
+        const float Hv = (lane < N) ? w.H[MSEL_IDX(hg + lane, BD * nch * N)] : 0.0f;
+        const float Gv = (lane < N) ? w.G[MSEL_IDX(hg + lane, BD * nch * N)] : 0.0f;
 
         int n = rot;  // state of step 0
 
@@ -521,8 +540,10 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
             const int nc = n;
             float bv[K], cv[K];
             {
-                const f32x4 b0 = B4[(nc * 2) * 64 + lane], b1 = B4[(nc * 2 + 1) * 64 + lane];
-                const f32x4 c0 = C4[(nc * 2) * 64 + lane], c1 = C4[(nc * 2 + 1) * 64 + lane];
+                const f32x4 b0 = B4[MSEL_IDX((nc * 2) * 64 + lane, N * kChunk / 4)],
+                            b1 = B4[MSEL_IDX((nc * 2 + 1) * 64 + lane, N * kChunk / 4)];
+                const f32x4 c0 = C4[MSEL_IDX((nc * 2) * 64 + lane, N * kChunk / 4)],
+                            c1 = C4[MSEL_IDX((nc * 2 + 1) * 64 + lane, N * kChunk / 4)];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     bv[q] = b0[q];
@@ -553,7 +574,8 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
             if (need > 0) {
                 unsigned polls = 0;
                 while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                           gflags + nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < need) {
+                           gflags + MSEL_IDX(nc, kMaxRingFlags - grp * N), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP)) < need) {
                     if (++polls >= w.spin_limit) {  // give up: counted, never a hang
                         if (lane == 0)
                             __hip_atomic_fetch_add(&g_ring_timeouts_bwd, 1ull, __ATOMIC_RELAXED,
@@ -567,8 +589,10 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
             if (active) {
                 // this step's accumulator slots: each tensor's reads are issued together,
                 // ahead of their use, and written back as soon as its pass is done
-                float* sBn = myB + nc * K * KP + lane;
-                float* sCn = myC + nc * K * KP + lane;
+                // rows k = 0 .. K-1 of this step are sBn[k * KP] (the base's extent leaves
+                // room for them and the 64 lanes)
+                float* sBn = myB + MSEL_IDX(nc * K * KP, tile - (K - 1) * KP - 63) + lane;
+                float* sCn = myC + MSEL_IDX(nc * K * KP, tile - (K - 1) * KP - 63) + lane;
                 float oc[K];
 #pragma unroll
                 for (int k = 0; k < K; ++k) oc[k] = sCn[k * KP];
@@ -670,15 +694,17 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 // channels (the B_prev term of h_0)
                 if constexpr (TRAP) {
                     if (c == 0 && lane == 0 && g.dB_prev != nullptr)
-                        unsafeAtomicAdd(g.dB_prev + static_cast<size_t>(b) * N + nc, first_lac);
+                        unsafeAtomicAdd(g.dB_prev + MSEL_IDX(static_cast<size_t>(b) * N + nc,
+                                                             static_cast<size_t>(p.B) * N),
+                                        first_lac);
                 }
                 const float dq = quad_sum(dA_part);
-                if ((lane & 3) == 0) dAs[nc * kDaQuads + (lane >> 2)] = dq;
+                if ((lane & 3) == 0) dAs[MSEL_IDX(nc * kDaQuads + (lane >> 2), N * kDaQuads)] = dq;
             }
             // publish: this step's LDS writes are complete
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __hip_atomic_store(gflags + nc, gstep + 1, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(gflags + MSEL_IDX(nc, kMaxRingFlags - grp * N), gstep + 1,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             ++gstep;
         };
 
@@ -742,7 +768,8 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
         // LDS order, no barrier needed)
         float sa = 0.0f;
         if (lane < N) {
-            const f32x4* src = reinterpret_cast<const f32x4*>(dAs + lane * kDaQuads);
+            const f32x4* src =
+                reinterpret_cast<const f32x4*>(dAs + MSEL_IDX(lane * kDaQuads, N * kDaQuads));
 #pragma unroll
             for (int q = 0; q < kDaQuads / 4; ++q) {
                 const f32x4 v = src[q];
@@ -755,13 +782,13 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
         float* dst = nullptr;
         float val = 0.0f;
         if (lane < N) {
-            dst = g.dA ? g.dA + static_cast<size_t>(d) * N + lane : nullptr;
+            dst = g.dA ? g.dA + MSEL_IDX(static_cast<size_t>(d) * N + lane, DN) : nullptr;
             val = sa;
         } else if (lane == 62) {
-            dst = g.dD ? g.dD + d : nullptr;
+            dst = g.dD ? g.dD + MSEL_IDX(d, p.D) : nullptr;
             val = sD;
         } else if (lane == 63) {
-            dst = g.dbias ? g.dbias + d : nullptr;
+            dst = g.dbias ? g.dbias + MSEL_IDX(d, p.D) : nullptr;
             val = sb;
         }
         if (dst != nullptr) unsafeAtomicAdd(dst, val);
@@ -776,10 +803,11 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
         const int slot = (nn * K + tt % K) * KP + tt / K;
         float vb = 0.0f, vc = 0.0f;
         for (int q = 0; q < groups; ++q) {
-            vb += accB[q * tile + slot];
-            vc += accC[q * tile + slot];
+            vb += accB[MSEL_IDX(q * tile + slot, groups * tile)];
+            vc += accC[MSEL_IDX(q * tile + slot, groups * tile)];
         }
-        const size_t o = (static_cast<size_t>(b) * N + nn) * L + t;
+        const size_t o =
+            MSEL_IDX((static_cast<size_t>(b) * N + nn) * L + t, static_cast<size_t>(p.B) * N * L);
         if (g.dB != nullptr) unsafeAtomicAdd(g.dB + o, vb);
         if (g.dC != nullptr) unsafeAtomicAdd(g.dC + o, vc);
     }
@@ -934,5 +962,7 @@ hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float
     if (bf16) return bwd_dispatch<bf16_t>(p, g, w, stream, tm);
     return bwd_dispatch<float>(p, g, w, stream, tm);
 }
+
+MSEL_BOUNDS_TAKER(take_bounds_bwd)
 
 }  // namespace msel

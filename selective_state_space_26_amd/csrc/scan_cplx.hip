@@ -42,10 +42,11 @@ __global__ __launch_bounds__(256) void scan_cplx_fwd_kernel(ScanParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ch = blockIdx.x * (blockDim.x >> 6) + wave;  // b * D + d
     if (ch >= p.B * p.D) return;  // whole wavefront leaves; no barriers here
-    const int b = ch / p.D;
+    const int b = MSEL_IDX(ch / p.D, p.B);
     const int d = ch - b * p.D;
     const int L = p.L;
     const int N = p.N;  // even: N / 2 complex states
+    [[maybe_unused]] const size_t BDN = static_cast<size_t>(p.B) * p.D * N;
     const size_t row = static_cast<size_t>(ch) * L;
     const T* __restrict__ u = static_cast<const T*>(p.u) + row;
     const T* __restrict__ dl = static_cast<const T*>(p.delta) + row;
@@ -53,16 +54,16 @@ __global__ __launch_bounds__(256) void scan_cplx_fwd_kernel(ScanParams p) {
     T* __restrict__ out = static_cast<T*>(p.out) + row;
     const T* __restrict__ Bb = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
     const T* __restrict__ Cb = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
-    const float bias = p.bias ? p.bias[d] : 0.0f;
-    const float Dd = p.Dv ? p.Dv[d] : 0.0f;
+    const float bias = p.bias ? p.bias[MSEL_IDX(d, p.D)] : 0.0f;
+    const float Dd = p.Dv ? p.Dv[MSEL_IDX(d, p.D)] : 0.0f;
     // lane 2j: A_re * log2(e) (for exp2), lane 2j+1: A_im / (2 pi) (revolutions)
     float Av = 0.0f;
     if (lane < N) {
-        const float a = p.A[static_cast<size_t>(d) * N + lane];
+        const float a = p.A[MSEL_IDX(static_cast<size_t>(d) * N + lane, static_cast<size_t>(p.D) * N)];
         Av = (lane & 1) ? a * kInv2Pi : a * kLog2e;
     }
     float carry = 0.0f;  // lane n: component n of the state entering the tile
-    if (p.h0 != nullptr && lane < N) carry = p.h0[static_cast<size_t>(ch) * N + lane];
+    if (p.h0 != nullptr && lane < N) carry = p.h0[MSEL_IDX(static_cast<size_t>(ch) * N + lane, BDN)];
 
     constexpr int TILE = 64 * K;
     static_assert(TILE % kChunk == 0, "a tile must hold whole chunks");
@@ -92,8 +93,8 @@ __global__ __launch_bounds__(256) void scan_cplx_fwd_kernel(ScanParams p) {
         for (int n = 0; n < N; n += 2) {
             const float Ar = readlane(Av, n), Ai = readlane(Av, n + 1);
             float ar[K], ai[K], p1[K], p2[K];
-            load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, p1);
-            load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n + 1) * L, t0, L, p2);
+            load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(n, N)) * L, t0, L, p1);
+            load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(n + 1, N)) * L, t0, L, p2);
             float h1 = 0.0f, h2 = 0.0f;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
@@ -125,8 +126,8 @@ __global__ __launch_bounds__(256) void scan_cplx_fwd_kernel(ScanParams p) {
             }
 
             float c1[K], c2[K];
-            load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n) * L, t0, L, c1);
-            load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n + 1) * L, t0, L, c2);
+            load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(MSEL_IDX(n, N)) * L, t0, L, c1);
+            load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(MSEL_IDX(n + 1, N)) * L, t0, L, c2);
             h1 = hr;
             h2 = hi;
 #pragma unroll
@@ -149,13 +150,13 @@ __global__ __launch_bounds__(256) void scan_cplx_fwd_kernel(ScanParams p) {
             for (int q = 0; q < kCpt; ++q) {
                 const int cidx = tile / kChunk + q;
                 if (cidx < p.nchunks)
-                    p.chunk_states[(static_cast<size_t>(ch) * p.nchunks + cidx) * N + lane] =
-                        csv[q];
+                    p.chunk_states[MSEL_IDX((static_cast<size_t>(ch) * p.nchunks + cidx) * N + lane,
+                                            BDN * p.nchunks)] = csv[q];
             }
         }
     }
     if (p.final_state != nullptr && lane < N)
-        p.final_state[static_cast<size_t>(ch) * N + lane] = carry;
+        p.final_state[MSEL_IDX(static_cast<size_t>(ch) * N + lane, BDN)] = carry;
 }
 
 // The recurrent (decode) step: a 16-lane row per channel, lane n for state component n.  Each
@@ -168,27 +169,33 @@ __global__ __launch_bounds__(256) void scan_cplx_step_kernel(ScanParams p) {
     // b * D + d, formed in 64 bits: 16 * batch * dim threads may pass 2^32
     const long long ch =
         (static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x) >> 4;
-    const bool in = ch < static_cast<long long>(p.B) * p.D;
-    const int chc = in ? static_cast<int>(ch) : 0;
+    const long long BD = static_cast<long long>(p.B) * p.D;
+    const bool in = ch < BD;
+    const int chc = MSEL_IDX(in ? static_cast<int>(ch) : 0, BD);
     const int b = chc / p.D;
     const int d = chc - b * p.D;
     const int N = p.N;
     const bool st = in && n < N;
     const int ne = (n < N ? n : N - 1) & ~1;  // the pair's real component
+    [[maybe_unused]] const size_t BN = static_cast<size_t>(p.B) * N;
+    [[maybe_unused]] const size_t BDN = static_cast<size_t>(BD) * N;
     const float u = Elem<T>::load1(static_cast<const T*>(p.u) + chc);
-    const float x = Elem<T>::load1(static_cast<const T*>(p.delta) + chc) + (p.bias ? p.bias[d] : 0.0f);
+    const float x = Elem<T>::load1(static_cast<const T*>(p.delta) + chc) +
+                    (p.bias ? p.bias[MSEL_IDX(d, p.D)] : 0.0f);
     const float dt = SOFTPLUS ? softplus_f(x) : x;
     const size_t bn = static_cast<size_t>(b) * N + ne;  // B and C are [batch, dstate, 1]
-    const float Br = Elem<T>::load1(static_cast<const T*>(p.Bm) + bn);
-    const float Bi = Elem<T>::load1(static_cast<const T*>(p.Bm) + bn + 1);
-    const float Cv = Elem<T>::load1(static_cast<const T*>(p.Cm) + bn + (n & 1));
-    const float* Ad = p.A + static_cast<size_t>(d) * N + ne;
+    // the pair's two components: bn and bn + 1
+    const float Br = Elem<T>::load1(static_cast<const T*>(p.Bm) + MSEL_IDX(bn, BN - 1));
+    const float Bi = Elem<T>::load1(static_cast<const T*>(p.Bm) + MSEL_IDX(bn, BN - 1) + 1);
+    const float Cv = Elem<T>::load1(static_cast<const T*>(p.Cm) + MSEL_IDX(bn, BN - 1) + (n & 1));
+    // the pair's A_re and A_im: Ad[0], Ad[1]
+    const float* Ad = p.A + static_cast<size_t>(MSEL_IDX(d, p.D)) * N + MSEL_IDX(ne, N - 1);
     const float e = exp2_hw(dt * Ad[0] * kLog2e);
     const float r = dt * Ad[1] * kInv2Pi;
     const float ar = e * cos_rev(r), ai = e * sin_rev(r);
     const size_t sidx = static_cast<size_t>(chc) * N + ne;
-    const float h0r = p.h0 ? p.h0[sidx] : 0.0f;
-    const float h0i = p.h0 ? p.h0[sidx + 1] : 0.0f;
+    const float h0r = p.h0 ? p.h0[MSEL_IDX(sidx, BDN)] : 0.0f;
+    const float h0i = p.h0 ? p.h0[MSEL_IDX(sidx + 1, BDN)] : 0.0f;
     const float h = (n & 1) ? fmaf(ai, h0r, fmaf(ar, h0i, dt * u * Bi))
                             : fmaf(ar, h0r, fmaf(-ai, h0i, dt * u * Br));
     float part = st ? Cv * h : 0.0f;
@@ -203,12 +210,12 @@ __global__ __launch_bounds__(256) void scan_cplx_step_kernel(ScanParams p) {
                  "v_add_f32_dpp %[v], %[v], %[v] row_shr:8 row_mask:0xf bank_mask:0xf\n"
                  : [v] "+v"(part));
     if (st) {
-        const size_t own = static_cast<size_t>(chc) * N + n;
+        const size_t own = MSEL_IDX(static_cast<size_t>(chc) * N + n, BDN);
         if (p.chunk_states != nullptr) p.chunk_states[own] = (n & 1) ? h0i : h0r;
         if (p.final_state != nullptr) p.final_state[own] = h;
     }
     if (in && n == 15) {
-        float yv = part + (p.Dv ? p.Dv[d] : 0.0f) * u;
+        float yv = part + (p.Dv ? p.Dv[MSEL_IDX(d, p.D)] : 0.0f) * u;
         if constexpr (HAS_Z) {
             const float z = Elem<T>::load1(static_cast<const T*>(p.z) + chc);
             yv *= z * sigmoid_f(z);
@@ -256,5 +263,7 @@ hipError_t cplx_dispatch(const ScanParams& p, hipStream_t s) {
 hipError_t launch_scan_cplx_fwd(const ScanParams& p, bool bf16, hipStream_t stream) {
     return bf16 ? cplx_dispatch<bf16_t>(p, stream) : cplx_dispatch<float>(p, stream);
 }
+
+MSEL_BOUNDS_TAKER(take_bounds_cplx)
 
 }  // namespace msel

@@ -66,10 +66,11 @@ __global__ __launch_bounds__(256) void cplx_summary_kernel(ScanParams p, GradPar
     const int c = w.c0 + static_cast<int>((unit / p.D) % nsum);
     const int b = static_cast<int>(unit / (static_cast<long long>(p.D) * nsum));
     const int L = p.L, N = p.N;
-    const size_t ch = static_cast<size_t>(b) * p.D + d;
+    [[maybe_unused]] const size_t BD = static_cast<size_t>(p.B) * p.D;
+    const size_t ch = MSEL_IDX(static_cast<size_t>(b) * p.D + d, BD);
     const size_t row = ch * L;
     const int t0 = c * kChunk + lane * K;
-    const float bias = p.bias ? p.bias[d] : 0.0f;
+    const float bias = p.bias ? p.bias[MSEL_IDX(d, p.D)] : 0.0f;
 
     float dt[K], dy[K];
     {
@@ -103,8 +104,9 @@ __global__ __launch_bounds__(256) void cplx_summary_kernel(ScanParams p, GradPar
 #pragma unroll
     for (int k = 0; k < K; ++k) E[k] += before;
 
-    const T* __restrict__ Cg = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
-    const float* Ad = p.A + static_cast<size_t>(d) * N;
+    const T* __restrict__ Cg =
+        static_cast<const T*>(p.Cm) + static_cast<size_t>(MSEL_IDX(b, p.B)) * N * L;
+    const float* Ad = p.A + static_cast<size_t>(MSEL_IDX(d, p.D)) * N;
     float outv = 0.0f;  // lane n: component n of the summary
     for (int n = 0; n < N; n += 4) {
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // (re, im) of pairs n/2 and n/2 + 1
@@ -112,10 +114,10 @@ __global__ __launch_bounds__(256) void cplx_summary_kernel(ScanParams p, GradPar
         for (int q = 0; q < 2; ++q) {
             const int m = n + 2 * q;
             if (m >= N) break;
-            const float Ar = Ad[m] * kLog2e, Ai = Ad[m + 1] * kInv2Pi;
+            const float Ar = Ad[MSEL_IDX(m, N)] * kLog2e, Ai = Ad[MSEL_IDX(m + 1, N)] * kInv2Pi;
             float cr[K], ci[K];
-            load_k_cached<T, K, VEC>(Cg + static_cast<size_t>(m) * L, t0, L, cr);
-            load_k_cached<T, K, VEC>(Cg + static_cast<size_t>(m + 1) * L, t0, L, ci);
+            load_k_cached<T, K, VEC>(Cg + static_cast<size_t>(MSEL_IDX(m, N)) * L, t0, L, cr);
+            load_k_cached<T, K, VEC>(Cg + static_cast<size_t>(MSEL_IDX(m + 1, N)) * L, t0, L, ci);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 // exp(conj(A) E) C dy
@@ -130,8 +132,8 @@ __global__ __launch_bounds__(256) void cplx_summary_kernel(ScanParams p, GradPar
         for (int q = 0; q < 4; ++q)
             if (n + q < N) outv = writelane(acc[q], n + q, outv);
     }
-    const size_t base = ch * nch + c;
-    if (lane < N) w.G[base * N + lane] = outv;
+    const size_t base = MSEL_IDX(ch * nch + c, BD * nch);
+    if (lane < N) w.G[MSEL_IDX(base * N + lane, BD * nch * N)] = outv;
     if (lane == 0) {
         w.sdt[base] = total;
         w.dfirst[base] = first;
@@ -152,12 +154,14 @@ __global__ __launch_bounds__(256) void cplx_link_kernel(ScanParams p, GradParams
     const int j = static_cast<int>(i - ch * J);
     const int d = static_cast<int>(ch % p.D);
     const int nch = p.nchunks;
-    const float Ar = p.A[static_cast<size_t>(d) * p.N + 2 * j] * kLog2e;
-    const float Ai = p.A[static_cast<size_t>(d) * p.N + 2 * j + 1] * kInv2Pi;
+    [[maybe_unused]] const size_t DN = static_cast<size_t>(p.D) * p.N;
+    [[maybe_unused]] const size_t BDC = static_cast<size_t>(p.B) * p.D * nch;
+    const float Ar = p.A[MSEL_IDX(static_cast<size_t>(d) * p.N + 2 * j, DN)] * kLog2e;
+    const float Ai = p.A[MSEL_IDX(static_cast<size_t>(d) * p.N + 2 * j + 1, DN)] * kInv2Pi;
     float Gr = 0.0f, Gi = 0.0f;
     for (int c = nch - 1; c >= w.c0; --c) {
-        const size_t base = static_cast<size_t>(ch) * nch + c;
-        float* slot = w.G + base * p.N + 2 * j;
+        const size_t base = MSEL_IDX(static_cast<size_t>(ch) * nch + c, BDC);
+        float* slot = w.G + base * p.N + MSEL_IDX(2 * j, p.N - 1);  // slot[0], slot[1]
         const float Sr = slot[0], Si = slot[1];
         slot[0] = Gr;
         slot[1] = Gi;
@@ -173,13 +177,13 @@ __global__ __launch_bounds__(256) void cplx_link_kernel(ScanParams p, GradParams
         Gi = ai + bi;
     }
     if (w.c0 > 0) {  // the carry after chunk 0 (no summary of its own)
-        float* slot = w.G + static_cast<size_t>(ch) * nch * p.N + 2 * j;
+        float* slot = w.G + static_cast<size_t>(ch) * nch * p.N + MSEL_IDX(2 * j, p.N - 1);
         slot[0] = Gr;
         slot[1] = Gi;
     }
     if (g.dh0 != nullptr) {
-        g.dh0[static_cast<size_t>(ch) * p.N + 2 * j] = Gr;
-        g.dh0[static_cast<size_t>(ch) * p.N + 2 * j + 1] = Gi;
+        g.dh0[static_cast<size_t>(ch) * p.N + MSEL_IDX(2 * j, p.N - 1)] = Gr;
+        g.dh0[static_cast<size_t>(ch) * p.N + MSEL_IDX(2 * j, p.N - 1) + 1] = Gi;
     }
 }
 
@@ -269,12 +273,16 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
     float* BCs = acc + 2 * groups * tile;                            // B rows, then C rows
     float* dAs = BCs + 2 * N * kChunk + wave * N * kRingQuads;     // this wave's dA partials
     for (int i = tid; i < 2 * groups * tile; i += 64 * W) acc[i] = 0.0f;
-    for (int i = tid; i < groups * J; i += 64 * W) ring_flags[i] = 0;
+    for (int i = tid; i < groups * J; i += 64 * W) ring_flags[MSEL_IDX(i, kMaxRingFlags)] = 0;
+    [[maybe_unused]] const size_t BD = static_cast<size_t>(p.B) * p.D;
+    [[maybe_unused]] const size_t DN = static_cast<size_t>(p.D) * N;
     {
         // B and C of this (batch row, chunk), read once per workgroup, zero past the end;
         // lane l's 8 steps of a row are two 16-byte vectors, consecutive lanes adjacent
-        const T* __restrict__ Bg = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
-        const T* __restrict__ Cg = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
+        const T* __restrict__ Bg =
+            static_cast<const T*>(p.Bm) + static_cast<size_t>(MSEL_IDX(b, p.B)) * N * L;
+        const T* __restrict__ Cg =
+            static_cast<const T*>(p.Cm) + static_cast<size_t>(MSEL_IDX(b, p.B)) * N * L;
         for (int i = tid; i < N * kChunk; i += 64 * W) {
             const int nn = i / kChunk;
             const int tl = i - nn * kChunk;
@@ -284,7 +292,8 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
                 vb = Elem<T>::load1(Bg + static_cast<size_t>(nn) * L + t);
                 vc = Elem<T>::load1(Cg + static_cast<size_t>(nn) * L + t);
             }
-            const int o = ((nn * 2 + (tl % K) / 4) * 64 + tl / K) * 4 + tl % 4;
+            const int o = MSEL_IDX(((nn * 2 + (tl % K) / 4) * 64 + tl / K) * 4 + tl % 4,
+                                   N * kChunk);
             BCs[o] = vb;
             BCs[N * kChunk + o] = vc;
         }
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
 
     const int grp = wave / J;
     const int rot = wave - grp * J;
-    int* gflags = ring_flags + grp * J;
+    int* gflags = ring_flags + MSEL_IDX(grp * J, kMaxRingFlags);
     int gstep = 0;
     float* myB = accB + grp * tile;
     float* myC = accC + grp * tile;
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
     const T* __restrict__ gd = static_cast<const T*>(p.delta);
     const T* __restrict__ gg_ = static_cast<const T*>(g.dout);
     const T* __restrict__ gz = static_cast<const T*>(p.z);
-    auto chan_row = [&](int d) { return (static_cast<size_t>(b) * p.D + d) * L; };
+    auto chan_row = [&](int d) { return MSEL_IDX(static_cast<size_t>(b) * p.D + d, BD) * L; };
 
     // raw input rows of the channel about to start, fetched ahead of time
     Raw<T, K> ru, rd, rg, rz;
@@ -323,16 +332,16 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
         const bool active = d < p.D;  // wave-uniform; inactive waves still run the protocol
         const bool next_active = (r + 1 < per_wave) && (d + W < p.D);
         const int dd_ = active ? d : 0;
-        const size_t ch = static_cast<size_t>(b) * p.D + dd_;
+        const size_t ch = MSEL_IDX(static_cast<size_t>(b) * p.D + dd_, BD);
         const size_t row = ch * L;
         const size_t row_next = chan_row(next_active ? d + W : 0);
-        const float bias = p.bias ? p.bias[dd_] : 0.0f;
-        const float Dd = p.Dv ? p.Dv[dd_] : 0.0f;
+        const float bias = p.bias ? p.bias[MSEL_IDX(dd_, p.D)] : 0.0f;
+        const float Dd = p.Dv ? p.Dv[MSEL_IDX(dd_, p.D)] : 0.0f;
         // per-channel rows of A, H_c and G_c, one component per lane ((Re, Im) interleaved)
         const size_t hg = (ch * nch + c) * N;
-        const float Av = (lane < N) ? p.A[static_cast<size_t>(dd_) * N + lane] : 0.0f;
-        const float Hv = (lane < N) ? w.H[hg + lane] : 0.0f;
-        const float Gv = (lane < N) ? w.G[hg + lane] : 0.0f;
+        const float Av = (lane < N) ? p.A[MSEL_IDX(static_cast<size_t>(dd_) * N + lane, DN)] : 0.0f;
+        const float Hv = (lane < N) ? w.H[MSEL_IDX(hg + lane, BD * nch * N)] : 0.0f;
+        const float Gv = (lane < N) ? w.G[MSEL_IDX(hg + lane, BD * nch * N)] : 0.0f;
 
         int jn = rot;  // pair of step 0
 
@@ -372,10 +381,15 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
             const int n0 = 2 * jc;
             float Br[K], Bi[K], Cr[K], Ci[K];
             {
-                const f32x4 b0 = B4[(n0 * 2) * 64 + lane], b1 = B4[(n0 * 2 + 1) * 64 + lane];
-                const f32x4 b2 = B4[(n0 * 2 + 2) * 64 + lane], b3 = B4[(n0 * 2 + 3) * 64 + lane];
-                const f32x4 c0 = C4[(n0 * 2) * 64 + lane], c1 = C4[(n0 * 2 + 1) * 64 + lane];
-                const f32x4 c2 = C4[(n0 * 2 + 2) * 64 + lane], c3 = C4[(n0 * 2 + 3) * 64 + lane];
+                [[maybe_unused]] const int NW = N * kChunk / 4;  // 16-byte words per tensor
+                const f32x4 b0 = B4[MSEL_IDX((n0 * 2) * 64 + lane, NW)],
+                            b1 = B4[MSEL_IDX((n0 * 2 + 1) * 64 + lane, NW)];
+                const f32x4 b2 = B4[MSEL_IDX((n0 * 2 + 2) * 64 + lane, NW)],
+                            b3 = B4[MSEL_IDX((n0 * 2 + 3) * 64 + lane, NW)];
+                const f32x4 c0 = C4[MSEL_IDX((n0 * 2) * 64 + lane, NW)],
+                            c1 = C4[MSEL_IDX((n0 * 2 + 1) * 64 + lane, NW)];
+                const f32x4 c2 = C4[MSEL_IDX((n0 * 2 + 2) * 64 + lane, NW)],
+                            c3 = C4[MSEL_IDX((n0 * 2 + 3) * 64 + lane, NW)];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     Br[q] = b0[q];
@@ -408,7 +422,8 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
             if (gstep > 0) {
                 unsigned polls = 0;
                 while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                           gflags + jc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < gstep) {
+                           gflags + MSEL_IDX(jc, kMaxRingFlags - grp * J), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP)) < gstep) {
                     if (++polls >= w.spin_limit) {  // give up: counted, never a hang
                         if (lane == 0)
                             __hip_atomic_fetch_add(&g_ring_timeouts_cplx, 1ull, __ATOMIC_RELAXED,
@@ -420,9 +435,11 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
             }
             asm volatile("" ::: "memory");
             if (active) {
-                float* sBr = myB + n0 * K * KP + lane;
+                // rows k of the pair's two components are sBr[k * KP], sBi[k * KP] (the
+                // base's extent leaves room for both and the 64 lanes)
+                float* sBr = myB + MSEL_IDX(n0 * K * KP, tile - (2 * K - 1) * KP - 63) + lane;
                 float* sBi = sBr + K * KP;
-                float* sCr = myC + n0 * K * KP + lane;
+                float* sCr = myC + MSEL_IDX(n0 * K * KP, tile - (2 * K - 1) * KP - 63) + lane;
                 float* sCi = sCr + K * KP;
                 float ocr[K], oci[K];
 #pragma unroll
@@ -557,14 +574,14 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
                 }
                 const float qr = quad_sum(dAr), qi = quad_sum(dAi);
                 if ((lane & 3) == 0) {
-                    dAs[n0 * kRingQuads + (lane >> 2)] = qr;
-                    dAs[(n0 + 1) * kRingQuads + (lane >> 2)] = qi;
+                    dAs[MSEL_IDX(n0 * kRingQuads + (lane >> 2), N * kRingQuads)] = qr;
+                    dAs[MSEL_IDX((n0 + 1) * kRingQuads + (lane >> 2), N * kRingQuads)] = qi;
                 }
             }
             // publish: this step's LDS writes are complete
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __hip_atomic_store(gflags + jc, gstep + 1, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(gflags + MSEL_IDX(jc, kMaxRingFlags - grp * J), gstep + 1,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             ++gstep;
         };
 
@@ -619,7 +636,8 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
         // wave LDS order, no barrier needed)
         float sa = 0.0f;
         if (lane < N) {
-            const f32x4* src = reinterpret_cast<const f32x4*>(dAs + lane * kRingQuads);
+            const f32x4* src = reinterpret_cast<const f32x4*>(
+                dAs + MSEL_IDX(lane * kRingQuads, N * kRingQuads));
 #pragma unroll
             for (int q = 0; q < kRingQuads / 4; ++q) {
                 const f32x4 v = src[q];
@@ -632,13 +650,13 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
         float* dst = nullptr;
         float val = 0.0f;
         if (lane < N) {
-            dst = g.dA ? g.dA + static_cast<size_t>(d) * N + lane : nullptr;
+            dst = g.dA ? g.dA + MSEL_IDX(static_cast<size_t>(d) * N + lane, DN) : nullptr;
             val = sa;
         } else if (lane == 62) {
-            dst = g.dD ? g.dD + d : nullptr;
+            dst = g.dD ? g.dD + MSEL_IDX(d, p.D) : nullptr;
             val = sD;
         } else if (lane == 63) {
-            dst = g.dbias ? g.dbias + d : nullptr;
+            dst = g.dbias ? g.dbias + MSEL_IDX(d, p.D) : nullptr;
             val = sb;
         }
         if (dst != nullptr) unsafeAtomicAdd(dst, val);
@@ -654,10 +672,11 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
         const int slot = (nn * K + tt % K) * KP + tt / K;
         float vb = 0.0f, vc = 0.0f;
         for (int q = 0; q < groups; ++q) {
-            vb += accB[q * tile + slot];
-            vc += accC[q * tile + slot];
+            vb += accB[MSEL_IDX(q * tile + slot, groups * tile)];
+            vc += accC[MSEL_IDX(q * tile + slot, groups * tile)];
         }
-        const size_t o = (static_cast<size_t>(b) * N + nn) * L + t;
+        const size_t o =
+            MSEL_IDX((static_cast<size_t>(b) * N + nn) * L + t, static_cast<size_t>(p.B) * N * L);
         if (g.dB != nullptr) unsafeAtomicAdd(g.dB + o, vb);
         if (g.dC != nullptr) unsafeAtomicAdd(g.dC + o, vc);
     }
@@ -758,5 +777,7 @@ hipError_t launch_scan_cplx_bwd(const ScanParams& p, const GradParams& g,
     return bf16 ? cplx_bwd_dispatch<bf16_t>(p, g, w, stream)
                 : cplx_bwd_dispatch<float>(p, g, w, stream);
 }
+
+MSEL_BOUNDS_TAKER(take_bounds_cplx_bwd)
 
 }  // namespace msel

@@ -74,7 +74,7 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
     const bool active = dw < p.D;
     if (!STAGE && !active) return;
     const int d = active ? dw : p.D - 1;
-    const int ch = b * p.D + d;
+    const int ch = MSEL_IDX(b * p.D + d, static_cast<long long>(p.B) * p.D);
     const int L = p.L;
     const int N = p.N;
     const size_t row = static_cast<size_t>(ch) * L;
@@ -82,21 +82,29 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
     const T* __restrict__ dl = static_cast<const T*>(p.delta) + row;
     const T* __restrict__ zr = HAS_Z ? static_cast<const T*>(p.z) + row : nullptr;
     T* __restrict__ out = static_cast<T*>(p.out) + row;
-    const T* __restrict__ Bb = static_cast<const T*>(p.Bm) + static_cast<size_t>(b) * N * L;
-    const T* __restrict__ Cb = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
-    const float bias = p.bias ? p.bias[d] : 0.0f;
-    const float Dd = p.Dv ? p.Dv[d] : 0.0f;
+    const T* __restrict__ Bb =
+        static_cast<const T*>(p.Bm) + static_cast<size_t>(MSEL_IDX(b, p.B)) * N * L;
+    const T* __restrict__ Cb =
+        static_cast<const T*>(p.Cm) + static_cast<size_t>(MSEL_IDX(b, p.B)) * N * L;
+    const float bias = p.bias ? p.bias[MSEL_IDX(d, p.D)] : 0.0f;
+    const float Dd = p.Dv ? p.Dv[MSEL_IDX(d, p.D)] : 0.0f;
+    [[maybe_unused]] const size_t DN = static_cast<size_t>(p.D) * N;
+    [[maybe_unused]] const size_t BDN = static_cast<size_t>(p.B) * DN;
     // lane n holds A[d, n] * log2(e): one vector load, read per state with readlane
-    const float Av = (lane < N) ? p.A[static_cast<size_t>(d) * N + lane] * kLog2e : 0.0f;
+    const float Av =
+        (lane < N) ? p.A[MSEL_IDX(static_cast<size_t>(d) * N + lane, DN)] * kLog2e : 0.0f;
 
     float carry = 0.0f;  // lane n: state h_n entering the current tile
-    if (p.h0 != nullptr && lane < N) carry = p.h0[static_cast<size_t>(ch) * N + lane];
+    if (p.h0 != nullptr && lane < N)
+        carry = p.h0[MSEL_IDX(static_cast<size_t>(ch) * N + lane, BDN)];
     // TRAP: the step before the tile: its u (wave-uniform) and B (lane n: state n)
     float u_last = 0.0f, B_last = 0.0f;
     if constexpr (TRAP) {
         if (p.u_prev != nullptr) u_last = Elem<T>::load1(static_cast<const T*>(p.u_prev) + ch);
         if (p.B_prev != nullptr && lane < N)
-            B_last = Elem<T>::load1(static_cast<const T*>(p.B_prev) + static_cast<size_t>(b) * N + lane);
+            B_last = Elem<T>::load1(static_cast<const T*>(p.B_prev) +
+                                    MSEL_IDX(static_cast<size_t>(b) * N + lane,
+                                             static_cast<size_t>(p.B) * N));
     }
 
     constexpr int TILE = 64 * K;
@@ -104,7 +112,9 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
 
     Stage st(tid);
     auto rows = [&](int n) {  // staged row x of state n: B (x = 0) or C (x = 1)
-        return [=](int x) { return (x == 0 ? Bb : Cb) + static_cast<size_t>(n) * L; };
+        return [=](int x) {
+            return (x == 0 ? Bb : Cb) + static_cast<size_t>(MSEL_IDX(n, N)) * L;
+        };
     };
     int buf = 0;
     if constexpr (STAGE) {
@@ -160,7 +170,7 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
             const float An = readlane(Av, n);
             float a[K], bb[K], bc[K];
             if constexpr (STAGE) Stage::read(stage[buf], 0, lane, bc);
-            else load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(n) * L, t0, L, bc);
+            else load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(n, N)) * L, t0, L, bc);
             float bprev0 = 0.0f;  // TRAP: B_{n} of the step before the lane's first
             if constexpr (TRAP) {
                 bprev0 = shift_up(bc[K - 1], readlane(B_last, n));
@@ -188,7 +198,7 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
                 csv[q] = writelane(readlane(hin, q * (kChunk / K)), n, csv[q]);
 
             if constexpr (STAGE) Stage::read(stage[buf], 1, lane, bc);
-            else load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(n) * L, t0, L, bc);
+            else load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(MSEL_IDX(n, N)) * L, t0, L, bc);
             h = hin;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
@@ -213,13 +223,13 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
             for (int q = 0; q < kCpt; ++q) {
                 const int cidx = tile / kChunk + q;
                 if (cidx < p.nchunks)
-                    p.chunk_states[(static_cast<size_t>(ch) * p.nchunks + cidx) * N + lane] =
-                        csv[q];
+                    p.chunk_states[MSEL_IDX((static_cast<size_t>(ch) * p.nchunks + cidx) * N + lane,
+                                            BDN * p.nchunks)] = csv[q];
             }
         }
     }
     if (active && p.final_state != nullptr && lane < N)
-        p.final_state[static_cast<size_t>(ch) * N + lane] = carry;
+        p.final_state[MSEL_IDX(static_cast<size_t>(ch) * N + lane, BDN)] = carry;
 }
 
 // Recurrent mode (page 3, recurrent mode; page 1 and 2: the state kept in a cache): one
@@ -237,21 +247,24 @@ __global__ __launch_bounds__(256) void scan_step_kernel(ScanParams p) {
     // b * D + d, formed in 64 bits: 16 * batch * dim threads may pass 2^32
     const long long ch =
         (static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x) >> 4;
-    const bool in = ch < static_cast<long long>(p.B) * p.D;
-    const int chc = in ? static_cast<int>(ch) : 0;
+    const long long BD = static_cast<long long>(p.B) * p.D;
+    const bool in = ch < BD;
+    const int chc = MSEL_IDX(in ? static_cast<int>(ch) : 0, BD);
     const int b = chc / p.D;
     const int d = chc - b * p.D;
     const int N = p.N;
     const bool st = in && n < N;
     const int nc = n < N ? n : N - 1;
     const float u = Elem<T>::load1(static_cast<const T*>(p.u) + chc);
-    const float x = Elem<T>::load1(static_cast<const T*>(p.delta) + chc) + (p.bias ? p.bias[d] : 0.0f);
+    const float x = Elem<T>::load1(static_cast<const T*>(p.delta) + chc) +
+                    (p.bias ? p.bias[MSEL_IDX(d, p.D)] : 0.0f);
     const float dt = SOFTPLUS ? softplus_f(x) : x;
-    const size_t bn = static_cast<size_t>(b) * N + nc;  // B and C are [batch, dstate, 1]
+    // B and C are [batch, dstate, 1]
+    const size_t bn = MSEL_IDX(static_cast<size_t>(b) * N + nc, static_cast<size_t>(p.B) * N);
     const float Bv = Elem<T>::load1(static_cast<const T*>(p.Bm) + bn);
     const float Cv = Elem<T>::load1(static_cast<const T*>(p.Cm) + bn);
-    const float An = p.A[static_cast<size_t>(d) * N + nc] * kLog2e;
-    const size_t sidx = static_cast<size_t>(chc) * N + nc;
+    const float An = p.A[MSEL_IDX(static_cast<size_t>(d) * N + nc, static_cast<size_t>(p.D) * N)] * kLog2e;
+    const size_t sidx = MSEL_IDX(static_cast<size_t>(chc) * N + nc, static_cast<size_t>(BD) * N);
     const float h0 = p.h0 ? p.h0[sidx] : 0.0f;
     const float a = exp2_hw(dt * An);
     float h;
@@ -279,7 +292,7 @@ __global__ __launch_bounds__(256) void scan_step_kernel(ScanParams p) {
         if (p.final_state != nullptr) p.final_state[sidx] = h;
     }
     if (in && n == 15) {
-        float y = part + (p.Dv ? p.Dv[d] : 0.0f) * u;
+        float y = part + (p.Dv ? p.Dv[MSEL_IDX(d, p.D)] : 0.0f) * u;
         if constexpr (HAS_Z) {
             const float z = Elem<T>::load1(static_cast<const T*>(p.z) + chc);
             y *= z * sigmoid_f(z);
@@ -352,5 +365,27 @@ hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, hipStream_t stream) {
     if (bf16) return fwd_dispatch<bf16_t, 16>(p, stream);
     return fwd_dispatch<float, 16>(p, stream);
 }
+
+// The checked build's test of its own checks: index `i` of a one-element array, which
+// MSEL_IDX counts and redirects to element 0 when i != 0 (launched by the checked build only:
+// the release build has no check and would store out of range).
+__device__ float g_selftest_cell[1];
+
+__global__ void bounds_selftest_kernel(int i) {
+    if (threadIdx.x == 0) g_selftest_cell[MSEL_IDX(i, 1)] = 1.0f;
+}
+
+hipError_t launch_bounds_selftest(int i, hipStream_t stream) {
+#ifdef MSEL_CHECKED
+    hipLaunchKernelGGL(bounds_selftest_kernel, dim3(1), dim3(64), 0, stream, i);
+    return hipGetLastError();
+#else
+    (void)i;
+    (void)stream;
+    return hipErrorNotSupported;
+#endif
+}
+
+MSEL_BOUNDS_TAKER(take_bounds_fwd)
 
 }  // namespace msel

@@ -451,3 +451,30 @@ def set_ring_spin_limit(polls: int) -> None:
     """Poll limit of those waits for later calls (0: the default); for tests of the timeout
     path (msel_set_ring_spin_limit)."""
     _lib.load().msel_set_ring_spin_limit(int(polls))
+
+
+BOUNDS_FILES = {1: "scan_fwd.hip", 2: "chunk_carry.hip", 3: "scan_bwd.hip", 4: "conv1d.hip",
+                5: "scan_cplx.hip", 6: "scan_cplx_bwd.hip"}
+
+
+def checked_build() -> bool:
+    """Whether the loaded library is the checked build (msel_checked_build)."""
+    return bool(_lib.load().msel_checked_build())
+
+
+def bound_violations():
+    """(count, file, line): out-of-range kernel indexes on the current device since the last
+    call, and the source file and line of the first (msel_bound_violations; always (0, None, 0)
+    in the release build).  Waits for the device to finish its work; clears the records."""
+    n, f, ln = ctypes.c_ulonglong(0), ctypes.c_uint32(0), ctypes.c_uint32(0)
+    _lib.check("msel_bound_violations",
+               _lib.load().msel_bound_violations(ctypes.byref(n), ctypes.byref(f),
+                                                 ctypes.byref(ln)))
+    return int(n.value), BOUNDS_FILES.get(int(f.value)), int(ln.value)
+
+
+def bounds_selftest(device=None) -> None:
+    """Checked build: one kernel that forms an out-of-range index, which its check must count
+    (msel_bounds_selftest).  Raises MselError (MSEL_ERR_UNSUPPORTED) in the release build."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    _lib.check("msel_bounds_selftest", _lib.load().msel_bounds_selftest(_stream(dev)))

@@ -34,6 +34,32 @@ def test_exports_every_declared_function(lib):
         assert hasattr(lib, name)
 
 
+def test_checked_build_exports_the_same_functions(lib):
+    """The checked twin (every kernel index range-checked) exports every declared function;
+    msel_checked_build tells the two apart; the release build's self-test refuses without
+    enqueuing anything, and the violation reader checks its pointers before any HIP call."""
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(msel_\w+)\s*\(", text))
+    nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_CHECKED_PATH],
+                        capture_output=True, text=True, check=True).stdout
+    assert declared <= set(re.findall(r" T (msel_\w+)$", nm, re.M))
+    chk = _lib.load(_lib.LIB_CHECKED_PATH)
+    assert chk.msel_checked_build() == 1
+    assert lib.msel_checked_build() == 0
+    assert lib.msel_bounds_selftest(None) == 5  # MSEL_ERR_UNSUPPORTED
+    n, f = ctypes.c_ulonglong(7), ctypes.c_uint32(7)
+    assert lib.msel_bound_violations(ctypes.byref(n), ctypes.byref(f), None) == 1  # NULL
+    assert chk.msel_bound_violations(None, ctypes.byref(f), ctypes.byref(f)) == 1
+
+
+def test_binding_switches_to_the_checked_build():
+    import selective_state_space_26_amd as msel
+    assert not msel.checked_build()
+    with _lib.using(_lib.LIB_CHECKED_PATH):
+        assert msel.checked_build()
+    assert not msel.checked_build()
+
+
 def test_struct_layout_matches_header(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(
