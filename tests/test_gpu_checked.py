@@ -3,8 +3,10 @@ LDS array compared with the extent of what it indexes) on the GPU:
 
 * its own check fires: the self-test kernel's out-of-range index is counted once, in its file;
 * every seeded random case of the parity tests (every variant's forward, chunk-carry pass and
-  backward, the convolution, the decode steps) meets no out-of-range index and still matches
-  the fp64 oracles at the parity bar;
+  backward, the convolution) meets no out-of-range index and still matches the fp64 oracles at
+  the parity bar;
+* the decode kernels (seqlen 1) of every variant meet none, and their outputs equal the release
+  build's bit for bit;
 * at the full sizes of the 2048- and 65536-step workloads, in the benchmark's launch
   configuration, the forward, the chunk-carry pass and the backward (chunk states given and
   rebuilt, and the allocation-free backward) meet no out-of-range index, and their outputs
@@ -92,3 +94,48 @@ def test_full_workload_in_range_and_equal_to_release(wid, given):
             assert_close(k, host(got[k]), host(v), w.dtype)
         else:
             assert torch.equal(got[k], v), k
+
+
+def _decode(kind, d):
+    """One recurrent step (seqlen 1) of `kind` from a carried state."""
+    if kind == "conv":
+        out, st = msel.msel_conv1d_fwd(d["x"], d["weight"], d["bias"], d["state"], True,
+                                       return_state=True)
+        torch.cuda.synchronize()
+        return {"out": out, "state": st}
+    if kind == "trap":
+        out, fin, _ = msel.msel_scan_trap_fwd(d["u"], d["delta"], d["lam"], d["A"], d["B"],
+                                              d["C"], d["D"], d["z"], d["bias"], True, d["h0"],
+                                              d["u_prev"], d["B_prev"])
+    else:
+        f = msel.msel_scan_complex_fwd if kind == "cplx" else msel.msel_scan_fwd
+        out, fin, _ = f(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["bias"],
+                        True, d["h0"])
+    torch.cuda.synchronize()
+    return {"out": out, "final_state": fin}
+
+
+@pytest.mark.parametrize("kind", ["scan", "trap", "cplx", "conv"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_step_in_range_and_equal_to_release(kind, dtype):
+    """The decode kernels (seqlen 1), which the random cases reach only for the plain scan."""
+    log(f"checked build, decode step {kind} {dtype}")
+    bsz, dim, N = 3, 37, 16
+    if kind == "conv":
+        t = msel_inputs.make_conv(bsz, dim, 1, 4, dtype, 41, with_state=True)
+    else:
+        t = msel_inputs.make(bsz, dim, N, 1, dtype, 42, with_h0=True, with_lam=kind == "trap",
+                             with_prev=kind == "trap", complex_A=kind == "cplx")
+    d = to_device(t)
+    if kind == "trap":  # the step before the first, in the activation dtype
+        act = torch.bfloat16 if dtype == "bf16" else torch.float32
+        for k in ("lam", "u_prev", "B_prev"):
+            d[k] = d[k].to(act)
+    ref = _decode(kind, d)
+    with _lib.using(_lib.LIB_CHECKED_PATH):
+        msel.bound_violations()
+        got = _decode(kind, d)
+        count, f, line = msel.bound_violations()
+        assert count == 0, f"{count} out-of-range indexes, the first at {f}:{line}"
+    for k, v in ref.items():
+        assert torch.equal(got[k], v), k
