@@ -22,11 +22,15 @@ def to_device(t: msel_inputs.Tensors, device="cuda"):
     for k, v in t.items():
         if v is None:
             out[k] = None
-        elif v.dtype == np.uint16:
-            out[k] = torch.from_numpy(v.view(np.int16)).to(device).view(torch.bfloat16)
         else:
-            dt = act if k in ("u", "delta", "z", "B", "C", "dout") else torch.float32
-            out[k] = torch.from_numpy(np.ascontiguousarray(v)).to(device=device, dtype=dt)
+            v = np.ascontiguousarray(v)
+            if not v.flags.writeable:  # torch.from_numpy wants a writable array
+                v = v.copy()
+            if v.dtype == np.uint16:
+                out[k] = torch.from_numpy(v.view(np.int16)).to(device).view(torch.bfloat16)
+            else:
+                dt = act if k in ("u", "delta", "z", "B", "C", "dout") else torch.float32
+                out[k] = torch.from_numpy(v).to(device=device, dtype=dt)
     return out
 
 
