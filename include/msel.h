@@ -159,20 +159,31 @@ msel_status msel_scan_fwd(const msel_scan_args *args, hipStream_t stream);
  * (optional).  Reads u, delta, B, A, delta_bias, h0 only. */
 msel_status msel_scan_chunk_carry(const msel_scan_args *args, hipStream_t stream);
 
-/* Workspace the backward needs, in bytes: the adjoint carry per chunk and state, two floats
- * per chunk, and the chunk-start states when args->chunk_states is NULL (in all about
- * 4*batch*dim*n_chunks*(dstate + 2) bytes, twice the state part without chunk_states).
+/* Workspace the backward needs, in bytes, for the plan it takes (msel_scan_bwd_fused):
+ *  - chunk-parallel: the adjoint carry per chunk and state, two floats per chunk, and the
+ *    chunk-start states when args->chunk_states is NULL (in all about
+ *    4*batch*dim*n_chunks*(dstate + 2) bytes, twice the state part without chunk_states);
+ *  - fused: the adjoint carry per state, and partial sums: of dB and dC per workgroup (about
+ *    256 in all, each 2*dstate*512 floats per chunk: 16 MiB per chunk at 16 states), and of
+ *    dA, dD and ddelta_bias per batch row and chunk (about 68 MiB in all for 8 x 1536
+ *    channels, 16 states and 2048 steps).
  * Returns 0 for invalid args.  The workspace must be 256-byte aligned; its contents on entry
  * do not matter. */
 size_t msel_scan_bwd_workspace_bytes(const msel_scan_args *args);
 
 /* Backward with recomputation (page 1; page 4 Appendix D, Memory: intermediate states are
- * recomputed, not stored).  Launches on `stream`: zero-fills of the summed outputs, per-chunk
- * summaries of the states and of the adjoint, their link across chunks (the chunk carry run
- * forward and backward), and the chunk-parallel gradient kernel.  Only chunk-boundary values
- * live in the workspace.  Reductions over channels (dB, dC) and over batch and time (dA, dD,
- * ddelta_bias) use fp32 atomics, so those outputs may differ in the last bits between runs;
- * du, ddelta, dz and dh0 are deterministic. */
+ * recomputed, not stored).  One of two plans, chosen from the sizes (msel_scan_bwd_fused):
+ *  - chunk-parallel: launches on `stream` zero-fills of the summed outputs, per-chunk
+ *    summaries of the states and of the adjoint, their link across chunks (the chunk carry
+ *    run forward and backward), and the chunk-parallel gradient kernel.  Only chunk-boundary
+ *    values live in the workspace.  Reductions over channels (dB, dC) and over batch and time
+ *    (dA, dD, ddelta_bias) use fp32 atomics, so those outputs may differ in the last bits
+ *    between runs; du, ddelta, dz and dh0 are deterministic;
+ *  - fused (chunk_states given, a few chunks): one gradient kernel walks each channel's chunks
+ *    from the last to the first, carrying the adjoint from chunk to chunk itself (the chunk
+ *    carry run backward inside it), and stores partial sums that a reduce kernel adds in a
+ *    fixed order.  No summary, link or atomics: every output is deterministic.
+ * The two plans compute the same values up to fp32 rounding order. */
 msel_status msel_scan_bwd(const msel_scan_args *args, const msel_scan_grads *grads,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -182,9 +193,11 @@ msel_status msel_scan_bwd(const msel_scan_args *args, const msel_scan_grads *gra
  * array of MSEL_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
  * until the process ends.  The call allocates nothing (no hipMalloc, no allocating library
  * routine); on its first call on a device it looks up that device's address of the array.
- * Problems whose msel_scan_bwd_workspace_bytes exceed MSEL_NOALLOC_SCRATCH_BYTES are refused
- * with MSEL_ERR_TOO_LARGE before anything is enqueued (with chunk_states given, the workspace
- * is about 4 * batch * dim * n_chunks * (dstate + 2) bytes; rebuilt, twice the state part).
+ * It takes the fused plan only when that plan's workspace fits in the array, else the
+ * chunk-parallel one.  Problems whose chunk-parallel workspace exceeds
+ * MSEL_NOALLOC_SCRATCH_BYTES are refused with MSEL_ERR_TOO_LARGE before anything is enqueued
+ * (with chunk_states given, it is about 4 * batch * dim * n_chunks * (dstate + 2) bytes;
+ * rebuilt, twice the state part).
  * Every call on a device shares that device's array: calls that overlap on one device (on
  * different streams, or from different threads) race and give wrong results; calls in one
  * stream's order are safe.  The workspace needs no clearing between calls: the backward
@@ -195,9 +208,9 @@ msel_status msel_scan_bwd_noalloc(const msel_scan_args *args, const msel_scan_gr
 
 /* msel_scan_bwd for profiling: the same launches and results, and in addition the caller's
  * events ev_begin and ev_end (hipEvent_t created by the caller; either may be NULL) are
- * recorded on `stream` immediately before and after the chunk-parallel gradient kernel, the
- * longest of the backward's launches, so that it can be timed on the stream it runs on.  A
- * failed event record returns MSEL_ERR_HIP. */
+ * recorded on `stream` immediately before and after the gradient kernel (of either plan),
+ * the longest of the backward's launches, so that it can be timed on the stream it runs on.
+ * A failed event record returns MSEL_ERR_HIP. */
 msel_status msel_scan_bwd_profiled(const msel_scan_args *args, const msel_scan_grads *grads,
                                    void *workspace, size_t workspace_bytes, hipStream_t stream,
                                    hipEvent_t ev_begin, hipEvent_t ev_end);
@@ -212,6 +225,19 @@ msel_status msel_scan_bwd_profiled(const msel_scan_args *args, const msel_scan_g
  * place where the library keeps state: a counter per device.  MSEL_ERR_NULL if count is NULL,
  * MSEL_ERR_HIP if the runtime fails. */
 msel_status msel_ring_timeouts(unsigned long long *count);
+
+/* 1 if msel_scan_bwd takes the fused plan for these args (with a workspace of
+ * msel_scan_bwd_workspace_bytes(args)), 0 if the chunk-parallel one or the args are invalid.
+ * By default the fused plan is taken when chunk_states is given, n_chunks <= 4 and its grid
+ * (a workgroup per batch row and group of channels, about 256 in all) has at least 128
+ * workgroups.  The trapezoidal and complex backwards always take their chunk-parallel plan. */
+int32_t msel_scan_bwd_fused(const msel_scan_args *args);
+
+/* Changes that choice for calls made after it in this process: mode 0 restores the default,
+ * 1 takes the fused plan wherever it applies (chunk_states given), -1 never.  For tests that
+ * compare the two plans at any size.  msel_scan_bwd_workspace_bytes follows the setting, so
+ * size a workspace after setting it.  Not thread-safe against concurrent backward calls. */
+void msel_set_bwd_fused(int32_t mode);
 
 /* Sets the poll limit of those waits for calls made after it in this process: `polls`
  * polls, each after a sleep of about 64 clocks; 0 restores the default of 2^22 polls (about

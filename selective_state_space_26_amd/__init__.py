@@ -12,11 +12,11 @@ from .scan import (bwd_workspace_bytes, chunk_len, msel_scan_bwd,  # noqa: F401
                    msel_scan_bwd_noalloc, msel_scan_complex_chunk_carry,
                    msel_scan_trap_bwd, msel_scan_trap_chunk_carry, msel_scan_trap_fwd,
                    num_chunks, ring_timeouts, set_ring_spin_limit, checked_build,
-                   bound_violations, bounds_selftest)
+                   bound_violations, bounds_selftest, bwd_fused, set_bwd_fused)
 
 __all__ = ["msel_scan_fwd", "msel_scan_bwd", "msel_scan_chunk_carry", "chunk_len", "num_chunks",
            "bwd_workspace_bytes", "msel_conv1d_fwd", "msel_conv1d_bwd", "msel_scan_trap_fwd",
            "msel_scan_complex_fwd", "msel_scan_trap_bwd", "msel_scan_complex_bwd",
            "ring_timeouts", "set_ring_spin_limit", "msel_scan_bwd_noalloc",
            "msel_scan_trap_chunk_carry", "msel_scan_complex_chunk_carry", "checked_build",
-           "bound_violations", "bounds_selftest"]
+           "bound_violations", "bounds_selftest", "bwd_fused", "set_bwd_fused"]

@@ -77,7 +77,7 @@ EXPORTS = ["msel_abi_version", "msel_chunk_len", "msel_num_chunks", "msel_status
            "msel_set_ring_spin_limit", "msel_scan_bwd_noalloc", "msel_validate_trap_chunk_carry",
            "msel_scan_trap_chunk_carry", "msel_validate_complex_chunk_carry",
            "msel_scan_complex_chunk_carry", "msel_checked_build", "msel_bound_violations",
-           "msel_bounds_selftest"]
+           "msel_bounds_selftest", "msel_scan_bwd_fused", "msel_set_bwd_fused"]
 
 
 def default_path() -> str:
@@ -173,6 +173,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                           ctypes.POINTER(ctypes.c_uint32)]
     lib.msel_bounds_selftest.restype = ctypes.c_int
     lib.msel_bounds_selftest.argtypes = [_P]
+    lib.msel_scan_bwd_fused.restype = ctypes.c_int32
+    lib.msel_scan_bwd_fused.argtypes = [a]
+    lib.msel_set_bwd_fused.restype = None
+    lib.msel_set_bwd_fused.argtypes = [ctypes.c_int32]
     if lib.msel_abi_version() != ABI_VERSION:
         raise RuntimeError("libmsel.so ABI version mismatch")
     if path is None:

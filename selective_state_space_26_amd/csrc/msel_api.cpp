@@ -138,8 +138,8 @@ size_t states_bytes_aligned(const msel_scan_args* a) {
 // kernels (the trapezoidal variant when `tr` is given; with no chunk states given, its
 // chunk-carry pass rebuilds them first).
 msel_status run_bwd(const msel_scan_args* a, const msel_scan_grads* g, const msel_trap_args* tr,
-                    const msel_trap_grads* tg, void* workspace, hipStream_t stream,
-                    hipEvent_t ev_begin, hipEvent_t ev_end) {
+                    const msel_trap_grads* tg, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
     const bool bf16 = a->dtype == MSEL_BF16;
     msel::ScanParams p = to_params(a);
     if (tr != nullptr) {
@@ -181,9 +181,10 @@ msel_status run_bwd(const msel_scan_args* a, const msel_scan_grads* g, const mse
         if (msel::launch_chunk_carry(pc, bf16, false, stream) != hipSuccess) return MSEL_ERR_HIP;
         states = H;
         workspace = static_cast<char*>(workspace) + states_bytes_aligned(a);
+        workspace_bytes -= states_bytes_aligned(a);
     }
-    return hip_status(msel::launch_scan_bwd(p, gp, states, workspace, bf16, fill, stream,
-                                            ev_begin, ev_end));
+    return hip_status(msel::launch_scan_bwd(p, gp, states, workspace, workspace_bytes, bf16,
+                                            fill, stream, ev_begin, ev_end));
 }
 
 }  // namespace
@@ -556,7 +557,7 @@ msel_status msel_scan_bwd_profiled(const msel_scan_args* a, const msel_scan_grad
                                    hipEvent_t ev_begin, hipEvent_t ev_end) {
     msel_status s = msel_validate_bwd(a, g, workspace, workspace_bytes);
     if (s != MSEL_OK) return s;
-    return run_bwd(a, g, nullptr, nullptr, workspace, stream, ev_begin, ev_end);
+    return run_bwd(a, g, nullptr, nullptr, workspace, workspace_bytes, stream, ev_begin, ev_end);
 }
 
 msel_status msel_scan_trap_bwd(const msel_scan_args* a, const msel_trap_args* tr,
@@ -564,7 +565,7 @@ msel_status msel_scan_trap_bwd(const msel_scan_args* a, const msel_trap_args* tr
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
     msel_status s = msel_validate_trap_bwd(a, tr, g, tg, workspace, workspace_bytes);
     if (s != MSEL_OK) return s;
-    return run_bwd(a, g, tr, tg, workspace, stream, nullptr, nullptr);
+    return run_bwd(a, g, tr, tg, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 msel_status msel_ring_timeouts(unsigned long long* count) {
@@ -579,6 +580,17 @@ msel_status msel_ring_timeouts(unsigned long long* count) {
 }
 
 void msel_set_ring_spin_limit(uint32_t polls) { msel::set_ring_spin_limit(polls); }
+
+void msel_set_bwd_fused(int32_t mode) { msel::set_bwd_fused_mode(mode); }
+
+int32_t msel_scan_bwd_fused(const msel_scan_args* a) {
+    if (check_common(a) != MSEL_OK) return 0;
+    return msel::bwd_plan(a->batch, a->dim, a->dstate, a->seqlen, a->chunk_states == nullptr,
+                          SIZE_MAX)
+                   .fused
+               ? 1
+               : 0;
+}
 
 int msel_checked_build(void) {
 #ifdef MSEL_CHECKED
@@ -624,10 +636,13 @@ msel_status msel_scan_bwd_noalloc(const msel_scan_args* a, const msel_scan_grads
                                   hipStream_t stream) {
     msel_status s = check_bwd(a, g);
     if (s != MSEL_OK) return s;
-    if (msel_scan_bwd_workspace_bytes(a) > kScratchBytes) return MSEL_ERR_TOO_LARGE;
+    // the plan that fits in the scratch (the fused pass only if its partial sums do)
+    if (msel::bwd_workspace_bytes(a->batch, a->dim, a->dstate, a->seqlen,
+                                  a->chunk_states == nullptr, kScratchBytes) > kScratchBytes)
+        return MSEL_ERR_TOO_LARGE;
     void* ws = scratch_on_current_device();
     if (ws == nullptr) return MSEL_ERR_HIP;
-    return run_bwd(a, g, nullptr, nullptr, ws, stream, nullptr, nullptr);
+    return run_bwd(a, g, nullptr, nullptr, ws, kScratchBytes, stream, nullptr, nullptr);
 }
 
 msel_status msel_scan_bwd(const msel_scan_args* a, const msel_scan_grads* g, void* workspace,

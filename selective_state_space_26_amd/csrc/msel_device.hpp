@@ -158,6 +158,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const T* row, int L) 
                                              L * static_cast<int>(sizeof(T)), 0x00020000);
 }
 
+// Lane l's element of a wave-uniform row of n floats, through the row's buffer resource: lanes
+// at or past n read 0 and store nothing.  The address stays the row's scalar base plus the
+// lane's byte offset, so no 64-bit address per lane is kept in registers.
+__device__ __forceinline__ float load_lane(const float* row, int n, int lane) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row_rsrc(row, n), lane * 4, 0, 0));
+}
+__device__ __forceinline__ void store_lane(float* row, int n, int lane, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), row_rsrc(row, n), lane * 4, 0, 0);
+}
+
 // One 16-byte vector of a VEC row holding steps [t, t + width): with the row 16-byte aligned,
 // L a multiple of the vector width and t a multiple of it, the vector is wholly in range or
 // wholly past the end (then it reads zeros).  NT: non-temporal (streaming) hint.

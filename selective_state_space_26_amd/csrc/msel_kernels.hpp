@@ -147,14 +147,37 @@ inline unsigned fill_blocks(const FillList& f) {
 hipError_t launch_scan_cplx_bwd(const ScanParams& p, const GradParams& g,
                                 const float* chunk_states, void* workspace, bool bf16,
                                 const FillList& fill, hipStream_t stream);
-// Backward: the summary/link passes write into `workspace` (bwd_workspace_bytes), then the
-// chunk-parallel main kernel.  chunk_states may be NULL (rebuilt in the workspace).
-size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states);
+// Backward of the plain and trapezoidal rules.  Two plans:
+//  * chunk-parallel: the summary/link passes write into the workspace, then the gradient
+//    kernel runs one workgroup per (batch row, chunk, channel group) and adds its sums into
+//    the outputs with fp32 atomics; chunk_states may be NULL (rebuilt in the workspace);
+//  * fused (plain rule, chunk states given): the gradient kernel walks the chunks from the
+//    last to the first in one workgroup per (batch row, channel group), carrying the adjoint
+//    itself, and stores partial sums that a reduce kernel adds in a fixed order (no summary,
+//    no link, no atomics: deterministic).  Taken when the workspace holds its partial sums
+//    and, by default, for at most kFusedMaxChunks chunks and enough channel groups.
+constexpr int kFusedWorkgroups = 256;  // the fused grid's target (a pure function of the sizes)
+constexpr int kFusedMaxChunks = 4;
+struct BwdPlan {
+    bool fused;
+    int cgroups, per_wave;  // the fused grid
+    size_t bytes;           // workspace
+};
+// The plan for these sizes when `cap` workspace bytes are available (need_states: the chunk
+// states are rebuilt).  A pure function of its arguments and of the fused-pass setting.
+BwdPlan bwd_plan(int B, int D, int N, int L, bool need_states, size_t cap);
+size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states,
+                           size_t cap = SIZE_MAX);
+// Fused-pass setting for later calls: 0 by size (the default), 1 wherever it applies, -1 never.
+void set_bwd_fused_mode(int mode);
+int bwd_fused_mode();
 // ev_begin / ev_end (either may be null) are recorded on `stream` right before and after the
 // gradient kernel, so that a caller can time it alone.
-// `fill`: the reduction targets the gradient kernel adds into, zeroed by the link launch.
+// `fill`: the reduction targets the chunk-parallel gradient kernel adds into, zeroed by the
+// link launch.  `workspace_bytes`: the workspace's size (it decides the plan).
 hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float* chunk_states,
-                           void* workspace, bool bf16, const FillList& fill, hipStream_t stream,
+                           void* workspace, size_t workspace_bytes, bool bf16,
+                           const FillList& fill, hipStream_t stream,
                            hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 // Zero-fill of up to kFillSlots float buffers in one launch (null slots are skipped).
 hipError_t launch_fill_zero(const FillList& f, hipStream_t stream);

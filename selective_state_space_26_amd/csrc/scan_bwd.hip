@@ -61,6 +61,13 @@ struct BwdWork {
                     // it is skipped (c0 = 1) when neither dh0 nor the states are built here
     FillList fill;  // the gradient kernel's reduction targets, zeroed by the link launch
     unsigned spin_limit;  // polls after which a ring wait gives up (ring_spin_limit())
+    // The fused pass (bwd_plan): G is then the adjoint carry [B*D*N] of the chunk being
+    // walked, and the sums over channels, batch rows and chunks go to partial sums that the
+    // reduce kernel adds in a fixed order.
+    float* part;    // [B][cgroups][nch][2][N][kChunk]: each workgroup's dB, dC rows per chunk
+    float* dApart;  // [B][nch][D][N]
+    float* dDpart;  // [B][nch][D]
+    float* dbpart;  // [B][nch][D]
 };
 
 // Ring waits of this file's gradient kernel that gave up (see ring_spin_limit).
@@ -333,11 +340,19 @@ static_assert(kMainWaves + kMaxN - 1 <= kMaxRingFlags, "ring flags do not fit");
 // Step t-1's u and B come from the lane's registers, lane l-1, and for the chunk's first step
 // from HBM (u) or the LDS row staged for it (B); step t+1's lam and Delta likewise from lane
 // l+1 or the next chunk's first step.  The chunk states must be the trapezoidal forward's.
-template <typename T, bool VEC, bool HAS_Z, bool SOFTPLUS, bool TRAP>
+//
+// FUSED (the plain rule with the chunk states given, see bwd_plan): one workgroup per (batch
+// row, channel group) walks the chunks from the last to the first.  A wavefront keeps its
+// channels in every chunk, so it carries each channel's adjoint from one chunk into the one
+// before it itself (the value the scan leaves on the left of lane 0, through w.G), and no
+// summary or link pass is needed; after chunk 0 that carry is dh0.  The sums over channels,
+// batch rows and chunks are stored as partial sums, which the reduce kernel adds.
+template <typename T, bool VEC, bool HAS_Z, bool SOFTPLUS, bool TRAP, bool FUSED>
 __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanParams p,
                                                                           GradParams g,
                                                                           BwdWork w,
                                                                           int per_wave) {
+    static_assert(!(TRAP && FUSED), "the fused pass has the plain rule only");
     constexpr int K = kChunk / 64;
     constexpr int W = main_waves<TRAP>();
     constexpr int KP = kAccKP;
@@ -349,12 +364,13 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // one-dimensional grid over (batch row, chunk, channel group), channel groups fastest
-    const int cgroups = static_cast<int>(gridDim.x) / (p.B * p.nchunks);
+    // one-dimensional grid over (batch row, chunk, channel group), channel groups fastest;
+    // FUSED: over (batch row, channel group), starting at the last chunk
+    const int cgroups = static_cast<int>(gridDim.x) / (FUSED ? p.B : p.B * p.nchunks);
     const int bc_ = static_cast<int>(blockIdx.x) / cgroups;
     const int cgrp = static_cast<int>(blockIdx.x) - bc_ * cgroups;
-    const int b = bc_ / p.nchunks;
-    const int c = bc_ - b * p.nchunks;
+    const int b = FUSED ? bc_ : bc_ / p.nchunks;
+    int c = FUSED ? p.nchunks - 1 : bc_ - b * p.nchunks;
     const int N = p.N;
     const int L = p.L;
     const int nch = p.nchunks;
@@ -370,25 +386,91 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     [[maybe_unused]] const size_t DN = static_cast<size_t>(p.D) * N;
     for (int i = tid; i < 2 * groups * tile; i += 64 * W) acc[i] = 0.0f;
     for (int i = tid; i < groups * N; i += 64 * W) ring_flags[MSEL_IDX(i, kMaxRingFlags)] = 0;
+    int gstep = 0;  // the ring's global step (see below)
+    for (;;) {  // FUSED: chunks nch-1 down to 0; otherwise the one chunk c
+    const int t0 = c * kChunk + lane * K;
+    const int rev_addr = (63 - lane) << 2;
+    const f32x4* __restrict__ B4 = reinterpret_cast<const f32x4*>(BCs);
+    const f32x4* __restrict__ C4 = reinterpret_cast<const f32x4*>(BCs + N * kChunk);
+    const T* __restrict__ gu = static_cast<const T*>(p.u);
+    const T* __restrict__ gd = static_cast<const T*>(p.delta);
+    const T* __restrict__ gg_ = static_cast<const T*>(g.dout);
+    const T* __restrict__ gz = static_cast<const T*>(p.z);
+    const T* __restrict__ gl = static_cast<const T*>(p.lam);
+    auto chan_row = [&](int d) { return MSEL_IDX(static_cast<size_t>(b) * p.D + d, BD) * L; };
+
+    // raw input rows of the channel about to start, fetched ahead of time: issued before the
+    // chunk's B and C are staged, so that the two wait for L2 and HBM together
+    Raw<T, K> ru, rd, rg, rz;
+    Raw<T, K> rl;  // TRAP: lambda (unused otherwise)
+    const int d_first = cgrp * per_wave * W + wave;
+    if (d_first < p.D) {
+        const size_t row = chan_row(d_first);
+        load_raw<T, K, VEC>(gu + row, t0, L, ru);
+        load_raw<T, K, VEC>(gd + row, t0, L, rd);
+        if constexpr (TRAP) load_raw<T, K, VEC>(gl + row, t0, L, rl);
+        load_raw<T, K, VEC>(gg_ + row, t0, L, rg);
+        if constexpr (HAS_Z) load_raw<T, K, VEC>(gz + row, t0, L, rz);
+    }
+
     {
         // B and C of this (batch row, chunk), read once per workgroup, zero past the end
         const T* __restrict__ Bg =
             static_cast<const T*>(p.Bm) + static_cast<size_t>(MSEL_IDX(b, p.B)) * N * L;
         const T* __restrict__ Cg =
             static_cast<const T*>(p.Cm) + static_cast<size_t>(MSEL_IDX(b, p.B)) * N * L;
-        for (int i = tid; i < N * kChunk; i += 64 * W) {
-            const int nn = i / kChunk;
-            const int tl = i - nn * kChunk;
-            const int t = c * kChunk + tl;
-            float vb = 0.0f, vc = 0.0f;
-            if (t < L) {
-                vb = Elem<T>::load1(Bg + static_cast<size_t>(nn) * L + t);
-                vc = Elem<T>::load1(Cg + static_cast<size_t>(nn) * L + t);
+        if constexpr (VEC) {
+            // 16-byte vectors (a lane's K steps in bf16, half of them in fp32); a wavefront's
+            // 64 vectors lie in one row, so the row is a scalar base.  Every load of the thread
+            // is issued before its stores: one round trip to L2 per chunk, not one per element.
+            constexpr int VW = Elem<T>::kPerVec;                      // elements per vector
+            constexpr int RV = kChunk / VW;                           // vectors per row
+            constexpr int kV = (kMaxN * RV + 64 * W - 1) / (64 * W);  // vectors per thread
+            static_assert(RV % 64 == 0 && K % VW == 0 || VW % K == 0, "vector layout");
+            f32x4* BCs4 = reinterpret_cast<f32x4*>(BCs);
+            u32x4 rb[kV], rc[kV];
+#pragma unroll
+            for (int j = 0; j < kV; ++j) {
+                const int v = tid + j * 64 * W;
+                const int nn = __builtin_amdgcn_readfirstlane(v / RV);
+                if (nn < N) {
+                    const int t = c * kChunk + (v - nn * RV) * VW;
+                    rb[j] = load_vec<T, false>(Bg + static_cast<size_t>(nn) * L, t, L);
+                    rc[j] = load_vec<T, false>(Cg + static_cast<size_t>(nn) * L, t, L);
+                }
             }
-            const int o = MSEL_IDX(((nn * 2 + (tl % K) / 4) * 64 + tl / K) * 4 + tl % 4,
-                                   N * kChunk);
-            BCs[o] = vb;
-            BCs[N * kChunk + o] = vc;
+#pragma unroll
+            for (int j = 0; j < kV; ++j) {
+                const int v = tid + j * 64 * W;
+                const int nn = __builtin_amdgcn_readfirstlane(v / RV);
+                if (nn >= N) break;
+                const int tl = (v - nn * RV) * VW;  // the vector's first step in the chunk
+                float fb[VW], fc[VW];
+                unpack_vec<T, VW>(rb[j], 0, fb);
+                unpack_vec<T, VW>(rc[j], 0, fc);
+#pragma unroll
+                for (int q = 0; q < VW / 4; ++q) {  // words (nn, (tl % K) / 4 + q) of lane tl / K
+                    const int o = MSEL_IDX((nn * 2 + (tl % K) / 4 + q) * 64 + tl / K, N * kChunk / 4);
+                    BCs4[o] = f32x4{fb[4 * q], fb[4 * q + 1], fb[4 * q + 2], fb[4 * q + 3]};
+                    BCs4[N * kChunk / 4 + o] = f32x4{fc[4 * q], fc[4 * q + 1], fc[4 * q + 2],
+                                                     fc[4 * q + 3]};
+                }
+            }
+        } else {
+            for (int i = tid; i < N * kChunk; i += 64 * W) {
+                const int nn = i / kChunk;
+                const int tl = i - nn * kChunk;
+                const int t = c * kChunk + tl;
+                float vb = 0.0f, vc = 0.0f;
+                if (t < L) {
+                    vb = Elem<T>::load1(Bg + static_cast<size_t>(nn) * L + t);
+                    vc = Elem<T>::load1(Cg + static_cast<size_t>(nn) * L + t);
+                }
+                const int o = MSEL_IDX(((nn * 2 + (tl % K) / 4) * 64 + tl / K) * 4 + tl % 4,
+                                       N * kChunk);
+                BCs[o] = vb;
+                BCs[N * kChunk + o] = vc;
+            }
         }
         if constexpr (TRAP) {
             if (tid < N) {
@@ -419,33 +501,8 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     const int Wg = (W - grp * N < N) ? W - grp * N : N;  // waves sharing this group's rows
     const int kp = (rot + 1 < Wg) ? 1 : N - rot;
     int* gflags = ring_flags + MSEL_IDX(grp * N, kMaxRingFlags);
-    int gstep = 0;
     float* myB = accB + grp * tile;
     float* myC = accC + grp * tile;
-
-    const int t0 = c * kChunk + lane * K;
-    const int rev_addr = (63 - lane) << 2;
-    const f32x4* __restrict__ B4 = reinterpret_cast<const f32x4*>(BCs);
-    const f32x4* __restrict__ C4 = reinterpret_cast<const f32x4*>(BCs + N * kChunk);
-    const T* __restrict__ gu = static_cast<const T*>(p.u);
-    const T* __restrict__ gd = static_cast<const T*>(p.delta);
-    const T* __restrict__ gg_ = static_cast<const T*>(g.dout);
-    const T* __restrict__ gz = static_cast<const T*>(p.z);
-    const T* __restrict__ gl = static_cast<const T*>(p.lam);
-    auto chan_row = [&](int d) { return MSEL_IDX(static_cast<size_t>(b) * p.D + d, BD) * L; };
-
-    // raw input rows of the channel about to start, fetched ahead of time
-    Raw<T, K> ru, rd, rg, rz;
-    Raw<T, K> rl;  // TRAP: lambda (unused otherwise)
-    const int d_first = cgrp * per_wave * W + wave;
-    if (d_first < p.D) {
-        const size_t row = chan_row(d_first);
-        load_raw<T, K, VEC>(gu + row, t0, L, ru);
-        load_raw<T, K, VEC>(gd + row, t0, L, rd);
-        if constexpr (TRAP) load_raw<T, K, VEC>(gl + row, t0, L, rl);
-        load_raw<T, K, VEC>(gg_ + row, t0, L, rg);
-        if constexpr (HAS_Z) load_raw<T, K, VEC>(gz + row, t0, L, rz);
-    }
 
     for (int r = 0; r < per_wave; ++r) {
         const int d = (cgrp * per_wave + r) * W + wave;
@@ -461,7 +518,12 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
         const size_t hg = (ch * nch + c) * N;
         const float Av = (lane < N) ? p.A[MSEL_IDX(static_cast<size_t>(dd_) * N + lane, DN)] : 0.0f;
         const float Hv = (lane < N) ? w.H[MSEL_IDX(hg + lane, BD * nch * N)] : 0.0f;
-        const float Gv = (lane < N) ? w.G[MSEL_IDX(hg + lane, BD * nch * N)] : 0.0f;
+        float Gv;
+        if constexpr (FUSED)  // the carry of this channel from the chunk after (none after the last)
+            Gv = c + 1 < nch ? load_lane(w.G + MSEL_IDX(ch, BD) * N, N, lane) : 0.0f;
+        else
+            Gv = (lane < N) ? w.G[MSEL_IDX(hg + lane, BD * nch * N)] : 0.0f;
+        float Gnext = 0.0f;  // FUSED: lane n, the carry of state n into the chunk before
 
         int n = rot;  // state of step 0
 
@@ -631,7 +693,10 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 const float hin = shift_up(fmaf(P, Hn, S), Hn);
                 // reversed lane 63 - l now maps G_c to the adjoint leaving lane l on its left;
                 // lane l receives lane l + 1's (G_c for lane 63), carried into its last step
-                float lam = rev_lanes(shift_up(fmaf(Pr, Gn, Sr), Gn), rev_addr);
+                const float Gl = fmaf(Pr, Gn, Sr);
+                if constexpr (FUSED)  // reversed lane 63: the adjoint leaving lane 0
+                    Gnext = writelane(readlane(Gl, 63), nc, Gnext);
+                float lam = rev_lanes(shift_up(Gl, Gn), rev_addr);
                 float hs[K];
                 h = hin;
 #pragma unroll
@@ -722,6 +787,12 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
             if constexpr (HAS_Z) load_raw<T, K, VEC>(gz + row_next, t0, L, rz);
         }
         if (!active) continue;
+        if constexpr (FUSED) {  // the carry into the chunk before; after chunk 0 it is dh0
+            if (c > 0)
+                store_lane(w.G + MSEL_IDX(ch, BD) * N, N, lane, Gnext);
+            else if (g.dh0 != nullptr)
+                store_lane(g.dh0 + MSEL_IDX(ch, BD) * N, N, lane, Gnext);
+        }
 
         // du and ddelta.  With the softplus, ddelta = dDelta * sigmoid(delta + bias), formed
         // from delta + bias and Delta (softplus_grad_f); delta, and u, are read again (this
@@ -778,6 +849,13 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
         }
         const float sD = wave_sum_fused(dD_part);
         const float sb = wave_sum_fused(db_part);
+        if constexpr (FUSED) {  // this (batch row, chunk, channel)'s share, stored
+            const size_t pc = MSEL_IDX((static_cast<size_t>(b) * nch + c) * p.D + d, BD * nch);
+            if (g.dA != nullptr) store_lane(w.dApart + pc * N, N, lane, sa);  // lanes n < N
+            if (g.dD != nullptr && lane == 62) w.dDpart[pc] = sD;
+            if (g.dbias != nullptr && lane == 63) w.dbpart[pc] = sb;
+            continue;
+        }
         // one vector atomic per channel: lane n < N adds dA[d, n], lane 62 dD[d], 63 dbias[d]
         float* dst = nullptr;
         float val = 0.0f;
@@ -795,6 +873,32 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     }
 
     __syncthreads();
+    if constexpr (FUSED) {
+        // this chunk's rows of the workgroup's dB and dC sums, stored whole (past the end of
+        // the sequence too: the reduce kernel reads only steps < L); the accumulators are
+        // zeroed for the chunk before
+        float* dst = w.part + MSEL_IDX(((static_cast<size_t>(b) * cgroups + cgrp) * nch + c) *
+                                           2 * N * kChunk,
+                                       static_cast<size_t>(p.B) * cgroups * nch * 2 * N * kChunk);
+        for (int i = tid; i < N * kChunk; i += 64 * W) {
+            const int nn = i / kChunk;
+            const int tt = i - nn * kChunk;
+            const int slot = (nn * K + tt % K) * KP + tt / K;
+            float vb = 0.0f, vc = 0.0f;
+            for (int q = 0; q < groups; ++q) {
+                const int o = MSEL_IDX(q * tile + slot, groups * tile);
+                vb += accB[o];
+                vc += accC[o];
+                accB[o] = 0.0f;
+                accC[o] = 0.0f;
+            }
+            dst[i] = vb;
+            dst[N * kChunk + i] = vc;
+        }
+        if (c == 0) break;
+        --c;
+        continue;  // the next chunk's staging follows; its barrier orders the zeroing
+    }
     for (int i = tid; i < N * kChunk; i += 64 * W) {
         const int nn = i / kChunk;
         const int tt = i - nn * kChunk;
@@ -811,6 +915,8 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
         if (g.dB != nullptr) unsafeAtomicAdd(g.dB + o, vb);
         if (g.dC != nullptr) unsafeAtomicAdd(g.dC + o, vc);
     }
+    break;
+    }  // chunks
 }
 
 // Zeroes up to kFillSlots buffers in one launch (for reductions with no launch of their own
@@ -827,12 +933,116 @@ hipError_t launch_fill_zero(const FillList& f, hipStream_t stream) {
     return hipGetLastError();
 }
 
-size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states) {
+// The fused pass's reductions, each summed in a fixed order (so the fused backward is
+// deterministic): dB and dC over the channel groups, dA, dD and dbias over batch rows and
+// chunks.  Thread i < B*N*L: element i of dB and dC; the next D*N: dA; the next D: dD, dbias.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(ScanParams p, GradParams g, BwdWork w,
+                                                         int cgroups) {
+    const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int N = p.N, L = p.L, nch = p.nchunks;
+    const size_t BNL = static_cast<size_t>(p.B) * N * L;
+    const size_t DN = static_cast<size_t>(p.D) * N;
+    const size_t BC = static_cast<size_t>(p.B) * nch;  // (batch row, chunk) partials
+    if (i < BNL) {
+        const size_t bn = i / L;
+        const int t = static_cast<int>(i - bn * L);
+        const int b = static_cast<int>(bn / N);
+        const int n = static_cast<int>(bn - static_cast<size_t>(b) * N);
+        const int c = t / kChunk;
+        const size_t rows = static_cast<size_t>(nch) * 2 * N * kChunk;  // per channel group
+        const size_t o = static_cast<size_t>(b) * cgroups * rows +
+                         (static_cast<size_t>(c) * 2 * N + n) * kChunk + (t - c * kChunk);
+        // eight groups' values loaded together, then added in group order
+        const float* src = w.part + o;
+        const size_t cw = static_cast<size_t>(N) * kChunk;  // from a group's dB rows to its dC
+        float sb = 0.0f, sc = 0.0f;
+        for (int j0 = 0; j0 < cgroups; j0 += 8) {
+            float vb[8], vc[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const size_t at = static_cast<size_t>(j0 + q) * rows;
+                const bool in = j0 + q < cgroups;
+                vb[q] = in ? src[MSEL_IDX(at, BC * cgroups * 2 * N * kChunk - o)] : 0.0f;
+                vc[q] = in ? src[MSEL_IDX(at + cw, BC * cgroups * 2 * N * kChunk - o)] : 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                sb += vb[q];
+                sc += vc[q];
+            }
+        }
+        if (g.dB != nullptr) g.dB[i] = sb;
+        if (g.dC != nullptr) g.dC[i] = sc;
+        return;
+    }
+    size_t k = i - BNL;
+    // the other sums: over (batch row, chunk) partials, eight loaded together and added in order
+    auto sum_bc = [&](const float* part, size_t stride, size_t k_) {
+        float acc = 0.0f;
+        for (size_t j0 = 0; j0 < BC; j0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                v[q] = j0 + q < BC ? part[MSEL_IDX((j0 + q) * stride + k_, BC * stride)] : 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc += v[q];
+        }
+        return acc;
+    };
+    if (k < DN) {
+        if (g.dA != nullptr) g.dA[k] = sum_bc(w.dApart, DN, k);
+        return;
+    }
+    k -= DN;
+    if (k < static_cast<size_t>(p.D)) {
+        if (g.dD != nullptr) g.dD[k] = sum_bc(w.dDpart, p.D, k);
+        if (g.dbias != nullptr) g.dbias[k] = sum_bc(w.dbpart, p.D, k);
+    }
+}
+
+std::atomic<int> g_bwd_fused_mode{0};
+
+int bwd_fused_mode() { return g_bwd_fused_mode.load(std::memory_order_relaxed); }
+
+void set_bwd_fused_mode(int mode) {
+    g_bwd_fused_mode.store(mode > 0 ? 1 : (mode < 0 ? -1 : 0), std::memory_order_relaxed);
+}
+
+BwdPlan bwd_plan(int B, int D, int N, int L, bool need_states, size_t cap) {
     const size_t nch = (static_cast<size_t>(L) + kChunk - 1) / kChunk;
     const size_t states = static_cast<size_t>(B) * D * nch * N * sizeof(float);
     const size_t per_chunk = static_cast<size_t>(B) * D * nch * sizeof(float);
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-    return (need_states ? up(states) : 0) + up(states) + 2 * up(per_chunk);
+    BwdPlan plan{};
+    plan.bytes = (need_states ? up(states) : 0) + up(states) + 2 * up(per_chunk);
+    const int mode = bwd_fused_mode();
+    if (need_states || mode < 0 || N > kMaxN) return plan;
+    // about kFusedWorkgroups workgroups of kMainWaves channels at a time; a pure function of
+    // the sizes (the workspace size must not depend on the device)
+    constexpr int W = kMainWaves;
+    long long cg = (kFusedWorkgroups + B - 1) / B;
+    const long long cg_max = (static_cast<long long>(D) + W - 1) / W;
+    if (cg > cg_max) cg = cg_max;
+    const long long per = (static_cast<long long>(D) + cg * W - 1) / (cg * W);
+    cg = (static_cast<long long>(D) + per * W - 1) / (per * W);
+    const size_t fused = up(static_cast<size_t>(B) * D * N * sizeof(float)) +          // carry
+                         up(static_cast<size_t>(B) * cg * nch * 2 * N * kChunk * 4) +  // dB, dC
+                         up(static_cast<size_t>(B) * nch * D * N * sizeof(float)) +    // dA
+                         2 * up(per_chunk);                                             // dD, dbias
+    const size_t bytes = fused > plan.bytes ? fused : plan.bytes;
+    if (bytes > cap) return plan;
+    // automatically: a few chunks (the partial sums grow with the sequence, the summary the
+    // fused pass saves does not) and enough workgroups to fill most of the chip
+    if (mode == 0 && (nch > kFusedMaxChunks || B * cg < kFusedWorkgroups / 2)) return plan;
+    plan.fused = true;
+    plan.cgroups = static_cast<int>(cg);
+    plan.per_wave = static_cast<int>(per);
+    plan.bytes = bytes;
+    return plan;
+}
+
+size_t bwd_workspace_bytes(int B, int D, int N, int L, bool need_states, size_t cap) {
+    return bwd_plan(B, D, N, L, need_states, cap).bytes;
 }
 
 namespace {
@@ -855,9 +1065,38 @@ struct Timing {
     hipEvent_t begin, end;
 };
 
+// The fused plan: the gradient kernel over (batch row, channel group), then the reduce kernel.
+template <typename T, bool VEC, bool HAS_Z, bool SP>
+hipError_t bwd_fused_go(const ScanParams& p, const GradParams& g, const BwdWork& w,
+                        const BwdPlan& plan, hipStream_t s, Timing tm) {
+    constexpr int W = main_waves<false>();
+    hipError_t e = allow_dynamic_lds<&bwd_main_kernel<T, VEC, HAS_Z, SP, false, true>>(
+        static_cast<int>(main_lds_bytes_max(W)));
+    if (e != hipSuccess) return e;
+    const long long mblocks = static_cast<long long>(plan.cgroups) * p.B;
+    if (mblocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (tm.begin != nullptr && (e = hipEventRecord(tm.begin, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_main_kernel<T, VEC, HAS_Z, SP, false, true>),
+                       dim3(static_cast<unsigned>(mblocks)), dim3(64 * W), main_lds_bytes(p.N, W),
+                       s, p, g, w, plan.per_wave);
+    e = hipGetLastError();
+    if (e == hipSuccess && tm.end != nullptr) e = hipEventRecord(tm.end, s);
+    if (e != hipSuccess) return e;
+    const size_t threads = static_cast<size_t>(p.B) * p.N * p.L +
+                           static_cast<size_t>(p.D) * p.N + static_cast<size_t>(p.D);
+    const size_t rblocks = (threads + 255) / 256;
+    if (rblocks > 0x7fffffffULL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>(rblocks)), dim3(256), 0, s,
+                       p, g, w, plan.cgroups);
+    return hipGetLastError();
+}
+
 template <typename T, bool VEC, bool HAS_Z, bool SP, bool TRAP>
-hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hipStream_t s,
-                  Timing tm) {
+hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w,
+                  const BwdPlan& plan, hipStream_t s, Timing tm) {
+    if constexpr (!TRAP) {
+        if (plan.fused) return bwd_fused_go<T, VEC, HAS_Z, SP>(p, g, w, plan, s, tm);
+    }
     constexpr int W = main_waves<TRAP>();
     const int per_sum = w.want_fwd ? sum_channels<true>() : sum_channels<false>();
     const int sum_waves = p.B * (p.nchunks - w.c0) * ((p.D + per_sum - 1) / per_sum);
@@ -883,15 +1122,15 @@ hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hi
     const int cgroups = (p.D + per_wave * W - 1) / (per_wave * W);
     const size_t lds = main_lds_bytes(p.N, W);
     // the LDS exceeds the 64 KB default; allow the largest need over N <= kMaxN
-    e = allow_dynamic_lds<&bwd_main_kernel<T, VEC, HAS_Z, SP, TRAP>>(
+    e = allow_dynamic_lds<&bwd_main_kernel<T, VEC, HAS_Z, SP, TRAP, false>>(
         static_cast<int>(main_lds_bytes_max(W)));
     if (e != hipSuccess) return e;
     const long long mblocks = static_cast<long long>(cgroups) * p.nchunks * p.B;
     if (mblocks > 0x7fffffffLL) return hipErrorInvalidValue;
     dim3 mgrid(static_cast<unsigned>(mblocks)), mblock(64 * W);
     if (tm.begin != nullptr && (e = hipEventRecord(tm.begin, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_main_kernel<T, VEC, HAS_Z, SP, TRAP>), mgrid, mblock, lds, s, p, g,
-                       w, per_wave);
+    hipLaunchKernelGGL((bwd_main_kernel<T, VEC, HAS_Z, SP, TRAP, false>), mgrid, mblock, lds, s,
+                       p, g, w, per_wave);
     e = hipGetLastError();
     if (e == hipSuccess && tm.end != nullptr) e = hipEventRecord(tm.end, s);
     return e;
@@ -899,13 +1138,13 @@ hipError_t bwd_go(const ScanParams& p, const GradParams& g, const BwdWork& w, hi
 
 template <typename T>
 hipError_t bwd_dispatch(const ScanParams& p, const GradParams& g, const BwdWork& w,
-                        hipStream_t s, Timing tm) {
+                        const BwdPlan& plan, hipStream_t s, Timing tm) {
     const bool vec = (static_cast<size_t>(p.L) * sizeof(T)) % 16 == 0;
     const bool hz = p.z != nullptr;
     const bool sp = p.softplus != 0;
     if (p.lam != nullptr) {  // the trapezoidal variant (chunk states given by its forward)
 #define MSEL_BWD_T(V, Z, S) \
-        if (vec == V && hz == Z && sp == S) return bwd_go<T, V, Z, S, true>(p, g, w, s, tm);
+        if (vec == V && hz == Z && sp == S) return bwd_go<T, V, Z, S, true>(p, g, w, plan, s, tm);
         MSEL_BWD_T(true, true, true)
         MSEL_BWD_T(true, true, false)
         MSEL_BWD_T(true, false, true)
@@ -918,7 +1157,7 @@ hipError_t bwd_dispatch(const ScanParams& p, const GradParams& g, const BwdWork&
         return hipErrorInvalidValue;
     }
 #define MSEL_BWD(V, Z, S) \
-    if (vec == V && hz == Z && sp == S) return bwd_go<T, V, Z, S, false>(p, g, w, s, tm);
+    if (vec == V && hz == Z && sp == S) return bwd_go<T, V, Z, S, false>(p, g, w, plan, s, tm);
     MSEL_BWD(true, true, true)
     MSEL_BWD(true, true, false)
     MSEL_BWD(true, false, true)
@@ -934,33 +1173,52 @@ hipError_t bwd_dispatch(const ScanParams& p, const GradParams& g, const BwdWork&
 }  // namespace
 
 hipError_t launch_scan_bwd(const ScanParams& p, const GradParams& g, const float* chunk_states,
-                           void* workspace, bool bf16, const FillList& fill, hipStream_t stream,
-                           hipEvent_t ev_begin, hipEvent_t ev_end) {
+                           void* workspace, size_t workspace_bytes, bool bf16,
+                           const FillList& fill, hipStream_t stream, hipEvent_t ev_begin,
+                           hipEvent_t ev_end) {
     if (p.N > kMaxN) return hipErrorInvalidValue;
     const size_t nch = static_cast<size_t>(p.nchunks);
     const size_t states = static_cast<size_t>(p.B) * p.D * nch * p.N * sizeof(float);
     const size_t per_chunk = static_cast<size_t>(p.B) * p.D * nch * sizeof(float);
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     char* ws = static_cast<char*>(workspace);
-    BwdWork w;
+    BwdWork w{};
     w.want_fwd = chunk_states == nullptr;
-    if (w.want_fwd) {
-        w.H = reinterpret_cast<float*>(ws);
-        ws += up(states);
-    } else {
-        w.H = const_cast<float*>(chunk_states);
-    }
-    w.G = reinterpret_cast<float*>(ws);
-    ws += up(states);
-    w.sdt = reinterpret_cast<float*>(ws);
-    ws += up(per_chunk);
-    w.dfirst = reinterpret_cast<float*>(ws);
-    w.c0 = (!w.want_fwd && g.dh0 == nullptr) ? 1 : 0;
     w.fill = fill;
     w.spin_limit = ring_spin_limit();
+    // the trapezoidal rule has no fused pass: its plan is the one that fits in no bytes
+    const BwdPlan plan =
+        bwd_plan(p.B, p.D, p.N, p.L, w.want_fwd, p.lam != nullptr ? 0 : workspace_bytes);
+    if (plan.bytes > workspace_bytes) return hipErrorInvalidValue;
     const Timing tm{ev_begin, ev_end};
-    if (bf16) return bwd_dispatch<bf16_t>(p, g, w, stream, tm);
-    return bwd_dispatch<float>(p, g, w, stream, tm);
+    if (plan.fused) {
+        w.H = const_cast<float*>(chunk_states);
+        w.G = reinterpret_cast<float*>(ws);
+        ws += up(static_cast<size_t>(p.B) * p.D * p.N * sizeof(float));
+        w.part = reinterpret_cast<float*>(ws);
+        ws += up(static_cast<size_t>(p.B) * plan.cgroups * nch * 2 * p.N * kChunk *
+                 sizeof(float));
+        w.dApart = reinterpret_cast<float*>(ws);
+        ws += up(states);
+        w.dDpart = reinterpret_cast<float*>(ws);
+        ws += up(per_chunk);
+        w.dbpart = reinterpret_cast<float*>(ws);
+    } else {
+        if (w.want_fwd) {
+            w.H = reinterpret_cast<float*>(ws);
+            ws += up(states);
+        } else {
+            w.H = const_cast<float*>(chunk_states);
+        }
+        w.G = reinterpret_cast<float*>(ws);
+        ws += up(states);
+        w.sdt = reinterpret_cast<float*>(ws);
+        ws += up(per_chunk);
+        w.dfirst = reinterpret_cast<float*>(ws);
+        w.c0 = (!w.want_fwd && g.dh0 == nullptr) ? 1 : 0;
+    }
+    if (bf16) return bwd_dispatch<bf16_t>(p, g, w, plan, stream, tm);
+    return bwd_dispatch<float>(p, g, w, plan, stream, tm);
 }
 
 MSEL_BOUNDS_TAKER(take_bounds_bwd)

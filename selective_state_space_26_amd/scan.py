@@ -247,19 +247,37 @@ def msel_scan_complex_chunk_carry(u, delta, A, B, delta_bias=None, delta_softplu
     return chunk_states, final_state
 
 
-def bwd_workspace_bytes(u, A, chunk_states_given=False) -> int:
-    """Bytes of workspace msel_scan_bwd needs for this problem (msel_scan_bwd_workspace_bytes)."""
+def _shape_args(u, A, chunk_states_given):
     bsz, dim, L = u.shape
     a = _lib.ScanArgs()
     a.abi_version = _lib.ABI_VERSION
     a.batch, a.dim, a.dstate, a.seqlen = int(bsz), int(dim), int(A.shape[1]), int(L)
     a.dtype = _dtype_code(u.dtype)
     a.delta_softplus, a.reserved = 1, 0
-    # the size depends only on the shapes; non-null placeholders satisfy the argument checks
+    # the answer depends only on the shapes; non-null placeholders satisfy the argument checks
     for f in ("u", "delta", "B", "A"):
         setattr(a, f, 256)
     a.chunk_states = 256 if chunk_states_given else None
+    return a
+
+
+def bwd_workspace_bytes(u, A, chunk_states_given=False) -> int:
+    """Bytes of workspace msel_scan_bwd needs for this problem (msel_scan_bwd_workspace_bytes)."""
+    a = _shape_args(u, A, chunk_states_given)
     return int(_lib.load().msel_scan_bwd_workspace_bytes(ctypes.byref(a)))
+
+
+def bwd_fused(u, A, chunk_states_given=True) -> bool:
+    """Whether msel_scan_bwd takes its fused, deterministic plan for this problem
+    (msel_scan_bwd_fused)."""
+    a = _shape_args(u, A, chunk_states_given)
+    return bool(_lib.load().msel_scan_bwd_fused(ctypes.byref(a)))
+
+
+def set_bwd_fused(mode: int) -> None:
+    """The backward's plan for later calls (msel_set_bwd_fused): 0 by size (the default),
+    1 fused wherever it applies, -1 never."""
+    _lib.load().msel_set_bwd_fused(int(mode))
 
 
 def msel_scan_complex_bwd(u, delta, A, B, C, dout, chunk_states=None, D=None, z=None,

@@ -265,6 +265,43 @@ def test_bwd_workspace_rules(lib):
     assert lib.msel_validate_bwd(ctypes.byref(a), ctypes.byref(g), a.chunk_states, need2) == 7
 
 
+def test_bwd_plan_choice(lib):
+    """The fused plan: chunk states given, at most 4 chunks and a grid of at least 128
+    workgroups by default; its workspace holds the partial sums (a pure function of the
+    sizes); the setting forces or forbids it; the rebuilt-state backward never takes it."""
+    T = lib.msel_chunk_len()
+    up = lambda x: (x + 255) // 256 * 256
+
+    def plan(bsz, dim, N, L, given=True):
+        a = _good_args(bsz=bsz, dim=dim, N=N, L=L, dtype=1)
+        if given:
+            a.chunk_states = _addr()
+        return lib.msel_scan_bwd_fused(ctypes.byref(a)), lib.msel_scan_bwd_workspace_bytes(
+            ctypes.byref(a))
+
+    try:
+        fused, need = plan(8, 1536, 16, 2048)  # 32 channel groups per batch row
+        assert fused == 1
+        nch, cg = 2048 // T, 32
+        assert need == (up(8 * 1536 * 16 * 4) + up(8 * cg * nch * 2 * 16 * T * 4) +
+                        up(8 * nch * 1536 * 16 * 4) + 2 * up(8 * 1536 * nch * 4))
+        assert need > 64 << 20  # beyond the no-allocation scratch: that call stays chunk-parallel
+        assert plan(8, 1536, 16, 2048, given=False)[0] == 0  # rebuilt states
+        assert plan(1, 5120, 16, 65536)[0] == 0  # 128 chunks
+        assert plan(2, 3, 16, 1000)[0] == 0  # a grid of 2 workgroups
+        small = plan(2, 3, 16, 1000)[1]
+        lib.msel_set_bwd_fused(1)
+        fused, need = plan(2, 3, 16, 1000)
+        assert fused == 1 and need >= small
+        assert plan(1, 5120, 16, 65536)[0] == 1
+        assert plan(2, 3, 16, 1000, given=False)[0] == 0
+        lib.msel_set_bwd_fused(-1)
+        assert plan(8, 1536, 16, 2048) == (0, up(8 * 1536 * 4 * 16 * 4) + 2 * up(8 * 1536 * 4 * 4))
+    finally:
+        lib.msel_set_bwd_fused(0)
+    assert plan(8, 1536, 16, 2048)[0] == 1
+
+
 def test_bwd_noalloc_checks_before_any_launch(lib):
     """msel_scan_bwd_noalloc refuses bad arguments, and a problem whose workspace would exceed
     its static scratch, on the host (these calls make no HIP call)."""
