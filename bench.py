@@ -57,8 +57,10 @@ COLD_REPS = 10
 TRAFFIC_FILE = "profiles/{kernel}_d768x2_bf16_traffic.txt"
 
 
-def algorithmic_bytes(w, nchunks, dtype_bytes=None):
-    """Bytes each pass must move at least once between HBM and the chip."""
+def algorithmic_bytes(w, nchunks, dtype_bytes=None, fused=False):
+    """Bytes each pass must move at least once between HBM and the chip.  fused: the backward
+    takes its fused plan (its gradient kernel reads the chunk states, not the adjoint carries
+    of a link pass)."""
     s = dtype_bytes or (2 if w.dtype == "bf16" else 4)
     tc = w.batch * w.dim * w.seqlen
     bnl = w.batch * w.dstate * w.seqlen
@@ -71,9 +73,10 @@ def algorithmic_bytes(w, nchunks, dtype_bytes=None):
     cc = 2 * tc * s + bnl * s + states + dn * 4 + d * 4
     # the whole backward: u, delta, dout, z in; du, ddelta, dz out; B, C in; dB, dC out
     # (fp32); A, D, bias in; dA, dD, dbias out.  The gradient kernel alone moves the same
-    # tensors, plus the chunk-start states and adjoint carries it reads (counted for it).
+    # tensors, plus the chunk-start states (and with the chunk-parallel plan the adjoint
+    # carries) it reads, counted for it.  The fused plan's partial sums are not counted.
     bwd = 7 * tc * s + 2 * bnl * s + 2 * bnl * 4 + 2 * dn * 4 + 4 * d * 4
-    bwd_main = bwd + 2 * states
+    bwd_main = bwd + (1 if fused else 2) * states
     return {"fwd": fwd, "chunk_carry": cc, "bwd_main": bwd_main, "bwd": bwd}
 
 
@@ -217,7 +220,8 @@ def main():
     s_ = 2 if w.dtype == "bf16" else 4
     tc = w.batch * w.dim * w.seqlen
     upd = tc * w.dstate
-    alg = algorithmic_bytes(w, nch)
+    fused = msel.bwd_fused(d0["u"], d0["A"], True)  # the plan the step's backward takes
+    alg = algorithmic_bytes(w, nch, fused=fused)
 
     # a ring of input copies, together more than twice the last-level cache
     streamed = ("u", "delta", "z", "dout", "B", "C")
@@ -293,11 +297,13 @@ def main():
     kernels = {
         "fwd": entry(step_ms["fwd"], alg["fwd"], tc, "scan_fwd_kernel in the step (one launch)",
                      upd, VALU_FLOOR_FWD),
-        "bwd": entry(step_ms["bwd"], alg["bwd"], tc, "the msel_scan_bwd call in the step: "
-                     "zero-fills, summary, link and bwd_main_kernel"),
+        "bwd": entry(step_ms["bwd"], alg["bwd"], tc, "the msel_scan_bwd call in the step: " +
+                     ("the fused bwd_main_kernel and bwd_reduce_kernel" if fused else
+                      "zero-fills, summary, link and bwd_main_kernel")),
         "bwd_main": entry(step_ms["bwd_main"], alg["bwd_main"], tc,
-                          "bwd_main_kernel in the step, the chunk-parallel gradient kernel",
-                          upd, vf_bwd),
+                          "bwd_main_kernel in the step, " +
+                          ("the fused gradient kernel (chunks walked last to first)" if fused
+                           else "the chunk-parallel gradient kernel"), upd, vf_bwd),
     }
     for k in ("fwd", "bwd_main"):
         kernels[k]["traffic"] = measured_traffic(
@@ -352,6 +358,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
                    "seqlen": w.seqlen, "io_dtype": w.dtype,
                    "step": "fwd (with chunk-boundary states) + bwd",
+                   "bwd_plan": "fused" if fused else "chunk-parallel",
                    "input_copies": nsets, "input_copy_bytes": int(set_bytes)},
         "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
     }
@@ -391,12 +398,16 @@ def extra_timings(cx, msel, msel_inputs, w, sets, nsets, alg, tc, upd, vf_bwd, w
         onch = msel.num_chunks(ow.seqlen)
         otc = ow.batch * ow.dim * ow.seqlen
         oupd = otc * ow.dstate
-        oalg = algorithmic_bytes(ow, onch)
+        # the backward as that workload's description asks: chunk states rebuilt by the
+        # backward (workload 4: "no stored intermediate states"), else the forward's
+        given = wid != 4
+        oalg = algorithmic_bytes(ow, onch, fused=given and msel.bwd_fused(od["u"], od["A"], True))
         od["out"] = torch.empty_like(od["u"])
         od["fin"] = torch.empty(ow.batch, ow.dim, ow.dstate, device=dev, dtype=torch.float32)
         od["cs"] = torch.empty(ow.batch, ow.dim, onch, ow.dstate, device=dev,
                                dtype=torch.float32)
-        ows = torch.empty(msel.bwd_workspace_bytes(od["u"], od["A"], False), device=dev,
+        ows = torch.empty(max(msel.bwd_workspace_bytes(od["u"], od["A"], False),
+                              msel.bwd_workspace_bytes(od["u"], od["A"], True)), device=dev,
                           dtype=torch.uint8)
         tag = f"w{wid}"
         shape = f"{ow.batch}x{ow.dim}x{ow.dstate}x{ow.seqlen} {ow.dtype}"
@@ -415,9 +426,6 @@ def extra_timings(cx, msel, msel_inputs, w, sets, nsets, alg, tc, upd, vf_bwd, w
                     od["u"], od["delta"], od["A"], od["B"], od["bias"], True,
                     chunk_states=od["cs"], final_state=od["fin"])),
                 oalg["chunk_carry"], otc, f"chunk_carry_kernel at workload {wid}, cold cache")
-        # the backward as that workload's description asks: chunk states rebuilt by the
-        # backward (workload 4: "no stored intermediate states"), else the forward's
-        given = wid != 4
         ofwd()
 
         def obwd(ev=None):
