@@ -113,8 +113,29 @@ def _conv():
     return step, ("out", "state_out", "dx", "dstate"), ("dweight", "dbias")
 
 
+def _fused():
+    """The backward's fused plan (gradient kernel and reduce kernel; no atomics, so every
+    output replays bit for bit)."""
+    t = msel_inputs.make(*SHAPE, "bf16", 38, with_dout=True, with_h0=True)
+    d = to_device(t)
+    a = (d["u"], d["delta"], d["A"], d["B"], d["C"])
+    o = (d["D"], d["z"], d["bias"], True, d["h0"])
+
+    def step():
+        out, fin, cs = msel.msel_scan_fwd(*a, *o, return_chunk_states=True)
+        msel.set_bwd_fused(1)
+        try:
+            assert msel.bwd_fused(d["u"], d["A"])
+            g = msel.msel_scan_bwd(*a, d["dout"], *o, chunk_states=cs, want_dh0=True)
+        finally:
+            msel.set_bwd_fused(0)
+        return dict(out=out, fin=fin, **g)
+    return step, ("out", "fin", "du", "ddelta", "dz", "dh0", "dA", "dB", "dC", "dD",
+                  "ddelta_bias"), ()
+
+
 STEPS = {"scan": _scan, "trap": _trap, "complex": _complex, "conv": _conv, "noalloc": _noalloc,
-         "variants_rebuilt": _variants_rebuilt}
+         "variants_rebuilt": _variants_rebuilt, "fused": _fused}
 
 
 @pytest.mark.parametrize("variant", list(STEPS))
