@@ -14,7 +14,7 @@
 //   ddelta_t = dDelta_t * sigmoid(delta_t + bias) with the softplus, dbias += ddelta_t
 //   dD += dy_t u_t       dh0 = a_0 lam_0
 //
-// Three launches, all parallel over chunks:
+// Two plans (bwd_plan).  The chunk-parallel plan: three launches, all parallel over chunks:
 //  1. summary: one wavefront per (batch, chunk, few channels).  For every state n it forms
 //     the chunk's local end state from a zero start and the adjoint at the chunk's first step
 //     from a zero adjoint beyond the chunk, in closed form from prefix sums of Delta (see the
@@ -37,6 +37,10 @@
 //     a small fraction of the plain LDS rate on this chip): the wavefronts visit the states
 //     in rotated order and hand each state's rows on in a ring, so a plain read-add-write
 //     suffices.
+// The fused plan (chunk states given, a few chunks): the main kernel alone, its workgroups
+// each on (batch row, channel range) walking the chunks from the last to the first and
+// carrying the adjoint between them itself (the link's backward walk, inside the kernel), then
+// a reduce kernel that adds the workgroups' stored partial sums in a fixed order.
 #include "msel_device.hpp"
 #include "msel_kernels.hpp"
 
