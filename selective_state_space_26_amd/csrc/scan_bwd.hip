@@ -437,11 +437,13 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
             for (int j = 0; j < kV; ++j) {
                 const int v = tid + j * 64 * W;
                 const int nn = __builtin_amdgcn_readfirstlane(v / RV);
-                if (nn < N) {
-                    const int t = c * kChunk + (v - nn * RV) * VW;
-                    rb[j] = load_vec<T, false>(Bg + static_cast<size_t>(nn) * L, t, L);
-                    rc[j] = load_vec<T, false>(Cg + static_cast<size_t>(nn) * L, t, L);
-                }
+                // no branch between the loads: a vector past the last state reads row 0 at
+                // offset L, which is past the row's end, so it reads zeros (and is not stored)
+                const bool in = nn < N;
+                const int t = in ? c * kChunk + (v - nn * RV) * VW : L;
+                const size_t row = static_cast<size_t>(in ? nn : 0) * L;
+                rb[j] = load_vec<T, false>(Bg + row, t, L);
+                rc[j] = load_vec<T, false>(Cg + row, t, L);
             }
 #pragma unroll
             for (int j = 0; j < kV; ++j) {
@@ -879,8 +881,9 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     __syncthreads();
     if constexpr (FUSED) {
         // this chunk's rows of the workgroup's dB and dC sums, stored whole (past the end of
-        // the sequence too: the reduce kernel reads only steps < L); the accumulators are
-        // zeroed for the chunk before
+        // the sequence too: the reduce kernel reads only steps < L) with streaming stores (the
+        // reduce kernel reads them once, after this kernel); the accumulators are zeroed for
+        // the chunk before
         float* dst = w.part + MSEL_IDX(((static_cast<size_t>(b) * cgroups + cgrp) * nch + c) *
                                            2 * N * kChunk,
                                        static_cast<size_t>(p.B) * cgroups * nch * 2 * N * kChunk);
@@ -896,8 +899,8 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 accB[o] = 0.0f;
                 accC[o] = 0.0f;
             }
-            dst[i] = vb;
-            dst[N * kChunk + i] = vc;
+            __builtin_nontemporal_store(vb, dst + i);
+            __builtin_nontemporal_store(vc, dst + N * kChunk + i);
         }
         if (c == 0) break;
         --c;
