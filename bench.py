@@ -7,7 +7,10 @@ the fused forward scan (out, final state and the state at every chunk boundary),
 backward with recomputation (all gradients): it rebuilds every state inside the chunks from
 those boundary states and runs the chunk carry backward for the adjoint.  Consecutive steps
 take consecutive copies of the inputs, from a ring of copies larger than the chip's 256 MB
-last-level cache (MALL), so that each step's forward reads its inputs from HBM.  The default
+last-level cache (MALL), so that each step's forward reads its inputs from HBM.  The timed
+steps follow an untimed clock ramp (--ramp-ms, 300 ms of the same step) and the W warmup
+steps, all back to back, so that they run at the clocks the chip holds under sustained load
+(after the setup's idle time the first steps run ~10% slower).  The default
 workload is batch 8, d_model 768 x expand 2 = 1536 channels, dstate 16, seqlen 2048, bf16
 activations with fp32 state -- the workload that runs both the forward and the backward.
 
@@ -108,6 +111,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--ramp-ms", type=float, default=300.0,
+                    help="run the step untimed for this long before the warmup steps, so that "
+                         "the GPU's clocks reach their level under sustained load")
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
@@ -277,14 +283,24 @@ def main():
             ev[2].record()
         return g
 
+    # Clock ramp: the GPU's power management raises its clocks only under sustained load; a
+    # step started from idle (setup above, or a few ms of host work between steps) runs about
+    # 10% slower than the same step among back-to-back ones.  So the step first runs untimed
+    # for ramp_ms, then the W warmup steps, then the K timed ones, all back to back.
+    ramp_steps = 0
+    t_ramp = time.perf_counter()
+    while (time.perf_counter() - t_ramp) * 1e3 < args.ramp_ms:
+        for _ in range(8):
+            step(ramp_steps)
+            ramp_steps += 1
+        torch.cuda.synchronize()
     for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
+        step(ramp_steps + k)
     evs = [new_events(5) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(args.warmup + k, evs[k])
+        step(ramp_steps + args.warmup + k, evs[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -351,6 +367,7 @@ def main():
     line = {
         "metric": METRIC, "value": float(f"{tc / (ms_per_step * 1e-3):.5g}"),
         "unit": "token*channels/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "clock_ramp": {"ms": args.ramp_ms, "steps": ramp_steps},
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         # dtype: the arithmetic type of every step (state, transitions, sums); the activations
         # are stored in io_dtype
