@@ -565,8 +565,14 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float x = dd[k] + bias;
-                const float v = SOFTPLUS ? softplus_f(x) : x;
-                dt[k] = (t0 + k < L) ? v : 0.0f;
+                dt[k] = SOFTPLUS ? softplus_f(x) : x;
+            }
+            if ((c + 1) * kChunk > L) {  // Delta = 0 past the end: identity steps
+#pragma unroll
+                for (int k = 0; k < K; ++k) dt[k] = (t0 + k < L) ? dt[k] : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
                 if constexpr (TRAP) {
                     uT[k] = uu[k];
                     dtu[k] = lm[k] * dt[k] * uu[k];
@@ -680,7 +686,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                         bb[k] = fmaf(a[k], cp[k] * (k == 0 ? bp0 : bv[k - 1]), dtu[k] * bv[k]);
                     else
                         bb[k] = dtu[k] * bv[k];
-                    h = fmaf(a[k], h, bb[k]);
+                    h = k == 0 ? bb[0] : fmaf(a[k], h, bb[k]);  // the chain from a zero state
                     cd[k] = cv[k] * dy[k];
                 }
                 // the lane's adjoint chain from a zero input on its right
@@ -881,9 +887,9 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     __syncthreads();
     if constexpr (FUSED) {
         // this chunk's rows of the workgroup's dB and dC sums, stored whole (past the end of
-        // the sequence too: the reduce kernel reads only steps < L) with streaming stores (the
-        // reduce kernel reads them once, after this kernel); the accumulators are zeroed for
-        // the chunk before
+        // the sequence too: the reduce kernel reads only steps < L); the accumulators are
+        // zeroed for the chunk before.  (Plain stores: with non-temporal ones the sums leave
+        // the last-level cache and the reduce kernel reads them from HBM, 4 us slower.)
         float* dst = w.part + MSEL_IDX(((static_cast<size_t>(b) * cgroups + cgrp) * nch + c) *
                                            2 * N * kChunk,
                                        static_cast<size_t>(p.B) * cgroups * nch * 2 * N * kChunk);
@@ -899,8 +905,8 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 accB[o] = 0.0f;
                 accC[o] = 0.0f;
             }
-            __builtin_nontemporal_store(vb, dst + i);
-            __builtin_nontemporal_store(vc, dst + N * kChunk + i);
+            dst[i] = vb;
+            dst[N * kChunk + i] = vc;
         }
         if (c == 0) break;
         --c;

@@ -138,8 +138,14 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float x = dd[k] + bias;
-                const float v = SOFTPLUS ? softplus_f(x) : x;
-                dt[k] = (t0 + k < L) ? v : 0.0f;  // Delta = 0 past the end: identity step
+                dt[k] = SOFTPLUS ? softplus_f(x) : x;
+            }
+            if (tile + TILE > L) {  // Delta = 0 past the end: identity steps
+#pragma unroll
+                for (int k = 0; k < K; ++k) dt[k] = (t0 + k < L) ? dt[k] : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
                 if constexpr (TRAP) {
                     const float um1 = k == 0 ? shift_up(uu[K - 1], u_last) : uu[k - 1];
                     du[k] = lm[k] * dt[k] * uu[k];
