@@ -14,6 +14,8 @@
 #include "msel.h"  // include/ is on the include path
 #include "msel_kernels.hpp"
 
+static_assert(MSEL_MAX_DSTATE == msel::kMaxN, "the kernels' state limit is the boundary's");
+
 namespace {
 
 constexpr int64_t kMaxSeq = MSEL_MAX_SEQLEN;

@@ -44,6 +44,8 @@ inline int device_compute_units() {
 // Chunk length of the scan: 64 lanes x 8 time steps.  chunk_states hold the state before
 // every multiple of it; the backward and the chunk-carry pass work one chunk per wave step.
 constexpr int kChunk = 512;
+// The most states per channel (the boundary's MSEL_MAX_DSTATE).
+constexpr int kMaxN = 16;
 
 struct ScanParams {
     int B, D, N, L, nchunks;

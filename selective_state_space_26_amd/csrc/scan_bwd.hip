@@ -46,7 +46,6 @@
 
 namespace msel {
 
-constexpr int kMaxN = 16;
 constexpr int kSumWaves = 4;
 constexpr int kMainWaves = 12;  // 3 per SIMD: the main kernel needs ~160 VGPRs
 // The trapezoidal variant keeps ~50 more values per lane (the previous and next step's input

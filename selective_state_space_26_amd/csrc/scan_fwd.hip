@@ -61,6 +61,12 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
     constexpr int kFwdWaves = fwd_waves<T, TRAP>();
     using Stage = TileStage<T, K, 2, 64 * kFwdWaves, VEC>;  // rows: B, C of one state
     __shared__ f32x4 stage[STAGE ? 2 : 1][STAGE ? Stage::kWords : 1];
+    // Per wavefront, one float per state: A' (row 0), the state carried into the tile (row
+    // 1) and the states entering the tile's chunks (rows 2 ..).  A state's value is read by
+    // address (one broadcast LDS read) and written by the one lane that has it, instead of a
+    // v_readlane / v_writelane per state.
+    constexpr int kCpt = 64 * K / kChunk;  // chunks per tile
+    __shared__ float cells[kFwdWaves][2 + kCpt][kMaxN];
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -90,13 +96,14 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
     const float Dd = p.Dv ? p.Dv[MSEL_IDX(d, p.D)] : 0.0f;
     [[maybe_unused]] const size_t DN = static_cast<size_t>(p.D) * N;
     [[maybe_unused]] const size_t BDN = static_cast<size_t>(p.B) * DN;
-    // lane n holds A[d, n] * log2(e): one vector load, read per state with readlane
-    const float Av =
-        (lane < N) ? p.A[MSEL_IDX(static_cast<size_t>(d) * N + lane, DN)] * kLog2e : 0.0f;
-
-    float carry = 0.0f;  // lane n: state h_n entering the current tile
-    if (p.h0 != nullptr && lane < N)
-        carry = p.h0[MSEL_IDX(static_cast<size_t>(ch) * N + lane, BDN)];
+    // A[d, n] * log2(e) and the state h_n entering the current tile, from lane n
+    float* const cA = cells[wave][0];
+    float* const cH = cells[wave][1];
+    if (lane < N) {
+        cA[lane] = p.A[MSEL_IDX(static_cast<size_t>(d) * N + lane, DN)] * kLog2e;
+        cH[lane] = p.h0 != nullptr ? p.h0[MSEL_IDX(static_cast<size_t>(ch) * N + lane, BDN)]
+                                   : 0.0f;
+    }
     // TRAP: the step before the tile: its u (wave-uniform) and B (lane n: state n)
     float u_last = 0.0f, B_last = 0.0f;
     if constexpr (TRAP) {
@@ -158,13 +165,10 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
             }
             if constexpr (TRAP) u_last = readlane(uu[K - 1], 63);
         }
-        // States entering the lanes that start a chunk: gathered into lane-distributed
-        // registers (lane n = state n), one per chunk of the tile, and stored after the state
-        // loop -- a store inside the loop would make every later load wait for it.
-        constexpr int kCpt = TILE / kChunk;  // chunks per tile
-        float csv[kCpt];
-#pragma unroll
-        for (int q = 0; q < kCpt; ++q) csv[q] = 0.0f;
+        // States entering the lanes that start a chunk: gathered in the wavefront's cells
+        // (row 2 + chunk of the tile) and stored after the state loop -- a store inside the
+        // loop would make every later load wait for it.
+        static_assert(TILE == kCpt * kChunk, "chunks per tile");
 
         for (int n = 0; n < N; ++n) {
             // the next state's rows (the next tile's first state after the last one); one
@@ -173,7 +177,8 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
             const int t_next = (n + 1 < N) ? tile : tile + TILE;
             const bool more = STAGE && t_next < L;
             if (more) st.load(tid, rows(n_next), t_next, L);
-            const float An = readlane(Av, n);
+            const float An = cA[MSEL_IDX(n, kMaxN)];
+            const float cn = cH[MSEL_IDX(n, kMaxN)];  // read early: used right after the scan
             float a[K], bb[K], bc[K];
             if constexpr (STAGE) Stage::read(stage[buf], 0, lane, bc);
             else load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(n, N)) * L, t0, L, bc);
@@ -195,13 +200,11 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
             float P = exp2_hw(An * sum_dt);
             float S = h;
             scan_fwd_fused(P, S);
-            const float cn = readlane(carry, n);
             const float Q = fmaf(P, cn, S);       // state after the lane's last step
             const float hin = shift_up(Q, cn);    // state entering the lane
-            carry = writelane(readlane(Q, 63), n, carry);
-#pragma unroll
-            for (int q = 0; q < kCpt; ++q)
-                csv[q] = writelane(readlane(hin, q * (kChunk / K)), n, csv[q]);
+            if (lane == 63) cH[MSEL_IDX(n, kMaxN)] = Q;
+            if (lane % (kChunk / K) == 0)  // the first lane of a chunk
+                cells[wave][MSEL_IDX(2 + lane / (kChunk / K), 2 + kCpt)][MSEL_IDX(n, kMaxN)] = hin;
 
             if constexpr (STAGE) Stage::read(stage[buf], 1, lane, bc);
             else load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(MSEL_IDX(n, N)) * L, t0, L, bc);
@@ -230,12 +233,12 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
                 const int cidx = tile / kChunk + q;
                 if (cidx < p.nchunks)
                     p.chunk_states[MSEL_IDX((static_cast<size_t>(ch) * p.nchunks + cidx) * N + lane,
-                                            BDN * p.nchunks)] = csv[q];
+                                            BDN * p.nchunks)] = cells[wave][2 + q][lane];
             }
         }
     }
     if (active && p.final_state != nullptr && lane < N)
-        p.final_state[MSEL_IDX(static_cast<size_t>(ch) * N + lane, BDN)] = carry;
+        p.final_state[MSEL_IDX(static_cast<size_t>(ch) * N + lane, BDN)] = cH[lane];
 }
 
 // Recurrent mode (page 3, recurrent mode; page 1 and 2: the state kept in a cache): one
