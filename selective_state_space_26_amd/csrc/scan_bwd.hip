@@ -327,8 +327,13 @@ __host__ __device__ constexpr size_t main_lds_bytes_max(int W) {
     for (int n = 1; n <= kMaxN; ++n) m = main_lds_bytes(n, W) > m ? main_lds_bytes(n, W) : m;
     return m;
 }
-static_assert(main_lds_bytes_max(kMainWaves) + kMaxRingFlags * sizeof(int) <= 160 * 1024 &&
-                  main_lds_bytes_max(kTrapWaves) + kMaxRingFlags * sizeof(int) <= 160 * 1024,
+// static LDS of the main kernel besides the dynamic part: ring flags, per-wave cells and
+// carries
+__host__ __device__ constexpr size_t main_static_lds_bytes(int W) {
+    return kMaxRingFlags * sizeof(int) + static_cast<size_t>(W) * kMaxN * (16 + 4);
+}
+static_assert(main_lds_bytes_max(kMainWaves) + main_static_lds_bytes(kMainWaves) <= 160 * 1024 &&
+                  main_lds_bytes_max(kTrapWaves) + main_static_lds_bytes(kTrapWaves) <= 160 * 1024,
               "main kernel LDS exceeds a compute unit's 160 KB");
 static_assert(kMainWaves + kMaxN - 1 <= kMaxRingFlags, "ring flags do not fit");
 
@@ -385,6 +390,11 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     float* dAs = BCs + 2 * N * kChunk + wave * N * kDaQuads;  // this wave's dA partials
     float* Bm1 = BCs + 2 * N * kChunk + W * N * kDaQuads;     // TRAP: B at step c*T - 1
     __shared__ int ring_flags[kMaxRingFlags];
+    // Per wavefront and state, the channel's A, A log2(e), H_c and G_c (written once per
+    // channel by lane n, read per step with one broadcast LDS read instead of v_readlane's),
+    // and FUSED: the carry into the chunk before (written per step by the lane that has it).
+    __shared__ f32x4 cells[W][kMaxN];
+    __shared__ float gnext[FUSED ? W : 1][kMaxN];
     [[maybe_unused]] const size_t BD = static_cast<size_t>(p.B) * p.D;
     [[maybe_unused]] const size_t DN = static_cast<size_t>(p.D) * N;
     for (int i = tid; i < 2 * groups * tile; i += 64 * W) acc[i] = 0.0f;
@@ -528,7 +538,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
             Gv = c + 1 < nch ? load_lane(w.G + MSEL_IDX(ch, BD) * N, N, lane) : 0.0f;
         else
             Gv = (lane < N) ? w.G[MSEL_IDX(hg + lane, BD * nch * N)] : 0.0f;
-        float Gnext = 0.0f;  // FUSED: lane n, the carry of state n into the chunk before
+        if (lane < N) cells[wave][lane] = f32x4{Av, Av * kLog2e, Hv, Gv};
 
         int n = rot;  // state of step 0
 
@@ -611,6 +621,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
         // for dz and the next channel, and finishes dz, which needs y summed over every state.
         auto step = [&](const bool last) __attribute__((always_inline)) {
             const int nc = n;
+            const f32x4 cell = cells[wave][MSEL_IDX(nc, kMaxN)];  // A, A log2(e), H_c, G_c
             float bv[K], cv[K];
             {
                 const f32x4 b0 = B4[MSEL_IDX((nc * 2) * 64 + lane, N * kChunk / 4)],
@@ -669,10 +680,10 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 float oc[K];
 #pragma unroll
                 for (int k = 0; k < K; ++k) oc[k] = sCn[k * KP];
-                const float An = readlane(Av, nc);
-                const float An2 = An * kLog2e;
-                const float Hn = readlane(Hv, nc);
-                const float Gn = readlane(Gv, nc);
+                const float An = cell[0];
+                const float An2 = cell[1];
+                const float Hn = cell[2];
+                const float Gn = cell[3];
                 // lane-local chains: states from a zero start, adjoint from a zero end
                 float a[K], bb[K], cd[K];
                 float bp0 = 0.0f;  // TRAP: B of state nc at the step before the lane's first
@@ -706,7 +717,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 // lane l receives lane l + 1's (G_c for lane 63), carried into its last step
                 const float Gl = fmaf(Pr, Gn, Sr);
                 if constexpr (FUSED)  // reversed lane 63: the adjoint leaving lane 0
-                    Gnext = writelane(readlane(Gl, 63), nc, Gnext);
+                    if (lane == 63) gnext[0][MSEL_IDX(wave * kMaxN + nc, W * kMaxN)] = Gl;
                 float lam = rev_lanes(shift_up(Gl, Gn), rev_addr);
                 float hs[K];
                 h = hin;
@@ -799,6 +810,8 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
         }
         if (!active) continue;
         if constexpr (FUSED) {  // the carry into the chunk before; after chunk 0 it is dh0
+            const float Gnext = lane < N ? gnext[0][MSEL_IDX(wave * kMaxN + lane, W * kMaxN)]
+                                         : 0.0f;
             if (c > 0)
                 store_lane(w.G + MSEL_IDX(ch, BD) * N, N, lane, Gnext);
             else if (g.dh0 != nullptr)
