@@ -444,10 +444,14 @@ __device__ __forceinline__ float rev_lanes(float v, int rev_addr) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(rev_addr, __builtin_bit_cast(int, v)));
 }
 
-// Sum over each group of four consecutive lanes (every lane of the group gets it).
+// Sum over each group of four consecutive lanes (every lane of the group gets it): two DPP
+// adds (the wait states before each DPP read of a VGPR written just before are the s_nops).
 __device__ __forceinline__ float quad_sum(float v) {
-    v += dpp<0xB1, 0xf>(0.0f, v);  // quad_perm [1,0,3,2]
-    v += dpp<0x4E, 0xf>(0.0f, v);  // quad_perm [2,3,0,1]
+    asm("s_nop 1\n"
+        "v_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+        "s_nop 1\n"
+        "v_add_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+        : "+v"(v));
     return v;
 }
 

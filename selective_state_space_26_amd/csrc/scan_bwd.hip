@@ -301,8 +301,9 @@ __global__ __launch_bounds__(256) void bwd_link_kernel(ScanParams p, GradParams 
 //  * dB and dC accumulators [2 tensors][group][n][k][65] floats: the padded stride 65 keeps
 //    both the per-lane updates (consecutive lanes) and the flush (consecutive time steps)
 //    free of bank conflicts;
-//  * B and C of the workgroup's (batch row, chunk) as fp32, [2 tensors][n][2][64 lanes][4]:
-//    lane l's 8 steps are two 16-byte vectors, consecutive lanes adjacent (conflict-free);
+//  * B and C of the workgroup's (batch row, chunk) as fp32, [n][2 tensors][2][64 lanes][4]:
+//    lane l's 8 steps are two 16-byte vectors, consecutive lanes adjacent (conflict-free), and
+//    a state's four vectors per lane sit at constant offsets from one address;
 //  * per-wave dA partials [wave][n][16]: sums over groups of four lanes, per state;
 //  * kMaxN floats: B of every state at the step before the chunk (trapezoidal variant);
 //  * (static) one int per (group, state): 1 + the global step of the last completed update
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     const int tile = N * K * KP;             // floats per (tensor, group)
     float* accB = acc;
     float* accC = acc + groups * tile;
-    float* BCs = acc + 2 * groups * tile;                   // B rows, then C rows
+    float* BCs = acc + 2 * groups * tile;                   // B and C rows, by state
     float* dAs = BCs + 2 * N * kChunk + wave * N * kDaQuads;  // this wave's dA partials
     float* Bm1 = BCs + 2 * N * kChunk + W * N * kDaQuads;     // TRAP: B at step c*T - 1
     __shared__ int ring_flags[kMaxRingFlags];
@@ -403,8 +404,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
     for (;;) {  // FUSED: chunks nch-1 down to 0; otherwise the one chunk c
     const int t0 = c * kChunk + lane * K;
     const int rev_addr = (63 - lane) << 2;
-    const f32x4* __restrict__ B4 = reinterpret_cast<const f32x4*>(BCs);
-    const f32x4* __restrict__ C4 = reinterpret_cast<const f32x4*>(BCs + N * kChunk);
+    const f32x4* __restrict__ BC4 = reinterpret_cast<const f32x4*>(BCs);
     const T* __restrict__ gu = static_cast<const T*>(p.u);
     const T* __restrict__ gd = static_cast<const T*>(p.delta);
     const T* __restrict__ gg_ = static_cast<const T*>(g.dout);
@@ -464,11 +464,11 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 unpack_vec<T, VW>(rb[j], 0, fb);
                 unpack_vec<T, VW>(rc[j], 0, fc);
 #pragma unroll
-                for (int q = 0; q < VW / 4; ++q) {  // words (nn, (tl % K) / 4 + q) of lane tl / K
-                    const int o = MSEL_IDX((nn * 2 + (tl % K) / 4 + q) * 64 + tl / K, N * kChunk / 4);
+                for (int q = 0; q < VW / 4; ++q) {  // words (nn, B, (tl % K) / 4 + q) of lane tl / K
+                    const int o =
+                        MSEL_IDX((nn * 4 + (tl % K) / 4 + q) * 64 + tl / K, N * kChunk / 2 - 128);
                     BCs4[o] = f32x4{fb[4 * q], fb[4 * q + 1], fb[4 * q + 2], fb[4 * q + 3]};
-                    BCs4[N * kChunk / 4 + o] = f32x4{fc[4 * q], fc[4 * q + 1], fc[4 * q + 2],
-                                                     fc[4 * q + 3]};
+                    BCs4[o + 128] = f32x4{fc[4 * q], fc[4 * q + 1], fc[4 * q + 2], fc[4 * q + 3]};
                 }
             }
         } else {
@@ -481,10 +481,10 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                     vb = Elem<T>::load1(Bg + static_cast<size_t>(nn) * L + t);
                     vc = Elem<T>::load1(Cg + static_cast<size_t>(nn) * L + t);
                 }
-                const int o = MSEL_IDX(((nn * 2 + (tl % K) / 4) * 64 + tl / K) * 4 + tl % 4,
-                                       N * kChunk);
+                const int o = MSEL_IDX(((nn * 4 + (tl % K) / 4) * 64 + tl / K) * 4 + tl % 4,
+                                       2 * N * kChunk - 512);
                 BCs[o] = vb;
-                BCs[N * kChunk + o] = vc;
+                BCs[o + 512] = vc;  // C: two words of 64 lanes further
             }
         }
         if constexpr (TRAP) {
@@ -624,10 +624,9 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
             const f32x4 cell = cells[wave][MSEL_IDX(nc, kMaxN)];  // A, A log2(e), H_c, G_c
             float bv[K], cv[K];
             {
-                const f32x4 b0 = B4[MSEL_IDX((nc * 2) * 64 + lane, N * kChunk / 4)],
-                            b1 = B4[MSEL_IDX((nc * 2 + 1) * 64 + lane, N * kChunk / 4)];
-                const f32x4 c0 = C4[MSEL_IDX((nc * 2) * 64 + lane, N * kChunk / 4)],
-                            c1 = C4[MSEL_IDX((nc * 2 + 1) * 64 + lane, N * kChunk / 4)];
+                // state nc's vectors: B steps 0-3 and 4-7, then C's, 64 words apart
+                const f32x4* bc = BC4 + MSEL_IDX(nc * 256 + lane, N * kChunk / 2 - 192);
+                const f32x4 b0 = bc[0], b1 = bc[64], c0 = bc[128], c1 = bc[192];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     bv[q] = b0[q];
