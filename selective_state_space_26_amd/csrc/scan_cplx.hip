@@ -56,18 +56,22 @@ __global__ __launch_bounds__(256) void scan_cplx_fwd_kernel(ScanParams p) {
     const T* __restrict__ Cb = static_cast<const T*>(p.Cm) + static_cast<size_t>(b) * N * L;
     const float bias = p.bias ? p.bias[MSEL_IDX(d, p.D)] : 0.0f;
     const float Dd = p.Dv ? p.Dv[MSEL_IDX(d, p.D)] : 0.0f;
-    // lane 2j: A_re * log2(e) (for exp2), lane 2j+1: A_im / (2 pi) (revolutions)
-    float Av = 0.0f;
-    if (lane < N) {
-        const float a = p.A[MSEL_IDX(static_cast<size_t>(d) * N + lane, static_cast<size_t>(p.D) * N)];
-        Av = (lane & 1) ? a * kInv2Pi : a * kLog2e;
-    }
-    float carry = 0.0f;  // lane n: component n of the state entering the tile
-    if (p.h0 != nullptr && lane < N) carry = p.h0[MSEL_IDX(static_cast<size_t>(ch) * N + lane, BDN)];
-
     constexpr int TILE = 64 * K;
     static_assert(TILE % kChunk == 0, "a tile must hold whole chunks");
     constexpr int kCpt = TILE / kChunk;
+    // Per wavefront, one float per state component: A (row 0; component 2j: A_re * log2(e)
+    // for exp2, 2j+1: A_im / (2 pi) in revolutions), the state entering the tile (row 1) and
+    // the states entering the tile's chunks (rows 2 ..).  Read by address (broadcast LDS reads)
+    // and written by the one lane that has the value, instead of v_readlane / v_writelane.
+    __shared__ float cells[4][2 + kCpt][kMaxN];
+    float* const cA = cells[wave][0];
+    float* const cH = cells[wave][1];
+    if (lane < N) {
+        const float a = p.A[MSEL_IDX(static_cast<size_t>(d) * N + lane, static_cast<size_t>(p.D) * N)];
+        cA[lane] = (lane & 1) ? a * kInv2Pi : a * kLog2e;
+        cH[lane] = p.h0 != nullptr ? p.h0[MSEL_IDX(static_cast<size_t>(ch) * N + lane, BDN)] : 0.0f;
+    }
+
     for (int tile = 0; tile < L; tile += TILE) {
         const int t0 = tile + lane * K;
         float dt[K], du[K], y[K];
@@ -86,12 +90,10 @@ __global__ __launch_bounds__(256) void scan_cplx_fwd_kernel(ScanParams p) {
                 sum_dt += dt[k];
             }
         }
-        float csv[kCpt];
-#pragma unroll
-        for (int q = 0; q < kCpt; ++q) csv[q] = 0.0f;
-
         for (int n = 0; n < N; n += 2) {
-            const float Ar = readlane(Av, n), Ai = readlane(Av, n + 1);
+            const float Ar = cA[MSEL_IDX(n, kMaxN - 1)], Ai = cA[MSEL_IDX(n, kMaxN - 1) + 1];
+            // the state entering the tile, read early: used right after the scan
+            const float cr = cH[MSEL_IDX(n, kMaxN - 1)], ci = cH[MSEL_IDX(n, kMaxN - 1) + 1];
             float ar[K], ai[K], p1[K], p2[K];
             load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(n, N)) * L, t0, L, p1);
             load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(n + 1, N)) * L, t0, L, p2);
@@ -112,17 +114,18 @@ __global__ __launch_bounds__(256) void scan_cplx_fwd_kernel(ScanParams p) {
             const float r = sum_dt * Ai;
             float Pr = e * cos_rev(r), Pi = e * sin_rev(r), Sr = h1, Si = h2;
             cscan(Pr, Pi, Sr, Si);
-            const float cr = readlane(carry, n), ci = readlane(carry, n + 1);
             // state after the lane's last step, and the state entering the lane
             const float Qr = fmaf(Pr, cr, fmaf(-Pi, ci, Sr));
             const float Qi = fmaf(Pr, ci, fmaf(Pi, cr, Si));
             const float hr = shift_up(Qr, cr), hi = shift_up(Qi, ci);
-            carry = writelane(readlane(Qr, 63), n, carry);
-            carry = writelane(readlane(Qi, 63), n + 1, carry);
-#pragma unroll
-            for (int q = 0; q < kCpt; ++q) {
-                csv[q] = writelane(readlane(hr, q * (kChunk / K)), n, csv[q]);
-                csv[q] = writelane(readlane(hi, q * (kChunk / K)), n + 1, csv[q]);
+            if (lane == 63) {
+                cH[MSEL_IDX(n, kMaxN - 1)] = Qr;
+                cH[MSEL_IDX(n, kMaxN - 1) + 1] = Qi;
+            }
+            if (lane % (kChunk / K) == 0) {  // the first lane of a chunk
+                float* cs = cells[wave][MSEL_IDX(2 + lane / (kChunk / K), 2 + kCpt)];
+                cs[MSEL_IDX(n, kMaxN - 1)] = hr;
+                cs[MSEL_IDX(n, kMaxN - 1) + 1] = hi;
             }
 
             float c1[K], c2[K];
@@ -151,12 +154,12 @@ __global__ __launch_bounds__(256) void scan_cplx_fwd_kernel(ScanParams p) {
                 const int cidx = tile / kChunk + q;
                 if (cidx < p.nchunks)
                     p.chunk_states[MSEL_IDX((static_cast<size_t>(ch) * p.nchunks + cidx) * N + lane,
-                                            BDN * p.nchunks)] = csv[q];
+                                            BDN * p.nchunks)] = cells[wave][2 + q][lane];
             }
         }
     }
     if (p.final_state != nullptr && lane < N)
-        p.final_state[MSEL_IDX(static_cast<size_t>(ch) * N + lane, BDN)] = carry;
+        p.final_state[MSEL_IDX(static_cast<size_t>(ch) * N + lane, BDN)] = cH[lane];
 }
 
 // The recurrent (decode) step: a 16-lane row per channel, lane n for state component n.  Each

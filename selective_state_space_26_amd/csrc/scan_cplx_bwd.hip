@@ -222,7 +222,8 @@ __host__ __device__ constexpr size_t ring_lds_bytes_max() {
     for (int n = 2; n <= 2 * kMaxPairs; n += 2) m = ring_lds_bytes(n) > m ? ring_lds_bytes(n) : m;
     return m;
 }
-static_assert(ring_lds_bytes_max() + kMaxRingFlags * sizeof(int) <= 160 * 1024,
+static_assert(ring_lds_bytes_max() + kMaxRingFlags * sizeof(int) +
+                      static_cast<size_t>(kRingWaves) * kMaxN * 16 <= 160 * 1024,
               "complex gradient kernel LDS exceeds a compute unit's 160 KB");
 
 // The forward composition over the 64 lanes of (P, S) and the row levels of the suffix
@@ -251,6 +252,10 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
     constexpr bool kEarlyUD = sizeof(T) == 2;
     extern __shared__ float acc[];
     __shared__ int ring_flags[kMaxRingFlags];
+    // Per wavefront and state component, the channel's A, A scaled for exp2 (Re: log2(e)) or
+    // in revolutions (Im: 1 / (2 pi)), H_c and G_c: written once per channel by lane n, read
+    // per step with broadcast LDS reads instead of v_readlane's.
+    __shared__ f32x4 ccells[kRingWaves][kMaxN];
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -342,6 +347,7 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
         const float Av = (lane < N) ? p.A[MSEL_IDX(static_cast<size_t>(dd_) * N + lane, DN)] : 0.0f;
         const float Hv = (lane < N) ? w.H[MSEL_IDX(hg + lane, BD * nch * N)] : 0.0f;
         const float Gv = (lane < N) ? w.G[MSEL_IDX(hg + lane, BD * nch * N)] : 0.0f;
+        if (lane < N) ccells[wave][lane] = f32x4{Av, Av * ((lane & 1) ? kInv2Pi : kLog2e), Hv, Gv};
 
         int jn = rot;  // pair of step 0
 
@@ -379,6 +385,9 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
         auto step = [&](const bool last) __attribute__((always_inline)) {
             const int jc = jn;
             const int n0 = 2 * jc;
+            // the pair's A, scaled A, H_c and G_c: (Re) component n0 and (Im) n0 + 1
+            const f32x4 cre = ccells[wave][MSEL_IDX(n0, kMaxN - 1)];
+            const f32x4 cim = ccells[wave][MSEL_IDX(n0, kMaxN - 1) + 1];
             float Br[K], Bi[K], Cr[K], Ci[K];
             {
                 [[maybe_unused]] const int NW = N * kChunk / 4;  // 16-byte words per tensor
@@ -447,10 +456,10 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
                     ocr[k] = sCr[k * KP];
                     oci[k] = sCi[k * KP];
                 }
-                const float ArRaw = readlane(Av, n0), AiRaw = readlane(Av, n0 + 1);
-                const float Ar = ArRaw * kLog2e, Ai = AiRaw * kInv2Pi;
-                const float Hr = readlane(Hv, n0), Hi = readlane(Hv, n0 + 1);
-                const float Gr = readlane(Gv, n0), Gi = readlane(Gv, n0 + 1);
+                const float ArRaw = cre[0], AiRaw = cim[0];
+                const float Ar = cre[1], Ai = cim[1];
+                const float Hr = cre[2], Hi = cim[2];
+                const float Gr = cre[3], Gi = cim[3];
 
                 // pass 1: transitions, the lane chain of states from zero, and the lane chain
                 // of adjoints from a zero input on the right
