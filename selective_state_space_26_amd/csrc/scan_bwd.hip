@@ -839,7 +839,6 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 const float dD_ = fmaf(sP[k], um1 - lm[k] * um1, fmaf(sB[k], lm[k] * uT[k], sgA[k]));
                 o2[k] = dD_ * dsp;                                                       // ddelta
                 o3[k] = dt[k] * fmaf(uT[k], sB[k], -um1 * sP[k]);                         // dlam
-                db_part += (t0 + k < L) ? o2[k] : 0.0f;
             }
             store_k<T, K, VEC>(static_cast<T*>(g.dlam) + row, t0, L, o3);
             // the u_prev term of h_0: (1 - lam_0) Delta_0 sum_n lam_0 a_0 B_prev
@@ -853,8 +852,16 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 const float dsp = SOFTPLUS ? softplus_grad_f(xs[k], dt[k]) : 1.0f;
                 o1[k] = fmaf(sB[k], dt[k], dy[k] * Dd);            // du
                 o2[k] = fmaf(sB[k], uu[k], sgA[k]) * dsp;         // ddelta
-                db_part += (t0 + k < L) ? o2[k] : 0.0f;
             }
+        }
+        // dbias sums the chunk's ddelta; steps past the end are masked only in a chunk that
+        // reaches past it
+        if ((c + 1) * kChunk > L) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) db_part += (t0 + k < L) ? o2[k] : 0.0f;
+        } else {
+#pragma unroll
+            for (int k = 0; k < K; ++k) db_part += o2[k];
         }
         store_k<T, K, VEC>(static_cast<T*>(g.du) + row, t0, L, o1);
         store_k<T, K, VEC>(static_cast<T*>(g.ddelta) + row, t0, L, o2);
