@@ -638,18 +638,18 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
             if (!last) {
                 n = (n + 1 == N) ? 0 : n + 1;
             } else {
+                // no branches around these loads: for a channel that is not there they start
+                // past the row's end (zeros, no memory access), so that the waits for them
+                // count exactly the loads issued after them
                 if constexpr (HAS_Z) {
-                    if (active) {
-                        load_raw<T, K, VEC>(gz + row, t0, L, cz);
-                        load_raw<T, K, VEC>(gg_ + row, t0, L, cg);
-                    }
+                    load_raw<T, K, VEC>(gz + row, active ? t0 : L, L, cz);
+                    load_raw<T, K, VEC>(gg_ + row, active ? t0 : L, L, cg);
                 }
                 if constexpr (kEarlyUD) {
-                    if (next_active) {
-                        load_raw<T, K, VEC>(gu + row_next, t0, L, ru);
-                        load_raw<T, K, VEC>(gd + row_next, t0, L, rd);
-                        if constexpr (TRAP) load_raw<T, K, VEC>(gl + row_next, t0, L, rl);
-                    }
+                    const int tn = next_active ? t0 : L;
+                    load_raw<T, K, VEC>(gu + row_next, tn, L, ru);
+                    load_raw<T, K, VEC>(gd + row_next, tn, L, rd);
+                    if constexpr (TRAP) load_raw<T, K, VEC>(gl + row_next, tn, L, rl);
                 }
             }
             // wait until the previous update of state nc (step gstep - kp) is complete
@@ -797,34 +797,44 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
         for (int j = 0; j + 1 < N; ++j) step(false);
         step(true);
 
-        // the rest of the next channel's inputs, in flight while this one is finished
-        if (next_active) {
-            if constexpr (!kEarlyUD) {
-                load_raw<T, K, VEC>(gu + row_next, t0, L, ru);
-                load_raw<T, K, VEC>(gd + row_next, t0, L, rd);
-                if constexpr (TRAP) load_raw<T, K, VEC>(gl + row_next, t0, L, rl);
+        // this channel's delta (for the softplus derivative) and u again, for du and ddelta
+        // (its rows, still in L2: one load costs fewer instructions than keeping them), issued
+        // before the next channel's loads so that waiting for them does not wait for those
+        if constexpr (FUSED) {  // the carry into the chunk before; after chunk 0 it is dh0
+            if (active) {
+                const float Gnext =
+                    lane < N ? gnext[0][MSEL_IDX(wave * kMaxN + lane, W * kMaxN)] : 0.0f;
+                if (c > 0)
+                    store_lane(w.G + MSEL_IDX(ch, BD) * N, N, lane, Gnext);
+                else if (g.dh0 != nullptr)
+                    store_lane(g.dh0 + MSEL_IDX(ch, BD) * N, N, lane, Gnext);
             }
-            load_raw<T, K, VEC>(gg_ + row_next, t0, L, rg);
-            if constexpr (HAS_Z) load_raw<T, K, VEC>(gz + row_next, t0, L, rz);
+        }
+        // (as in the last step, no branches around the loads below)
+        [[maybe_unused]] Raw<T, K> rxs, ruu;
+        if constexpr (SOFTPLUS) load_raw<T, K, VEC>(gd + row, active ? t0 : L, L, rxs);
+        if constexpr (!TRAP) load_raw<T, K, VEC>(gu + row, active ? t0 : L, L, ruu);
+        asm volatile("" ::: "memory");  // keep them ahead of the loads below
+        // the rest of the next channel's inputs, in flight while this one is finished
+        {
+            const int tn = next_active ? t0 : L;
+            if constexpr (!kEarlyUD) {
+                load_raw<T, K, VEC>(gu + row_next, tn, L, ru);
+                load_raw<T, K, VEC>(gd + row_next, tn, L, rd);
+                if constexpr (TRAP) load_raw<T, K, VEC>(gl + row_next, tn, L, rl);
+            }
+            load_raw<T, K, VEC>(gg_ + row_next, tn, L, rg);
+            if constexpr (HAS_Z) load_raw<T, K, VEC>(gz + row_next, tn, L, rz);
         }
         if (!active) continue;
-        if constexpr (FUSED) {  // the carry into the chunk before; after chunk 0 it is dh0
-            const float Gnext = lane < N ? gnext[0][MSEL_IDX(wave * kMaxN + lane, W * kMaxN)]
-                                         : 0.0f;
-            if (c > 0)
-                store_lane(w.G + MSEL_IDX(ch, BD) * N, N, lane, Gnext);
-            else if (g.dh0 != nullptr)
-                store_lane(g.dh0 + MSEL_IDX(ch, BD) * N, N, lane, Gnext);
-        }
 
         // du and ddelta.  With the softplus, ddelta = dDelta * sigmoid(delta + bias), formed
-        // from delta + bias and Delta (softplus_grad_f); delta, and u, are read again (this
-        // channel's rows, still in L2): one load costs fewer instructions than keeping them.
+        // from delta + bias and Delta (softplus_grad_f).
         float o1[K], o2[K];
         float db_part = 0.0f;
         float xs[SOFTPLUS ? K : 1];  // delta + bias
         if constexpr (SOFTPLUS) {
-            load_k_cached<T, K, VEC>(gd + row, t0, L, xs);
+            unpack(rxs, xs);
 #pragma unroll
             for (int k = 0; k < K; ++k) xs[k] += bias;
         }
@@ -846,7 +856,7 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 g.du_prev[ch] = (dt[0] - lm[0] * dt[0]) * sP[0];
         } else {
             float uu[K];
-            load_k_cached<T, K, VEC>(gu + row, t0, L, uu);
+            unpack(ruu, uu);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float dsp = SOFTPLUS ? softplus_grad_f(xs[k], dt[k]) : 1.0f;
