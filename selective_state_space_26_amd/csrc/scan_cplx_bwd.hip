@@ -414,17 +414,16 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
             if (!last) {
                 jn = (jn + 1 == J) ? 0 : jn + 1;
             } else {
+                // no branches around these loads: for a channel that is not there they start
+                // past the row's end (zeros, no memory access), so that the waits for them
+                // count exactly the loads issued after them
                 if constexpr (HAS_Z) {
-                    if (active) {
-                        load_raw<T, K, VEC>(gz + row, t0, L, cz);
-                        load_raw<T, K, VEC>(gg_ + row, t0, L, cg);
-                    }
+                    load_raw<T, K, VEC>(gz + row, active ? t0 : L, L, cz);
+                    load_raw<T, K, VEC>(gg_ + row, active ? t0 : L, L, cg);
                 }
                 if constexpr (kEarlyUD) {
-                    if (next_active) {
-                        load_raw<T, K, VEC>(gu + row_next, t0, L, ru);
-                        load_raw<T, K, VEC>(gd + row_next, t0, L, rd);
-                    }
+                    load_raw<T, K, VEC>(gu + row_next, next_active ? t0 : L, L, ru);
+                    load_raw<T, K, VEC>(gd + row_next, next_active ? t0 : L, L, rd);
                 }
             }
             // wait until the previous update of pair jc (one step earlier) is complete
@@ -597,25 +596,33 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
         for (int q = 0; q + 1 < J; ++q) step(false);
         step(true);
 
+        // this channel's u and delta again (its rows, still in L2), issued before the next
+        // channel's loads so that waiting for them does not wait for those (and, as in the last
+        // step, without branches)
+        Raw<T, K> ruu;
+        [[maybe_unused]] Raw<T, K> rxs;
+        load_raw<T, K, VEC>(gu + row, active ? t0 : L, L, ruu);
+        if constexpr (SOFTPLUS) load_raw<T, K, VEC>(gd + row, active ? t0 : L, L, rxs);
+        asm volatile("" ::: "memory");  // keep them ahead of the loads below
         // the rest of the next channel's inputs, in flight while this one is finished
-        if (next_active) {
+        {
+            const int tn = next_active ? t0 : L;
             if constexpr (!kEarlyUD) {
-                load_raw<T, K, VEC>(gu + row_next, t0, L, ru);
-                load_raw<T, K, VEC>(gd + row_next, t0, L, rd);
+                load_raw<T, K, VEC>(gu + row_next, tn, L, ru);
+                load_raw<T, K, VEC>(gd + row_next, tn, L, rd);
             }
-            load_raw<T, K, VEC>(gg_ + row_next, t0, L, rg);
-            if constexpr (HAS_Z) load_raw<T, K, VEC>(gz + row_next, t0, L, rz);
+            load_raw<T, K, VEC>(gg_ + row_next, tn, L, rg);
+            if constexpr (HAS_Z) load_raw<T, K, VEC>(gz + row_next, tn, L, rz);
         }
         if (!active) continue;
 
-        // du, ddelta and dz.  u and delta are read again (this channel's rows, still in L2);
-        // with the softplus, ddelta = dDelta * sigmoid(delta + bias), formed from delta + bias
-        // and Delta (softplus_grad_f).
+        // du, ddelta and dz; with the softplus, ddelta = dDelta * sigmoid(delta + bias), formed
+        // from delta + bias and Delta (softplus_grad_f).
         float uu[K];
-        load_k_cached<T, K, VEC>(gu + row, t0, L, uu);
+        unpack(ruu, uu);
         float xs[SOFTPLUS ? K : 1];  // delta + bias
         if constexpr (SOFTPLUS) {
-            load_k_cached<T, K, VEC>(gd + row, t0, L, xs);
+            unpack(rxs, xs);
 #pragma unroll
             for (int k = 0; k < K; ++k) xs[k] += bias;
         }
