@@ -543,7 +543,9 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
         int n = rot;  // state of step 0
 
         float dt[K], dtu[K], dy[K], sB[K], sgA[K];
-        float y[HAS_Z ? K : 1];
+        // HAS_Z: y for dz, and dz's factor dout * silu'(z) = dout s (1 + z (1 - s)), formed
+        // here beside dy with the same sigmoid s
+        float y[HAS_Z ? K : 1], fz[HAS_Z ? K : 1];
         float sum_dt = 0.0f, dD_part = 0.0f;
         // TRAP: u, lambda, c_t, (1 - lam_{t+1}) Delta_{t+1}, c_{t+1}, u before the chunk, and
         // the sums of at B and of lam a B_{t-1}
@@ -592,7 +594,9 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 }
                 sum_dt += dt[k];
                 if constexpr (HAS_Z) {
-                    dy[k] = go[k] * zz[k] * sigmoid_f(zz[k]);
+                    const float sg = sigmoid_f(zz[k]);
+                    dy[k] = go[k] * zz[k] * sg;
+                    fz[k] = go[k] * sg * fmaf(zz[k], 1.0f - sg, 1.0f);
                     y[k] = Dd * uu[k];
                 } else {
                     dy[k] = go[k];
@@ -614,8 +618,6 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 }
             }
         }
-        // this channel's z and dout, fetched during the last step for dz
-        Raw<T, K> cz, cg;
 
         // One step: state nc of this channel.  `last` (the final state) also fetches inputs
         // for dz and the next channel, and finishes dz, which needs y summed over every state.
@@ -641,10 +643,6 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 // no branches around these loads: for a channel that is not there they start
                 // past the row's end (zeros, no memory access), so that the waits for them
                 // count exactly the loads issued after them
-                if constexpr (HAS_Z) {
-                    load_raw<T, K, VEC>(gz + row, active ? t0 : L, L, cz);
-                    load_raw<T, K, VEC>(gg_ + row, active ? t0 : L, L, cg);
-                }
                 if constexpr (kEarlyUD) {
                     const int tn = next_active ? t0 : L;
                     load_raw<T, K, VEC>(gu + row_next, tn, L, ru);
@@ -735,14 +733,9 @@ __global__ __launch_bounds__(64 * main_waves<TRAP>()) void bwd_main_kernel(ScanP
                 }
                 if constexpr (HAS_Z) {
                     if (last) {  // y is complete: dz = dout * y * silu'(z)
-                        float zz[K], go[K], o[K];
-                        unpack(cz, zz);
-                        unpack(cg, go);
+                        float o[K];
 #pragma unroll
-                        for (int k = 0; k < K; ++k) {
-                            const float sg = sigmoid_f(zz[k]);
-                            o[k] = go[k] * sg * fmaf(zz[k], 1.0f - sg, 1.0f) * y[k];
-                        }
+                        for (int k = 0; k < K; ++k) o[k] = fz[k] * y[k];
                         store_k<T, K, VEC>(static_cast<T*>(g.dz) + row, t0, L, o);
                     }
                 }
