@@ -352,7 +352,9 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
         int jn = rot;  // pair of step 0
 
         float dt[K], dtu[K], dy[K], sB[K], sgA[K];
-        float y[HAS_Z ? K : 1];
+        // HAS_Z: y for dz, and dz's factor dout * silu'(z) = dout s (1 + z (1 - s)), formed
+        // here beside dy with the same sigmoid s
+        float y[HAS_Z ? K : 1], fz[HAS_Z ? K : 1];
         float sum_dt = 0.0f, dD_part = 0.0f;
         {
             float uu[K], dd[K], go[K];
@@ -364,12 +366,20 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float x = dd[k] + bias;
-                const float v = SOFTPLUS ? softplus_f(x) : x;
-                dt[k] = (t0 + k < L) ? v : 0.0f;  // Delta = 0 past the end: identity step
+                dt[k] = SOFTPLUS ? softplus_f(x) : x;
+            }
+            if ((c + 1) * kChunk > L) {  // Delta = 0 past the end: identity steps
+#pragma unroll
+                for (int k = 0; k < K; ++k) dt[k] = (t0 + k < L) ? dt[k] : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
                 dtu[k] = dt[k] * uu[k];
                 sum_dt += dt[k];
                 if constexpr (HAS_Z) {
-                    dy[k] = go[k] * zz[k] * sigmoid_f(zz[k]);
+                    const float sg = sigmoid_f(zz[k]);
+                    dy[k] = go[k] * zz[k] * sg;
+                    fz[k] = go[k] * sg * fmaf(zz[k], 1.0f - sg, 1.0f);
                     y[k] = Dd * uu[k];
                 } else {
                     dy[k] = go[k];
@@ -379,8 +389,6 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
                 sgA[k] = 0.0f;
             }
         }
-        // this channel's z and dout, fetched during the last step for dz
-        Raw<T, K> cz, cg;
 
         auto step = [&](const bool last) __attribute__((always_inline)) {
             const int jc = jn;
@@ -417,10 +425,6 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
                 // no branches around these loads: for a channel that is not there they start
                 // past the row's end (zeros, no memory access), so that the waits for them
                 // count exactly the loads issued after them
-                if constexpr (HAS_Z) {
-                    load_raw<T, K, VEC>(gz + row, active ? t0 : L, L, cz);
-                    load_raw<T, K, VEC>(gg_ + row, active ? t0 : L, L, cg);
-                }
                 if constexpr (kEarlyUD) {
                     load_raw<T, K, VEC>(gu + row_next, next_active ? t0 : L, L, ru);
                     load_raw<T, K, VEC>(gd + row_next, next_active ? t0 : L, L, rd);
@@ -633,19 +637,20 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
             const float dsp = SOFTPLUS ? softplus_grad_f(xs[k], dt[k]) : 1.0f;
             o1[k] = fmaf(sB[k], dt[k], dy[k] * Dd);        // du
             o2[k] = fmaf(sB[k], uu[k], sgA[k]) * dsp;     // ddelta
-            db_part += (t0 + k < L) ? o2[k] : 0.0f;
+        }
+        if ((c + 1) * kChunk > L) {  // dbias: past-the-end steps masked in a ragged chunk only
+#pragma unroll
+            for (int k = 0; k < K; ++k) db_part += (t0 + k < L) ? o2[k] : 0.0f;
+        } else {
+#pragma unroll
+            for (int k = 0; k < K; ++k) db_part += o2[k];
         }
         store_k<T, K, VEC>(static_cast<T*>(g.du) + row, t0, L, o1);
         store_k<T, K, VEC>(static_cast<T*>(g.ddelta) + row, t0, L, o2);
         if constexpr (HAS_Z) {  // dz = dout * y * silu'(z), y complete over every pair
-            float zz[K], go[K], o3[K];
-            unpack(cz, zz);
-            unpack(cg, go);
+            float o3[K];
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const float sg = sigmoid_f(zz[k]);
-                o3[k] = go[k] * sg * fmaf(zz[k], 1.0f - sg, 1.0f) * y[k];
-            }
+            for (int k = 0; k < K; ++k) o3[k] = fz[k] * y[k];
             store_k<T, K, VEC>(static_cast<T*>(g.dz) + row, t0, L, o3);
         }
         // dA[d, n]: lane n sums the quad partials of component n (the wave's own rows: same-
