@@ -21,11 +21,11 @@
 // state are read (and, in bf16, converted to fp32) once per workgroup into a double-buffered
 // LDS stage (see the kernel) and read from there by every wavefront.
 //
-// The state never leaves registers: the carried state of all N states lives in one VGPR
-// (lane n holds h_n), so long sequences are handled by the tile loop with the state carried
-// across tiles (page 4, Appendix D: split the sequence into chunks, continue the scan from the
-// intermediate state).  Lanes at multiples of the chunk length also write the state entering
-// them to chunk_states.
+// The state never leaves the chip: the carried state of all N states lives in the
+// wavefront's LDS cells (one float per state), so long sequences are handled by the tile loop
+// with the state carried across tiles (page 4, Appendix D: split the sequence into chunks,
+// continue the scan from the intermediate state).  Lanes at multiples of the chunk length also
+// write the state entering them to chunk_states.
 //
 // TRAP: the exponential-trapezoidal rule of Mamba-3 (page 5, first bullet: the input integral
 // over a step taken from both ends of the interval, mixed by a data-dependent weight lambda):
