@@ -10,7 +10,8 @@ take consecutive copies of the inputs, from a ring of copies larger than the chi
 last-level cache (MALL), so that each step's forward reads its inputs from HBM.  The timed
 steps follow an untimed clock ramp (--ramp-ms, 300 ms of the same step) and the W warmup
 steps, all back to back, so that they run at the clocks the chip holds under sustained load
-(after the setup's idle time the first steps run ~10% slower).  The default
+(after the setup's idle time the first steps run ~10% slower).  The K timed steps carry no
+events; K more steps with HIP events around each pass give the per-kernel times.  The default
 workload is batch 8, d_model 768 x expand 2 = 1536 channels, dstate 16, seqlen 2048, bf16
 activations with fp32 state -- the workload that runs both the forward and the backward.
 
@@ -296,14 +297,25 @@ def main():
         torch.cuda.synchronize()
     for k in range(args.warmup):
         step(ramp_steps + k)
-    evs = [new_events(5) for _ in range(args.steps)]
+    # The timed steps: the host clock around K back-to-back steps with nothing else on the
+    # stream.  Then the same K steps again with HIP events around each pass and the gradient
+    # kernel, for the per-kernel figures and the roofline: each event record costs the stream
+    # ~3 us between kernels, so the events stay out of the headline steps.
+    k0 = ramp_steps + args.warmup
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(ramp_steps + args.warmup + k, evs[k])
+        step(k0 + k)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    evs = [new_events(5) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for k in range(args.steps):
+        step(k0 + args.steps + k, evs[k])
+    torch.cuda.synchronize()
+    ms_per_step_events = (time.perf_counter() - t2) * 1e3 / args.steps
     step_ms = {
         "fwd": summary([e[0].elapsed_time(e[1]) for e in evs]),
         "bwd": summary([e[1].elapsed_time(e[2]) for e in evs]),
@@ -369,6 +381,8 @@ def main():
         "unit": "token*channels/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "clock_ramp": {"ms": args.ramp_ms, "steps": ramp_steps},
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        # the same steps timed again with the per-kernel HIP events on the stream
+        "ms_per_step_with_events": round(ms_per_step_events, 4),
         # dtype: the arithmetic type of every step (state, transitions, sums); the activations
         # are stored in io_dtype
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
