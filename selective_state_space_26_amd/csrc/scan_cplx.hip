@@ -16,7 +16,8 @@
 //   scan    an inclusive 64-lane scan of the complex affine pairs (P, S): four DPP moves and
 //           eight multiply-adds per level, identity (1, 0), (0, 0) where a lane has no source;
 //   pass 2  replay from the state entering the lane, y += C . h.
-// K = 8 keeps the per-step factors of a pair (a_re, a_im and the two inputs) in registers.
+// K steps per lane: 16 for bf16 rows (half the scans per step; 142 VGPRs, 3 wavefronts per
+// SIMD), 8 for fp32 rows, whose wider loads of B and C made 16 slower there (76 VGPRs).
 // v_sin_f32 / v_cos_f32 take the angle in revolutions; it is reduced to [0, 1) first so that
 // any step size stays inside the instructions' input range.
 #include "msel_device.hpp"
@@ -238,7 +239,8 @@ hipError_t cplx_go(const ScanParams& p, hipStream_t s) {
         return hipGetLastError();
     }
     const int ch = p.B * p.D;
-    hipLaunchKernelGGL((scan_cplx_fwd_kernel<T, 8, VEC, HAS_Z, SP>),
+    constexpr int K = sizeof(T) == 2 ? 16 : 8;
+    hipLaunchKernelGGL((scan_cplx_fwd_kernel<T, K, VEC, HAS_Z, SP>),
                        dim3((ch + kWaves - 1) / kWaves), dim3(64 * kWaves), 0, s, p);
     return hipGetLastError();
 }
