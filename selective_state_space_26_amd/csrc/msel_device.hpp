@@ -566,22 +566,61 @@ __device__ __forceinline__ void cmul(float ar, float ai, float br, float bi, flo
     i = fmaf(ar, bi, ai * br);
 }
 
-// One level of a 64-lane scan of complex affine pairs: (P, S) <- (P Q, P T + S), (Q, T) the
-// pair of the DPP source lane; lanes without one take the identity (1, 0), (0, 0).
-template <int CTRL, int RM>
-__device__ __forceinline__ void cplx_level(float& Pr, float& Pi, float& Sr, float& Si) {
-    const float qr = dpp<CTRL, RM>(1.0f, Pr);
-    const float qi = dpp<CTRL, RM>(0.0f, Pi);
-    const float tr = dpp<CTRL, RM>(0.0f, Sr);
-    const float ti = dpp<CTRL, RM>(0.0f, Si);
-    const float nSr = fmaf(Pr, tr, fmaf(-Pi, ti, Sr));
-    const float nSi = fmaf(Pr, ti, fmaf(Pi, tr, Si));
-    const float nPr = fmaf(Pr, qr, -Pi * qi);
-    const float nPi = fmaf(Pr, qi, Pi * qr);
-    Pr = nPr;
-    Pi = nPi;
-    Sr = nSr;
-    Si = nSi;
+// Scans of complex affine pairs over the lanes: (P, S) <- (P Q, P T + S), (Q, T) the pair of
+// the DPP source lane, with the DPP moves fused into the arithmetic as in the real scans above
+// (a lane without a source is not written: the identity).  A level reads the source's Q and
+// T while this lane's P and S are being replaced, so it first copies S_im, P_re and P_im
+// (cs, cr, ci), then, with src0 the source lane's value:
+//   S_im += T_re P_im   S_re += T_re P_re   P_re = Q_re P_re   P_im = Q_re P_im
+//   S_im += T_im P_re   S_re -= T_im P_im   P_re -= Q_im P_im  P_im += Q_im P_re
+// S_re is read through DPP before it is written; every DPP read of a register comes at least
+// two instructions after its write (the copies lead, and the next level's DPP read of S_re
+// follows five instructions after this level's write), so no s_nop is needed.
+#define MSEL_CPLX_LEVEL(CTRL, RMASK, PR, PI, SR, SI)                                        \
+    "v_mov_b32 %[cs], %[" SI "]\n"                                                          \
+    "v_mov_b32 %[cr], %[" PR "]\n"                                                          \
+    "v_mov_b32 %[ci], %[" PI "]\n"                                                          \
+    "v_fmac_f32_dpp %[" SI "], %[" SR "], %[ci] " CTRL " row_mask:" RMASK " bank_mask:0xf\n" \
+    "v_fmac_f32_dpp %[" SR "], %[" SR "], %[cr] " CTRL " row_mask:" RMASK " bank_mask:0xf\n" \
+    "v_mul_f32_dpp %[" PR "], %[cr], %[cr] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"      \
+    "v_mul_f32_dpp %[" PI "], %[cr], %[ci] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"      \
+    "v_fmac_f32_dpp %[" SI "], %[cs], %[cr] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"     \
+    "v_fmac_f32_dpp %[" SR "], %[cs], -%[ci] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"    \
+    "v_fmac_f32_dpp %[" PR "], %[ci], -%[ci] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"    \
+    "v_fmac_f32_dpp %[" PI "], %[ci], %[cr] " CTRL " row_mask:" RMASK " bank_mask:0xf\n"
+
+// Inclusive scan over the 64 lanes, lane 0 first.
+__device__ __forceinline__ void cscan_fused(float& Pr, float& Pi, float& Sr, float& Si) {
+    float cs, cr, ci;
+    asm volatile(MSEL_CPLX_LEVEL("row_shr:1", "0xf", "Pr", "Pi", "Sr", "Si")
+                 MSEL_CPLX_LEVEL("row_shr:2", "0xf", "Pr", "Pi", "Sr", "Si")
+                 MSEL_CPLX_LEVEL("row_shr:4", "0xf", "Pr", "Pi", "Sr", "Si")
+                 MSEL_CPLX_LEVEL("row_shr:8", "0xf", "Pr", "Pi", "Sr", "Si")
+                 MSEL_CPLX_LEVEL("row_bcast:15", "0xa", "Pr", "Pi", "Sr", "Si")
+                 MSEL_CPLX_LEVEL("row_bcast:31", "0xc", "Pr", "Pi", "Sr", "Si")
+                 : [Pr] "+v"(Pr), [Pi] "+v"(Pi), [Sr] "+v"(Sr), [Si] "+v"(Si), [cs] "=&v"(cs),
+                   [cr] "=&v"(cr), [ci] "=&v"(ci));
 }
+
+// The same forward scan of (P, S) and, in one instruction stream, the suffix composition of
+// (R, T) within each 16-lane row (row_shl: each lane composes the lanes after it in its row).
+__device__ __forceinline__ void cscan2_fused(float& Pr, float& Pi, float& Sr, float& Si,
+                                             float& Rr, float& Ri, float& Tr, float& Ti) {
+    float cs, cr, ci;
+    asm volatile(MSEL_CPLX_LEVEL("row_shr:1", "0xf", "Pr", "Pi", "Sr", "Si")
+                 MSEL_CPLX_LEVEL("row_shl:1", "0xf", "Rr", "Ri", "Tr", "Ti")
+                 MSEL_CPLX_LEVEL("row_shr:2", "0xf", "Pr", "Pi", "Sr", "Si")
+                 MSEL_CPLX_LEVEL("row_shl:2", "0xf", "Rr", "Ri", "Tr", "Ti")
+                 MSEL_CPLX_LEVEL("row_shr:4", "0xf", "Pr", "Pi", "Sr", "Si")
+                 MSEL_CPLX_LEVEL("row_shl:4", "0xf", "Rr", "Ri", "Tr", "Ti")
+                 MSEL_CPLX_LEVEL("row_shr:8", "0xf", "Pr", "Pi", "Sr", "Si")
+                 MSEL_CPLX_LEVEL("row_shl:8", "0xf", "Rr", "Ri", "Tr", "Ti")
+                 MSEL_CPLX_LEVEL("row_bcast:15", "0xa", "Pr", "Pi", "Sr", "Si")
+                 MSEL_CPLX_LEVEL("row_bcast:31", "0xc", "Pr", "Pi", "Sr", "Si")
+                 : [Pr] "+v"(Pr), [Pi] "+v"(Pi), [Sr] "+v"(Sr), [Si] "+v"(Si), [Rr] "+v"(Rr),
+                   [Ri] "+v"(Ri), [Tr] "+v"(Tr), [Ti] "+v"(Ti), [cs] "=&v"(cs), [cr] "=&v"(cr),
+                   [ci] "=&v"(ci));
+}
+#undef MSEL_CPLX_LEVEL
 
 }  // namespace msel

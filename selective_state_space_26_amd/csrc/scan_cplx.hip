@@ -13,11 +13,12 @@
 // of 64*K steps, lane l holding K consecutive steps.  Per state pair:
 //   pass 1  the lane-local chain of complex affine steps from 0 -> S, and the lane's transition
 //           P = exp(A * sum Delta) in closed form (one exp, one sin, one cos);
-//   scan    an inclusive 64-lane scan of the complex affine pairs (P, S): four DPP moves and
-//           eight multiply-adds per level, identity (1, 0), (0, 0) where a lane has no source;
+//   scan    an inclusive 64-lane scan of the complex affine pairs (P, S): per level three
+//           copies and eight multiplies and multiply-adds that read the source lane through
+//           DPP (a lane without a source keeps its pair: the identity);
 //   pass 2  replay from the state entering the lane, y += C . h.
 // K steps per lane: 16 for bf16 rows (half the scans per step; 142 VGPRs, 3 wavefronts per
-// SIMD), 8 for fp32 rows, whose wider loads of B and C made 16 slower there (76 VGPRs).
+// SIMD), 8 for fp32 rows, whose wider loads of B and C made 16 slower there (86 VGPRs).
 // v_sin_f32 / v_cos_f32 take the angle in revolutions; it is reduced to [0, 1) first so that
 // any step size stays inside the instructions' input range.
 #include "msel_device.hpp"
@@ -26,16 +27,6 @@
 namespace msel {
 
 namespace {
-
-// Inclusive scan over the 64 lanes, lane 0 first.
-__device__ __forceinline__ void cscan(float& Pr, float& Pi, float& Sr, float& Si) {
-    cplx_level<kRowShr1, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowShr2, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowShr4, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowShr8, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowBcast15, 0xa>(Pr, Pi, Sr, Si);
-    cplx_level<kRowBcast31, 0xc>(Pr, Pi, Sr, Si);
-}
 
 template <typename T, int K, bool VEC, bool HAS_Z, bool SOFTPLUS>
 __global__ __launch_bounds__(256) void scan_cplx_fwd_kernel(ScanParams p) {
@@ -114,7 +105,7 @@ __global__ __launch_bounds__(256) void scan_cplx_fwd_kernel(ScanParams p) {
             const float e = exp2_hw(sum_dt * Ar);
             const float r = sum_dt * Ai;
             float Pr = e * cos_rev(r), Pi = e * sin_rev(r), Sr = h1, Si = h2;
-            cscan(Pr, Pi, Sr, Si);
+            cscan_fused(Pr, Pi, Sr, Si);
             // state after the lane's last step, and the state entering the lane
             const float Qr = fmaf(Pr, cr, fmaf(-Pi, ci, Sr));
             const float Qi = fmaf(Pr, ci, fmaf(Pi, cr, Si));

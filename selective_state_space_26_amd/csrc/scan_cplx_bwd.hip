@@ -226,22 +226,6 @@ static_assert(ring_lds_bytes_max() + kMaxRingFlags * sizeof(int) +
                       static_cast<size_t>(kRingWaves) * kMaxN * 16 <= 160 * 1024,
               "complex gradient kernel LDS exceeds a compute unit's 160 KB");
 
-// The forward composition over the 64 lanes of (P, S) and the row levels of the suffix
-// composition of (R, T), in one instruction stream (independent, so they interleave).
-__device__ __forceinline__ void cplx_scans(float& Pr, float& Pi, float& Sr, float& Si, float& Rr,
-                                           float& Ri, float& Tr, float& Ti) {
-    cplx_level<kRowShr1, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowShl1, 0xf>(Rr, Ri, Tr, Ti);
-    cplx_level<kRowShr2, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowShl2, 0xf>(Rr, Ri, Tr, Ti);
-    cplx_level<kRowShr4, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowShl4, 0xf>(Rr, Ri, Tr, Ti);
-    cplx_level<kRowShr8, 0xf>(Pr, Pi, Sr, Si);
-    cplx_level<kRowShl8, 0xf>(Rr, Ri, Tr, Ti);
-    cplx_level<kRowBcast15, 0xa>(Pr, Pi, Sr, Si);
-    cplx_level<kRowBcast31, 0xc>(Pr, Pi, Sr, Si);
-}
-
 template <typename T, bool VEC, bool HAS_Z, bool SOFTPLUS>
 __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p, GradParams g,
                                                                     CWork w, int per_wave) {
@@ -496,7 +480,7 @@ __global__ __launch_bounds__(64 * kRingWaves) void cplx_main_kernel(ScanParams p
                 float Pr = eP * cos_rev(rP), Pi = eP * sin_rev(rP), Sr = hr, Si = hi;
                 float Rr = Pr, Ri = -Pi, Tr, Ti;
                 cmul(ar[0], -ai[0], gr, gi, Tr, Ti);
-                cplx_scans(Pr, Pi, Sr, Si, Rr, Ri, Tr, Ti);
+                cscan2_fused(Pr, Pi, Sr, Si, Rr, Ri, Tr, Ti);
                 float hin_r, hin_i;  // the state entering the lane
                 {
                     float tr, ti;
