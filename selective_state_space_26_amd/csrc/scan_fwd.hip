@@ -59,7 +59,10 @@ template <typename T, int K, bool VEC, bool HAS_Z, bool SOFTPLUS, bool TRAP>
 __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(ScanParams p) {
     constexpr bool STAGE = !TRAP;
     constexpr int kFwdWaves = fwd_waves<T, TRAP>();
-    using Stage = TileStage<T, K, 2, 64 * kFwdWaves, VEC>;  // rows: B, C of one state
+    // HALVES (bf16 rows of whole vectors): the two halves of the workgroup stage the states
+    // in turn (below)
+    constexpr bool HALVES = STAGE && sizeof(T) == 2 && VEC;
+    using Stage = TileStage<T, K, 2, (HALVES ? 32 : 64) * kFwdWaves, VEC>;  // rows: B, C
     __shared__ f32x4 stage[STAGE ? 2 : 1][STAGE ? Stage::kWords : 1];
     // Per wavefront, one float per state: A' (row 0), the state carried into the tile (row
     // 1) and the states entering the tile's chunks (rows 2 ..).  A state's value is read by
@@ -117,16 +120,30 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
     constexpr int TILE = 64 * K;
     static_assert(TILE % kChunk == 0, "a tile must hold whole chunks");
 
-    Stage st(tid);
+    // Each state's rows are loaded while the state before it is computed and staged at its
+    // end.  HALVES: the two halves of the workgroup (wavefronts 0, 2 and 1, 3) stage the
+    // states in turn, by the parity of a state's place g in the walk over all tiles: a half
+    // loads a state's rows at the start of the state two before it and stages them at the end
+    // of the state just before it, so that the loads have two states' work to arrive in, with
+    // one set of loads in flight per thread.  (In fp32 a thread's share of a state is twice
+    // the registers, and the kernel would no longer fit four wavefronts per SIMD.)
+    const int par = wave & 1;
+    const int stid = HALVES ? (wave >> 1) * 64 + lane : tid;  // the thread's place in its stager
+    Stage st(stid);
     auto rows = [&](int n) {  // staged row x of state n: B (x = 0) or C (x = 1)
         return [=](int x) {
             return (x == 0 ? Bb : Cb) + static_cast<size_t>(MSEL_IDX(n, N)) * L;
         };
     };
     int buf = 0;
+    int g = 0;  // the current state's place in the walk (wave-uniform)
     if constexpr (STAGE) {
-        st.load(tid, rows(0), 0, L);
-        st.store(tid, stage[0]);
+        if (!HALVES || par == 0) {
+            st.load(stid, rows(0), 0, L);
+            st.store(stid, stage[0]);
+        } else if (N > 1 || TILE < L) {  // the second state of the walk
+            st.load(stid, rows(N > 1 ? 1 : 0), N > 1 ? 0 : TILE, L);
+        }
         __syncthreads();
     }
 
@@ -170,13 +187,22 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
         // loop would make every later load wait for it.
         static_assert(TILE == kCpt * kChunk, "chunks per tile");
 
-        for (int n = 0; n < N; ++n) {
-            // the next state's rows (the next tile's first state after the last one); one
-            // compare of scalars (an || of two compares would be carried through a VGPR)
-            const int n_next = (n + 1 < N) ? n + 1 : 0;
-            const int t_next = (n + 1 < N) ? tile : tile + TILE;
-            const bool more = STAGE && t_next < L;
-            if (more) st.load(tid, rows(n_next), t_next, L);
+        for (int n = 0; n < N; ++n, ++g) {
+            // one compare of scalars each (an || of two compares would be carried through a
+            // VGPR)
+            const bool more = STAGE && (n + 1 < N || tile + TILE < L);  // a next state
+            const bool mine = (g & 1) == par;  // HALVES: this state is staged by this half
+            if (HALVES && mine) {
+                // the rows of the state two after this one (wrapping into the next tiles)
+                int n2 = n + 2, t2 = tile;
+                while (n2 >= N) {  // at most twice (N >= 1)
+                    n2 -= N;
+                    t2 += TILE;
+                }
+                if (t2 < L) st.load(stid, rows(n2), t2, L);
+            } else if (!HALVES && more) {  // the next state's rows
+                st.load(stid, rows(n + 1 < N ? n + 1 : 0), n + 1 < N ? tile : tile + TILE, L);
+            }
             const float An = cA[MSEL_IDX(n, kMaxN)];
             const float cn = cH[MSEL_IDX(n, kMaxN)];  // read early: used right after the scan
             float a[K], bb[K], bc[K];
@@ -215,7 +241,7 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
                 y[k] = fmaf(bc[k], h, y[k]);
             }
             if constexpr (STAGE) {
-                if (more) st.store(tid, stage[buf ^ 1]);
+                if (more && (!HALVES || !mine)) st.store(stid, stage[buf ^ 1]);  // the next state
                 __syncthreads();
                 buf ^= 1;
             }
