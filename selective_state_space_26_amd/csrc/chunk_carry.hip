@@ -104,8 +104,22 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
                                     MSEL_IDX(static_cast<size_t>(b) * N + lane,
                                              static_cast<size_t>(p.B) * N));
 
+    // each chunk's u, delta (TRAP: lambda) rows are loaded while the chunk before is computed
+    Raw<T, K> ru[R], rd[R], rl[TRAP ? R : 1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        load_raw<T, K, VEC>(u[r], lane * K, L, ru[r]);
+        load_raw<T, K, VEC>(dl[r], lane * K, L, rd[r]);
+        if constexpr (TRAP) load_raw<T, K, VEC>(lm[r], lane * K, L, rl[r]);
+    }
+    // the first pair of B rows of each chunk is loaded during the chunk before
+    Raw<T, K> B1, B2;
+    load_raw<T, K, VEC>(Bb, lane * K, L, B1);
+    load_raw<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(N > 1 ? 1 : 0, N)) * L, lane * K, L, B2);
     for (int c = 0; c < p.nchunks; ++c) {
         const int t0 = c * kChunk + lane * K;
+        // the next chunk's rows; after the last chunk past the row's end (zeros, no access)
+        const int tn = (c + 1 < p.nchunks) ? t0 + kChunk : L;
         // F'_t (sum of Delta over the chunk's steps after t), each step's input weight w_t
         // (Delta u; TRAP: g u + c_{t+1}), and the chunk's total
         float Fs[R][K], w[R][K], total[R];
@@ -117,9 +131,12 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
                     ((static_cast<size_t>(b) * p.D + dch[r]) * p.nchunks + c) * N + lane,
                     BDN * p.nchunks)] = carry[r];
             float uu[K], dd[K], ll[TRAP ? K : 1];
-            load_k_cached<T, K, VEC>(u[r], t0, L, uu);
-            load_k_cached<T, K, VEC>(dl[r], t0, L, dd);
-            if constexpr (TRAP) load_k_cached<T, K, VEC>(lm[r], t0, L, ll);
+            unpack(ru[r], uu);
+            unpack(rd[r], dd);
+            if constexpr (TRAP) unpack(rl[r], ll);
+            load_raw<T, K, VEC>(u[r], tn, L, ru[r]);
+            load_raw<T, K, VEC>(dl[r], tn, L, rd[r]);
+            if constexpr (TRAP) load_raw<T, K, VEC>(lm[r], tn, L, rl[r]);
             float dt[K];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
@@ -162,19 +179,20 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ScanParams p) {
 #pragma unroll
         for (int r = 0; r < R; ++r) S[r] = 0.0f;
         float B_next = B_last;  // TRAP: B of every state at this chunk's last step
-        Raw<T, K> B1, B2;
-        load_raw<T, K, VEC>(Bb, t0, L, B1);
-        load_raw<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(N > 1 ? 1 : 0, N)) * L, t0, L, B2);
         for (int n = 0; n < N; n += 2) {
             const int n2 = (n + 1 < N) ? n + 1 : n;
             float bv1[K], bv2[K];
             unpack(B1, bv1);
             unpack(B2, bv2);
-            if (n + 2 < N) {
-                load_raw<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(n + 2, N)) * L, t0, L, B1);
-                load_raw<T, K, VEC>(
-                    Bb + static_cast<size_t>(MSEL_IDX(n + 3 < N ? n + 3 : n + 2, N)) * L, t0, L,
-                    B2);
+            {
+                // the next pair's rows: of this chunk, or after the last pair the next chunk's
+                // first (past the row's end after the last chunk: zeros, no access)
+                const bool in = n + 2 < N;
+                const int na = in ? n + 2 : 0;
+                const int nb = in ? (n + 3 < N ? n + 3 : n + 2) : (N > 1 ? 1 : 0);
+                const int tb = in ? t0 : tn;
+                load_raw<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(na, N)) * L, tb, L, B1);
+                load_raw<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(nb, N)) * L, tb, L, B2);
             }
             if constexpr (TRAP) {
                 B_next = writelane(readlane(bv1[K - 1], 63), n, B_next);
