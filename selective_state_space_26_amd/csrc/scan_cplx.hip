@@ -87,6 +87,11 @@ __global__ __launch_bounds__(256) void scan_cplx_fwd_kernel(ScanParams p) {
             // the state entering the tile, read early: used right after the scan
             const float cr = cH[MSEL_IDX(n, kMaxN - 1)], ci = cH[MSEL_IDX(n, kMaxN - 1) + 1];
             float ar[K], ai[K], p1[K], p2[K];
+            // the pair's C rows are loaded with its B rows and used after the scan, so that
+            // their loads are in flight during the chain and the scan
+            Raw<T, K> rc1, rc2;
+            load_raw<T, K, VEC>(Cb + static_cast<size_t>(MSEL_IDX(n, N)) * L, t0, L, rc1);
+            load_raw<T, K, VEC>(Cb + static_cast<size_t>(MSEL_IDX(n + 1, N)) * L, t0, L, rc2);
             load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(n, N)) * L, t0, L, p1);
             load_k_cached<T, K, VEC>(Bb + static_cast<size_t>(MSEL_IDX(n + 1, N)) * L, t0, L, p2);
             float h1 = 0.0f, h2 = 0.0f;
@@ -121,8 +126,8 @@ __global__ __launch_bounds__(256) void scan_cplx_fwd_kernel(ScanParams p) {
             }
 
             float c1[K], c2[K];
-            load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(MSEL_IDX(n, N)) * L, t0, L, c1);
-            load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(MSEL_IDX(n + 1, N)) * L, t0, L, c2);
+            unpack(rc1, c1);
+            unpack(rc2, c2);
             h1 = hr;
             h2 = hi;
 #pragma unroll

@@ -223,6 +223,11 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
                     bb[k] = du[k] * bc[k];
                 h = k == 0 ? bb[0] : fmaf(a[k], h, bb[k]);  // the chain from a zero state
             }
+            // without the stage the C rows' loads are issued here, where the B values are no
+            // longer needed, and are in flight during the scan
+            [[maybe_unused]] Raw<T, K> rcn;
+            if constexpr (!STAGE)
+                load_raw<T, K, VEC>(Cb + static_cast<size_t>(MSEL_IDX(n, N)) * L, t0, L, rcn);
             float P = exp2_hw(An * sum_dt);
             float S = h;
             scan_fwd_fused(P, S);
@@ -233,7 +238,7 @@ __global__ __launch_bounds__((64 * fwd_waves<T, TRAP>())) void scan_fwd_kernel(S
                 cells[wave][MSEL_IDX(2 + lane / (kChunk / K), 2 + kCpt)][MSEL_IDX(n, kMaxN)] = hin;
 
             if constexpr (STAGE) Stage::read(stage[buf], 1, lane, bc);
-            else load_k_cached<T, K, VEC>(Cb + static_cast<size_t>(MSEL_IDX(n, N)) * L, t0, L, bc);
+            else unpack(rcn, bc);
             h = hin;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
